@@ -1,0 +1,235 @@
+// C ABI of libmita.so: argument validation, workspace layout and the launch
+// sequence of the MiTA forward pass.  No allocation, no host copies, no
+// synchronisation: everything is enqueued on the caller's stream.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/mita.h"
+#include "internal.h"
+
+using mita::Shape;
+using mita::align_up;
+
+namespace {
+
+thread_local std::string g_error;
+
+mita_status fail(mita_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+mita_status ok() {
+  g_error.clear();
+  return MITA_OK;
+}
+
+mita_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MITA_OK;
+  return fail(MITA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Shape checks common to every entry point.  Returns MITA_OK and fills *s.
+mita_status make_shape(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
+                       mita_dtype dt, Shape* s) {
+  if (B < 1 || H < 1) return fail(MITA_ERR_INVALID_ARG, "B=%d and H=%d must be >= 1", B, H);
+  if (grid_h < 1 || grid_w < 1)
+    return fail(MITA_ERR_INVALID_ARG, "grid %dx%d must be at least 1x1", grid_h, grid_w);
+  if (m_h < 1 || m_w < 1 || m_h > grid_h || m_w > grid_w)
+    return fail(MITA_ERR_INVALID_ARG, "landmark grid %dx%d must lie within 1x1..%dx%d", m_h, m_w,
+                grid_h, grid_w);
+  if (dt != MITA_F32 && dt != MITA_BF16)
+    return fail(MITA_ERR_INVALID_ARG, "unknown input dtype %d", (int)dt);
+  const long long N = (long long)grid_h * grid_w;
+  const long long m = (long long)m_h * m_w;
+  if (k < 1 || k > N) return fail(MITA_ERR_INVALID_ARG, "k=%d must lie in [1, N=%lld]", k, N);
+  if (d != MITA_HEAD_DIM)
+    return fail(MITA_ERR_UNSUPPORTED, "head dim d=%d: only %d is implemented", d, MITA_HEAD_DIM);
+  if (N > MITA_MAX_N) return fail(MITA_ERR_UNSUPPORTED, "N=%lld exceeds %d", N, MITA_MAX_N);
+  if (m > MITA_MAX_M) return fail(MITA_ERR_UNSUPPORTED, "m=%lld exceeds %d", m, MITA_MAX_M);
+  if (k > MITA_MAX_K) return fail(MITA_ERR_UNSUPPORTED, "k=%d exceeds %d", k, MITA_MAX_K);
+  const long long BH = (long long)B * H;
+  if (BH > 65535) return fail(MITA_ERR_UNSUPPORTED, "B*H=%lld exceeds 65535", BH);
+  s->B = B; s->H = H; s->grid_h = grid_h; s->grid_w = grid_w; s->d = d;
+  s->m_h = m_h; s->m_w = m_w; s->k = k;
+  s->N = (int)N; s->m = (int)m; s->BH = (int)BH;
+  s->bf16 = (dt == MITA_BF16);
+  return MITA_OK;
+}
+
+// Workspace of the staged schedule: every intermediate the caller did not
+// supply, then the landmark pass's scratch.
+struct Layout {
+  size_t ql, vl, idx, route, counts, offsets, perm, scratch, total;
+};
+
+Layout layout_of(const Shape& s) {
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t at = off; off += align_up(bytes, 256); return at; };
+  L.ql = take((size_t)s.BH * s.m * s.d * 4);
+  L.vl = take((size_t)s.BH * s.m * s.d * 4);
+  L.idx = take((size_t)s.BH * s.m * s.k * 4);
+  L.route = take((size_t)s.BH * s.N * 4);
+  L.counts = take((size_t)s.BH * s.m * 4);
+  L.offsets = take((size_t)s.BH * (s.m + 1) * 4);
+  L.perm = take((size_t)s.BH * s.N * 4);
+  L.scratch = take(mita::landmark_scratch_bytes(s));
+  L.total = off;
+  return L;
+}
+
+template <typename P>
+P* pick(P* user, void* ws, size_t off) {
+  return user ? user : (P*)((char*)ws + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mita_status_string(mita_status s) {
+  switch (s) {
+    case MITA_OK: return "MITA_OK";
+    case MITA_ERR_INVALID_ARG: return "MITA_ERR_INVALID_ARG";
+    case MITA_ERR_UNSUPPORTED: return "MITA_ERR_UNSUPPORTED";
+    case MITA_ERR_WORKSPACE: return "MITA_ERR_WORKSPACE";
+    case MITA_ERR_HIP: return "MITA_ERR_HIP";
+  }
+  return "MITA_ERR_UNKNOWN";
+}
+
+const char* mita_last_error(void) { return g_error.c_str(); }
+
+const char* mita_version(void) { return "mita-gfx950 0.1"; }
+
+size_t mita_workspace_bytes(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
+                            mita_dtype in_dtype) {
+  Shape s;
+  if (make_shape(B, H, grid_h, grid_w, d, m_h, m_w, k, in_dtype, &s) != MITA_OK) return 0;
+  return layout_of(s).total;
+}
+
+mita_status mita_forward_ex(const void* Q, const void* K, const void* V, int B, int H, int grid_h,
+                            int grid_w, int d, int m_h, int m_w, int k, mita_dtype in_dtype,
+                            float* out, int32_t* idx, int32_t* route, const mita_extras* extras,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Shape s;
+  mita_status st = make_shape(B, H, grid_h, grid_w, d, m_h, m_w, k, in_dtype, &s);
+  if (st != MITA_OK) return st;
+  if (!Q || !K || !V || !out) return fail(MITA_ERR_INVALID_ARG, "Q, K, V and out are required");
+  const Layout L = layout_of(s);
+  if (!workspace) return fail(MITA_ERR_INVALID_ARG, "workspace is required");
+  if (workspace_bytes < L.total)
+    return fail(MITA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
+                L.total);
+  if (((uintptr_t)workspace) & 255) return fail(MITA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  const int path = extras ? extras->path : MITA_PATH_AUTO;
+  if (path != MITA_PATH_AUTO && path != MITA_PATH_STAGED && path != MITA_PATH_FUSED)
+    return fail(MITA_ERR_INVALID_ARG, "unknown path %d", path);
+  if (path == MITA_PATH_FUSED) return fail(MITA_ERR_UNSUPPORTED, "fused schedule not available");
+
+  float* ql = pick(extras ? extras->ql : nullptr, workspace, L.ql);
+  float* vl = pick(extras ? extras->vl : nullptr, workspace, L.vl);
+  int32_t* counts = pick(extras ? extras->counts : nullptr, workspace, L.counts);
+  int32_t* offsets = pick(extras ? extras->offsets : nullptr, workspace, L.offsets);
+  int32_t* perm = pick(extras ? extras->perm : nullptr, workspace, L.perm);
+  int32_t* idx_p = pick(idx, workspace, L.idx);
+  int32_t* route_p = pick(route, workspace, L.route);
+  void* scratch = (char*)workspace + L.scratch;
+
+  if ((st = hip_status(mita::launch_pool(Q, ql, s, stream), "pool launch")) != MITA_OK) return st;
+  if ((st = hip_status(mita::launch_landmark(ql, K, V, idx_p, vl, scratch, s, stream),
+                       "landmark launch")) != MITA_OK)
+    return st;
+  if ((st = hip_status(mita::launch_route(Q, ql, route_p, counts, offsets, perm, s, stream),
+                       "route launch")) != MITA_OK)
+    return st;
+  if ((st = hip_status(mita::launch_attend(Q, K, V, ql, vl, idx_p, route_p, offsets, perm, out, s,
+                                           stream),
+                       "attend launch")) != MITA_OK)
+    return st;
+  return ok();
+}
+
+mita_status mita_forward(const void* Q, const void* K, const void* V, int B, int H, int grid_h,
+                         int grid_w, int d, int m_h, int m_w, int k, mita_dtype in_dtype,
+                         float* out, int32_t* idx, int32_t* route, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  return mita_forward_ex(Q, K, V, B, H, grid_h, grid_w, d, m_h, m_w, k, in_dtype, out, idx, route,
+                         nullptr, workspace, workspace_bytes, stream);
+}
+
+mita_status mita_pool(const void* Q, int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w,
+                      mita_dtype in_dtype, float* ql, hipStream_t stream) {
+  Shape s;
+  mita_status st = make_shape(B, H, grid_h, grid_w, d, m_h, m_w, 1, in_dtype, &s);
+  if (st != MITA_OK) return st;
+  if (!Q || !ql) return fail(MITA_ERR_INVALID_ARG, "Q and ql are required");
+  if ((st = hip_status(mita::launch_pool(Q, ql, s, stream), "pool launch")) != MITA_OK) return st;
+  return ok();
+}
+
+size_t mita_landmark_workspace_bytes(int B, int H, int N, int d, int m, int k,
+                                     mita_dtype in_dtype) {
+  Shape s;
+  if (make_shape(B, H, N, 1, d, m, 1, k, in_dtype, &s) != MITA_OK) return 0;
+  return mita::landmark_scratch_bytes(s);
+}
+
+mita_status mita_landmark(const float* ql, const void* K, const void* V, int B, int H, int N, int d,
+                          int m, int k, mita_dtype in_dtype, int32_t* idx, float* vl,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  Shape s;
+  mita_status st = make_shape(B, H, N, 1, d, m, 1, k, in_dtype, &s);
+  if (st != MITA_OK) return st;
+  if (!ql || !K || !V || !idx || !vl)
+    return fail(MITA_ERR_INVALID_ARG, "ql, K, V, idx and vl are required");
+  const size_t need = mita::landmark_scratch_bytes(s);
+  if (need && !workspace) return fail(MITA_ERR_INVALID_ARG, "workspace is required");
+  if (workspace_bytes < need)
+    return fail(MITA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+  if ((st = hip_status(mita::launch_landmark(ql, K, V, idx, vl, workspace, s, stream),
+                       "landmark launch")) != MITA_OK)
+    return st;
+  return ok();
+}
+
+mita_status mita_route(const void* Q, const float* ql, int B, int H, int N, int d, int m,
+                       mita_dtype in_dtype, int32_t* route, int32_t* counts, int32_t* offsets,
+                       int32_t* perm, hipStream_t stream) {
+  Shape s;
+  mita_status st = make_shape(B, H, N, 1, d, m, 1, 1, in_dtype, &s);
+  if (st != MITA_OK) return st;
+  if (!Q || !ql || !route || !counts || !offsets || !perm)
+    return fail(MITA_ERR_INVALID_ARG, "Q, ql, route, counts, offsets and perm are required");
+  if ((st = hip_status(mita::launch_route(Q, ql, route, counts, offsets, perm, s, stream),
+                       "route launch")) != MITA_OK)
+    return st;
+  return ok();
+}
+
+mita_status mita_attend(const void* Q, const void* K, const void* V, const float* ql,
+                        const float* vl, const int32_t* idx, const int32_t* route,
+                        const int32_t* offsets, const int32_t* perm, int B, int H, int N, int d,
+                        int m, int k, mita_dtype in_dtype, float* out, hipStream_t stream) {
+  Shape s;
+  mita_status st = make_shape(B, H, N, 1, d, m, 1, k, in_dtype, &s);
+  if (st != MITA_OK) return st;
+  if (!Q || !K || !V || !ql || !vl || !idx || !route || !offsets || !perm || !out)
+    return fail(MITA_ERR_INVALID_ARG, "every tensor argument of mita_attend is required");
+  if ((st = hip_status(mita::launch_attend(Q, K, V, ql, vl, idx, route, offsets, perm, out, s,
+                                           stream),
+                       "attend launch")) != MITA_OK)
+    return st;
+  return ok();
+}
+
+}  // extern "C"

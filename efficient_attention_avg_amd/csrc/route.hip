@@ -1,0 +1,95 @@
+// Steps a5-a6 -- routing and grouping (page "NeurIPS'26：注意力也是FFN？...",
+// landmark-query section: each query picks the routed expert of the landmark
+// it matches best; Algorithm 1 then groups the queries by that route so each
+// expert's keys are fetched once per group).
+//
+// route_n = argmax_i q_n . Q_L[i] with ties to the lowest i (a strict '>'
+// scan in landmark order).  Grouping is a per-head stable counting sort:
+// histogram, exclusive scan, then an order-preserving scatter.
+#include "common.h"
+#include "internal.h"
+
+namespace mita {
+
+template <typename T>
+__global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ Q,
+                                                    const float* __restrict__ ql,
+                                                    int32_t* __restrict__ route, int N, int m) {
+  const int bh = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  const T* qr = Q + ((size_t)bh * N + n) * kHeadDim;
+  float q[kHeadDim];
+#pragma unroll
+  for (int c = 0; c < kHeadDim; ++c) q[c] = to_f32(qr[c]);
+  const float* L = ql + (size_t)bh * m * kHeadDim;
+  float best = -INFINITY;
+  int arg = 0;
+  for (int i = 0; i < m; ++i) {
+    float a = 0.f;
+#pragma unroll
+    for (int c = 0; c < kHeadDim; ++c) a = fmaf(q[c], L[i * kHeadDim + c], a);
+    if (a > best) {
+      best = a;
+      arg = i;
+    }
+  }
+  route[(size_t)bh * N + n] = arg;
+}
+
+__global__ __launch_bounds__(256) void group_kernel(const int32_t* __restrict__ route,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ perm, int N, int m) {
+  extern __shared__ int gsm[];
+  int* cnt = gsm;          // [m]
+  int* cur = gsm + m;      // [m]
+  int* cr = gsm + 2 * m;   // [256]
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int32_t* r = route + (size_t)bh * N;
+  for (int e = tid; e < m; e += 256) cnt[e] = 0;
+  __syncthreads();
+  for (int n = tid; n < N; n += 256) atomicAdd(&cnt[r[n]], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int e = 0; e < m; ++e) {
+      cur[e] = run;
+      offsets[(size_t)bh * (m + 1) + e] = run;
+      run += cnt[e];
+    }
+    offsets[(size_t)bh * (m + 1) + m] = run;
+  }
+  for (int e = tid; e < m; e += 256) counts[(size_t)bh * m + e] = cnt[e];
+  __syncthreads();
+  for (int n0 = 0; n0 < N; n0 += 256) {
+    const int n = n0 + tid;
+    const int e = n < N ? r[n] : -1;
+    cr[tid] = e;
+    __syncthreads();
+    if (n < N) {
+      int rank = 0;
+      for (int j = 0; j < tid; ++j) rank += (cr[j] == e);
+      perm[(size_t)bh * N + cur[e] + rank] = n;
+    }
+    __syncthreads();
+    if (n < N) atomicAdd(&cur[e], 1);
+    __syncthreads();
+  }
+}
+
+hipError_t launch_route(const void* Q, const float* ql, int32_t* route, int32_t* counts,
+                        int32_t* offsets, int32_t* perm, const Shape& s, hipStream_t st) {
+  dim3 grid((s.N + 255) / 256, s.BH);
+  if (s.bf16)
+    route_kernel<bf16_t><<<grid, 256, 0, st>>>((const bf16_t*)Q, ql, route, s.N, s.m);
+  else
+    route_kernel<float><<<grid, 256, 0, st>>>((const float*)Q, ql, route, s.N, s.m);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const size_t lds = (size_t)(2 * s.m + 256) * sizeof(int);
+  group_kernel<<<s.BH, 256, lds, st>>>(route, counts, offsets, perm, s.N, s.m);
+  return hipGetLastError();
+}
+
+}  // namespace mita

@@ -1,0 +1,167 @@
+/*
+ * mita.h -- C ABI of the MiTA (Mixture-of-Top-k Attention) forward pass on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the attention layer described on the page
+ * "NeurIPS'26：注意力也是FFN？从快权重出发，重新理解高效注意力" (新智元/36氪),
+ * section "用少量地标查询，同时构造全局概括与细节专家" and its Algorithm 1
+ * (English version: "NeurIPS'26: Is Attention Also FFN? ...", section
+ * "Construct global generalization and detail experts at the same time with
+ * a small number of landmark queries").  Per (batch b, head h), with
+ * N = grid_h*grid_w tokens in row-major order, m = m_h*m_w landmarks and
+ * tau = 1/sqrt(d):
+ *   Q_L     = 2-D adaptive average pooling of Q over the token grid  (m x d)
+ *   S       = tau * Q_L K^T                                           (m x N)
+ *   idx_i   = top-k keys of S[i,:], ties to the lowest key index      (m x k)
+ *   V_L     = softmax_row(S) V                                        (m x d)
+ *   route_n = argmax_i q_n . Q_L[i], ties to the lowest landmark      (N)
+ *   out_n   = softmax(tau*[q_n Q_L^T, q_n K[idx_e]^T]) [V_L; V[idx_e]],
+ *             e = route_n                                              (N x d)
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees, copies to the host or synchronises; it
+ *     enqueues kernels on `stream` and returns (asynchronous).
+ *   - Q, K, V, out are contiguous [B, H, N, d] row-major (token n = y*grid_w+x),
+ *     16-byte aligned.  Q, K, V are fp32 or bf16 (`in_dtype`); out is fp32.
+ *   - Index outputs are int32.  idx rows list key ids in ascending order.
+ *   - d must be 64 (MITA_ERR_UNSUPPORTED otherwise).
+ *   - Arguments are validated on the host before anything is enqueued; on a
+ *     non-OK status nothing was launched.  MITA_ERR_HIP reports a failed
+ *     launch.  mita_last_error() gives a thread-local description.
+ *   - The same inputs give bitwise-identical outputs on every call.
+ */
+#ifndef MITA_H
+#define MITA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MITA_OK = 0,
+  MITA_ERR_INVALID_ARG = 1,  /* null pointer, bad size or range            */
+  MITA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (d != 64, ...)    */
+  MITA_ERR_WORKSPACE = 3,    /* workspace too small                         */
+  MITA_ERR_HIP = 4           /* a HIP call or kernel launch failed          */
+} mita_status;
+
+typedef enum { MITA_F32 = 0, MITA_BF16 = 1 } mita_dtype;
+
+/* Implementation limits (checked, MITA_ERR_UNSUPPORTED beyond them). */
+#define MITA_HEAD_DIM 64
+#define MITA_MAX_M 1024
+#define MITA_MAX_K 1024
+#define MITA_MAX_N (1 << 22)
+
+/* Which kernel schedule mita_forward_ex runs. AUTO picks by shape. */
+typedef enum { MITA_PATH_AUTO = 0, MITA_PATH_FUSED = 1, MITA_PATH_STAGED = 2 } mita_path;
+
+/* Human-readable name of a status code (static storage). */
+const char* mita_status_string(mita_status s);
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char* mita_last_error(void);
+
+/* Library version string (static storage). */
+const char* mita_version(void);
+
+/*
+ * Bytes of device workspace mita_forward needs for this shape (the "device
+ * memory query"): the caller allocates it (e.g. through PyTorch) and passes it
+ * in.  Returns 0 for an invalid shape.  The layout inside is private.
+ */
+size_t mita_workspace_bytes(int B, int H, int grid_h, int grid_w, int d,
+                            int m_h, int m_w, int k, mita_dtype in_dtype);
+
+/*
+ * The whole forward pass (all steps above) on `stream`.
+ *   out   [B,H,N,d] fp32, required.
+ *   idx   [B,H,m,k] int32 or NULL: each landmark's expert (ascending key ids).
+ *   route [B,H,N]   int32 or NULL: each query's landmark id in [0, m).
+ *   workspace: at least mita_workspace_bytes(...) bytes of device memory,
+ *   256-byte aligned; contents on entry are ignored.
+ */
+mita_status mita_forward(const void* Q, const void* K, const void* V,
+                         int B, int H, int grid_h, int grid_w, int d,
+                         int m_h, int m_w, int k, mita_dtype in_dtype,
+                         float* out, int32_t* idx, int32_t* route,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Optional extra outputs of mita_forward_ex (any member may be NULL), and the
+ * schedule to run.  Used to check every intermediate of the pass.
+ *   ql      [B,H,m,d] fp32  landmark queries
+ *   vl      [B,H,m,d] fp32  landmark values (shared expert values)
+ *   counts  [B,H,m]   int32 queries routed to each landmark
+ *   offsets [B,H,m+1] int32 exclusive prefix sum of counts
+ *   perm    [B,H,N]   int32 query ids grouped by route, ascending within a group
+ */
+typedef struct {
+  float* ql;
+  float* vl;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int path; /* mita_path */
+} mita_extras;
+
+mita_status mita_forward_ex(const void* Q, const void* K, const void* V,
+                            int B, int H, int grid_h, int grid_w, int d,
+                            int m_h, int m_w, int k, mita_dtype in_dtype,
+                            float* out, int32_t* idx, int32_t* route,
+                            const mita_extras* extras,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * The steps one at a time (same kernels as the staged schedule).  Each takes
+ * its inputs from device memory and writes its outputs there, so a caller can
+ * run, time or check one step in isolation.
+ * ------------------------------------------------------------------------- */
+
+/* Landmark pooling: Q [B,H,N,d] -> ql [B,H,m,d] fp32 (window mean, fp32 sums). */
+mita_status mita_pool(const void* Q, int B, int H, int grid_h, int grid_w, int d,
+                      int m_h, int m_w, mita_dtype in_dtype, float* ql, hipStream_t stream);
+
+/*
+ * Landmark pass: scores of ql [B,H,m,d] fp32 against K [B,H,N,d], each row's
+ * top-k keys -> idx [B,H,m,k] (ascending), and the row softmax applied to V
+ * -> vl [B,H,m,d] fp32.  Needs mita_landmark_workspace_bytes(...) of scratch.
+ */
+size_t mita_landmark_workspace_bytes(int B, int H, int N, int d, int m, int k,
+                                     mita_dtype in_dtype);
+mita_status mita_landmark(const float* ql, const void* K, const void* V,
+                          int B, int H, int N, int d, int m, int k, mita_dtype in_dtype,
+                          int32_t* idx, float* vl,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Routing and grouping: route [B,H,N] = argmax_i q_n . ql[i] (lowest i on
+ * ties), then a stable counting sort of each head's queries by route:
+ * counts [B,H,m], offsets [B,H,m+1], perm [B,H,N].
+ */
+mita_status mita_route(const void* Q, const float* ql, int B, int H, int N, int d, int m,
+                       mita_dtype in_dtype, int32_t* route, int32_t* counts,
+                       int32_t* offsets, int32_t* perm, hipStream_t stream);
+
+/*
+ * Grouped expert attention: for every query, one softmax over its m shared
+ * logits and the k logits of its routed expert (idx row route_n), applied to
+ * [vl; V[idx]] -> out [B,H,N,d] fp32.  offsets/perm must be the grouping of
+ * `route` produced by mita_route.
+ */
+mita_status mita_attend(const void* Q, const void* K, const void* V,
+                        const float* ql, const float* vl, const int32_t* idx,
+                        const int32_t* route, const int32_t* offsets, const int32_t* perm,
+                        int B, int H, int N, int d, int m, int k, mita_dtype in_dtype,
+                        float* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MITA_H */

@@ -1,0 +1,101 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, and
+rejects bad arguments before anything reaches the GPU (no launches here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import efficient_attention_avg_amd as mita
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "mita.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mita_[a-z_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(mita.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = mita.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    assert L.mita_version().decode().startswith("mita-gfx950")
+
+
+def test_status_strings():
+    L = mita.lib()
+    names = [L.mita_status_string(s).decode() for s in range(5)]
+    assert names == ["MITA_OK", "MITA_ERR_INVALID_ARG", "MITA_ERR_UNSUPPORTED",
+                     "MITA_ERR_WORKSPACE", "MITA_ERR_HIP"]
+
+
+def test_workspace_bytes():
+    ws = mita.mita_workspace_bytes
+    assert ws(256, 6, 14, 14, 64, 5, 5, 25, mita.MITA_BF16) > 0
+    assert ws(32, 6, 56, 56, 64, 7, 7, 64, mita.MITA_BF16) > 0
+    assert ws(1, 1, 14, 14, 64, 5, 5, 0, mita.MITA_F32) == 0       # k < 1
+    assert ws(1, 1, 14, 14, 32, 5, 5, 25, mita.MITA_F32) == 0      # d != 64
+    assert ws(1, 1, 14, 14, 64, 15, 5, 25, mita.MITA_F32) == 0     # m_h > grid_h
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every case fails validation first
+
+
+def _fwd(B=1, H=1, gh=14, gw=14, d=64, mh=5, mw=5, k=25, dt=mita.MITA_BF16, q=FAKE, out=FAKE,
+         ws=FAKE, nbytes=1 << 40, extras=None):
+    L = mita.lib()
+    return L.mita_forward_ex(q, FAKE, FAKE, B, H, gh, gw, d, mh, mw, k, dt, out, None, None,
+                             extras, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), mita.MITA_ERR_INVALID_ARG),
+    (dict(H=-1), mita.MITA_ERR_INVALID_ARG),
+    (dict(k=0), mita.MITA_ERR_INVALID_ARG),
+    (dict(k=197), mita.MITA_ERR_INVALID_ARG),
+    (dict(mh=15), mita.MITA_ERR_INVALID_ARG),
+    (dict(mw=0), mita.MITA_ERR_INVALID_ARG),
+    (dict(gh=0), mita.MITA_ERR_INVALID_ARG),
+    (dict(dt=7), mita.MITA_ERR_INVALID_ARG),
+    (dict(d=128), mita.MITA_ERR_UNSUPPORTED),
+    (dict(q=None), mita.MITA_ERR_INVALID_ARG),
+    (dict(out=None), mita.MITA_ERR_INVALID_ARG),
+    (dict(ws=None), mita.MITA_ERR_INVALID_ARG),
+    (dict(nbytes=16), mita.MITA_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x10010)), mita.MITA_ERR_INVALID_ARG),   # misaligned
+    (dict(B=65536), mita.MITA_ERR_UNSUPPORTED),
+])
+def test_forward_rejects_before_launch(kw, status):
+    assert _fwd(**kw) == status
+    assert mita.lib().mita_last_error().decode() != ""
+
+
+def test_forward_rejects_unknown_path():
+    ex = mita._Extras(path=9)
+    assert _fwd(extras=ctypes.byref(ex)) == mita.MITA_ERR_INVALID_ARG
+
+
+def test_stage_entry_points_validate():
+    L = mita.lib()
+    assert L.mita_pool(None, 1, 1, 14, 14, 64, 5, 5, 1, FAKE, None) == mita.MITA_ERR_INVALID_ARG
+    assert L.mita_landmark(FAKE, FAKE, FAKE, 1, 1, 196, 64, 25, 26 * 0 + 197, 1, FAKE, FAKE, FAKE,
+                           1 << 40, None) == mita.MITA_ERR_INVALID_ARG          # k > N
+    assert L.mita_landmark(FAKE, FAKE, FAKE, 1, 1, 196, 64, 25, 25, 1, FAKE, FAKE, FAKE, 4,
+                           None) == mita.MITA_ERR_WORKSPACE
+    assert L.mita_route(FAKE, FAKE, 1, 1, 196, 64, 25, 1, FAKE, FAKE, None, FAKE,
+                        None) == mita.MITA_ERR_INVALID_ARG
+    assert L.mita_attend(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 196, 64, 25,
+                         25, 1, None, None) == mita.MITA_ERR_INVALID_ARG
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 196, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mita.mita_forward(q, q, q, 14, 14, 5, 5, 25)

@@ -1,0 +1,150 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerances: max-abs 1e-4 on fp32 inputs, 1e-2 on bf16 inputs, for Q_L, V_L
+and out; top-k sets and routes bit-exact outside counted near-ties (see
+tests/parity.py).  Every case prints its name before touching the GPU.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 1e-2}
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible GPU")
+    return torch
+
+
+def _say(msg):
+    print(f"[gpu case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _to_dev(x, dtype):
+    torch = _torch()
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)
+    return t.cuda()
+
+
+def run_gpu(Q, K, V, dtype, grid_h, grid_w, m_h, m_w, k, path="auto", extras=True):
+    import efficient_attention_avg_amd as mita
+    torch = _torch()
+    q, kk, v = (_to_dev(x, dtype) for x in (Q, K, V))
+    res = mita.mita_forward_ex(q, kk, v, grid_h, grid_w, m_h, m_w, k, idx=True, route=True,
+                               extras=extras, path=path)
+    torch.cuda.synchronize()
+    return {key: val.cpu().numpy() for key, val in res.items() if val is not None}
+
+
+SMALL = [
+    # B, H, gh, gw, mh, mw, k, dtype, smooth
+    (2, 3, 14, 14, 5, 5, 25, "bf16", True),
+    (1, 2, 20, 24, 6, 5, 37, "bf16", True),
+    (1, 1, 56, 56, 7, 7, 64, "bf16", True),
+    (1, 2, 9, 7, 3, 2, 63, "f32", False),     # k = N
+    (1, 1, 10, 10, 1, 1, 100, "bf16", True),  # m = 1, k = N
+    (1, 1, 6, 6, 6, 6, 3, "f32", False),      # m = N
+    (3, 1, 5, 5, 2, 2, 1, "bf16", True),      # k = 1
+    (1, 1, 1, 1, 1, 1, 1, "f32", False),      # N = 1
+    (1, 1, 33, 31, 4, 5, 200, "bf16", True),  # ragged everywhere
+    (2, 2, 14, 14, 5, 5, 25, "f32", False),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "x".join(map(str, c[:7])) + "-" + c[7])
+def test_small_shapes(case):
+    B, H, gh, gw, mh, mw, k, dtype, smooth = case
+    _say(f"small shape {case}")
+    Q, K, V = synth.make_qkv(B, H, gh, gw, 64, workload_id=100 + gh * 7 + gw, smooth=smooth,
+                             dtype=dtype)
+    res = run_gpu(Q, K, V, dtype, gh, gw, mh, mw, k)
+    rep = parity.run_and_check(res, Q, K, V, gh, gw, mh, mw, k, TOL[dtype])
+    _say(f"ok {rep}")
+
+
+@pytest.mark.parametrize("name", ["tiny-fp32", "deit-t", "deit-s", "hires-3136"])
+def test_workload_full(name):
+    w = synth.workload(name)
+    _say(f"workload {name} (all heads)")
+    Q, K, V = synth.workload_inputs(name)
+    res = run_gpu(Q, K, V, w["dtype"], w["grid_h"], w["grid_w"], w["m_h"], w["m_w"], w["k"])
+    rep = parity.run_and_check(res, Q, K, V, w["grid_h"], w["grid_w"], w["m_h"], w["m_w"], w["k"],
+                               TOL[w["dtype"]])
+    _say(f"ok {name}: {rep}")
+
+
+def test_workload_long_16k_sampled():
+    name = "long-16k"
+    w = synth.workload(name)
+    _say(f"workload {name} (full launch, sampled heads)")
+    Q, K, V = synth.workload_inputs(name)
+    res = run_gpu(Q, K, V, w["dtype"], w["grid_h"], w["grid_w"], w["m_h"], w["m_w"], w["k"])
+    heads = [(0, 0), (1, 3), (2, 7), (3, 5)]
+    rep = parity.run_and_check(res, Q, K, V, w["grid_h"], w["grid_w"], w["m_h"], w["m_w"], w["k"],
+                               TOL[w["dtype"]], heads=heads)
+    _say(f"ok {name}: {rep}")
+
+
+def test_stage_entry_points():
+    """Each step's own entry point against the oracle, fed the oracle's inputs where it needs them."""
+    import efficient_attention_avg_amd as mita
+    import oracle.mita_oracle as O
+    torch = _torch()
+    B, H, gh, gw, mh, mw, k = 2, 2, 21, 19, 4, 3, 30
+    _say("stage entry points")
+    Q, K, V = synth.make_qkv(B, H, gh, gw, 64, workload_id=777)
+    q, kk, v = (_to_dev(x, "bf16") for x in (Q, K, V))
+    ql = mita.mita_pool(q, gh, gw, mh, mw)
+    ref_ql = O.landmark_queries(Q, gh, gw, mh, mw)
+    assert np.abs(ql.cpu().numpy() - ref_ql).max() < 1e-5
+    ql_in = torch.from_numpy(ref_ql.astype(np.float32)).cuda()
+    idx, vl = mita.mita_landmark(ql_in, kk, v, k)
+    route, counts, offsets, perm = mita.mita_route(q, ql_in)
+    out = mita.mita_attend(q, kk, v, ql_in, vl, idx, route, offsets, perm)
+    torch.cuda.synchronize()
+    res = dict(out=out, idx=idx, route=route, vl=vl, counts=counts, offsets=offsets, perm=perm)
+    res = {key: val.cpu().numpy() for key, val in res.items()}
+    rep = parity.run_and_check(res, Q, K, V, gh, gw, mh, mw, k, 1e-2)
+    _say(f"ok stages: {rep}")
+
+
+def test_deterministic_and_fully_written():
+    import efficient_attention_avg_amd as mita
+    torch = _torch()
+    w = synth.workload("deit-s")
+    _say("determinism + NaN-poisoned outputs")
+    Q, K, V = synth.workload_inputs("deit-s", B=8)
+    q, kk, v = (_to_dev(x, "bf16") for x in (Q, K, V))
+    args = (w["grid_h"], w["grid_w"], w["m_h"], w["m_w"], w["k"])
+    out1 = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    mita.mita_forward(q, kk, v, *args, out=out1)
+    out2 = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.full((mita.mita_workspace_bytes(8, 6, 14, 14, 64, 5, 5, 25, mita.MITA_BF16),),
+                    255, dtype=torch.uint8, device="cuda")
+    mita.mita_forward(q, kk, v, *args, out=out2, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out1).all()
+    assert torch.equal(out1, out2)
+
+
+def test_constant_values_give_constant_output():
+    import efficient_attention_avg_amd as mita
+    torch = _torch()
+    _say("constant V")
+    Q, K, _ = synth.make_qkv(2, 2, 14, 14, 64, workload_id=31)
+    V = np.full_like(Q, 0.625)
+    q, kk, v = (_to_dev(x, "bf16") for x in (Q, K, V))
+    out = mita.mita_forward(q, kk, v, 14, 14, 5, 5, 25)
+    torch.cuda.synchronize()
+    assert np.abs(out.cpu().numpy() - 0.625).max() < 1e-5
