@@ -141,12 +141,21 @@ def measure(name, steps, warmup, path="auto"):
     wall = time.perf_counter() - t0
     warm_ms, _ = r.timed(r.step, steps, flush=False)
     log(f"{name}: cold {cold_ms * 1e3:.1f} us/step, warm {warm_ms * 1e3:.1f} us/step")
-    stages = r.stage_times(max(5, min(steps, 20)))
-    log(f"{name}: stage event times (us) " + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in stages.items()))
+    qh = alg["qh"]
+    code = r.mita.MITA_BF16 if w["dtype"] == "bf16" else r.mita.MITA_F32
+    sched = r.mita.mita_schedule(w["B"], w["H"], w["grid_h"], w["grid_w"], w["d"], w["m_h"],
+                                 w["m_w"], w["k"], code) if path == "auto" else path
+    if sched == "fused":
+        # one kernel is the whole pass: its algorithmic bytes are the pass's
+        stages = {"fused": cold_ms}
+        alg["kernel_bytes"]["fused"] = alg["bytes_per_qh"] * qh
+    else:
+        stages = r.stage_times(max(5, min(steps, 20)))
+    log(f"{name}: {sched} schedule, kernel event times (us) "
+        + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in stages.items()))
     dom = max(stages, key=stages.get)
     dom_bytes = alg["kernel_bytes"][dom]
     dom_gbs = dom_bytes / (stages[dom] * 1e-3) / 1e9
-    qh = alg["qh"]
     pass_gbs = alg["bytes_per_qh"] * qh / (cold_ms * 1e-3) / 1e9
     res = dict(
         workload=w, value=qh / (cold_ms * 1e-3), ms_per_step=cold_ms,
@@ -158,7 +167,8 @@ def measure(name, steps, warmup, path="auto"):
         pass_roofline=dict(bound="hbm", achieved=pass_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                            frac=pass_gbs / HBM_PEAK_GBS, bytes_per_qh=alg["bytes_per_qh"],
                            flops_per_qh=alg["flops_per_qh"]),
-        stage_us={k: v * 1e3 for k, v in stages.items()},
+        stage_us={k: v * 1e3 for k, v in stages.items()}, schedule=sched,
+        dtype="bf16" if (sched == "fused") else "f32",
     )
     return r, res
 
@@ -229,16 +239,17 @@ def main():
             "workload": describe(res2["workload"]), "value": res2["value"], "unit": "query-heads/s",
             "ms_per_step": res2["ms_per_step"], "warm_ms_per_step": res2["warm_ms_per_step"],
             "roofline": res2["roofline"], "pass_roofline": res2["pass_roofline"],
-            "stage_us": res2["stage_us"],
+            "stage_us": res2["stage_us"], "schedule": res2["schedule"], "dtype": res2["dtype"],
         }
     w = main_res["workload"]
     line = {
         "metric": METRIC, "value": main_res["value"], "unit": "query-heads/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
+        "dtype": main_res["dtype"], "data": "synthetic",
         "config": {"workload": describe(w), "B": w["B"], "H": w["H"], "seq_len": w["grid_h"] * w["grid_w"],
                    "m": w["m_h"] * w["m_w"], "k": w["k"], "path": args.path,
+                   "schedule": main_res["schedule"],
                    "timing": "HIP events per step, L2 + Infinity Cache flushed before each step"},
         "ms_p10": main_res["ms_p10"], "ms_p90": main_res["ms_p90"],
         "warm_ms_per_step": main_res["warm_ms_per_step"], "warm_value": main_res["warm_value"],

@@ -23,6 +23,7 @@ PATHS = {"auto": 0, "fused": 1, "staged": 2}
 # Every symbol include/mita.h declares.
 EXPORTS = [
     "mita_status_string", "mita_last_error", "mita_version", "mita_workspace_bytes",
+    "mita_schedule",
     "mita_forward", "mita_forward_ex", "mita_pool", "mita_landmark_workspace_bytes",
     "mita_landmark", "mita_route", "mita_attend",
 ]
@@ -59,6 +60,8 @@ def lib() -> ctypes.CDLL:
         L.mita_version.argtypes = []
         L.mita_workspace_bytes.restype = Z
         L.mita_workspace_bytes.argtypes = [I] * 8 + [I]
+        L.mita_schedule.restype = I
+        L.mita_schedule.argtypes = [I] * 8 + [I]
         L.mita_forward.restype = S
         L.mita_forward.argtypes = [P, P, P] + [I] * 8 + [I, P, P, P, P, Z, P]
         L.mita_forward_ex.restype = S
@@ -135,6 +138,14 @@ def _qkv(q, k, v):
 
 def mita_workspace_bytes(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code) -> int:
     return int(lib().mita_workspace_bytes(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code))
+
+
+def mita_schedule(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code) -> str:
+    """'fused' or 'staged': the schedule mita_forward picks for this shape."""
+    r = int(lib().mita_schedule(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code))
+    if r < 0:
+        raise MitaError(MITA_ERR_INVALID_ARG, "invalid shape")
+    return {1: "fused", 2: "staged"}[r]
 
 
 def mita_forward(q, k, v, grid_h, grid_w, m_h, m_w, topk, *, out=None, idx=None, route=None,

@@ -117,6 +117,13 @@ size_t mita_workspace_bytes(int B, int H, int grid_h, int grid_w, int d, int m_h
   return layout_of(s).total;
 }
 
+int mita_schedule(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
+                  mita_dtype in_dtype) {
+  Shape s;
+  if (make_shape(B, H, grid_h, grid_w, d, m_h, m_w, k, in_dtype, &s) != MITA_OK) return -1;
+  return mita::fused_supported(s) ? MITA_PATH_FUSED : MITA_PATH_STAGED;
+}
+
 mita_status mita_forward_ex(const void* Q, const void* K, const void* V, int B, int H, int grid_h,
                             int grid_w, int d, int m_h, int m_w, int k, mita_dtype in_dtype,
                             float* out, int32_t* idx, int32_t* route, const mita_extras* extras,
@@ -134,7 +141,19 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V, int B, 
   const int path = extras ? extras->path : MITA_PATH_AUTO;
   if (path != MITA_PATH_AUTO && path != MITA_PATH_STAGED && path != MITA_PATH_FUSED)
     return fail(MITA_ERR_INVALID_ARG, "unknown path %d", path);
-  if (path == MITA_PATH_FUSED) return fail(MITA_ERR_UNSUPPORTED, "fused schedule not available");
+  const bool fusable = mita::fused_supported(s);
+  if (path == MITA_PATH_FUSED && !fusable)
+    return fail(MITA_ERR_UNSUPPORTED,
+                "fused schedule needs bf16 inputs, N <= 208, m <= 32 and k <= 32");
+  if (fusable && path != MITA_PATH_STAGED) {
+    st = hip_status(mita::launch_fused(Q, K, V, out, idx, route, extras ? extras->ql : nullptr,
+                                       extras ? extras->vl : nullptr,
+                                       extras ? extras->counts : nullptr,
+                                       extras ? extras->offsets : nullptr,
+                                       extras ? extras->perm : nullptr, s, stream),
+                    "fused launch");
+    return st != MITA_OK ? st : ok();
+  }
 
   float* ql = pick(extras ? extras->ql : nullptr, workspace, L.ql);
   float* vl = pick(extras ? extras->vl : nullptr, workspace, L.vl);

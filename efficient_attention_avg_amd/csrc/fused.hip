@@ -1,0 +1,671 @@
+// The whole MiTA forward for one (batch, head) in one workgroup, for short
+// token grids (N <= 208, m <= 32, k <= 32, d = 64, bf16 inputs): the DeiT-T /
+// DeiT-S shape (14x14 patches, 5x5 landmarks, k = 25) of the page
+// "NeurIPS'26：注意力也是FFN？从快权重出发，重新理解高效注意力", section
+// "用少量地标查询，同时构造全局概括与细节专家" and Algorithm 1.
+//
+// A head's Q, K and V (75 KB in bf16) fit in LDS with room for the score
+// matrix, so every step runs out of LDS and each input byte crosses HBM once:
+//   A  stage Q, K (bf16, XOR-swizzled rows) and V^T (f16, keys contiguous)
+//      into LDS; issue the NEXT head's global loads into registers so they
+//      fly during this head's compute (persistent grid, one 8-wave
+//      workgroup per CU);
+//   B  landmark pooling -> Q_L (fp32) split into bf16 hi + lo;
+//   C  S^T = K Q_L^T and R = Q Q_L^T on bf16 MFMA (hi + lo: near-fp32 scores,
+//      so top-k sets and routes are decided at fp32 accuracy); routes are a
+//      16-lane argmax over R with ties to the lower landmark;
+//   D  per landmark row, exact top-k by value-range histogram refinement
+//      (ties to the lower key id), then P = exp(S - max) in f16;
+//   E  V_L^T = V^T P^T on f16 MFMA, normalised by the row sums;
+//   F  stable counting sort of the queries by route (ballots) and a list of
+//      <= 16-query tiles per expert;
+//   G  per tile: logits^T = [Q_L; K_e] Q_g^T (bf16 MFMA, K_e rows read in
+//      place from LDS), one softmax over the m + k entries per query, and
+//      out^T = [V_L; V_e]^T P^T (f16 MFMA, P fed straight from the logits'
+//      accumulators), written as fp32.
+#include "common.h"
+#include "internal.h"
+#include "mfma.h"
+
+namespace mita {
+namespace fused {
+
+constexpr int MAXNT = 13;           // 16-token tiles
+constexpr int NP = MAXNT * 16;      // 208 padded tokens
+constexpr int KPMAX = 224;          // keys padded to a multiple of 32 (P V k-steps)
+constexpr int THREADS = 512;
+constexpr int NWAVES = THREADS / 64;
+constexpr int MMAX = 32, KMAX = 32;
+
+constexpr int VT_STRIDE = 464;      // bytes per V^T row (f16 keys)
+constexpr int S_STRIDE = 212;       // floats per score row
+constexpr int H_STRIDE = 528;       // bytes per histogram / P row
+constexpr int VLT_STRIDE = 80;      // bytes per V_L^T row (f16 landmarks)
+
+constexpr int OFF_Q = 0;
+constexpr int OFF_K = OFF_Q + NP * 128;
+constexpr int OFF_VT = OFF_K + NP * 128;
+constexpr int OFF_S = OFF_VT + 64 * VT_STRIDE;
+constexpr int OFF_H = OFF_S + MMAX * S_STRIDE * 4;
+constexpr int OFF_QLH = OFF_H + MMAX * H_STRIDE;
+constexpr int OFF_QLL = OFF_QLH + MMAX * 128;
+constexpr int OFF_VLT = OFF_QLL + MMAX * 128;
+constexpr int OFF_IDX = OFF_VLT + 64 * VLT_STRIDE;
+constexpr int OFF_ROUTE = OFF_IDX + MMAX * KMAX * 4;
+constexpr int OFF_PERM = OFF_ROUTE + 256 * 4;
+constexpr int OFF_CNT = OFF_PERM + 256 * 4;       // [4 chunks][32] int
+constexpr int OFF_BASE = OFF_CNT + 4 * 32 * 4;    // [4 chunks][32] int
+constexpr int OFF_OFFS = OFF_BASE + 4 * 32 * 4;   // [33] int
+constexpr int OFF_TILES = OFF_OFFS + 48 * 4;      // [64] x (e, start, len, -)
+constexpr int OFF_STAT = OFF_TILES + 64 * 16;     // rowmax[32], rowsum[32], ntiles
+constexpr int LDS_BYTES = OFF_STAT + 80 * 4;
+static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 workgroup");
+static_assert(OFF_VT % 16 == 0 && OFF_S % 16 == 0 && OFF_H % 16 == 0 && OFF_QLH % 16 == 0 &&
+                  OFF_VLT % 16 == 0 && OFF_IDX % 16 == 0 && OFF_TILES % 16 == 0,
+              "16-byte aligned LDS regions");
+
+struct Outputs {
+  float* out;
+  int32_t* idx;
+  int32_t* route;
+  float* ql;
+  float* vl;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+};
+
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+  return z;
+}
+
+// Byte offset of 16-byte chunk `c` (0..7) of a 128-byte row, XOR-swizzled so
+// that 16 consecutive rows read at one logical chunk spread over the banks.
+__device__ __forceinline__ int rc(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
+
+template <typename P>
+__device__ __forceinline__ P* lds(char* base, int off) {
+  return reinterpret_cast<P*>(base + off);
+}
+
+// Values held by the 16-lane group of this lane (xor offsets < 16 stay inside).
+__device__ __forceinline__ float g16_max(float v) {
+  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float g16_min(float v) {
+  for (int o = 8; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float g16_sumf(float v) {
+  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ int g16_sumi(int v) {
+  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+// This lane's 16-lane group's bits of a wave ballot.
+__device__ __forceinline__ uint32_t g16_bits(uint64_t ballot, int g) {
+  return (uint32_t)(ballot >> (16 * g)) & 0xFFFFu;
+}
+
+// Q_L fragments (hi, lo) for both 16-landmark tiles and both 32-channel
+// steps: lane holds Q_L[16lt + c16][32ks + 8g .. +8].  They serve as the B
+// operand of S^T and R and as the A operand of the shared logits.
+__device__ __forceinline__ void load_ql(char* sm, u32x4 (&qlh)[2][2], u32x4 (&qll)[2][2], int g,
+                                        int c16) {
+#pragma unroll
+  for (int lt = 0; lt < 2; ++lt)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      qlh[lt][ks] = *lds<u32x4>(sm, OFF_QLH + rc(16 * lt + c16, 4 * ks + g));
+      qll[lt][ks] = *lds<u32x4>(sm, OFF_QLL + rc(16 * lt + c16, 4 * ks + g));
+    }
+}
+
+struct Prefetch {
+  u32x4 q[4], k[4], v0[2], v1[2];
+};
+
+__device__ __forceinline__ void prefetch(Prefetch& pf, const uint16_t* Qh, const uint16_t* Kh,
+                                         const uint16_t* Vh, int N, int tid) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = tid + THREADS * i, row = id >> 3, c = id & 7;
+    const bool ok = row < N;
+    pf.q[i] = ok ? *reinterpret_cast<const u32x4*>(Qh + row * 64 + c * 8) : z;
+    pf.k[i] = ok ? *reinterpret_cast<const u32x4*>(Kh + row * 64 + c * 8) : z;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int id = tid + THREADS * i;
+    const int c = id / (KPMAX / 2), p = id % (KPMAX / 2);
+    const int j0 = 2 * p, j1 = 2 * p + 1;
+    pf.v0[i] = (c < 8 && j0 < N) ? *reinterpret_cast<const u32x4*>(Vh + j0 * 64 + c * 8) : z;
+    pf.v1[i] = (c < 8 && j1 < N) ? *reinterpret_cast<const u32x4*>(Vh + j1 * 64 + c * 8) : z;
+  }
+}
+
+__device__ __forceinline__ void stage(const Prefetch& pf, char* sm, int tid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = tid + THREADS * i, row = id >> 3, c = id & 7;
+    if (row < NP) {
+      *lds<u32x4>(sm, OFF_Q + rc(row, c)) = pf.q[i];
+      *lds<u32x4>(sm, OFF_K + rc(row, c)) = pf.k[i];
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int id = tid + THREADS * i;
+    const int c = id / (KPMAX / 2), p = id % (KPMAX / 2);
+    if (c < 8) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t a = (pf.v0[i][t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
+        const uint32_t b = (pf.v1[i][t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
+        const uint32_t w = pack2(f16_bits(bf16_bits_to_f32(a)), f16_bits(bf16_bits_to_f32(b)));
+        *lds<uint32_t>(sm, OFF_VT + (8 * c + t) * VT_STRIDE + 4 * p) = w;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, Outputs o, int BH, int gh, int gw, int mh, int mw, int k) {
+  __shared__ __attribute__((aligned(16))) char sm[LDS_BYTES];
+  const int N = gh * gw, m = mh * mw;
+  const int nt = (N + 15) >> 4;
+  const int KP = (N + 31) & ~31;
+  const float tau = 0.125f;  // 1/sqrt(64)
+  const size_t head_elems = (size_t)N * 64;
+
+  Prefetch pf;
+  int bh = blockIdx.x;
+  if (bh < BH)
+    prefetch(pf, Q + bh * head_elems, K + bh * head_elems, V + bh * head_elems, N, threadIdx.x);
+
+  for (; bh < BH; bh += gridDim.x) {
+    // Thread coordinates are re-derived through an opaque zero every head so
+    // that the compiler recomputes per-thread LDS addresses inside each phase
+    // instead of hoisting them all out of the loop and pinning registers.
+    const int tid = threadIdx.x + opaque_zero(), lane = tid & 63, w = tid >> 6;
+    const int g = lane >> 4, c16 = lane & 15;
+    // ---------------- A: stage this head, prefetch the next one
+    __syncthreads();
+    stage(pf, sm, tid);
+    __syncthreads();
+    {
+      const int nx = bh + gridDim.x;
+      if (nx < BH)
+        prefetch(pf, Q + nx * head_elems, K + nx * head_elems, V + nx * head_elems, N, tid);
+    }
+
+    // ---------------- B: landmark pooling (one thread per landmark x 4 channels)
+    {
+      const int i = tid >> 4, q4 = tid & 15;  // 32 landmark slots x 16 channel quads
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+      if (i < m) {
+        const int r = i / mw, c = i % mw;
+        int y0, y1, x0, x1;
+        pool_window(r, gh, mh, &y0, &y1);
+        pool_window(c, gw, mw, &x0, &x1);
+        for (int y = y0; y < y1; ++y)
+          for (int x = x0; x < x1; ++x) {
+            const u32x2 v = *lds<u32x2>(sm, OFF_Q + rc(y * gw + x, q4 >> 1) + (q4 & 1) * 8);
+            a0 += bf16_bits_to_f32(v[0] & 0xFFFFu);
+            a1 += bf16_bits_to_f32(v[0] >> 16);
+            a2 += bf16_bits_to_f32(v[1] & 0xFFFFu);
+            a3 += bf16_bits_to_f32(v[1] >> 16);
+          }
+        const float cnt = (float)((y1 - y0) * (x1 - x0));
+        a0 /= cnt; a1 /= cnt; a2 /= cnt; a3 /= cnt;
+        if (o.ql) {
+          float4* dst = reinterpret_cast<float4*>(o.ql + ((size_t)bh * m + i) * 64 + 4 * q4);
+          *dst = make_float4(a0, a1, a2, a3);
+        }
+      }
+      const uint32_t h0 = bf16_rne_bits(a0), h1 = bf16_rne_bits(a1);
+      const uint32_t h2 = bf16_rne_bits(a2), h3 = bf16_rne_bits(a3);
+      const uint32_t l0 = bf16_rne_bits(a0 - bf16_bits_to_f32(h0));
+      const uint32_t l1 = bf16_rne_bits(a1 - bf16_bits_to_f32(h1));
+      const uint32_t l2 = bf16_rne_bits(a2 - bf16_bits_to_f32(h2));
+      const uint32_t l3 = bf16_rne_bits(a3 - bf16_bits_to_f32(h3));
+      const int off = rc(i, q4 >> 1) + (q4 & 1) * 8;
+      *lds<u32x2>(sm, OFF_QLH + off) = u32x2{h0 | (h1 << 16), h2 | (h3 << 16)};
+      *lds<u32x2>(sm, OFF_QLL + off) = u32x2{l0 | (l1 << 16), l2 | (l3 << 16)};
+    }
+    __syncthreads();
+
+    // ---------------- C: S^T = K Q_L^T (to LDS, row = landmark) and routes from R = Q Q_L^T
+    for (int job = w; job < 2 * nt; job += NWAVES) {
+      u32x4 qlh[2][2], qll[2][2];
+      load_ql(sm, qlh, qll, g, c16);
+      const int tt = job >> 1;
+      const bool isR = job & 1;
+      const int base = isR ? OFF_Q : OFF_K;
+      const u32x4 a0 = *lds<u32x4>(sm, base + rc(16 * tt + c16, g));
+      const u32x4 a1 = *lds<u32x4>(sm, base + rc(16 * tt + c16, 4 + g));
+      f32x4 acc[2];
+#pragma unroll
+      for (int lt = 0; lt < 2; ++lt) {
+        f32x4 c = zero4();
+        c = mfma_bf16(a0, qlh[lt][0], c);
+        c = mfma_bf16(a0, qll[lt][0], c);
+        c = mfma_bf16(a1, qlh[lt][1], c);
+        c = mfma_bf16(a1, qll[lt][1], c);
+        acc[lt] = c;
+      }
+      if (!isR) {
+#pragma unroll
+        for (int lt = 0; lt < 2; ++lt) {
+          float4 s = make_float4(acc[lt][0] * tau, acc[lt][1] * tau, acc[lt][2] * tau,
+                                 acc[lt][3] * tau);
+          *lds<float4>(sm, OFF_S + ((16 * lt + c16) * S_STRIDE + 16 * tt + 4 * g) * 4) = s;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float best = c16 < m ? acc[0][r] : -INFINITY;
+          int bi = c16;
+          const float v1 = (16 + c16) < m ? acc[1][r] : -INFINITY;
+          if (v1 > best) { best = v1; bi = 16 + c16; }
+#pragma unroll
+          for (int off = 8; off > 0; off >>= 1) {
+            const float ov = __shfl_xor(best, off, 64);
+            const int oi = __shfl_xor(bi, off, 64);
+            if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
+          }
+          const int tok = 16 * tt + 4 * g + r;
+          if (c16 == 0 && tok < N) {
+            *lds<int>(sm, OFF_ROUTE + tok * 4) = bi;
+            if (o.route) o.route[(size_t)bh * N + tok] = bi;
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---------------- D: exact top-k of each landmark row; then P = exp(S - max) in f16
+    {
+      const int i = 4 * w + g;           // landmark row of this 16-lane group
+      const bool active = i < m;
+      const int t = c16;
+      float v[MAXNT];
+      uint32_t cand = 0;
+#pragma unroll
+      for (int u = 0; u < MAXNT; ++u) {
+        const int j = t + 16 * u;
+        const bool ok = active && u < nt && j < N;
+        v[u] = ok ? *lds<float>(sm, OFF_S + (i * S_STRIDE + j) * 4) : -INFINITY;
+        cand |= (ok ? 1u : 0u) << u;
+      }
+      auto range = [&](uint32_t cm, float& lo, float& hi) {
+        float a = INFINITY, b = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < MAXNT; ++u)
+          if (cm >> u & 1u) { a = fminf(a, v[u]); b = fmaxf(b, v[u]); }
+        lo = g16_min(a);
+        hi = g16_max(b);
+      };
+      float lo, hi;
+      range(cand, lo, hi);
+      const float rmax = hi;
+      uint32_t take = 0;
+      int need = active ? k : 0;
+      bool done = !active;
+      const uint32_t below = (1u << t) - 1u;
+      char* hrow = sm + OFF_H + i * H_STRIDE;
+      for (int pass = 0; pass < 64; ++pass) {
+        const int cc = g16_sumi(__popc(cand));
+        if (!done) {
+          if (need == cc) {
+            take |= cand;
+            cand = 0;
+            done = true;
+          } else if (!(hi > lo)) {
+            // every candidate ties: keep the lowest key ids
+            int run = 0;
+#pragma unroll
+            for (int u = 0; u < MAXNT; ++u) {
+              const bool bit = cand >> u & 1u;
+              const uint32_t gm = g16_bits(__ballot(bit), g);
+              const int rank = run + __popc(gm & below);
+              if (bit && rank < need) take |= 1u << u;
+              run += __popc(gm);
+            }
+            cand = 0;
+            done = true;
+          }
+        }
+        if (__ballot(!done) == 0) break;
+        if (!done) {
+          const float scale = 256.0f / (hi - lo);
+          // clear this row's 256 packed 16-bit bins (128 dwords, 8 per lane)
+          *reinterpret_cast<u32x4*>(hrow + 32 * t) = u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(hrow + 32 * t + 16) = u32x4{0u, 0u, 0u, 0u};
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+#pragma unroll
+          for (int u = 0; u < MAXNT; ++u)
+            if (cand >> u & 1u) {
+              const int b = min(255, (int)((v[u] - lo) * scale));
+              atomicAdd(reinterpret_cast<uint32_t*>(hrow + (b >> 1) * 4), 1u << (16 * (b & 1)));
+            }
+          __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          const u32x4 d0 = *reinterpret_cast<const u32x4*>(hrow + 32 * t);
+          const u32x4 d1 = *reinterpret_cast<const u32x4*>(hrow + 32 * t + 16);
+          // bin 16t + q holds (q < 8 ? d0 : d1)[(q & 7) >> 1], half q & 1
+          auto cnt = [&](int q) -> int {
+            const uint32_t dw = (q < 8 ? d0 : d1)[(q & 7) >> 1];
+            return (q & 1) ? (int)(dw >> 16) : (int)(dw & 0xFFFFu);
+          };
+          int local = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            local += (int)((d0[q] & 0xFFFFu) + (d0[q] >> 16) + (d1[q] & 0xFFFFu) + (d1[q] >> 16));
+          // inclusive suffix sum over the group's lanes (higher lane = higher bins)
+          int suf = local;
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) {
+            const int x = __shfl_down(suf, off, 16);
+            suf += (t + off < 16) ? x : 0;
+          }
+          const int above = suf - local;
+          const bool mine = above < need && need <= suf;
+          int bstar = 0, abv = above, cst = 0;
+          if (mine) {
+            int acc = above;
+            bool found = false;
+#pragma unroll
+            for (int q = 15; q >= 0; --q) {
+              if (!found) {
+                const int cq = cnt(q);
+                if (acc + cq >= need) {
+                  found = true;
+                  bstar = 16 * t + q;
+                  abv = acc;
+                  cst = cq;
+                } else {
+                  acc += cq;
+                }
+              }
+            }
+          }
+          const uint32_t gm = g16_bits(__ballot(mine), g);
+          const int src = 16 * g + (gm ? __ffs(gm) - 1 : 0);
+          bstar = __shfl(bstar, src, 64);
+          abv = __shfl(abv, src, 64);
+          cst = __shfl(cst, src, 64);
+          uint32_t nc = 0;
+#pragma unroll
+          for (int u = 0; u < MAXNT; ++u)
+            if (cand >> u & 1u) {
+              const int b = min(255, (int)((v[u] - lo) * scale));
+              if (b > bstar) take |= 1u << u;
+              if (b == bstar) nc |= 1u << u;
+            }
+          need -= abv;
+          cand = nc;
+          (void)cst;
+        }
+        range(cand, lo, hi);
+      }
+      // the expert: kept key ids in ascending order
+      {
+        int run = 0;
+#pragma unroll
+        for (int u = 0; u < MAXNT; ++u) {
+          const bool bit = take >> u & 1u;
+          const uint32_t gm = g16_bits(__ballot(bit), g);
+          const int pos = run + __popc(gm & below);
+          if (bit) {
+            const int j = t + 16 * u;
+            *lds<int>(sm, OFF_IDX + (i * KMAX + pos) * 4) = j;
+            if (o.idx) o.idx[((size_t)bh * m + i) * k + pos] = j;
+          }
+          run += __popc(gm);
+        }
+      }
+      // P row (f16) over this row's bytes, and its sum
+      float sum = 0.f;
+      uint16_t* prow = reinterpret_cast<uint16_t*>(hrow);
+#pragma unroll
+      for (int u = 0; u < KPMAX / 16; ++u) {
+        const int j = t + 16 * u;
+        if (j < KP) {
+          uint32_t hb = 0;
+          if (active && u < MAXNT && j < N) {
+            hb = f16_bits(fast_exp(v[u < MAXNT ? u : 0] - rmax));
+            sum += f16_bits_to_f32(hb);
+          }
+          prow[j] = (uint16_t)hb;
+        }
+      }
+      sum = g16_sumf(sum);
+      if (t == 0) {
+        *lds<float>(sm, OFF_STAT + i * 4) = rmax;
+        *lds<float>(sm, OFF_STAT + (32 + i) * 4) = active ? sum : 1.0f;
+      }
+    }
+    __syncthreads();
+
+    // ---------------- E: V_L^T = V^T P^T (one 16-channel x 16-landmark tile per wave)
+    {
+      const int ct = w & 3, lt = w >> 2;
+      f32x4 acc = zero4();
+      for (int ks = 0; ks < KP / 32; ++ks) {
+        const u32x4 a = *lds<u32x4>(sm, OFF_VT + (16 * ct + c16) * VT_STRIDE + (32 * ks + 8 * g) * 2);
+        const u32x4 b = *lds<u32x4>(sm, OFF_H + (16 * lt + c16) * H_STRIDE + (32 * ks + 8 * g) * 2);
+        acc = mfma_f16(a, b, acc);
+      }
+      const int L = 16 * lt + c16;
+      const bool ok = L < m;
+      const float inv = ok ? 1.0f / *lds<float>(sm, OFF_STAT + (32 + L) * 4) : 0.f;
+      float vl4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        vl4[r] = ok ? acc[r] * inv : 0.f;
+        *lds<uint16_t>(sm, OFF_VLT + (16 * ct + 4 * g + r) * VLT_STRIDE + L * 2) =
+            (uint16_t)f16_bits(vl4[r]);
+      }
+      if (ok && o.vl) {
+        *reinterpret_cast<float4*>(o.vl + ((size_t)bh * m + L) * 64 + 16 * ct + 4 * g) =
+            make_float4(vl4[0], vl4[1], vl4[2], vl4[3]);
+      }
+    }
+
+    // ---------------- F: group queries by route (stable counting sort), tile list
+    const int nchunks = (N + 63) >> 6;
+    int myroute = -1, myrank = 0;
+    if (w < nchunks) {
+      const int n = 64 * w + lane;
+      myroute = n < N ? *lds<int>(sm, OFF_ROUTE + n * 4) : -1;
+      int mycnt = 0;
+      for (int e = 0; e < m; ++e) {
+        const uint64_t b = __ballot(myroute == e);
+        if (myroute == e) myrank = __popcll(b & ((1ull << lane) - 1ull));
+        if (lane == e) mycnt = __popcll(b);
+      }
+      if (lane < 32) *lds<int>(sm, OFF_CNT + (w * 32 + lane) * 4) = lane < m ? mycnt : 0;
+    }
+    __syncthreads();
+    if (w == 0) {
+      int tot = 0, pre[4] = {0, 0, 0, 0};
+      if (lane < 32) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          pre[c] = tot;
+          if (c < nchunks) tot += *lds<int>(sm, OFF_CNT + (c * 32 + lane) * 4);
+        }
+      }
+      // exclusive scans over the 32 expert lanes: query offsets and tile offsets
+      const int ntl = (tot + 15) >> 4;
+      int s1 = tot, s2 = ntl;
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) {
+        const int x1 = __shfl_up(s1, off, 64), x2 = __shfl_up(s2, off, 64);
+        if (lane >= off) { s1 += x1; s2 += x2; }
+      }
+      const int off_e = s1 - tot, toff = s2 - ntl;
+      if (lane < 32) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (c < nchunks) *lds<int>(sm, OFF_BASE + (c * 32 + lane) * 4) = off_e + pre[c];
+        if (lane < m) {
+          *lds<int>(sm, OFF_OFFS + lane * 4) = off_e;
+          for (int s = 0; s < ntl; ++s) {
+            int4* tl = lds<int4>(sm, OFF_TILES + (toff + s) * 16);
+            *tl = make_int4(lane, off_e + 16 * s, min(16, tot - 16 * s), 0);
+          }
+          if (o.counts) o.counts[(size_t)bh * m + lane] = tot;
+          if (o.offsets) o.offsets[(size_t)bh * (m + 1) + lane] = off_e;
+        }
+      }
+      const int ntiles = __shfl(s2, 31, 64);
+      if (lane == 0) {
+        *lds<int>(sm, OFF_STAT + 64 * 4) = ntiles;
+        if (o.offsets) o.offsets[(size_t)bh * (m + 1) + m] = N;
+      }
+    }
+    __syncthreads();
+    if (w < nchunks && myroute >= 0) {
+      const int pos = *lds<int>(sm, OFF_BASE + (w * 32 + myroute) * 4) + myrank;
+      *lds<int>(sm, OFF_PERM + pos * 4) = 64 * w + lane;
+      if (o.perm) o.perm[(size_t)bh * N + pos] = 64 * w + lane;
+    }
+    __syncthreads();
+
+    // ---------------- G: grouped expert attention, one <=16-query tile at a time
+    {
+      u32x4 avl[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int rowb = OFF_VLT + (16 * ct + c16) * VLT_STRIDE;
+        const u32x2 lo2 = *lds<u32x2>(sm, rowb + (4 * g) * 2);
+        const u32x2 hi2 = *lds<u32x2>(sm, rowb + (16 + 4 * g) * 2);
+        avl[ct] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+      }
+      const int ntiles = *lds<int>(sm, OFF_STAT + 64 * 4);
+      float* outh = o.out + (size_t)bh * N * 64;
+      for (int tile = w; tile < ntiles; tile += NWAVES) {
+        u32x4 qlh[2][2], qll[2][2];
+        load_ql(sm, qlh, qll, g, c16);
+        const int4 tl = *lds<int4>(sm, OFF_TILES + tile * 16);
+        const int e = tl.x, start = tl.y, len = tl.z;
+        const int qi = c16 < len ? *lds<int>(sm, OFF_PERM + (start + c16) * 4) : -1;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const u32x4 bq0 = qi >= 0 ? *lds<u32x4>(sm, OFF_Q + rc(qi, g)) : z;
+        const u32x4 bq1 = qi >= 0 ? *lds<u32x4>(sm, OFF_Q + rc(qi, 4 + g)) : z;
+        f32x4 ls[2], lr[2];
+#pragma unroll
+        for (int lt = 0; lt < 2; ++lt) {
+          f32x4 c = zero4();
+          c = mfma_bf16(qlh[lt][0], bq0, c);
+          c = mfma_bf16(qll[lt][0], bq0, c);
+          c = mfma_bf16(qlh[lt][1], bq1, c);
+          c = mfma_bf16(qll[lt][1], bq1, c);
+          ls[lt] = c;
+        }
+        const int* idxe = lds<int>(sm, OFF_IDX + e * KMAX * 4);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int slot = 16 * st + c16;
+          const int key = slot < k ? idxe[slot] : -1;
+          const u32x4 ak0 = key >= 0 ? *lds<u32x4>(sm, OFF_K + rc(key, g)) : z;
+          const u32x4 ak1 = key >= 0 ? *lds<u32x4>(sm, OFF_K + rc(key, 4 + g)) : z;
+          f32x4 c = zero4();
+          c = mfma_bf16(ak0, bq0, c);
+          c = mfma_bf16(ak1, bq1, c);
+          lr[st] = c;
+        }
+        // logits of this lane: shared entries 16lt+4g+r, routed slots 16st+4g+r, query c16
+        float mx = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int ent = 16 * h + 4 * g + r;
+            ls[h][r] = ent < m ? ls[h][r] * tau : -INFINITY;
+            lr[h][r] = ent < k ? lr[h][r] * tau : -INFINITY;
+            mx = fmaxf(mx, fmaxf(ls[h][r], lr[h][r]));
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        uint32_t ps[8], pr[8];
+        float sum = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            ps[4 * h + r] = f16_bits(fast_exp(ls[h][r] - mx));
+            pr[4 * h + r] = f16_bits(fast_exp(lr[h][r] - mx));
+            sum += f16_bits_to_f32(ps[4 * h + r]) + f16_bits_to_f32(pr[4 * h + r]);
+          }
+        sum += __shfl_xor(sum, 16, 64);
+        sum += __shfl_xor(sum, 32, 64);
+        const u32x4 bps = {pack2(ps[0], ps[1]), pack2(ps[2], ps[3]), pack2(ps[4], ps[5]),
+                           pack2(ps[6], ps[7])};
+        const u32x4 bpr = {pack2(pr[0], pr[1]), pack2(pr[2], pr[3]), pack2(pr[4], pr[5]),
+                           pack2(pr[6], pr[7])};
+        // this lane's routed slots {4g+r, 16+4g+r}: their key ids
+        int keys[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int slot = (q < 4 ? 0 : 16) + 4 * g + (q & 3);
+          keys[q] = slot < k ? idxe[slot] : -1;
+        }
+        const float inv = 1.0f / sum;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const uint16_t* vrow =
+              reinterpret_cast<const uint16_t*>(sm + OFF_VT + (16 * ct + c16) * VT_STRIDE);
+          uint32_t hv[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) hv[q] = keys[q] >= 0 ? vrow[keys[q]] : 0u;
+          const u32x4 ave = {pack2(hv[0], hv[1]), pack2(hv[2], hv[3]), pack2(hv[4], hv[5]),
+                             pack2(hv[6], hv[7])};
+          f32x4 acc = zero4();
+          acc = mfma_f16(avl[ct], bps, acc);
+          acc = mfma_f16(ave, bpr, acc);
+          if (qi >= 0)
+            *reinterpret_cast<float4*>(outh + (size_t)qi * 64 + 16 * ct + 4 * g) =
+                make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace fused
+
+bool fused_supported(const Shape& s) {
+  return s.bf16 && s.d == 64 && s.N <= fused::NP && s.m <= fused::MMAX && s.k <= fused::KMAX;
+}
+
+static int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+hipError_t launch_fused(const void* Q, const void* K, const void* V, float* out, int32_t* idx,
+                        int32_t* route, float* ql, float* vl, int32_t* counts, int32_t* offsets,
+                        int32_t* perm, const Shape& s, hipStream_t st) {
+  fused::Outputs o{out, idx, route, ql, vl, counts, offsets, perm};
+  const int grid = s.BH < device_cu_count() ? s.BH : device_cu_count();
+  fused::mita_fused_kernel<<<grid, fused::THREADS, 0, st>>>(
+      (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, o, s.BH, s.grid_h, s.grid_w,
+      s.m_h, s.m_w, s.k);
+  return hipGetLastError();
+}
+
+}  // namespace mita

@@ -33,4 +33,10 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V, const floa
                          const int32_t* offsets, const int32_t* perm, float* out,
                          const Shape& s, hipStream_t st);
 
+// whole pass for short grids in one persistent kernel
+bool fused_supported(const Shape& s);
+hipError_t launch_fused(const void* Q, const void* K, const void* V, float* out, int32_t* idx,
+                        int32_t* route, float* ql, float* vl, int32_t* counts, int32_t* offsets,
+                        int32_t* perm, const Shape& s, hipStream_t st);
+
 }  // namespace mita

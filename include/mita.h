@@ -79,6 +79,14 @@ size_t mita_workspace_bytes(int B, int H, int grid_h, int grid_w, int d,
                             int m_h, int m_w, int k, mita_dtype in_dtype);
 
 /*
+ * The schedule mita_forward runs for this shape with MITA_PATH_AUTO:
+ * MITA_PATH_FUSED (one persistent kernel per call; bf16, N <= 208, m <= 32,
+ * k <= 32) or MITA_PATH_STAGED (one kernel per step).  -1 for an invalid shape.
+ */
+int mita_schedule(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
+                  mita_dtype in_dtype);
+
+/*
  * The whole forward pass (all steps above) on `stream`.
  *   out   [B,H,N,d] fp32, required.
  *   idx   [B,H,m,k] int32 or NULL: each landmark's expert (ascending key ids).

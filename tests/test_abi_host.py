@@ -44,6 +44,17 @@ def test_workspace_bytes():
     assert ws(1, 1, 14, 14, 64, 15, 5, 25, mita.MITA_F32) == 0     # m_h > grid_h
 
 
+def test_schedule_choice():
+    sched = mita.mita_schedule
+    assert sched(256, 6, 14, 14, 64, 5, 5, 25, mita.MITA_BF16) == "fused"
+    assert sched(32, 6, 56, 56, 64, 7, 7, 64, mita.MITA_BF16) == "staged"
+    assert sched(1, 1, 14, 14, 64, 5, 5, 25, mita.MITA_F32) == "staged"
+    assert sched(1, 1, 13, 16, 64, 8, 4, 32, mita.MITA_BF16) == "fused"
+    assert sched(1, 1, 13, 16, 64, 8, 4, 33, mita.MITA_BF16) == "staged"
+    with pytest.raises(mita.MitaError):
+        sched(1, 1, 14, 14, 64, 5, 5, 0, mita.MITA_BF16)
+
+
 FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every case fails validation first
 
 

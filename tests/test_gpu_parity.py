@@ -73,6 +73,52 @@ def test_small_shapes(case):
     _say(f"ok {rep}")
 
 
+FUSED = [
+    # B, H, gh, gw, mh, mw, k: shapes the single-kernel schedule accepts
+    (2, 3, 14, 14, 5, 5, 25),   # DeiT shape
+    (2, 2, 13, 16, 8, 4, 32),   # largest N, m and k it takes
+    (1, 3, 4, 4, 1, 1, 16),     # m = 1, k = N
+    (1, 1, 5, 5, 5, 5, 25),     # m = N = k
+    (2, 1, 7, 9, 3, 3, 1),      # k = 1
+    (1, 1, 1, 1, 1, 1, 1),      # N = 1
+    (3, 2, 11, 6, 4, 3, 17),    # ragged tails everywhere
+]
+
+
+@pytest.mark.parametrize("path", ["fused", "staged"])
+@pytest.mark.parametrize("case", FUSED, ids=lambda c: "x".join(map(str, c)))
+def test_both_schedules(case, path):
+    B, H, gh, gw, mh, mw, k = case
+    _say(f"{path} schedule {case}")
+    Q, K, V = synth.make_qkv(B, H, gh, gw, 64, workload_id=300 + gh * 5 + gw + k)
+    res = run_gpu(Q, K, V, "bf16", gh, gw, mh, mw, k, path=path)
+    rep = parity.run_and_check(res, Q, K, V, gh, gw, mh, mw, k, TOL["bf16"])
+    _say(f"ok {rep}")
+
+
+@pytest.mark.parametrize("path", ["fused", "staged"])
+def test_exact_ties_take_lowest_index(path):
+    """Small-integer inputs with one landmark per token make every score and
+    route logit exact in fp32 and fp64, so exact ties are common and both
+    choices must equal the oracle's lowest-index picks bit for bit."""
+    import oracle.mita_oracle as O
+    B, H, gh, gw, k = 2, 2, 4, 8, 7
+    rng = np.random.default_rng(5)
+    Q, K, V = (rng.integers(-2, 3, size=(B, H, gh * gw, 64)).astype(np.float32) for _ in range(3))
+    _say(f"exact ties ({path})")
+    res = run_gpu(Q, K, V, "bf16", gh, gw, gh, gw, k, path=path)
+    ties = 0
+    for b in range(B):
+        for h in range(H):
+            ref = O.mita_head(Q[b, h], K[b, h], V[b, h], gh, gw, gh, gw, k)
+            ties += int(np.sum(ref["gap"] == 0)) + int(np.sum(ref["rgap"] == 0))
+            assert np.array_equal(res["idx"][b, h], ref["idx"]), (b, h)
+            assert np.array_equal(res["route"][b, h], ref["route"]), (b, h)
+    assert ties > 10, "the case must actually contain exact ties"
+    rep = parity.run_and_check(res, Q, K, V, gh, gw, gh, gw, k, TOL["bf16"])
+    _say(f"ok ties={ties} {rep}")
+
+
 @pytest.mark.parametrize("name", ["tiny-fp32", "deit-t", "deit-s", "hires-3136"])
 def test_workload_full(name):
     w = synth.workload(name)
