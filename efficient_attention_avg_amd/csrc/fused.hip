@@ -90,22 +90,72 @@ __device__ __forceinline__ P* lds(char* base, int off) {
   return reinterpret_cast<P*>(base + off);
 }
 
-// Values held by the 16-lane group of this lane (xor offsets < 16 stay inside).
+// Reductions and scans inside a 16-lane group with DPP (full-rate VALU, no
+// LDS round trip).  quad_perm [1,0,3,2] and [2,3,0,1] pair lanes at xor 1 and
+// xor 2; row_half_mirror (i <-> 7-i) then row_mirror (i <-> 15-i) combine the
+// quads and then the halves, so after four steps every lane holds the result.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
+}
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+constexpr int DPP_ROW_SHL1 = 0x101, DPP_ROW_SHL2 = 0x102, DPP_ROW_SHL4 = 0x104,
+              DPP_ROW_SHL8 = 0x108;
+
 __device__ __forceinline__ float g16_max(float v) {
-  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  v = fmaxf(v, dpp_f<DPP_XOR1>(v));
+  v = fmaxf(v, dpp_f<DPP_XOR2>(v));
+  v = fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp_f<DPP_MIRROR>(v));
   return v;
 }
 __device__ __forceinline__ float g16_min(float v) {
-  for (int o = 8; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
+  v = fminf(v, dpp_f<DPP_XOR1>(v));
+  v = fminf(v, dpp_f<DPP_XOR2>(v));
+  v = fminf(v, dpp_f<DPP_HALF_MIRROR>(v));
+  v = fminf(v, dpp_f<DPP_MIRROR>(v));
   return v;
 }
 __device__ __forceinline__ float g16_sumf(float v) {
-  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v += dpp_f<DPP_XOR1>(v);
+  v += dpp_f<DPP_XOR2>(v);
+  v += dpp_f<DPP_HALF_MIRROR>(v);
+  v += dpp_f<DPP_MIRROR>(v);
   return v;
 }
 __device__ __forceinline__ int g16_sumi(int v) {
-  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v += dpp_i<DPP_XOR1>(v);
+  v += dpp_i<DPP_XOR2>(v);
+  v += dpp_i<DPP_HALF_MIRROR>(v);
+  v += dpp_i<DPP_MIRROR>(v);
   return v;
+}
+// Inclusive suffix sum over a 16-lane group: lane t gets sum over t' >= t
+// (row_shl:n hands lane t the value of lane t+n, zero past the row end).
+__device__ __forceinline__ int g16_suffix_sum(int v) {
+  v += dpp_i<DPP_ROW_SHL1>(v);
+  v += dpp_i<DPP_ROW_SHL2>(v);
+  v += dpp_i<DPP_ROW_SHL4>(v);
+  v += dpp_i<DPP_ROW_SHL8>(v);
+  return v;
+}
+// (value, index) argmax over a 16-lane group, ties to the lower index.
+__device__ __forceinline__ void g16_argmax(float& v, int& i) {
+#define MITA_ARGMAX_STEP(CTRL)                                         \
+  {                                                                    \
+    const float ov = dpp_f<CTRL>(v);                                   \
+    const int oi = dpp_i<CTRL>(i);                                     \
+    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }            \
+  }
+  MITA_ARGMAX_STEP(DPP_XOR1)
+  MITA_ARGMAX_STEP(DPP_XOR2)
+  MITA_ARGMAX_STEP(DPP_HALF_MIRROR)
+  MITA_ARGMAX_STEP(DPP_MIRROR)
+#undef MITA_ARGMAX_STEP
 }
 // This lane's 16-lane group's bits of a wave ballot.
 __device__ __forceinline__ uint32_t g16_bits(uint64_t ballot, int g) {
@@ -183,6 +233,7 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
   const int nt = (N + 15) >> 4;
   const int KP = (N + 31) & ~31;
   const float tau = 0.125f;  // 1/sqrt(64)
+  const float kLogitScale = tau * 1.4426950408889634f;  // tau * log2(e): base-2 softmax
   const size_t head_elems = (size_t)N * 64;
 
   Prefetch pf;
@@ -215,14 +266,24 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
         int y0, y1, x0, x1;
         pool_window(r, gh, mh, &y0, &y1);
         pool_window(c, gw, mw, &x0, &x1);
-        for (int y = y0; y < y1; ++y)
-          for (int x = x0; x < x1; ++x) {
-            const u32x2 v = *lds<u32x2>(sm, OFF_Q + rc(y * gw + x, q4 >> 1) + (q4 & 1) * 8);
-            a0 += bf16_bits_to_f32(v[0] & 0xFFFFu);
-            a1 += bf16_bits_to_f32(v[0] >> 16);
-            a2 += bf16_bits_to_f32(v[1] & 0xFFFFu);
-            a3 += bf16_bits_to_f32(v[1] >> 16);
+        const int co = (q4 & 1) * 8;
+        for (int y = y0; y < y1; ++y) {
+          // issue up to four row reads before consuming any (LDS latency)
+          for (int x = x0; x < x1; x += 4) {
+            u32x2 v[4];
+#pragma unroll
+            for (int dx = 0; dx < 4; ++dx)
+              v[dx] = x + dx < x1 ? *lds<u32x2>(sm, OFF_Q + rc(y * gw + x + dx, q4 >> 1) + co)
+                                  : u32x2{0u, 0u};
+#pragma unroll
+            for (int dx = 0; dx < 4; ++dx) {
+              a0 += bf16_bits_to_f32(v[dx][0] & 0xFFFFu);
+              a1 += bf16_bits_to_f32(v[dx][0] >> 16);
+              a2 += bf16_bits_to_f32(v[dx][1] & 0xFFFFu);
+              a3 += bf16_bits_to_f32(v[dx][1] >> 16);
+            }
           }
+        }
         const float cnt = (float)((y1 - y0) * (x1 - x0));
         a0 /= cnt; a1 /= cnt; a2 /= cnt; a3 /= cnt;
         if (o.ql) {
@@ -242,16 +303,12 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
     }
     __syncthreads();
 
-    // ---------------- C: S^T = K Q_L^T (to LDS, row = landmark) and routes from R = Q Q_L^T
-    for (int job = w; job < 2 * nt; job += NWAVES) {
+    // ---------------- C: S^T = K Q_L^T, written to LDS row = landmark
+    for (int tt = w; tt < nt; tt += NWAVES) {
       u32x4 qlh[2][2], qll[2][2];
       load_ql(sm, qlh, qll, g, c16);
-      const int tt = job >> 1;
-      const bool isR = job & 1;
-      const int base = isR ? OFF_Q : OFF_K;
-      const u32x4 a0 = *lds<u32x4>(sm, base + rc(16 * tt + c16, g));
-      const u32x4 a1 = *lds<u32x4>(sm, base + rc(16 * tt + c16, 4 + g));
-      f32x4 acc[2];
+      const u32x4 a0 = *lds<u32x4>(sm, OFF_K + rc(16 * tt + c16, g));
+      const u32x4 a1 = *lds<u32x4>(sm, OFF_K + rc(16 * tt + c16, 4 + g));
 #pragma unroll
       for (int lt = 0; lt < 2; ++lt) {
         f32x4 c = zero4();
@@ -259,34 +316,9 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
         c = mfma_bf16(a0, qll[lt][0], c);
         c = mfma_bf16(a1, qlh[lt][1], c);
         c = mfma_bf16(a1, qll[lt][1], c);
-        acc[lt] = c;
-      }
-      if (!isR) {
-#pragma unroll
-        for (int lt = 0; lt < 2; ++lt) {
-          float4 s = make_float4(acc[lt][0] * tau, acc[lt][1] * tau, acc[lt][2] * tau,
-                                 acc[lt][3] * tau);
-          *lds<float4>(sm, OFF_S + ((16 * lt + c16) * S_STRIDE + 16 * tt + 4 * g) * 4) = s;
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float best = c16 < m ? acc[0][r] : -INFINITY;
-          int bi = c16;
-          const float v1 = (16 + c16) < m ? acc[1][r] : -INFINITY;
-          if (v1 > best) { best = v1; bi = 16 + c16; }
-#pragma unroll
-          for (int off = 8; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(best, off, 64);
-            const int oi = __shfl_xor(bi, off, 64);
-            if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
-          }
-          const int tok = 16 * tt + 4 * g + r;
-          if (c16 == 0 && tok < N) {
-            *lds<int>(sm, OFF_ROUTE + tok * 4) = bi;
-            if (o.route) o.route[(size_t)bh * N + tok] = bi;
-          }
-        }
+        // lane holds S^T[key 16tt + 4g + r][landmark 16lt + c16]
+        *lds<float4>(sm, OFF_S + ((16 * lt + c16) * S_STRIDE + 16 * tt + 4 * g) * 4) =
+            make_float4(c[0] * tau, c[1] * tau, c[2] * tau, c[3] * tau);
       }
     }
     __syncthreads();
@@ -371,15 +403,10 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
           for (int q = 0; q < 4; ++q)
             local += (int)((d0[q] & 0xFFFFu) + (d0[q] >> 16) + (d1[q] & 0xFFFFu) + (d1[q] >> 16));
           // inclusive suffix sum over the group's lanes (higher lane = higher bins)
-          int suf = local;
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) {
-            const int x = __shfl_down(suf, off, 16);
-            suf += (t + off < 16) ? x : 0;
-          }
+          const int suf = g16_suffix_sum(local);
           const int above = suf - local;
           const bool mine = above < need && need <= suf;
-          int bstar = 0, abv = above, cst = 0;
+          int bstar = 0, abv = above;
           if (mine) {
             int acc = above;
             bool found = false;
@@ -391,18 +418,15 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
                   found = true;
                   bstar = 16 * t + q;
                   abv = acc;
-                  cst = cq;
                 } else {
                   acc += cq;
                 }
               }
             }
           }
-          const uint32_t gm = g16_bits(__ballot(mine), g);
-          const int src = 16 * g + (gm ? __ffs(gm) - 1 : 0);
-          bstar = __shfl(bstar, src, 64);
-          abv = __shfl(abv, src, 64);
-          cst = __shfl(cst, src, 64);
+          // exactly one lane of the group is `mine`: a masked group sum broadcasts
+          bstar = g16_sumi(mine ? bstar : 0);
+          abv = g16_sumi(mine ? abv : 0);
           uint32_t nc = 0;
 #pragma unroll
           for (int u = 0; u < MAXNT; ++u)
@@ -413,7 +437,6 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
             }
           need -= abv;
           cand = nc;
-          (void)cst;
         }
         range(cand, lo, hi);
       }
@@ -481,6 +504,59 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
       }
     }
 
+    // ---------------- E': R^T = Q_L Q^T per token tile: routes, and the shared
+    // expert's logits (the same query-landmark scores, scaled by tau*log2 e for
+    // a base-2 softmax) into the score region, which is free after D.
+    {
+      u32x4 qlh[2][2], qll[2][2];
+      load_ql(sm, qlh, qll, g, c16);
+      for (int tt = w; tt < nt; tt += NWAVES) {
+        const int tok = 16 * tt + c16;
+        const u32x4 b0 = *lds<u32x4>(sm, OFF_Q + rc(tok, g));
+        const u32x4 b1 = *lds<u32x4>(sm, OFF_Q + rc(tok, 4 + g));
+        f32x4 acc[2];
+#pragma unroll
+        for (int lt = 0; lt < 2; ++lt) {
+          f32x4 c = zero4();
+          c = mfma_bf16(qlh[lt][0], b0, c);
+          c = mfma_bf16(qll[lt][0], b0, c);
+          c = mfma_bf16(qlh[lt][1], b1, c);
+          c = mfma_bf16(qll[lt][1], b1, c);
+          acc[lt] = c;  // lane holds R[token tok][landmark 16lt + 4g + r]
+        }
+        float best = -INFINITY;
+        int bi = 0;
+#pragma unroll
+        for (int lt = 0; lt < 2; ++lt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int L = 16 * lt + 4 * g + r;  // increasing: strict '>' keeps the lowest
+            const float v = L < m ? acc[lt][r] : -INFINITY;
+            if (v > best) { best = v; bi = L; }
+          }
+#pragma unroll
+        for (int off = 16; off <= 32; off <<= 1) {
+          const float ov = __shfl_xor(best, off, 64);
+          const int oi = __shfl_xor(bi, off, 64);
+          if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
+        }
+        if (g == 0 && tok < N) {
+          *lds<int>(sm, OFF_ROUTE + tok * 4) = bi;
+          if (o.route) o.route[(size_t)bh * N + tok] = bi;
+        }
+#pragma unroll
+        for (int lt = 0; lt < 2; ++lt) {
+          float4 lg;
+          lg.x = 16 * lt + 4 * g + 0 < m ? acc[lt][0] * kLogitScale : -INFINITY;
+          lg.y = 16 * lt + 4 * g + 1 < m ? acc[lt][1] * kLogitScale : -INFINITY;
+          lg.z = 16 * lt + 4 * g + 2 < m ? acc[lt][2] * kLogitScale : -INFINITY;
+          lg.w = 16 * lt + 4 * g + 3 < m ? acc[lt][3] * kLogitScale : -INFINITY;
+          *lds<float4>(sm, OFF_S + rc(tok, 4 * lt + g)) = lg;
+        }
+      }
+    }
+    __syncthreads();
+
     // ---------------- F: group queries by route (stable counting sort), tile list
     const int nchunks = (N + 63) >> 6;
     int myroute = -1, myrank = 0;
@@ -544,6 +620,8 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
 
     // ---------------- G: grouped expert attention, one <=16-query tile at a time
     {
+      // V_L^T fragments, the A operand of the shared half of every tile: lane
+      // holds V_L^T[ch 16ct + c16][landmarks 4g..4g+3, 16+4g..16+4g+3]
       u32x4 avl[4];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
@@ -555,86 +633,79 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
       const int ntiles = *lds<int>(sm, OFF_STAT + 64 * 4);
       float* outh = o.out + (size_t)bh * N * 64;
       for (int tile = w; tile < ntiles; tile += NWAVES) {
-        u32x4 qlh[2][2], qll[2][2];
-        load_ql(sm, qlh, qll, g, c16);
         const int4 tl = *lds<int4>(sm, OFF_TILES + tile * 16);
         const int e = tl.x, start = tl.y, len = tl.z;
-        const int qi = c16 < len ? *lds<int>(sm, OFF_PERM + (start + c16) * 4) : -1;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        const u32x4 bq0 = qi >= 0 ? *lds<u32x4>(sm, OFF_Q + rc(qi, g)) : z;
-        const u32x4 bq1 = qi >= 0 ? *lds<u32x4>(sm, OFF_Q + rc(qi, 4 + g)) : z;
-        f32x4 ls[2], lr[2];
-#pragma unroll
-        for (int lt = 0; lt < 2; ++lt) {
-          f32x4 c = zero4();
-          c = mfma_bf16(qlh[lt][0], bq0, c);
-          c = mfma_bf16(qll[lt][0], bq0, c);
-          c = mfma_bf16(qlh[lt][1], bq1, c);
-          c = mfma_bf16(qll[lt][1], bq1, c);
-          ls[lt] = c;
-        }
+        // lane column c16 is query qi of the tile; columns past len compute on
+        // query 0 and are never stored
+        const bool live = c16 < len;
+        const int qi = live ? *lds<int>(sm, OFF_PERM + (start + c16) * 4) : 0;
+        const u32x4 bq0 = *lds<u32x4>(sm, OFF_Q + rc(qi, g));
+        const u32x4 bq1 = *lds<u32x4>(sm, OFF_Q + rc(qi, 4 + g));
+        // shared logits (base 2, -inf past m), from the route step
+        const f32x4 ls0 = *lds<f32x4>(sm, OFF_S + rc(qi, g));
+        const f32x4 ls1 = *lds<f32x4>(sm, OFF_S + rc(qi, 4 + g));
+        // routed logits^T = K_e Q_g^T; slot rows past k are zero and masked below
         const int* idxe = lds<int>(sm, OFF_IDX + e * KMAX * 4);
+        f32x4 lr[2];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           const int slot = 16 * st + c16;
-          const int key = slot < k ? idxe[slot] : -1;
-          const u32x4 ak0 = key >= 0 ? *lds<u32x4>(sm, OFF_K + rc(key, g)) : z;
-          const u32x4 ak1 = key >= 0 ? *lds<u32x4>(sm, OFF_K + rc(key, 4 + g)) : z;
+          const int key = slot < k ? idxe[slot] : 0;
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          const u32x4 ak0 = slot < k ? *lds<u32x4>(sm, OFF_K + rc(key, g)) : z;
+          const u32x4 ak1 = slot < k ? *lds<u32x4>(sm, OFF_K + rc(key, 4 + g)) : z;
           f32x4 c = zero4();
           c = mfma_bf16(ak0, bq0, c);
           c = mfma_bf16(ak1, bq1, c);
           lr[st] = c;
         }
-        // logits of this lane: shared entries 16lt+4g+r, routed slots 16st+4g+r, query c16
-        float mx = -INFINITY;
+        float x[16];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int r = 0; r < 4; ++r) {
+          x[r] = ls0[r];
+          x[4 + r] = ls1[r];
+          x[8 + r] = 4 * g + r < k ? lr[0][r] * kLogitScale : -INFINITY;
+          x[12 + r] = 16 + 4 * g + r < k ? lr[1][r] * kLogitScale : -INFINITY;
+        }
+        float mx = x[0];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int ent = 16 * h + 4 * g + r;
-            ls[h][r] = ent < m ? ls[h][r] * tau : -INFINITY;
-            lr[h][r] = ent < k ? lr[h][r] * tau : -INFINITY;
-            mx = fmaxf(mx, fmaxf(ls[h][r], lr[h][r]));
-          }
+        for (int q = 1; q < 16; ++q) mx = fmaxf(mx, x[q]);
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        uint32_t ps[8], pr[8];
-        float sum = 0.f;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int q = 0; q < 16; ++q) x[q] = __builtin_amdgcn_exp2f(x[q] - mx);
+        // P^T as the B operand: entries {4g+r, 16+4g+r} of each half, query c16
+        u32x4 bps, bpr;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            ps[4 * h + r] = f16_bits(fast_exp(ls[h][r] - mx));
-            pr[4 * h + r] = f16_bits(fast_exp(lr[h][r] - mx));
-            sum += f16_bits_to_f32(ps[4 * h + r]) + f16_bits_to_f32(pr[4 * h + r]);
-          }
-        sum += __shfl_xor(sum, 16, 64);
-        sum += __shfl_xor(sum, 32, 64);
-        const u32x4 bps = {pack2(ps[0], ps[1]), pack2(ps[2], ps[3]), pack2(ps[4], ps[5]),
-                           pack2(ps[6], ps[7])};
-        const u32x4 bpr = {pack2(pr[0], pr[1]), pack2(pr[2], pr[3]), pack2(pr[4], pr[5]),
-                           pack2(pr[6], pr[7])};
-        // this lane's routed slots {4g+r, 16+4g+r}: their key ids
+        for (int q = 0; q < 4; ++q) {
+          bps[q] = pk_f16(x[2 * q], x[2 * q + 1]);
+          bpr[q] = pk_f16(x[8 + 2 * q], x[8 + 2 * q + 1]);
+        }
+        // softmax normaliser of the same f16 weights the products use: an
+        // all-ones A operand sums every entry column into each output row
+        const u32x4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+        f32x4 tot = mfma_f16(ones, bps, zero4());
+        tot = mfma_f16(ones, bpr, tot);
+        const float inv = 1.0f / tot[0];
+        // key ids of this lane's routed slots {4g..4g+3, 16+4g..16+4g+3}
+        const i32x4 kv0 = *lds<i32x4>(sm, OFF_IDX + (e * KMAX + 4 * g) * 4);
+        const i32x4 kv1 = *lds<i32x4>(sm, OFF_IDX + (e * KMAX + 16 + 4 * g) * 4);
         int keys[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int slot = (q < 4 ? 0 : 16) + 4 * g + (q & 3);
-          keys[q] = slot < k ? idxe[slot] : -1;
+        for (int r = 0; r < 4; ++r) {
+          keys[r] = 4 * g + r < k ? kv0[r] : 0;
+          keys[4 + r] = 16 + 4 * g + r < k ? kv1[r] : 0;
         }
-        const float inv = 1.0f / sum;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
           const uint16_t* vrow =
               reinterpret_cast<const uint16_t*>(sm + OFF_VT + (16 * ct + c16) * VT_STRIDE);
-          uint32_t hv[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) hv[q] = keys[q] >= 0 ? vrow[keys[q]] : 0u;
-          const u32x4 ave = {pack2(hv[0], hv[1]), pack2(hv[2], hv[3]), pack2(hv[4], hv[5]),
-                             pack2(hv[6], hv[7])};
+          const u32x4 ave = {pack2(vrow[keys[0]], vrow[keys[1]]), pack2(vrow[keys[2]], vrow[keys[3]]),
+                             pack2(vrow[keys[4]], vrow[keys[5]]), pack2(vrow[keys[6]], vrow[keys[7]])};
           f32x4 acc = zero4();
           acc = mfma_f16(avl[ct], bps, acc);
           acc = mfma_f16(ave, bpr, acc);
-          if (qi >= 0)
+          if (live)
             *reinterpret_cast<float4*>(outh + (size_t)qi * 64 + 16 * ct + 4 * g) =
                 make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
         }

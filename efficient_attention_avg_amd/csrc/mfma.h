@@ -18,6 +18,8 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -47,6 +49,12 @@ __device__ __forceinline__ uint32_t f16_bits(float x) {
 
 __device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+}
+
+// Two fp32 -> packed f16x2 (round to nearest even, one v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+  const f16x2_t h = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, h);
 }
 
 // Pack two f16 bit patterns into one dword (lo in bits 0..15).
