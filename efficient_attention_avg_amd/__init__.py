@@ -25,7 +25,7 @@ EXPORTS = [
     "mita_status_string", "mita_last_error", "mita_version", "mita_workspace_bytes",
     "mita_schedule",
     "mita_forward", "mita_forward_ex", "mita_pool", "mita_landmark_workspace_bytes",
-    "mita_landmark", "mita_route", "mita_attend",
+    "mita_landmark", "mita_route_workspace_bytes", "mita_route", "mita_attend",
 ]
 
 
@@ -73,8 +73,10 @@ def lib() -> ctypes.CDLL:
         L.mita_landmark_workspace_bytes.argtypes = [I] * 6 + [I]
         L.mita_landmark.restype = S
         L.mita_landmark.argtypes = [P, P, P] + [I] * 6 + [I, P, P, P, Z, P]
+        L.mita_route_workspace_bytes.restype = Z
+        L.mita_route_workspace_bytes.argtypes = [I] * 5 + [I]
         L.mita_route.restype = S
-        L.mita_route.argtypes = [P, P] + [I] * 5 + [I, P, P, P, P, P]
+        L.mita_route.argtypes = [P, P] + [I] * 5 + [I, P, P, P, P, P, Z, P]
         L.mita_attend.restype = S
         L.mita_attend.argtypes = [P] * 9 + [I] * 6 + [I, P, P]
         _lib = L
@@ -231,8 +233,11 @@ def mita_route(q, ql, *, stream=None):
     counts = torch.empty((B, H, m), **i32)
     offsets = torch.empty((B, H, m + 1), **i32)
     perm = torch.empty((B, H, N), **i32)
+    nbytes = int(lib().mita_route_workspace_bytes(B, H, N, d, m, _dtype_code(q)))
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     _check(lib().mita_route(_ptr(q), _ptr(ql), B, H, N, d, m, _dtype_code(q), _ptr(route),
-                            _ptr(counts), _ptr(offsets), _ptr(perm), _stream(q, stream)))
+                            _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(ws), ws.numel(),
+                            _stream(q, stream)))
     return route, counts, offsets, perm
 
 

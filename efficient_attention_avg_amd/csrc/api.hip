@@ -64,10 +64,58 @@ mita_status make_shape(int B, int H, int grid_h, int grid_w, int d, int m_h, int
   return MITA_OK;
 }
 
+// Which kernels each staged step uses: the MFMA kernels for bf16 inputs
+// within their limits, the scalar kernels otherwise (fp32 inputs).
+bool pool_mfma(const Shape& s) { return s.bf16 && s.grid_w <= 256; }
+bool landmark_mfma(const Shape& s) { return mita::landmark_bf16_supported(s); }
+bool route_mfma(const Shape& s) { return mita::route_bf16_supported(s); }
+bool attend_mfma(const Shape& s) { return mita::attend_bf16_supported(s); }
+
+size_t landmark_scratch(const Shape& s) {
+  return landmark_mfma(s) ? mita::landmark_minmax_bytes(s) : mita::landmark_scratch_bytes(s);
+}
+size_t route_scratch(const Shape& s) { return route_mfma(s) ? mita::route_chist_bytes(s) : 0; }
+
+mita_status run_pool(const void* Q, float* ql, const Shape& s, hipStream_t st) {
+  return hip_status(pool_mfma(s) ? mita::launch_pool_bf16(Q, ql, s, st)
+                                 : mita::launch_pool(Q, ql, s, st),
+                    "pool launch");
+}
+mita_status run_landmark(const float* ql, const void* K, const void* V, int32_t* idx, float* vl,
+                         void* scratch, const Shape& s, hipStream_t st) {
+  return hip_status(landmark_mfma(s) ? mita::launch_landmark_bf16(ql, K, V, idx, vl,
+                                                                  (float*)scratch, s, st)
+                                     : mita::launch_landmark(ql, K, V, idx, vl, scratch, s, st),
+                    "landmark launch");
+}
+mita_status run_route(const void* Q, const float* ql, int32_t* route, int32_t* counts,
+                      int32_t* offsets, int32_t* perm, void* scratch, const Shape& s,
+                      hipStream_t st) {
+  if (!route_mfma(s))
+    return hip_status(mita::launch_route(Q, ql, route, counts, offsets, perm, s, st),
+                      "route launch");
+  mita_status r = hip_status(mita::launch_route_bf16(Q, ql, route, (int32_t*)scratch, s, st),
+                             "route launch");
+  if (r != MITA_OK) return r;
+  return hip_status(mita::launch_group_bf16(route, (const int32_t*)scratch, counts, offsets, perm,
+                                            s, st),
+                    "group launch");
+}
+mita_status run_attend(const void* Q, const void* K, const void* V, const float* ql,
+                       const float* vl, const int32_t* idx, const int32_t* route,
+                       const int32_t* offsets, const int32_t* perm, float* out, const Shape& s,
+                       hipStream_t st) {
+  return hip_status(
+      attend_mfma(s)
+          ? mita::launch_attend_bf16(Q, K, V, ql, vl, idx, offsets, perm, out, s, st)
+          : mita::launch_attend(Q, K, V, ql, vl, idx, route, offsets, perm, out, s, st),
+      "attend launch");
+}
+
 // Workspace of the staged schedule: every intermediate the caller did not
-// supply, then the landmark pass's scratch.
+// supply, then the landmark and route steps' scratch.
 struct Layout {
-  size_t ql, vl, idx, route, counts, offsets, perm, scratch, total;
+  size_t ql, vl, idx, route, counts, offsets, perm, scratch, rscratch, total;
 };
 
 Layout layout_of(const Shape& s) {
@@ -81,7 +129,8 @@ Layout layout_of(const Shape& s) {
   L.counts = take((size_t)s.BH * s.m * 4);
   L.offsets = take((size_t)s.BH * (s.m + 1) * 4);
   L.perm = take((size_t)s.BH * s.N * 4);
-  L.scratch = take(mita::landmark_scratch_bytes(s));
+  L.scratch = take(landmark_scratch(s));
+  L.rscratch = take(route_scratch(s));
   L.total = off;
   return L;
 }
@@ -108,7 +157,7 @@ const char* mita_status_string(mita_status s) {
 
 const char* mita_last_error(void) { return g_error.c_str(); }
 
-const char* mita_version(void) { return "mita-gfx950 0.1"; }
+const char* mita_version(void) { return "mita-gfx950 0.2"; }
 
 size_t mita_workspace_bytes(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
                             mita_dtype in_dtype) {
@@ -163,17 +212,13 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V, int B, 
   int32_t* idx_p = pick(idx, workspace, L.idx);
   int32_t* route_p = pick(route, workspace, L.route);
   void* scratch = (char*)workspace + L.scratch;
+  void* rscratch = (char*)workspace + L.rscratch;
 
-  if ((st = hip_status(mita::launch_pool(Q, ql, s, stream), "pool launch")) != MITA_OK) return st;
-  if ((st = hip_status(mita::launch_landmark(ql, K, V, idx_p, vl, scratch, s, stream),
-                       "landmark launch")) != MITA_OK)
+  if ((st = run_pool(Q, ql, s, stream)) != MITA_OK) return st;
+  if ((st = run_landmark(ql, K, V, idx_p, vl, scratch, s, stream)) != MITA_OK) return st;
+  if ((st = run_route(Q, ql, route_p, counts, offsets, perm, rscratch, s, stream)) != MITA_OK)
     return st;
-  if ((st = hip_status(mita::launch_route(Q, ql, route_p, counts, offsets, perm, s, stream),
-                       "route launch")) != MITA_OK)
-    return st;
-  if ((st = hip_status(mita::launch_attend(Q, K, V, ql, vl, idx_p, route_p, offsets, perm, out, s,
-                                           stream),
-                       "attend launch")) != MITA_OK)
+  if ((st = run_attend(Q, K, V, ql, vl, idx_p, route_p, offsets, perm, out, s, stream)) != MITA_OK)
     return st;
   return ok();
 }
@@ -192,7 +237,7 @@ mita_status mita_pool(const void* Q, int B, int H, int grid_h, int grid_w, int d
   mita_status st = make_shape(B, H, grid_h, grid_w, d, m_h, m_w, 1, in_dtype, &s);
   if (st != MITA_OK) return st;
   if (!Q || !ql) return fail(MITA_ERR_INVALID_ARG, "Q and ql are required");
-  if ((st = hip_status(mita::launch_pool(Q, ql, s, stream), "pool launch")) != MITA_OK) return st;
+  if ((st = run_pool(Q, ql, s, stream)) != MITA_OK) return st;
   return ok();
 }
 
@@ -200,7 +245,7 @@ size_t mita_landmark_workspace_bytes(int B, int H, int N, int d, int m, int k,
                                      mita_dtype in_dtype) {
   Shape s;
   if (make_shape(B, H, N, 1, d, m, 1, k, in_dtype, &s) != MITA_OK) return 0;
-  return mita::landmark_scratch_bytes(s);
+  return landmark_scratch(s);
 }
 
 mita_status mita_landmark(const float* ql, const void* K, const void* V, int B, int H, int N, int d,
@@ -211,26 +256,34 @@ mita_status mita_landmark(const float* ql, const void* K, const void* V, int B, 
   if (st != MITA_OK) return st;
   if (!ql || !K || !V || !idx || !vl)
     return fail(MITA_ERR_INVALID_ARG, "ql, K, V, idx and vl are required");
-  const size_t need = mita::landmark_scratch_bytes(s);
+  const size_t need = landmark_scratch(s);
   if (need && !workspace) return fail(MITA_ERR_INVALID_ARG, "workspace is required");
   if (workspace_bytes < need)
     return fail(MITA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
-  if ((st = hip_status(mita::launch_landmark(ql, K, V, idx, vl, workspace, s, stream),
-                       "landmark launch")) != MITA_OK)
-    return st;
+  if ((st = run_landmark(ql, K, V, idx, vl, workspace, s, stream)) != MITA_OK) return st;
   return ok();
+}
+
+size_t mita_route_workspace_bytes(int B, int H, int N, int d, int m, mita_dtype in_dtype) {
+  Shape s;
+  if (make_shape(B, H, N, 1, d, m, 1, 1, in_dtype, &s) != MITA_OK) return 0;
+  return route_scratch(s);
 }
 
 mita_status mita_route(const void* Q, const float* ql, int B, int H, int N, int d, int m,
                        mita_dtype in_dtype, int32_t* route, int32_t* counts, int32_t* offsets,
-                       int32_t* perm, hipStream_t stream) {
+                       int32_t* perm, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
   Shape s;
   mita_status st = make_shape(B, H, N, 1, d, m, 1, 1, in_dtype, &s);
   if (st != MITA_OK) return st;
   if (!Q || !ql || !route || !counts || !offsets || !perm)
     return fail(MITA_ERR_INVALID_ARG, "Q, ql, route, counts, offsets and perm are required");
-  if ((st = hip_status(mita::launch_route(Q, ql, route, counts, offsets, perm, s, stream),
-                       "route launch")) != MITA_OK)
+  const size_t need = route_scratch(s);
+  if (need && !workspace) return fail(MITA_ERR_INVALID_ARG, "workspace is required");
+  if (workspace_bytes < need)
+    return fail(MITA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+  if ((st = run_route(Q, ql, route, counts, offsets, perm, workspace, s, stream)) != MITA_OK)
     return st;
   return ok();
 }
@@ -244,9 +297,7 @@ mita_status mita_attend(const void* Q, const void* K, const void* V, const float
   if (st != MITA_OK) return st;
   if (!Q || !K || !V || !ql || !vl || !idx || !route || !offsets || !perm || !out)
     return fail(MITA_ERR_INVALID_ARG, "every tensor argument of mita_attend is required");
-  if ((st = hip_status(mita::launch_attend(Q, K, V, ql, vl, idx, route, offsets, perm, out, s,
-                                           stream),
-                       "attend launch")) != MITA_OK)
+  if ((st = run_attend(Q, K, V, ql, vl, idx, route, offsets, perm, out, s, stream)) != MITA_OK)
     return st;
   return ok();
 }

@@ -33,6 +33,23 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V, const floa
                          const int32_t* offsets, const int32_t* perm, float* out,
                          const Shape& s, hipStream_t st);
 
+// bf16 kernels for long grids (MFMA, LDS-staged)
+hipError_t launch_pool_bf16(const void* Q, float* ql, const Shape& s, hipStream_t st);
+bool landmark_bf16_supported(const Shape& s);
+size_t landmark_minmax_bytes(const Shape& s);
+hipError_t launch_landmark_bf16(const float* ql, const void* K, const void* V, int32_t* idx,
+                                float* vl, float* minmax, const Shape& s, hipStream_t st);
+bool route_bf16_supported(const Shape& s);
+size_t route_chist_bytes(const Shape& s);
+hipError_t launch_route_bf16(const void* Q, const float* ql, int32_t* route, int32_t* chist,
+                             const Shape& s, hipStream_t st);
+hipError_t launch_group_bf16(const int32_t* route, const int32_t* chist, int32_t* counts,
+                             int32_t* offsets, int32_t* perm, const Shape& s, hipStream_t st);
+bool attend_bf16_supported(const Shape& s);
+hipError_t launch_attend_bf16(const void* Q, const void* K, const void* V, const float* ql,
+                              const float* vl, const int32_t* idx, const int32_t* offsets,
+                              const int32_t* perm, float* out, const Shape& s, hipStream_t st);
+
 // whole pass for short grids in one persistent kernel
 bool fused_supported(const Shape& s);
 hipError_t launch_fused(const void* Q, const void* K, const void* V, float* out, int32_t* idx,

@@ -150,11 +150,15 @@ mita_status mita_landmark(const float* ql, const void* K, const void* V,
 /*
  * Routing and grouping: route [B,H,N] = argmax_i q_n . ql[i] (lowest i on
  * ties), then a stable counting sort of each head's queries by route:
- * counts [B,H,m], offsets [B,H,m+1], perm [B,H,N].
+ * counts [B,H,m], offsets [B,H,m+1], perm [B,H,N].  Needs
+ * mita_route_workspace_bytes(...) of scratch (may be 0; workspace may then be
+ * NULL).
  */
+size_t mita_route_workspace_bytes(int B, int H, int N, int d, int m, mita_dtype in_dtype);
 mita_status mita_route(const void* Q, const float* ql, int B, int H, int N, int d, int m,
                        mita_dtype in_dtype, int32_t* route, int32_t* counts,
-                       int32_t* offsets, int32_t* perm, hipStream_t stream);
+                       int32_t* offsets, int32_t* perm,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Grouped expert attention: for every query, one softmax over its m shared

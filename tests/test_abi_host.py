@@ -26,6 +26,8 @@ def test_library_exports_every_declared_symbol():
     for name in _declared():
         assert hasattr(L, name), name
     assert L.mita_version().decode().startswith("mita-gfx950")
+    assert L.mita_route_workspace_bytes(32, 6, 3136, 64, 49, mita.MITA_BF16) > 0
+    assert L.mita_route_workspace_bytes(1, 1, 196, 64, 25, mita.MITA_F32) == 0
 
 
 def test_status_strings():
@@ -97,10 +99,14 @@ def test_stage_entry_points_validate():
     assert L.mita_pool(None, 1, 1, 14, 14, 64, 5, 5, 1, FAKE, None) == mita.MITA_ERR_INVALID_ARG
     assert L.mita_landmark(FAKE, FAKE, FAKE, 1, 1, 196, 64, 25, 26 * 0 + 197, 1, FAKE, FAKE, FAKE,
                            1 << 40, None) == mita.MITA_ERR_INVALID_ARG          # k > N
-    assert L.mita_landmark(FAKE, FAKE, FAKE, 1, 1, 196, 64, 25, 25, 1, FAKE, FAKE, FAKE, 4,
-                           None) == mita.MITA_ERR_WORKSPACE
-    assert L.mita_route(FAKE, FAKE, 1, 1, 196, 64, 25, 1, FAKE, FAKE, None, FAKE,
+    # fp32 inputs take the scalar landmark kernel, which needs scratch
+    assert L.mita_landmark(FAKE, FAKE, FAKE, 1, 1, 196, 64, 25, 25, mita.MITA_F32, FAKE, FAKE,
+                           FAKE, 4, None) == mita.MITA_ERR_WORKSPACE
+    assert L.mita_landmark_workspace_bytes(1, 1, 196, 64, 25, 25, mita.MITA_BF16) == 25 * 8
+    assert L.mita_route(FAKE, FAKE, 1, 1, 196, 64, 25, 1, FAKE, FAKE, None, FAKE, FAKE, 1 << 40,
                         None) == mita.MITA_ERR_INVALID_ARG
+    assert L.mita_route(FAKE, FAKE, 1, 1, 3136, 64, 49, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 8,
+                        None) == mita.MITA_ERR_WORKSPACE
     assert L.mita_attend(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 196, 64, 25,
                          25, 1, None, None) == mita.MITA_ERR_INVALID_ARG
 
