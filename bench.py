@@ -168,7 +168,7 @@ def measure(name, steps, warmup, path="auto"):
                            frac=pass_gbs / HBM_PEAK_GBS, bytes_per_qh=alg["bytes_per_qh"],
                            flops_per_qh=alg["flops_per_qh"]),
         stage_us={k: v * 1e3 for k, v in stages.items()}, schedule=sched,
-        dtype="bf16" if (sched == "fused") else "f32",
+        dtype=w["dtype"],
     )
     return r, res
 
