@@ -36,9 +36,8 @@ hipError_t launch_attend(const void* Q, const void* K, const void* V, const floa
 // bf16 kernels for long grids (MFMA, LDS-staged)
 hipError_t launch_pool_bf16(const void* Q, float* ql, const Shape& s, hipStream_t st);
 bool landmark_bf16_supported(const Shape& s);
-size_t landmark_minmax_bytes(const Shape& s);
 hipError_t launch_landmark_bf16(const float* ql, const void* K, const void* V, int32_t* idx,
-                                float* vl, float* minmax, const Shape& s, hipStream_t st);
+                                float* vl, const Shape& s, hipStream_t st);
 bool route_bf16_supported(const Shape& s);
 size_t route_chist_bytes(const Shape& s);
 hipError_t launch_route_bf16(const void* Q, const float* ql, int32_t* route, int32_t* chist,

@@ -4,23 +4,33 @@
 // routed expert; the same scores, softmax-normalised over all N keys, weight V
 // into the landmark values V_L).
 //
-// Two streaming kernels over one head's keys, each workgroup owning 16*NW
-// landmark rows (16 per wave), keys in 64-key blocks staged through LDS with
-// the next block prefetched into registers:
-//   values: S^T = K Q_L^T on bf16 MFMA (Q_L split hi + lo: fp32-accurate
-//     scores), an online softmax folded into V_L^T = V^T P^T on f16 MFMA (the
-//     normaliser from an all-ones MFMA over the same f16 weights), and each
-//     row's min and max score;
-//   select: recomputes S from K (now in L2).  Pass 1 counts the row's scores
-//     in 256 equal bins over [min, max] and finds the bin holding the k-th
-//     best.  Pass 2 collects the keys in that bin or above (typically k plus
-//     a few) into the row's LDS buffer; one exact selection (ties to the lower
-//     key id) keeps k, emitted in ascending key order via a bitmap.  Should the
-//     boundary bin overflow the buffer, pass 2 cuts the buffer back to its
-//     exact k best whenever it fills and only admits later keys above the
-//     k-th kept score, so the result stays exact.
-// Workgroups of one head are launched on the same XCD so K and V come from
-// HBM once and are re-read from that XCD's L2.
+// One kernel.  A workgroup owns 32 landmark rows of one head (two 16-row MFMA
+// tiles, so every K block loaded feeds both); its four waves split the head's
+// keys (wave w takes the 64-key blocks w, w+4, ...).  Raw scores
+// c = Q_L . K (the scale tau = 1/8 is a power of two, so it is folded into the
+// softmax and bin constants without changing any order) run on bf16 MFMA
+// with K rows loaded straight into the A operand and Q_L split hi + lo
+// (fp32-accurate).  Phases, separated by workgroup barriers:
+//   V  values: per wave, an online softmax of its keys' scores folded into
+//      V_L^T = V^T P^T (f16 MFMA; V staged transposed in the wave's own LDS
+//      slot; the running maximum is only raised when a score exceeds it by
+//      more than 2^8 in weight, so most blocks skip the rescale); the four
+//      partial results merge by log-sum-exp into V_L, and each row's score
+//      min and max fix 256 equal histogram bins;
+//   H  histogram: the waves recompute their scores (K now in L2) and count
+//      them per row in LDS; the bin holding the k-th best is found per row;
+//   C  collect: scores in that bin or above go to the row's LDS buffer
+//      (k + 64 entries).  The histogram says beforehand whether a row's
+//      candidates fit; when one does not (many equal scores), the collection
+//      runs one block at a time and cuts such buffers back to their exact k
+//      best whenever the next block could overflow them, later keys having to
+//      beat the k-th kept one in (value, lower key id) order;
+//   F  final: the keys above the boundary bin are all taken, the boundary
+//      bin's by rank among themselves (ties to the lower key id); the k ids
+//      are written ascending through a bitmap in the row's histogram space
+//      (or, for N > 8192, by counting).
+// Workgroups of one head are launched on one XCD so its K and V come from HBM
+// once and are re-read from that XCD's L2.
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
@@ -29,14 +39,38 @@
 namespace mita {
 namespace lmk {
 
-constexpr int KB = 64;                    // keys per block
-constexpr int KST_BYTES = KB * 128;       // K block: 64 bf16 rows, XOR-swizzled chunks
-constexpr int VT_STRIDE = KB * 2 + 16;    // bytes per V^T row: 64 f16 keys + pad
+constexpr int KB = 64;                  // keys per block
+constexpr int NW = 4;                   // waves per workgroup
+constexpr int TL = 2;                   // 16-row MFMA tiles per workgroup
+constexpr int ROWS = 16 * TL;           // landmark rows per workgroup
+constexpr int VT_STRIDE = KB * 2 + 16;  // bytes per V^T row: 64 f16 keys + pad
 constexpr int VT_BYTES = 64 * VT_STRIDE;
-constexpr int HIST_BYTES = 512;           // one row's 256 packed 16-bit bins
-constexpr int HIST_STRIDE = 528;          // rows 4 banks apart: the 16 rows' atomics spread
+constexpr int HIST_STRIDE = 1040;       // one row's 256 32-bit bins + pad (rows 4 banks apart)
+constexpr int BITMAP_MAX_N = 8192;      // keys whose bitmap fits in a histogram row
+constexpr int LIST_MAX = 128;           // boundary entries listed in a histogram row
+constexpr int MERGE_STRIDE = 68;        // floats per (wave, row): 64 acc, max, sum, min, max
+constexpr float kTauLog2e = 0.125f * 1.4426950408889634f;
+constexpr float kSlack = 8.0f;          // log2 headroom of the lazily raised maximum
 
-__device__ __forceinline__ int rc(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
+// per-row state in LDS
+struct RowState {
+  float lo, A, B;     // bin(c) = clamp(fma(c, A, B), 0, 255): 256 bins over [lo, hi]
+  float bthr;         // collect when fma(c, A, B) >= bthr (the boundary bin or above)
+  int bstar, above;   // boundary bin, count strictly above it
+  int cnt;            // entries in the row's buffer
+  float thr;          // admission bound (k-th kept), -inf while unbounded
+  int thrkey;         // key id of the k-th kept entry
+  int over;           // candidates may not fit: collect block by block
+  int pad[2];
+};
+
+constexpr int OFF_HIST = 0;
+constexpr int OFF_ROW = OFF_HIST + ROWS * HIST_STRIDE;
+constexpr int OFF_FLAG = OFF_ROW + ROWS * (int)sizeof(RowState);
+constexpr int OFF_UNION = (OFF_FLAG + 16 + 15) & ~15;
+constexpr int VALUES_BYTES = NW * VT_BYTES;  // phase V staging (the merge area aliases it)
+static_assert(NW * ROWS * MERGE_STRIDE * 4 <= VALUES_BYTES, "merge area fits in the staging");
+static_assert(BITMAP_MAX_N / 8 <= HIST_STRIDE && LIST_MAX * 8 <= HIST_STRIDE, "row space");
 
 struct Args {
   const float* ql;
@@ -44,53 +78,63 @@ struct Args {
   const uint16_t* V;
   int32_t* idx;
   float* vl;
-  float* minmax;  // [BH][m][2] row min and max score
-  int BH, N, m, k, cap, rblocks;  // rblocks = workgroups per head
+  int BH, N, m, k, cap, tiles;
 };
 
-// K block (and, for the values kernel, the V block) for one 64-key block.
-template <int NW, bool WITH_V>
-struct Pf {
-  static constexpr int KC = 8 / NW;               // 16-byte K chunks per thread
-  static constexpr int VC = WITH_V ? 4 / NW : 0;  // V key-pair chunks per thread
-  u32x4 k[KC], v0[VC > 0 ? VC : 1], v1[VC > 0 ? VC : 1];
+__host__ __device__ constexpr size_t lds_bytes(int cap) {
+  return (size_t)OFF_UNION + ((size_t)ROWS * cap * 8 > (size_t)VALUES_BYTES
+                                  ? (size_t)ROWS * cap * 8
+                                  : (size_t)VALUES_BYTES);
+}
+
+// A operands of one 64-key block: lane (g, c16) holds key 16kt + c16,
+// channels 8g.. (k-step 0) and 32 + 8g.. (k-step 1).  Keys past N read key
+// N-1 (their scores are masked).
+struct KRegs {
+  u32x4 a[4][2];
 };
 
-template <int NW, bool WITH_V>
-__device__ __forceinline__ void load_block(Pf<NW, WITH_V>& pf, const uint16_t* Kh,
-                                           const uint16_t* Vh, int blk, int N, int tid) {
-  const u32x4 z = {0u, 0u, 0u, 0u};
+__device__ __forceinline__ void load_k(KRegs& kr, const uint16_t* Kh, int blk, int N, int g,
+                                       int c16) {
 #pragma unroll
-  for (int i = 0; i < Pf<NW, WITH_V>::KC; ++i) {
-    const int id = tid + 64 * NW * i, row = id >> 3, c = id & 7, key = blk * KB + row;
-    pf.k[i] = key < N ? *reinterpret_cast<const u32x4*>(Kh + (size_t)key * 64 + 8 * c) : z;
-  }
-#pragma unroll
-  for (int i = 0; i < Pf<NW, WITH_V>::VC; ++i) {
-    const int id = tid + 64 * NW * i, p = id & 31, c = id >> 5;  // 32 key pairs x 8 chunks
-    const int j0 = blk * KB + 2 * p, j1 = j0 + 1;
-    pf.v0[i] = j0 < N ? *reinterpret_cast<const u32x4*>(Vh + (size_t)j0 * 64 + 8 * c) : z;
-    pf.v1[i] = j1 < N ? *reinterpret_cast<const u32x4*>(Vh + (size_t)j1 * 64 + 8 * c) : z;
+  for (int kt = 0; kt < 4; ++kt) {
+    const uint16_t* p = Kh + (size_t)min(blk * KB + 16 * kt + c16, N - 1) * 64;
+    kr.a[kt][0] = *reinterpret_cast<const u32x4*>(p + 8 * g);
+    kr.a[kt][1] = *reinterpret_cast<const u32x4*>(p + 32 + 8 * g);
   }
 }
 
-template <int NW, bool WITH_V>
-__device__ __forceinline__ void store_block(const Pf<NW, WITH_V>& pf, char* kst, char* vt,
-                                            int tid) {
+// V block for the transposed LDS copy: lane holds keys 4p..4p+3 of chunk c
+// (8 channels) for items it = lane, lane + 64 (p = it >> 3, c = it & 7).
+// Keys past N read key N-1 (finite; their weights are 0).
+struct VRegs {
+  u32x4 v[2][4];
+};
+
+__device__ __forceinline__ void load_v(VRegs& vr, const uint16_t* Vh, int blk, int N, int lane) {
 #pragma unroll
-  for (int i = 0; i < Pf<NW, WITH_V>::KC; ++i) {
-    const int id = tid + 64 * NW * i, row = id >> 3, c = id & 7;
-    *reinterpret_cast<u32x4*>(kst + rc(row, c)) = pf.k[i];
+  for (int j = 0; j < 2; ++j) {
+    const int it = lane + 64 * j, p = it >> 3, c = it & 7;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      vr.v[j][i] = *reinterpret_cast<const u32x4*>(
+          Vh + (size_t)min(blk * KB + 4 * p + i, N - 1) * 64 + 8 * c);
   }
+}
+
+// V^T (f16) into the wave's slot: row = channel, 64 keys per row.
+__device__ __forceinline__ void store_vt(const VRegs& vr, char* vt, int lane) {
 #pragma unroll
-  for (int i = 0; i < Pf<NW, WITH_V>::VC; ++i) {
-    const int id = tid + 64 * NW * i, p = id & 31, c = id >> 5;
+  for (int j = 0; j < 2; ++j) {
+    const int it = lane + 64 * j, p = it >> 3, c = it & 7;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const uint32_t a = (pf.v0[i][t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
-      const uint32_t b = (pf.v1[i][t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
-      *reinterpret_cast<uint32_t*>(vt + (8 * c + t) * VT_STRIDE + 4 * p) =
-          pk_f16(bf16_bits_to_f32(a), bf16_bits_to_f32(b));
+      float f[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        f[i] = bf16_bits_to_f32((vr.v[j][i][t >> 1] >> (16 * (t & 1))) & 0xFFFFu);
+      *reinterpret_cast<u32x2*>(vt + (8 * c + t) * VT_STRIDE + 8 * p) =
+          u32x2{pk_f16(f[0], f[1]), pk_f16(f[2], f[3])};
     }
   }
 }
@@ -113,326 +157,493 @@ __device__ __forceinline__ void load_ql_b(const float* ql, int bh, int m, int ro
       h[i] = bf16_rne_bits(v);
       l[i] = bf16_rne_bits(v - bf16_bits_to_f32(h[i]));
     }
-    bqh[ks] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-    bql[ks] = u32x4{l[0] | (l[1] << 16), l[2] | (l[3] << 16), l[4] | (l[5] << 16), l[6] | (l[7] << 16)};
+    bqh[ks] = u32x4{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
+    bql[ks] = u32x4{pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7])};
   }
 }
 
-// Scores of the staged block: lane holds key 64blk + 16kt + 4g + r of its row
-// (tau-scaled; -inf past N).
-__device__ __forceinline__ void block_scores(const char* kst, const u32x4 (&bqh)[2],
-                                             const u32x4 (&bql)[2], int blk, int N, int g,
-                                             int c16, float (&s)[4][4]) {
+// Raw scores of one block: lane holds key 64blk + 16kt + 4g + r of row c16.
+// Every phase computes them with this same sequence, so a score is
+// bit-identical wherever it is recomputed.
+__device__ __forceinline__ void block_scores(const KRegs& kr, const u32x4 (&bqh)[2],
+                                             const u32x4 (&bql)[2], float (&s)[4][4]) {
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
-    const u32x4 a0 = *reinterpret_cast<const u32x4*>(kst + rc(16 * kt + c16, g));
-    const u32x4 a1 = *reinterpret_cast<const u32x4*>(kst + rc(16 * kt + c16, 4 + g));
     f32x4 c = zero4();
-    c = mfma_bf16(a0, bqh[0], c);
-    c = mfma_bf16(a0, bql[0], c);
-    c = mfma_bf16(a1, bqh[1], c);
-    c = mfma_bf16(a1, bql[1], c);
+    c = mfma_bf16(kr.a[kt][0], bqh[0], c);
+    c = mfma_bf16(kr.a[kt][0], bql[0], c);
+    c = mfma_bf16(kr.a[kt][1], bqh[1], c);
+    c = mfma_bf16(kr.a[kt][1], bql[1], c);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = blk * KB + 16 * kt + 4 * g + r;
-      s[kt][r] = key < N ? c[r] * 0.125f : -INFINITY;
-    }
+    for (int r = 0; r < 4; ++r) s[kt][r] = c[r];
   }
 }
 
-__device__ __forceinline__ void head_of_block(const Args& a, int& bh, int& rb) {
-  // round-robin dispatch puts workgroup b on XCD b % 8: keep a head's
-  // workgroups on one XCD so its K and V stay in that XCD's L2
-  const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
-  bh = xcd + 8 * (slot / a.rblocks);
-  rb = slot % a.rblocks;
+__device__ __forceinline__ int key_of(int blk, int kt, int g, int r) {
+  return blk * KB + 16 * kt + 4 * g + r;
 }
 
-// ---------------------------------------------------------------- values
-template <int NW>
-__global__ __launch_bounds__(64 * NW) void lmk_values_kernel(Args a) {
-  __shared__ __attribute__((aligned(16))) char sm[KST_BYTES + VT_BYTES];
-  char* kst = sm;
-  char* vt = sm + KST_BYTES;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int g = lane >> 4, c16 = lane & 15;
-  int bh, rb;
-  head_of_block(a, bh, rb);
-  if (bh >= a.BH) return;
-  const int N = a.N;
-  const uint16_t* Kh = a.K + (size_t)bh * N * 64;
-  const uint16_t* Vh = a.V + (size_t)bh * N * 64;
-  const int myrow = rb * 16 * NW + 16 * w + c16;
-  u32x4 bqh[2], bql[2];
-  load_ql_b(a.ql, bh, a.m, myrow, g, bqh, bql);
-  const float l2e = 1.4426950408889634f;
-  float mrun = -INFINITY, mn = INFINITY;
-  f32x4 accv[4] = {zero4(), zero4(), zero4(), zero4()};
-  f32x4 lsum = zero4();
-  const u32x4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
-  // one block computes while the next two are in flight
-  auto compute = [&](int blk) {
-    float s[4][4];
-    block_scores(kst, bqh, bql, blk, N, g, c16, s);
-    float bmax = s[0][0];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        bmax = fmaxf(bmax, s[kt][r]);
-        if (s[kt][r] > -INFINITY) mn = fminf(mn, s[kt][r]);
+__device__ __forceinline__ int bin_of(float c, float A, float B) {
+  return (int)__builtin_amdgcn_fmed3f(__builtin_fmaf(c, A, B), 0.f, 255.f);
+}
+
+// Candidate order: larger score first, ties to the lower key id.
+__device__ __forceinline__ bool better(float va, int ka, float vb, int kb) {
+  return va > vb || (va == vb && ka < kb);
+}
+
+// Number of the n entries at `list` (interleaved score, key) that rank
+// before (v, key).  The 16 lanes of a group read the same entries.
+__device__ __forceinline__ int rank_in_list(const float* list, int n, float v, int key) {
+  int r = 0;
+  int j = 0;
+  for (; j + 2 <= n; j += 2) {
+    const float4 e = *reinterpret_cast<const float4*>(list + 2 * j);
+    r += better(e.x, __float_as_int(e.y), v, key) + better(e.z, __float_as_int(e.w), v, key);
+  }
+  if (j < n) r += better(list[2 * j], __float_as_int(list[2 * j + 1]), v, key);
+  return r;
+}
+
+// Same over the row's buffer (separate score and key arrays).
+__device__ __forceinline__ int rank_in(const float* vals, const int* keys, int n, float v,
+                                       int key) {
+  int r = 0;
+  int j = 0;
+  for (; j + 4 <= n; j += 4) {
+    const float4 vv = *reinterpret_cast<const float4*>(vals + j);
+    const int4 kk = *reinterpret_cast<const int4*>(keys + j);
+    r += better(vv.x, kk.x, v, key) + better(vv.y, kk.y, v, key) + better(vv.z, kk.z, v, key) +
+         better(vv.w, kk.w, v, key);
+  }
+  for (; j < n; ++j) r += better(vals[j], keys[j], v, key);
+  return r;
+}
+
+__device__ __forceinline__ void group_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Cuts row lr's buffer back to its exact k best (kept in buffer order) and
+// sets the admission bound to the k-th of them.  Lane t of the group takes
+// entries t, t + 16, ...
+__device__ void row_cut(char* sm, const Args& a, int lr, bool work, int t, int g) {
+  RowState* rs = reinterpret_cast<RowState*>(sm + OFF_ROW) + lr;
+  float* vals = reinterpret_cast<float*>(sm + OFF_UNION + (size_t)lr * a.cap * 8);
+  int* keys = reinterpret_cast<int*>(vals + a.cap);
+  const int cnt = work ? rs->cnt : 0;
+  uint32_t keep = 0u;
+  float tv = -INFINITY;
+  int tk = 0;
+  for (int u = 0; 16 * u < cnt; ++u) {
+    const int e = t + 16 * u;
+    if (e < cnt) {
+      const float v = vals[e];
+      const int key = keys[e];
+      const int r = rank_in(vals, keys, cnt, v, key);
+      keep |= (r < a.k ? 1u : 0u) << u;
+      if (r == a.k - 1) {
+        tv = v;
+        tk = key + 1;
       }
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32, 64));
-    const float mnew = fmaxf(mrun, bmax);
-    const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * l2e);
-    mrun = mnew;
-    u32x4 bp[2];
-#pragma unroll
-    for (int sp = 0; sp < 2; ++sp) {
-      float p[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[r] = __builtin_amdgcn_exp2f((s[2 * sp][r] - mnew) * l2e);
-        p[4 + r] = __builtin_amdgcn_exp2f((s[2 * sp + 1][r] - mnew) * l2e);
-      }
-      bp[sp] = u32x4{pk_f16(p[0], p[1]), pk_f16(p[2], p[3]), pk_f16(p[4], p[5]), pk_f16(p[6], p[7])};
-    }
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      const char* vrow = vt + (16 * ct + c16) * VT_STRIDE;
-      f32x4 acc = accv[ct] * alpha;
-#pragma unroll
-      for (int sp = 0; sp < 2; ++sp) {
-        const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vrow + (32 * sp + 4 * g) * 2);
-        const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vrow + (32 * sp + 16 + 4 * g) * 2);
-        acc = mfma_f16(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, bp[sp], acc);
-      }
-      accv[ct] = acc;
-    }
-    lsum = mfma_f16(ones, bp[0], lsum * alpha);
-    lsum = mfma_f16(ones, bp[1], lsum);
-  };
-  Pf<NW, true> pfa, pfb;
-  const int nblk = (N + KB - 1) / KB;
-  load_block<NW, true>(pfa, Kh, Vh, 0, N, tid);
-  if (nblk > 1) load_block<NW, true>(pfb, Kh, Vh, 1, N, tid);
-  for (int blk = 0; blk < nblk; blk += 2) {
-    __syncthreads();
-    store_block<NW, true>(pfa, kst, vt, tid);
-    __syncthreads();
-    if (blk + 2 < nblk) load_block<NW, true>(pfa, Kh, Vh, blk + 2, N, tid);
-    compute(blk);
-    if (blk + 1 < nblk) {
-      __syncthreads();
-      store_block<NW, true>(pfb, kst, vt, tid);
-      __syncthreads();
-      if (blk + 3 < nblk) load_block<NW, true>(pfb, Kh, Vh, blk + 3, N, tid);
-      compute(blk + 1);
     }
   }
-  mn = fminf(mn, __shfl_xor(mn, 16, 64));
-  mn = fminf(mn, __shfl_xor(mn, 32, 64));
-  if (myrow < a.m) {
-    const float inv = 1.0f / lsum[0];
-    float* dst = a.vl + ((size_t)bh * a.m + myrow) * 64;
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-      *reinterpret_cast<float4*>(dst + 16 * ct + 4 * g) =
-          make_float4(accv[ct][0] * inv, accv[ct][1] * inv, accv[ct][2] * inv, accv[ct][3] * inv);
-    if (g == 0) {
-      a.minmax[((size_t)bh * a.m + myrow) * 2 + 0] = mn;
-      a.minmax[((size_t)bh * a.m + myrow) * 2 + 1] = mrun;
+  // exactly one lane holds the k-th kept entry
+  tv = g16_maxf(tv);
+  tk = g16_addi(tk) - 1;
+  group_sync();
+  // stable in-place filter, 16 entries at a time (writes land at or below
+  // the entries read in the same step)
+  const uint32_t below = (1u << t) - 1u;
+  int run = 0;
+  for (int u = 0; 16 * u < cnt; ++u) {
+    const int e = t + 16 * u;
+    const bool kp = e < cnt && (keep >> u & 1u);
+    const float v = kp ? vals[e] : 0.f;
+    const int key = kp ? keys[e] : 0;
+    const uint32_t gm = g16_ballot(kp, g);
+    group_sync();
+    if (kp) {
+      vals[run + __popc(gm & below)] = v;
+      keys[run + __popc(gm & below)] = key;
     }
+    run += __popc(gm);
+  }
+  if (work && t == 0) {
+    rs->cnt = run;
+    rs->thr = tv;
+    rs->thrkey = tk;
   }
 }
 
-// ---------------------------------------------------------------- select
-template <int NW>
-struct SelLayout {
-  static constexpr int ROWS = 16 * NW;
-  static constexpr int OFF_K = 0;
-  static constexpr int OFF_HIST = OFF_K + KST_BYTES;              // [ROWS] x HIST_STRIDE
-  static constexpr int OFF_CNT = OFF_HIST + ROWS * HIST_STRIDE;   // [ROWS] int
-  static constexpr int OFF_THR = OFF_CNT + ROWS * 4;              // [ROWS] float
-  static constexpr int OFF_BSTAR = OFF_THR + ROWS * 4;            // [ROWS] int
-  static constexpr int OFF_BUF = OFF_BSTAR + ROWS * 4;
-  static size_t bytes(int cap) { return (size_t)OFF_BUF + (size_t)ROWS * cap * 8; }
-};
-
-// Cut rows' candidate buffers back (final == false: only rows whose buffer is
-// nearly full) to their exact k best, or emit each row's exact k best in
-// ascending key order (final == true).  Group g handles rows 4*batch + g.
-template <int NW, int NV>
-__device__ void select_rows(char* sm, const Args& a, int bh, int row0, int w, int g, int t,
-                            bool final) {
-  using L = SelLayout<NW>;
-  const int cnt_limit = a.cap - KB;
-#pragma unroll 1
-  for (int batch = 0; batch < 4; ++batch) {
-    const int lr = 16 * w + 4 * batch + g;
-    const int row = row0 + lr;
-    const bool active = row < a.m;
-    int* cntp = reinterpret_cast<int*>(sm + L::OFF_CNT) + lr;
-    const int cnt = active ? *cntp : 0;
-    const bool work = final ? active : (active && cnt > cnt_limit);
-    if (__ballot(work) == 0) continue;
-    char* hist = sm + L::OFF_HIST + lr * HIST_STRIDE;
-    float* vals = reinterpret_cast<float*>(sm + L::OFF_BUF + (size_t)lr * a.cap * 8);
-    int* keys = reinterpret_cast<int*>(vals + a.cap);
-    float sv[NV], x[NV];
-    int kk[NV];
-    uint32_t cand = 0u;
-#pragma unroll
-    for (int u = 0; u < NV; ++u) {
+// Row lr's k best of its buffer, written ascending to `out`.
+__device__ void row_final(char* sm, const Args& a, int lr, bool work, int t, int g,
+                          int32_t* out) {
+  RowState* rs = reinterpret_cast<RowState*>(sm + OFF_ROW) + lr;
+  float* vals = reinterpret_cast<float*>(sm + OFF_UNION + (size_t)lr * a.cap * 8);
+  int* keys = reinterpret_cast<int*>(vals + a.cap);
+  float* list = reinterpret_cast<float*>(sm + OFF_HIST + lr * HIST_STRIDE);
+  const int cnt = work ? rs->cnt : 0;
+  const float A = rs->A, B = rs->B;
+  const int bstar = rs->bstar, above = rs->above;
+  // entries above the boundary bin are in; the boundary bin's are ranked
+  // among themselves, in a compact list when it fits
+  const float upthr = bstar < 255 ? (float)(bstar + 1) : INFINITY;
+  const int nb = cnt - above;
+  const bool listed = nb <= LIST_MAX;
+  const uint32_t below = (1u << t) - 1u;
+  uint32_t up = 0u;
+  int run = 0;
+  for (int u = 0; 16 * u < cnt; ++u) {
+    const int e = t + 16 * u;
+    bool inb = false;
+    if (e < cnt) {
+      const bool isup = __builtin_fmaf(vals[e], A, B) >= upthr;
+      up |= (isup ? 1u : 0u) << u;
+      inb = !isup;
+    }
+    const uint32_t gm = g16_ballot(inb, g);
+    if (listed && inb) {
+      const int pos = run + __popc(gm & below);
+      list[2 * pos] = vals[e];
+      list[2 * pos + 1] = __int_as_float(keys[e]);
+    }
+    run += __popc(gm);
+  }
+  group_sync();
+  uint32_t take = up;
+  const int need = a.k - above;
+  for (int u = 0; 16 * u < cnt; ++u) {
+    const int e = t + 16 * u;
+    if (e < cnt && !(up >> u & 1u)) {
+      const float v = vals[e];
+      const int key = keys[e];
+      const int r = listed ? rank_in_list(list, nb, v, key) : rank_in(vals, keys, cnt, v, key) - above;
+      take |= (r < need ? 1u : 0u) << u;
+    }
+  }
+  group_sync();
+  if (a.N <= BITMAP_MAX_N) {
+    // bitmap of the taken keys in the row's histogram space; slot = number of
+    // taken keys below
+    uint32_t* bm = reinterpret_cast<uint32_t*>(list);
+    const int nw = (a.N + 31) >> 5;
+    for (int q = t; q < nw; q += 16) bm[q] = 0u;
+    group_sync();
+    for (int u = 0; 16 * u < cnt; ++u) {
       const int e = t + 16 * u;
-      const bool ok = work && e < cnt;
-      sv[u] = ok ? vals[e] : -INFINITY;
-      kk[u] = ok ? keys[e] : 0;
-      x[u] = sv[u];
-      cand |= (ok ? 1u : 0u) << u;
+      if (e < cnt && (take >> u & 1u)) atomicOr(&bm[keys[e] >> 5], 1u << (keys[e] & 31));
     }
-    const uint32_t take = group_topk<NV>(x, kk, cand, a.k, hist, t, g);
-    if (!final) {
-      int run = 0;
-      float kmin = INFINITY;
-      const uint32_t below = (1u << t) - 1u;
-#pragma unroll
-      for (int u = 0; u < NV; ++u) {
-        const bool bit = take >> u & 1u;
-        const uint32_t gm = g16_ballot(bit, g);
-        const int pos = run + __popc(gm & below);
-        if (bit) {
-          vals[pos] = sv[u];
-          keys[pos] = kk[u];
-          kmin = fminf(kmin, sv[u]);
-        }
-        run += __popc(gm);
-      }
-      kmin = g16_minf(kmin);
-      if (work && t == 0) {
-        *cntp = run;
-        reinterpret_cast<float*>(sm + L::OFF_THR)[lr] = run >= a.k ? kmin : -INFINITY;
-      }
-    } else {
-      uint32_t* bm = reinterpret_cast<uint32_t*>(vals);
-      const int nw = (a.N + 31) >> 5;
-      for (int q = t; q < nw; q += 16) bm[q] = 0u;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int u = 0; u < NV; ++u)
-        if (take >> u & 1u) atomicOr(&bm[kk[u] >> 5], 1u << (kk[u] & 31));
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      const int wpl = (nw + 15) >> 4;
-      const int q0 = t * wpl, q1 = min(nw, q0 + wpl);
-      int mine = 0;
-      for (int q = q0; q < q1; ++q) mine += __popc(bm[q]);
-      const int total = g16_addi(mine);
-      int pos = total - g16_suffix(mine);
-      int32_t* out = a.idx + ((size_t)bh * a.m + row) * a.k;
-      if (active) {
-        for (int q = q0; q < q1; ++q) {
-          uint32_t wbits = bm[q];
-          while (wbits) {
-            const int b = __ffs(wbits) - 1;
-            wbits &= wbits - 1u;
-            if (pos < a.k) out[pos] = 32 * q + b;
-            ++pos;
-          }
+    group_sync();
+    const int wpl = (nw + 15) >> 4;
+    const int q0 = t * wpl, q1 = min(nw, q0 + wpl);
+    int mine = 0;
+    for (int q = q0; q < q1; ++q) mine += __popc(bm[q]);
+    int pos = g16_addi(mine) - g16_suffix(mine);
+    if (work) {
+      for (int q = q0; q < q1; ++q) {
+        uint32_t wbits = bm[q];
+        while (wbits) {
+          const int b = __ffs(wbits) - 1;
+          wbits &= wbits - 1u;
+          if (pos < a.k) out[pos] = 32 * q + b;
+          ++pos;
         }
       }
+    }
+  } else {
+    // slot = number of taken keys below, counted over the buffer with the
+    // untaken keys replaced by INT_MAX (the scores are no longer needed)
+    int* tkeys = reinterpret_cast<int*>(vals);
+    for (int u = 0; 16 * u < cnt; ++u) {
+      const int e = t + 16 * u;
+      if (e < cnt) tkeys[e] = (take >> u & 1u) ? keys[e] : 0x7FFFFFFF;
+    }
+    group_sync();
+    for (int u0 = 0; 16 * u0 < cnt; u0 += 4) {
+      int kq[4], pos[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = t + 16 * (u0 + i);
+        kq[i] = (e < cnt && (take >> (u0 + i) & 1u)) ? tkeys[e] : -1;
+      }
+      int j = 0;
+      for (; j + 4 <= cnt; j += 4) {
+        const int4 kk = *reinterpret_cast<const int4*>(tkeys + j);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          pos[i] += (kk.x < kq[i]) + (kk.y < kq[i]) + (kk.z < kq[i]) + (kk.w < kq[i]);
+      }
+      for (; j < cnt; ++j) {
+        const int kj = tkeys[j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pos[i] += kj < kq[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (work && kq[i] >= 0) out[pos[i]] = kq[i];
     }
   }
 }
 
-template <int NW, int NV>
-__global__ __launch_bounds__(64 * NW) void lmk_select_kernel(Args a) {
-  using L = SelLayout<NW>;
+__global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  int bh, rb;
-  head_of_block(a, bh, rb);
+  // round-robin dispatch puts workgroup b on XCD b % 8: keep a head's
+  // workgroups on one XCD so its K and V stay in that XCD's L2
+  const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
+  const int bh = xcd + 8 * (slot / a.tiles), row0 = (slot % a.tiles) * ROWS;
   if (bh >= a.BH) return;
-  const int N = a.N, row0 = rb * L::ROWS;
+  const int N = a.N, nblk = (N + KB - 1) / KB;
+  const bool ragged = (N % KB) != 0;  // the last block has keys past N
   const uint16_t* Kh = a.K + (size_t)bh * N * 64;
-  const int lr = 16 * w + c16;  // this lane's row (column c16 of the S^T tiles)
-  const int myrow = row0 + lr;
-  const bool rowok = myrow < a.m;
-  u32x4 bqh[2], bql[2];
-  load_ql_b(a.ql, bh, a.m, myrow, g, bqh, bql);
-  // 256 equal bins over the row's [min, max]
-  float lo = 0.f, hi = 0.f;
-  if (rowok) {
-    lo = a.minmax[((size_t)bh * a.m + myrow) * 2 + 0];
-    hi = a.minmax[((size_t)bh * a.m + myrow) * 2 + 1];
-  }
-  const float scale = hi > lo ? 256.0f / (hi - lo) : 0.f;
-  char* myhist = sm + L::OFF_HIST + lr * HIST_STRIDE;
-  for (int i = tid; i < L::ROWS * HIST_STRIDE / 16; i += 64 * NW)
-    reinterpret_cast<u32x4*>(sm + L::OFF_HIST)[i] = u32x4{0u, 0u, 0u, 0u};
-  if (tid < L::ROWS) {
-    reinterpret_cast<int*>(sm + L::OFF_CNT)[tid] = 0;
-    reinterpret_cast<float*>(sm + L::OFF_THR)[tid] = -INFINITY;
-  }
-  const int nblk = (N + KB - 1) / KB;
-  Pf<NW, false> pfa, pfb;
-  // Streams the head's keys with two blocks in flight, calling body(blk)
-  // with block blk staged in LDS.
-  auto stream = [&](auto&& body) {
-    load_block<NW, false>(pfa, Kh, nullptr, 0, N, tid);
-    for (int blk = 0; blk < nblk; ++blk) {
-      __syncthreads();
-      store_block<NW, false>(pfa, sm + L::OFF_K, nullptr, tid);
-      __syncthreads();
-      if (blk + 1 < nblk) load_block<NW, false>(pfa, Kh, nullptr, blk + 1, N, tid);
-      body(blk);
+  const uint16_t* Vh = a.V + (size_t)bh * N * 64;
+  RowState* rows = reinterpret_cast<RowState*>(sm + OFF_ROW);
+  int* flag = reinterpret_cast<int*>(sm + OFF_FLAG);
+
+  for (int i = tid; i < ROWS * HIST_STRIDE / 16; i += 64 * NW)
+    reinterpret_cast<u32x4*>(sm + OFF_HIST)[i] = u32x4{0u, 0u, 0u, 0u};
+  if (tid == 0) flag[0] = 0;
+
+  // this lane's rows: 16 * tl + c16 of the workgroup's rows (column c16 of
+  // tile tl of S^T)
+  u32x4 bqh[TL][2], bql[TL][2];
+#pragma unroll
+  for (int tl = 0; tl < TL; ++tl)
+    load_ql_b(a.ql, bh, a.m, row0 + 16 * tl + c16, g, bqh[tl], bql[tl]);
+
+  // ------------------------------------------------------------ V: values
+  {
+    char* vt = sm + OFF_UNION + w * VT_BYTES;
+    float mref[TL], mn[TL], mx[TL];
+    f32x4 accv[TL][4], lsum[TL];
+#pragma unroll
+    for (int tl = 0; tl < TL; ++tl) {
+      mref[tl] = -INFINITY;
+      mn[tl] = INFINITY;
+      mx[tl] = -INFINITY;
+      lsum[tl] = zero4();
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) accv[tl][ct] = zero4();
     }
-  };
-  // ---- pass 1: histogram
-  stream([&](int blk) {
-    float s[4][4];
-    block_scores(sm + L::OFF_K, bqh, bql, blk, N, g, c16, s);
-    if (rowok) {
+    const u32x4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+    KRegs kr;
+    VRegs vr;
+    if (w < nblk) {
+      load_k(kr, Kh, w, N, g, c16);
+      load_v(vr, Vh, w, N, lane);
+    }
+    for (int blk = w; blk < nblk; blk += NW) {
+      // the V registers are free once stored and the K registers once the
+      // scores are out: the next block's loads go out right after each
+      store_vt(vr, vt, lane);
+      if (blk + NW < nblk) load_v(vr, Vh, blk + NW, N, lane);
+      group_sync();
+      const bool last = ragged && blk == nblk - 1;
+      // one tile at a time keeps one tile's scores and weights live
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+      for (int tl = 0; tl < TL; ++tl) {
+        float s[4][4];
+        block_scores(kr, bqh[tl], bql[tl], s);
+        if (tl == TL - 1 && blk + NW < nblk) load_k(kr, Kh, blk + NW, N, g, c16);
+        if (last) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (s[kt][r] > -INFINITY) {
-            const int b = min(255, max(0, (int)((s[kt][r] - lo) * scale)));
-            atomicAdd(reinterpret_cast<uint32_t*>(myhist + (b >> 1) * 4), 1u << (16 * (b & 1)));
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const bool ok = key_of(blk, kt, g, r) < N;
+              if (ok) mn[tl] = fminf(mn[tl], s[kt][r]);
+              if (!ok) s[kt][r] = -INFINITY;
+            }
+        } else {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mn[tl] = fminf(mn[tl], s[kt][r]);
+        }
+        float bmax = s[0][0];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) bmax = fmaxf(bmax, s[kt][r]);
+        mx[tl] = fmaxf(mx[tl], bmax);
+        // raise the reference maximum only when some weight would exceed 2^8
+        const bool raise = (bmax - mref[tl]) * kTauLog2e > kSlack;
+        if (__ballot(raise) != 0) {
+          float m2 = fmaxf(bmax, __shfl_xor(bmax, 16, 64));
+          m2 = fmaxf(m2, __shfl_xor(m2, 32, 64));
+          const float mnew = fmaxf(mref[tl], m2);
+          const float alpha = __builtin_amdgcn_exp2f((mref[tl] - mnew) * kTauLog2e);
+          mref[tl] = mnew;
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) accv[tl][ct] = accv[tl][ct] * alpha;
+          lsum[tl] = lsum[tl] * alpha;
+        }
+        const float moff = -mref[tl] * kTauLog2e;
+        u32x4 bp[2];
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+          float p[8];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * sp][r], kTauLog2e, moff));
+            p[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * sp + 1][r], kTauLog2e, moff));
           }
+          bp[sp] = u32x4{pk_f16(p[0], p[1]), pk_f16(p[2], p[3]), pk_f16(p[4], p[5]),
+                         pk_f16(p[6], p[7])};
+        }
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const char* vrow = vt + (16 * ct + c16) * VT_STRIDE;
+          f32x4 acc = accv[tl][ct];
+#pragma unroll
+          for (int sp = 0; sp < 2; ++sp) {
+            const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vrow + (32 * sp + 4 * g) * 2);
+            const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vrow + (32 * sp + 16 + 4 * g) * 2);
+            acc = mfma_f16(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, bp[sp], acc);
+          }
+          accv[tl][ct] = acc;
+        }
+        lsum[tl] = mfma_f16(ones, bp[0], lsum[tl]);
+        lsum[tl] = mfma_f16(ones, bp[1], lsum[tl]);
+      }
+      group_sync();
     }
-  });
+#pragma unroll
+    for (int tl = 0; tl < TL; ++tl) {
+      mn[tl] = fminf(mn[tl], __shfl_xor(mn[tl], 16, 64));
+      mn[tl] = fminf(mn[tl], __shfl_xor(mn[tl], 32, 64));
+      mx[tl] = fmaxf(mx[tl], __shfl_xor(mx[tl], 16, 64));
+      mx[tl] = fmaxf(mx[tl], __shfl_xor(mx[tl], 32, 64));
+    }
+    __syncthreads();  // every wave is done with its staging slot
+    // partials: acc[tl][ct][r] = V_L^T[channel 16ct + 4g + r][row 16tl + c16],
+    // relative to exp2((c - mref) tau log2e); mref <= the true maximum mx
+#pragma unroll
+    for (int tl = 0; tl < TL; ++tl) {
+      float* part =
+          reinterpret_cast<float*>(sm + OFF_UNION) + (w * ROWS + 16 * tl + c16) * MERGE_STRIDE;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        *reinterpret_cast<float4*>(part + 16 * ct + 4 * g) =
+            make_float4(accv[tl][ct][0], accv[tl][ct][1], accv[tl][ct][2], accv[tl][ct][3]);
+      if (g == 0) {
+        part[64] = mref[tl];
+        part[65] = lsum[tl][0];
+        part[66] = mn[tl];
+        part[67] = mx[tl];
+      }
+    }
+    __syncthreads();
+    // merge: thread -> (row, 4 channels), ROWS * 16 items
+    const float* base = reinterpret_cast<const float*>(sm + OFF_UNION);
+    for (int it = tid; it < ROWS * 16; it += 64 * NW) {
+      const int r = it >> 4, c4 = (it & 15) * 4;
+      float M = -INFINITY, lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float* pw = base + (ww * ROWS + r) * MERGE_STRIDE;
+        M = fmaxf(M, pw[64]);
+        lo = fminf(lo, pw[66]);
+        hi = fmaxf(hi, pw[67]);
+      }
+      float L = 0.f;
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) {
+        const float* pw = base + (ww * ROWS + r) * MERGE_STRIDE;
+        const float mw = pw[64];
+        const float f = mw > -INFINITY ? __builtin_amdgcn_exp2f((mw - M) * kTauLog2e) : 0.f;
+        L += f * pw[65];
+        const float4 v = *reinterpret_cast<const float4*>(pw + c4);
+        o.x += f * v.x;
+        o.y += f * v.y;
+        o.z += f * v.z;
+        o.w += f * v.w;
+      }
+      if (row0 + r < a.m) {
+        const float inv = 1.0f / L;
+        *reinterpret_cast<float4*>(a.vl + ((size_t)bh * a.m + row0 + r) * 64 + c4) =
+            make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+      }
+      if (c4 == 0) {
+        // capped so that fma(c, A, B) stays finite
+        const float A = hi > lo ? fminf(256.0f / (hi - lo), 1e30f) : 0.f;
+        rows[r].lo = lo;
+        rows[r].A = A;
+        rows[r].B = -lo * A;
+      }
+    }
+    __syncthreads();
+  }
+  float A[TL], B[TL];
+#pragma unroll
+  for (int tl = 0; tl < TL; ++tl) {
+    A[tl] = rows[16 * tl + c16].A;
+    B[tl] = rows[16 * tl + c16].B;
+  }
+
+  // ------------------------------------------------------------ H: histogram
+  {
+    KRegs kr;
+    if (w < nblk) load_k(kr, Kh, w, N, g, c16);
+    for (int blk = w; blk < nblk; blk += NW) {
+      const bool last = ragged && blk == nblk - 1;
+#pragma unroll
+      for (int tl = 0; tl < TL; ++tl) {
+        float s[4][4];
+        block_scores(kr, bqh[tl], bql[tl], s);
+        if (tl == TL - 1 && blk + NW < nblk) load_k(kr, Kh, blk + NW, N, g, c16);
+        uint32_t* myhist =
+            reinterpret_cast<uint32_t*>(sm + OFF_HIST + (16 * tl + c16) * HIST_STRIDE);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (!last || key_of(blk, kt, g, r) < N)
+              atomicAdd(myhist + bin_of(s[kt][r], A[tl], B[tl]), 1u);
+      }
+    }
+  }
   __syncthreads();
-  // ---- the bin holding each row's k-th best (group g of wave w: rows 4*batch + g)
-  for (int batch = 0; batch < 4; ++batch) {
-    const int r2 = 16 * w + 4 * batch + g;
-    const char* hrow = sm + L::OFF_HIST + r2 * HIST_STRIDE;
-    const u32x4 d0 = *reinterpret_cast<const u32x4*>(hrow + 32 * c16);
-    const u32x4 d1 = *reinterpret_cast<const u32x4*>(hrow + 32 * c16 + 16);
+  // the bin holding each row's k-th best: group g of wave w takes rows
+  // 4w + g + 16i
+#pragma unroll
+  for (int i = 0; i < TL; ++i) {
+    const int r = 4 * w + g + 16 * i;
+    const uint32_t* hrow = reinterpret_cast<const uint32_t*>(sm + OFF_HIST + r * HIST_STRIDE);
+    uint32_t cb[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const u32x4 d = *reinterpret_cast<const u32x4*>(hrow + 16 * c16 + 4 * q);
+      cb[4 * q] = d[0];
+      cb[4 * q + 1] = d[1];
+      cb[4 * q + 2] = d[2];
+      cb[4 * q + 3] = d[3];
+    }
     int local = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      local += (int)((d0[q] & 0xFFFFu) + (d0[q] >> 16) + (d1[q] & 0xFFFFu) + (d1[q] >> 16));
+    for (int q = 0; q < 16; ++q) local += (int)cb[q];
     const int suf = g16_suffix(local);
-    const int above = suf - local;
+    const int above_lane = suf - local;
     const int need = a.k;
-    const bool mine = above < need && need <= suf;
-    int bstar = 0;
+    const bool mine = above_lane < need && need <= suf;
+    int bstar = 0, above = 0, inbin = 0;
     if (mine) {
-      int acc = above;
+      int acc = above_lane;
       bool found = false;
 #pragma unroll
       for (int q = 15; q >= 0; --q) {
-        const uint32_t dw = (q < 8 ? d0 : d1)[(q & 7) >> 1];
-        const int cq = (q & 1) ? (int)(dw >> 16) : (int)(dw & 0xFFFFu);
+        const int cq = (int)cb[q];
         if (!found) {
           if (acc + cq >= need) {
             found = true;
             bstar = 16 * c16 + q;
+            above = acc;
+            inbin = cq;
           } else {
             acc += cq;
           }
@@ -440,105 +651,151 @@ __global__ __launch_bounds__(64 * NW) void lmk_select_kernel(Args a) {
       }
     }
     bstar = g16_addi(mine ? bstar : 0);
-    if (c16 == 0) reinterpret_cast<int*>(sm + L::OFF_BSTAR)[r2] = bstar;
+    above = g16_addi(mine ? above : 0);
+    inbin = g16_addi(mine ? inbin : 0);
+    if (c16 == 0) {
+      const bool real = row0 + r < a.m;
+      const bool over = real && above + inbin > a.cap;
+      rows[r].bstar = bstar;
+      rows[r].above = above;
+      // padding rows collect nothing
+      rows[r].bthr = !real ? INFINITY : (bstar == 0 ? -INFINITY : (float)bstar);
+      rows[r].cnt = 0;
+      rows[r].thr = -INFINITY;
+      rows[r].thrkey = 0x7FFFFFFF;
+      rows[r].over = over ? 1 : 0;
+      if (over) atomicOr(flag, 1);
+    }
   }
   __syncthreads();
-  const int mybstar = reinterpret_cast<const int*>(sm + L::OFF_BSTAR)[lr];
-  float thr = -INFINITY;
-  const int cnt_limit = a.cap - KB;
-  // ---- pass 2: collect the keys in the k-th best's bin or above
-  stream([&](int blk) {
-    float s[4][4];
-    block_scores(sm + L::OFF_K, bqh, bql, blk, N, g, c16, s);
-    bool inb[4][4];
-    bool any = false;
+
+  // ------------------------------------------------------------ C: collect
+  {
+    float bthr[TL];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+    for (int tl = 0; tl < TL; ++tl) bthr[tl] = rows[16 * tl + c16].bthr;
+    // appends the block's scores of tile tl that are in the boundary bin or
+    // above (and, when bounded, beat the admission bound (thr, thrkey))
+    auto collect = [&](const float (&s)[4][4], int tl, int blk, bool last, bool bounded,
+                       float thr, int thrkey) {
+      const int lr = 16 * tl + c16;
+      uint32_t msk = 0u;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int b = min(255, max(0, (int)((s[kt][r] - lo) * scale)));
-        inb[kt][r] = rowok && s[kt][r] > -INFINITY && b >= mybstar;
-        any |= inb[kt][r] && s[kt][r] > thr;
-      }
-    if (__ballot(any) != 0) {
-      const int* cnt = reinterpret_cast<const int*>(sm + L::OFF_CNT);
-      const bool full = rowok && cnt[lr] > cnt_limit;
-      if (__ballot(full) != 0) {
-        select_rows<NW, NV>(sm, a, bh, row0, w, g, c16, false);
-        thr = reinterpret_cast<const float*>(sm + L::OFF_THR)[lr];
-      }
-      int* cntw = reinterpret_cast<int*>(sm + L::OFF_CNT) + lr;
-      float* vals = reinterpret_cast<float*>(sm + L::OFF_BUF + (size_t)lr * a.cap * 8);
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = key_of(blk, kt, g, r);
+          const float v = s[kt][r];
+          bool q = __builtin_fmaf(v, A[tl], B[tl]) >= bthr[tl];
+          if (last) q = q && key < N;
+          if (bounded) q = q && (v > thr || (v == thr && key < thrkey));
+          msk |= (q ? 1u : 0u) << (4 * kt + r);
+        }
+      if (__ballot(msk != 0u) == 0) return;
+      // the row's four lanes (g = 0..3) take consecutive slots
+      const int c = __popc(msk);
+      const int c0 = __shfl(c, c16, 64), c1 = __shfl(c, c16 + 16, 64);
+      const int c2 = __shfl(c, c16 + 32, 64), c3 = __shfl(c, c16 + 48, 64);
+      const int total = c0 + c1 + c2 + c3;
+      const int pre = (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
+      int base = 0;
+      if (g == 0 && total > 0) base = atomicAdd(&rows[lr].cnt, total);
+      base = __shfl(base, c16, 64);
+      float* vals = reinterpret_cast<float*>(sm + OFF_UNION + (size_t)lr * a.cap * 8);
       int* keys = reinterpret_cast<int*>(vals + a.cap);
+      int pos = base + pre;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (inb[kt][r] && s[kt][r] > thr) {
-            const int pos = atomicAdd(cntw, 1);
+          if (msk >> (4 * kt + r) & 1u) {
             vals[pos] = s[kt][r];
-            keys[pos] = blk * KB + 16 * kt + 4 * g + r;
+            keys[pos] = key_of(blk, kt, g, r);
+            ++pos;
           }
+    };
+    if (flag[0] == 0) {
+      // every row's candidates fit: one streaming pass
+      KRegs kr;
+      if (w < nblk) load_k(kr, Kh, w, N, g, c16);
+      for (int blk = w; blk < nblk; blk += NW) {
+        const bool last = ragged && blk == nblk - 1;
+#pragma unroll
+        for (int tl = 0; tl < TL; ++tl) {
+          float s[4][4];
+          block_scores(kr, bqh[tl], bql[tl], s);
+          if (tl == TL - 1 && blk + NW < nblk) load_k(kr, Kh, blk + NW, N, g, c16);
+          collect(s, tl, blk, last, false, 0.f, 0);
+        }
+      }
+    } else {
+      // one block at a time (its owner wave appends, at most KB entries per
+      // row); rows that could overflow on the next block are cut back first
+      for (int blk = 0; blk < nblk; ++blk) {
+        if (blk % NW == w) {
+          const bool last = ragged && blk == nblk - 1;
+          KRegs kr;
+          load_k(kr, Kh, blk, N, g, c16);
+#pragma unroll
+          for (int tl = 0; tl < TL; ++tl) {
+            float s[4][4];
+            block_scores(kr, bqh[tl], bql[tl], s);
+            const int lr = 16 * tl + c16;
+            collect(s, tl, blk, last, true, rows[lr].thr, rows[lr].thrkey);
+          }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < TL; ++i) {
+          const int r = 4 * w + g + 16 * i;
+          const bool work = row0 + r < a.m && rows[r].over && rows[r].cnt > a.cap - KB;
+          if (__ballot(work) != 0) row_cut(sm, a, r, work, c16, g);
+        }
+        __syncthreads();
+      }
     }
-  });
+  }
   __syncthreads();
-  select_rows<NW, NV>(sm, a, bh, row0, w, g, c16, true);
+
+  // ------------------------------------------------------------ F: final
+#pragma unroll 1
+  for (int i = 0; i < TL; ++i) {
+    const int r = 4 * w + g + 16 * i;
+    const bool work = row0 + r < a.m;
+    int32_t* out = a.idx + ((size_t)bh * a.m + (work ? row0 + r : 0)) * a.k;
+    row_final(sm, a, r, work, c16, g, out);
+  }
 }
 
 }  // namespace lmk
 
-bool landmark_bf16_supported(const Shape& s) {
-  // the select kernel's per-row buffer: k kept plus one block, and room for a
-  // bitmap of N keys at the end
-  int need = s.k + 2 * lmk::KB;
-  if (need < (s.N + 63) / 64) need = (s.N + 63) / 64;
-  return s.bf16 && need <= 512;
+// The row buffer holds k plus one block of candidates (k + 64 entries, at
+// most 512: one bit each in the selection masks).
+static int landmark_cap(const Shape& s) {
+  const int cap = (s.k + lmk::KB + 15) & ~15;
+  return cap <= 512 ? cap : 0;
 }
 
-size_t landmark_minmax_bytes(const Shape& s) { return (size_t)s.BH * s.m * 2 * sizeof(float); }
-
-template <int NW, int NV>
-static hipError_t launch_select(const lmk::Args& a0, const Shape& s, hipStream_t st) {
-  lmk::Args a = a0;
-  a.cap = 16 * NV;
-  a.rblocks = (s.m + 16 * NW - 1) / (16 * NW);
-  const size_t lds = lmk::SelLayout<NW>::bytes(a.cap);
-  if (lds > 160 * 1024) return hipErrorInvalidValue;
-  static bool attr = false;
-  if (!attr) {
-    hipFuncSetAttribute((const void*)lmk::lmk_select_kernel<NW, NV>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr = true;
-  }
-  const int grid = ((s.BH + 7) / 8) * 8 * a.rblocks;
-  lmk::lmk_select_kernel<NW, NV><<<grid, 64 * NW, lds, st>>>(a);
-  return hipGetLastError();
+bool landmark_bf16_supported(const Shape& s) {
+  return s.bf16 && landmark_cap(s) > 0 && lmk::lds_bytes(landmark_cap(s)) <= 160 * 1024;
 }
 
 hipError_t launch_landmark_bf16(const float* ql, const void* K, const void* V, int32_t* idx,
-                                float* vl, float* minmax, const Shape& s, hipStream_t st) {
-  lmk::Args a{ql, (const uint16_t*)K, (const uint16_t*)V, idx, vl, minmax,
-              s.BH, s.N, s.m, s.k, 0, 0};
-  // values: 64 rows per workgroup (16 per wave)
-  {
-    constexpr int NW = 4;
-    a.rblocks = (s.m + 16 * NW - 1) / (16 * NW);
-    const int grid = ((s.BH + 7) / 8) * 8 * a.rblocks;
-    lmk::lmk_values_kernel<NW><<<grid, 64 * NW, 0, st>>>(a);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+                                float* vl, const Shape& s, hipStream_t st) {
+  lmk::Args a{ql, (const uint16_t*)K, (const uint16_t*)V, idx, vl, s.BH, s.N, s.m, s.k,
+              landmark_cap(s), (s.m + lmk::ROWS - 1) / lmk::ROWS};
+  if (a.cap == 0) return hipErrorInvalidValue;
+  const size_t lds = lmk::lds_bytes(a.cap);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  static bool attr = false;
+  if (!attr) {
+    hipFuncSetAttribute((const void*)lmk::landmark_kernel,
+                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    attr = true;
   }
-  // select: per-row buffer of k + 128 entries (one block of slack plus room
-  // for the boundary bin, so the exact cut-back is rarely needed), at least
-  // N/64 (the final bitmap); 32 rows per workgroup, 16 for big buffers
-  int need = s.k + 2 * lmk::KB;
-  if (need < (s.N + 63) / 64) need = (s.N + 63) / 64;
-  if (need <= 128) return launch_select<2, 8>(a, s, st);
-  if (need <= 192) return launch_select<2, 12>(a, s, st);
-  if (need <= 256) return launch_select<2, 16>(a, s, st);
-  if (need <= 384) return launch_select<1, 24>(a, s, st);
-  if (need <= 512) return launch_select<1, 32>(a, s, st);
-  return hipErrorInvalidValue;
+  const int grid = ((s.BH + 7) / 8) * 8 * a.tiles;
+  lmk::landmark_kernel<<<grid, 64 * lmk::NW, lds, st>>>(a);
+  return hipGetLastError();
 }
 
 }  // namespace mita

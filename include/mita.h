@@ -138,7 +138,9 @@ mita_status mita_pool(const void* Q, int B, int H, int grid_h, int grid_w, int d
 /*
  * Landmark pass: scores of ql [B,H,m,d] fp32 against K [B,H,N,d], each row's
  * top-k keys -> idx [B,H,m,k] (ascending), and the row softmax applied to V
- * -> vl [B,H,m,d] fp32.  Needs mita_landmark_workspace_bytes(...) of scratch.
+ * -> vl [B,H,m,d] fp32.  Needs mita_landmark_workspace_bytes(...) of scratch
+ * (0 for bf16 inputs with k + 256 <= 512 and N <= 32768; workspace may then
+ * be NULL).
  */
 size_t mita_landmark_workspace_bytes(int B, int H, int N, int d, int m, int k,
                                      mita_dtype in_dtype);

@@ -102,7 +102,7 @@ def test_stage_entry_points_validate():
     # fp32 inputs take the scalar landmark kernel, which needs scratch
     assert L.mita_landmark(FAKE, FAKE, FAKE, 1, 1, 196, 64, 25, 25, mita.MITA_F32, FAKE, FAKE,
                            FAKE, 4, None) == mita.MITA_ERR_WORKSPACE
-    assert L.mita_landmark_workspace_bytes(1, 1, 196, 64, 25, 25, mita.MITA_BF16) == 25 * 8
+    assert L.mita_landmark_workspace_bytes(1, 1, 196, 64, 25, 25, mita.MITA_BF16) == 0
     assert L.mita_route(FAKE, FAKE, 1, 1, 196, 64, 25, 1, FAKE, FAKE, None, FAKE, FAKE, 1 << 40,
                         None) == mita.MITA_ERR_INVALID_ARG
     assert L.mita_route(FAKE, FAKE, 1, 1, 3136, 64, 49, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 8,

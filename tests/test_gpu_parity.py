@@ -119,6 +119,32 @@ def test_exact_ties_take_lowest_index(path):
     _say(f"ok ties={ties} {rep}")
 
 
+def test_equal_scores_overflow_the_candidate_buffer():
+    """Rows whose boundary histogram bin holds more keys than the landmark
+    pass's candidate buffer (k + 256 entries).  Head 0 has Q = 0, so every
+    score and every route logit is equal and the answer is keys 0..k-1 and
+    landmark 0; head 1 has integer Q and sparse ternary K, so scores are exact
+    multiples of 1/512 that repeat many times.  idx and route must equal the
+    oracle's lowest-index picks bit for bit."""
+    import oracle.mita_oracle as O
+    B, H, gh, gw, mh, mw, k = 1, 2, 24, 32, 3, 4, 20
+    N = gh * gw
+    rng = np.random.default_rng(11)
+    Q = rng.integers(-2, 3, size=(B, H, N, 64)).astype(np.float32)
+    Q[0, 0] = 0.0
+    K = (rng.integers(-1, 2, size=(B, H, N, 64)) * (rng.random((B, H, N, 64)) < 0.1)).astype(np.float32)
+    V = synth.bf16_round(rng.standard_normal((B, H, N, 64)).astype(np.float32))
+    _say("equal scores, buffer overflow")
+    res = run_gpu(Q, K, V, "bf16", gh, gw, mh, mw, k)
+    for h in range(H):
+        ref = O.mita_head(Q[0, h], K[0, h], V[0, h], gh, gw, mh, mw, k)
+        assert np.array_equal(res["idx"][0, h], ref["idx"]), h
+        assert np.array_equal(res["route"][0, h], ref["route"]), h
+    assert np.array_equal(res["idx"][0, 0], np.tile(np.arange(k), (mh * mw, 1)))
+    rep = parity.run_and_check(res, Q, K, V, gh, gw, mh, mw, k, TOL["bf16"])
+    _say(f"ok {rep}")
+
+
 @pytest.mark.parametrize("name", ["tiny-fp32", "deit-t", "deit-s", "hires-3136"])
 def test_workload_full(name):
     w = synth.workload(name)
