@@ -3,18 +3,24 @@
 // grouped by route attend their expert's k raw key/value pairs and the m
 // shared ones under one softmax; partial results merge by online softmax).
 //
-// Persistent workgroups, several per head, placed on the head's XCD so the
-// head's K, V and Q rows are re-read from that XCD's L2.  Per workgroup:
-//   * stage the head's Q_L (bf16 hi + lo) and V_L^T (f16) once;
-//   * derive the tile list from the group offsets: tiles of <= 64 queries of
-//     one expert; the workgroup takes tiles p, p + P, ...;
-//   * per tile, each wave owns 16 queries: Q rows are the B operand of
-//     logits^T = [Q_L; K_e] Q^T; an online softmax runs over 32-entry chunks
-//     (shared entries first, then the expert's keys), and each chunk's weights
-//     go straight from the logit accumulators into out^T += [V_L; V_e]^T P^T
-//     on f16 MFMA, with the normaliser from an all-ones MFMA;
-//   * the expert's K rows (bf16) and V rows (f16, transposed) are gathered
-//     into LDS 64 slots at a time and shared by the four waves.
+// Persistent workgroups, P per head, placed on the head's XCD so the head's
+// K, V and Q rows are re-read from that XCD's L2.  Workgroup p of a head takes
+// experts p, p + P, ...  Per workgroup:
+//   * load its experts' table (query range, key ids, first 64 query ids)
+//     and the head's Q_L (bf16 hi + lo) and V_L^T (f16) into LDS once;
+//   * per expert: its k key rows (bf16) and value rows (f16, transposed) sit
+//     in LDS, shared by the four waves.  While one expert is computed the
+//     next one's rows (and the Q rows of its first 64 queries) are already
+//     loading into registers; the expert's output stores are issued only
+//     after those rows have been waited for, since stores and loads drain
+//     through one counter.  For k > 64 the slots past the first 64 are
+//     gathered in place, 64 at a time;
+//   * per pass of <= 64 of the expert's queries, each wave owns 16: Q rows
+//     are the B operand of logits^T = [Q_L; K_e] Q^T; an online softmax runs
+//     over 32-entry chunks (shared entries first, then the expert's keys), and
+//     each chunk's weights go straight from the logit accumulators into
+//     out^T += [V_L; V_e]^T P^T on f16 MFMA, with the normaliser from an
+//     all-ones MFMA.
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
@@ -22,7 +28,7 @@
 namespace mita {
 namespace att {
 
-constexpr int TQ = 64;    // queries per tile (16 per wave)
+constexpr int TQ = 64;    // queries per pass (16 per wave)
 constexpr int EC = 64;    // expert slots per LDS chunk
 constexpr int EVT_STRIDE = EC * 2 + 16;
 constexpr int MAXM = 256;
@@ -39,22 +45,26 @@ struct Args {
   const int32_t* offsets;
   const int32_t* perm;
   float* out;
-  int BH, N, m, k, parts;
+  int BH, N, m, k, parts;  // workgroups per head
 };
 
+// LDS layout; the expert table holds, per expert of the workgroup,
+// [q0, count, k key ids, first TQ query ids].
 struct Lay {
-  int mp, vlt_stride;
-  int off_qlh, off_qll, off_vlt, off_ke, off_vet, off_tstart, bytes;
-  __host__ __device__ Lay(int m) {
+  int mp, vlt_stride, ew, ts;
+  int off_qlh, off_qll, off_vlt, off_ke, off_vet, off_tab, bytes;
+  __host__ __device__ Lay(int m, int k, int parts) {
     mp = (m + 31) & ~31;
     vlt_stride = mp * 2 + 16;
+    ew = (m + parts - 1) / parts;
+    ts = 2 + k + TQ;
     off_qlh = 0;
     off_qll = off_qlh + mp * 128;
     off_vlt = off_qll + mp * 128;
     off_ke = off_vlt + 64 * vlt_stride;
     off_vet = off_ke + EC * 128;
-    off_tstart = off_vet + 64 * EVT_STRIDE;
-    bytes = off_tstart + (MAXM + 1) * 4;
+    off_tab = off_vet + 64 * EVT_STRIDE;
+    bytes = off_tab + ew * ts * 4;
   }
 };
 
@@ -81,18 +91,57 @@ __device__ __forceinline__ void chunk_update(const float (&x)[8], const u32x4 (&
   lsum = mfma_f16(ones, bp, lsum * alpha);
 }
 
-__global__ __launch_bounds__(256) void attend_bf16_kernel(Args a) {
+// A pass's result for this lane's query, written to out row nq when live.
+struct PassOut {
+  f32x4 acc[4];
+  float inv;
+  int nq;
+  bool live;
+};
+
+__device__ __forceinline__ void store_out(float* outh, const PassOut& o, int g) {
+  if (!o.live) return;
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+    *reinterpret_cast<float4*>(outh + (size_t)o.nq * 64 + 16 * ct + 4 * g) =
+        make_float4(o.acc[ct][0] * o.inv, o.acc[ct][1] * o.inv, o.acc[ct][2] * o.inv,
+                    o.acc[ct][3] * o.inv);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void attend_bf16_kernel(Args a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
-  const Lay L(a.m);
+  const Lay L(a.m, a.k, a.parts);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
   const int bh = xcd + 8 * (slot / a.parts), part = slot % a.parts;
-  if (bh >= a.BH) return;
-  const int N = a.N, m = a.m, k = a.k;
+  if (bh >= a.BH || part >= a.m) return;
+  const int N = a.N, m = a.m, k = a.k, P = a.parts;
+  const int nexp = (m - part + P - 1) / P;  // this workgroup's experts
   const float cs = 0.125f * 1.4426950408889634f;  // tau * log2(e)
+  const uint16_t* Qh = a.Q + (size_t)bh * N * 64;
+  const uint16_t* Kh = a.K + (size_t)bh * N * 64;
+  const uint16_t* Vh = a.V + (size_t)bh * N * 64;
+  const int32_t* offs = a.offsets + (size_t)bh * (m + 1);
+  const int32_t* permh = a.perm + (size_t)bh * N;
+  const int32_t* idxh = a.idx + (size_t)bh * m * k;
+  float* outh = a.out + (size_t)bh * N * 64;
+  int* tab = reinterpret_cast<int*>(sm + L.off_tab);
+  const u32x4 z = {0u, 0u, 0u, 0u};
 
-  // ---- stage Q_L (hi / lo) and V_L^T for the head; rows past m are zero
+  // ---- the experts' table
+  for (int it = tid; it < nexp * L.ts; it += 256) {
+    const int j = it / L.ts, o = it - j * L.ts, e = part + j * P;
+    const int q0 = offs[e], cnt = offs[e + 1] - q0;
+    int v;
+    if (o == 0) v = q0;
+    else if (o == 1) v = cnt;
+    else if (o < 2 + k) v = idxh[(size_t)e * k + (o - 2)];
+    else v = o - 2 - k < cnt ? permh[q0 + (o - 2 - k)] : -1;
+    tab[it] = v;
+  }
+  // ---- Q_L (hi / lo) and V_L^T for the head; rows past m are zero
   for (int it = tid; it < L.mp * 16; it += 256) {
     const int row = it >> 4, q4 = it & 15;
     float4 f = make_float4(0.f, 0.f, 0.f, 0.f), v = f;
@@ -116,47 +165,54 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(Args a) {
       *reinterpret_cast<uint16_t*>(sm + L.off_vlt + (4 * q4 + i) * L.vlt_stride + 2 * row) =
           (uint16_t)f16_bits(vv[i]);
   }
-  // ---- tile list: expert e owns tiles tstart[e] .. tstart[e+1]-1
-  const int32_t* offs = a.offsets + (size_t)bh * (m + 1);
-  int* tstart = reinterpret_cast<int*>(sm + L.off_tstart);
-  if (tid == 0) {
-    int run = 0;
-    for (int e = 0; e < m; ++e) {
-      tstart[e] = run;
-      run += (offs[e + 1] - offs[e] + TQ - 1) / TQ;
-    }
-    tstart[m] = run;
-  }
   __syncthreads();
-  const int ntiles = tstart[m];
-  const uint16_t* Qh = a.Q + (size_t)bh * N * 64;
-  const uint16_t* Kh = a.K + (size_t)bh * N * 64;
-  const uint16_t* Vh = a.V + (size_t)bh * N * 64;
-  const int32_t* permh = a.perm + (size_t)bh * N;
-  float* outh = a.out + (size_t)bh * N * 64;
 
-  for (int t = part; t < ntiles; t += a.parts) {
-    // expert of tile t: the last e with tstart[e] <= t (binary search)
-    int lo = 0, hi = m - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (tstart[mid] <= t) lo = mid; else hi = mid - 1;
+  // gather items of this thread: K rows (slots tid>>3 and +32, chunk tid&7)
+  // and the V slot pair (2p, 2p+1) of chunk c
+  const int ksl = tid >> 3, kc = tid & 7;
+  const int vp = tid & 31, vc = tid >> 5;
+  struct Rows {
+    u32x4 k0, k1, v0, v1, q0r, q1r;
+  };
+  // rows of slots [s0, s0 + 64) of expert j, and (s0 == 0) the Q row of this
+  // lane's first-pass query
+  auto load_rows = [&](int j, int s0, Rows& r) {
+    const int* te = tab + j * L.ts;
+    const int* ke = te + 2;
+    const int a0 = s0 + ksl, a1 = a0 + 32, b0 = s0 + 2 * vp, b1 = b0 + 1;
+    r.k0 = a0 < k ? *reinterpret_cast<const u32x4*>(Kh + (size_t)ke[a0] * 64 + 8 * kc) : z;
+    r.k1 = a1 < k ? *reinterpret_cast<const u32x4*>(Kh + (size_t)ke[a1] * 64 + 8 * kc) : z;
+    r.v0 = b0 < k ? *reinterpret_cast<const u32x4*>(Vh + (size_t)ke[b0] * 64 + 8 * vc) : z;
+    r.v1 = b1 < k ? *reinterpret_cast<const u32x4*>(Vh + (size_t)ke[b1] * 64 + 8 * vc) : z;
+    if (s0 == 0) {
+      const int n = max(te[2 + k + 16 * w + c16], 0);
+      r.q0r = *reinterpret_cast<const u32x4*>(Qh + (size_t)n * 64 + 8 * g);
+      r.q1r = *reinterpret_cast<const u32x4*>(Qh + (size_t)n * 64 + 32 + 8 * g);
     }
-    const int e = lo;
-    const int q0 = offs[e] + (t - tstart[e]) * TQ;
-    const int len = min(TQ, offs[e + 1] - q0);
-    const int32_t* keys_e = a.idx + ((size_t)bh * m + e) * k;
-    // this lane's query (column c16 of wave w's 16)
-    const int qi = 16 * w + c16;
-    const bool live = qi < len;
-    const bool wave_has = 16 * w < len;
-    const int n = live ? permh[q0 + qi] : 0;
-    const u32x4 bq0 = *reinterpret_cast<const u32x4*>(Qh + (size_t)n * 64 + 8 * g);
-    const u32x4 bq1 = *reinterpret_cast<const u32x4*>(Qh + (size_t)n * 64 + 32 + 8 * g);
-    float mx = -INFINITY;
-    f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
-    f32x4 lsum = zero4();
+  };
+  auto store_rows = [&](const Rows& r) {
+    *reinterpret_cast<u32x4*>(sm + L.off_ke + rc(ksl, kc)) = r.k0;
+    *reinterpret_cast<u32x4*>(sm + L.off_ke + rc(ksl + 32, kc)) = r.k1;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t x0 = (r.v0[q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
+      const uint32_t x1 = (r.v1[q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
+      *reinterpret_cast<uint32_t*>(sm + L.off_vet + (8 * vc + q) * EVT_STRIDE + 4 * vp) =
+          pk_f16(bf16_bits_to_f32(x0), bf16_bits_to_f32(x1));
+    }
+  };
 
+  // one pass over <= 64 queries of expert j starting at p0
+  auto run_pass = [&](int j, int p0, int nq, const u32x4 bq0, const u32x4 bq1) {
+    const int* te = tab + j * L.ts;
+    const int cnt = te[1];
+    const int qi = p0 + 16 * w + c16;
+    const bool wave_has = p0 + 16 * w < cnt;
+    float mx = -INFINITY;
+    PassOut o;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) o.acc[ct] = zero4();
+    f32x4 lsum = zero4();
     // ---- shared entries: landmarks, 32 at a time
     if (wave_has) {
       for (int c = 0; c < L.mp / 32; ++c) {
@@ -185,36 +241,19 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(Args a) {
           const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vr + (32 * c + 16 + 4 * g) * 2);
           av[ct] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
         }
-        chunk_update(x, av, mx, acc, lsum);
+        chunk_update(x, av, mx, o.acc, lsum);
       }
     }
-    // ---- routed entries: the expert's keys, gathered 64 slots at a time
+    // ---- routed entries: the expert's keys, 64 slots per LDS chunk
     for (int s0 = 0; s0 < k; s0 += EC) {
-      __syncthreads();  // the previous chunk's readers are done
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int id = tid + 256 * i, sl = id >> 3, c = id & 7;
-        const bool ok = s0 + sl < k;
-        const int key = ok ? keys_e[s0 + sl] : 0;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        *reinterpret_cast<u32x4*>(sm + L.off_ke + rc(sl, c)) =
-            ok ? *reinterpret_cast<const u32x4*>(Kh + (size_t)key * 64 + 8 * c) : z;
+      if (k > EC && (s0 > 0 || p0 > 0)) {
+        // slots past the first 64, or a later pass over a multi-chunk expert
+        __syncthreads();  // the previous chunk's readers are done
+        Rows r;
+        load_rows(j, s0, r);
+        store_rows(r);
+        __syncthreads();
       }
-      {
-        const int p = tid & 31, c = tid >> 5;  // slot pair (2p, 2p+1), 8-channel chunk
-        const bool ok0 = s0 + 2 * p < k, ok1 = s0 + 2 * p + 1 < k;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        const u32x4 v0 = ok0 ? *reinterpret_cast<const u32x4*>(Vh + (size_t)keys_e[s0 + 2 * p] * 64 + 8 * c) : z;
-        const u32x4 v1 = ok1 ? *reinterpret_cast<const u32x4*>(Vh + (size_t)keys_e[s0 + 2 * p + 1] * 64 + 8 * c) : z;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const uint32_t x0 = (v0[q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
-          const uint32_t x1 = (v1[q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
-          *reinterpret_cast<uint32_t*>(sm + L.off_vet + (8 * c + q) * EVT_STRIDE + 4 * p) =
-              pk_f16(bf16_bits_to_f32(x0), bf16_bits_to_f32(x1));
-        }
-      }
-      __syncthreads();
       if (wave_has) {
         for (int hs = 0; hs < 2 && s0 + 32 * hs < k; ++hs) {
           float x[8];
@@ -238,41 +277,83 @@ __global__ __launch_bounds__(256) void attend_bf16_kernel(Args a) {
             const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vr + (32 * hs + 16 + 4 * g) * 2);
             av[ct] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
           }
-          chunk_update(x, av, mx, acc, lsum);
+          chunk_update(x, av, mx, o.acc, lsum);
         }
       }
     }
-    if (live) {
-      const float inv = 1.0f / lsum[0];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        *reinterpret_cast<float4*>(outh + (size_t)n * 64 + 16 * ct + 4 * g) =
-            make_float4(acc[ct][0] * inv, acc[ct][1] * inv, acc[ct][2] * inv, acc[ct][3] * inv);
+    o.live = qi < cnt;
+    o.nq = nq;
+    o.inv = 1.0f / lsum[0];
+    return o;
+  };
+
+  Rows rows;
+  if (nexp > 0) load_rows(0, 0, rows);
+  PassOut pending;
+  pending.live = false;
+  for (int j = 0; j < nexp; ++j) {
+    const int* te = tab + j * L.ts;
+    const int q0 = te[0], cnt = te[1];
+    store_rows(rows);  // waits for this expert's rows (and the stores before them)
+    const u32x4 bq0 = rows.q0r, bq1 = rows.q1r;
+    // take the Q rows now too: a wait after the stores below would also wait
+    // for the stores
+    asm volatile("" ::"v"(bq0), "v"(bq1));
+    store_out(outh, pending, g);  // the previous expert's last pass
+    pending.live = false;
+    if (j + 1 < nexp) load_rows(j + 1, 0, rows);
+    __syncthreads();
+    if (cnt > 0) {
+      const int n0 = te[2 + k + 16 * w + c16];
+      PassOut o = run_pass(j, 0, max(n0, 0), bq0, bq1);
+      for (int p0 = TQ; p0 < cnt; p0 += TQ) {
+        // later passes: query ids and Q rows straight from global memory
+        store_out(outh, o, g);
+        const int qi = p0 + 16 * w + c16;
+        const int nq = qi < cnt ? permh[q0 + qi] : 0;
+        const u32x4 b0 = *reinterpret_cast<const u32x4*>(Qh + (size_t)nq * 64 + 8 * g);
+        const u32x4 b1 = *reinterpret_cast<const u32x4*>(Qh + (size_t)nq * 64 + 32 + 8 * g);
+        o = run_pass(j, p0, nq, b0, b1);
+      }
+      pending = o;
     }
+    __syncthreads();  // readers of this expert's rows are done
   }
+  store_out(outh, pending, g);
 }
 
 }  // namespace att
 
-bool attend_bf16_supported(const Shape& s) { return s.bf16 && s.m <= att::MAXM; }
+bool attend_bf16_supported(const Shape& s) {
+  return s.bf16 && s.m <= att::MAXM;
+}
+
+static int attend_parts(const Shape& s) {
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) == hipSuccess)
+    hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  // about three resident workgroups per CU in total, at least one per head,
+  // at most one per expert
+  int parts = (3 * ncu + s.BH - 1) / s.BH;
+  if (parts > s.m) parts = s.m;
+  if (parts < 1) parts = 1;
+  return parts;
+}
 
 hipError_t launch_attend_bf16(const void* Q, const void* K, const void* V, const float* ql,
                               const float* vl, const int32_t* idx, const int32_t* offsets,
                               const int32_t* perm, float* out, const Shape& s, hipStream_t st) {
-  const att::Lay L(s.m);
+  int parts = attend_parts(s);
+  // the table must fit next to the rest: fewer experts per workgroup if not
+  while (att::Lay(s.m, s.k, parts).bytes > 160 * 1024 && parts < s.m) ++parts;
+  const att::Lay L(s.m, s.k, parts);
+  if (L.bytes > 160 * 1024) return hipErrorInvalidValue;
   static bool attr = false;
   if (!attr) {
     hipFuncSetAttribute((const void*)att::attend_bf16_kernel,
                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr = true;
   }
-  int dev = 0, ncu = 256;
-  if (hipGetDevice(&dev) == hipSuccess)
-    hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-  // about six workgroups per CU in total (several resident per CU keep more
-  // gathers in flight), at least one per head
-  int parts = (6 * ncu + s.BH - 1) / s.BH;
-  if (parts < 1) parts = 1;
   att::Args a{(const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, ql, vl, idx, offsets,
               perm, out, s.BH, s.N, s.m, s.k, parts};
   const int grid = ((s.BH + 7) / 8) * 8 * parts;
