@@ -68,27 +68,43 @@ struct Lay {
   }
 };
 
-// One 32-entry chunk of the online softmax for this lane's query column.
-// x: base-2 logits of entries {4g+r, 16+4g+r} (-inf when masked); av: the
-// chunk's A fragments of [V_L; V_e]^T for the four channel tiles.
-__device__ __forceinline__ void chunk_update(const float (&x)[8], const u32x4 (&av)[4], float& mx,
-                                             f32x4 (&acc)[4], f32x4& lsum) {
+// One softmax update over NC 32-entry chunks for this lane's query column.
+// x: raw logits (q . key) of entries {32i + 4g + r, 32i + 16 + 4g + r}
+// (-inf when masked); get_av(i, av) fetches chunk i's A fragments of
+// [V_L; V_e]^T for the four channel tiles.  Weights are exp2((x - mref) tau log2e) against a
+// reference maximum that is only raised when some weight would exceed 2^8,
+// so most updates skip rescaling the accumulators.
+template <int NC, class GetAv>
+__device__ __forceinline__ void softmax_update(const float (&x)[8 * NC], GetAv get_av,
+                                               float& mref, f32x4 (&acc)[4], f32x4& lsum) {
+  constexpr float cs = 0.125f * 1.4426950408889634f;  // tau * log2(e)
   float cm = x[0];
 #pragma unroll
-  for (int i = 1; i < 8; ++i) cm = fmaxf(cm, x[i]);
-  cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
-  cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
-  const float mnew = fmaxf(mx, cm);
-  const float alpha = __builtin_amdgcn_exp2f(mx - mnew);
-  mx = mnew;
-  float p[8];
+  for (int i = 1; i < 8 * NC; ++i) cm = fmaxf(cm, x[i]);
+  if (__ballot((cm - mref) * cs > 8.0f) != 0) {
+    cm = fmaxf(cm, __shfl_xor(cm, 16, 64));
+    cm = fmaxf(cm, __shfl_xor(cm, 32, 64));
+    const float mnew = fmaxf(mref, cm);
+    const float alpha = __builtin_amdgcn_exp2f((mref - mnew) * cs);
+    mref = mnew;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - mnew);
-  const u32x4 bp = {pk_f16(p[0], p[1]), pk_f16(p[2], p[3]), pk_f16(p[4], p[5]), pk_f16(p[6], p[7])};
+    for (int ct = 0; ct < 4; ++ct) acc[ct] = acc[ct] * alpha;
+    lsum = lsum * alpha;
+  }
+  const float moff = -mref * cs;
   const u32x4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) acc[ct] = mfma_f16(av[ct], bp, acc[ct] * alpha);
-  lsum = mfma_f16(ones, bp, lsum * alpha);
+  for (int i = 0; i < NC; ++i) {
+    float p[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[8 * i + r], cs, moff));
+    const u32x4 bp = {pk_f16(p[0], p[1]), pk_f16(p[2], p[3]), pk_f16(p[4], p[5]), pk_f16(p[6], p[7])};
+    u32x4 av[4];
+    get_av(i, av);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[ct] = mfma_f16(av[ct], bp, acc[ct]);
+    lsum = mfma_f16(ones, bp, lsum);
+  }
 }
 
 // A pass's result for this lane's query, written to out row nq when live.
@@ -119,7 +135,6 @@ void attend_bf16_kernel(Args a) {
   if (bh >= a.BH || part >= a.m) return;
   const int N = a.N, m = a.m, k = a.k, P = a.parts;
   const int nexp = (m - part + P - 1) / P;  // this workgroup's experts
-  const float cs = 0.125f * 1.4426950408889634f;  // tau * log2(e)
   const uint16_t* Qh = a.Q + (size_t)bh * N * 64;
   const uint16_t* Kh = a.K + (size_t)bh * N * 64;
   const uint16_t* Vh = a.V + (size_t)bh * N * 64;
@@ -130,16 +145,40 @@ void attend_bf16_kernel(Args a) {
   int* tab = reinterpret_cast<int*>(sm + L.off_tab);
   const u32x4 z = {0u, 0u, 0u, 0u};
 
-  // ---- the experts' table
-  for (int it = tid; it < nexp * L.ts; it += 256) {
-    const int j = it / L.ts, o = it - j * L.ts, e = part + j * P;
-    const int q0 = offs[e], cnt = offs[e + 1] - q0;
-    int v;
-    if (o == 0) v = q0;
-    else if (o == 1) v = cnt;
-    else if (o < 2 + k) v = idxh[(size_t)e * k + (o - 2)];
-    else v = o - 2 - k < cnt ? permh[q0 + (o - 2 - k)] : -1;
-    tab[it] = v;
+  // ---- the experts' table: query ranges first, then key ids and first
+  // query ids with every load of a thread issued before any is used
+  if (tid < nexp) {
+    const int e = part + tid * P;
+    const int q0 = offs[e];
+    tab[tid * L.ts] = q0;
+    tab[tid * L.ts + 1] = offs[e + 1] - q0;
+  }
+  __syncthreads();
+  {
+    constexpr int U = 8;
+    const int total = nexp * L.ts;
+    for (int base = 0; base < total; base += 256 * U) {
+      int v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int it = base + 256 * u + tid;
+        v[u] = -1;
+        if (it < total) {
+          const int j = it / L.ts, o = it - j * L.ts, e = part + j * P;
+          if (o >= 2 && o < 2 + k) {
+            v[u] = idxh[(size_t)e * k + (o - 2)];
+          } else if (o >= 2 + k) {
+            const int q0 = tab[j * L.ts], cnt = tab[j * L.ts + 1];
+            if (o - 2 - k < cnt) v[u] = permh[q0 + (o - 2 - k)];
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int it = base + 256 * u + tid;
+        if (it < total && it - (it / L.ts) * L.ts >= 2) tab[it] = v[u];
+      }
+    }
   }
   // ---- Q_L (hi / lo) and V_L^T for the head; rows past m are zero
   for (int it = tid; it < L.mp * 16; it += 256) {
@@ -202,46 +241,97 @@ void attend_bf16_kernel(Args a) {
     }
   };
 
+  // logits of 32 shared entries (landmarks 32c ..) into x[0..8)
+  auto shared_logits = [&](int c, const u32x4 bq0, const u32x4 bq1, float* x) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 32 * c + 16 * h + c16;
+      const u32x4 ah0 = *reinterpret_cast<const u32x4*>(sm + L.off_qlh + rc(row, g));
+      const u32x4 al0 = *reinterpret_cast<const u32x4*>(sm + L.off_qll + rc(row, g));
+      const u32x4 ah1 = *reinterpret_cast<const u32x4*>(sm + L.off_qlh + rc(row, 4 + g));
+      const u32x4 al1 = *reinterpret_cast<const u32x4*>(sm + L.off_qll + rc(row, 4 + g));
+      f32x4 s = zero4();
+      s = mfma_bf16(ah0, bq0, s);
+      s = mfma_bf16(al0, bq0, s);
+      s = mfma_bf16(ah1, bq1, s);
+      s = mfma_bf16(al1, bq1, s);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[4 * h + r] = s[r];
+    }
+    if (32 * c + 32 > m) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (32 * c + 16 * h + 4 * g + r >= m) x[4 * h + r] = -INFINITY;
+    }
+  };
+  auto shared_av = [&](int c, u32x4 (&av)[4]) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const char* vr = sm + L.off_vlt + (16 * ct + c16) * L.vlt_stride;
+      const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vr + (32 * c + 4 * g) * 2);
+      const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vr + (32 * c + 16 + 4 * g) * 2);
+      av[ct] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+    }
+  };
+  // logits of 32 routed entries (LDS slots 32hs .., expert slots s0 + 32hs ..)
+  auto routed_logits = [&](int s0, int hs, const u32x4 bq0, const u32x4 bq1, float* x) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 32 * hs + 16 * h + c16;
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(sm + L.off_ke + rc(row, g));
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(sm + L.off_ke + rc(row, 4 + g));
+      f32x4 s = zero4();
+      s = mfma_bf16(a0, bq0, s);
+      s = mfma_bf16(a1, bq1, s);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[4 * h + r] = s[r];
+    }
+    if (s0 + 32 * hs + 32 > k) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (s0 + 32 * hs + 16 * h + 4 * g + r >= k) x[4 * h + r] = -INFINITY;
+    }
+  };
+  auto routed_av = [&](int hs, u32x4 (&av)[4]) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const char* vr = sm + L.off_vet + (16 * ct + c16) * EVT_STRIDE;
+      const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vr + (32 * hs + 4 * g) * 2);
+      const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vr + (32 * hs + 16 + 4 * g) * 2);
+      av[ct] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+    }
+  };
+
   // one pass over <= 64 queries of expert j starting at p0
   auto run_pass = [&](int j, int p0, int nq, const u32x4 bq0, const u32x4 bq1) {
     const int* te = tab + j * L.ts;
     const int cnt = te[1];
     const int qi = p0 + 16 * w + c16;
     const bool wave_has = p0 + 16 * w < cnt;
-    float mx = -INFINITY;
+    float mref = -INFINITY;
     PassOut o;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) o.acc[ct] = zero4();
     f32x4 lsum = zero4();
-    // ---- shared entries: landmarks, 32 at a time
+    // ---- shared entries: landmarks, 64 per softmax update
     if (wave_has) {
-      for (int c = 0; c < L.mp / 32; ++c) {
+      const int nc = L.mp / 32;
+      int c = 0;
+      for (; c + 2 <= nc; c += 2) {
+        float x[16];
+        shared_logits(c, bq0, bq1, x);
+        shared_logits(c + 1, bq0, bq1, x + 8);
+        softmax_update<2>(x, [&](int i, u32x4 (&av)[4]) { shared_av(c + i, av); }, mref, o.acc,
+                          lsum);
+      }
+      if (c < nc) {
         float x[8];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int row = 32 * c + 16 * h + c16;
-          const u32x4 ah0 = *reinterpret_cast<const u32x4*>(sm + L.off_qlh + rc(row, g));
-          const u32x4 al0 = *reinterpret_cast<const u32x4*>(sm + L.off_qll + rc(row, g));
-          const u32x4 ah1 = *reinterpret_cast<const u32x4*>(sm + L.off_qlh + rc(row, 4 + g));
-          const u32x4 al1 = *reinterpret_cast<const u32x4*>(sm + L.off_qll + rc(row, 4 + g));
-          f32x4 s = zero4();
-          s = mfma_bf16(ah0, bq0, s);
-          s = mfma_bf16(al0, bq0, s);
-          s = mfma_bf16(ah1, bq1, s);
-          s = mfma_bf16(al1, bq1, s);
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            x[4 * h + r] = (32 * c + 16 * h + 4 * g + r) < m ? s[r] * cs : -INFINITY;
-        }
-        u32x4 av[4];
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          const char* vr = sm + L.off_vlt + (16 * ct + c16) * L.vlt_stride;
-          const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vr + (32 * c + 4 * g) * 2);
-          const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vr + (32 * c + 16 + 4 * g) * 2);
-          av[ct] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-        }
-        chunk_update(x, av, mx, o.acc, lsum);
+        shared_logits(c, bq0, bq1, x);
+        softmax_update<1>(x, [&](int, u32x4 (&av)[4]) { shared_av(c, av); }, mref, o.acc, lsum);
       }
     }
     // ---- routed entries: the expert's keys, 64 slots per LDS chunk
@@ -255,29 +345,16 @@ void attend_bf16_kernel(Args a) {
         __syncthreads();
       }
       if (wave_has) {
-        for (int hs = 0; hs < 2 && s0 + 32 * hs < k; ++hs) {
+        if (s0 + 32 < k) {
+          float x[16];
+          routed_logits(s0, 0, bq0, bq1, x);
+          routed_logits(s0, 1, bq0, bq1, x + 8);
+          softmax_update<2>(x, [&](int i, u32x4 (&av)[4]) { routed_av(i, av); }, mref, o.acc,
+                            lsum);
+        } else {
           float x[8];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int row = 32 * hs + 16 * h + c16;
-            const u32x4 a0 = *reinterpret_cast<const u32x4*>(sm + L.off_ke + rc(row, g));
-            const u32x4 a1 = *reinterpret_cast<const u32x4*>(sm + L.off_ke + rc(row, 4 + g));
-            f32x4 s = zero4();
-            s = mfma_bf16(a0, bq0, s);
-            s = mfma_bf16(a1, bq1, s);
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              x[4 * h + r] = (s0 + 32 * hs + 16 * h + 4 * g + r) < k ? s[r] * cs : -INFINITY;
-          }
-          u32x4 av[4];
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct) {
-            const char* vr = sm + L.off_vet + (16 * ct + c16) * EVT_STRIDE;
-            const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vr + (32 * hs + 4 * g) * 2);
-            const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vr + (32 * hs + 16 + 4 * g) * 2);
-            av[ct] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-          }
-          chunk_update(x, av, mx, o.acc, lsum);
+          routed_logits(s0, 0, bq0, bq1, x);
+          softmax_update<1>(x, [&](int, u32x4 (&av)[4]) { routed_av(0, av); }, mref, o.acc, lsum);
         }
       }
     }

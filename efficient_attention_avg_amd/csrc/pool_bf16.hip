@@ -26,13 +26,21 @@ __global__ __launch_bounds__(256) void pool_bf16_kernel(const uint16_t* __restri
   for (int it = tid; it < gw * 8; it += blockDim.x) {
     const int x = it >> 3, c = it & 7;
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int y = y0; y < y1; ++y) {
-      const uint4 v = *reinterpret_cast<const uint4*>(q + (size_t)(y * gw + x) * kHeadDim + 8 * c);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    // eight rows' loads in flight at a time
+    for (int y = y0; y < y1; y += 8) {
+      uint4 v[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[2 * i] += __uint_as_float(w[i] << 16);
-        a[2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
+      for (int u = 0; u < 8; ++u)
+        if (y + u < y1) v[u] = *reinterpret_cast<const uint4*>(q + (size_t)((y + u) * gw + x) * kHeadDim + 8 * c);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (y + u >= y1) break;
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          a[2 * i] += __uint_as_float(w[i] << 16);
+          a[2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
+        }
       }
     }
     float4* dst = reinterpret_cast<float4*>(colsum + x * kHeadDim + 8 * c);

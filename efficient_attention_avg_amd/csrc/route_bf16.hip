@@ -39,6 +39,19 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(const uint16_t* __restr
   char* qlh = sm;
   char* qll = sm + mt * 16 * 128;
   int* hist = reinterpret_cast<int*>(sm + 2 * mt * 16 * 128);
+  const uint16_t* Qh = Q + (size_t)bh * N * 64;
+  // this wave's four 16-query tiles: every Q row load is issued up front
+  constexpr int TPW = QC / 16 / 4;
+  u32x4 qb[TPW][2];
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int n = chunk * QC + 16 * (w + 4 * i) + c16;
+      qb[i][0] = n < N ? *reinterpret_cast<const u32x4*>(Qh + (size_t)n * 64 + 8 * g) : z;
+      qb[i][1] = n < N ? *reinterpret_cast<const u32x4*>(Qh + (size_t)n * 64 + 32 + 8 * g) : z;
+    }
+  }
   // stage Q_L (rows past m are zero) as bf16 hi / lo, 128-byte swizzled rows
   for (int it = tid; it < mt * 16 * 16; it += 256) {
     const int row = it >> 4, q4 = it & 15;  // 4 channels per item
@@ -57,13 +70,12 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(const uint16_t* __restr
   }
   for (int e = tid; e < m; e += 256) hist[e] = 0;
   __syncthreads();
-  const uint16_t* Qh = Q + (size_t)bh * N * 64;
-  for (int tt = w; tt < QC / 16; tt += 4) {
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int tt = w + 4 * i;
     const int n = chunk * QC + 16 * tt + c16;  // this lane's query column
     const bool ok = n < N;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const u32x4 b0 = ok ? *reinterpret_cast<const u32x4*>(Qh + (size_t)n * 64 + 8 * g) : z;
-    const u32x4 b1 = ok ? *reinterpret_cast<const u32x4*>(Qh + (size_t)n * 64 + 32 + 8 * g) : z;
+    const u32x4 b0 = qb[i][0], b1 = qb[i][1];
     float best = -INFINITY;
     int bi = 0;
     for (int lt = 0; lt < mt; ++lt) {
@@ -100,7 +112,7 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(const uint16_t* __restr
   for (int e = tid; e < m; e += 256) dst[e] = hist[e];
 }
 
-__global__ __launch_bounds__(256) void group_bf16_kernel(const int32_t* __restrict__ route,
+__global__ __launch_bounds__(1024) void group_bf16_kernel(const int32_t* __restrict__ route,
                                                          const int32_t* __restrict__ chist,
                                                          int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets,
@@ -110,13 +122,18 @@ __global__ __launch_bounds__(256) void group_bf16_kernel(const int32_t* __restri
   int* cur = gsm;                   // [nchunks][m]: next free position per chunk/expert
   int* tot = gsm + nchunks * m;     // [m]
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nt = blockDim.x, nw = nt >> 6;
   const int32_t* ch = chist + (size_t)bh * nchunks * m;
-  // per-expert totals, and each chunk's count before it
-  for (int e = tid; e < m; e += 256) {
+  // the chunk histograms into LDS in one coalesced sweep (independent loads),
+  // then per expert: totals and each chunk's count before it
+  for (int it = tid; it < nchunks * m; it += nt) cur[it] = ch[it];
+  __syncthreads();
+  for (int e = tid; e < m; e += nt) {
     int run = 0;
     for (int c = 0; c < nchunks; ++c) {
+      const int v = cur[c * m + e];
       cur[c * m + e] = run;
-      run += ch[(size_t)c * m + e];
+      run += v;
     }
     tot[e] = run;
   }
@@ -133,12 +150,12 @@ __global__ __launch_bounds__(256) void group_bf16_kernel(const int32_t* __restri
     offsets[(size_t)bh * (m + 1) + m] = run;
   }
   __syncthreads();
-  for (int it = tid; it < nchunks * m; it += 256) cur[it] += tot[it % m];
+  for (int it = tid; it < nchunks * m; it += nt) cur[it] += tot[it % m];
   __syncthreads();
-  // stable scatter: wave w takes chunks w, w+4, ...; runs of 64 queries in order
+  // stable scatter: wave w takes chunks w, w + nw, ...; runs of 64 queries in order
   const int32_t* r = route + (size_t)bh * N;
   int32_t* pm = perm + (size_t)bh * N;
-  for (int c = w; c < nchunks; c += 4) {
+  for (int c = w; c < nchunks; c += nw) {
     int* cc = cur + c * m;
     for (int base = c * QC; base < min(N, (c + 1) * QC); base += 64) {
       const int n = base + lane;
@@ -200,8 +217,8 @@ hipError_t launch_group_bf16(const int32_t* route, const int32_t* chist, int32_t
                         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     attr = true;
   }
-  rt::group_bf16_kernel<<<s.BH, 256, lds, st>>>(route, chist, counts, offsets, perm, s.N, s.m,
-                                                nchunks);
+  rt::group_bf16_kernel<<<s.BH, 1024, lds, st>>>(route, chist, counts, offsets, perm, s.N, s.m,
+                                                 nchunks);
   return hipGetLastError();
 }
 
