@@ -180,29 +180,39 @@ void attend_bf16_kernel(Args a) {
       }
     }
   }
-  // ---- Q_L (hi / lo) and V_L^T for the head; rows past m are zero
-  for (int it = tid; it < L.mp * 16; it += 256) {
-    const int row = it >> 4, q4 = it & 15;
-    float4 f = make_float4(0.f, 0.f, 0.f, 0.f), v = f;
-    if (row < m) {
-      f = *reinterpret_cast<const float4*>(a.ql + ((size_t)bh * m + row) * 64 + 4 * q4);
-      v = *reinterpret_cast<const float4*>(a.vl + ((size_t)bh * m + row) * 64 + 4 * q4);
-    }
-    const float fv[4] = {f.x, f.y, f.z, f.w};
-    uint32_t h[4], l[4];
+  // ---- Q_L (hi / lo) and V_L^T for the head; rows past m are zero.  All of
+  // a thread's loads go out before any is used.
+  for (int base = 0; base < L.mp * 16; base += 256 * 4) {
+    float4 fq[4], fv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      h[i] = bf16_rne_bits(fv[i]);
-      l[i] = bf16_rne_bits(fv[i] - bf16_bits_to_f32(h[i]));
+    for (int u = 0; u < 4; ++u) {
+      const int it = base + 256 * u + tid, row = it >> 4, q4 = it & 15;
+      fq[u] = fv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (it < L.mp * 16 && row < m) {
+        fq[u] = *reinterpret_cast<const float4*>(a.ql + ((size_t)bh * m + row) * 64 + 4 * q4);
+        fv[u] = *reinterpret_cast<const float4*>(a.vl + ((size_t)bh * m + row) * 64 + 4 * q4);
+      }
     }
-    const int off = rc(row, q4 >> 1) + (q4 & 1) * 8;
-    *reinterpret_cast<u32x2*>(sm + L.off_qlh + off) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-    *reinterpret_cast<u32x2*>(sm + L.off_qll + off) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
-    const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint16_t*>(sm + L.off_vlt + (4 * q4 + i) * L.vlt_stride + 2 * row) =
-          (uint16_t)f16_bits(vv[i]);
+    for (int u = 0; u < 4; ++u) {
+      const int it = base + 256 * u + tid, row = it >> 4, q4 = it & 15;
+      if (it >= L.mp * 16) break;
+      const float f4[4] = {fq[u].x, fq[u].y, fq[u].z, fq[u].w};
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h[i] = bf16_rne_bits(f4[i]);
+        l[i] = bf16_rne_bits(f4[i] - bf16_bits_to_f32(h[i]));
+      }
+      const int off = rc(row, q4 >> 1) + (q4 & 1) * 8;
+      *reinterpret_cast<u32x2*>(sm + L.off_qlh + off) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+      *reinterpret_cast<u32x2*>(sm + L.off_qll + off) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+      const float vv[4] = {fv[u].x, fv[u].y, fv[u].z, fv[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint16_t*>(sm + L.off_vlt + (4 * q4 + i) * L.vlt_stride + 2 * row) =
+            (uint16_t)f16_bits(vv[i]);
+    }
   }
   __syncthreads();
 

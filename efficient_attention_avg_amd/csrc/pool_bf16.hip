@@ -22,30 +22,45 @@ __global__ __launch_bounds__(256) void pool_bf16_kernel(const uint16_t* __restri
   const uint16_t* q = Q + (size_t)bh * N * kHeadDim;
   int y0, y1;
   pool_window(r, gh, mh, &y0, &y1);
-  // column sums over the window rows: item = (column x, 8-channel chunk c)
-  for (int it = tid; it < gw * 8; it += blockDim.x) {
-    const int x = it >> 3, c = it & 7;
-    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    // eight rows' loads in flight at a time
+  // column sums over the window rows: item = (column x, 8-channel chunk c);
+  // a thread's items go two at a time with all their row loads in flight
+  for (int it0 = tid; it0 < gw * 8; it0 += 2 * blockDim.x) {
+    float a[2][8];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a[j][i] = 0.f;
     for (int y = y0; y < y1; y += 8) {
-      uint4 v[8];
+      uint4 v[2][8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (y + u < y1) v[u] = *reinterpret_cast<const uint4*>(q + (size_t)((y + u) * gw + x) * kHeadDim + 8 * c);
+      for (int j = 0; j < 2; ++j) {
+        const int it = it0 + j * blockDim.x, x = it >> 3, c = it & 7;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (y + u >= y1) break;
-        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          a[2 * i] += __uint_as_float(w[i] << 16);
-          a[2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
-        }
+        for (int u = 0; u < 8; ++u)
+          if (it < gw * 8 && y + u < y1)
+            v[j][u] = *reinterpret_cast<const uint4*>(q + (size_t)((y + u) * gw + x) * kHeadDim + 8 * c);
       }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (it0 + j * (int)blockDim.x >= gw * 8 || y + u >= y1) continue;
+          const uint32_t w[4] = {v[j][u].x, v[j][u].y, v[j][u].z, v[j][u].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            a[j][2 * i] += __uint_as_float(w[i] << 16);
+            a[j][2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
+          }
+        }
     }
-    float4* dst = reinterpret_cast<float4*>(colsum + x * kHeadDim + 8 * c);
-    dst[0] = make_float4(a[0], a[1], a[2], a[3]);
-    dst[1] = make_float4(a[4], a[5], a[6], a[7]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int it = it0 + j * blockDim.x, x = it >> 3, c = it & 7;
+      if (it >= gw * 8) continue;
+      float4* dst = reinterpret_cast<float4*>(colsum + x * kHeadDim + 8 * c);
+      dst[0] = make_float4(a[j][0], a[j][1], a[j][2], a[j][3]);
+      dst[1] = make_float4(a[j][4], a[j][5], a[j][6], a[j][7]);
+    }
   }
   __syncthreads();
   const float rows = (float)(y1 - y0);

@@ -4,17 +4,20 @@
 // being the ones the shared expert reuses; Algorithm 1 groups the queries by
 // route before attending).
 //
-// route_bf16_kernel: one workgroup per (head, 256-query chunk).  The head's
-// Q_L is staged in LDS as bf16 hi + lo; R^T = Q_L Q^T runs on bf16 MFMA with
-// fp32 accumulation (near-fp32 scores, so the argmax is decided at fp32
-// accuracy); the argmax scans landmarks in increasing order with a strict '>'
-// and combines lanes with ties to the lower landmark.  The chunk's route
-// histogram goes to the workspace.
+// route_bf16_kernel: a few workgroups per head, each owning a chunk of qc
+// queries (a multiple of the run length R, itself a multiple of 64).  The head's Q_L is staged once in LDS as bf16
+// hi + lo; R^T = Q_L Q^T runs on bf16 MFMA with fp32 accumulation
+// (near-fp32 scores, so the argmax is decided at fp32 accuracy); the argmax
+// scans landmarks in increasing order with a strict '>' and combines lanes
+// with ties to the lower landmark.  Each of the eight waves walks its
+// 16-query tiles with the next tile's Q rows already loading; routes collect
+// in LDS and go out once, with the route histogram of each R-query run, at
+// the end.
 //
-// group_bf16_kernel: one workgroup per head.  Chunk histograms -> per-expert
-// counts and offsets -> per-chunk starting positions; each wave then places
-// its chunks' queries stably: within a 64-query run, queries sharing a route
-// are found by ballot and ranked by lane order.
+// group_bf16_kernel: one workgroup per head.  Run histograms -> per-expert
+// counts and offsets -> per-run starting positions; the sixteen waves then
+// place the runs' queries stably, 64 at a time: queries sharing a route are
+// found by ballot and ranked by lane order.
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
@@ -22,15 +25,16 @@
 namespace mita {
 namespace rt {
 
-constexpr int QC = 256;  // queries per route workgroup
 
 __device__ __forceinline__ int rc(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
 
-__global__ __launch_bounds__(256) void route_bf16_kernel(const uint16_t* __restrict__ Q,
+constexpr int RW = 8;  // waves per route workgroup
+
+__global__ __launch_bounds__(64 * RW) void route_bf16_kernel(const uint16_t* __restrict__ Q,
                                                          const float* __restrict__ ql,
                                                          int32_t* __restrict__ route,
                                                          int32_t* __restrict__ chist, int N, int m,
-                                                         int nchunks) {
+                                                         int nruns, int qc, int R) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -38,23 +42,51 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(const uint16_t* __restr
   const int mt = (m + 15) >> 4;  // landmark tiles
   char* qlh = sm;
   char* qll = sm + mt * 16 * 128;
-  int* hist = reinterpret_cast<int*>(sm + 2 * mt * 16 * 128);
+  const int cruns = qc / R;  // runs per chunk
+  int* hist = reinterpret_cast<int*>(sm + 2 * mt * 16 * 128);  // [cruns][m]
+  int* rbuf = hist + cruns * m;  // the chunk's routes
   const uint16_t* Qh = Q + (size_t)bh * N * 64;
-  // this wave's four 16-query tiles: every Q row load is issued up front
-  constexpr int TPW = QC / 16 / 4;
-  u32x4 qb[TPW][2];
-  {
-    const u32x4 z = {0u, 0u, 0u, 0u};
+  const int base = chunk * qc, ntile = qc >> 4;
+  // Q_L (rows past m are zero): all of this thread's loads first, before the
+  // Q rows (vector memory counters drain in issue order)
+  constexpr int SU = 4;  // staging items per thread (up to 128 landmark rows)
+  float4 qlv[SU];
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int n = chunk * QC + 16 * (w + 4 * i) + c16;
-      qb[i][0] = n < N ? *reinterpret_cast<const u32x4*>(Qh + (size_t)n * 64 + 8 * g) : z;
-      qb[i][1] = n < N ? *reinterpret_cast<const u32x4*>(Qh + (size_t)n * 64 + 32 + 8 * g) : z;
-    }
+  for (int u = 0; u < SU; ++u) {
+    const int it = tid + 64 * RW * u, row = it >> 4, q4 = it & 15;
+    qlv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (it < mt * 16 * 16 && row < m)
+      qlv[u] = *reinterpret_cast<const float4*>(ql + ((size_t)bh * m + row) * 64 + 4 * q4);
   }
-  // stage Q_L (rows past m are zero) as bf16 hi / lo, 128-byte swizzled rows
-  for (int it = tid; it < mt * 16 * 16; it += 256) {
-    const int row = it >> 4, q4 = it & 15;  // 4 channels per item
+  // the first tile's Q rows (B operand: lane = query column c16, channels
+  // 8g.. and 32 + 8g..)
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  auto load_q = [&](int tt, u32x4& b0, u32x4& b1) {
+    const int n = base + 16 * tt + c16;
+    b0 = n < N ? *reinterpret_cast<const u32x4*>(Qh + (size_t)n * 64 + 8 * g) : z;
+    b1 = n < N ? *reinterpret_cast<const u32x4*>(Qh + (size_t)n * 64 + 32 + 8 * g) : z;
+  };
+  u32x4 nb0, nb1;
+  load_q(w, nb0, nb1);
+  // ... then as bf16 hi / lo into 128-byte swizzled rows
+#pragma unroll
+  for (int u = 0; u < SU; ++u) {
+    const int it = tid + 64 * RW * u, row = it >> 4, q4 = it & 15;
+    if (it >= mt * 16 * 16) break;
+    const float v[4] = {qlv[u].x, qlv[u].y, qlv[u].z, qlv[u].w};
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[i] = bf16_rne_bits(v[i]);
+      l[i] = bf16_rne_bits(v[i] - bf16_bits_to_f32(h[i]));
+    }
+    const int off = rc(row, q4 >> 1) + (q4 & 1) * 8;
+    *reinterpret_cast<u32x2*>(qlh + off) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+    *reinterpret_cast<u32x2*>(qll + off) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+  }
+  // landmark tiles beyond what the unrolled items cover (m > 128)
+  for (int it = tid + 64 * RW * SU; it < mt * 16 * 16; it += 64 * RW) {
+    const int row = it >> 4, q4 = it & 15;
     float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
     if (row < m) f = *reinterpret_cast<const float4*>(ql + ((size_t)bh * m + row) * 64 + 4 * q4);
     const float v[4] = {f.x, f.y, f.z, f.w};
@@ -68,14 +100,13 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(const uint16_t* __restr
     *reinterpret_cast<u32x2*>(qlh + off) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
     *reinterpret_cast<u32x2*>(qll + off) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
   }
-  for (int e = tid; e < m; e += 256) hist[e] = 0;
+  for (int e = tid; e < cruns * m; e += 64 * RW) hist[e] = 0;
   __syncthreads();
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int tt = w + 4 * i;
-    const int n = chunk * QC + 16 * tt + c16;  // this lane's query column
+  for (int tt = w; tt < ntile; tt += RW) {
+    const int n = base + 16 * tt + c16;  // this lane's query column
     const bool ok = n < N;
-    const u32x4 b0 = qb[i][0], b1 = qb[i][1];
+    const u32x4 b0 = nb0, b1 = nb1;
+    if (tt + RW < ntile) load_q(tt + RW, nb0, nb1);
     float best = -INFINITY;
     int bi = 0;
     for (int lt = 0; lt < mt; ++lt) {
@@ -103,13 +134,15 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(const uint16_t* __restr
       if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
     }
     if (g == 0 && ok) {
-      route[(size_t)bh * N + n] = bi;
-      atomicAdd(&hist[bi], 1);
+      rbuf[16 * tt + c16] = bi;
+      atomicAdd(&hist[(16 * tt / R) * m + bi], 1);
     }
   }
   __syncthreads();
-  int32_t* dst = chist + ((size_t)bh * nchunks + chunk) * m;
-  for (int e = tid; e < m; e += 256) dst[e] = hist[e];
+  for (int i = tid; i < qc && base + i < N; i += 64 * RW) route[(size_t)bh * N + base + i] = rbuf[i];
+  const int run0 = chunk * cruns, nr = min(cruns, nruns - run0);
+  int32_t* dst = chist + ((size_t)bh * nruns + run0) * m;
+  for (int e = tid; e < nr * m; e += 64 * RW) dst[e] = hist[e];
 }
 
 __global__ __launch_bounds__(1024) void group_bf16_kernel(const int32_t* __restrict__ route,
@@ -117,7 +150,8 @@ __global__ __launch_bounds__(1024) void group_bf16_kernel(const int32_t* __restr
                                                          int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ perm, int N, int m,
-                                                         int nchunks) {
+                                                         int nchunks, int qc) {
+  // here a "chunk" is one run of qc = R queries
   extern __shared__ int gsm[];
   int* cur = gsm;                   // [nchunks][m]: next free position per chunk/expert
   int* tot = gsm + nchunks * m;     // [m]
@@ -157,7 +191,7 @@ __global__ __launch_bounds__(1024) void group_bf16_kernel(const int32_t* __restr
   int32_t* pm = perm + (size_t)bh * N;
   for (int c = w; c < nchunks; c += nw) {
     int* cc = cur + c * m;
-    for (int base = c * QC; base < min(N, (c + 1) * QC); base += 64) {
+    for (int base = c * qc; base < min(N, (c + 1) * qc); base += 64) {
       const int n = base + lane;
       const int e = n < N ? r[n] : -1;
       uint64_t left = __ballot(e >= 0);
@@ -179,21 +213,44 @@ __global__ __launch_bounds__(1024) void group_bf16_kernel(const int32_t* __restr
 
 }  // namespace rt
 
+// Run length R: a multiple of 64, doubled until a head's run histograms fit
+// in 64 KB of LDS.  Queries per route workgroup qc: a multiple of R such that
+// about 768 workgroups cover all heads.
+static void route_chunking(const Shape& s, int& qc, int& nchunks, int& R, int& nruns) {
+  R = 64;
+  while ((size_t)((s.N + R - 1) / R) * s.m * 4 > 64 * 1024 && R < s.N) R *= 2;
+  nruns = (s.N + R - 1) / R;
+  int parts = (768 + s.BH - 1) / s.BH;
+  if (parts > nruns) parts = nruns;
+  if (parts < 1) parts = 1;
+  qc = (((s.N + parts - 1) / parts) + R - 1) / R * R;
+  nchunks = (s.N + qc - 1) / qc;
+}
+
+static size_t route_lds(const Shape& s, int qc, int R) {
+  const int mt = (s.m + 15) / 16;
+  return (size_t)2 * mt * 16 * 128 + (size_t)(qc / R) * s.m * 4 + (size_t)qc * 4;
+}
+
 bool route_bf16_supported(const Shape& s) {
-  const size_t nchunks = (s.N + rt::QC - 1) / rt::QC;
-  return s.bf16 && s.m <= 512 && (nchunks * s.m + s.m) * 4 <= 160 * 1024;
+  int qc, nchunks, R, nruns;
+  route_chunking(s, qc, nchunks, R, nruns);
+  return s.bf16 && s.m <= 512 && ((size_t)nruns * s.m + s.m) * 4 <= 160 * 1024 &&
+         route_lds(s, qc, R) <= 160 * 1024;
 }
 
 size_t route_chist_bytes(const Shape& s) {
-  const int nchunks = (s.N + rt::QC - 1) / rt::QC;
-  return (size_t)s.BH * nchunks * s.m * 4;
+  int qc, nchunks, R, nruns;
+  route_chunking(s, qc, nchunks, R, nruns);
+  return (size_t)s.BH * nruns * s.m * 4;
 }
 
 hipError_t launch_route_bf16(const void* Q, const float* ql, int32_t* route, int32_t* chist,
                              const Shape& s, hipStream_t st) {
-  const int nchunks = (s.N + rt::QC - 1) / rt::QC;
-  const int mt = (s.m + 15) / 16;
-  const size_t lds = (size_t)2 * mt * 16 * 128 + (size_t)s.m * 4;
+  int qc, nchunks, R, nruns;
+  route_chunking(s, qc, nchunks, R, nruns);
+  const size_t lds = route_lds(s, qc, R);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
   static bool attr = false;
   if (!attr) {
     hipFuncSetAttribute((const void*)rt::route_bf16_kernel,
@@ -201,15 +258,16 @@ hipError_t launch_route_bf16(const void* Q, const float* ql, int32_t* route, int
     attr = true;
   }
   dim3 grid(nchunks, s.BH);
-  rt::route_bf16_kernel<<<grid, 256, lds, st>>>((const uint16_t*)Q, ql, route, chist, s.N, s.m,
-                                                nchunks);
+  rt::route_bf16_kernel<<<grid, 64 * rt::RW, lds, st>>>((const uint16_t*)Q, ql, route, chist, s.N,
+                                                        s.m, nruns, qc, R);
   return hipGetLastError();
 }
 
 hipError_t launch_group_bf16(const int32_t* route, const int32_t* chist, int32_t* counts,
                              int32_t* offsets, int32_t* perm, const Shape& s, hipStream_t st) {
-  const int nchunks = (s.N + rt::QC - 1) / rt::QC;
-  const size_t lds = ((size_t)nchunks * s.m + s.m) * 4;
+  int qc, nchunks, R, nruns;
+  route_chunking(s, qc, nchunks, R, nruns);
+  const size_t lds = ((size_t)nruns * s.m + s.m) * 4;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   static bool attr = false;
   if (!attr) {
@@ -218,7 +276,7 @@ hipError_t launch_group_bf16(const int32_t* route, const int32_t* chist, int32_t
     attr = true;
   }
   rt::group_bf16_kernel<<<s.BH, 1024, lds, st>>>(route, chist, counts, offsets, perm, s.N, s.m,
-                                                 nchunks);
+                                                 nruns, R);
   return hipGetLastError();
 }
 
