@@ -2,15 +2,18 @@
 """Throughput of the MiTA forward pass on one MI355X, with its roofline.
 
     python bench.py [--steps K] [--warmup W] [--workload deit-s] [--also hires-3136]
+    python bench.py --summarize-pmc FETCH_DIR WRITE_DIR WORKLOAD   (counter summary)
 
 A step is one full ``mita_forward`` (pooling, landmark scores + top-k +
 landmark values, routing + grouping, grouped expert attention) over one batch
 of synthetic, seeded inputs already resident in device memory.  Before every
 timed step a 512 MiB buffer is overwritten so that neither L2 nor the 256 MB
 Infinity Cache holds the inputs (the DeiT-S inputs would otherwise fit in
-it); each step is bracketed by HIP events on the stream the library launches
-on, and ms_per_step is the mean of those event times.  A warm (no flush)
-back-to-back figure is reported beside it.
+it).  The library records HIP events on its launch stream before its first
+kernel and after each kernel (mita_forward_ex's timing events): a step's time
+is first event to last, a kernel's time the interval that closes with it;
+ms_per_step is the mean step time.  A warm (no flush) figure is reported
+beside it unless --no-warm.
 
 Prints ONE JSON line.  ``value`` is query-heads per second (B*H*N per step)
 on the headline workload (DeiT-S shape); the 3136-token workload is reported
@@ -33,6 +36,50 @@ HBM_PEAK_GBS = 8000.0
 FLUSH_BYTES = 512 << 20
 
 
+# measured HBM traffic per launch, written by --summarize-pmc from two rocprofv3
+# counter runs (FETCH_SIZE, WRITE_SIZE) of this script, scaled by a plain copy
+# kernel's readings; an entry is used only while its kernel's sources still
+# hash to the value recorded with it
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+CSRC = os.path.join(ROOT, "efficient_attention_avg_amd", "csrc")
+SHARED_SOURCES = ["common.h", "mfma.h", "select.h", "internal.h"]
+KERNEL_SOURCES = {
+    "bf16": {"fused": "fused.hip", "pool": "pool_bf16.hip", "landmark": "landmark_bf16.hip",
+             "route": "route_bf16.hip", "group": "route_bf16.hip", "attend": "attend_bf16.hip"},
+    "f32": {"pool": "pool.hip", "landmark": "landmark.hip", "route": "route.hip",
+            "group": "route.hip", "attend": "attend.hip"},
+}
+# rocprofv3 kernel names -> the names mita_kernel_names uses
+PROFILE_NAMES = [("mita_fused_kernel", "fused"), ("pool_bf16_kernel", "pool"),
+                 ("pool_kernel", "pool"), ("landmark_kernel", "landmark"),
+                 ("route_bf16_kernel", "route"), ("route_kernel", "route"),
+                 ("group_bf16_kernel", "group"), ("group_kernel", "group"),
+                 ("attend_bf16_kernel", "attend"), ("attend_kernel", "attend")]
+
+
+def source_hash(dtype, kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in [KERNEL_SOURCES[dtype][kernel]] + SHARED_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, dtype, kernel):
+    """HBM bytes per launch from the committed counter summary, or None when absent or
+    taken on other sources."""
+    if not os.path.exists(TRAFFIC_FILE) or kernel not in KERNEL_SOURCES.get(dtype, {}):
+        return None
+    want = source_hash(dtype, kernel)
+    for line in open(TRAFFIC_FILE):
+        f = line.split()
+        if len(f) == 5 and not line.startswith("#") and f[0] == kernel and f[1] == workload \
+                and f[4] == want:
+            return int(f[2]) + int(f[3])
+    return None
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -50,15 +97,19 @@ def algorithmic(w):
     BH = w["B"] * w["H"]
     per_qh = 3 * d * s_in + d * 4
     kern = {
+        # the whole pass in one kernel: read Q, K, V once, write out
+        "fused": BH * N * per_qh,
         # pooling: read Q, write Q_L
         "pool": BH * (N * d * s_in + m * d * 4),
         # landmark pass: read Q_L, K, V; write idx and V_L
         "landmark": BH * (m * d * 4 + 2 * N * d * s_in + m * k * 4 + m * d * 4),
-        # routing + grouping: read Q, Q_L; write route, counts, offsets, perm
-        "route": BH * (N * d * s_in + m * d * 4 + 2 * N * 4 + (2 * m + 1) * 4),
-        # attention: read Q, each expert's K/V rows once, Q_L, V_L, idx, route, perm; write out
+        # routing: read Q and Q_L, write routes
+        "route": BH * (N * d * s_in + m * d * 4 + N * 4),
+        # grouping: read routes, write perm, counts and offsets
+        "group": BH * (2 * N * 4 + (2 * m + 1) * 4),
+        # attention: read Q, each expert's K/V rows once, Q_L, V_L, idx, perm; write out
         "attend": BH * (N * d * s_in + 2 * m * k * d * s_in + 2 * m * d * 4 + m * k * 4
-                        + 2 * N * 4 + N * d * 4),
+                        + N * 4 + N * d * 4),
     }
     return dict(bytes_per_qh=per_qh, flops_per_qh=4 * d * (2 * m + k), kernel_bytes=kern,
                 qh=BH * N)
@@ -86,71 +137,60 @@ class Runner:
                                        w["m_h"], w["m_w"], w["k"], code)
         self.ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
         self.flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+        self.kernels = mita.mita_kernel_names(w["B"], w["H"], w["grid_h"], w["grid_w"], w["d"],
+                                              w["m_h"], w["m_w"], w["k"], code, path=path)
 
-    def step(self):
+    def step(self, events=None):
         self.mita.mita_forward_ex(self.q, self.k, self.v, *self.args, out=self.out,
-                                  workspace=self.ws, path=self.path)
+                                  workspace=self.ws, path=self.path, events=events)
 
     def flush(self):
         self.flush_buf.fill_(1)
 
-    def timed(self, fn, n, flush=True):
-        """Mean event time (ms) of fn over n calls, optionally flushing caches before each."""
+    def timed(self, n, flush=True):
+        """n steps, optionally flushing the caches before each.  The library records an event
+        on its launch stream before its first kernel and after each kernel; a step's time is
+        first event to last (the kernels and any gaps between them), each kernel's time the
+        interval that closes with it.  Returns the mean step time (ms), every step's time, and
+        each kernel's mean time (ms)."""
         torch = self.torch
-        ev = []
-        for _ in range(n):
+        kevs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(self.kernels) + 1)]
+                for _ in range(n)]
+        for kev in kevs:
+            for e in kev:
+                e.record()  # creates the HIP event before the timed steps
+        torch.cuda.synchronize()
+        for kev in kevs:
             if flush:
                 self.flush()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn()
-            b.record()
-            ev.append((a, b))
+            self.step(events=kev)
         torch.cuda.synchronize()
-        ms = [a.elapsed_time(b) for a, b in ev]
-        return sum(ms) / len(ms), ms
-
-    def stage_times(self, n):
-        """Per-step-kernel event times through the stage entry points (same kernels)."""
-        mita, torch = self.mita, self.torch
-        gh, gw, mh, mw, k = self.args
-        ql = mita.mita_pool(self.q, gh, gw, mh, mw)
-        idx, vl = mita.mita_landmark(ql, self.k, self.v, k)
-        route, counts, offsets, perm = mita.mita_route(self.q, ql)
-        torch.cuda.synchronize()
-        return {
-            "pool": self.timed(lambda: mita.mita_pool(self.q, gh, gw, mh, mw, ql=ql), n)[0],
-            "landmark": self.timed(lambda: mita.mita_landmark(ql, self.k, self.v, k), n)[0],
-            "route": self.timed(lambda: mita.mita_route(self.q, ql), n)[0],
-            "attend": self.timed(lambda: mita.mita_attend(self.q, self.k, self.v, ql, vl, idx,
-                                                          route, offsets, perm), n)[0],
-        }
+        ms = [kev[0].elapsed_time(kev[-1]) for kev in kevs]
+        per = {name: sum(kev[i].elapsed_time(kev[i + 1]) for kev in kevs) / n
+               for i, name in enumerate(self.kernels)}
+        return sum(ms) / len(ms), ms, per
 
 
-def measure(name, steps, warmup, path="auto"):
+def measure(name, steps, warmup, path="auto", warm=True):
     import torch
     r = Runner(name, path)
     w = r.w
     alg = algorithmic(w)
     for _ in range(warmup):
+        r.flush()
         r.step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    cold_ms, cold_all = r.timed(r.step, steps, flush=True)
+    cold_ms, cold_all, stages = r.timed(steps, flush=True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    warm_ms, _ = r.timed(r.step, steps, flush=False)
-    log(f"{name}: cold {cold_ms * 1e3:.1f} us/step, warm {warm_ms * 1e3:.1f} us/step")
+    warm_ms = None
+    if warm:
+        warm_ms, _, _ = r.timed(steps, flush=False)
+    log(f"{name}: cold {cold_ms * 1e3:.1f} us/step"
+        + (f", warm {warm_ms * 1e3:.1f} us/step" if warm_ms else ""))
     qh = alg["qh"]
-    code = r.mita.MITA_BF16 if w["dtype"] == "bf16" else r.mita.MITA_F32
-    sched = r.mita.mita_schedule(w["B"], w["H"], w["grid_h"], w["grid_w"], w["d"], w["m_h"],
-                                 w["m_w"], w["k"], code) if path == "auto" else path
-    if sched == "fused":
-        # one kernel is the whole pass: its algorithmic bytes are the pass's
-        stages = {"fused": cold_ms}
-        alg["kernel_bytes"]["fused"] = alg["bytes_per_qh"] * qh
-    else:
-        stages = r.stage_times(max(5, min(steps, 20)))
+    sched = "fused" if r.kernels == ["fused"] else "staged"
     log(f"{name}: {sched} schedule, kernel event times (us) "
         + ", ".join(f"{k}={v * 1e3:.1f}" for k, v in stages.items()))
     dom = max(stages, key=stages.get)
@@ -160,15 +200,18 @@ def measure(name, steps, warmup, path="auto"):
     res = dict(
         workload=w, value=qh / (cold_ms * 1e-3), ms_per_step=cold_ms,
         ms_p10=sorted(cold_all)[len(cold_all) // 10], ms_p90=sorted(cold_all)[(9 * len(cold_all)) // 10],
-        warm_ms_per_step=warm_ms, warm_value=qh / (warm_ms * 1e-3), wall_s=wall,
+        warm_ms_per_step=warm_ms, warm_value=qh / (warm_ms * 1e-3) if warm_ms else None,
+        wall_s=wall,
         roofline=dict(bound="hbm", kernel=dom, achieved=dom_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=dom_gbs / HBM_PEAK_GBS, traffic=None,
+                      frac=dom_gbs / HBM_PEAK_GBS,
+                      traffic=measured_traffic(w["name"], w["dtype"], dom),
                       algorithmic_bytes_per_launch=dom_bytes, avg_launch_us=stages[dom] * 1e3),
         pass_roofline=dict(bound="hbm", achieved=pass_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
                            frac=pass_gbs / HBM_PEAK_GBS, bytes_per_qh=alg["bytes_per_qh"],
                            flops_per_qh=alg["flops_per_qh"]),
-        stage_us={k: v * 1e3 for k, v in stages.items()}, schedule=sched,
-        dtype=w["dtype"],
+        stage_us={k: v * 1e3 for k, v in stages.items()},
+        kernel_gbs={k: alg["kernel_bytes"][k] / (v * 1e-3) / 1e9 for k, v in stages.items()},
+        schedule=sched, dtype=w["dtype"],
     )
     return r, res
 
@@ -199,7 +242,54 @@ def cpu_baseline(runner, seconds):
                        f"{el:.1f}s, numpy fp64 with BLAS limited to 1 thread")
 
 
+COPY_MIB = 256
+
+
+def copy_calibration():
+    """One plain copy kernel of known size (reads and writes COPY_MIB MiB), for scaling the
+    FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    a = torch.ones(COPY_MIB << 18, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    torch.neg(a, out=b)
+    torch.cuda.synchronize()
+
+
+def summarize_pmc(fetch_dir, write_dir, workload):
+    """Per-launch HBM bytes of each MiTA kernel from two rocprofv3 counter runs of this script
+    (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), scaled by the copy kernel's readings.
+    Prints lines for profiles/hbm_traffic.txt."""
+    import csv
+    import glob
+
+    def read(d, counter):
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for row in csv.DictReader(open(f)):
+                if row["Counter_Name"] != counter:
+                    continue
+                name = row["Kernel_Name"]
+                key = "copy" if "neg" in name.lower() else next(
+                    (k for pat, k in PROFILE_NAMES if pat in name), None)
+                if key:
+                    vals.setdefault(key, []).append(float(row["Counter_Value"]) * 1024.0)
+        return {k: sum(v) / len(v) for k, v in vals.items()}
+
+    fetch, write = read(fetch_dir, "FETCH_SIZE"), read(write_dir, "WRITE_SIZE")
+    copy_bytes = float(COPY_MIB << 20)
+    sf, sw = copy_bytes / fetch["copy"], copy_bytes / write["copy"]
+    print(f"# copy kernel of {COPY_MIB} MiB: FETCH_SIZE reads {fetch['copy'] / 1024:.0f} KiB "
+          f"(x{sf:.4f}), WRITE_SIZE reads {write['copy'] / 1024:.0f} KiB (x{sw:.4f})")
+    import synth
+    dtype = synth.workload(workload)["dtype"]
+    for k in sorted(set(fetch) & set(write) - {"copy"}):
+        print(f"{k} {workload} {int(fetch[k] * sf)} {int(write[k] * sw)} {source_hash(dtype, k)}")
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
+        summarize_pmc(sys.argv[2], sys.argv[3], sys.argv[4])
+        return
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -209,6 +299,10 @@ def main():
     ap.add_argument("--path", default="auto", choices=["auto", "fused", "staged"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-warm", action="store_true",
+                    help="skip the warm (no flush) figure, e.g. under a profiler")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain copy kernel of known size (counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this MiTA build runs on exactly one GPU; every (batch, head) is "
@@ -223,7 +317,10 @@ def main():
         _b.build()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
-    runner, main_res = measure(args.workload, args.steps, args.warmup, args.path)
+    if args.copy_calibration:
+        copy_calibration()
+    runner, main_res = measure(args.workload, args.steps, args.warmup, args.path,
+                               warm=not args.no_warm)
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host")
@@ -233,13 +330,14 @@ def main():
     torch.cuda.empty_cache()
     secondary = None
     if args.also:
-        r2, res2 = measure(args.also, args.steps, args.warmup, args.path)
+        r2, res2 = measure(args.also, args.steps, args.warmup, args.path, warm=not args.no_warm)
         del r2
         secondary = {
             "workload": describe(res2["workload"]), "value": res2["value"], "unit": "query-heads/s",
             "ms_per_step": res2["ms_per_step"], "warm_ms_per_step": res2["warm_ms_per_step"],
             "roofline": res2["roofline"], "pass_roofline": res2["pass_roofline"],
-            "stage_us": res2["stage_us"], "schedule": res2["schedule"], "dtype": res2["dtype"],
+            "stage_us": res2["stage_us"], "kernel_gbs": res2["kernel_gbs"],
+            "schedule": res2["schedule"], "dtype": res2["dtype"],
         }
     w = main_res["workload"]
     line = {
@@ -250,11 +348,13 @@ def main():
         "config": {"workload": describe(w), "B": w["B"], "H": w["H"], "seq_len": w["grid_h"] * w["grid_w"],
                    "m": w["m_h"] * w["m_w"], "k": w["k"], "path": args.path,
                    "schedule": main_res["schedule"],
-                   "timing": "HIP events per step, L2 + Infinity Cache flushed before each step"},
+                   "timing": "HIP events the library records around its kernels on the launch "
+                             "stream, L2 + Infinity Cache flushed before each step"},
         "ms_p10": main_res["ms_p10"], "ms_p90": main_res["ms_p90"],
         "warm_ms_per_step": main_res["warm_ms_per_step"], "warm_value": main_res["warm_value"],
         "roofline": main_res["roofline"], "pass_roofline": main_res["pass_roofline"],
-        "stage_us": main_res["stage_us"], "cpu_baseline": cpu, "secondary": secondary,
+        "stage_us": main_res["stage_us"], "kernel_gbs": main_res["kernel_gbs"],
+        "cpu_baseline": cpu, "secondary": secondary,
         "library": mita.lib().mita_version().decode(),
     }
     print(json.dumps(line))

@@ -23,7 +23,7 @@ PATHS = {"auto": 0, "fused": 1, "staged": 2}
 # Every symbol include/mita.h declares.
 EXPORTS = [
     "mita_status_string", "mita_last_error", "mita_version", "mita_workspace_bytes",
-    "mita_schedule",
+    "mita_schedule", "mita_kernel_names",
     "mita_forward", "mita_forward_ex", "mita_pool", "mita_landmark_workspace_bytes",
     "mita_landmark", "mita_route_workspace_bytes", "mita_route", "mita_attend",
 ]
@@ -37,7 +37,8 @@ class MitaError(RuntimeError):
 
 class _Extras(ctypes.Structure):
     _fields_ = [("ql", ctypes.c_void_p), ("vl", ctypes.c_void_p), ("counts", ctypes.c_void_p),
-                ("offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p), ("path", ctypes.c_int)]
+                ("offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p), ("path", ctypes.c_int),
+                ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int)]
 
 
 _lib = None
@@ -62,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.mita_workspace_bytes.argtypes = [I] * 8 + [I]
         L.mita_schedule.restype = I
         L.mita_schedule.argtypes = [I] * 8 + [I]
+        L.mita_kernel_names.restype = I
+        L.mita_kernel_names.argtypes = [I] * 8 + [I, I, ctypes.POINTER(ctypes.c_char_p), I]
         L.mita_forward.restype = S
         L.mita_forward.argtypes = [P, P, P] + [I] * 8 + [I, P, P, P, P, Z, P]
         L.mita_forward_ex.restype = S
@@ -157,12 +160,26 @@ def mita_forward(q, k, v, grid_h, grid_w, m_h, m_w, topk, *, out=None, idx=None,
                            route=route, workspace=workspace, stream=stream)["out"]
 
 
+def mita_kernel_names(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code, path="auto") -> list:
+    """The kernels mita_forward_ex launches, in order (host only)."""
+    names = (ctypes.c_char_p * 8)()
+    n = int(lib().mita_kernel_names(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code, PATHS[path],
+                                    names, 8))
+    if n < 0:
+        _check(-n)
+    return [names[i].decode() for i in range(n)]
+
+
 def mita_forward_ex(q, k, v, grid_h, grid_w, m_h, m_w, topk, *, out=None, idx=None, route=None,
-                    extras=False, path="auto", workspace=None, stream=None):
+                    extras=False, path="auto", workspace=None, stream=None, events=None):
     """Whole pass with optional intermediates.
 
     ``idx`` / ``route``: a preallocated int32 tensor, True (allocate) or None.
     ``extras=True`` also returns ql, vl, counts, offsets and perm.
+    ``events``: torch.cuda.Event objects (enable_timing=True), recorded on the
+    launch stream before the first kernel and after each kernel (see
+    mita_kernel_names); each must have been recorded once already so that
+    its HIP event exists.
     """
     code, torch = _qkv(q, k, v)
     B, H, N, d = q.shape
@@ -180,6 +197,10 @@ def mita_forward_ex(q, k, v, grid_h, grid_w, m_h, m_w, topk, *, out=None, idx=No
     route = alloc(route, (B, H, N), i32, "route")
     res = dict(out=out, idx=idx, route=route)
     ex = _Extras(path=PATHS[path])
+    if events:
+        handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+        ex.events = ctypes.cast(handles, ctypes.POINTER(ctypes.c_void_p))
+        ex.n_events = len(events)
     if extras:
         res.update(ql=alloc(True, (B, H, m, d), torch.float32, "ql"),
                    vl=alloc(True, (B, H, m, d), torch.float32, "vl"),

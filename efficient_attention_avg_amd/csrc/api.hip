@@ -37,6 +37,16 @@ mita_status hip_status(hipError_t e, const char* what) {
 }
 
 // Shape checks common to every entry point.  Returns MITA_OK and fills *s.
+// Records the caller's timing events around the kernels of one call.
+struct Marker {
+  void* const* ev = nullptr;
+  int n = 0, i = 0;
+  void mark(hipStream_t st) {
+    if (ev && i < n && ev[i]) hipEventRecord((hipEvent_t)ev[i], st);
+    ++i;
+  }
+};
+
 mita_status make_shape(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
                        mita_dtype dt, Shape* s) {
   if (B < 1 || H < 1) return fail(MITA_ERR_INVALID_ARG, "B=%d and H=%d must be >= 1", B, H);
@@ -76,41 +86,51 @@ size_t landmark_scratch(const Shape& s) {
 }
 size_t route_scratch(const Shape& s) { return route_mfma(s) ? mita::route_chist_bytes(s) : 0; }
 
-mita_status run_pool(const void* Q, float* ql, const Shape& s, hipStream_t st) {
-  return hip_status(pool_mfma(s) ? mita::launch_pool_bf16(Q, ql, s, st)
-                                 : mita::launch_pool(Q, ql, s, st),
-                    "pool launch");
+mita_status run_pool(const void* Q, float* ql, const Shape& s, hipStream_t st,
+                     Marker* mk = nullptr) {
+  const mita_status r = hip_status(pool_mfma(s) ? mita::launch_pool_bf16(Q, ql, s, st)
+                                                : mita::launch_pool(Q, ql, s, st),
+                                   "pool launch");
+  if (mk) mk->mark(st);
+  return r;
 }
 mita_status run_landmark(const float* ql, const void* K, const void* V, int32_t* idx, float* vl,
-                         void* scratch, const Shape& s, hipStream_t st) {
-  return hip_status(landmark_mfma(s) ? mita::launch_landmark_bf16(ql, K, V, idx, vl, s, st)
-                                     : mita::launch_landmark(ql, K, V, idx, vl, scratch, s, st),
-                    "landmark launch");
+                         void* scratch, const Shape& s, hipStream_t st, Marker* mk = nullptr) {
+  const mita_status r =
+      hip_status(landmark_mfma(s) ? mita::launch_landmark_bf16(ql, K, V, idx, vl, s, st)
+                                  : mita::launch_landmark(ql, K, V, idx, vl, scratch, s, st),
+                 "landmark launch");
+  if (mk) mk->mark(st);
+  return r;
 }
 mita_status run_route(const void* Q, const float* ql, int32_t* route, int32_t* counts,
                       int32_t* offsets, int32_t* perm, void* scratch, const Shape& s,
-                      hipStream_t st) {
-  if (!route_mfma(s))
-    return hip_status(mita::launch_route(Q, ql, route, counts, offsets, perm, s, st),
-                      "route launch");
-  mita_status r = hip_status(mita::launch_route_bf16(Q, ql, route, (int32_t*)scratch, s, st),
+                      hipStream_t st, Marker* mk = nullptr) {
+  const bool mfma = route_mfma(s);
+  mita_status r = hip_status(mfma ? mita::launch_route_bf16(Q, ql, route, (int32_t*)scratch, s, st)
+                                  : mita::launch_route(Q, ql, route, s, st),
                              "route launch");
+  if (mk) mk->mark(st);
   if (r != MITA_OK) return r;
-  return hip_status(mita::launch_group_bf16(route, (const int32_t*)scratch, counts, offsets, perm,
-                                            s, st),
-                    "group launch");
+  r = hip_status(mfma ? mita::launch_group_bf16(route, (const int32_t*)scratch, counts, offsets,
+                                                perm, s, st)
+                      : mita::launch_group(route, counts, offsets, perm, s, st),
+                 "group launch");
+  if (mk) mk->mark(st);
+  return r;
 }
 mita_status run_attend(const void* Q, const void* K, const void* V, const float* ql,
                        const float* vl, const int32_t* idx, const int32_t* route,
                        const int32_t* offsets, const int32_t* perm, float* out, const Shape& s,
-                       hipStream_t st) {
-  return hip_status(
+                       hipStream_t st, Marker* mk = nullptr) {
+  const mita_status r = hip_status(
       attend_mfma(s)
           ? mita::launch_attend_bf16(Q, K, V, ql, vl, idx, offsets, perm, out, s, st)
           : mita::launch_attend(Q, K, V, ql, vl, idx, route, offsets, perm, out, s, st),
       "attend launch");
+  if (mk) mk->mark(st);
+  return r;
 }
-
 // Workspace of the staged schedule: every intermediate the caller did not
 // supply, then the landmark and route steps' scratch.
 struct Layout {
@@ -193,6 +213,12 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V, int B, 
   if (path == MITA_PATH_FUSED && !fusable)
     return fail(MITA_ERR_UNSUPPORTED,
                 "fused schedule needs bf16 inputs, N <= 208, m <= 32 and k <= 32");
+  Marker mk;
+  if (extras && extras->events && extras->n_events > 0) {
+    mk.ev = extras->events;
+    mk.n = extras->n_events;
+  }
+  mk.mark(stream);
   if (fusable && path != MITA_PATH_STAGED) {
     st = hip_status(mita::launch_fused(Q, K, V, out, idx, route, extras ? extras->ql : nullptr,
                                        extras ? extras->vl : nullptr,
@@ -200,6 +226,7 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V, int B, 
                                        extras ? extras->offsets : nullptr,
                                        extras ? extras->perm : nullptr, s, stream),
                     "fused launch");
+    mk.mark(stream);
     return st != MITA_OK ? st : ok();
   }
 
@@ -213,13 +240,34 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V, int B, 
   void* scratch = (char*)workspace + L.scratch;
   void* rscratch = (char*)workspace + L.rscratch;
 
-  if ((st = run_pool(Q, ql, s, stream)) != MITA_OK) return st;
-  if ((st = run_landmark(ql, K, V, idx_p, vl, scratch, s, stream)) != MITA_OK) return st;
-  if ((st = run_route(Q, ql, route_p, counts, offsets, perm, rscratch, s, stream)) != MITA_OK)
+  if ((st = run_pool(Q, ql, s, stream, &mk)) != MITA_OK) return st;
+  if ((st = run_landmark(ql, K, V, idx_p, vl, scratch, s, stream, &mk)) != MITA_OK) return st;
+  if ((st = run_route(Q, ql, route_p, counts, offsets, perm, rscratch, s, stream, &mk)) != MITA_OK)
     return st;
-  if ((st = run_attend(Q, K, V, ql, vl, idx_p, route_p, offsets, perm, out, s, stream)) != MITA_OK)
+  if ((st = run_attend(Q, K, V, ql, vl, idx_p, route_p, offsets, perm, out, s, stream, &mk)) !=
+      MITA_OK)
     return st;
   return ok();
+}
+
+int mita_kernel_names(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
+                      mita_dtype in_dtype, int path, const char** names, int capacity) {
+  Shape s;
+  const mita_status st = make_shape(B, H, grid_h, grid_w, d, m_h, m_w, k, in_dtype, &s);
+  if (st != MITA_OK) return -(int)st;
+  if (path != MITA_PATH_AUTO && path != MITA_PATH_STAGED && path != MITA_PATH_FUSED)
+    return -(int)fail(MITA_ERR_INVALID_ARG, "unknown path %d", path);
+  const bool fusable = mita::fused_supported(s);
+  if (path == MITA_PATH_FUSED && !fusable)
+    return -(int)fail(MITA_ERR_UNSUPPORTED, "fused schedule not available for this shape");
+  static const char* const kFused[] = {"fused"};
+  static const char* const kStaged[] = {"pool", "landmark", "route", "group", "attend"};
+  const bool fused = fusable && path != MITA_PATH_STAGED;
+  const char* const* list = fused ? kFused : kStaged;
+  const int n = fused ? 1 : 5;
+  for (int i = 0; names && i < n && i < capacity; ++i) names[i] = list[i];
+  ok();
+  return n;
 }
 
 mita_status mita_forward(const void* Q, const void* K, const void* V, int B, int H, int grid_h,

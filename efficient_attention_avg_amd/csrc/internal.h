@@ -24,8 +24,10 @@ hipError_t launch_landmark(const float* ql, const void* K, const void* V, int32_
                            float* vl, void* scratch, const Shape& s, hipStream_t st);
 
 // steps a5-a6: routing and grouping
-hipError_t launch_route(const void* Q, const float* ql, int32_t* route, int32_t* counts,
-                        int32_t* offsets, int32_t* perm, const Shape& s, hipStream_t st);
+hipError_t launch_route(const void* Q, const float* ql, int32_t* route, const Shape& s,
+                        hipStream_t st);
+hipError_t launch_group(const int32_t* route, int32_t* counts, int32_t* offsets, int32_t* perm,
+                        const Shape& s, hipStream_t st);
 
 // step a7: grouped expert attention
 hipError_t launch_attend(const void* Q, const void* K, const void* V, const float* ql,

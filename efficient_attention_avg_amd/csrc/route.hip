@@ -78,15 +78,18 @@ __global__ __launch_bounds__(256) void group_kernel(const int32_t* __restrict__ 
   }
 }
 
-hipError_t launch_route(const void* Q, const float* ql, int32_t* route, int32_t* counts,
-                        int32_t* offsets, int32_t* perm, const Shape& s, hipStream_t st) {
+hipError_t launch_route(const void* Q, const float* ql, int32_t* route, const Shape& s,
+                        hipStream_t st) {
   dim3 grid((s.N + 255) / 256, s.BH);
   if (s.bf16)
     route_kernel<bf16_t><<<grid, 256, 0, st>>>((const bf16_t*)Q, ql, route, s.N, s.m);
   else
     route_kernel<float><<<grid, 256, 0, st>>>((const float*)Q, ql, route, s.N, s.m);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  return hipGetLastError();
+}
+
+hipError_t launch_group(const int32_t* route, int32_t* counts, int32_t* offsets, int32_t* perm,
+                        const Shape& s, hipStream_t st) {
   const size_t lds = (size_t)(2 * s.m + 256) * sizeof(int);
   group_kernel<<<s.BH, 256, lds, st>>>(route, counts, offsets, perm, s.N, s.m);
   return hipGetLastError();

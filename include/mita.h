@@ -101,13 +101,18 @@ mita_status mita_forward(const void* Q, const void* K, const void* V,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Optional extra outputs of mita_forward_ex (any member may be NULL), and the
- * schedule to run.  Used to check every intermediate of the pass.
+ * Optional extra outputs of mita_forward_ex (any member may be NULL), the
+ * schedule to run, and optional per-kernel timing events.  Used to check
+ * every intermediate of the pass and to time its kernels.
  *   ql      [B,H,m,d] fp32  landmark queries
  *   vl      [B,H,m,d] fp32  landmark values (shared expert values)
  *   counts  [B,H,m]   int32 queries routed to each landmark
  *   offsets [B,H,m+1] int32 exclusive prefix sum of counts
  *   perm    [B,H,N]   int32 query ids grouped by route, ascending within a group
+ *   events  NULL, or n_events caller-created hipEvent_t handles: the call
+ *           records events[0] on `stream` before its first kernel and
+ *           events[i] right after its i-th kernel, for i < n_events (the
+ *           kernels, in launch order, are the ones mita_kernel_names lists)
  */
 typedef struct {
   float* ql;
@@ -116,6 +121,8 @@ typedef struct {
   int32_t* offsets;
   int32_t* perm;
   int path; /* mita_path */
+  void* const* events;
+  int n_events;
 } mita_extras;
 
 mita_status mita_forward_ex(const void* Q, const void* K, const void* V,
@@ -124,6 +131,16 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V,
                             float* out, int32_t* idx, int32_t* route,
                             const mita_extras* extras,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Names of the kernels mita_forward_ex launches for this configuration and
+ * path, in launch order: "fused" for the fused schedule; "pool", "landmark",
+ * "route", "group", "attend" for the staged one.  Writes up to `capacity`
+ * static strings to names (may be NULL) and returns the kernel count, or a
+ * negative mita_status for invalid sizes or an unsupported path.  Host only.
+ */
+int mita_kernel_names(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
+                      mita_dtype in_dtype, int path, const char** names, int capacity);
 
 /* ---------------------------------------------------------------------------
  * The steps one at a time (same kernels as the staged schedule).  Each takes

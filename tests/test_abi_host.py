@@ -46,6 +46,19 @@ def test_workspace_bytes():
     assert ws(1, 1, 14, 14, 64, 15, 5, 25, mita.MITA_F32) == 0     # m_h > grid_h
 
 
+def test_kernel_names_follow_the_schedule():
+    names = mita.mita_kernel_names
+    assert names(256, 6, 14, 14, 64, 5, 5, 25, mita.MITA_BF16) == ["fused"]
+    staged = ["pool", "landmark", "route", "group", "attend"]
+    assert names(256, 6, 14, 14, 64, 5, 5, 25, mita.MITA_BF16, path="staged") == staged
+    assert names(32, 6, 56, 56, 64, 7, 7, 64, mita.MITA_BF16) == staged
+    assert names(1, 1, 14, 14, 64, 5, 5, 25, mita.MITA_F32) == staged
+    with pytest.raises(mita.MitaError):
+        names(32, 6, 56, 56, 64, 7, 7, 64, mita.MITA_BF16, path="fused")
+    with pytest.raises(mita.MitaError):
+        names(1, 1, 14, 14, 64, 5, 5, 0, mita.MITA_BF16)
+
+
 def test_schedule_choice():
     sched = mita.mita_schedule
     assert sched(256, 6, 14, 14, 64, 5, 5, 25, mita.MITA_BF16) == "fused"

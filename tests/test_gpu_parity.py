@@ -210,6 +210,32 @@ def test_deterministic_and_fully_written():
     assert torch.equal(out1, out2)
 
 
+@pytest.mark.parametrize("name,path", [("deit-s", "auto"), ("hires-3136", "auto")])
+def test_kernel_timing_events(name, path):
+    """The per-kernel events of mita_forward_ex bracket every kernel in order:
+    each interval is positive and they add up to the whole call."""
+    torch = _torch()
+    import efficient_attention_avg_amd as mita
+    w = synth.workload(name)
+    B = 8
+    Q, K, V = synth.workload_inputs(name, B=B)
+    q, k, v = (_to_dev(x, w["dtype"]) for x in (Q, K, V))
+    code = mita.MITA_BF16 if w["dtype"] == "bf16" else mita.MITA_F32
+    names = mita.mita_kernel_names(B, w["H"], w["grid_h"], w["grid_w"], 64, w["m_h"], w["m_w"],
+                                   w["k"], code, path=path)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    for e in ev:
+        e.record()
+    _say(f"timing events {name}: {names}")
+    mita.mita_forward_ex(q, k, v, w["grid_h"], w["grid_w"], w["m_h"], w["m_w"], w["k"],
+                         path=path, events=ev)
+    torch.cuda.synchronize()
+    dts = [ev[i].elapsed_time(ev[i + 1]) for i in range(len(names))]
+    assert all(dt > 0 for dt in dts), dts
+    total = ev[0].elapsed_time(ev[-1])
+    assert abs(sum(dts) - total) <= 1e-3 * max(total, 1e-3) + 1e-4, (dts, total)
+
+
 def test_constant_values_give_constant_output():
     import efficient_attention_avg_amd as mita
     torch = _torch()
