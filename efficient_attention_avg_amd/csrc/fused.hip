@@ -241,6 +241,11 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
   if (bh < BH)
     prefetch(pf, Q + bh * head_elems, K + bh * head_elems, V + bh * head_elems, N, threadIdx.x);
 
+  // the first head's rows are in before the loop, so that no wait for them
+  // is left pending at the loop head (where it would also wait for stores)
+  asm volatile("" ::"v"(pf.q[0]), "v"(pf.q[1]), "v"(pf.q[2]), "v"(pf.q[3]));
+  asm volatile("" ::"v"(pf.k[0]), "v"(pf.k[1]), "v"(pf.k[2]), "v"(pf.k[3]));
+  asm volatile("" ::"v"(pf.v0[0]), "v"(pf.v0[1]), "v"(pf.v1[0]), "v"(pf.v1[1]));
   for (; bh < BH; bh += gridDim.x) {
     // Thread coordinates are re-derived through an opaque zero every head so
     // that the compiler recomputes per-thread LDS addresses inside each phase
@@ -337,109 +342,124 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
         v[u] = ok ? *lds<float>(sm, OFF_S + (i * S_STRIDE + j) * 4) : -INFINITY;
         cand |= (ok ? 1u : 0u) << u;
       }
-      auto range = [&](uint32_t cm, float& lo, float& hi) {
-        float a = INFINITY, b = -INFINITY;
+      // one 256-bin histogram over the row's [min, max]: every key above the
+      // bin holding the k-th best is in; the rest come from that bin by rank
+      // (larger score first, ties to the lower key id)
+      float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < MAXNT; ++u)
-          if (cm >> u & 1u) { a = fminf(a, v[u]); b = fmaxf(b, v[u]); }
-        lo = g16_min(a);
-        hi = g16_max(b);
-      };
-      float lo, hi;
-      range(cand, lo, hi);
+      for (int u = 0; u < MAXNT; ++u)
+        if (cand >> u & 1u) { lo = fminf(lo, v[u]); hi = fmaxf(hi, v[u]); }
+      lo = g16_min(lo);
+      hi = g16_max(hi);
       const float rmax = hi;
-      uint32_t take = 0;
-      int need = active ? k : 0;
-      bool done = !active;
+      const float scale = hi > lo ? fminf(256.0f / (hi - lo), 1e30f) : 0.f;
+      auto bin = [&](float x) { return min(255, max(0, (int)((x - lo) * scale))); };
       const uint32_t below = (1u << t) - 1u;
       char* hrow = sm + OFF_H + i * H_STRIDE;
-      for (int pass = 0; pass < 64; ++pass) {
-        const int cc = g16_sumi(__popc(cand));
-        if (!done) {
-          if (need == cc) {
-            take |= cand;
-            cand = 0;
-            done = true;
-          } else if (!(hi > lo)) {
-            // every candidate ties: keep the lowest key ids
-            int run = 0;
+      *reinterpret_cast<u32x4*>(hrow + 32 * t) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(hrow + 32 * t + 16) = u32x4{0u, 0u, 0u, 0u};
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
-            for (int u = 0; u < MAXNT; ++u) {
-              const bool bit = cand >> u & 1u;
-              const uint32_t gm = g16_bits(__ballot(bit), g);
-              const int rank = run + __popc(gm & below);
-              if (bit && rank < need) take |= 1u << u;
-              run += __popc(gm);
-            }
-            cand = 0;
-            done = true;
-          }
+      for (int u = 0; u < MAXNT; ++u)
+        if (cand >> u & 1u) {
+          const int b = bin(v[u]);
+          atomicAdd(reinterpret_cast<uint32_t*>(hrow + (b >> 1) * 4), 1u << (16 * (b & 1)));
         }
-        if (__ballot(!done) == 0) break;
-        if (!done) {
-          const float scale = 256.0f / (hi - lo);
-          // clear this row's 256 packed 16-bit bins (128 dwords, 8 per lane)
-          *reinterpret_cast<u32x4*>(hrow + 32 * t) = u32x4{0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4*>(hrow + 32 * t + 16) = u32x4{0u, 0u, 0u, 0u};
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      int bstar = 0, above = 0, inbin = 0;
+      {
+        const u32x4 d0 = *reinterpret_cast<const u32x4*>(hrow + 32 * t);
+        const u32x4 d1 = *reinterpret_cast<const u32x4*>(hrow + 32 * t + 16);
+        // bin 16t + q holds (q < 8 ? d0 : d1)[(q & 7) >> 1], half q & 1
+        auto cnt = [&](int q) -> int {
+          const uint32_t dw = (q < 8 ? d0 : d1)[(q & 7) >> 1];
+          return (q & 1) ? (int)(dw >> 16) : (int)(dw & 0xFFFFu);
+        };
+        int local = 0;
 #pragma unroll
-          for (int u = 0; u < MAXNT; ++u)
-            if (cand >> u & 1u) {
-              const int b = min(255, (int)((v[u] - lo) * scale));
-              atomicAdd(reinterpret_cast<uint32_t*>(hrow + (b >> 1) * 4), 1u << (16 * (b & 1)));
-            }
-          __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          const u32x4 d0 = *reinterpret_cast<const u32x4*>(hrow + 32 * t);
-          const u32x4 d1 = *reinterpret_cast<const u32x4*>(hrow + 32 * t + 16);
-          // bin 16t + q holds (q < 8 ? d0 : d1)[(q & 7) >> 1], half q & 1
-          auto cnt = [&](int q) -> int {
-            const uint32_t dw = (q < 8 ? d0 : d1)[(q & 7) >> 1];
-            return (q & 1) ? (int)(dw >> 16) : (int)(dw & 0xFFFFu);
-          };
-          int local = 0;
+        for (int q = 0; q < 4; ++q)
+          local += (int)((d0[q] & 0xFFFFu) + (d0[q] >> 16) + (d1[q] & 0xFFFFu) + (d1[q] >> 16));
+        // inclusive suffix sum over the group's lanes (higher lane = higher bins)
+        const int suf = g16_suffix_sum(local);
+        const int abv = suf - local;
+        const bool mine = active && abv < k && k <= suf;
+        if (mine) {
+          int acc = abv;
+          bool found = false;
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            local += (int)((d0[q] & 0xFFFFu) + (d0[q] >> 16) + (d1[q] & 0xFFFFu) + (d1[q] >> 16));
-          // inclusive suffix sum over the group's lanes (higher lane = higher bins)
-          const int suf = g16_suffix_sum(local);
-          const int above = suf - local;
-          const bool mine = above < need && need <= suf;
-          int bstar = 0, abv = above;
-          if (mine) {
-            int acc = above;
-            bool found = false;
-#pragma unroll
-            for (int q = 15; q >= 0; --q) {
-              if (!found) {
-                const int cq = cnt(q);
-                if (acc + cq >= need) {
-                  found = true;
-                  bstar = 16 * t + q;
-                  abv = acc;
-                } else {
-                  acc += cq;
-                }
+          for (int q = 15; q >= 0; --q) {
+            if (!found) {
+              const int cq = cnt(q);
+              if (acc + cq >= k) {
+                found = true;
+                bstar = 16 * t + q;
+                above = acc;
+                inbin = cq;
+              } else {
+                acc += cq;
               }
             }
           }
-          // exactly one lane of the group is `mine`: a masked group sum broadcasts
-          bstar = g16_sumi(mine ? bstar : 0);
-          abv = g16_sumi(mine ? abv : 0);
-          uint32_t nc = 0;
-#pragma unroll
-          for (int u = 0; u < MAXNT; ++u)
-            if (cand >> u & 1u) {
-              const int b = min(255, (int)((v[u] - lo) * scale));
-              if (b > bstar) take |= 1u << u;
-              if (b == bstar) nc |= 1u << u;
-            }
-          need -= abv;
-          cand = nc;
         }
-        range(cand, lo, hi);
+        // exactly one lane of the group is `mine`: a masked group sum broadcasts
+        bstar = g16_sumi(mine ? bstar : 0);
+        above = g16_sumi(mine ? above : 0);
+        inbin = g16_sumi(mine ? inbin : 0);
       }
+      uint32_t take = 0, bnd = 0;
+#pragma unroll
+      for (int u = 0; u < MAXNT; ++u)
+        if (cand >> u & 1u) {
+          const int b = bin(v[u]);
+          if (b > bstar) take |= 1u << u;
+          if (b == bstar) bnd |= 1u << u;
+        }
+      // the boundary bin's entries as (score, key) pairs over the histogram
+      // bytes (66 fit); each ranks itself among them
+      const int need = k - above;
+      const bool listed = inbin <= H_STRIDE / 8;
+      float* list = reinterpret_cast<float*>(hrow);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      if (listed) {
+        int run = 0;
+#pragma unroll
+        for (int u = 0; u < MAXNT; ++u) {
+          const bool bit = bnd >> u & 1u;
+          const uint32_t gm = g16_bits(__ballot(bit), g);
+          if (bit) {
+            const int pos = run + __popc(gm & below);
+            list[2 * pos] = v[u];
+            list[2 * pos + 1] = __int_as_float(t + 16 * u);
+          }
+          run += __popc(gm);
+        }
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int u = 0; u < MAXNT; ++u)
+        if (bnd >> u & 1u) {
+          const float x = v[u];
+          const int key = t + 16 * u;
+          int r = 0;
+          if (listed) {
+            for (int e = 0; e < inbin; ++e) {
+              const float y = list[2 * e];
+              const int ky = __float_as_int(list[2 * e + 1]);
+              r += (y > x || (y == x && ky < key)) ? 1 : 0;
+            }
+          } else {
+            // many equal scores: rank against the row's scores in the boundary bin
+            for (int j = 0; j < N; ++j) {
+              const float y = *lds<float>(sm, OFF_S + (i * S_STRIDE + j) * 4);
+              r += (bin(y) == bstar && (y > x || (y == x && j < key))) ? 1 : 0;
+            }
+          }
+          if (r < need) take |= 1u << u;
+        }
       // the expert: kept key ids in ascending order
       {
         int run = 0;
@@ -619,6 +639,12 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
     __syncthreads();
 
     // ---------------- G: grouped expert attention, one <=16-query tile at a time
+    // The next head's rows must have arrived before this phase's output stores
+    // are issued: loads and stores drain through one counter, so waiting for
+    // them later would also wait for every store.
+    asm volatile("" ::"v"(pf.q[0]), "v"(pf.q[1]), "v"(pf.q[2]), "v"(pf.q[3]));
+    asm volatile("" ::"v"(pf.k[0]), "v"(pf.k[1]), "v"(pf.k[2]), "v"(pf.k[3]));
+    asm volatile("" ::"v"(pf.v0[0]), "v"(pf.v0[1]), "v"(pf.v1[0]), "v"(pf.v1[1]));
     {
       // V_L^T fragments, the A operand of the shared half of every tile: lane
       // holds V_L^T[ch 16ct + c16][landmarks 4g..4g+3, 16+4g..16+4g+3]
