@@ -4,25 +4,28 @@
 // "NeurIPS'26：注意力也是FFN？从快权重出发，重新理解高效注意力", section
 // "用少量地标查询，同时构造全局概括与细节专家" and Algorithm 1.
 //
-// A head's Q, K and V (75 KB in bf16) fit in LDS with room for the score
-// matrix, so every step runs out of LDS and each input byte crosses HBM once:
-//   A  stage Q, K (bf16, XOR-swizzled rows) and V^T (f16, keys contiguous)
-//      into LDS; issue the NEXT head's global loads into registers so they
-//      fly during this head's compute (persistent grid, one 8-wave
-//      workgroup per CU);
-//   B  landmark pooling -> Q_L (fp32) split into bf16 hi + lo;
-//   C  S^T = K Q_L^T and R = Q Q_L^T on bf16 MFMA (hi + lo: near-fp32 scores,
-//      so top-k sets and routes are decided at fp32 accuracy); routes are a
-//      16-lane argmax over R with ties to the lower landmark;
-//   D  per landmark row, exact top-k by value-range histogram refinement
-//      (ties to the lower key id), then P = exp(S - max) in f16;
+// A persistent grid of 4-wave workgroups, two per CU, each walking heads.  A
+// head needs 67 KB of LDS, so two heads are in flight per CU and one's
+// barrier-bound phases overlap the other's work.  Q and K rows are read
+// straight from global memory (L2 after first touch) as MFMA operands; only
+// the transposed values, scores, histograms and small tables live in LDS:
+//   B  landmark pooling from the Q rows -> Q_L (fp32), split bf16 hi + lo;
+//   C  S^T = K Q_L^T on bf16 MFMA (hi + lo: near-fp32 scores, so top-k sets
+//      and routes are decided at fp32 accuracy), into the shared region X;
+//   D  per landmark row, exact top-k: one 256-bin histogram over the row's
+//      range, every key above the k-th best's bin taken, that bin's keys by
+//      rank (ties to the lower key id); then P = exp(S - max) in f16;
+//   V  V^T (f16, keys contiguous), loaded into registers at the head's start,
+//      replaces the scores in X;
 //   E  V_L^T = V^T P^T on f16 MFMA, normalised by the row sums;
+//   E' R^T = Q_L Q^T per token tile: routes by a 16-lane argmax (ties to the
+//      lower landmark);
 //   F  stable counting sort of the queries by route (ballots) and a list of
 //      <= 16-query tiles per expert;
-//   G  per tile: logits^T = [Q_L; K_e] Q_g^T (bf16 MFMA, K_e rows read in
-//      place from LDS), one softmax over the m + k entries per query, and
-//      out^T = [V_L; V_e]^T P^T (f16 MFMA, P fed straight from the logits'
-//      accumulators), written as fp32.
+//   G  per tile: logits^T = [Q_L; K_e] Q_g^T (bf16 MFMA; the shared half
+//      recomputed from Q_L, K_e rows gathered from global memory), one
+//      softmax over the m + k entries per query, and out^T = [V_L; V_e]^T P^T
+//      (f16 MFMA, P fed straight from the logits' accumulators), in fp32.
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
@@ -33,7 +36,7 @@ namespace fused {
 constexpr int MAXNT = 13;           // 16-token tiles
 constexpr int NP = MAXNT * 16;      // 208 padded tokens
 constexpr int KPMAX = 224;          // keys padded to a multiple of 32 (P V k-steps)
-constexpr int THREADS = 512;
+constexpr int THREADS = 256;
 constexpr int NWAVES = THREADS / 64;
 constexpr int MMAX = 32, KMAX = 32;
 
@@ -42,11 +45,9 @@ constexpr int S_STRIDE = 212;       // floats per score row
 constexpr int H_STRIDE = 528;       // bytes per histogram / P row
 constexpr int VLT_STRIDE = 80;      // bytes per V_L^T row (f16 landmarks)
 
-constexpr int OFF_Q = 0;
-constexpr int OFF_K = OFF_Q + NP * 128;
-constexpr int OFF_VT = OFF_K + NP * 128;
-constexpr int OFF_S = OFF_VT + 64 * VT_STRIDE;
-constexpr int OFF_H = OFF_S + MMAX * S_STRIDE * 4;
+constexpr int X_BYTES = 64 * VT_STRIDE > MMAX * S_STRIDE * 4 ? 64 * VT_STRIDE : MMAX * S_STRIDE * 4;
+constexpr int OFF_X = 0;                          // S (phases C, D), then V^T (E, G)
+constexpr int OFF_H = OFF_X + X_BYTES;
 constexpr int OFF_QLH = OFF_H + MMAX * H_STRIDE;
 constexpr int OFF_QLL = OFF_QLH + MMAX * 128;
 constexpr int OFF_VLT = OFF_QLL + MMAX * 128;
@@ -59,9 +60,9 @@ constexpr int OFF_OFFS = OFF_BASE + 4 * 32 * 4;   // [33] int
 constexpr int OFF_TILES = OFF_OFFS + 48 * 4;      // [64] x (e, start, len, -)
 constexpr int OFF_STAT = OFF_TILES + 64 * 16;     // rowmax[32], rowsum[32], ntiles
 constexpr int LDS_BYTES = OFF_STAT + 80 * 4;
-static_assert(LDS_BYTES <= 160 * 1024, "LDS budget of one gfx950 workgroup");
-static_assert(OFF_VT % 16 == 0 && OFF_S % 16 == 0 && OFF_H % 16 == 0 && OFF_QLH % 16 == 0 &&
-                  OFF_VLT % 16 == 0 && OFF_IDX % 16 == 0 && OFF_TILES % 16 == 0,
+static_assert(2 * LDS_BYTES <= 160 * 1024, "two workgroups per gfx950 CU");
+static_assert(OFF_H % 16 == 0 && OFF_QLH % 16 == 0 && OFF_VLT % 16 == 0 && OFF_IDX % 16 == 0 &&
+                  OFF_TILES % 16 == 0,
               "16-byte aligned LDS regions");
 
 struct Outputs {
@@ -176,56 +177,42 @@ __device__ __forceinline__ void load_ql(char* sm, u32x4 (&qlh)[2][2], u32x4 (&ql
     }
 }
 
-struct Prefetch {
-  u32x4 q[4], k[4], v0[2], v1[2];
+// The head's V rows for the transposed copy: key pairs (2p, 2p+1) of 8-channel
+// chunk c, items tid + THREADS i (c = item / 112, p = item % 112).
+struct VRows {
+  u32x4 v0[4], v1[4];
 };
 
-__device__ __forceinline__ void prefetch(Prefetch& pf, const uint16_t* Qh, const uint16_t* Kh,
-                                         const uint16_t* Vh, int N, int tid) {
+__device__ __forceinline__ void load_v(VRows& vr, const uint16_t* Vh, int N, int tid) {
   const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int id = tid + THREADS * i, row = id >> 3, c = id & 7;
-    const bool ok = row < N;
-    pf.q[i] = ok ? *reinterpret_cast<const u32x4*>(Qh + row * 64 + c * 8) : z;
-    pf.k[i] = ok ? *reinterpret_cast<const u32x4*>(Kh + row * 64 + c * 8) : z;
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
     const int id = tid + THREADS * i;
     const int c = id / (KPMAX / 2), p = id % (KPMAX / 2);
     const int j0 = 2 * p, j1 = 2 * p + 1;
-    pf.v0[i] = (c < 8 && j0 < N) ? *reinterpret_cast<const u32x4*>(Vh + j0 * 64 + c * 8) : z;
-    pf.v1[i] = (c < 8 && j1 < N) ? *reinterpret_cast<const u32x4*>(Vh + j1 * 64 + c * 8) : z;
+    vr.v0[i] = (c < 8 && j0 < N) ? *reinterpret_cast<const u32x4*>(Vh + j0 * 64 + c * 8) : z;
+    vr.v1[i] = (c < 8 && j1 < N) ? *reinterpret_cast<const u32x4*>(Vh + j1 * 64 + c * 8) : z;
   }
 }
 
-__device__ __forceinline__ void stage(const Prefetch& pf, char* sm, int tid) {
+__device__ __forceinline__ void store_vt(const VRows& vr, char* sm, int tid) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int id = tid + THREADS * i, row = id >> 3, c = id & 7;
-    if (row < NP) {
-      *lds<u32x4>(sm, OFF_Q + rc(row, c)) = pf.q[i];
-      *lds<u32x4>(sm, OFF_K + rc(row, c)) = pf.k[i];
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
     const int id = tid + THREADS * i;
     const int c = id / (KPMAX / 2), p = id % (KPMAX / 2);
     if (c < 8) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const uint32_t a = (pf.v0[i][t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
-        const uint32_t b = (pf.v1[i][t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
-        const uint32_t w = pack2(f16_bits(bf16_bits_to_f32(a)), f16_bits(bf16_bits_to_f32(b)));
-        *lds<uint32_t>(sm, OFF_VT + (8 * c + t) * VT_STRIDE + 4 * p) = w;
+        const uint32_t a = (vr.v0[i][t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
+        const uint32_t b = (vr.v1[i][t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
+        *lds<uint32_t>(sm, OFF_X + (8 * c + t) * VT_STRIDE + 4 * p) =
+            pk_f16(bf16_bits_to_f32(a), bf16_bits_to_f32(b));
       }
     }
   }
 }
 
-__global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
+__global__ __launch_bounds__(THREADS, 2) void mita_fused_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, Outputs o, int BH, int gh, int gw, int mh, int mw, int k) {
   __shared__ __attribute__((aligned(16))) char sm[LDS_BYTES];
@@ -235,51 +222,40 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
   const float tau = 0.125f;  // 1/sqrt(64)
   const float kLogitScale = tau * 1.4426950408889634f;  // tau * log2(e): base-2 softmax
   const size_t head_elems = (size_t)N * 64;
+  const u32x4 z = {0u, 0u, 0u, 0u};
 
-  Prefetch pf;
-  int bh = blockIdx.x;
-  if (bh < BH)
-    prefetch(pf, Q + bh * head_elems, K + bh * head_elems, V + bh * head_elems, N, threadIdx.x);
-
-  // the first head's rows are in before the loop, so that no wait for them
-  // is left pending at the loop head (where it would also wait for stores)
-  asm volatile("" ::"v"(pf.q[0]), "v"(pf.q[1]), "v"(pf.q[2]), "v"(pf.q[3]));
-  asm volatile("" ::"v"(pf.k[0]), "v"(pf.k[1]), "v"(pf.k[2]), "v"(pf.k[3]));
-  asm volatile("" ::"v"(pf.v0[0]), "v"(pf.v0[1]), "v"(pf.v1[0]), "v"(pf.v1[1]));
-  for (; bh < BH; bh += gridDim.x) {
+  for (int bh = blockIdx.x; bh < BH; bh += gridDim.x) {
     // Thread coordinates are re-derived through an opaque zero every head so
     // that the compiler recomputes per-thread LDS addresses inside each phase
     // instead of hoisting them all out of the loop and pinning registers.
     const int tid = threadIdx.x + opaque_zero(), lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
-    // ---------------- A: stage this head, prefetch the next one
-    __syncthreads();
-    stage(pf, sm, tid);
-    __syncthreads();
-    {
-      const int nx = bh + gridDim.x;
-      if (nx < BH)
-        prefetch(pf, Q + nx * head_elems, K + nx * head_elems, V + nx * head_elems, N, tid);
-    }
+    const uint16_t* Qh = Q + bh * head_elems;
+    const uint16_t* Kh = K + bh * head_elems;
+    const uint16_t* Vh = V + bh * head_elems;
+    // the head's V rows fly while pooling, scores and top-k run
+    VRows vr;
+    load_v(vr, Vh, N, tid);
+    __syncthreads();  // the previous head is done with LDS
 
-    // ---------------- B: landmark pooling (one thread per landmark x 4 channels)
-    {
-      const int i = tid >> 4, q4 = tid & 15;  // 32 landmark slots x 16 channel quads
+    // ---------------- B: landmark pooling from the Q rows (landmark x 4 channels)
+    for (int it = tid; it < MMAX * 16; it += THREADS) {
+      const int i = it >> 4, q4 = it & 15;
       float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
       if (i < m) {
         const int r = i / mw, c = i % mw;
         int y0, y1, x0, x1;
         pool_window(r, gh, mh, &y0, &y1);
         pool_window(c, gw, mw, &x0, &x1);
-        const int co = (q4 & 1) * 8;
         for (int y = y0; y < y1; ++y) {
-          // issue up to four row reads before consuming any (LDS latency)
+          // four columns' loads in flight before any is consumed
           for (int x = x0; x < x1; x += 4) {
             u32x2 v[4];
 #pragma unroll
             for (int dx = 0; dx < 4; ++dx)
-              v[dx] = x + dx < x1 ? *lds<u32x2>(sm, OFF_Q + rc(y * gw + x + dx, q4 >> 1) + co)
-                                  : u32x2{0u, 0u};
+              v[dx] = x + dx < x1
+                          ? *reinterpret_cast<const u32x2*>(Qh + (size_t)(y * gw + x + dx) * 64 + 4 * q4)
+                          : u32x2{0u, 0u};
 #pragma unroll
             for (int dx = 0; dx < 4; ++dx) {
               a0 += bf16_bits_to_f32(v[dx][0] & 0xFFFFu);
@@ -308,29 +284,43 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
     }
     __syncthreads();
 
-    // ---------------- C: S^T = K Q_L^T, written to LDS row = landmark
-    for (int tt = w; tt < nt; tt += NWAVES) {
+    // ---------------- C: S^T = K Q_L^T (K rows from global memory) -> S rows in X
+    {
       u32x4 qlh[2][2], qll[2][2];
       load_ql(sm, qlh, qll, g, c16);
-      const u32x4 a0 = *lds<u32x4>(sm, OFF_K + rc(16 * tt + c16, g));
-      const u32x4 a1 = *lds<u32x4>(sm, OFF_K + rc(16 * tt + c16, 4 + g));
+      u32x4 ka[4][2];
 #pragma unroll
-      for (int lt = 0; lt < 2; ++lt) {
-        f32x4 c = zero4();
-        c = mfma_bf16(a0, qlh[lt][0], c);
-        c = mfma_bf16(a0, qll[lt][0], c);
-        c = mfma_bf16(a1, qlh[lt][1], c);
-        c = mfma_bf16(a1, qll[lt][1], c);
-        // lane holds S^T[key 16tt + 4g + r][landmark 16lt + c16]
-        *lds<float4>(sm, OFF_S + ((16 * lt + c16) * S_STRIDE + 16 * tt + 4 * g) * 4) =
-            make_float4(c[0] * tau, c[1] * tau, c[2] * tau, c[3] * tau);
+      for (int j = 0; j < 4; ++j) {
+        const int tt = w + NWAVES * j, key = 16 * tt + c16;
+        const bool ok = tt < nt && key < N;
+        const uint16_t* kr = Kh + (size_t)(ok ? key : 0) * 64;
+        ka[j][0] = ok ? *reinterpret_cast<const u32x4*>(kr + 8 * g) : z;
+        ka[j][1] = ok ? *reinterpret_cast<const u32x4*>(kr + 32 + 8 * g) : z;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tt = w + NWAVES * j;
+        if (tt < nt) {
+#pragma unroll
+          for (int lt = 0; lt < 2; ++lt) {
+            f32x4 c = zero4();
+            c = mfma_bf16(ka[j][0], qlh[lt][0], c);
+            c = mfma_bf16(ka[j][0], qll[lt][0], c);
+            c = mfma_bf16(ka[j][1], qlh[lt][1], c);
+            c = mfma_bf16(ka[j][1], qll[lt][1], c);
+            // lane holds S^T[key 16tt + 4g + r][landmark 16lt + c16]
+            *lds<float4>(sm, OFF_X + ((16 * lt + c16) * S_STRIDE + 16 * tt + 4 * g) * 4) =
+                make_float4(c[0] * tau, c[1] * tau, c[2] * tau, c[3] * tau);
+          }
+        }
       }
     }
     __syncthreads();
 
     // ---------------- D: exact top-k of each landmark row; then P = exp(S - max) in f16
-    {
-      const int i = 4 * w + g;           // landmark row of this 16-lane group
+#pragma unroll 1
+    for (int jr = 0; jr < MMAX / 16; ++jr) {
+      const int i = 4 * w + g + 16 * jr;  // landmark row of this 16-lane group
       const bool active = i < m;
       const int t = c16;
       float v[MAXNT];
@@ -339,7 +329,7 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
       for (int u = 0; u < MAXNT; ++u) {
         const int j = t + 16 * u;
         const bool ok = active && u < nt && j < N;
-        v[u] = ok ? *lds<float>(sm, OFF_S + (i * S_STRIDE + j) * 4) : -INFINITY;
+        v[u] = ok ? *lds<float>(sm, OFF_X + (i * S_STRIDE + j) * 4) : -INFINITY;
         cand |= (ok ? 1u : 0u) << u;
       }
       // one 256-bin histogram over the row's [min, max]: every key above the
@@ -454,7 +444,7 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
           } else {
             // many equal scores: rank against the row's scores in the boundary bin
             for (int j = 0; j < N; ++j) {
-              const float y = *lds<float>(sm, OFF_S + (i * S_STRIDE + j) * 4);
+              const float y = *lds<float>(sm, OFF_X + (i * S_STRIDE + j) * 4);
               r += (bin(y) == bstar && (y > x || (y == x && j < key))) ? 1 : 0;
             }
           }
@@ -499,12 +489,19 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
     }
     __syncthreads();
 
-    // ---------------- E: V_L^T = V^T P^T (one 16-channel x 16-landmark tile per wave)
-    {
-      const int ct = w & 3, lt = w >> 2;
+    __syncthreads();  // the scores are no longer needed
+
+    // ---------------- V: V^T (f16) over the score region
+    store_vt(vr, sm, tid);
+    __syncthreads();
+
+    // ---------------- E: V_L^T = V^T P^T (16-channel x 16-landmark tiles)
+#pragma unroll 1
+    for (int tile = w; tile < 8; tile += NWAVES) {
+      const int ct = tile & 3, lt = tile >> 2;
       f32x4 acc = zero4();
       for (int ks = 0; ks < KP / 32; ++ks) {
-        const u32x4 a = *lds<u32x4>(sm, OFF_VT + (16 * ct + c16) * VT_STRIDE + (32 * ks + 8 * g) * 2);
+        const u32x4 a = *lds<u32x4>(sm, OFF_X + (16 * ct + c16) * VT_STRIDE + (32 * ks + 8 * g) * 2);
         const u32x4 b = *lds<u32x4>(sm, OFF_H + (16 * lt + c16) * H_STRIDE + (32 * ks + 8 * g) * 2);
         acc = mfma_f16(a, b, acc);
       }
@@ -524,24 +521,32 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
       }
     }
 
-    // ---------------- E': R^T = Q_L Q^T per token tile: routes, and the shared
-    // expert's logits (the same query-landmark scores, scaled by tau*log2 e for
-    // a base-2 softmax) into the score region, which is free after D.
+    // ---------------- E': R^T = Q_L Q^T per token tile (Q rows from global memory): routes
     {
       u32x4 qlh[2][2], qll[2][2];
       load_ql(sm, qlh, qll, g, c16);
-      for (int tt = w; tt < nt; tt += NWAVES) {
+      u32x4 qb[4][2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tok = 16 * (w + NWAVES * j) + c16;
+        const bool ok = tok < N;
+        const uint16_t* qr = Qh + (size_t)(ok ? tok : 0) * 64;
+        qb[j][0] = ok ? *reinterpret_cast<const u32x4*>(qr + 8 * g) : z;
+        qb[j][1] = ok ? *reinterpret_cast<const u32x4*>(qr + 32 + 8 * g) : z;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int tt = w + NWAVES * j;
+        if (tt >= nt) break;
         const int tok = 16 * tt + c16;
-        const u32x4 b0 = *lds<u32x4>(sm, OFF_Q + rc(tok, g));
-        const u32x4 b1 = *lds<u32x4>(sm, OFF_Q + rc(tok, 4 + g));
         f32x4 acc[2];
 #pragma unroll
         for (int lt = 0; lt < 2; ++lt) {
           f32x4 c = zero4();
-          c = mfma_bf16(qlh[lt][0], b0, c);
-          c = mfma_bf16(qll[lt][0], b0, c);
-          c = mfma_bf16(qlh[lt][1], b1, c);
-          c = mfma_bf16(qll[lt][1], b1, c);
+          c = mfma_bf16(qlh[lt][0], qb[j][0], c);
+          c = mfma_bf16(qll[lt][0], qb[j][0], c);
+          c = mfma_bf16(qlh[lt][1], qb[j][1], c);
+          c = mfma_bf16(qll[lt][1], qb[j][1], c);
           acc[lt] = c;  // lane holds R[token tok][landmark 16lt + 4g + r]
         }
         float best = -INFINITY;
@@ -563,15 +568,6 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
         if (g == 0 && tok < N) {
           *lds<int>(sm, OFF_ROUTE + tok * 4) = bi;
           if (o.route) o.route[(size_t)bh * N + tok] = bi;
-        }
-#pragma unroll
-        for (int lt = 0; lt < 2; ++lt) {
-          float4 lg;
-          lg.x = 16 * lt + 4 * g + 0 < m ? acc[lt][0] * kLogitScale : -INFINITY;
-          lg.y = 16 * lt + 4 * g + 1 < m ? acc[lt][1] * kLogitScale : -INFINITY;
-          lg.z = 16 * lt + 4 * g + 2 < m ? acc[lt][2] * kLogitScale : -INFINITY;
-          lg.w = 16 * lt + 4 * g + 3 < m ? acc[lt][3] * kLogitScale : -INFINITY;
-          *lds<float4>(sm, OFF_S + rc(tok, 4 * lt + g)) = lg;
         }
       }
     }
@@ -639,13 +635,9 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
     __syncthreads();
 
     // ---------------- G: grouped expert attention, one <=16-query tile at a time
-    // The next head's rows must have arrived before this phase's output stores
-    // are issued: loads and stores drain through one counter, so waiting for
-    // them later would also wait for every store.
-    asm volatile("" ::"v"(pf.q[0]), "v"(pf.q[1]), "v"(pf.q[2]), "v"(pf.q[3]));
-    asm volatile("" ::"v"(pf.k[0]), "v"(pf.k[1]), "v"(pf.k[2]), "v"(pf.k[3]));
-    asm volatile("" ::"v"(pf.v0[0]), "v"(pf.v0[1]), "v"(pf.v1[0]), "v"(pf.v1[1]));
     {
+      u32x4 qlh[2][2], qll[2][2];
+      load_ql(sm, qlh, qll, g, c16);
       // V_L^T fragments, the A operand of the shared half of every tile: lane
       // holds V_L^T[ch 16ct + c16][landmarks 4g..4g+3, 16+4g..16+4g+3]
       u32x4 avl[4];
@@ -665,31 +657,43 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
         // query 0 and are never stored
         const bool live = c16 < len;
         const int qi = live ? *lds<int>(sm, OFF_PERM + (start + c16) * 4) : 0;
-        const u32x4 bq0 = *lds<u32x4>(sm, OFF_Q + rc(qi, g));
-        const u32x4 bq1 = *lds<u32x4>(sm, OFF_Q + rc(qi, 4 + g));
-        // shared logits (base 2, -inf past m), from the route step
-        const f32x4 ls0 = *lds<f32x4>(sm, OFF_S + rc(qi, g));
-        const f32x4 ls1 = *lds<f32x4>(sm, OFF_S + rc(qi, 4 + g));
-        // routed logits^T = K_e Q_g^T; slot rows past k are zero and masked below
+        // the expert's key rows for this lane's two slot tiles, and the query rows
         const int* idxe = lds<int>(sm, OFF_IDX + e * KMAX * 4);
-        f32x4 lr[2];
+        u32x4 ak[2][2];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           const int slot = 16 * st + c16;
-          const int key = slot < k ? idxe[slot] : 0;
-          const u32x4 z = {0u, 0u, 0u, 0u};
-          const u32x4 ak0 = slot < k ? *lds<u32x4>(sm, OFF_K + rc(key, g)) : z;
-          const u32x4 ak1 = slot < k ? *lds<u32x4>(sm, OFF_K + rc(key, 4 + g)) : z;
+          const bool ok = slot < k;
+          const uint16_t* kr = Kh + (size_t)(ok ? idxe[slot] : 0) * 64;
+          ak[st][0] = ok ? *reinterpret_cast<const u32x4*>(kr + 8 * g) : z;
+          ak[st][1] = ok ? *reinterpret_cast<const u32x4*>(kr + 32 + 8 * g) : z;
+        }
+        const uint16_t* qrow = Qh + (size_t)qi * 64;
+        const u32x4 bq0 = *reinterpret_cast<const u32x4*>(qrow + 8 * g);
+        const u32x4 bq1 = *reinterpret_cast<const u32x4*>(qrow + 32 + 8 * g);
+        // shared logits^T = Q_L Q_g^T (hi + lo) and routed logits^T = K_e Q_g^T
+        f32x4 ls[2], lr[2];
+#pragma unroll
+        for (int lt = 0; lt < 2; ++lt) {
           f32x4 c = zero4();
-          c = mfma_bf16(ak0, bq0, c);
-          c = mfma_bf16(ak1, bq1, c);
+          c = mfma_bf16(qlh[lt][0], bq0, c);
+          c = mfma_bf16(qll[lt][0], bq0, c);
+          c = mfma_bf16(qlh[lt][1], bq1, c);
+          c = mfma_bf16(qll[lt][1], bq1, c);
+          ls[lt] = c;
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          f32x4 c = zero4();
+          c = mfma_bf16(ak[st][0], bq0, c);
+          c = mfma_bf16(ak[st][1], bq1, c);
           lr[st] = c;
         }
         float x[16];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          x[r] = ls0[r];
-          x[4 + r] = ls1[r];
+          x[r] = 4 * g + r < m ? ls[0][r] * kLogitScale : -INFINITY;
+          x[4 + r] = 16 + 4 * g + r < m ? ls[1][r] * kLogitScale : -INFINITY;
           x[8 + r] = 4 * g + r < k ? lr[0][r] * kLogitScale : -INFINITY;
           x[12 + r] = 16 + 4 * g + r < k ? lr[1][r] * kLogitScale : -INFINITY;
         }
@@ -725,7 +729,7 @@ __global__ __launch_bounds__(THREADS, 1) void mita_fused_kernel(
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
           const uint16_t* vrow =
-              reinterpret_cast<const uint16_t*>(sm + OFF_VT + (16 * ct + c16) * VT_STRIDE);
+              reinterpret_cast<const uint16_t*>(sm + OFF_X + (16 * ct + c16) * VT_STRIDE);
           const u32x4 ave = {pack2(vrow[keys[0]], vrow[keys[1]]), pack2(vrow[keys[2]], vrow[keys[3]]),
                              pack2(vrow[keys[4]], vrow[keys[5]]), pack2(vrow[keys[6]], vrow[keys[7]])};
           f32x4 acc = zero4();
@@ -758,7 +762,9 @@ hipError_t launch_fused(const void* Q, const void* K, const void* V, float* out,
                         int32_t* route, float* ql, float* vl, int32_t* counts, int32_t* offsets,
                         int32_t* perm, const Shape& s, hipStream_t st) {
   fused::Outputs o{out, idx, route, ql, vl, counts, offsets, perm};
-  const int grid = s.BH < device_cu_count() ? s.BH : device_cu_count();
+  // two resident workgroups per CU, each walking heads
+  const int slots = 2 * device_cu_count();
+  const int grid = s.BH < slots ? s.BH : slots;
   fused::mita_fused_kernel<<<grid, fused::THREADS, 0, st>>>(
       (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, o, s.BH, s.grid_h, s.grid_w,
       s.m_h, s.m_w, s.k);
