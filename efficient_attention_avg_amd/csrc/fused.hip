@@ -158,6 +158,21 @@ __device__ __forceinline__ void g16_argmax(float& v, int& i) {
   MITA_ARGMAX_STEP(DPP_MIRROR)
 #undef MITA_ARGMAX_STEP
 }
+// (value, key) argmax over a 16-lane group: larger value, ties to the lower
+// key (keys distinct; empty lanes hold -inf and INT_MAX).
+__device__ __forceinline__ void g16_argmax_key(float& v, int& key) {
+#define MITA_ARGMAX_KEY_STEP(CTRL)                                    \
+  {                                                                    \
+    const float ov = dpp_f<CTRL>(v);                                   \
+    const int ok = dpp_i<CTRL>(key);                                   \
+    if (ov > v || (ov == v && ok < key)) { v = ov; key = ok; }         \
+  }
+  MITA_ARGMAX_KEY_STEP(DPP_XOR1)
+  MITA_ARGMAX_KEY_STEP(DPP_XOR2)
+  MITA_ARGMAX_KEY_STEP(DPP_HALF_MIRROR)
+  MITA_ARGMAX_KEY_STEP(DPP_MIRROR)
+#undef MITA_ARGMAX_KEY_STEP
+}
 // This lane's 16-lane group's bits of a wave ballot.
 __device__ __forceinline__ uint32_t g16_bits(uint64_t ballot, int g) {
   return (uint32_t)(ballot >> (16 * g)) & 0xFFFFu;
@@ -321,135 +336,94 @@ __global__ __launch_bounds__(THREADS, 2) void mita_fused_kernel(
 #pragma unroll 1
     for (int jr = 0; jr < MMAX / 16; ++jr) {
       const int i = 4 * w + g + 16 * jr;  // landmark row of this 16-lane group
+      if (__ballot(i < m) == 0) continue;
       const bool active = i < m;
       const int t = c16;
+      // this lane's scores (keys t + 16u); -inf marks none
       float v[MAXNT];
-      uint32_t cand = 0;
 #pragma unroll
       for (int u = 0; u < MAXNT; ++u) {
         const int j = t + 16 * u;
-        const bool ok = active && u < nt && j < N;
-        v[u] = ok ? *lds<float>(sm, OFF_X + (i * S_STRIDE + j) * 4) : -INFINITY;
-        cand |= (ok ? 1u : 0u) << u;
+        v[u] = active && j < N ? *lds<float>(sm, OFF_X + (i * S_STRIDE + j) * 4) : -INFINITY;
       }
-      // one 256-bin histogram over the row's [min, max]: every key above the
-      // bin holding the k-th best is in; the rest come from that bin by rank
-      // (larger score first, ties to the lower key id)
       float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < MAXNT; ++u)
-        if (cand >> u & 1u) { lo = fminf(lo, v[u]); hi = fmaxf(hi, v[u]); }
+      for (int u = 0; u < MAXNT; ++u) {
+        lo = fminf(lo, v[u] > -INFINITY ? v[u] : INFINITY);
+        hi = fmaxf(hi, v[u]);
+      }
       lo = g16_min(lo);
       hi = g16_max(hi);
       const float rmax = hi;
-      const float scale = hi > lo ? fminf(256.0f / (hi - lo), 1e30f) : 0.f;
-      auto bin = [&](float x) { return min(255, max(0, (int)((x - lo) * scale))); };
+      // 128 equal bins over [lo, hi], 32-bit counters in the row's histogram
+      // bytes (lane t owns bins 8t .. 8t+7); padding adds 0
+      const float A = hi > lo ? fminf(128.0f / (hi - lo), 1e30f) : 0.f, B = -lo * A;
+      auto bin = [&](float x) {
+        return (int)__builtin_amdgcn_fmed3f(__builtin_fmaf(x, A, B), 0.f, 127.f);
+      };
       const uint32_t below = (1u << t) - 1u;
       char* hrow = sm + OFF_H + i * H_STRIDE;
+      uint32_t* hist = reinterpret_cast<uint32_t*>(hrow);
       *reinterpret_cast<u32x4*>(hrow + 32 * t) = u32x4{0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4*>(hrow + 32 * t + 16) = u32x4{0u, 0u, 0u, 0u};
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int u = 0; u < MAXNT; ++u)
-        if (cand >> u & 1u) {
-          const int b = bin(v[u]);
-          atomicAdd(reinterpret_cast<uint32_t*>(hrow + (b >> 1) * 4), 1u << (16 * (b & 1)));
-        }
+        atomicAdd(hist + bin(v[u]), v[u] > -INFINITY ? 1u : 0u);
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       __builtin_amdgcn_wave_barrier();
-      int bstar = 0, above = 0, inbin = 0;
+      int bstar = 0, above = 0;
       {
         const u32x4 d0 = *reinterpret_cast<const u32x4*>(hrow + 32 * t);
         const u32x4 d1 = *reinterpret_cast<const u32x4*>(hrow + 32 * t + 16);
-        // bin 16t + q holds (q < 8 ? d0 : d1)[(q & 7) >> 1], half q & 1
-        auto cnt = [&](int q) -> int {
-          const uint32_t dw = (q < 8 ? d0 : d1)[(q & 7) >> 1];
-          return (q & 1) ? (int)(dw >> 16) : (int)(dw & 0xFFFFu);
-        };
+        const int cb[8] = {(int)d0[0], (int)d0[1], (int)d0[2], (int)d0[3],
+                           (int)d1[0], (int)d1[1], (int)d1[2], (int)d1[3]};
         int local = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          local += (int)((d0[q] & 0xFFFFu) + (d0[q] >> 16) + (d1[q] & 0xFFFFu) + (d1[q] >> 16));
+        for (int q = 0; q < 8; ++q) local += cb[q];
         // inclusive suffix sum over the group's lanes (higher lane = higher bins)
-        const int suf = g16_suffix_sum(local);
-        const int abv = suf - local;
-        const bool mine = active && abv < k && k <= suf;
-        if (mine) {
-          int acc = abv;
-          bool found = false;
+        int acc = g16_suffix_sum(local) - local;  // keys in bins above this lane's
+        int hit_b = 0, hit_a = 0;
+        bool hit = false;
 #pragma unroll
-          for (int q = 15; q >= 0; --q) {
-            if (!found) {
-              const int cq = cnt(q);
-              if (acc + cq >= k) {
-                found = true;
-                bstar = 16 * t + q;
-                above = acc;
-                inbin = cq;
-              } else {
-                acc += cq;
-              }
-            }
-          }
+        for (int q = 7; q >= 0; --q) {
+          const bool h = acc < k && acc + cb[q] >= k;
+          hit_b = h ? 8 * t + q : hit_b;
+          hit_a = h ? acc : hit_a;
+          hit = hit || h;
+          acc += cb[q];
         }
-        // exactly one lane of the group is `mine`: a masked group sum broadcasts
-        bstar = g16_sumi(mine ? bstar : 0);
-        above = g16_sumi(mine ? above : 0);
-        inbin = g16_sumi(mine ? inbin : 0);
+        // exactly one lane of an active group hits: a masked group sum broadcasts
+        bstar = g16_sumi(active && hit ? hit_b : 0);
+        above = g16_sumi(active && hit ? hit_a : 0);
       }
+      // keys above the boundary bin are in; the boundary bin supplies the
+      // rest, best first (larger score, then lower key id), one per round
       uint32_t take = 0, bnd = 0;
 #pragma unroll
-      for (int u = 0; u < MAXNT; ++u)
-        if (cand >> u & 1u) {
-          const int b = bin(v[u]);
-          if (b > bstar) take |= 1u << u;
-          if (b == bstar) bnd |= 1u << u;
-        }
-      // the boundary bin's entries as (score, key) pairs over the histogram
-      // bytes (66 fit); each ranks itself among them
-      const int need = k - above;
-      const bool listed = inbin <= H_STRIDE / 8;
-      float* list = reinterpret_cast<float*>(hrow);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      if (listed) {
-        int run = 0;
+      for (int u = 0; u < MAXNT; ++u) {
+        const int b = bin(v[u]);
+        const bool ok = v[u] > -INFINITY;
+        take |= (ok && b > bstar ? 1u : 0u) << u;
+        bnd |= (ok && b == bstar ? 1u : 0u) << u;
+      }
+      for (int need = active ? k - above : 0; __ballot(need > 0) != 0; --need) {
+        float bv = -INFINITY;
+        int bk = 0x7FFFFFFF;
 #pragma unroll
         for (int u = 0; u < MAXNT; ++u) {
-          const bool bit = bnd >> u & 1u;
-          const uint32_t gm = g16_bits(__ballot(bit), g);
-          if (bit) {
-            const int pos = run + __popc(gm & below);
-            list[2 * pos] = v[u];
-            list[2 * pos + 1] = __int_as_float(t + 16 * u);
-          }
-          run += __popc(gm);
+          const bool c = (bnd >> u & 1u) && (v[u] > bv || (v[u] == bv && t + 16 * u < bk));
+          bv = c ? v[u] : bv;
+          bk = c ? t + 16 * u : bk;
+        }
+        g16_argmax_key(bv, bk);
+        if (need > 0 && (bk & 15) == t) {
+          const int u = bk >> 4;
+          take |= 1u << u;
+          bnd &= ~(1u << u);
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int u = 0; u < MAXNT; ++u)
-        if (bnd >> u & 1u) {
-          const float x = v[u];
-          const int key = t + 16 * u;
-          int r = 0;
-          if (listed) {
-            for (int e = 0; e < inbin; ++e) {
-              const float y = list[2 * e];
-              const int ky = __float_as_int(list[2 * e + 1]);
-              r += (y > x || (y == x && ky < key)) ? 1 : 0;
-            }
-          } else {
-            // many equal scores: rank against the row's scores in the boundary bin
-            for (int j = 0; j < N; ++j) {
-              const float y = *lds<float>(sm, OFF_X + (i * S_STRIDE + j) * 4);
-              r += (bin(y) == bstar && (y > x || (y == x && j < key))) ? 1 : 0;
-            }
-          }
-          if (r < need) take |= 1u << u;
-        }
       // the expert: kept key ids in ascending order
       {
         int run = 0;
@@ -469,13 +443,14 @@ __global__ __launch_bounds__(THREADS, 2) void mita_fused_kernel(
       // P row (f16) over this row's bytes, and its sum
       float sum = 0.f;
       uint16_t* prow = reinterpret_cast<uint16_t*>(hrow);
+      const float moff = -rmax * 1.4426950408889634f;
 #pragma unroll
       for (int u = 0; u < KPMAX / 16; ++u) {
         const int j = t + 16 * u;
         if (j < KP) {
           uint32_t hb = 0;
-          if (active && u < MAXNT && j < N) {
-            hb = f16_bits(fast_exp(v[u < MAXNT ? u : 0] - rmax));
+          if (active && u < MAXNT) {
+            hb = f16_bits(__builtin_amdgcn_exp2f(__builtin_fmaf(v[u < MAXNT ? u : 0], 1.4426950408889634f, moff)));
             sum += f16_bits_to_f32(hb);
           }
           prow[j] = (uint16_t)hb;
