@@ -253,49 +253,68 @@ __global__ __launch_bounds__(THREADS, 2) void mita_fused_kernel(
     load_v(vr, Vh, N, tid);
     __syncthreads();  // the previous head is done with LDS
 
-    // ---------------- B: landmark pooling from the Q rows (landmark x 4 channels)
-    for (int it = tid; it < MMAX * 16; it += THREADS) {
-      const int i = it >> 4, q4 = it & 15;
-      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    // C's K rows go out first, so that they fly with the pooling loads
+    u32x4 ka[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tt = w + NWAVES * j, key = 16 * tt + c16;
+      const bool ok = tt < nt && key < N;
+      const uint16_t* kr = Kh + (size_t)(ok ? key : 0) * 64;
+      ka[j][0] = ok ? *reinterpret_cast<const u32x4*>(kr + 8 * g) : z;
+      ka[j][1] = ok ? *reinterpret_cast<const u32x4*>(kr + 32 + 8 * g) : z;
+    }
+
+    // ---------------- B: landmark pooling from the Q rows (landmark x 8 channels)
+    {
+      static_assert(THREADS == MMAX * 8, "one (landmark, 8-channel chunk) per thread");
+      const int i = tid >> 3, c8 = tid & 7;
+      float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
       if (i < m) {
         const int r = i / mw, c = i % mw;
         int y0, y1, x0, x1;
         pool_window(r, gh, mh, &y0, &y1);
         pool_window(c, gw, mw, &x0, &x1);
-        for (int y = y0; y < y1; ++y) {
-          // four columns' loads in flight before any is consumed
-          for (int x = x0; x < x1; x += 4) {
-            u32x2 v[4];
+        const int cnt = (y1 - y0) * (x1 - x0);
+        // the window's tokens in row-major order, PB loads in flight at once
+        constexpr int PB = 16;
+        int y = y0, x = x0;
+        for (int base = 0; base < cnt; base += PB) {
+          u32x4 v[PB];
 #pragma unroll
-            for (int dx = 0; dx < 4; ++dx)
-              v[dx] = x + dx < x1
-                          ? *reinterpret_cast<const u32x2*>(Qh + (size_t)(y * gw + x + dx) * 64 + 4 * q4)
-                          : u32x2{0u, 0u};
-#pragma unroll
-            for (int dx = 0; dx < 4; ++dx) {
-              a0 += bf16_bits_to_f32(v[dx][0] & 0xFFFFu);
-              a1 += bf16_bits_to_f32(v[dx][0] >> 16);
-              a2 += bf16_bits_to_f32(v[dx][1] & 0xFFFFu);
-              a3 += bf16_bits_to_f32(v[dx][1] >> 16);
-            }
+          for (int u = 0; u < PB; ++u) {
+            const bool ok = base + u < cnt;
+            v[u] = ok ? *reinterpret_cast<const u32x4*>(Qh + (size_t)(y * gw + x) * 64 + 8 * c8) : z;
+            x = ok && x + 1 == x1 ? x0 : x + 1;
+            y = ok && x == x0 ? y + 1 : y;
           }
+#pragma unroll
+          for (int u = 0; u < PB; ++u)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              a[2 * q] += bf16_bits_to_f32(v[u][q] & 0xFFFFu);
+              a[2 * q + 1] += bf16_bits_to_f32(v[u][q] >> 16);
+            }
         }
-        const float cnt = (float)((y1 - y0) * (x1 - x0));
-        a0 /= cnt; a1 /= cnt; a2 /= cnt; a3 /= cnt;
+        const float fc = (float)cnt;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) a[q] /= fc;
         if (o.ql) {
-          float4* dst = reinterpret_cast<float4*>(o.ql + ((size_t)bh * m + i) * 64 + 4 * q4);
-          *dst = make_float4(a0, a1, a2, a3);
+          float4* dst = reinterpret_cast<float4*>(o.ql + ((size_t)bh * m + i) * 64 + 8 * c8);
+          dst[0] = make_float4(a[0], a[1], a[2], a[3]);
+          dst[1] = make_float4(a[4], a[5], a[6], a[7]);
         }
       }
-      const uint32_t h0 = bf16_rne_bits(a0), h1 = bf16_rne_bits(a1);
-      const uint32_t h2 = bf16_rne_bits(a2), h3 = bf16_rne_bits(a3);
-      const uint32_t l0 = bf16_rne_bits(a0 - bf16_bits_to_f32(h0));
-      const uint32_t l1 = bf16_rne_bits(a1 - bf16_bits_to_f32(h1));
-      const uint32_t l2 = bf16_rne_bits(a2 - bf16_bits_to_f32(h2));
-      const uint32_t l3 = bf16_rne_bits(a3 - bf16_bits_to_f32(h3));
-      const int off = rc(i, q4 >> 1) + (q4 & 1) * 8;
-      *lds<u32x2>(sm, OFF_QLH + off) = u32x2{h0 | (h1 << 16), h2 | (h3 << 16)};
-      *lds<u32x2>(sm, OFF_QLL + off) = u32x2{l0 | (l1 << 16), l2 | (l3 << 16)};
+      u32x4 hv, lv;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t h0 = bf16_rne_bits(a[2 * q]), h1 = bf16_rne_bits(a[2 * q + 1]);
+        const uint32_t l0 = bf16_rne_bits(a[2 * q] - bf16_bits_to_f32(h0));
+        const uint32_t l1 = bf16_rne_bits(a[2 * q + 1] - bf16_bits_to_f32(h1));
+        hv[q] = h0 | (h1 << 16);
+        lv[q] = l0 | (l1 << 16);
+      }
+      *lds<u32x4>(sm, OFF_QLH + rc(i, c8)) = hv;
+      *lds<u32x4>(sm, OFF_QLL + rc(i, c8)) = lv;
     }
     __syncthreads();
 
@@ -303,15 +322,6 @@ __global__ __launch_bounds__(THREADS, 2) void mita_fused_kernel(
     {
       u32x4 qlh[2][2], qll[2][2];
       load_ql(sm, qlh, qll, g, c16);
-      u32x4 ka[4][2];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tt = w + NWAVES * j, key = 16 * tt + c16;
-        const bool ok = tt < nt && key < N;
-        const uint16_t* kr = Kh + (size_t)(ok ? key : 0) * 64;
-        ka[j][0] = ok ? *reinterpret_cast<const u32x4*>(kr + 8 * g) : z;
-        ka[j][1] = ok ? *reinterpret_cast<const u32x4*>(kr + 32 + 8 * g) : z;
-      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int tt = w + NWAVES * j;
@@ -462,8 +472,16 @@ __global__ __launch_bounds__(THREADS, 2) void mita_fused_kernel(
         *lds<float>(sm, OFF_STAT + (32 + i) * 4) = active ? sum : 1.0f;
       }
     }
-    __syncthreads();
-
+    // E's query rows fly while V^T is stored and V_L is formed
+    u32x4 qb[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tok = 16 * (w + NWAVES * j) + c16;
+      const bool ok = tok < N;
+      const uint16_t* qr = Qh + (size_t)(ok ? tok : 0) * 64;
+      qb[j][0] = ok ? *reinterpret_cast<const u32x4*>(qr + 8 * g) : z;
+      qb[j][1] = ok ? *reinterpret_cast<const u32x4*>(qr + 32 + 8 * g) : z;
+    }
     __syncthreads();  // the scores are no longer needed
 
     // ---------------- V: V^T (f16) over the score region
@@ -500,15 +518,6 @@ __global__ __launch_bounds__(THREADS, 2) void mita_fused_kernel(
     {
       u32x4 qlh[2][2], qll[2][2];
       load_ql(sm, qlh, qll, g, c16);
-      u32x4 qb[4][2];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tok = 16 * (w + NWAVES * j) + c16;
-        const bool ok = tok < N;
-        const uint16_t* qr = Qh + (size_t)(ok ? tok : 0) * 64;
-        qb[j][0] = ok ? *reinterpret_cast<const u32x4*>(qr + 8 * g) : z;
-        qb[j][1] = ok ? *reinterpret_cast<const u32x4*>(qr + 32 + 8 * g) : z;
-      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int tt = w + NWAVES * j;
@@ -625,43 +634,68 @@ __global__ __launch_bounds__(THREADS, 2) void mita_fused_kernel(
       }
       const int ntiles = *lds<int>(sm, OFF_STAT + 64 * 4);
       float* outh = o.out + (size_t)bh * N * 64;
-      for (int tile = w; tile < ntiles; tile += NWAVES) {
+      // A tile's gathered operands: the expert's key rows for this lane's two
+      // slot tiles and the query row of lane column c16 (columns past the
+      // tile's length compute on query 0 and are never stored).  The next
+      // tile's are loaded while this one computes.
+      struct TileIn {
+        int e, qi;
+        bool live;
+        u32x4 ak[2][2], bq0, bq1;
+      };
+      auto fetch = [&](int tile, TileIn& ti) {
         const int4 tl = *lds<int4>(sm, OFF_TILES + tile * 16);
-        const int e = tl.x, start = tl.y, len = tl.z;
-        // lane column c16 is query qi of the tile; columns past len compute on
-        // query 0 and are never stored
-        const bool live = c16 < len;
-        const int qi = live ? *lds<int>(sm, OFF_PERM + (start + c16) * 4) : 0;
-        // the expert's key rows for this lane's two slot tiles, and the query rows
-        const int* idxe = lds<int>(sm, OFF_IDX + e * KMAX * 4);
-        u32x4 ak[2][2];
+        ti.e = tl.x;
+        ti.live = c16 < tl.z;
+        ti.qi = ti.live ? *lds<int>(sm, OFF_PERM + (tl.y + c16) * 4) : 0;
+        const int* idxe = lds<int>(sm, OFF_IDX + ti.e * KMAX * 4);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           const int slot = 16 * st + c16;
           const bool ok = slot < k;
           const uint16_t* kr = Kh + (size_t)(ok ? idxe[slot] : 0) * 64;
-          ak[st][0] = ok ? *reinterpret_cast<const u32x4*>(kr + 8 * g) : z;
-          ak[st][1] = ok ? *reinterpret_cast<const u32x4*>(kr + 32 + 8 * g) : z;
+          ti.ak[st][0] = ok ? *reinterpret_cast<const u32x4*>(kr + 8 * g) : z;
+          ti.ak[st][1] = ok ? *reinterpret_cast<const u32x4*>(kr + 32 + 8 * g) : z;
         }
-        const uint16_t* qrow = Qh + (size_t)qi * 64;
-        const u32x4 bq0 = *reinterpret_cast<const u32x4*>(qrow + 8 * g);
-        const u32x4 bq1 = *reinterpret_cast<const u32x4*>(qrow + 32 + 8 * g);
+        const uint16_t* qrow = Qh + (size_t)ti.qi * 64;
+        ti.bq0 = *reinterpret_cast<const u32x4*>(qrow + 8 * g);
+        ti.bq1 = *reinterpret_cast<const u32x4*>(qrow + 32 + 8 * g);
+      };
+      // the previous tile's output rows, stored once the next loads have landed
+      // (one counter tracks loads and stores: stores issued ahead of a load
+      // would make its wait cover them too)
+      f32x4 pend[4];
+      int pqi = 0;
+      bool plive = false;
+      TileIn cur;
+      if (w < ntiles) fetch(w, cur);
+      for (int tile = w; tile < ntiles; tile += NWAVES) {
+        asm volatile("" ::"v"(cur.bq0), "v"(cur.bq1), "v"(cur.ak[0][0]), "v"(cur.ak[0][1]),
+                     "v"(cur.ak[1][0]), "v"(cur.ak[1][1]));
+        if (plive) {
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+            *reinterpret_cast<f32x4*>(outh + (size_t)pqi * 64 + 16 * ct + 4 * g) = pend[ct];
+        }
+        TileIn nxt = cur;
+        if (tile + NWAVES < ntiles) fetch(tile + NWAVES, nxt);
+        const int e = cur.e;
         // shared logits^T = Q_L Q_g^T (hi + lo) and routed logits^T = K_e Q_g^T
         f32x4 ls[2], lr[2];
 #pragma unroll
         for (int lt = 0; lt < 2; ++lt) {
           f32x4 c = zero4();
-          c = mfma_bf16(qlh[lt][0], bq0, c);
-          c = mfma_bf16(qll[lt][0], bq0, c);
-          c = mfma_bf16(qlh[lt][1], bq1, c);
-          c = mfma_bf16(qll[lt][1], bq1, c);
+          c = mfma_bf16(qlh[lt][0], cur.bq0, c);
+          c = mfma_bf16(qll[lt][0], cur.bq0, c);
+          c = mfma_bf16(qlh[lt][1], cur.bq1, c);
+          c = mfma_bf16(qll[lt][1], cur.bq1, c);
           ls[lt] = c;
         }
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           f32x4 c = zero4();
-          c = mfma_bf16(ak[st][0], bq0, c);
-          c = mfma_bf16(ak[st][1], bq1, c);
+          c = mfma_bf16(cur.ak[st][0], cur.bq0, c);
+          c = mfma_bf16(cur.ak[st][1], cur.bq1, c);
           lr[st] = c;
         }
         float x[16];
@@ -710,10 +744,16 @@ __global__ __launch_bounds__(THREADS, 2) void mita_fused_kernel(
           f32x4 acc = zero4();
           acc = mfma_f16(avl[ct], bps, acc);
           acc = mfma_f16(ave, bpr, acc);
-          if (live)
-            *reinterpret_cast<float4*>(outh + (size_t)qi * 64 + 16 * ct + 4 * g) =
-                make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+          pend[ct] = acc * inv;
         }
+        pqi = cur.qi;
+        plive = cur.live;
+        cur = nxt;
+      }
+      if (plive) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          *reinterpret_cast<f32x4*>(outh + (size_t)pqi * 64 + 16 * ct + 4 * g) = pend[ct];
       }
     }
   }
