@@ -36,8 +36,10 @@ namespace fused {
 constexpr int MAXNT = 13;           // 16-token tiles
 constexpr int NP = MAXNT * 16;      // 208 padded tokens
 constexpr int KPMAX = 224;          // keys padded to a multiple of 32 (P V k-steps)
-constexpr int THREADS = 256;
+constexpr int THREADS = 512;
 constexpr int NWAVES = THREADS / 64;
+constexpr int TPW = (MAXNT + NWAVES - 1) / NWAVES;  // 16-token tiles per wave
+constexpr int VITEMS = (8 * (KPMAX / 2) + THREADS - 1) / THREADS;  // V pair items per thread
 constexpr int MMAX = 32, KMAX = 32;
 
 constexpr int VT_STRIDE = 464;      // bytes per V^T row (f16 keys)
@@ -59,7 +61,8 @@ constexpr int OFF_BASE = OFF_CNT + 4 * 32 * 4;    // [4 chunks][32] int
 constexpr int OFF_OFFS = OFF_BASE + 4 * 32 * 4;   // [33] int
 constexpr int OFF_TILES = OFF_OFFS + 48 * 4;      // [64] x (e, start, len, -)
 constexpr int OFF_STAT = OFF_TILES + 64 * 16;     // rowmax[32], rowsum[32], ntiles
-constexpr int LDS_BYTES = OFF_STAT + 80 * 4;
+constexpr int OFF_WMASK = OFF_STAT + 80 * 4;      // [KPMAX] landmark-membership bits per token
+constexpr int LDS_BYTES = OFF_WMASK + KPMAX * 4;
 static_assert(2 * LDS_BYTES <= 160 * 1024, "two workgroups per gfx950 CU");
 static_assert(OFF_H % 16 == 0 && OFF_QLH % 16 == 0 && OFF_VLT % 16 == 0 && OFF_IDX % 16 == 0 &&
                   OFF_TILES % 16 == 0,
@@ -192,27 +195,38 @@ __device__ __forceinline__ void load_ql(char* sm, u32x4 (&qlh)[2][2], u32x4 (&ql
     }
 }
 
+// A head's [N][64] bf16 rows as a raw buffer: 32-bit byte offsets, and an
+// offset past the head's bytes reads zeros (the buffer range check), which
+// stands in for padding rows without a branch or a select on the data.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int PAST = 0x40000000;
+__device__ __forceinline__ Rsrc head_rows(const uint16_t* base, int N) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, N * 128, 0x00020000);
+}
+__device__ __forceinline__ u32x4 ld16(Rsrc r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 // The head's V rows for the transposed copy: key pairs (2p, 2p+1) of 8-channel
 // chunk c, items tid + THREADS i (c = item / 112, p = item % 112).
 struct VRows {
-  u32x4 v0[4], v1[4];
+  u32x4 v0[VITEMS], v1[VITEMS];
 };
 
-__device__ __forceinline__ void load_v(VRows& vr, const uint16_t* Vh, int N, int tid) {
-  const u32x4 z = {0u, 0u, 0u, 0u};
+__device__ __forceinline__ void load_v(VRows& vr, Rsrc rows, int N, int tid) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < VITEMS; ++i) {
     const int id = tid + THREADS * i;
     const int c = id / (KPMAX / 2), p = id % (KPMAX / 2);
     const int j0 = 2 * p, j1 = 2 * p + 1;
-    vr.v0[i] = (c < 8 && j0 < N) ? *reinterpret_cast<const u32x4*>(Vh + j0 * 64 + c * 8) : z;
-    vr.v1[i] = (c < 8 && j1 < N) ? *reinterpret_cast<const u32x4*>(Vh + j1 * 64 + c * 8) : z;
+    vr.v0[i] = ld16(rows, c < 8 && j0 < N ? j0 * 128 + c * 16 : PAST);
+    vr.v1[i] = ld16(rows, c < 8 && j1 < N ? j1 * 128 + c * 16 : PAST);
   }
 }
 
 __device__ __forceinline__ void store_vt(const VRows& vr, char* sm, int tid) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < VITEMS; ++i) {
     const int id = tid + THREADS * i;
     const int c = id / (KPMAX / 2), p = id % (KPMAX / 2);
     if (c < 8) {
@@ -227,7 +241,30 @@ __device__ __forceinline__ void store_vt(const VRows& vr, char* sm, int tid) {
   }
 }
 
-__global__ __launch_bounds__(THREADS, 2) void mita_fused_kernel(
+// Q^T (bf16, tokens contiguous) over X from the same register layout.
+__device__ __forceinline__ void store_qt(const VRows& qr, char* sm, int tid) {
+#pragma unroll
+  for (int i = 0; i < VITEMS; ++i) {
+    const int id = tid + THREADS * i;
+    const int c = id / (KPMAX / 2), p = id % (KPMAX / 2);
+    if (c < 8) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t a = qr.v0[i][t >> 1], b = qr.v1[i][t >> 1];
+        *lds<uint32_t>(sm, OFF_X + (8 * c + t) * VT_STRIDE + 4 * p) =
+            (t & 1) ? (a >> 16) | (b & 0xFFFF0000u) : (a & 0xFFFFu) | (b << 16);
+      }
+    }
+  }
+}
+
+// Two 0/1 bf16 entries of the pooling matrix: bit L of two tokens' masks.
+__device__ __forceinline__ uint32_t member_pair(uint32_t m0, uint32_t m1, int L) {
+  const uint32_t b = __builtin_amdgcn_ubfe(m0, L, 1) | (__builtin_amdgcn_ubfe(m1, L, 1) << 16);
+  return b * 0x3F80u;
+}
+
+__global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, Outputs o, int BH, int gh, int gw, int mh, int mw, int k) {
   __shared__ __attribute__((aligned(16))) char sm[LDS_BYTES];
@@ -238,6 +275,37 @@ __global__ __launch_bounds__(THREADS, 2) void mita_fused_kernel(
   const float kLogitScale = tau * 1.4426950408889634f;  // tau * log2(e): base-2 softmax
   const size_t head_elems = (size_t)N * 64;
   const u32x4 z = {0u, 0u, 0u, 0u};
+  static_assert(NWAVES == 8, "pooling: one 16-channel x 16-landmark tile per wave");
+
+  // which landmark windows hold each token (the same for every head)
+  for (int tok = threadIdx.x; tok < KPMAX; tok += THREADS) {
+    uint32_t bits = 0;
+    if (tok < N) {
+      const int y = tok / gw, x = tok % gw;
+      for (int i = 0; i < m; ++i) {
+        int y0, y1, x0, x1;
+        pool_window(i / mw, gh, mh, &y0, &y1);
+        pool_window(i % mw, gw, mw, &x0, &x1);
+        bits |= (y >= y0 && y < y1 && x >= x0 && x < x1 ? 1u : 0u) << i;
+      }
+    }
+    *lds<uint32_t>(sm, OFF_WMASK + tok * 4) = bits;
+  }
+  // 1 / window size of this lane's pooling column
+  float inv_cnt = 0.f;
+  {
+    const int L = 16 * ((threadIdx.x >> 6) >> 2) + (threadIdx.x & 15);
+    if (L < m) {
+      int y0, y1, x0, x1;
+      pool_window(L / mw, gh, mh, &y0, &y1);
+      pool_window(L % mw, gw, mw, &x0, &x1);
+      inv_cnt = 1.0f / (float)((y1 - y0) * (x1 - x0));
+    }
+  }
+
+  // a head's Q rows are requested while the previous head runs its expert tiles
+  VRows qr;
+  if (blockIdx.x < BH) load_v(qr, head_rows(Q + (size_t)blockIdx.x * head_elems, N), N, threadIdx.x);
 
   for (int bh = blockIdx.x; bh < BH; bh += gridDim.x) {
     // Thread coordinates are re-derived through an opaque zero every head so
@@ -246,75 +314,55 @@ __global__ __launch_bounds__(THREADS, 2) void mita_fused_kernel(
     const int tid = threadIdx.x + opaque_zero(), lane = tid & 63, w = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
     const uint16_t* Qh = Q + bh * head_elems;
-    const uint16_t* Kh = K + bh * head_elems;
-    const uint16_t* Vh = V + bh * head_elems;
-    // the head's V rows fly while pooling, scores and top-k run
-    VRows vr;
-    load_v(vr, Vh, N, tid);
+    const Rsrc rQ = head_rows(Qh, N), rK = head_rows(K + bh * head_elems, N);
     __syncthreads();  // the previous head is done with LDS
-
-    // C's K rows go out first, so that they fly with the pooling loads
-    u32x4 ka[4][2];
+    store_qt(qr, sm, tid);
+    // C's K rows, issued after the Q^T store so that its wait does not cover them
+    u32x4 ka[TPW][2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tt = w + NWAVES * j, key = 16 * tt + c16;
-      const bool ok = tt < nt && key < N;
-      const uint16_t* kr = Kh + (size_t)(ok ? key : 0) * 64;
-      ka[j][0] = ok ? *reinterpret_cast<const u32x4*>(kr + 8 * g) : z;
-      ka[j][1] = ok ? *reinterpret_cast<const u32x4*>(kr + 32 + 8 * g) : z;
+    for (int j = 0; j < TPW; ++j) {
+      const int key = 16 * (w + NWAVES * j) + c16;
+      const int off = key < N ? key * 128 + 16 * g : PAST;
+      ka[j][0] = ld16(rK, off);
+      ka[j][1] = ld16(rK, off + 64);
+    }
+    // the routing phase's query rows fly with C's K rows
+    u32x4 qb[TPW][2];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int tok = 16 * (w + NWAVES * j) + c16;
+      const int off = tok < N ? tok * 128 + 16 * g : PAST;
+      qb[j][0] = ld16(rQ, off);
+      qb[j][1] = ld16(rQ, off + 64);
     }
 
-    // ---------------- B: landmark pooling from the Q rows (landmark x 8 channels)
+    __syncthreads();
+
+    // ---------------- B: landmark pooling as a contraction over tokens,
+    // Q_L^T = Q^T W (W: 0/1 window membership) on bf16 MFMA, then / window size
     {
-      static_assert(THREADS == MMAX * 8, "one (landmark, 8-channel chunk) per thread");
-      const int i = tid >> 3, c8 = tid & 7;
-      float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (i < m) {
-        const int r = i / mw, c = i % mw;
-        int y0, y1, x0, x1;
-        pool_window(r, gh, mh, &y0, &y1);
-        pool_window(c, gw, mw, &x0, &x1);
-        const int cnt = (y1 - y0) * (x1 - x0);
-        // the window's tokens in row-major order, PB loads in flight at once
-        constexpr int PB = 16;
-        int y = y0, x = x0;
-        for (int base = 0; base < cnt; base += PB) {
-          u32x4 v[PB];
-#pragma unroll
-          for (int u = 0; u < PB; ++u) {
-            const bool ok = base + u < cnt;
-            v[u] = ok ? *reinterpret_cast<const u32x4*>(Qh + (size_t)(y * gw + x) * 64 + 8 * c8) : z;
-            x = ok && x + 1 == x1 ? x0 : x + 1;
-            y = ok && x == x0 ? y + 1 : y;
-          }
-#pragma unroll
-          for (int u = 0; u < PB; ++u)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              a[2 * q] += bf16_bits_to_f32(v[u][q] & 0xFFFFu);
-              a[2 * q + 1] += bf16_bits_to_f32(v[u][q] >> 16);
-            }
-        }
-        const float fc = (float)cnt;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) a[q] /= fc;
-        if (o.ql) {
-          float4* dst = reinterpret_cast<float4*>(o.ql + ((size_t)bh * m + i) * 64 + 8 * c8);
-          dst[0] = make_float4(a[0], a[1], a[2], a[3]);
-          dst[1] = make_float4(a[4], a[5], a[6], a[7]);
-        }
+      const int ct = w & 3, L = 16 * (w >> 2) + c16;
+      f32x4 acc = zero4();
+      for (int ks = 0; ks < KP / 32; ++ks) {
+        const u32x4 a = *lds<u32x4>(sm, OFF_X + (16 * ct + c16) * VT_STRIDE + (32 * ks + 8 * g) * 2);
+        const u32x4 m0 = *lds<u32x4>(sm, OFF_WMASK + (32 * ks + 8 * g) * 4);
+        const u32x4 m1 = *lds<u32x4>(sm, OFF_WMASK + (32 * ks + 8 * g + 4) * 4);
+        const u32x4 b = {member_pair(m0[0], m0[1], L), member_pair(m0[2], m0[3], L),
+                         member_pair(m1[0], m1[1], L), member_pair(m1[2], m1[3], L)};
+        acc = mfma_bf16(a, b, acc);
       }
-      u32x4 hv, lv;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t h0 = bf16_rne_bits(a[2 * q]), h1 = bf16_rne_bits(a[2 * q + 1]);
-        const uint32_t l0 = bf16_rne_bits(a[2 * q] - bf16_bits_to_f32(h0));
-        const uint32_t l1 = bf16_rne_bits(a[2 * q + 1] - bf16_bits_to_f32(h1));
-        hv[q] = h0 | (h1 << 16);
-        lv[q] = l0 | (l1 << 16);
-      }
-      *lds<u32x4>(sm, OFF_QLH + rc(i, c8)) = hv;
-      *lds<u32x4>(sm, OFF_QLL + rc(i, c8)) = lv;
+      // lane holds Q_L[landmark L][channels 16ct + 4g .. +3]: fp32, then bf16 hi + lo
+      const float q0 = acc[0] * inv_cnt, q1 = acc[1] * inv_cnt;
+      const float q2 = acc[2] * inv_cnt, q3 = acc[3] * inv_cnt;
+      const uint32_t h01 = pk_bf16(q0, q1), h23 = pk_bf16(q2, q3);
+      const uint32_t l01 = pk_bf16(q0 - bf16_bits_to_f32(h01 & 0xFFFFu), q1 - bf16_bits_to_f32(h01 >> 16));
+      const uint32_t l23 = pk_bf16(q2 - bf16_bits_to_f32(h23 & 0xFFFFu), q3 - bf16_bits_to_f32(h23 >> 16));
+      const int off = rc(L, 2 * ct + (g >> 1)) + (g & 1) * 8;
+      *lds<u32x2>(sm, OFF_QLH + off) = u32x2{h01, h23};
+      *lds<u32x2>(sm, OFF_QLL + off) = u32x2{l01, l23};
+      if (o.ql && L < m)
+        *reinterpret_cast<float4*>(o.ql + ((size_t)bh * m + L) * 64 + 16 * ct + 4 * g) =
+            make_float4(q0, q1, q2, q3);
     }
     __syncthreads();
 
@@ -323,7 +371,7 @@ __global__ __launch_bounds__(THREADS, 2) void mita_fused_kernel(
       u32x4 qlh[2][2], qll[2][2];
       load_ql(sm, qlh, qll, g, c16);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < TPW; ++j) {
         const int tt = w + NWAVES * j;
         if (tt < nt) {
 #pragma unroll
@@ -340,12 +388,53 @@ __global__ __launch_bounds__(THREADS, 2) void mita_fused_kernel(
         }
       }
     }
+    // ---------------- E': R^T = Q_L Q^T per token tile (Q rows from global memory): routes
+    {
+      u32x4 qlh[2][2], qll[2][2];
+      load_ql(sm, qlh, qll, g, c16);
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) {
+        const int tt = w + NWAVES * j;
+        if (tt >= nt) break;
+        const int tok = 16 * tt + c16;
+        f32x4 acc[2];
+#pragma unroll
+        for (int lt = 0; lt < 2; ++lt) {
+          f32x4 c = zero4();
+          c = mfma_bf16(qlh[lt][0], qb[j][0], c);
+          c = mfma_bf16(qll[lt][0], qb[j][0], c);
+          c = mfma_bf16(qlh[lt][1], qb[j][1], c);
+          c = mfma_bf16(qll[lt][1], qb[j][1], c);
+          acc[lt] = c;  // lane holds R[token tok][landmark 16lt + 4g + r]
+        }
+        float best = -INFINITY;
+        int bi = 0;
+#pragma unroll
+        for (int lt = 0; lt < 2; ++lt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int L = 16 * lt + 4 * g + r;  // increasing: strict '>' keeps the lowest
+            const float v = L < m ? acc[lt][r] : -INFINITY;
+            if (v > best) { best = v; bi = L; }
+          }
+#pragma unroll
+        for (int off = 16; off <= 32; off <<= 1) {
+          const float ov = __shfl_xor(best, off, 64);
+          const int oi = __shfl_xor(bi, off, 64);
+          if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
+        }
+        if (g == 0 && tok < N) {
+          *lds<int>(sm, OFF_ROUTE + tok * 4) = bi;
+          if (o.route) o.route[(size_t)bh * N + tok] = bi;
+        }
+      }
+    }
     __syncthreads();
 
     // ---------------- D: exact top-k of each landmark row; then P = exp(S - max) in f16
 #pragma unroll 1
-    for (int jr = 0; jr < MMAX / 16; ++jr) {
-      const int i = 4 * w + g + 16 * jr;  // landmark row of this 16-lane group
+    for (int jr = 0; jr < MMAX / (4 * NWAVES); ++jr) {
+      const int i = 4 * w + g + 4 * NWAVES * jr;  // landmark row of this 16-lane group
       if (__ballot(i < m) == 0) continue;
       const bool active = i < m;
       const int t = c16;
@@ -472,89 +561,9 @@ __global__ __launch_bounds__(THREADS, 2) void mita_fused_kernel(
         *lds<float>(sm, OFF_STAT + (32 + i) * 4) = active ? sum : 1.0f;
       }
     }
-    // E's query rows fly while V^T is stored and V_L is formed
-    u32x4 qb[4][2];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int tok = 16 * (w + NWAVES * j) + c16;
-      const bool ok = tok < N;
-      const uint16_t* qr = Qh + (size_t)(ok ? tok : 0) * 64;
-      qb[j][0] = ok ? *reinterpret_cast<const u32x4*>(qr + 8 * g) : z;
-      qb[j][1] = ok ? *reinterpret_cast<const u32x4*>(qr + 32 + 8 * g) : z;
-    }
-    __syncthreads();  // the scores are no longer needed
-
-    // ---------------- V: V^T (f16) over the score region
-    store_vt(vr, sm, tid);
-    __syncthreads();
-
-    // ---------------- E: V_L^T = V^T P^T (16-channel x 16-landmark tiles)
-#pragma unroll 1
-    for (int tile = w; tile < 8; tile += NWAVES) {
-      const int ct = tile & 3, lt = tile >> 2;
-      f32x4 acc = zero4();
-      for (int ks = 0; ks < KP / 32; ++ks) {
-        const u32x4 a = *lds<u32x4>(sm, OFF_X + (16 * ct + c16) * VT_STRIDE + (32 * ks + 8 * g) * 2);
-        const u32x4 b = *lds<u32x4>(sm, OFF_H + (16 * lt + c16) * H_STRIDE + (32 * ks + 8 * g) * 2);
-        acc = mfma_f16(a, b, acc);
-      }
-      const int L = 16 * lt + c16;
-      const bool ok = L < m;
-      const float inv = ok ? 1.0f / *lds<float>(sm, OFF_STAT + (32 + L) * 4) : 0.f;
-      float vl4[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        vl4[r] = ok ? acc[r] * inv : 0.f;
-        *lds<uint16_t>(sm, OFF_VLT + (16 * ct + 4 * g + r) * VLT_STRIDE + L * 2) =
-            (uint16_t)f16_bits(vl4[r]);
-      }
-      if (ok && o.vl) {
-        *reinterpret_cast<float4*>(o.vl + ((size_t)bh * m + L) * 64 + 16 * ct + 4 * g) =
-            make_float4(vl4[0], vl4[1], vl4[2], vl4[3]);
-      }
-    }
-
-    // ---------------- E': R^T = Q_L Q^T per token tile (Q rows from global memory): routes
-    {
-      u32x4 qlh[2][2], qll[2][2];
-      load_ql(sm, qlh, qll, g, c16);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tt = w + NWAVES * j;
-        if (tt >= nt) break;
-        const int tok = 16 * tt + c16;
-        f32x4 acc[2];
-#pragma unroll
-        for (int lt = 0; lt < 2; ++lt) {
-          f32x4 c = zero4();
-          c = mfma_bf16(qlh[lt][0], qb[j][0], c);
-          c = mfma_bf16(qll[lt][0], qb[j][0], c);
-          c = mfma_bf16(qlh[lt][1], qb[j][1], c);
-          c = mfma_bf16(qll[lt][1], qb[j][1], c);
-          acc[lt] = c;  // lane holds R[token tok][landmark 16lt + 4g + r]
-        }
-        float best = -INFINITY;
-        int bi = 0;
-#pragma unroll
-        for (int lt = 0; lt < 2; ++lt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int L = 16 * lt + 4 * g + r;  // increasing: strict '>' keeps the lowest
-            const float v = L < m ? acc[lt][r] : -INFINITY;
-            if (v > best) { best = v; bi = L; }
-          }
-#pragma unroll
-        for (int off = 16; off <= 32; off <<= 1) {
-          const float ov = __shfl_xor(best, off, 64);
-          const int oi = __shfl_xor(bi, off, 64);
-          if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
-        }
-        if (g == 0 && tok < N) {
-          *lds<int>(sm, OFF_ROUTE + tok * 4) = bi;
-          if (o.route) o.route[(size_t)bh * N + tok] = bi;
-        }
-      }
-    }
+    // the V rows fly while the queries are grouped
+    VRows vr;
+    load_v(vr, head_rows(V + bh * head_elems, N), N, tid);
     __syncthreads();
 
     // ---------------- F: group queries by route (stable counting sort), tile list
@@ -618,20 +627,45 @@ __global__ __launch_bounds__(THREADS, 2) void mita_fused_kernel(
     }
     __syncthreads();
 
+    // ---------------- V: V^T (f16) over the score region
+    store_vt(vr, sm, tid);
+    __syncthreads();
+
+    // ---------------- E: V_L^T = V^T P^T (16-channel x 16-landmark tiles)
+#pragma unroll 1
+    for (int tile = w; tile < 8; tile += NWAVES) {
+      const int ct = tile & 3, lt = tile >> 2;
+      f32x4 acc = zero4();
+      for (int ks = 0; ks < KP / 32; ++ks) {
+        const u32x4 a = *lds<u32x4>(sm, OFF_X + (16 * ct + c16) * VT_STRIDE + (32 * ks + 8 * g) * 2);
+        const u32x4 b = *lds<u32x4>(sm, OFF_H + (16 * lt + c16) * H_STRIDE + (32 * ks + 8 * g) * 2);
+        acc = mfma_f16(a, b, acc);
+      }
+      const int L = 16 * lt + c16;
+      const bool ok = L < m;
+      const float inv = ok ? 1.0f / *lds<float>(sm, OFF_STAT + (32 + L) * 4) : 0.f;
+      float vl4[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        vl4[r] = ok ? acc[r] * inv : 0.f;
+        *lds<uint16_t>(sm, OFF_VLT + (16 * ct + 4 * g + r) * VLT_STRIDE + L * 2) =
+            (uint16_t)f16_bits(vl4[r]);
+      }
+      if (ok && o.vl) {
+        *reinterpret_cast<float4*>(o.vl + ((size_t)bh * m + L) * 64 + 16 * ct + 4 * g) =
+            make_float4(vl4[0], vl4[1], vl4[2], vl4[3]);
+      }
+    }
+
+    __syncthreads();
+
     // ---------------- G: grouped expert attention, one <=16-query tile at a time
     {
-      u32x4 qlh[2][2], qll[2][2];
-      load_ql(sm, qlh, qll, g, c16);
-      // V_L^T fragments, the A operand of the shared half of every tile: lane
-      // holds V_L^T[ch 16ct + c16][landmarks 4g..4g+3, 16+4g..16+4g+3]
-      u32x4 avl[4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        const int rowb = OFF_VLT + (16 * ct + c16) * VLT_STRIDE;
-        const u32x2 lo2 = *lds<u32x2>(sm, rowb + (4 * g) * 2);
-        const u32x2 hi2 = *lds<u32x2>(sm, rowb + (16 + 4 * g) * 2);
-        avl[ct] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-      }
+      // Q_L (hi, lo) and V_L^T fragments are re-read from LDS by every tile
+      // rather than held in registers across the loop
+      // (the last head re-reads its own rows, which are in cache, so that the
+      // registers are written on every path)
+      load_v(qr, head_rows(bh + (int)gridDim.x < BH ? Qh + (size_t)gridDim.x * head_elems : Qh, N), N, tid);
       const int ntiles = *lds<int>(sm, OFF_STAT + 64 * 4);
       float* outh = o.out + (size_t)bh * N * 64;
       // A tile's gathered operands: the expert's key rows for this lane's two
@@ -652,14 +686,12 @@ __global__ __launch_bounds__(THREADS, 2) void mita_fused_kernel(
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           const int slot = 16 * st + c16;
-          const bool ok = slot < k;
-          const uint16_t* kr = Kh + (size_t)(ok ? idxe[slot] : 0) * 64;
-          ti.ak[st][0] = ok ? *reinterpret_cast<const u32x4*>(kr + 8 * g) : z;
-          ti.ak[st][1] = ok ? *reinterpret_cast<const u32x4*>(kr + 32 + 8 * g) : z;
+          const int off = slot < k ? idxe[slot] * 128 + 16 * g : PAST;
+          ti.ak[st][0] = ld16(rK, off);
+          ti.ak[st][1] = ld16(rK, off + 64);
         }
-        const uint16_t* qrow = Qh + (size_t)ti.qi * 64;
-        ti.bq0 = *reinterpret_cast<const u32x4*>(qrow + 8 * g);
-        ti.bq1 = *reinterpret_cast<const u32x4*>(qrow + 32 + 8 * g);
+        ti.bq0 = ld16(rQ, ti.qi * 128 + 16 * g);
+        ti.bq1 = ld16(rQ, ti.qi * 128 + 16 * g + 64);
       };
       // the previous tile's output rows, stored once the next loads have landed
       // (one counter tracks loads and stores: stores issued ahead of a load
@@ -677,10 +709,11 @@ __global__ __launch_bounds__(THREADS, 2) void mita_fused_kernel(
           for (int ct = 0; ct < 4; ++ct)
             *reinterpret_cast<f32x4*>(outh + (size_t)pqi * 64 + 16 * ct + 4 * g) = pend[ct];
         }
-        TileIn nxt = cur;
-        if (tile + NWAVES < ntiles) fetch(tile + NWAVES, nxt);
+
         const int e = cur.e;
         // shared logits^T = Q_L Q_g^T (hi + lo) and routed logits^T = K_e Q_g^T
+        u32x4 qlh[2][2], qll[2][2];
+        load_ql(sm, qlh, qll, g, c16);
         f32x4 ls[2], lr[2];
 #pragma unroll
         for (int lt = 0; lt < 2; ++lt) {
@@ -725,7 +758,7 @@ __global__ __launch_bounds__(THREADS, 2) void mita_fused_kernel(
         const u32x4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
         f32x4 tot = mfma_f16(ones, bps, zero4());
         tot = mfma_f16(ones, bpr, tot);
-        const float inv = 1.0f / tot[0];
+        const float inv = __builtin_amdgcn_rcpf(tot[0]);
         // key ids of this lane's routed slots {4g..4g+3, 16+4g..16+4g+3}
         const i32x4 kv0 = *lds<i32x4>(sm, OFF_IDX + (e * KMAX + 4 * g) * 4);
         const i32x4 kv1 = *lds<i32x4>(sm, OFF_IDX + (e * KMAX + 16 + 4 * g) * 4);
@@ -737,18 +770,23 @@ __global__ __launch_bounds__(THREADS, 2) void mita_fused_kernel(
         }
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
+          // V_L^T[ch 16ct + c16][landmarks 4g..4g+3, 16+4g..16+4g+3]
+          const int rowb = OFF_VLT + (16 * ct + c16) * VLT_STRIDE;
+          const u32x2 lo2 = *lds<u32x2>(sm, rowb + (4 * g) * 2);
+          const u32x2 hi2 = *lds<u32x2>(sm, rowb + (16 + 4 * g) * 2);
+          const u32x4 avl = {lo2[0], lo2[1], hi2[0], hi2[1]};
           const uint16_t* vrow =
               reinterpret_cast<const uint16_t*>(sm + OFF_X + (16 * ct + c16) * VT_STRIDE);
           const u32x4 ave = {pack2(vrow[keys[0]], vrow[keys[1]]), pack2(vrow[keys[2]], vrow[keys[3]]),
                              pack2(vrow[keys[4]], vrow[keys[5]]), pack2(vrow[keys[6]], vrow[keys[7]])};
           f32x4 acc = zero4();
-          acc = mfma_f16(avl[ct], bps, acc);
+          acc = mfma_f16(avl, bps, acc);
           acc = mfma_f16(ave, bpr, acc);
           pend[ct] = acc * inv;
         }
         pqi = cur.qi;
         plive = cur.live;
-        cur = nxt;
+        if (tile + NWAVES < ntiles) fetch(tile + NWAVES, cur);
       }
       if (plive) {
 #pragma unroll

@@ -57,6 +57,13 @@ __device__ __forceinline__ uint32_t pk_f16(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// Two fp32 -> packed bf16x2 (round to nearest even, one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t h = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 // Pack two f16 bit patterns into one dword (lo in bits 0..15).
 __device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
 
