@@ -85,6 +85,17 @@ __device__ __forceinline__ int opaque_zero() {
   return z;
 }
 
+// This thread's coordinates, re-derived through an opaque zero at the start of
+// each phase: the compiler then recomputes them (a few cheap instructions)
+// instead of holding them, and values built from them, across phases.
+#define FUSED_IDS                                                              \
+  const int tid = threadIdx.x + opaque_zero(), lane = tid & 63, w = tid >> 6; \
+  const int g = lane >> 4, c16 = lane & 15;                                    \
+  (void)lane;                                                                  \
+  (void)w;                                                                     \
+  (void)g;                                                                     \
+  (void)c16
+
 // Byte offset of 16-byte chunk `c` (0..7) of a 128-byte row, XOR-swizzled so
 // that 16 consecutive rows read at one logical chunk spread over the banks.
 __device__ __forceinline__ int rc(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
@@ -145,6 +156,17 @@ __device__ __forceinline__ int g16_suffix_sum(int v) {
   v += dpp_i<DPP_ROW_SHL2>(v);
   v += dpp_i<DPP_ROW_SHL4>(v);
   v += dpp_i<DPP_ROW_SHL8>(v);
+  return v;
+}
+// Inclusive prefix sum over a 16-lane group: lane t gets sum over t' <= t
+// (row_shr:n hands lane t the value of lane t-n, zero before the row start).
+constexpr int DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114,
+              DPP_ROW_SHR8 = 0x118;
+__device__ __forceinline__ int g16_prefix_sum(int v) {
+  v += dpp_i<DPP_ROW_SHR1>(v);
+  v += dpp_i<DPP_ROW_SHR2>(v);
+  v += dpp_i<DPP_ROW_SHR4>(v);
+  v += dpp_i<DPP_ROW_SHR8>(v);
   return v;
 }
 // (value, index) argmax over a 16-lane group, ties to the lower index.
@@ -264,6 +286,9 @@ __device__ __forceinline__ uint32_t member_pair(uint32_t m0, uint32_t m1, int L)
   return b * 0x3F80u;
 }
 
+// EXTRAS: whether any of the optional intermediate outputs is requested; the
+// plain forward is compiled without their stores and branches.
+template <bool EXTRAS>
 __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, Outputs o, int BH, int gh, int gw, int mh, int mw, int k) {
@@ -326,21 +351,12 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
       ka[j][0] = ld16(rK, off);
       ka[j][1] = ld16(rK, off + 64);
     }
-    // the routing phase's query rows fly with C's K rows
-    u32x4 qb[TPW][2];
-#pragma unroll
-    for (int j = 0; j < TPW; ++j) {
-      const int tok = 16 * (w + NWAVES * j) + c16;
-      const int off = tok < N ? tok * 128 + 16 * g : PAST;
-      qb[j][0] = ld16(rQ, off);
-      qb[j][1] = ld16(rQ, off + 64);
-    }
-
     __syncthreads();
 
     // ---------------- B: landmark pooling as a contraction over tokens,
     // Q_L^T = Q^T W (W: 0/1 window membership) on bf16 MFMA, then / window size
     {
+      FUSED_IDS;
       const int ct = w & 3, L = 16 * (w >> 2) + c16;
       f32x4 acc = zero4();
       for (int ks = 0; ks < KP / 32; ++ks) {
@@ -360,36 +376,196 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
       const int off = rc(L, 2 * ct + (g >> 1)) + (g & 1) * 8;
       *lds<u32x2>(sm, OFF_QLH + off) = u32x2{h01, h23};
       *lds<u32x2>(sm, OFF_QLL + off) = u32x2{l01, l23};
-      if (o.ql && L < m)
+      if (EXTRAS && o.ql && L < m)
         *reinterpret_cast<float4*>(o.ql + ((size_t)bh * m + L) * 64 + 16 * ct + 4 * g) =
             make_float4(q0, q1, q2, q3);
     }
     __syncthreads();
 
-    // ---------------- C: S^T = K Q_L^T (K rows from global memory) -> S rows in X
+    // ---------------- C: S^T = K Q_L^T (K rows from global memory) -> S rows in X,
+    // and (same Q_L fragments) the routing scores of E'
     {
+      FUSED_IDS;
       u32x4 qlh[2][2], qll[2][2];
       load_ql(sm, qlh, qll, g, c16);
+      // every key column up to 16 * MAXNT is written: keys past N get -inf
 #pragma unroll
       for (int j = 0; j < TPW; ++j) {
         const int tt = w + NWAVES * j;
-        if (tt < nt) {
+        if (tt < MAXNT) {
+          const int kb = 16 * tt + 4 * g;
 #pragma unroll
           for (int lt = 0; lt < 2; ++lt) {
             f32x4 c = zero4();
-            c = mfma_bf16(ka[j][0], qlh[lt][0], c);
-            c = mfma_bf16(ka[j][0], qll[lt][0], c);
-            c = mfma_bf16(ka[j][1], qlh[lt][1], c);
-            c = mfma_bf16(ka[j][1], qll[lt][1], c);
-            // lane holds S^T[key 16tt + 4g + r][landmark 16lt + c16]
-            *lds<float4>(sm, OFF_X + ((16 * lt + c16) * S_STRIDE + 16 * tt + 4 * g) * 4) =
-                make_float4(c[0] * tau, c[1] * tau, c[2] * tau, c[3] * tau);
+            if (tt < nt) {
+              c = mfma_bf16(ka[j][0], qlh[lt][0], c);
+              c = mfma_bf16(ka[j][0], qll[lt][0], c);
+              c = mfma_bf16(ka[j][1], qlh[lt][1], c);
+              c = mfma_bf16(ka[j][1], qll[lt][1], c);
+            }
+            // lane holds S^T[key kb + r][landmark 16lt + c16]
+            *lds<float4>(sm, OFF_X + ((16 * lt + c16) * S_STRIDE + kb) * 4) =
+                make_float4(kb < N ? c[0] * tau : -INFINITY, kb + 1 < N ? c[1] * tau : -INFINITY,
+                            kb + 2 < N ? c[2] * tau : -INFINITY, kb + 3 < N ? c[3] * tau : -INFINITY);
           }
+        }
+      }
+    }
+    // the routing phase's query rows fly while the rows' top-k runs
+    u32x4 qb[TPW][2];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int tok = 16 * (w + NWAVES * j) + c16;
+      const int off = tok < N ? tok * 128 + 16 * g : PAST;
+      qb[j][0] = ld16(rQ, off);
+      qb[j][1] = ld16(rQ, off + 64);
+    }
+    __syncthreads();
+
+    // ---------------- D: exact top-k of each landmark row; then P = exp(S - max) in f16
+    {
+      FUSED_IDS;
+      static_assert(4 * NWAVES == MMAX, "one landmark row per 16-lane group");
+      const int i = 4 * w + g;  // landmark row of this 16-lane group
+      const bool active = i < m;
+      if (__ballot(active) != 0) {
+        const int t = c16, key0 = MAXNT * t;  // this lane owns keys key0 .. key0 + 12
+        // scores (-inf at padding keys; rows past m hold zeros and are
+        // computed but never used)
+        float v[MAXNT];
+#pragma unroll
+        for (int u = 0; u < MAXNT; ++u) v[u] = *lds<float>(sm, OFF_X + (i * S_STRIDE + key0 + u) * 4);
+        float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < MAXNT; ++u) {
+          lo = fminf(lo, key0 + u < N ? v[u] : INFINITY);
+          hi = fmaxf(hi, v[u]);
+        }
+        lo = g16_min(lo);
+        hi = g16_max(hi);
+        const float rmax = hi;
+        // 128 equal bins over [lo, hi]: f = (x - lo) * 128 / (hi - lo), bin =
+        // floor(f) clamped to [0, 127] (A > 0, so padding has f = -inf and
+        // lands in bin 0, whose counter starts at minus the padding count).
+        // Lane t owns the 32-bit counters of bins 8t .. 8t+7.
+        const float A = hi > lo ? fminf(128.0f / (hi - lo), 1e30f) : 1.f, B = -lo * A;
+        float f[MAXNT];
+#pragma unroll
+        for (int u = 0; u < MAXNT; ++u) f[u] = __builtin_fmaf(v[u], A, B);
+        char* hrow = sm + OFF_H + i * H_STRIDE;
+        uint32_t* hist = reinterpret_cast<uint32_t*>(hrow);
+        // (constants through an opaque zero: built here, not held in
+        // registers across the head loop)
+        const uint32_t z0 = (uint32_t)opaque_zero();
+        const float c127 = 127.0f + (float)opaque_zero();
+        *reinterpret_cast<u32x4*>(hrow + 32 * t) = u32x4{t == 0 ? (uint32_t)(N - 16 * MAXNT) : z0, z0, z0, z0};
+        *reinterpret_cast<u32x4*>(hrow + 32 * t + 16) = u32x4{z0, z0, z0, z0};
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int u = 0; u < MAXNT; ++u) atomicAdd(hist + (int)__builtin_amdgcn_fmed3f(f[u], 0.f, c127), 1u);
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        // the boundary bin b*: the bin holding the k-th largest score; `above`
+        // keys lie in higher bins, `inb` in b* itself
+        int bstar = 0, above = 0, inb = 0;
+        {
+          const u32x4 d0 = *reinterpret_cast<const u32x4*>(hrow + 32 * t);
+          const u32x4 d1 = *reinterpret_cast<const u32x4*>(hrow + 32 * t + 16);
+          const int cb[8] = {(int)d0[0], (int)d0[1], (int)d0[2], (int)d0[3],
+                             (int)d1[0], (int)d1[1], (int)d1[2], (int)d1[3]};
+          int local = 0;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) local += cb[q];
+          // keys in bins above this lane's (higher lane = higher bins)
+          int acc = g16_suffix_sum(local) - local;
+          int hit_b = 0, hit_a = 0, hit_n = 0;
+#pragma unroll
+          for (int q = 7; q >= 0; --q) {
+            const bool h = acc < k && acc + cb[q] >= k;
+            hit_b = h ? 8 * t + q : hit_b;
+            hit_a = h ? acc : hit_a;
+            hit_n = h ? cb[q] : hit_n;
+            acc += cb[q];
+          }
+          // exactly one lane of an active group hits: masked group sums broadcast
+          const bool mine = active && hit_n > 0;
+          bstar = g16_sumi(mine ? hit_b : 0);
+          above = g16_sumi(mine ? hit_a : 0);
+          inb = g16_sumi(mine ? hit_n : 0);
+        }
+        // bin > b* <=> f >= b* + 1 and bin == b* <=> f in [b*, b* + 1), with the
+        // clamped end bins open-ended
+        const float th = bstar == 127 ? INFINITY : (float)(bstar + 1);
+        const float tl = bstar == 0 ? -1e30f : (float)bstar;
+        uint32_t take = 0, bnd = 0;
+#pragma unroll
+        for (int u = 0; u < MAXNT; ++u) {
+          take |= (f[u] >= th ? 1u : 0u) << u;
+          bnd |= (f[u] >= tl && f[u] < th ? 1u : 0u) << u;
+        }
+        // the boundary bin supplies k - above keys: all of them when that is
+        // its whole count, else the best first (larger score, then lower key
+        // id), one per round
+        int need = active ? k - above : 0;
+        if (active && need == inb) {
+          take |= bnd;
+          need = 0;
+        }
+        for (; __ballot(need > 0) != 0; --need) {
+          float bv = -INFINITY;
+          int bk = 0x7FFFFFFF;
+#pragma unroll
+          for (int u = MAXNT - 1; u >= 0; --u) {  // descending: ties keep the lower key
+            const bool c = (bnd >> u & 1u) && v[u] >= bv;
+            bv = c ? v[u] : bv;
+            bk = c ? key0 + u : bk;
+          }
+          g16_argmax_key(bv, bk);
+          if (need > 0 && bk - key0 >= 0 && bk - key0 < MAXNT) {
+            const int u = bk - key0;
+            take |= 1u << u;
+            bnd &= ~(1u << u);
+          }
+        }
+        // the expert: kept key ids in ascending order (lane-major, since each
+        // lane owns a contiguous key range); lanes without a key to write
+        // (and, as a guard, any position past the row's slots) aim at their
+        // own word of the spent histogram
+        {
+          const int cnt = __popc(take);
+          int pos = g16_prefix_sum(cnt) - cnt;
+#pragma unroll
+          for (int u = 0; u < MAXNT; ++u) {
+            const bool bit = take >> u & 1u;
+            const int off = bit && pos < KMAX ? OFF_IDX + (i * KMAX + pos) * 4 : OFF_H + i * H_STRIDE + 4 * t;
+            *lds<int>(sm, off) = key0 + u;
+            pos += bit ? 1 : 0;
+          }
+        }
+        // P row (f16) over this row's bytes, zero past the owned keys up to the
+        // padded width, and its sum (of the rounded values the products use)
+        float sum = 0.f;
+        uint16_t* prow = reinterpret_cast<uint16_t*>(hrow);
+        const float moff = active ? -rmax * 1.4426950408889634f : 0.f;
+#pragma unroll
+        for (int u = 0; u < MAXNT; ++u) {
+          const uint32_t hb = f16_bits(__builtin_amdgcn_exp2f(__builtin_fmaf(v[u], 1.4426950408889634f, moff)));
+          sum += f16_bits_to_f32(hb);
+          prow[key0 + u] = (uint16_t)hb;
+        }
+        static_assert(MAXNT * 16 + 16 == KPMAX, "one zero column per lane past the owned keys");
+        prow[MAXNT * 16 + t] = 0;
+        sum = g16_sumf(sum);
+        if (t == 0) {
+          *lds<float>(sm, OFF_STAT + i * 4) = rmax;
+          *lds<float>(sm, OFF_STAT + (32 + i) * 4) = active ? sum : 1.0f;
         }
       }
     }
     // ---------------- E': R^T = Q_L Q^T per token tile (Q rows from global memory): routes
     {
+      FUSED_IDS;
       u32x4 qlh[2][2], qll[2][2];
       load_ql(sm, qlh, qll, g, c16);
 #pragma unroll
@@ -425,140 +601,8 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
         }
         if (g == 0 && tok < N) {
           *lds<int>(sm, OFF_ROUTE + tok * 4) = bi;
-          if (o.route) o.route[(size_t)bh * N + tok] = bi;
+          if (EXTRAS && o.route) o.route[(size_t)bh * N + tok] = bi;
         }
-      }
-    }
-    __syncthreads();
-
-    // ---------------- D: exact top-k of each landmark row; then P = exp(S - max) in f16
-#pragma unroll 1
-    for (int jr = 0; jr < MMAX / (4 * NWAVES); ++jr) {
-      const int i = 4 * w + g + 4 * NWAVES * jr;  // landmark row of this 16-lane group
-      if (__ballot(i < m) == 0) continue;
-      const bool active = i < m;
-      const int t = c16;
-      // this lane's scores (keys t + 16u); -inf marks none
-      float v[MAXNT];
-#pragma unroll
-      for (int u = 0; u < MAXNT; ++u) {
-        const int j = t + 16 * u;
-        v[u] = active && j < N ? *lds<float>(sm, OFF_X + (i * S_STRIDE + j) * 4) : -INFINITY;
-      }
-      float lo = INFINITY, hi = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < MAXNT; ++u) {
-        lo = fminf(lo, v[u] > -INFINITY ? v[u] : INFINITY);
-        hi = fmaxf(hi, v[u]);
-      }
-      lo = g16_min(lo);
-      hi = g16_max(hi);
-      const float rmax = hi;
-      // 128 equal bins over [lo, hi], 32-bit counters in the row's histogram
-      // bytes (lane t owns bins 8t .. 8t+7); padding adds 0
-      const float A = hi > lo ? fminf(128.0f / (hi - lo), 1e30f) : 0.f, B = -lo * A;
-      auto bin = [&](float x) {
-        return (int)__builtin_amdgcn_fmed3f(__builtin_fmaf(x, A, B), 0.f, 127.f);
-      };
-      const uint32_t below = (1u << t) - 1u;
-      char* hrow = sm + OFF_H + i * H_STRIDE;
-      uint32_t* hist = reinterpret_cast<uint32_t*>(hrow);
-      *reinterpret_cast<u32x4*>(hrow + 32 * t) = u32x4{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4*>(hrow + 32 * t + 16) = u32x4{0u, 0u, 0u, 0u};
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int u = 0; u < MAXNT; ++u)
-        atomicAdd(hist + bin(v[u]), v[u] > -INFINITY ? 1u : 0u);
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      int bstar = 0, above = 0;
-      {
-        const u32x4 d0 = *reinterpret_cast<const u32x4*>(hrow + 32 * t);
-        const u32x4 d1 = *reinterpret_cast<const u32x4*>(hrow + 32 * t + 16);
-        const int cb[8] = {(int)d0[0], (int)d0[1], (int)d0[2], (int)d0[3],
-                           (int)d1[0], (int)d1[1], (int)d1[2], (int)d1[3]};
-        int local = 0;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) local += cb[q];
-        // inclusive suffix sum over the group's lanes (higher lane = higher bins)
-        int acc = g16_suffix_sum(local) - local;  // keys in bins above this lane's
-        int hit_b = 0, hit_a = 0;
-        bool hit = false;
-#pragma unroll
-        for (int q = 7; q >= 0; --q) {
-          const bool h = acc < k && acc + cb[q] >= k;
-          hit_b = h ? 8 * t + q : hit_b;
-          hit_a = h ? acc : hit_a;
-          hit = hit || h;
-          acc += cb[q];
-        }
-        // exactly one lane of an active group hits: a masked group sum broadcasts
-        bstar = g16_sumi(active && hit ? hit_b : 0);
-        above = g16_sumi(active && hit ? hit_a : 0);
-      }
-      // keys above the boundary bin are in; the boundary bin supplies the
-      // rest, best first (larger score, then lower key id), one per round
-      uint32_t take = 0, bnd = 0;
-#pragma unroll
-      for (int u = 0; u < MAXNT; ++u) {
-        const int b = bin(v[u]);
-        const bool ok = v[u] > -INFINITY;
-        take |= (ok && b > bstar ? 1u : 0u) << u;
-        bnd |= (ok && b == bstar ? 1u : 0u) << u;
-      }
-      for (int need = active ? k - above : 0; __ballot(need > 0) != 0; --need) {
-        float bv = -INFINITY;
-        int bk = 0x7FFFFFFF;
-#pragma unroll
-        for (int u = 0; u < MAXNT; ++u) {
-          const bool c = (bnd >> u & 1u) && (v[u] > bv || (v[u] == bv && t + 16 * u < bk));
-          bv = c ? v[u] : bv;
-          bk = c ? t + 16 * u : bk;
-        }
-        g16_argmax_key(bv, bk);
-        if (need > 0 && (bk & 15) == t) {
-          const int u = bk >> 4;
-          take |= 1u << u;
-          bnd &= ~(1u << u);
-        }
-      }
-      // the expert: kept key ids in ascending order
-      {
-        int run = 0;
-#pragma unroll
-        for (int u = 0; u < MAXNT; ++u) {
-          const bool bit = take >> u & 1u;
-          const uint32_t gm = g16_bits(__ballot(bit), g);
-          const int pos = run + __popc(gm & below);
-          if (bit) {
-            const int j = t + 16 * u;
-            *lds<int>(sm, OFF_IDX + (i * KMAX + pos) * 4) = j;
-            if (o.idx) o.idx[((size_t)bh * m + i) * k + pos] = j;
-          }
-          run += __popc(gm);
-        }
-      }
-      // P row (f16) over this row's bytes, and its sum
-      float sum = 0.f;
-      uint16_t* prow = reinterpret_cast<uint16_t*>(hrow);
-      const float moff = -rmax * 1.4426950408889634f;
-#pragma unroll
-      for (int u = 0; u < KPMAX / 16; ++u) {
-        const int j = t + 16 * u;
-        if (j < KP) {
-          uint32_t hb = 0;
-          if (active && u < MAXNT) {
-            hb = f16_bits(__builtin_amdgcn_exp2f(__builtin_fmaf(v[u < MAXNT ? u : 0], 1.4426950408889634f, moff)));
-            sum += f16_bits_to_f32(hb);
-          }
-          prow[j] = (uint16_t)hb;
-        }
-      }
-      sum = g16_sumf(sum);
-      if (t == 0) {
-        *lds<float>(sm, OFF_STAT + i * 4) = rmax;
-        *lds<float>(sm, OFF_STAT + (32 + i) * 4) = active ? sum : 1.0f;
       }
     }
     // the V rows fly while the queries are grouped
@@ -566,101 +610,116 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
     load_v(vr, head_rows(V + bh * head_elems, N), N, tid);
     __syncthreads();
 
+    if (EXTRAS && o.idx) {
+      for (int q = tid; q < m * k; q += THREADS)
+        o.idx[(size_t)bh * m * k + q] = *lds<int>(sm, OFF_IDX + ((q / k) * KMAX + q % k) * 4);
+    }
+
     // ---------------- F: group queries by route (stable counting sort), tile list
-    const int nchunks = (N + 63) >> 6;
-    int myroute = -1, myrank = 0;
-    if (w < nchunks) {
-      const int n = 64 * w + lane;
-      myroute = n < N ? *lds<int>(sm, OFF_ROUTE + n * 4) : -1;
-      int mycnt = 0;
-      for (int e = 0; e < m; ++e) {
-        const uint64_t b = __ballot(myroute == e);
-        if (myroute == e) myrank = __popcll(b & ((1ull << lane) - 1ull));
-        if (lane == e) mycnt = __popcll(b);
-      }
-      if (lane < 32) *lds<int>(sm, OFF_CNT + (w * 32 + lane) * 4) = lane < m ? mycnt : 0;
-    }
-    __syncthreads();
-    if (w == 0) {
-      int tot = 0, pre[4] = {0, 0, 0, 0};
-      if (lane < 32) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          pre[c] = tot;
-          if (c < nchunks) tot += *lds<int>(sm, OFF_CNT + (c * 32 + lane) * 4);
+    {
+      FUSED_IDS;
+      const int nchunks = (N + 63) >> 6;
+      int myroute = -1, myrank = 0;
+      if (w < nchunks) {
+        const int n = 64 * w + lane;
+        myroute = n < N ? *lds<int>(sm, OFF_ROUTE + n * 4) : -1;
+        int mycnt = 0;
+        for (int e = 0; e < m; ++e) {
+          const uint64_t b = __ballot(myroute == e);
+          if (myroute == e) myrank = __popcll(b & ((1ull << lane) - 1ull));
+          if (lane == e) mycnt = __popcll(b);
         }
+        if (lane < 32) *lds<int>(sm, OFF_CNT + (w * 32 + lane) * 4) = lane < m ? mycnt : 0;
       }
-      // exclusive scans over the 32 expert lanes: query offsets and tile offsets
-      const int ntl = (tot + 15) >> 4;
-      int s1 = tot, s2 = ntl;
-#pragma unroll
-      for (int off = 1; off < 32; off <<= 1) {
-        const int x1 = __shfl_up(s1, off, 64), x2 = __shfl_up(s2, off, 64);
-        if (lane >= off) { s1 += x1; s2 += x2; }
-      }
-      const int off_e = s1 - tot, toff = s2 - ntl;
-      if (lane < 32) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (c < nchunks) *lds<int>(sm, OFF_BASE + (c * 32 + lane) * 4) = off_e + pre[c];
-        if (lane < m) {
-          *lds<int>(sm, OFF_OFFS + lane * 4) = off_e;
-          for (int s = 0; s < ntl; ++s) {
-            int4* tl = lds<int4>(sm, OFF_TILES + (toff + s) * 16);
-            *tl = make_int4(lane, off_e + 16 * s, min(16, tot - 16 * s), 0);
+      __syncthreads();
+      if (w == 0) {
+        int tot = 0, pre[4] = {0, 0, 0, 0};
+        if (lane < 32) {
+  #pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            pre[c] = tot;
+            if (c < nchunks) tot += *lds<int>(sm, OFF_CNT + (c * 32 + lane) * 4);
           }
-          if (o.counts) o.counts[(size_t)bh * m + lane] = tot;
-          if (o.offsets) o.offsets[(size_t)bh * (m + 1) + lane] = off_e;
+        }
+        // exclusive scans over the 32 expert lanes: query offsets and tile offsets
+        const int ntl = (tot + 15) >> 4;
+        int s1 = tot, s2 = ntl;
+  #pragma unroll
+        for (int off = 1; off < 32; off <<= 1) {
+          const int x1 = __shfl_up(s1, off, 64), x2 = __shfl_up(s2, off, 64);
+          if (lane >= off) { s1 += x1; s2 += x2; }
+        }
+        const int off_e = s1 - tot, toff = s2 - ntl;
+        if (lane < 32) {
+  #pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (c < nchunks) *lds<int>(sm, OFF_BASE + (c * 32 + lane) * 4) = off_e + pre[c];
+          if (lane < m) {
+            *lds<int>(sm, OFF_OFFS + lane * 4) = off_e;
+            for (int s = 0; s < ntl; ++s) {
+              int4* tl = lds<int4>(sm, OFF_TILES + (toff + s) * 16);
+              *tl = make_int4(lane, off_e + 16 * s, min(16, tot - 16 * s), 0);
+            }
+            if (EXTRAS && o.counts) o.counts[(size_t)bh * m + lane] = tot;
+            if (EXTRAS && o.offsets) o.offsets[(size_t)bh * (m + 1) + lane] = off_e;
+          }
+        }
+        const int ntiles = __shfl(s2, 31, 64);
+        if (lane == 0) {
+          *lds<int>(sm, OFF_STAT + 64 * 4) = ntiles;
+          if (EXTRAS && o.offsets) o.offsets[(size_t)bh * (m + 1) + m] = N;
         }
       }
-      const int ntiles = __shfl(s2, 31, 64);
-      if (lane == 0) {
-        *lds<int>(sm, OFF_STAT + 64 * 4) = ntiles;
-        if (o.offsets) o.offsets[(size_t)bh * (m + 1) + m] = N;
+      __syncthreads();
+      if (w < nchunks && myroute >= 0) {
+        const int pos = *lds<int>(sm, OFF_BASE + (w * 32 + myroute) * 4) + myrank;
+        *lds<int>(sm, OFF_PERM + pos * 4) = 64 * w + lane;
+        if (EXTRAS && o.perm) o.perm[(size_t)bh * N + pos] = 64 * w + lane;
       }
+      __syncthreads();
     }
-    __syncthreads();
-    if (w < nchunks && myroute >= 0) {
-      const int pos = *lds<int>(sm, OFF_BASE + (w * 32 + myroute) * 4) + myrank;
-      *lds<int>(sm, OFF_PERM + pos * 4) = 64 * w + lane;
-      if (o.perm) o.perm[(size_t)bh * N + pos] = 64 * w + lane;
-    }
-    __syncthreads();
 
     // ---------------- V: V^T (f16) over the score region
-    store_vt(vr, sm, tid);
+    {
+      FUSED_IDS;
+      store_vt(vr, sm, tid);
+    }
     __syncthreads();
 
     // ---------------- E: V_L^T = V^T P^T (16-channel x 16-landmark tiles)
-#pragma unroll 1
-    for (int tile = w; tile < 8; tile += NWAVES) {
-      const int ct = tile & 3, lt = tile >> 2;
-      f32x4 acc = zero4();
-      for (int ks = 0; ks < KP / 32; ++ks) {
-        const u32x4 a = *lds<u32x4>(sm, OFF_X + (16 * ct + c16) * VT_STRIDE + (32 * ks + 8 * g) * 2);
-        const u32x4 b = *lds<u32x4>(sm, OFF_H + (16 * lt + c16) * H_STRIDE + (32 * ks + 8 * g) * 2);
-        acc = mfma_f16(a, b, acc);
+    {
+      FUSED_IDS;
+  #pragma unroll 1
+      for (int tile = w; tile < 8; tile += NWAVES) {
+        const int ct = tile & 3, lt = tile >> 2;
+        f32x4 acc = zero4();
+        for (int ks = 0; ks < KP / 32; ++ks) {
+          const u32x4 a = *lds<u32x4>(sm, OFF_X + (16 * ct + c16) * VT_STRIDE + (32 * ks + 8 * g) * 2);
+          const u32x4 b = *lds<u32x4>(sm, OFF_H + (16 * lt + c16) * H_STRIDE + (32 * ks + 8 * g) * 2);
+          acc = mfma_f16(a, b, acc);
+        }
+        const int L = 16 * lt + c16;
+        const bool ok = L < m;
+        const float inv = ok ? 1.0f / *lds<float>(sm, OFF_STAT + (32 + L) * 4) : 0.f;
+        float vl4[4];
+  #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          vl4[r] = ok ? acc[r] * inv : 0.f;
+          *lds<uint16_t>(sm, OFF_VLT + (16 * ct + 4 * g + r) * VLT_STRIDE + L * 2) =
+              (uint16_t)f16_bits(vl4[r]);
+        }
+        if (EXTRAS && ok && o.vl) {
+          *reinterpret_cast<float4*>(o.vl + ((size_t)bh * m + L) * 64 + 16 * ct + 4 * g) =
+              make_float4(vl4[0], vl4[1], vl4[2], vl4[3]);
+        }
       }
-      const int L = 16 * lt + c16;
-      const bool ok = L < m;
-      const float inv = ok ? 1.0f / *lds<float>(sm, OFF_STAT + (32 + L) * 4) : 0.f;
-      float vl4[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        vl4[r] = ok ? acc[r] * inv : 0.f;
-        *lds<uint16_t>(sm, OFF_VLT + (16 * ct + 4 * g + r) * VLT_STRIDE + L * 2) =
-            (uint16_t)f16_bits(vl4[r]);
-      }
-      if (ok && o.vl) {
-        *reinterpret_cast<float4*>(o.vl + ((size_t)bh * m + L) * 64 + 16 * ct + 4 * g) =
-            make_float4(vl4[0], vl4[1], vl4[2], vl4[3]);
-      }
-    }
 
+    }
     __syncthreads();
 
     // ---------------- G: grouped expert attention, one <=16-query tile at a time
     {
+      FUSED_IDS;
       // Q_L (hi, lo) and V_L^T fragments are re-read from LDS by every tile
       // rather than held in registers across the loop
       // (the last head re-reads its own rows, which are in cache, so that the
@@ -680,8 +739,9 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
       auto fetch = [&](int tile, TileIn& ti) {
         const int4 tl = *lds<int4>(sm, OFF_TILES + tile * 16);
         ti.e = tl.x;
-        ti.live = c16 < tl.z;
-        ti.qi = ti.live ? *lds<int>(sm, OFF_PERM + (tl.y + c16) * 4) : 0;
+        const int q = c16 < tl.z ? *lds<int>(sm, OFF_PERM + (tl.y + c16) * 4) : -1;
+        ti.live = (unsigned)q < (unsigned)N;  // (also guards the output store)
+        ti.qi = ti.live ? q : 0;
         const int* idxe = lds<int>(sm, OFF_IDX + ti.e * KMAX * 4);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
@@ -818,9 +878,10 @@ hipError_t launch_fused(const void* Q, const void* K, const void* V, float* out,
   // two resident workgroups per CU, each walking heads
   const int slots = 2 * device_cu_count();
   const int grid = s.BH < slots ? s.BH : slots;
-  fused::mita_fused_kernel<<<grid, fused::THREADS, 0, st>>>(
-      (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, o, s.BH, s.grid_h, s.grid_w,
-      s.m_h, s.m_w, s.k);
+  const bool extras = idx || route || ql || vl || counts || offsets || perm;
+  auto kernel = extras ? fused::mita_fused_kernel<true> : fused::mita_fused_kernel<false>;
+  kernel<<<grid, fused::THREADS, 0, st>>>((const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, o,
+                                          s.BH, s.grid_h, s.grid_w, s.m_h, s.m_w, s.k);
   return hipGetLastError();
 }
 
