@@ -729,8 +729,7 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
       float* outh = o.out + (size_t)bh * N * 64;
       // A tile's gathered operands: the expert's key rows for this lane's two
       // slot tiles and the query row of lane column c16 (columns past the
-      // tile's length compute on query 0 and are never stored).  The next
-      // tile's are loaded while this one computes.
+      // tile's length compute on query 0 and are never stored).
       struct TileIn {
         int e, qi;
         bool live;
@@ -791,6 +790,11 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
           c = mfma_bf16(cur.ak[st][1], cur.bq1, c);
           lr[st] = c;
         }
+        // the gathered operands are consumed: the next tile's loads reuse
+        // their registers and fly while this tile's softmax and products run
+        const int qi = cur.qi;
+        const bool live = cur.live;
+        if (tile + NWAVES < ntiles) fetch(tile + NWAVES, cur);
         float x[16];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -844,9 +848,8 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
           acc = mfma_f16(ave, bpr, acc);
           pend[ct] = acc * inv;
         }
-        pqi = cur.qi;
-        plive = cur.live;
-        if (tile + NWAVES < ntiles) fetch(tile + NWAVES, cur);
+        pqi = qi;
+        plive = live;
       }
       if (plive) {
 #pragma unroll
