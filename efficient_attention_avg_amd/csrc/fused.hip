@@ -50,22 +50,24 @@ constexpr int VLT_STRIDE = 80;      // bytes per V_L^T row (f16 landmarks)
 constexpr int X_BYTES = 64 * VT_STRIDE > MMAX * S_STRIDE * 4 ? 64 * VT_STRIDE : MMAX * S_STRIDE * 4;
 constexpr int OFF_X = 0;                          // S (phases C, D), then V^T (E, G)
 constexpr int OFF_H = OFF_X + X_BYTES;
-constexpr int OFF_QLH = OFF_H + MMAX * H_STRIDE;
+// H: histograms and P rows (D, E), then the head's K rows, bf16 and
+// chunk-swizzled like Q_L, for the expert tiles (G)
+constexpr int H_BYTES = MMAX * H_STRIDE > NP * 128 ? MMAX * H_STRIDE : NP * 128;
+constexpr int OFF_QLH = OFF_H + H_BYTES;
 constexpr int OFF_QLL = OFF_QLH + MMAX * 128;
 constexpr int OFF_VLT = OFF_QLL + MMAX * 128;
 constexpr int OFF_IDX = OFF_VLT + 64 * VLT_STRIDE;
 constexpr int OFF_ROUTE = OFF_IDX + MMAX * KMAX * 4;
 constexpr int OFF_PERM = OFF_ROUTE + 256 * 4;
-constexpr int OFF_CNT = OFF_PERM + 256 * 4;       // [4 chunks][32] int
-constexpr int OFF_BASE = OFF_CNT + 4 * 32 * 4;    // [4 chunks][32] int
-constexpr int OFF_OFFS = OFF_BASE + 4 * 32 * 4;   // [33] int
-constexpr int OFF_TILES = OFF_OFFS + 48 * 4;      // [64] x (e, start, len, -)
-constexpr int OFF_STAT = OFF_TILES + 64 * 16;     // rowmax[32], rowsum[32], ntiles
+constexpr int OFF_BM = OFF_PERM + 256 * 4;        // [32 experts][8] words: query bitmaps
+constexpr int OFF_OFFS = OFF_BM + MMAX * 8 * 4;   // [33] int: expert offsets in PERM
+constexpr int OFF_STAT = OFF_OFFS + 48 * 4;       // rowmax[32], rowsum[32], non-empty experts
 constexpr int OFF_WMASK = OFF_STAT + 80 * 4;      // [KPMAX] landmark-membership bits per token
-constexpr int LDS_BYTES = OFF_WMASK + KPMAX * 4;
+constexpr int OFF_INVC = OFF_WMASK + KPMAX * 4;   // [MMAX] 1 / pooling window size
+constexpr int LDS_BYTES = OFF_INVC + MMAX * 4;
 static_assert(2 * LDS_BYTES <= 160 * 1024, "two workgroups per gfx950 CU");
 static_assert(OFF_H % 16 == 0 && OFF_QLH % 16 == 0 && OFF_VLT % 16 == 0 && OFF_IDX % 16 == 0 &&
-                  OFF_TILES % 16 == 0,
+                  OFF_BM % 16 == 0,
               "16-byte aligned LDS regions");
 
 struct Outputs {
@@ -296,8 +298,7 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
   const int N = gh * gw, m = mh * mw;
   const int nt = (N + 15) >> 4;
   const int KP = (N + 31) & ~31;
-  const float tau = 0.125f;  // 1/sqrt(64)
-  const float kLogitScale = tau * 1.4426950408889634f;  // tau * log2(e): base-2 softmax
+  const float kLogitScale = 0.125f * 1.4426950408889634f;  // 1/sqrt(64) * log2(e): base-2 softmax
   const size_t head_elems = (size_t)N * 64;
   const u32x4 z = {0u, 0u, 0u, 0u};
   static_assert(NWAVES == 8, "pooling: one 16-channel x 16-landmark tile per wave");
@@ -316,16 +317,17 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
     }
     *lds<uint32_t>(sm, OFF_WMASK + tok * 4) = bits;
   }
-  // 1 / window size of this lane's pooling column
-  float inv_cnt = 0.f;
-  {
-    const int L = 16 * ((threadIdx.x >> 6) >> 2) + (threadIdx.x & 15);
+  // 1 / window size per landmark (0 past m)
+  if (threadIdx.x < MMAX) {
+    const int L = threadIdx.x;
+    float inv_cnt = 0.f;
     if (L < m) {
       int y0, y1, x0, x1;
       pool_window(L / mw, gh, mh, &y0, &y1);
       pool_window(L % mw, gw, mw, &x0, &x1);
       inv_cnt = 1.0f / (float)((y1 - y0) * (x1 - x0));
     }
+    *lds<float>(sm, OFF_INVC + L * 4) = inv_cnt;
   }
 
   // a head's Q rows are requested while the previous head runs its expert tiles
@@ -342,6 +344,7 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
     const Rsrc rQ = head_rows(Qh, N), rK = head_rows(K + bh * head_elems, N);
     __syncthreads();  // the previous head is done with LDS
     store_qt(qr, sm, tid);
+    if (tid < MMAX * 8) *lds<uint32_t>(sm, OFF_BM + tid * 4) = 0u;
     // C's K rows, issued after the Q^T store so that its wait does not cover them
     u32x4 ka[TPW][2];
 #pragma unroll
@@ -368,11 +371,16 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
         acc = mfma_bf16(a, b, acc);
       }
       // lane holds Q_L[landmark L][channels 16ct + 4g .. +3]: fp32, then bf16 hi + lo
+      const float inv_cnt = *lds<float>(sm, OFF_INVC + L * 4);
       const float q0 = acc[0] * inv_cnt, q1 = acc[1] * inv_cnt;
       const float q2 = acc[2] * inv_cnt, q3 = acc[3] * inv_cnt;
-      const uint32_t h01 = pk_bf16(q0, q1), h23 = pk_bf16(q2, q3);
-      const uint32_t l01 = pk_bf16(q0 - bf16_bits_to_f32(h01 & 0xFFFFu), q1 - bf16_bits_to_f32(h01 >> 16));
-      const uint32_t l23 = pk_bf16(q2 - bf16_bits_to_f32(h23 & 0xFFFFu), q3 - bf16_bits_to_f32(h23 >> 16));
+      // the LDS copy carries tau * log2(e): scores, routing scores and shared
+      // logits then come out of the products in the base-2 softmax domain
+      const float s0 = q0 * kLogitScale, s1 = q1 * kLogitScale;
+      const float s2 = q2 * kLogitScale, s3 = q3 * kLogitScale;
+      const uint32_t h01 = pk_bf16(s0, s1), h23 = pk_bf16(s2, s3);
+      const uint32_t l01 = pk_bf16(s0 - bf16_bits_to_f32(h01 & 0xFFFFu), s1 - bf16_bits_to_f32(h01 >> 16));
+      const uint32_t l23 = pk_bf16(s2 - bf16_bits_to_f32(h23 & 0xFFFFu), s3 - bf16_bits_to_f32(h23 >> 16));
       const int off = rc(L, 2 * ct + (g >> 1)) + (g & 1) * 8;
       *lds<u32x2>(sm, OFF_QLH + off) = u32x2{h01, h23};
       *lds<u32x2>(sm, OFF_QLL + off) = u32x2{l01, l23};
@@ -405,8 +413,8 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
             }
             // lane holds S^T[key kb + r][landmark 16lt + c16]
             *lds<float4>(sm, OFF_X + ((16 * lt + c16) * S_STRIDE + kb) * 4) =
-                make_float4(kb < N ? c[0] * tau : -INFINITY, kb + 1 < N ? c[1] * tau : -INFINITY,
-                            kb + 2 < N ? c[2] * tau : -INFINITY, kb + 3 < N ? c[3] * tau : -INFINITY);
+                make_float4(kb < N ? c[0] : -INFINITY, kb + 1 < N ? c[1] : -INFINITY,
+                            kb + 2 < N ? c[2] : -INFINITY, kb + 3 < N ? c[3] : -INFINITY);
           }
         }
       }
@@ -547,10 +555,10 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
         // padded width, and its sum (of the rounded values the products use)
         float sum = 0.f;
         uint16_t* prow = reinterpret_cast<uint16_t*>(hrow);
-        const float moff = active ? -rmax * 1.4426950408889634f : 0.f;
+        const float moff = active ? -rmax : 0.f;  // scores are in the base-2 domain
 #pragma unroll
         for (int u = 0; u < MAXNT; ++u) {
-          const uint32_t hb = f16_bits(__builtin_amdgcn_exp2f(__builtin_fmaf(v[u], 1.4426950408889634f, moff)));
+          const uint32_t hb = f16_bits(__builtin_amdgcn_exp2f(v[u] + moff));
           sum += f16_bits_to_f32(hb);
           prow[key0 + u] = (uint16_t)hb;
         }
@@ -601,6 +609,7 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
         }
         if (g == 0 && tok < N) {
           *lds<int>(sm, OFF_ROUTE + tok * 4) = bi;
+          atomicOr(lds<uint32_t>(sm, OFF_BM + (bi * 8 + (tok >> 5)) * 4), 1u << (tok & 31));
           if (EXTRAS && o.route) o.route[(size_t)bh * N + tok] = bi;
         }
       }
@@ -615,66 +624,51 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
         o.idx[(size_t)bh * m * k + q] = *lds<int>(sm, OFF_IDX + ((q / k) * KMAX + q % k) * 4);
     }
 
-    // ---------------- F: group queries by route (stable counting sort), tile list
+    // ---------------- F: group the queries by route (stable): expert counts and
+    // offsets from the route bitmaps, then each query's place in PERM
     {
       FUSED_IDS;
-      const int nchunks = (N + 63) >> 6;
-      int myroute = -1, myrank = 0;
-      if (w < nchunks) {
-        const int n = 64 * w + lane;
-        myroute = n < N ? *lds<int>(sm, OFF_ROUTE + n * 4) : -1;
-        int mycnt = 0;
-        for (int e = 0; e < m; ++e) {
-          const uint64_t b = __ballot(myroute == e);
-          if (myroute == e) myrank = __popcll(b & ((1ull << lane) - 1ull));
-          if (lane == e) mycnt = __popcll(b);
-        }
-        if (lane < 32) *lds<int>(sm, OFF_CNT + (w * 32 + lane) * 4) = lane < m ? mycnt : 0;
-      }
-      __syncthreads();
       if (w == 0) {
-        int tot = 0, pre[4] = {0, 0, 0, 0};
-        if (lane < 32) {
-  #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            pre[c] = tot;
-            if (c < nchunks) tot += *lds<int>(sm, OFF_CNT + (c * 32 + lane) * 4);
-          }
+        int cnt = 0;
+        if (lane < m) {
+          const u32x4 b0 = *lds<u32x4>(sm, OFF_BM + lane * 32);
+          const u32x4 b1 = *lds<u32x4>(sm, OFF_BM + lane * 32 + 16);
+          cnt = __popc(b0[0]) + __popc(b0[1]) + __popc(b0[2]) + __popc(b0[3]) + __popc(b1[0]) +
+                __popc(b1[1]) + __popc(b1[2]) + __popc(b1[3]);
         }
-        // exclusive scans over the 32 expert lanes: query offsets and tile offsets
-        const int ntl = (tot + 15) >> 4;
-        int s1 = tot, s2 = ntl;
-  #pragma unroll
-        for (int off = 1; off < 32; off <<= 1) {
-          const int x1 = __shfl_up(s1, off, 64), x2 = __shfl_up(s2, off, 64);
-          if (lane >= off) { s1 += x1; s2 += x2; }
+        int incl = cnt;  // inclusive scan over the wave (lanes past m hold 0)
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const int x = __shfl_up(incl, off, 64);
+          if (lane >= off) incl += x;
         }
-        const int off_e = s1 - tot, toff = s2 - ntl;
-        if (lane < 32) {
-  #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (c < nchunks) *lds<int>(sm, OFF_BASE + (c * 32 + lane) * 4) = off_e + pre[c];
-          if (lane < m) {
-            *lds<int>(sm, OFF_OFFS + lane * 4) = off_e;
-            for (int s = 0; s < ntl; ++s) {
-              int4* tl = lds<int4>(sm, OFF_TILES + (toff + s) * 16);
-              *tl = make_int4(lane, off_e + 16 * s, min(16, tot - 16 * s), 0);
-            }
-            if (EXTRAS && o.counts) o.counts[(size_t)bh * m + lane] = tot;
-            if (EXTRAS && o.offsets) o.offsets[(size_t)bh * (m + 1) + lane] = off_e;
-          }
+        const int off_e = incl - cnt;  // lane m holds N
+        if (lane <= m) *lds<int>(sm, OFF_OFFS + lane * 4) = off_e;
+        const uint64_t ne = __ballot(cnt > 0);
+        if (lane == 0) *lds<uint32_t>(sm, OFF_STAT + 64 * 4) = (uint32_t)ne;
+        if (EXTRAS && lane < m) {
+          if (o.counts) o.counts[(size_t)bh * m + lane] = cnt;
+          if (o.offsets) o.offsets[(size_t)bh * (m + 1) + lane] = off_e;
         }
-        const int ntiles = __shfl(s2, 31, 64);
-        if (lane == 0) {
-          *lds<int>(sm, OFF_STAT + 64 * 4) = ntiles;
-          if (EXTRAS && o.offsets) o.offsets[(size_t)bh * (m + 1) + m] = N;
-        }
+        if (EXTRAS && lane == m && o.offsets) o.offsets[(size_t)bh * (m + 1) + m] = N;
       }
       __syncthreads();
-      if (w < nchunks && myroute >= 0) {
-        const int pos = *lds<int>(sm, OFF_BASE + (w * 32 + myroute) * 4) + myrank;
-        *lds<int>(sm, OFF_PERM + pos * 4) = 64 * w + lane;
-        if (EXTRAS && o.perm) o.perm[(size_t)bh * N + pos] = 64 * w + lane;
+      if (tid < N) {
+        // rank among the expert's queries = its bitmap bits below tid
+        const int e = *lds<int>(sm, OFF_ROUTE + tid * 4);
+        const u32x4 b0 = *lds<u32x4>(sm, OFF_BM + e * 32);
+        const u32x4 b1 = *lds<u32x4>(sm, OFF_BM + e * 32 + 16);
+        const uint32_t bw[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        const int word = tid >> 5;
+        int rank = 0;
+#pragma unroll
+        for (int q = 0; q < 7; ++q) {
+          const uint32_t part = q < word ? bw[q] : (q == word ? bw[q] & ((1u << (tid & 31)) - 1u) : 0u);
+          rank += __popc(part);
+        }
+        const int pos = *lds<int>(sm, OFF_OFFS + e * 4) + rank;
+        *lds<int>(sm, OFF_PERM + pos * 4) = tid;
+        if (EXTRAS && o.perm) o.perm[(size_t)bh * N + pos] = tid;
       }
       __syncthreads();
     }
@@ -685,6 +679,15 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
       store_vt(vr, sm, tid);
     }
     __syncthreads();
+
+    // the K rows for the expert tiles' LDS copy fly while V_L is formed
+    constexpr int KITEMS = (NP * 8 + THREADS - 1) / THREADS;
+    u32x4 kst[KITEMS];
+#pragma unroll
+    for (int i = 0; i < KITEMS; ++i) {
+      const int id = tid + THREADS * i, row = id >> 3;
+      kst[i] = ld16(rK, row < N ? row * 128 + 16 * (id & 7) : PAST);
+    }
 
     // ---------------- E: V_L^T = V^T P^T (16-channel x 16-landmark tiles)
     {
@@ -715,93 +718,91 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
       }
 
     }
-    __syncthreads();
-
-    // ---------------- G: grouped expert attention, one <=16-query tile at a time
+    __syncthreads();  // the P rows are spent
     {
       FUSED_IDS;
-      // Q_L (hi, lo) and V_L^T fragments are re-read from LDS by every tile
-      // rather than held in registers across the loop
+#pragma unroll
+      for (int i = 0; i < KITEMS; ++i) {
+        const int id = tid + THREADS * i, row = id >> 3;
+        if (row < NP) *lds<u32x4>(sm, OFF_H + rc(row, id & 7)) = kst[i];
+      }
+    }
+    __syncthreads();
+
+    // ---------------- G: grouped expert attention over 16-query tiles of the
+    // sorted order; a tile spans the experts of its queries, each column
+    // taking the routed half of its own expert
+    {
+      FUSED_IDS;
       // (the last head re-reads its own rows, which are in cache, so that the
       // registers are written on every path)
       load_v(qr, head_rows(bh + (int)gridDim.x < BH ? Qh + (size_t)gridDim.x * head_elems : Qh, N), N, tid);
-      const int ntiles = *lds<int>(sm, OFF_STAT + 64 * 4);
+      const uint32_t nonempty =
+          __builtin_amdgcn_readfirstlane(*lds<uint32_t>(sm, OFF_STAT + 64 * 4));
+      const int nqt = (N + 15) >> 4;
       float* outh = o.out + (size_t)bh * N * 64;
-      // A tile's gathered operands: the expert's key rows for this lane's two
-      // slot tiles and the query row of lane column c16 (columns past the
-      // tile's length compute on query 0 and are never stored).
-      struct TileIn {
-        int e, qi;
-        bool live;
-        u32x4 ak[2][2], bq0, bq1;
-      };
-      auto fetch = [&](int tile, TileIn& ti) {
-        const int4 tl = *lds<int4>(sm, OFF_TILES + tile * 16);
-        ti.e = tl.x;
-        const int q = c16 < tl.z ? *lds<int>(sm, OFF_PERM + (tl.y + c16) * 4) : -1;
-        ti.live = (unsigned)q < (unsigned)N;  // (also guards the output store)
-        ti.qi = ti.live ? q : 0;
-        const int* idxe = lds<int>(sm, OFF_IDX + ti.e * KMAX * 4);
+      // expert e's key rows for this lane's two slot tiles, from the LDS copy
+      // (slots past k read row 0: their logits are masked)
+      auto load_k = [&](int e, u32x4 (&ak)[2][2]) {
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           const int slot = 16 * st + c16;
-          const int off = slot < k ? idxe[slot] * 128 + 16 * g : PAST;
-          ti.ak[st][0] = ld16(rK, off);
-          ti.ak[st][1] = ld16(rK, off + 64);
+          const int key = slot < k ? *lds<int>(sm, OFF_IDX + (e * KMAX + slot) * 4) : 0;
+          ak[st][0] = *lds<u32x4>(sm, OFF_H + rc(key, g));
+          ak[st][1] = *lds<u32x4>(sm, OFF_H + rc(key, g + 4));
         }
-        ti.bq0 = ld16(rQ, ti.qi * 128 + 16 * g);
-        ti.bq1 = ld16(rQ, ti.qi * 128 + 16 * g + 64);
       };
-      // the previous tile's output rows, stored once the next loads have landed
-      // (one counter tracks loads and stores: stores issued ahead of a load
-      // would make its wait cover them too)
-      f32x4 pend[4];
-      int pqi = 0;
-      bool plive = false;
-      TileIn cur;
-      if (w < ntiles) fetch(w, cur);
-      for (int tile = w; tile < ntiles; tile += NWAVES) {
-        asm volatile("" ::"v"(cur.bq0), "v"(cur.bq1), "v"(cur.ak[0][0]), "v"(cur.ak[0][1]),
-                     "v"(cur.ak[1][0]), "v"(cur.ak[1][1]));
-        if (plive) {
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
-            *reinterpret_cast<f32x4*>(outh + (size_t)pqi * 64 + 16 * ct + 4 * g) = pend[ct];
-        }
-
-        const int e = cur.e;
-        // shared logits^T = Q_L Q_g^T (hi + lo) and routed logits^T = K_e Q_g^T
-        u32x4 qlh[2][2], qll[2][2];
-        load_ql(sm, qlh, qll, g, c16);
-        f32x4 ls[2], lr[2];
-#pragma unroll
-        for (int lt = 0; lt < 2; ++lt) {
-          f32x4 c = zero4();
-          c = mfma_bf16(qlh[lt][0], cur.bq0, c);
-          c = mfma_bf16(qll[lt][0], cur.bq0, c);
-          c = mfma_bf16(qlh[lt][1], cur.bq1, c);
-          c = mfma_bf16(qll[lt][1], cur.bq1, c);
-          ls[lt] = c;
-        }
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          f32x4 c = zero4();
-          c = mfma_bf16(cur.ak[st][0], cur.bq0, c);
-          c = mfma_bf16(cur.ak[st][1], cur.bq1, c);
-          lr[st] = c;
-        }
-        // the gathered operands are consumed: the next tile's loads reuse
-        // their registers and fly while this tile's softmax and products run
-        const int qi = cur.qi;
-        const bool live = cur.live;
-        if (tile + NWAVES < ntiles) fetch(tile + NWAVES, cur);
+      for (int tile = w; tile < nqt; tile += NWAVES) {
+        const int p0 = 16 * tile, p = p0 + c16;
+        const bool live = p < N;  // columns past N compute on the tile's first query
+        const int qi = *lds<int>(sm, OFF_PERM + (live ? p : p0) * 4);
+        const int ce = *lds<int>(sm, OFF_ROUTE + qi * 4);
+        const int e_lo = __builtin_amdgcn_readfirstlane(
+            *lds<int>(sm, OFF_ROUTE + *lds<int>(sm, OFF_PERM + p0 * 4) * 4));
+        const int e_hi = __builtin_amdgcn_readfirstlane(
+            *lds<int>(sm, OFF_ROUTE + *lds<int>(sm, OFF_PERM + min(p0 + 15, N - 1) * 4) * 4));
+        // the tile's experts: the non-empty ones in [e_lo, e_hi] (sorted order)
+        const uint32_t blocks = nonempty & ((e_hi >= 31 ? ~0u : (2u << e_hi) - 1u) & ~((1u << e_lo) - 1u));
+        const u32x4 bq0 = ld16(rQ, qi * 128 + 16 * g);
+        const u32x4 bq1 = ld16(rQ, qi * 128 + 16 * g + 64);
+        u32x4 ak[2][2];
+        // shared logits^T = Q_L Q_g^T (hi + lo; Q_L carries the log2-domain scale)
         float x[16];
+        {
+          u32x4 qlh[2][2], qll[2][2];
+          load_ql(sm, qlh, qll, g, c16);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          x[r] = 4 * g + r < m ? ls[0][r] * kLogitScale : -INFINITY;
-          x[4 + r] = 16 + 4 * g + r < m ? ls[1][r] * kLogitScale : -INFINITY;
-          x[8 + r] = 4 * g + r < k ? lr[0][r] * kLogitScale : -INFINITY;
-          x[12 + r] = 16 + 4 * g + r < k ? lr[1][r] * kLogitScale : -INFINITY;
+          for (int lt = 0; lt < 2; ++lt) {
+            f32x4 c = zero4();
+            c = mfma_bf16(qlh[lt][0], bq0, c);
+            c = mfma_bf16(qll[lt][0], bq0, c);
+            c = mfma_bf16(qlh[lt][1], bq1, c);
+            c = mfma_bf16(qll[lt][1], bq1, c);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) x[4 * lt + r] = 16 * lt + 4 * g + r < m ? c[r] : -INFINITY;
+          }
+        }
+        // routed logits^T = K_e Q_g^T per expert, kept for the expert's columns
+#pragma unroll
+        for (int q = 8; q < 16; ++q) x[q] = -INFINITY;
+        for (uint32_t bl = blocks; bl != 0;) {
+          const int e = __builtin_ctz(bl);
+          bl &= bl - 1u;
+          load_k(e, ak);
+          f32x4 lr[2];
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            f32x4 c = zero4();
+            c = mfma_bf16(ak[st][0], bq0, c);
+            c = mfma_bf16(ak[st][1], bq1, c);
+            lr[st] = c;
+          }
+          const bool mine = ce == e;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            x[8 + r] = mine ? (4 * g + r < k ? lr[0][r] * kLogitScale : -INFINITY) : x[8 + r];
+            x[12 + r] = mine ? (16 + 4 * g + r < k ? lr[1][r] * kLogitScale : -INFINITY) : x[12 + r];
+          }
         }
         float mx = x[0];
 #pragma unroll
@@ -823,38 +824,45 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
         f32x4 tot = mfma_f16(ones, bps, zero4());
         tot = mfma_f16(ones, bpr, tot);
         const float inv = __builtin_amdgcn_rcpf(tot[0]);
-        // key ids of this lane's routed slots {4g..4g+3, 16+4g..16+4g+3}
-        const i32x4 kv0 = *lds<i32x4>(sm, OFF_IDX + (e * KMAX + 4 * g) * 4);
-        const i32x4 kv1 = *lds<i32x4>(sm, OFF_IDX + (e * KMAX + 16 + 4 * g) * 4);
-        int keys[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          keys[r] = 4 * g + r < k ? kv0[r] : 0;
-          keys[4 + r] = 16 + 4 * g + r < k ? kv1[r] : 0;
-        }
+        // out^T = V_L^T P_s^T + sum over the tile's experts of V_e^T P_r^T
+        // (P_r^T columns of other experts zeroed)
+        f32x4 acc[4];
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
           // V_L^T[ch 16ct + c16][landmarks 4g..4g+3, 16+4g..16+4g+3]
           const int rowb = OFF_VLT + (16 * ct + c16) * VLT_STRIDE;
           const u32x2 lo2 = *lds<u32x2>(sm, rowb + (4 * g) * 2);
           const u32x2 hi2 = *lds<u32x2>(sm, rowb + (16 + 4 * g) * 2);
-          const u32x4 avl = {lo2[0], lo2[1], hi2[0], hi2[1]};
-          const uint16_t* vrow =
-              reinterpret_cast<const uint16_t*>(sm + OFF_X + (16 * ct + c16) * VT_STRIDE);
-          const u32x4 ave = {pack2(vrow[keys[0]], vrow[keys[1]]), pack2(vrow[keys[2]], vrow[keys[3]]),
-                             pack2(vrow[keys[4]], vrow[keys[5]]), pack2(vrow[keys[6]], vrow[keys[7]])};
-          f32x4 acc = zero4();
-          acc = mfma_f16(avl, bps, acc);
-          acc = mfma_f16(ave, bpr, acc);
-          pend[ct] = acc * inv;
+          acc[ct] = mfma_f16(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, bps, zero4());
         }
-        pqi = qi;
-        plive = live;
-      }
-      if (plive) {
+        for (uint32_t bl = blocks; bl != 0;) {
+          const int e = __builtin_ctz(bl);
+          bl &= bl - 1u;
+          const bool mine = ce == e;
+          const u32x4 bpe = {mine ? bpr[0] : 0u, mine ? bpr[1] : 0u, mine ? bpr[2] : 0u, mine ? bpr[3] : 0u};
+          // key ids of this lane's routed slots {4g..4g+3, 16+4g..16+4g+3}
+          const i32x4 kv0 = *lds<i32x4>(sm, OFF_IDX + (e * KMAX + 4 * g) * 4);
+          const i32x4 kv1 = *lds<i32x4>(sm, OFF_IDX + (e * KMAX + 16 + 4 * g) * 4);
+          int keys[8];
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-          *reinterpret_cast<f32x4*>(outh + (size_t)pqi * 64 + 16 * ct + 4 * g) = pend[ct];
+          for (int r = 0; r < 4; ++r) {
+            keys[r] = 4 * g + r < k ? kv0[r] : 0;
+            keys[4 + r] = 16 + 4 * g + r < k ? kv1[r] : 0;
+          }
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            const uint16_t* vrow =
+                reinterpret_cast<const uint16_t*>(sm + OFF_X + (16 * ct + c16) * VT_STRIDE);
+            const u32x4 ave = {pack2(vrow[keys[0]], vrow[keys[1]]), pack2(vrow[keys[2]], vrow[keys[3]]),
+                               pack2(vrow[keys[4]], vrow[keys[5]]), pack2(vrow[keys[6]], vrow[keys[7]])};
+            acc[ct] = mfma_f16(ave, bpe, acc[ct]);
+          }
+        }
+        if (live) {
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+            *reinterpret_cast<f32x4*>(outh + (size_t)qi * 64 + 16 * ct + 4 * g) = acc[ct] * inv;
+        }
       }
     }
   }
