@@ -303,6 +303,8 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
   const u32x4 z = {0u, 0u, 0u, 0u};
   static_assert(NWAVES == 8, "pooling: one 16-channel x 16-landmark tile per wave");
 
+  // expert key slots past k stay 0 for every head (top-k fills slots < k)
+  for (int q = threadIdx.x; q < MMAX * KMAX; q += THREADS) *lds<int>(sm, OFF_IDX + q * 4) = 0;
   // which landmark windows hold each token (the same for every head)
   for (int tok = threadIdx.x; tok < KPMAX; tok += THREADS) {
     uint32_t bits = 0;
@@ -742,16 +744,20 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
       const int nqt = (N + 15) >> 4;
       float* outh = o.out + (size_t)bh * N * 64;
       // expert e's key rows for this lane's two slot tiles, from the LDS copy
-      // (slots past k read row 0: their logits are masked)
+      // (slots past k hold key 0: their logits are masked)
       auto load_k = [&](int e, u32x4 (&ak)[2][2]) {
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          const int slot = 16 * st + c16;
-          const int key = slot < k ? *lds<int>(sm, OFF_IDX + (e * KMAX + slot) * 4) : 0;
+          const int key = *lds<int>(sm, OFF_IDX + (e * KMAX + 16 * st + c16) * 4);
           ak[st][0] = *lds<u32x4>(sm, OFF_H + rc(key, g));
           ak[st][1] = *lds<u32x4>(sm, OFF_H + rc(key, g + 4));
         }
       };
+      // lane masks of this lane's valid routed slots {4g+r, 16+4g+r}
+      uint32_t slot_ok = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        slot_ok |= (4 * g + r < k ? 1u : 0u) << r | (16 + 4 * g + r < k ? 1u : 0u) << (4 + r);
       for (int tile = w; tile < nqt; tile += NWAVES) {
         const int p0 = 16 * tile, p = p0 + c16;
         const bool live = p < N;  // columns past N compute on the tile's first query
@@ -797,11 +803,16 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
             c = mfma_bf16(ak[st][1], bq1, c);
             lr[st] = c;
           }
-          const bool mine = ce == e;
+          // the expert's columns take its valid slots' logits (bit selects;
+          // the other slots stay -inf)
+          const uint32_t take = ce == e ? slot_ok : 0u;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            x[8 + r] = mine ? (4 * g + r < k ? lr[0][r] * kLogitScale : -INFINITY) : x[8 + r];
-            x[12 + r] = mine ? (16 + 4 * g + r < k ? lr[1][r] * kLogitScale : -INFINITY) : x[12 + r];
+            const uint32_t m0 = 0u - (take >> r & 1u), m1 = 0u - (take >> (4 + r) & 1u);
+            x[8 + r] = __uint_as_float((__float_as_uint(lr[0][r] * kLogitScale) & m0) |
+                                       (__float_as_uint(x[8 + r]) & ~m0));
+            x[12 + r] = __uint_as_float((__float_as_uint(lr[1][r] * kLogitScale) & m1) |
+                                        (__float_as_uint(x[12 + r]) & ~m1));
           }
         }
         float mx = x[0];
@@ -841,21 +852,24 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
           const bool mine = ce == e;
           const u32x4 bpe = {mine ? bpr[0] : 0u, mine ? bpr[1] : 0u, mine ? bpr[2] : 0u, mine ? bpr[3] : 0u};
           // key ids of this lane's routed slots {4g..4g+3, 16+4g..16+4g+3}
+          // (slots past k hold key 0, weighted 0)
           const i32x4 kv0 = *lds<i32x4>(sm, OFF_IDX + (e * KMAX + 4 * g) * 4);
           const i32x4 kv1 = *lds<i32x4>(sm, OFF_IDX + (e * KMAX + 16 + 4 * g) * 4);
-          int keys[8];
+          // V_e^T gathered from V^T rows 16ct + c16: one address per key, the
+          // channel tile in the instruction offset, halves loaded in place
+          const _Float16* vk[8];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            keys[r] = 4 * g + r < k ? kv0[r] : 0;
-            keys[4 + r] = 16 + 4 * g + r < k ? kv1[r] : 0;
+            vk[r] = reinterpret_cast<const _Float16*>(sm + OFF_X + c16 * VT_STRIDE + 2 * kv0[r]);
+            vk[4 + r] = reinterpret_cast<const _Float16*>(sm + OFF_X + c16 * VT_STRIDE + 2 * kv1[r]);
           }
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct) {
-            const uint16_t* vrow =
-                reinterpret_cast<const uint16_t*>(sm + OFF_X + (16 * ct + c16) * VT_STRIDE);
-            const u32x4 ave = {pack2(vrow[keys[0]], vrow[keys[1]]), pack2(vrow[keys[2]], vrow[keys[3]]),
-                               pack2(vrow[keys[4]], vrow[keys[5]]), pack2(vrow[keys[6]], vrow[keys[7]])};
-            acc[ct] = mfma_f16(ave, bpe, acc[ct]);
+            constexpr int CT = 16 * VT_STRIDE / 2;  // halves per channel tile
+            f16x8_t ave;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) ave[q] = vk[q][CT * ct];
+            acc[ct] = mfma_f16(__builtin_bit_cast(u32x4, ave), bpe, acc[ct]);
           }
         }
         if (live) {
