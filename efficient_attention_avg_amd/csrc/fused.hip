@@ -522,20 +522,38 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
           take |= bnd;
           need = 0;
         }
-        for (; __ballot(need > 0) != 0; --need) {
-          float bv = -INFINITY;
-          int bk = 0x7FFFFFFF;
+        if (__ballot(need > 0) != 0) {
+          // each lane's best boundary candidate (descending scan: ties keep the
+          // lower key); a lane rescans only after its candidate is taken and
+          // it holds more
+          auto best_of = [&](float& bv, int& bk) {
+            bv = -INFINITY;
+            bk = 0x7FFFFFFF;
 #pragma unroll
-          for (int u = MAXNT - 1; u >= 0; --u) {  // descending: ties keep the lower key
-            const bool c = (bnd >> u & 1u) && v[u] >= bv;
-            bv = c ? v[u] : bv;
-            bk = c ? key0 + u : bk;
-          }
-          g16_argmax_key(bv, bk);
-          if (need > 0 && bk - key0 >= 0 && bk - key0 < MAXNT) {
-            const int u = bk - key0;
-            take |= 1u << u;
-            bnd &= ~(1u << u);
+            for (int u = MAXNT - 1; u >= 0; --u) {
+              const bool c = (bnd >> u & 1u) && v[u] >= bv;
+              bv = c ? v[u] : bv;
+              bk = c ? key0 + u : bk;
+            }
+          };
+          float bv;
+          int bk;
+          best_of(bv, bk);
+          for (; __ballot(need > 0) != 0; --need) {
+            float wv = bv;
+            int wk = bk;
+            g16_argmax_key(wv, wk);
+            const bool win = need > 0 && wk == bk && bk != 0x7FFFFFFF;
+            if (win) {
+              const int u = bk - key0;
+              take |= 1u << u;
+              bnd &= ~(1u << u);
+              bv = -INFINITY;
+              bk = 0x7FFFFFFF;
+            }
+            if (__ballot(win && bnd != 0) != 0) {
+              if (win && bnd != 0) best_of(bv, bk);
+            }
           }
         }
         // the expert: kept key ids in ascending order (lane-major, since each
