@@ -219,18 +219,6 @@ __device__ __forceinline__ void load_ql(char* sm, u32x4 (&qlh)[2][2], u32x4 (&ql
     }
 }
 
-// A head's [N][64] bf16 rows as a raw buffer: 32-bit byte offsets, and an
-// offset past the head's bytes reads zeros (the buffer range check), which
-// stands in for padding rows without a branch or a select on the data.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-constexpr int PAST = 0x40000000;
-__device__ __forceinline__ Rsrc head_rows(const uint16_t* base, int N) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, N * 128, 0x00020000);
-}
-__device__ __forceinline__ u32x4 ld16(Rsrc r, int off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
 // The head's V rows for the transposed copy: key pairs (2p, 2p+1) of 8-channel
 // chunk c, items tid + THREADS i (c = item / 112, p = item % 112).
 struct VRows {

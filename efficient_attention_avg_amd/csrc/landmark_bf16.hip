@@ -67,7 +67,8 @@ struct RowState {
 constexpr int OFF_HIST = 0;
 constexpr int OFF_ROW = OFF_HIST + ROWS * HIST_STRIDE;
 constexpr int OFF_FLAG = OFF_ROW + ROWS * (int)sizeof(RowState);
-constexpr int OFF_UNION = (OFF_FLAG + 16 + 15) & ~15;
+constexpr int OFF_QL = (OFF_FLAG + 16 + 15) & ~15;  // Q_L B operands: [tl][ks][hi, lo][lane] x 16 B
+constexpr int OFF_UNION = OFF_QL + TL * 2 * 2 * 64 * 16;
 constexpr int VALUES_BYTES = NW * VT_BYTES;  // phase V staging (the merge area aliases it)
 static_assert(NW * ROWS * MERGE_STRIDE * 4 <= VALUES_BYTES, "merge area fits in the staging");
 static_assert(BITMAP_MAX_N / 8 <= HIST_STRIDE && LIST_MAX * 8 <= HIST_STRIDE, "row space");
@@ -88,37 +89,38 @@ __host__ __device__ constexpr size_t lds_bytes(int cap) {
 }
 
 // A operands of one 64-key block: lane (g, c16) holds key 16kt + c16,
-// channels 8g.. (k-step 0) and 32 + 8g.. (k-step 1).  Keys past N read key
-// N-1 (their scores are masked).
+// channels 8g.. (k-step 0) and 32 + 8g.. (k-step 1).  Keys past N read zeros
+// (their scores are masked).
 struct KRegs {
   u32x4 a[4][2];
 };
 
-__device__ __forceinline__ void load_k(KRegs& kr, const uint16_t* Kh, int blk, int N, int g,
-                                       int c16) {
+__device__ __forceinline__ void load_k(KRegs& kr, Rsrc Kh, int blk, int N, int g, int c16) {
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
-    const uint16_t* p = Kh + (size_t)min(blk * KB + 16 * kt + c16, N - 1) * 64;
-    kr.a[kt][0] = *reinterpret_cast<const u32x4*>(p + 8 * g);
-    kr.a[kt][1] = *reinterpret_cast<const u32x4*>(p + 32 + 8 * g);
+    const int key = blk * KB + 16 * kt + c16;
+    const int off = key < N ? key * 128 + 16 * g : PAST;
+    kr.a[kt][0] = ld16(Kh, off);
+    kr.a[kt][1] = ld16(Kh, off + 64);
   }
 }
 
 // V block for the transposed LDS copy: lane holds keys 4p..4p+3 of chunk c
 // (8 channels) for items it = lane, lane + 64 (p = it >> 3, c = it & 7).
-// Keys past N read key N-1 (finite; their weights are 0).
+// Keys past N read zeros (their weights are 0).
 struct VRegs {
   u32x4 v[2][4];
 };
 
-__device__ __forceinline__ void load_v(VRegs& vr, const uint16_t* Vh, int blk, int N, int lane) {
+__device__ __forceinline__ void load_v(VRegs& vr, Rsrc Vh, int blk, int N, int lane) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int it = lane + 64 * j, p = it >> 3, c = it & 7;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      vr.v[j][i] = *reinterpret_cast<const u32x4*>(
-          Vh + (size_t)min(blk * KB + 4 * p + i, N - 1) * 64 + 8 * c);
+    for (int i = 0; i < 4; ++i) {
+      const int key = blk * KB + 4 * p + i;
+      vr.v[j][i] = ld16(Vh, key < N ? key * 128 + 16 * c : PAST);
+    }
   }
 }
 
@@ -162,11 +164,28 @@ __device__ __forceinline__ void load_ql_b(const float* ql, int bh, int m, int ro
   }
 }
 
+// This lane's Q_L B operands of tile tl, kept in LDS (each lane its own
+// 16-byte slots) rather than in registers across the passes.
+__device__ __forceinline__ void ql_slot_store(char* sm, int tl, int lane, const u32x4 (&bqh)[2],
+                                              const u32x4 (&bql)[2]) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    *reinterpret_cast<u32x4*>(sm + OFF_QL + (((tl * 2 + ks) * 2 + 0) * 64 + lane) * 16) = bqh[ks];
+    *reinterpret_cast<u32x4*>(sm + OFF_QL + (((tl * 2 + ks) * 2 + 1) * 64 + lane) * 16) = bql[ks];
+  }
+}
+
 // Raw scores of one block: lane holds key 64blk + 16kt + 4g + r of row c16.
 // Every phase computes them with this same sequence, so a score is
 // bit-identical wherever it is recomputed.
-__device__ __forceinline__ void block_scores(const KRegs& kr, const u32x4 (&bqh)[2],
-                                             const u32x4 (&bql)[2], float (&s)[4][4]) {
+__device__ __forceinline__ void block_scores(const KRegs& kr, const char* sm, int tl, int lane,
+                                             float (&s)[4][4]) {
+  u32x4 bqh[2], bql[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    bqh[ks] = *reinterpret_cast<const u32x4*>(sm + OFF_QL + (((tl * 2 + ks) * 2 + 0) * 64 + lane) * 16);
+    bql[ks] = *reinterpret_cast<const u32x4*>(sm + OFF_QL + (((tl * 2 + ks) * 2 + 1) * 64 + lane) * 16);
+  }
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
     f32x4 c = zero4();
@@ -399,8 +418,8 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
   if (bh >= a.BH) return;
   const int N = a.N, nblk = (N + KB - 1) / KB;
   const bool ragged = (N % KB) != 0;  // the last block has keys past N
-  const uint16_t* Kh = a.K + (size_t)bh * N * 64;
-  const uint16_t* Vh = a.V + (size_t)bh * N * 64;
+  const Rsrc Kh = head_rows(a.K + (size_t)bh * N * 64, N);
+  const Rsrc Vh = head_rows(a.V + (size_t)bh * N * 64, N);
   RowState* rows = reinterpret_cast<RowState*>(sm + OFF_ROW);
   int* flag = reinterpret_cast<int*>(sm + OFF_FLAG);
 
@@ -410,10 +429,13 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
 
   // this lane's rows: 16 * tl + c16 of the workgroup's rows (column c16 of
   // tile tl of S^T)
-  u32x4 bqh[TL][2], bql[TL][2];
+  // (every wave writes the same values into the same slots)
 #pragma unroll
-  for (int tl = 0; tl < TL; ++tl)
-    load_ql_b(a.ql, bh, a.m, row0 + 16 * tl + c16, g, bqh[tl], bql[tl]);
+  for (int tl = 0; tl < TL; ++tl) {
+    u32x4 bqh[2], bql[2];
+    load_ql_b(a.ql, bh, a.m, row0 + 16 * tl + c16, g, bqh, bql);
+    ql_slot_store(sm, tl, lane, bqh, bql);
+  }
 
   // ------------------------------------------------------------ V: values
   {
@@ -447,7 +469,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
 #pragma unroll
       for (int tl = 0; tl < TL; ++tl) {
         float s[4][4];
-        block_scores(kr, bqh[tl], bql[tl], s);
+        block_scores(kr, sm, tl, lane, s);
         if (tl == TL - 1 && blk + NW < nblk) load_k(kr, Kh, blk + NW, N, g, c16);
         if (last) {
 #pragma unroll
@@ -595,7 +617,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
 #pragma unroll
       for (int tl = 0; tl < TL; ++tl) {
         float s[4][4];
-        block_scores(kr, bqh[tl], bql[tl], s);
+        block_scores(kr, sm, tl, lane, s);
         if (tl == TL - 1 && blk + NW < nblk) load_k(kr, Kh, blk + NW, N, g, c16);
         uint32_t* myhist =
             reinterpret_cast<uint32_t*>(sm + OFF_HIST + (16 * tl + c16) * HIST_STRIDE);
@@ -723,7 +745,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
 #pragma unroll
         for (int tl = 0; tl < TL; ++tl) {
           float s[4][4];
-          block_scores(kr, bqh[tl], bql[tl], s);
+          block_scores(kr, sm, tl, lane, s);
           if (tl == TL - 1 && blk + NW < nblk) load_k(kr, Kh, blk + NW, N, g, c16);
           collect(s, tl, blk, last, false, 0.f, 0);
         }
@@ -739,7 +761,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
 #pragma unroll
           for (int tl = 0; tl < TL; ++tl) {
             float s[4][4];
-            block_scores(kr, bqh[tl], bql[tl], s);
+            block_scores(kr, sm, tl, lane, s);
             const int lr = 16 * tl + c16;
             collect(s, tl, blk, last, true, rows[lr].thr, rows[lr].thrkey);
           }

@@ -67,4 +67,17 @@ __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
 // Pack two f16 bit patterns into one dword (lo in bits 0..15).
 __device__ __forceinline__ uint32_t pack2(uint32_t lo, uint32_t hi) { return lo | (hi << 16); }
 
+// A head's [N][64] bf16 rows as a raw buffer: 32-bit byte offsets, and an
+// offset past the head's bytes reads zeros (the buffer range check), which
+// stands in for padding rows without a branch or a select on the data.
+// (N * 128 stays below 2^29 for N <= 2^22, so PAST is past every head.)
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int PAST = 0x40000000;
+__device__ __forceinline__ Rsrc head_rows(const uint16_t* base, int N) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, N * 128, 0x00020000);
+}
+__device__ __forceinline__ u32x4 ld16(Rsrc r, int off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 }  // namespace mita
