@@ -10,10 +10,11 @@ of synthetic, seeded inputs already resident in device memory.  Before every
 timed step a 512 MiB buffer is read (summed) so that neither L2 nor the 256 MB
 Infinity Cache holds the inputs (the DeiT-S inputs would otherwise fit in
 it); a read leaves clean lines, so the first kernel does not share HBM with
-the write-back of a flush buffer.  The library records HIP events on its launch stream before its first
-kernel and after each kernel (mita_forward_ex's timing events): a step's time
-is first event to last, a kernel's time the interval that closes with it;
-ms_per_step is the mean step time.  A warm (no flush) figure is reported
+the write-back of a flush buffer.  The library records HIP events before its
+first kernel and after each kernel (mita_forward_ex's timing events; the staged
+schedule runs routing and grouping on a side stream beside the landmark pass):
+a step's time is first event to last, a kernel's time the interval from its
+start event to its end; ms_per_step is the mean step time.  A warm (no flush) figure is reported
 beside it unless --no-warm.
 
 Prints ONE JSON line.  ``value`` is query-heads per second (B*H*N per step)
@@ -140,8 +141,9 @@ class Runner:
         self.flush_buf = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
         self.flush_f32 = self.flush_buf.view(torch.float32)
         self.flush_sink = torch.zeros((), dtype=torch.float32, device="cuda")
-        self.kernels = mita.mita_kernel_names(w["B"], w["H"], w["grid_h"], w["grid_w"], w["d"],
+        self.sched = mita.mita_kernel_schedule(w["B"], w["H"], w["grid_h"], w["grid_w"], w["d"],
                                               w["m_h"], w["m_w"], w["k"], code, path=path)
+        self.kernels = [nm for nm, _ in self.sched]
 
     def step(self, events=None):
         self.mita.mita_forward_ex(self.q, self.k, self.v, *self.args, out=self.out,
@@ -155,10 +157,10 @@ class Runner:
 
     def timed(self, n, flush=True):
         """n steps, optionally flushing the caches before each.  The library records an event
-        on its launch stream before its first kernel and after each kernel; a step's time is
-        first event to last (the kernels and any gaps between them), each kernel's time the
-        interval that closes with it.  Returns the mean step time (ms), every step's time, and
-        each kernel's mean time (ms)."""
+        before its first kernel and after each kernel (the staged schedule's routing and
+        grouping on its side stream); a step's time is first event to last, each kernel's
+        time the interval from its start event (mita_kernel_schedule) to its own end.
+        Returns the mean step time (ms), every step's time, and each kernel's mean time (ms)."""
         torch = self.torch
         kevs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(self.kernels) + 1)]
                 for _ in range(n)]
@@ -172,8 +174,8 @@ class Runner:
             self.step(events=kev)
         torch.cuda.synchronize()
         ms = [kev[0].elapsed_time(kev[-1]) for kev in kevs]
-        per = {name: sum(kev[i].elapsed_time(kev[i + 1]) for kev in kevs) / n
-               for i, name in enumerate(self.kernels)}
+        per = {name: sum(kev[st].elapsed_time(kev[i + 1]) for kev in kevs) / n
+               for i, (name, st) in enumerate(self.sched)}
         return sum(ms) / len(ms), ms, per
 
 

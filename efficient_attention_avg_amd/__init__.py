@@ -64,7 +64,8 @@ def lib() -> ctypes.CDLL:
         L.mita_schedule.restype = I
         L.mita_schedule.argtypes = [I] * 8 + [I]
         L.mita_kernel_names.restype = I
-        L.mita_kernel_names.argtypes = [I] * 8 + [I, I, ctypes.POINTER(ctypes.c_char_p), I]
+        L.mita_kernel_names.argtypes = [I] * 8 + [I, I, ctypes.POINTER(ctypes.c_char_p),
+                                                 ctypes.POINTER(ctypes.c_int), I]
         L.mita_forward.restype = S
         L.mita_forward.argtypes = [P, P, P] + [I] * 8 + [I, P, P, P, P, Z, P]
         L.mita_forward_ex.restype = S
@@ -160,14 +161,23 @@ def mita_forward(q, k, v, grid_h, grid_w, m_h, m_w, topk, *, out=None, idx=None,
                            route=route, workspace=workspace, stream=stream)["out"]
 
 
-def mita_kernel_names(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code, path="auto") -> list:
-    """The kernels mita_forward_ex launches, in order (host only)."""
+def mita_kernel_schedule(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code, path="auto") -> list:
+    """The kernels mita_forward_ex launches, in the order of its timing events, as
+    (name, start) pairs: kernel i runs between events[start] and events[i + 1]
+    (host only)."""
     names = (ctypes.c_char_p * 8)()
+    starts = (ctypes.c_int * 8)()
     n = int(lib().mita_kernel_names(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code, PATHS[path],
-                                    names, 8))
+                                    names, starts, 8))
     if n < 0:
         _check(-n)
-    return [names[i].decode() for i in range(n)]
+    return [(names[i].decode(), int(starts[i])) for i in range(n)]
+
+
+def mita_kernel_names(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code, path="auto") -> list:
+    """The kernels mita_forward_ex launches, in the order of its timing events (host only)."""
+    return [nm for nm, _ in mita_kernel_schedule(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code,
+                                                 path)]
 
 
 def mita_forward_ex(q, k, v, grid_h, grid_w, m_h, m_w, topk, *, out=None, idx=None, route=None,
@@ -176,10 +186,11 @@ def mita_forward_ex(q, k, v, grid_h, grid_w, m_h, m_w, topk, *, out=None, idx=No
 
     ``idx`` / ``route``: a preallocated int32 tensor, True (allocate) or None.
     ``extras=True`` also returns ql, vl, counts, offsets and perm.
-    ``events``: torch.cuda.Event objects (enable_timing=True), recorded on the
-    launch stream before the first kernel and after each kernel (see
-    mita_kernel_names); each must have been recorded once already so that
-    its HIP event exists.
+    ``events``: torch.cuda.Event objects (enable_timing=True): events[0] before
+    the first kernel, events[i + 1] after the i-th kernel of
+    mita_kernel_schedule, whose start index gives the event the kernel's
+    interval opens with; each must have been recorded once already so that its
+    HIP event exists.
     """
     code, torch = _qkv(q, k, v)
     B, H, N, d = q.shape

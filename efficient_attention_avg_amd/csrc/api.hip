@@ -9,6 +9,8 @@
 #include "../../include/mita.h"
 #include "internal.h"
 
+#include <mutex>
+
 using mita::Shape;
 using mita::align_up;
 
@@ -46,6 +48,37 @@ struct Marker {
     ++i;
   }
 };
+
+// The staged schedule's side stream for routing and grouping, one per device:
+// created on first use (default priority, non-blocking), kept until the
+// process ends.  g_side_mu serialises creation and each call's fork and join.
+struct Side {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+constexpr int kMaxDevices = 64;
+Side g_side[kMaxDevices];
+bool g_side_failed[kMaxDevices];
+
+// The current device's side stream, or nullptr (routing then stays on the
+// caller's stream) if it cannot be created.  Call with g_side_mu held.
+Side* side_stream() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  Side& sd = g_side[dev];
+  if (sd.s) return &sd;
+  if (g_side_failed[dev]) return nullptr;
+  if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess ||
+      hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess) {
+    g_side_failed[dev] = true;
+    sd.s = nullptr;
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return &sd;
+}
 
 mita_status make_shape(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
                        mita_dtype dt, Shape* s) {
@@ -241,9 +274,24 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V, int B, 
   void* rscratch = (char*)workspace + L.rscratch;
 
   if ((st = run_pool(Q, ql, s, stream, &mk)) != MITA_OK) return st;
-  if ((st = run_landmark(ql, K, V, idx_p, vl, scratch, s, stream, &mk)) != MITA_OK) return st;
-  if ((st = run_route(Q, ql, route_p, counts, offsets, perm, rscratch, s, stream, &mk)) != MITA_OK)
-    return st;
+  {
+    // routing and grouping need only Q and Q_L: they run on the side stream
+    // beside the landmark pass and join before attention
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    Side* sd = side_stream();
+    hipStream_t rs = stream;
+    if (sd) {
+      if ((st = hip_status(hipEventRecord(sd->fork, stream), "fork")) != MITA_OK) return st;
+      if ((st = hip_status(hipStreamWaitEvent(sd->s, sd->fork, 0), "fork")) != MITA_OK) return st;
+      rs = sd->s;
+    }
+    if ((st = run_route(Q, ql, route_p, counts, offsets, perm, rscratch, s, rs, &mk)) != MITA_OK)
+      return st;
+    if (sd && (st = hip_status(hipEventRecord(sd->join, sd->s), "join")) != MITA_OK) return st;
+    if ((st = run_landmark(ql, K, V, idx_p, vl, scratch, s, stream, &mk)) != MITA_OK) return st;
+    if (sd && (st = hip_status(hipStreamWaitEvent(stream, sd->join, 0), "join")) != MITA_OK)
+      return st;
+  }
   if ((st = run_attend(Q, K, V, ql, vl, idx_p, route_p, offsets, perm, out, s, stream, &mk)) !=
       MITA_OK)
     return st;
@@ -251,7 +299,8 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V, int B, 
 }
 
 int mita_kernel_names(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
-                      mita_dtype in_dtype, int path, const char** names, int capacity) {
+                      mita_dtype in_dtype, int path, const char** names, int* starts,
+                      int capacity) {
   Shape s;
   const mita_status st = make_shape(B, H, grid_h, grid_w, d, m_h, m_w, k, in_dtype, &s);
   if (st != MITA_OK) return -(int)st;
@@ -261,11 +310,17 @@ int mita_kernel_names(int B, int H, int grid_h, int grid_w, int d, int m_h, int 
   if (path == MITA_PATH_FUSED && !fusable)
     return -(int)fail(MITA_ERR_UNSUPPORTED, "fused schedule not available for this shape");
   static const char* const kFused[] = {"fused"};
-  static const char* const kStaged[] = {"pool", "landmark", "route", "group", "attend"};
+  static const int kFusedStart[] = {0};
+  static const char* const kStaged[] = {"pool", "route", "group", "landmark", "attend"};
+  static const int kStagedStart[] = {0, 1, 2, 1, 4};
   const bool fused = fusable && path != MITA_PATH_STAGED;
   const char* const* list = fused ? kFused : kStaged;
+  const int* start = fused ? kFusedStart : kStagedStart;
   const int n = fused ? 1 : 5;
-  for (int i = 0; names && i < n && i < capacity; ++i) names[i] = list[i];
+  for (int i = 0; i < n && i < capacity; ++i) {
+    if (names) names[i] = list[i];
+    if (starts) starts[i] = start[i];
+  }
   ok();
   return n;
 }

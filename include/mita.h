@@ -111,8 +111,19 @@ mita_status mita_forward(const void* Q, const void* K, const void* V,
  *   perm    [B,H,N]   int32 query ids grouped by route, ascending within a group
  *   events  NULL, or n_events caller-created hipEvent_t handles: the call
  *           records events[0] on `stream` before its first kernel and
- *           events[i] right after its i-th kernel, for i < n_events (the
- *           kernels, in launch order, are the ones mita_kernel_names lists)
+ *           events[i] right after the i-th kernel mita_kernel_names lists,
+ *           for i < n_events; kernel i runs between events[starts[i]] and
+ *           events[i + 1] (starts as mita_kernel_names returns them).
+ *
+ * Streams: every kernel goes on `stream`, except that the staged schedule
+ * runs routing and grouping (which need only Q and Q_L) on a library-owned
+ * side stream of the current device, forked from `stream` after pooling and
+ * joined back before attention, so that they overlap the landmark pass.  The
+ * side stream and its two events are created on the device's first staged
+ * call (default priority) and kept until the process ends; calls that fork
+ * are serialised on the host by a lock around the fork and join.  The call
+ * stays asynchronous with respect to the host, and work queued on `stream`
+ * after it sees every output.
  */
 typedef struct {
   float* ql;
@@ -133,14 +144,19 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Names of the kernels mita_forward_ex launches for this configuration and
- * path, in launch order: "fused" for the fused schedule; "pool", "landmark",
- * "route", "group", "attend" for the staged one.  Writes up to `capacity`
- * static strings to names (may be NULL) and returns the kernel count, or a
- * negative mita_status for invalid sizes or an unsupported path.  Host only.
+ * The kernels mita_forward_ex launches for this configuration and path, in
+ * the order of its timing events: "fused" for the fused schedule; "pool",
+ * "route", "group", "landmark", "attend" for the staged one (route and group
+ * on the side stream).  Writes up to `capacity` static strings to names and,
+ * to starts, the index of the event each kernel's interval opens with (i for
+ * kernels that follow the previous one on the same stream; landmark starts
+ * with pooling's end event, like route).  names and starts may be NULL.
+ * Returns the kernel count, or a negative mita_status for invalid sizes or an
+ * unsupported path.  Host only.
  */
 int mita_kernel_names(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
-                      mita_dtype in_dtype, int path, const char** names, int capacity);
+                      mita_dtype in_dtype, int path, const char** names, int* starts,
+                      int capacity);
 
 /* ---------------------------------------------------------------------------
  * The steps one at a time (same kernels as the staged schedule).  Each takes
@@ -156,8 +172,8 @@ mita_status mita_pool(const void* Q, int B, int H, int grid_h, int grid_w, int d
  * Landmark pass: scores of ql [B,H,m,d] fp32 against K [B,H,N,d], each row's
  * top-k keys -> idx [B,H,m,k] (ascending), and the row softmax applied to V
  * -> vl [B,H,m,d] fp32.  Needs mita_landmark_workspace_bytes(...) of scratch
- * (0 for bf16 inputs with k + 256 <= 512 and N <= 32768; workspace may then
- * be NULL).
+ * (0 when the bf16 MFMA kernel serves the shape -- bf16 inputs, k <= 432;
+ * workspace may then be NULL).
  */
 size_t mita_landmark_workspace_bytes(int B, int H, int N, int d, int m, int k,
                                      mita_dtype in_dtype);

@@ -49,10 +49,14 @@ def test_workspace_bytes():
 def test_kernel_names_follow_the_schedule():
     names = mita.mita_kernel_names
     assert names(256, 6, 14, 14, 64, 5, 5, 25, mita.MITA_BF16) == ["fused"]
-    staged = ["pool", "landmark", "route", "group", "attend"]
+    staged = ["pool", "route", "group", "landmark", "attend"]
     assert names(256, 6, 14, 14, 64, 5, 5, 25, mita.MITA_BF16, path="staged") == staged
     assert names(32, 6, 56, 56, 64, 7, 7, 64, mita.MITA_BF16) == staged
     assert names(1, 1, 14, 14, 64, 5, 5, 25, mita.MITA_F32) == staged
+    # routing and grouping run beside the landmark pass: both open at pooling's end
+    assert mita.mita_kernel_schedule(32, 6, 56, 56, 64, 7, 7, 64, mita.MITA_BF16) == [
+        ("pool", 0), ("route", 1), ("group", 2), ("landmark", 1), ("attend", 4)]
+    assert mita.mita_kernel_schedule(256, 6, 14, 14, 64, 5, 5, 25, mita.MITA_BF16) == [("fused", 0)]
     with pytest.raises(mita.MitaError):
         names(32, 6, 56, 56, 64, 7, 7, 64, mita.MITA_BF16, path="fused")
     with pytest.raises(mita.MitaError):

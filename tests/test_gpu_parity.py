@@ -212,8 +212,9 @@ def test_deterministic_and_fully_written():
 
 @pytest.mark.parametrize("name,path", [("deit-s", "auto"), ("hires-3136", "auto")])
 def test_kernel_timing_events(name, path):
-    """The per-kernel events of mita_forward_ex bracket every kernel in order:
-    each interval is positive and they add up to the whole call."""
+    """The per-kernel events of mita_forward_ex bracket every kernel: each
+    kernel's interval (from its start event) is positive, the kernels on the
+    caller's stream tile the call, and routing ends before the call does."""
     torch = _torch()
     import efficient_attention_avg_amd as mita
     w = synth.workload(name)
@@ -221,19 +222,25 @@ def test_kernel_timing_events(name, path):
     Q, K, V = synth.workload_inputs(name, B=B)
     q, k, v = (_to_dev(x, w["dtype"]) for x in (Q, K, V))
     code = mita.MITA_BF16 if w["dtype"] == "bf16" else mita.MITA_F32
-    names = mita.mita_kernel_names(B, w["H"], w["grid_h"], w["grid_w"], 64, w["m_h"], w["m_w"],
-                                   w["k"], code, path=path)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    sched = mita.mita_kernel_schedule(B, w["H"], w["grid_h"], w["grid_w"], 64, w["m_h"],
+                                      w["m_w"], w["k"], code, path=path)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(sched) + 1)]
     for e in ev:
         e.record()
-    _say(f"timing events {name}: {names}")
+    _say(f"timing events {name}: {sched}")
     mita.mita_forward_ex(q, k, v, w["grid_h"], w["grid_w"], w["m_h"], w["m_w"], w["k"],
                          path=path, events=ev)
     torch.cuda.synchronize()
-    dts = [ev[i].elapsed_time(ev[i + 1]) for i in range(len(names))]
-    assert all(dt > 0 for dt in dts), dts
+    dts = {nm: ev[st].elapsed_time(ev[i + 1]) for i, (nm, st) in enumerate(sched)}
+    assert all(dt > 0 for dt in dts.values()), dts
     total = ev[0].elapsed_time(ev[-1])
-    assert abs(sum(dts) - total) <= 1e-3 * max(total, 1e-3) + 1e-4, (dts, total)
+    # the caller's stream: each of its kernels opens with the previous one's end
+    names = [nm for nm, _ in sched]
+    main = [i for i, (nm, st) in enumerate(sched) if nm not in ("route", "group")]
+    chain = sum(dts[sched[i][0]] for i in main)
+    assert abs(chain - total) <= 1e-3 * max(total, 1e-3) + 1e-4, (dts, total)
+    if "route" in names:  # the side stream joined before attention ended
+        assert ev[names.index("group") + 1].elapsed_time(ev[-1]) > 0
 
 
 def test_constant_values_give_constant_output():
