@@ -61,9 +61,10 @@ constexpr int OFF_ROUTE = OFF_IDX + MMAX * KMAX * 4;
 constexpr int OFF_PERM = OFF_ROUTE + 256 * 4;
 constexpr int OFF_BM = OFF_PERM + 256 * 4;        // [32 experts][8] words: query bitmaps
 constexpr int OFF_OFFS = OFF_BM + MMAX * 8 * 4;   // [33] int: expert offsets in PERM
-constexpr int OFF_STAT = OFF_OFFS + 48 * 4;       // rowmax[32], rowsum[32], non-empty experts
-constexpr int OFF_WMASK = OFF_STAT + 80 * 4;      // [KPMAX] landmark-membership bits per token
-constexpr int OFF_INVC = OFF_WMASK + KPMAX * 4;   // [MMAX] 1 / pooling window size
+constexpr int OFF_STAT = OFF_OFFS + 48 * 4;       // the non-empty experts' bit mask
+constexpr int OFF_WB = OFF_STAT + 16;             // [MMAX][KPMAX / 8] window-membership bytes
+constexpr int OFF_LUT = OFF_WB + MMAX * KPMAX / 8; // [16] x 4 bf16: a nibble's bits as 0 / 1
+constexpr int OFF_INVC = OFF_LUT + 16 * 8;        // [MMAX] 1 / pooling window size
 constexpr int LDS_BYTES = OFF_INVC + MMAX * 4;
 static_assert(2 * LDS_BYTES <= 160 * 1024, "two workgroups per gfx950 CU");
 static_assert(OFF_H % 16 == 0 && OFF_QLH % 16 == 0 && OFF_VLT % 16 == 0 && OFF_IDX % 16 == 0 &&
@@ -270,12 +271,6 @@ __device__ __forceinline__ void store_qt(const VRows& qr, char* sm, int tid) {
   }
 }
 
-// Two 0/1 bf16 entries of the pooling matrix: bit L of two tokens' masks.
-__device__ __forceinline__ uint32_t member_pair(uint32_t m0, uint32_t m1, int L) {
-  const uint32_t b = __builtin_amdgcn_ubfe(m0, L, 1) | (__builtin_amdgcn_ubfe(m1, L, 1) << 16);
-  return b * 0x3F80u;
-}
-
 // EXTRAS: whether any of the optional intermediate outputs is requested; the
 // plain forward is compiled without their stores and branches.
 template <bool EXTRAS>
@@ -293,19 +288,27 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
 
   // expert key slots past k stay 0 for every head (top-k fills slots < k)
   for (int q = threadIdx.x; q < MMAX * KMAX; q += THREADS) *lds<int>(sm, OFF_IDX + q * 4) = 0;
-  // which landmark windows hold each token (the same for every head)
-  for (int tok = threadIdx.x; tok < KPMAX; tok += THREADS) {
+  // which tokens each landmark window holds (the same for every head): byte o
+  // of landmark L has bit t set when token 8o + t lies in L's window
+  for (int it = threadIdx.x; it < MMAX * (KPMAX / 8); it += THREADS) {
+    const int L = it / (KPMAX / 8), o = it % (KPMAX / 8);
     uint32_t bits = 0;
-    if (tok < N) {
-      const int y = tok / gw, x = tok % gw;
-      for (int i = 0; i < m; ++i) {
-        int y0, y1, x0, x1;
-        pool_window(i / mw, gh, mh, &y0, &y1);
-        pool_window(i % mw, gw, mw, &x0, &x1);
-        bits |= (y >= y0 && y < y1 && x >= x0 && x < x1 ? 1u : 0u) << i;
+    if (L < m) {
+      int y0, y1, x0, x1;
+      pool_window(L / mw, gh, mh, &y0, &y1);
+      pool_window(L % mw, gw, mw, &x0, &x1);
+      for (int t = 0; t < 8; ++t) {
+        const int tok = 8 * o + t, y = tok / gw, x = tok % gw;
+        bits |= (tok < N && y >= y0 && y < y1 && x >= x0 && x < x1 ? 1u : 0u) << t;
       }
     }
-    *lds<uint32_t>(sm, OFF_WMASK + tok * 4) = bits;
+    *lds<uint8_t>(sm, OFF_WB + it) = (uint8_t)bits;
+  }
+  // bf16 1.0 / 0 for each bit of a nibble, pairs packed as the MFMA operand
+  if (threadIdx.x < 16) {
+    const uint32_t n = threadIdx.x, one = 0x3F80u;
+    *lds<u32x2>(sm, OFF_LUT + n * 8) = u32x2{(n & 1u ? one : 0u) | (n & 2u ? one << 16 : 0u),
+                                             (n & 4u ? one : 0u) | (n & 8u ? one << 16 : 0u)};
   }
   // 1 / window size per landmark (0 past m)
   if (threadIdx.x < MMAX) {
@@ -354,10 +357,11 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
       f32x4 acc = zero4();
       for (int ks = 0; ks < KP / 32; ++ks) {
         const u32x4 a = *lds<u32x4>(sm, OFF_X + (16 * ct + c16) * VT_STRIDE + (32 * ks + 8 * g) * 2);
-        const u32x4 m0 = *lds<u32x4>(sm, OFF_WMASK + (32 * ks + 8 * g) * 4);
-        const u32x4 m1 = *lds<u32x4>(sm, OFF_WMASK + (32 * ks + 8 * g + 4) * 4);
-        const u32x4 b = {member_pair(m0[0], m0[1], L), member_pair(m0[2], m0[3], L),
-                         member_pair(m1[0], m1[1], L), member_pair(m1[2], m1[3], L)};
+        // B = W[tokens 32ks + 8g .. +7][landmark L]: one membership byte, two nibbles
+        const uint32_t byte = *lds<uint8_t>(sm, OFF_WB + L * (KPMAX / 8) + 4 * ks + g);
+        const u32x2 b01 = *lds<u32x2>(sm, OFF_LUT + (byte & 15u) * 8);
+        const u32x2 b23 = *lds<u32x2>(sm, OFF_LUT + (byte >> 4) * 8);
+        const u32x4 b = {b01[0], b01[1], b23[0], b23[1]};
         acc = mfma_bf16(a, b, acc);
       }
       // lane holds Q_L[landmark L][channels 16ct + 4g .. +3]: fp32, then bf16 hi + lo
@@ -560,23 +564,14 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
           }
         }
         // P row (f16) over this row's bytes, zero past the owned keys up to the
-        // padded width, and its sum (of the rounded values the products use)
-        float sum = 0.f;
+        // padded width (its sum comes out of the V_L products)
         uint16_t* prow = reinterpret_cast<uint16_t*>(hrow);
         const float moff = active ? -rmax : 0.f;  // scores are in the base-2 domain
 #pragma unroll
-        for (int u = 0; u < MAXNT; ++u) {
-          const uint32_t hb = f16_bits(__builtin_amdgcn_exp2f(v[u] + moff));
-          sum += f16_bits_to_f32(hb);
-          prow[key0 + u] = (uint16_t)hb;
-        }
+        for (int u = 0; u < MAXNT; ++u)
+          prow[key0 + u] = (uint16_t)f16_bits(__builtin_amdgcn_exp2f(v[u] + moff));
         static_assert(MAXNT * 16 + 16 == KPMAX, "one zero column per lane past the owned keys");
         prow[MAXNT * 16 + t] = 0;
-        sum = g16_sumf(sum);
-        if (t == 0) {
-          *lds<float>(sm, OFF_STAT + i * 4) = rmax;
-          *lds<float>(sm, OFF_STAT + (32 + i) * 4) = active ? sum : 1.0f;
-        }
       }
     }
     // ---------------- E': R^T = Q_L Q^T per token tile (Q rows from global memory): routes
@@ -653,7 +648,7 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
         const int off_e = incl - cnt;  // lane m holds N
         if (lane <= m) *lds<int>(sm, OFF_OFFS + lane * 4) = off_e;
         const uint64_t ne = __ballot(cnt > 0);
-        if (lane == 0) *lds<uint32_t>(sm, OFF_STAT + 64 * 4) = (uint32_t)ne;
+        if (lane == 0) *lds<uint32_t>(sm, OFF_STAT) = (uint32_t)ne;
         if (EXTRAS && lane < m) {
           if (o.counts) o.counts[(size_t)bh * m + lane] = cnt;
           if (o.offsets) o.offsets[(size_t)bh * (m + 1) + lane] = off_e;
@@ -703,15 +698,18 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
   #pragma unroll 1
       for (int tile = w; tile < 8; tile += NWAVES) {
         const int ct = tile & 3, lt = tile >> 2;
-        f32x4 acc = zero4();
+        // the row sums of the same f16 weights: an all-ones A operand
+        const u32x4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+        f32x4 acc = zero4(), tot = zero4();
         for (int ks = 0; ks < KP / 32; ++ks) {
           const u32x4 a = *lds<u32x4>(sm, OFF_X + (16 * ct + c16) * VT_STRIDE + (32 * ks + 8 * g) * 2);
           const u32x4 b = *lds<u32x4>(sm, OFF_H + (16 * lt + c16) * H_STRIDE + (32 * ks + 8 * g) * 2);
           acc = mfma_f16(a, b, acc);
+          tot = mfma_f16(ones, b, tot);
         }
         const int L = 16 * lt + c16;
         const bool ok = L < m;
-        const float inv = ok ? 1.0f / *lds<float>(sm, OFF_STAT + (32 + L) * 4) : 0.f;
+        const float inv = ok ? __builtin_amdgcn_rcpf(tot[0]) : 0.f;
         float vl4[4];
   #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -746,7 +744,7 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
       // registers are written on every path)
       load_v(qr, head_rows(bh + (int)gridDim.x < BH ? Qh + (size_t)gridDim.x * head_elems : Qh, N), N, tid);
       const uint32_t nonempty =
-          __builtin_amdgcn_readfirstlane(*lds<uint32_t>(sm, OFF_STAT + 64 * 4));
+          __builtin_amdgcn_readfirstlane(*lds<uint32_t>(sm, OFF_STAT));
       const int nqt = (N + 15) >> 4;
       float* outh = o.out + (size_t)bh * N * 64;
       // expert e's key rows for this lane's two slot tiles, from the LDS copy
