@@ -12,7 +12,8 @@ Infinity Cache holds the inputs (the DeiT-S inputs would otherwise fit in
 it); a read leaves clean lines, so the first kernel does not share HBM with
 the write-back of a flush buffer.  The library records HIP events before its
 first kernel and after each kernel (mita_forward_ex's timing events; the staged
-schedule runs routing and grouping on a side stream beside the landmark pass):
+schedule runs routing and grouping on a side stream, which the binding owns and
+passes in, beside the landmark pass):
 a step's time is first event to last, a kernel's time the interval from its
 start event to its end; ms_per_step is the mean step time.  A warm (no flush) figure is reported
 beside it unless --no-warm.
@@ -142,12 +143,13 @@ class Runner:
         self.flush_f32 = self.flush_buf.view(torch.float32)
         self.flush_sink = torch.zeros((), dtype=torch.float32, device="cuda")
         self.sched = mita.mita_kernel_schedule(w["B"], w["H"], w["grid_h"], w["grid_w"], w["d"],
-                                              w["m_h"], w["m_w"], w["k"], code, path=path)
+                                              w["m_h"], w["m_w"], w["k"], code, path=path,
+                                              overlap=True)
         self.kernels = [nm for nm, _ in self.sched]
 
     def step(self, events=None):
         self.mita.mita_forward_ex(self.q, self.k, self.v, *self.args, out=self.out,
-                                  workspace=self.ws, path=self.path, events=events)
+                                  workspace=self.ws, path=self.path, events=events, overlap=True)
 
     def flush(self):
         # a read of 512 MiB evicts L2 and the Infinity Cache with clean lines; a write

@@ -38,7 +38,9 @@ class MitaError(RuntimeError):
 class _Extras(ctypes.Structure):
     _fields_ = [("ql", ctypes.c_void_p), ("vl", ctypes.c_void_p), ("counts", ctypes.c_void_p),
                 ("offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p), ("path", ctypes.c_int),
-                ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int)]
+                ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int),
+                ("side_stream", ctypes.c_void_p), ("fork_event", ctypes.c_void_p),
+                ("join_event", ctypes.c_void_p)]
 
 
 _lib = None
@@ -64,7 +66,7 @@ def lib() -> ctypes.CDLL:
         L.mita_schedule.restype = I
         L.mita_schedule.argtypes = [I] * 8 + [I]
         L.mita_kernel_names.restype = I
-        L.mita_kernel_names.argtypes = [I] * 8 + [I, I, ctypes.POINTER(ctypes.c_char_p),
+        L.mita_kernel_names.argtypes = [I] * 8 + [I, I, I, ctypes.POINTER(ctypes.c_char_p),
                                                  ctypes.POINTER(ctypes.c_int), I]
         L.mita_forward.restype = S
         L.mita_forward.argtypes = [P, P, P] + [I] * 8 + [I, P, P, P, P, Z, P]
@@ -161,14 +163,15 @@ def mita_forward(q, k, v, grid_h, grid_w, m_h, m_w, topk, *, out=None, idx=None,
                            route=route, workspace=workspace, stream=stream)["out"]
 
 
-def mita_kernel_schedule(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code, path="auto") -> list:
+def mita_kernel_schedule(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code, path="auto",
+                         overlap=False) -> list:
     """The kernels mita_forward_ex launches, in the order of its timing events, as
-    (name, start) pairs: kernel i runs between events[start] and events[i + 1]
-    (host only)."""
+    (name, start) pairs: kernel i runs between events[start] and events[i + 1];
+    ``overlap``: the call runs routing on a side stream (host only)."""
     names = (ctypes.c_char_p * 8)()
     starts = (ctypes.c_int * 8)()
     n = int(lib().mita_kernel_names(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code, PATHS[path],
-                                    names, starts, 8))
+                                    1 if overlap else 0, names, starts, 8))
     if n < 0:
         _check(-n)
     return [(names[i].decode(), int(starts[i])) for i in range(n)]
@@ -180,12 +183,32 @@ def mita_kernel_names(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code, path="au
                                                  path)]
 
 
+_sides = {}
+
+
+def _side(device):
+    """This process's side stream and fork/join events for `device` (created once)."""
+    import torch
+    key = torch.device(device).index
+    if key not in _sides:
+        with torch.cuda.device(device):
+            s = torch.cuda.Stream(device=device)
+            f, j = torch.cuda.Event(), torch.cuda.Event()
+            f.record(s)
+            j.record(s)  # creates the HIP events
+        _sides[key] = (s, f, j)
+    return _sides[key]
+
+
 def mita_forward_ex(q, k, v, grid_h, grid_w, m_h, m_w, topk, *, out=None, idx=None, route=None,
-                    extras=False, path="auto", workspace=None, stream=None, events=None):
+                    extras=False, path="auto", workspace=None, stream=None, events=None,
+                    overlap=False):
     """Whole pass with optional intermediates.
 
     ``idx`` / ``route``: a preallocated int32 tensor, True (allocate) or None.
     ``extras=True`` also returns ql, vl, counts, offsets and perm.
+    ``overlap=True``: the staged schedule runs routing and grouping on this
+    process's side stream for the device, beside the landmark pass.
     ``events``: torch.cuda.Event objects (enable_timing=True): events[0] before
     the first kernel, events[i + 1] after the i-th kernel of
     mita_kernel_schedule, whose start index gives the event the kernel's
@@ -208,6 +231,10 @@ def mita_forward_ex(q, k, v, grid_h, grid_w, m_h, m_w, topk, *, out=None, idx=No
     route = alloc(route, (B, H, N), i32, "route")
     res = dict(out=out, idx=idx, route=route)
     ex = _Extras(path=PATHS[path])
+    if overlap:
+        side, fork, join = _side(dev)
+        ex.side_stream, ex.fork_event, ex.join_event = side.cuda_stream, fork.cuda_event, \
+            join.cuda_event
     if events:
         handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
         ex.events = ctypes.cast(handles, ctypes.POINTER(ctypes.c_void_p))

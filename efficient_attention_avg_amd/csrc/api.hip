@@ -9,7 +9,6 @@
 #include "../../include/mita.h"
 #include "internal.h"
 
-#include <mutex>
 
 using mita::Shape;
 using mita::align_up;
@@ -48,37 +47,6 @@ struct Marker {
     ++i;
   }
 };
-
-// The staged schedule's side stream for routing and grouping, one per device:
-// created on first use (default priority, non-blocking), kept until the
-// process ends.  g_side_mu serialises creation and each call's fork and join.
-struct Side {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-std::mutex g_side_mu;
-constexpr int kMaxDevices = 64;
-Side g_side[kMaxDevices];
-bool g_side_failed[kMaxDevices];
-
-// The current device's side stream, or nullptr (routing then stays on the
-// caller's stream) if it cannot be created.  Call with g_side_mu held.
-Side* side_stream() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  Side& sd = g_side[dev];
-  if (sd.s) return &sd;
-  if (g_side_failed[dev]) return nullptr;
-  if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess ||
-      hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess) {
-    g_side_failed[dev] = true;
-    sd.s = nullptr;
-    (void)hipGetLastError();
-    return nullptr;
-  }
-  return &sd;
-}
 
 mita_status make_shape(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
                        mita_dtype dt, Shape* s) {
@@ -246,6 +214,9 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V, int B, 
   if (path == MITA_PATH_FUSED && !fusable)
     return fail(MITA_ERR_UNSUPPORTED,
                 "fused schedule needs bf16 inputs, N <= 208, m <= 32 and k <= 32");
+  const bool side = extras && (extras->side_stream || extras->fork_event || extras->join_event);
+  if (side && !(extras->side_stream && extras->fork_event && extras->join_event))
+    return fail(MITA_ERR_INVALID_ARG, "side_stream, fork_event and join_event go together");
   Marker mk;
   if (extras && extras->events && extras->n_events > 0) {
     mk.ev = extras->events;
@@ -275,21 +246,21 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V, int B, 
 
   if ((st = run_pool(Q, ql, s, stream, &mk)) != MITA_OK) return st;
   {
-    // routing and grouping need only Q and Q_L: they run on the side stream
-    // beside the landmark pass and join before attention
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    Side* sd = side_stream();
-    hipStream_t rs = stream;
-    if (sd) {
-      if ((st = hip_status(hipEventRecord(sd->fork, stream), "fork")) != MITA_OK) return st;
-      if ((st = hip_status(hipStreamWaitEvent(sd->s, sd->fork, 0), "fork")) != MITA_OK) return st;
-      rs = sd->s;
+    // routing and grouping need only Q and Q_L: with a caller-given side stream
+    // they run there, beside the landmark pass, and join before attention
+    const bool fork = side;
+    hipStream_t rs = fork ? (hipStream_t)extras->side_stream : stream;
+    hipEvent_t ef = fork ? (hipEvent_t)extras->fork_event : nullptr;
+    hipEvent_t ej = fork ? (hipEvent_t)extras->join_event : nullptr;
+    if (fork) {
+      if ((st = hip_status(hipEventRecord(ef, stream), "fork")) != MITA_OK) return st;
+      if ((st = hip_status(hipStreamWaitEvent(rs, ef, 0), "fork")) != MITA_OK) return st;
     }
     if ((st = run_route(Q, ql, route_p, counts, offsets, perm, rscratch, s, rs, &mk)) != MITA_OK)
       return st;
-    if (sd && (st = hip_status(hipEventRecord(sd->join, sd->s), "join")) != MITA_OK) return st;
+    if (fork && (st = hip_status(hipEventRecord(ej, rs), "join")) != MITA_OK) return st;
     if ((st = run_landmark(ql, K, V, idx_p, vl, scratch, s, stream, &mk)) != MITA_OK) return st;
-    if (sd && (st = hip_status(hipStreamWaitEvent(stream, sd->join, 0), "join")) != MITA_OK)
+    if (fork && (st = hip_status(hipStreamWaitEvent(stream, ej, 0), "join")) != MITA_OK)
       return st;
   }
   if ((st = run_attend(Q, K, V, ql, vl, idx_p, route_p, offsets, perm, out, s, stream, &mk)) !=
@@ -299,8 +270,8 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V, int B, 
 }
 
 int mita_kernel_names(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
-                      mita_dtype in_dtype, int path, const char** names, int* starts,
-                      int capacity) {
+                      mita_dtype in_dtype, int path, int forked, const char** names,
+                      int* starts, int capacity) {
   Shape s;
   const mita_status st = make_shape(B, H, grid_h, grid_w, d, m_h, m_w, k, in_dtype, &s);
   if (st != MITA_OK) return -(int)st;
@@ -312,10 +283,11 @@ int mita_kernel_names(int B, int H, int grid_h, int grid_w, int d, int m_h, int 
   static const char* const kFused[] = {"fused"};
   static const int kFusedStart[] = {0};
   static const char* const kStaged[] = {"pool", "route", "group", "landmark", "attend"};
-  static const int kStagedStart[] = {0, 1, 2, 1, 4};
+  static const int kStagedStart[] = {0, 1, 2, 3, 4};
+  static const int kForkedStart[] = {0, 1, 2, 1, 4};
   const bool fused = fusable && path != MITA_PATH_STAGED;
   const char* const* list = fused ? kFused : kStaged;
-  const int* start = fused ? kFusedStart : kStagedStart;
+  const int* start = fused ? kFusedStart : forked ? kForkedStart : kStagedStart;
   const int n = fused ? 1 : 5;
   for (int i = 0; i < n && i < capacity; ++i) {
     if (names) names[i] = list[i];

@@ -114,16 +114,16 @@ mita_status mita_forward(const void* Q, const void* K, const void* V,
  *           events[i] right after the i-th kernel mita_kernel_names lists,
  *           for i < n_events; kernel i runs between events[starts[i]] and
  *           events[i + 1] (starts as mita_kernel_names returns them).
- *
- * Streams: every kernel goes on `stream`, except that the staged schedule
- * runs routing and grouping (which need only Q and Q_L) on a library-owned
- * side stream of the current device, forked from `stream` after pooling and
- * joined back before attention, so that they overlap the landmark pass.  The
- * side stream and its two events are created on the device's first staged
- * call (default priority) and kept until the process ends; calls that fork
- * are serialised on the host by a lock around the fork and join.  The call
- * stays asynchronous with respect to the host, and work queued on `stream`
- * after it sees every output.
+ *   side_stream, fork_event, join_event
+ *           NULL, or all three: a caller-owned hipStream_t on the same device
+ *           and two caller-owned hipEvent_t.  The staged schedule then runs
+ *           routing and grouping (which need only Q and Q_L) on side_stream,
+ *           forked from `stream` after pooling (fork_event) and joined back
+ *           before attention (join_event), so that they overlap the landmark
+ *           pass.  The fused schedule ignores them.  Two calls in flight at
+ *           once must not share them.  Without them every kernel goes on
+ *           `stream`.  Either way the call is asynchronous with respect to
+ *           the host, and work queued on `stream` after it sees every output.
  */
 typedef struct {
   float* ql;
@@ -134,6 +134,9 @@ typedef struct {
   int path; /* mita_path */
   void* const* events;
   int n_events;
+  void* side_stream; /* hipStream_t */
+  void* fork_event;  /* hipEvent_t */
+  void* join_event;  /* hipEvent_t */
 } mita_extras;
 
 mita_status mita_forward_ex(const void* Q, const void* K, const void* V,
@@ -146,17 +149,17 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V,
 /*
  * The kernels mita_forward_ex launches for this configuration and path, in
  * the order of its timing events: "fused" for the fused schedule; "pool",
- * "route", "group", "landmark", "attend" for the staged one (route and group
- * on the side stream).  Writes up to `capacity` static strings to names and,
- * to starts, the index of the event each kernel's interval opens with (i for
- * kernels that follow the previous one on the same stream; landmark starts
- * with pooling's end event, like route).  names and starts may be NULL.
- * Returns the kernel count, or a negative mita_status for invalid sizes or an
- * unsupported path.  Host only.
+ * "route", "group", "landmark", "attend" for the staged one.  Writes up to
+ * `capacity` static strings to names and, to starts, the index of the event
+ * each kernel's interval opens with: i when the kernel follows the previous
+ * one on the same stream; with `forked` nonzero (a call given a side stream)
+ * landmark opens with pooling's end event, like route.  names and starts may
+ * be NULL.  Returns the kernel count, or a negative mita_status for invalid
+ * sizes or an unsupported path.  Host only.
  */
 int mita_kernel_names(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
-                      mita_dtype in_dtype, int path, const char** names, int* starts,
-                      int capacity);
+                      mita_dtype in_dtype, int path, int forked, const char** names,
+                      int* starts, int capacity);
 
 /* ---------------------------------------------------------------------------
  * The steps one at a time (same kernels as the staged schedule).  Each takes

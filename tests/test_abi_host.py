@@ -53,8 +53,12 @@ def test_kernel_names_follow_the_schedule():
     assert names(256, 6, 14, 14, 64, 5, 5, 25, mita.MITA_BF16, path="staged") == staged
     assert names(32, 6, 56, 56, 64, 7, 7, 64, mita.MITA_BF16) == staged
     assert names(1, 1, 14, 14, 64, 5, 5, 25, mita.MITA_F32) == staged
-    # routing and grouping run beside the landmark pass: both open at pooling's end
+    # one stream: each kernel opens with the previous one's end; with a side stream
+    # routing and grouping run beside the landmark pass, both opening at pooling's end
     assert mita.mita_kernel_schedule(32, 6, 56, 56, 64, 7, 7, 64, mita.MITA_BF16) == [
+        ("pool", 0), ("route", 1), ("group", 2), ("landmark", 3), ("attend", 4)]
+    assert mita.mita_kernel_schedule(32, 6, 56, 56, 64, 7, 7, 64, mita.MITA_BF16,
+                                     overlap=True) == [
         ("pool", 0), ("route", 1), ("group", 2), ("landmark", 1), ("attend", 4)]
     assert mita.mita_kernel_schedule(256, 6, 14, 14, 64, 5, 5, 25, mita.MITA_BF16) == [("fused", 0)]
     with pytest.raises(mita.MitaError):

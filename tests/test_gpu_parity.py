@@ -210,8 +210,9 @@ def test_deterministic_and_fully_written():
     assert torch.equal(out1, out2)
 
 
-@pytest.mark.parametrize("name,path", [("deit-s", "auto"), ("hires-3136", "auto")])
-def test_kernel_timing_events(name, path):
+@pytest.mark.parametrize("name,path,overlap", [("deit-s", "auto", False), ("hires-3136", "auto", False),
+                                               ("hires-3136", "auto", True)])
+def test_kernel_timing_events(name, path, overlap):
     """The per-kernel events of mita_forward_ex bracket every kernel: each
     kernel's interval (from its start event) is positive, the kernels on the
     caller's stream tile the call, and routing ends before the call does."""
@@ -223,20 +224,20 @@ def test_kernel_timing_events(name, path):
     q, k, v = (_to_dev(x, w["dtype"]) for x in (Q, K, V))
     code = mita.MITA_BF16 if w["dtype"] == "bf16" else mita.MITA_F32
     sched = mita.mita_kernel_schedule(B, w["H"], w["grid_h"], w["grid_w"], 64, w["m_h"],
-                                      w["m_w"], w["k"], code, path=path)
+                                      w["m_w"], w["k"], code, path=path, overlap=overlap)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(sched) + 1)]
     for e in ev:
         e.record()
     _say(f"timing events {name}: {sched}")
     mita.mita_forward_ex(q, k, v, w["grid_h"], w["grid_w"], w["m_h"], w["m_w"], w["k"],
-                         path=path, events=ev)
+                         path=path, events=ev, overlap=overlap)
     torch.cuda.synchronize()
     dts = {nm: ev[st].elapsed_time(ev[i + 1]) for i, (nm, st) in enumerate(sched)}
     assert all(dt > 0 for dt in dts.values()), dts
     total = ev[0].elapsed_time(ev[-1])
     # the caller's stream: each of its kernels opens with the previous one's end
     names = [nm for nm, _ in sched]
-    main = [i for i, (nm, st) in enumerate(sched) if nm not in ("route", "group")]
+    main = [i for i, (nm, st) in enumerate(sched) if not overlap or nm not in ("route", "group")]
     chain = sum(dts[sched[i][0]] for i in main)
     assert abs(chain - total) <= 1e-3 * max(total, 1e-3) + 1e-4, (dts, total)
     if "route" in names:  # the side stream joined before attention ended
