@@ -210,6 +210,7 @@ def measure(name, steps, warmup, path="auto", warm=True):
     res = dict(
         workload=w, value=qh / (cold_ms * 1e-3), ms_per_step=cold_ms,
         ms_p10=sorted(cold_all)[len(cold_all) // 10], ms_p90=sorted(cold_all)[(9 * len(cold_all)) // 10],
+        ms_median=sorted(cold_all)[len(cold_all) // 2],
         warm_ms_per_step=warm_ms, warm_value=qh / (warm_ms * 1e-3) if warm_ms else None,
         wall_s=wall,
         roofline=dict(bound="hbm", kernel=dom, achieved=dom_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
@@ -235,7 +236,8 @@ def cpu_baseline(runner, seconds):
     Q, K, V = runner.host
     N = w["grid_h"] * w["grid_w"]
     heads = 0
-    with threadpool_limits(limits=1):
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
         for b in range(w["B"]):
             for h in range(w["H"]):
@@ -247,9 +249,10 @@ def cpu_baseline(runner, seconds):
             if time.perf_counter() - t0 >= seconds:
                 break
         el = time.perf_counter() - t0
-    return dict(value=heads * N / el, unit="query-heads/s", cores=1, kind="oracle",
+    return dict(value=heads * N / el, unit="query-heads/s", cores=cores, kind="oracle",
                 sample=f"first {heads} of {w['B'] * w['H']} (b,h) heads of {w['name']}, "
-                       f"{el:.1f}s, numpy fp64 with BLAS limited to 1 thread")
+                       f"{el:.1f}s, numpy fp64, BLAS threads = the {cores} cores this process "
+                       f"may run on")
 
 
 COPY_MIB = 256
@@ -344,7 +347,10 @@ def main():
         del r2
         secondary = {
             "workload": describe(res2["workload"]), "value": res2["value"], "unit": "query-heads/s",
-            "ms_per_step": res2["ms_per_step"], "warm_ms_per_step": res2["warm_ms_per_step"],
+            "ms_per_step": res2["ms_per_step"], "ms_median": res2["ms_median"],
+            "ms_p10": res2["ms_p10"], "ms_p90": res2["ms_p90"],
+            "warm_ms_per_step": res2["warm_ms_per_step"],
+            "streams": "routing and grouping on a side stream beside the landmark pass",
             "roofline": res2["roofline"], "pass_roofline": res2["pass_roofline"],
             "stage_us": res2["stage_us"], "kernel_gbs": res2["kernel_gbs"],
             "schedule": res2["schedule"], "dtype": res2["dtype"],
@@ -358,9 +364,10 @@ def main():
         "config": {"workload": describe(w), "B": w["B"], "H": w["H"], "seq_len": w["grid_h"] * w["grid_w"],
                    "m": w["m_h"] * w["m_w"], "k": w["k"], "path": args.path,
                    "schedule": main_res["schedule"],
-                   "timing": "HIP events the library records around its kernels on the launch "
-                             "stream, L2 + Infinity Cache flushed (512 MiB read) before each step"},
-        "ms_p10": main_res["ms_p10"], "ms_p90": main_res["ms_p90"],
+                   "timing": "HIP events the library records around its kernels, mean over the "
+                             "timed steps (median and p10/p90 beside it), L2 + Infinity Cache "
+                             "flushed (512 MiB read) before each step"},
+        "ms_median": main_res["ms_median"], "ms_p10": main_res["ms_p10"], "ms_p90": main_res["ms_p90"],
         "warm_ms_per_step": main_res["warm_ms_per_step"], "warm_value": main_res["warm_value"],
         "roofline": main_res["roofline"], "pass_roofline": main_res["pass_roofline"],
         "stage_us": main_res["stage_us"], "kernel_gbs": main_res["kernel_gbs"],
