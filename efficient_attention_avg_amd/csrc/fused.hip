@@ -62,8 +62,8 @@ constexpr int OFF_PERM = OFF_ROUTE + 256 * 4;
 constexpr int OFF_BM = OFF_PERM + 256 * 4;        // [32 experts][8] words: query bitmaps
 constexpr int OFF_OFFS = OFF_BM + MMAX * 8 * 4;   // [33] int: expert offsets in PERM
 constexpr int OFF_STAT = OFF_OFFS + 48 * 4;       // the non-empty experts' bit mask
-constexpr int OFF_WB = OFF_STAT + 16;             // [MMAX][KPMAX / 8] window-membership bytes
-constexpr int OFF_LUT = OFF_WB + MMAX * KPMAX / 8; // [16] x 4 bf16: a nibble's bits as 0 / 1
+constexpr int OFF_WB = OFF_STAT + 16;             // [MMAX][4][8] window-membership bytes
+constexpr int OFF_LUT = OFF_WB + MMAX * 4 * 8;    // [16] x 4 bf16: a nibble's bits as 0 / 1
 constexpr int OFF_INVC = OFF_LUT + 16 * 8;        // [MMAX] 1 / pooling window size
 constexpr int LDS_BYTES = OFF_INVC + MMAX * 4;
 static_assert(2 * LDS_BYTES <= 160 * 1024, "two workgroups per gfx950 CU");
@@ -288,12 +288,14 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
 
   // expert key slots past k stay 0 for every head (top-k fills slots < k)
   for (int q = threadIdx.x; q < MMAX * KMAX; q += THREADS) *lds<int>(sm, OFF_IDX + q * 4) = 0;
-  // which tokens each landmark window holds (the same for every head): byte o
-  // of landmark L has bit t set when token 8o + t lies in L's window
-  for (int it = threadIdx.x; it < MMAX * (KPMAX / 8); it += THREADS) {
-    const int L = it / (KPMAX / 8), o = it % (KPMAX / 8);
+  // which tokens each landmark window holds (the same for every head): byte
+  // [L][g][ks] has bit t set when token 32ks + 8g + t lies in L's window, so a
+  // lane's bytes for every k-step of the pooling product are one 8-byte read
+  static_assert(KPMAX / 32 <= 8, "one byte per k-step");
+  for (int it = threadIdx.x; it < MMAX * 4 * 8; it += THREADS) {
+    const int L = it >> 5, gg = (it >> 3) & 3, ks = it & 7, o = 4 * ks + gg;
     uint32_t bits = 0;
-    if (L < m) {
+    if (L < m && 8 * o < KPMAX) {
       int y0, y1, x0, x1;
       pool_window(L / mw, gh, mh, &y0, &y1);
       pool_window(L % mw, gw, mw, &x0, &x1);
@@ -355,14 +357,19 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
       FUSED_IDS;
       const int ct = w & 3, L = 16 * (w >> 2) + c16;
       f32x4 acc = zero4();
-      for (int ks = 0; ks < KP / 32; ++ks) {
-        const u32x4 a = *lds<u32x4>(sm, OFF_X + (16 * ct + c16) * VT_STRIDE + (32 * ks + 8 * g) * 2);
-        // B = W[tokens 32ks + 8g .. +7][landmark L]: one membership byte, two nibbles
-        const uint32_t byte = *lds<uint8_t>(sm, OFF_WB + L * (KPMAX / 8) + 4 * ks + g);
-        const u32x2 b01 = *lds<u32x2>(sm, OFF_LUT + (byte & 15u) * 8);
-        const u32x2 b23 = *lds<u32x2>(sm, OFF_LUT + (byte >> 4) * 8);
-        const u32x4 b = {b01[0], b01[1], b23[0], b23[1]};
-        acc = mfma_bf16(a, b, acc);
+      const u32x2 wb = *lds<u32x2>(sm, OFF_WB + (L * 4 + g) * 8);
+      const int nks = KP / 32 + opaque_zero();  // per-step tests made here, not held
+#pragma unroll
+      for (int ks = 0; ks < KPMAX / 32; ++ks) {
+        if (ks < nks) {
+          const u32x4 a = *lds<u32x4>(sm, OFF_X + (16 * ct + c16) * VT_STRIDE + (32 * ks + 8 * g) * 2);
+          // B = W[tokens 32ks + 8g .. +7][landmark L]: one membership byte, two nibbles
+          const uint32_t byte = (wb[ks >> 2] >> (8 * (ks & 3))) & 0xFFu;
+          const u32x2 b01 = *lds<u32x2>(sm, OFF_LUT + (byte & 15u) * 8);
+          const u32x2 b23 = *lds<u32x2>(sm, OFF_LUT + (byte >> 4) * 8);
+          const u32x4 b = {b01[0], b01[1], b23[0], b23[1]};
+          acc = mfma_bf16(a, b, acc);
+        }
       }
       // lane holds Q_L[landmark L][channels 16ct + 4g .. +3]: fp32, then bf16 hi + lo
       const float inv_cnt = *lds<float>(sm, OFF_INVC + L * 4);

@@ -437,6 +437,9 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
     ql_slot_store(sm, tl, lane, bqh, bql);
   }
 
+  // each pass's first K block is requested before the previous pass's tail
+  // (merge, bin search), so that its latency hides behind that work
+  KRegs kpre;
   // ------------------------------------------------------------ V: values
   {
     char* vt = sm + OFF_UNION + w * VT_BYTES;
@@ -559,6 +562,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
         part[67] = mx[tl];
       }
     }
+    if (w < nblk) load_k(kpre, Kh, w, N, g, c16);
     __syncthreads();
     // merge: thread -> (row, 4 channels), ROWS * 16 items
     const float* base = reinterpret_cast<const float*>(sm + OFF_UNION);
@@ -610,8 +614,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
 
   // ------------------------------------------------------------ H: histogram
   {
-    KRegs kr;
-    if (w < nblk) load_k(kr, Kh, w, N, g, c16);
+    KRegs kr = kpre;
     for (int blk = w; blk < nblk; blk += NW) {
       const bool last = ragged && blk == nblk - 1;
 #pragma unroll
@@ -630,6 +633,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
       }
     }
   }
+  if (w < nblk) load_k(kpre, Kh, w, N, g, c16);
   __syncthreads();
   // the bin holding each row's k-th best: group g of wave w takes rows
   // 4w + g + 16i
@@ -738,8 +742,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
     };
     if (flag[0] == 0) {
       // every row's candidates fit: one streaming pass
-      KRegs kr;
-      if (w < nblk) load_k(kr, Kh, w, N, g, c16);
+      KRegs kr = kpre;
       for (int blk = w; blk < nblk; blk += NW) {
         const bool last = ragged && blk == nblk - 1;
 #pragma unroll
