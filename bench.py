@@ -15,8 +15,11 @@ first kernel and after each kernel (mita_forward_ex's timing events; the staged
 schedule runs routing and grouping on a side stream, which the binding owns and
 passes in, beside the landmark pass):
 a step's time is first event to last, a kernel's time the interval from its
-start event to its end; ms_per_step is the mean step time.  A warm (no flush) figure is reported
-beside it unless --no-warm.
+start event to its end; ms_per_step is the mean step time (median and p10/p90
+beside it).  Where a schedule forks onto the side stream, the same cold steps
+are also timed with every kernel on one stream (one_stream_*).  A warm (no
+flush) figure is reported beside it unless --no-warm.  Defaults: 100 timed
+steps after 20 warm-up steps.
 
 Prints ONE JSON line.  ``value`` is query-heads per second (B*H*N per step)
 on the headline workload (DeiT-S shape); the 3136-token workload is reported
@@ -147,9 +150,12 @@ class Runner:
                                               overlap=True)
         self.kernels = [nm for nm, _ in self.sched]
 
+        self.overlap = True
+
     def step(self, events=None):
         self.mita.mita_forward_ex(self.q, self.k, self.v, *self.args, out=self.out,
-                                  workspace=self.ws, path=self.path, events=events, overlap=True)
+                                  workspace=self.ws, path=self.path, events=events,
+                                  overlap=self.overlap)
 
     def flush(self):
         # a read of 512 MiB evicts L2 and the Infinity Cache with clean lines; a write
@@ -180,6 +186,29 @@ class Runner:
                for i, (name, st) in enumerate(self.sched)}
         return sum(ms) / len(ms), ms, per
 
+    def timed_one_stream(self, n):
+        """The same cold steps with every kernel on the caller's stream (no side stream);
+        returns the mean and median step time (ms)."""
+        torch = self.torch
+        self.overlap = False
+        try:
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+            for _ in range(3):
+                self.flush()
+                self.step()
+            torch.cuda.synchronize()
+            for e0, e1 in evs:
+                self.flush()
+                e0.record()
+                self.step()
+                e1.record()
+            torch.cuda.synchronize()
+        finally:
+            self.overlap = True
+        ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
+        return sum(ms) / n, ms[n // 2]
+
 
 def measure(name, steps, warmup, path="auto", warm=True):
     import torch
@@ -197,6 +226,12 @@ def measure(name, steps, warmup, path="auto", warm=True):
     warm_ms = None
     if warm:
         warm_ms, _, _ = r.timed(steps, flush=False)
+    one_stream = None
+    if any(st != i for i, (_, st) in enumerate(r.sched)):
+        # the staged schedule forks routing and grouping onto a side stream: time the
+        # single-stream form too (torch events around the call on the caller's stream)
+        one_stream = r.timed_one_stream(steps)
+        log(f"{name}: one stream {one_stream[0] * 1e3:.1f} us/step (median {one_stream[1] * 1e3:.1f})")
     log(f"{name}: cold {cold_ms * 1e3:.1f} us/step"
         + (f", warm {warm_ms * 1e3:.1f} us/step" if warm_ms else ""))
     qh = alg["qh"]
@@ -223,6 +258,7 @@ def measure(name, steps, warmup, path="auto", warm=True):
         stage_us={k: v * 1e3 for k, v in stages.items()},
         kernel_gbs={k: alg["kernel_bytes"][k] / (v * 1e-3) / 1e9 for k, v in stages.items()},
         schedule=sched, dtype=w["dtype"],
+        one_stream_ms=one_stream,
     )
     return r, res
 
@@ -305,8 +341,8 @@ def main():
         return
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="deit-s")
     ap.add_argument("--also", default="hires-3136", help="second workload ('' to skip)")
     ap.add_argument("--path", default="auto", choices=["auto", "fused", "staged"])
@@ -351,6 +387,8 @@ def main():
             "ms_p10": res2["ms_p10"], "ms_p90": res2["ms_p90"],
             "warm_ms_per_step": res2["warm_ms_per_step"],
             "streams": "routing and grouping on a side stream beside the landmark pass",
+            "one_stream_ms_per_step": res2["one_stream_ms"][0] if res2["one_stream_ms"] else None,
+            "one_stream_ms_median": res2["one_stream_ms"][1] if res2["one_stream_ms"] else None,
             "roofline": res2["roofline"], "pass_roofline": res2["pass_roofline"],
             "stage_us": res2["stage_us"], "kernel_gbs": res2["kernel_gbs"],
             "schedule": res2["schedule"], "dtype": res2["dtype"],

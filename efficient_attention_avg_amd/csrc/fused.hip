@@ -45,6 +45,9 @@ constexpr int MMAX = 32, KMAX = 32;
 constexpr int VT_STRIDE = 464;      // bytes per V^T row (f16 keys)
 constexpr int S_STRIDE = 212;       // floats per score row
 constexpr int H_STRIDE = 528;       // bytes per histogram / P row
+constexpr int BLIST = 16;           // boundary-bin entries ranked through a list
+constexpr int TBM_WORDS = (16 * MAXNT + 63) / 32;  // key bitmap words (+1 for a 2-word read)
+static_assert(8 * BLIST + 4 * TBM_WORDS <= 512, "list and bitmap fit in a histogram row");
 constexpr int VLT_STRIDE = 80;      // bytes per V_L^T row (f16 landmarks)
 
 constexpr int X_BYTES = 64 * VT_STRIDE > MMAX * S_STRIDE * 4 ? 64 * VT_STRIDE : MMAX * S_STRIDE * 4;
@@ -521,7 +524,54 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
           take |= bnd;
           need = 0;
         }
-        if (__ballot(need > 0) != 0) {
+        if (__ballot(need > 0 && inb > BLIST) == 0) {
+          // every boundary bin of the wave fits a BLIST-entry list: the bin's
+          // keys are listed in the row's spent histogram, lane t ranks entry t
+          // against the list (larger score first, then lower key id), and the
+          // entries ranked below `need` are marked in a key bitmap from which
+          // each lane takes its own bits
+          float* lst_v = reinterpret_cast<float*>(hrow);
+          int* lst_k = reinterpret_cast<int*>(hrow + 4 * BLIST);
+          uint32_t* tbm = reinterpret_cast<uint32_t*>(hrow + 8 * BLIST);
+          const bool sel = need > 0;
+          const int nbl = sel ? __popc(bnd) : 0;
+          int p = g16_prefix_sum(nbl) - nbl;
+          // (the histogram has been read: its row now takes the list)
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          // scores re-read from the score rows by key (a lane holds one or two)
+          // (the group's bnd bits number exactly inb <= BLIST; the bound on p
+          // keeps the writes inside the list regardless)
+          for (uint32_t bb = sel ? bnd : 0u; bb != 0u && p < BLIST; bb &= bb - 1u, ++p) {
+            const int key = key0 + __builtin_ctz(bb);
+            lst_v[p] = *lds<float>(sm, OFF_X + (i * S_STRIDE + key) * 4);
+            lst_k[p] = key;
+          }
+          if (t < TBM_WORDS) tbm[t] = 0u;
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          if (sel && t < inb) {
+            const float ev = lst_v[t];
+            const int ek = lst_k[t];
+            int r = 0;
+            for (int j = 0; j < inb; ++j) {
+              const float jv = lst_v[j];
+              r += (jv > ev || (jv == ev && lst_k[j] < ek)) ? 1 : 0;
+            }
+            if (r < need) atomicOr(tbm + (ek >> 5), 1u << (ek & 31));
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          if (sel) {
+            const int w0 = key0 >> 5;
+            const uint64_t two = (uint64_t)tbm[w0] | ((uint64_t)tbm[w0 + 1] << 32);
+            take |= (uint32_t)(two >> (key0 & 31)) & ((1u << MAXNT) - 1u);
+          }
+          need = 0;
+        } else if (__ballot(need > 0) != 0) {
           // each lane's best boundary candidate (descending scan: ties keep the
           // lower key); a lane rescans only after its candidate is taken and
           // it holds more
