@@ -356,19 +356,45 @@ __device__ void row_final(char* sm, const Args& a, int lr, bool work, int t, int
       if (e < cnt && (take >> u & 1u)) atomicOr(&bm[keys[e] >> 5], 1u << (keys[e] & 31));
     }
     group_sync();
-    const int wpl = (nw + 15) >> 4;
-    const int q0 = t * wpl, q1 = min(nw, q0 + wpl);
-    int mine = 0;
-    for (int q = q0; q < q1; ++q) mine += __popc(bm[q]);
-    int pos = g16_addi(mine) - g16_suffix(mine);
-    if (work) {
-      for (int q = q0; q < q1; ++q) {
-        uint32_t wbits = bm[q];
-        while (wbits) {
-          const int b = __ffs(wbits) - 1;
-          wbits &= wbits - 1u;
-          if (pos < a.k) out[pos] = 32 * q + b;
-          ++pos;
+    if (nw * 6 <= HIST_STRIDE) {
+      // taken keys before each bitmap word (16-bit, after the bitmap), lane t
+      // taking words t, t + 16, ...; then every taken entry writes its own
+      // slot: the taken keys before its word plus those below it in the word
+      uint16_t* wpre = reinterpret_cast<uint16_t*>(bm + nw);
+      int run = 0;
+      for (int r0 = 0; r0 < nw; r0 += 16) {
+        const int q = r0 + t;
+        const int c = q < nw ? __popc(bm[q]) : 0;
+        const int tot = g16_addi(c);
+        if (q < nw) wpre[q] = (uint16_t)(run + tot - g16_suffix(c));
+        run += tot;
+      }
+      group_sync();
+      if (work) {
+        for (int u = 0; 16 * u < cnt; ++u) {
+          const int e = t + 16 * u;
+          if (e < cnt && (take >> u & 1u)) {
+            const int key = keys[e], wq = key >> 5;
+            const int pos = wpre[wq] + __popc(bm[wq] & ((1u << (key & 31)) - 1u));
+            if (pos < a.k) out[pos] = key;
+          }
+        }
+      }
+    } else {
+      const int wpl = (nw + 15) >> 4;
+      const int q0 = t * wpl, q1 = min(nw, q0 + wpl);
+      int mine = 0;
+      for (int q = q0; q < q1; ++q) mine += __popc(bm[q]);
+      int pos = g16_addi(mine) - g16_suffix(mine);
+      if (work) {
+        for (int q = q0; q < q1; ++q) {
+          uint32_t wbits = bm[q];
+          while (wbits) {
+            const int b = __ffs(wbits) - 1;
+            wbits &= wbits - 1u;
+            if (pos < a.k) out[pos] = 32 * q + b;
+            ++pos;
+          }
         }
       }
     }
