@@ -73,7 +73,58 @@ def test_small_shapes(case):
     _say(f"ok {rep}")
 
 
-FUSED = [
+def _random_shapes(n, seed):
+    """Seeded random configurations across the implementation's ranges: grids up
+    to 64 on a side, landmark grids up to 16x16, k from 1 to min(N, 300), both
+    input types (fp32 at small sizes), smooth or plain inputs."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        gh, gw = (int(x) for x in rng.integers(1, 65, size=2))
+        mh, mw = int(rng.integers(1, min(gh, 16) + 1)), int(rng.integers(1, min(gw, 16) + 1))
+        N = gh * gw
+        k = int(rng.integers(1, min(N, 300) + 1))
+        dtype = "f32" if N <= 1024 and rng.random() < 0.3 else "bf16"
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        out.append((B, H, gh, gw, mh, mw, k, dtype, bool(rng.random() < 0.7)))
+    return out
+
+
+RANDOM = _random_shapes(16, 2024)
+
+
+def _random_fused_shapes(n, seed):
+    """Seeded random configurations inside the single-kernel schedule's range
+    (N <= 208, m <= 32, k <= 32, bf16)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        gh, gw = (int(x) for x in rng.integers(1, 17, size=2))
+        if gh * gw > 208:
+            continue
+        mh, mw = int(rng.integers(1, gh + 1)), int(rng.integers(1, gw + 1))
+        if mh * mw > 32:
+            continue
+        k = int(rng.integers(1, min(gh * gw, 32) + 1))
+        out.append((int(rng.integers(1, 4)), int(rng.integers(1, 4)), gh, gw, mh, mw, k))
+    return out
+
+
+RANDOM_FUSED = _random_fused_shapes(12, 77)
+
+
+@pytest.mark.parametrize("case", RANDOM, ids=lambda c: "x".join(map(str, c[:7])) + "-" + c[7])
+def test_random_shapes(case):
+    B, H, gh, gw, mh, mw, k, dtype, smooth = case
+    _say(f"random shape {case}")
+    Q, K, V = synth.make_qkv(B, H, gh, gw, 64, workload_id=500 + gh * 67 + gw, smooth=smooth,
+                             dtype=dtype)
+    res = run_gpu(Q, K, V, dtype, gh, gw, mh, mw, k)
+    rep = parity.run_and_check(res, Q, K, V, gh, gw, mh, mw, k, TOL[dtype])
+    _say(f"ok {rep}")
+
+
+FUSED = RANDOM_FUSED + [
     # B, H, gh, gw, mh, mw, k: shapes the single-kernel schedule accepts
     (2, 3, 14, 14, 5, 5, 25),   # DeiT shape
     (2, 2, 13, 16, 8, 4, 32),   # largest N, m and k it takes
