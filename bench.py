@@ -24,6 +24,9 @@ steps after 20 warm-up steps.
 Prints ONE JSON line.  ``value`` is query-heads per second (B*H*N per step)
 on the headline workload (DeiT-S shape); the 3136-token workload is reported
 in ``secondary``.  ``roofline`` covers the kernel that dominates the step;
+``kernel_gbs`` gives every kernel's algorithmic bytes per second and
+``kernel_mfma`` the contraction kernels' algorithmic matrix flops per second
+against the dense bf16 MFMA peak (2.5 PFLOP/s);
 ``cpu_baseline`` is the fp64 oracle timed on a bounded sample on this host.
 """
 from __future__ import annotations
@@ -39,6 +42,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MiTA fwd query-heads/sec (DeiT-S, 3136-tok); fraction of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0  # dense bf16
 FLUSH_BYTES = 512 << 20
 
 
@@ -117,8 +121,20 @@ def algorithmic(w):
         "attend": BH * (N * d * s_in + 2 * m * k * d * s_in + 2 * m * d * 4 + m * k * 4
                         + N * 4 + N * d * 4),
     }
+    # matrix flops each kernel must do (multiply-adds x 2; no hi/lo duplicates)
+    flops = {
+        "fused": BH * N * 4 * d * (2 * m + k),
+        "pool": 0,
+        # S = Q_L K^T and V_L = P V
+        "landmark": BH * 4 * m * N * d,
+        # R = Q Q_L^T
+        "route": BH * 2 * N * m * d,
+        "group": 0,
+        # shared logits and P V_L, routed logits and P V_e
+        "attend": BH * 4 * N * d * (m + k),
+    }
     return dict(bytes_per_qh=per_qh, flops_per_qh=4 * d * (2 * m + k), kernel_bytes=kern,
-                qh=BH * N)
+                kernel_flops=flops, qh=BH * N)
 
 
 class Runner:
@@ -257,6 +273,11 @@ def measure(name, steps, warmup, path="auto", warm=True):
                            flops_per_qh=alg["flops_per_qh"]),
         stage_us={k: v * 1e3 for k, v in stages.items()},
         kernel_gbs={k: alg["kernel_bytes"][k] / (v * 1e-3) / 1e9 for k, v in stages.items()},
+        # MFMA utilisation of the contraction kernels: algorithmic flops / time against
+        # the dense bf16 peak
+        kernel_mfma={k: dict(tflops=alg["kernel_flops"][k] / (v * 1e-3) / 1e12,
+                             frac=alg["kernel_flops"][k] / (v * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS)
+                     for k, v in stages.items() if alg["kernel_flops"].get(k)},
         schedule=sched, dtype=w["dtype"],
         one_stream_ms=one_stream,
     )
@@ -391,6 +412,7 @@ def main():
             "one_stream_ms_median": res2["one_stream_ms"][1] if res2["one_stream_ms"] else None,
             "roofline": res2["roofline"], "pass_roofline": res2["pass_roofline"],
             "stage_us": res2["stage_us"], "kernel_gbs": res2["kernel_gbs"],
+            "kernel_mfma": res2["kernel_mfma"],
             "schedule": res2["schedule"], "dtype": res2["dtype"],
         }
     w = main_res["workload"]
@@ -409,6 +431,7 @@ def main():
         "warm_ms_per_step": main_res["warm_ms_per_step"], "warm_value": main_res["warm_value"],
         "roofline": main_res["roofline"], "pass_roofline": main_res["pass_roofline"],
         "stage_us": main_res["stage_us"], "kernel_gbs": main_res["kernel_gbs"],
+        "kernel_mfma": main_res["kernel_mfma"],
         "cpu_baseline": cpu, "secondary": secondary,
         "library": mita.lib().mita_version().decode(),
     }
