@@ -175,17 +175,28 @@ __device__ __forceinline__ void ql_slot_store(char* sm, int tl, int lane, const 
   }
 }
 
+// This lane's Q_L B operands of both tiles, read back from its LDS slots into
+// registers for the length of one pass.
+struct QLRegs {
+  u32x4 h[TL][2], l[TL][2];
+};
+__device__ __forceinline__ void ql_load(QLRegs& q, const char* sm, int lane) {
+#pragma unroll
+  for (int tl = 0; tl < TL; ++tl)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      q.h[tl][ks] = *reinterpret_cast<const u32x4*>(sm + OFF_QL + (((tl * 2 + ks) * 2 + 0) * 64 + lane) * 16);
+      q.l[tl][ks] = *reinterpret_cast<const u32x4*>(sm + OFF_QL + (((tl * 2 + ks) * 2 + 1) * 64 + lane) * 16);
+    }
+}
+
 // Raw scores of one block: lane holds key 64blk + 16kt + 4g + r of row c16.
 // Every phase computes them with this same sequence, so a score is
 // bit-identical wherever it is recomputed.
-__device__ __forceinline__ void block_scores(const KRegs& kr, const char* sm, int tl, int lane,
+__device__ __forceinline__ void block_scores(const KRegs& kr, const QLRegs& q, int tl,
                                              float (&s)[4][4]) {
-  u32x4 bqh[2], bql[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    bqh[ks] = *reinterpret_cast<const u32x4*>(sm + OFF_QL + (((tl * 2 + ks) * 2 + 0) * 64 + lane) * 16);
-    bql[ks] = *reinterpret_cast<const u32x4*>(sm + OFF_QL + (((tl * 2 + ks) * 2 + 1) * 64 + lane) * 16);
-  }
+  const u32x4 (&bqh)[2] = q.h[tl];
+  const u32x4 (&bql)[2] = q.l[tl];
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) {
     f32x4 c = zero4();
@@ -481,6 +492,8 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
       for (int ct = 0; ct < 4; ++ct) accv[tl][ct] = zero4();
     }
     const u32x4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+    QLRegs qlr;
+    ql_load(qlr, sm, lane);  // (this lane's own slots: no barrier needed)
     KRegs kr;
     VRegs vr;
     if (w < nblk) {
@@ -493,12 +506,25 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
       store_vt(vr, vt, lane);
       if (blk + NW < nblk) load_v(vr, Vh, blk + NW, N, lane);
       group_sync();
+      // the block's V^T A operands, shared by both row tiles:
+      // V^T[channel 16ct + c16][keys 32sp + 4g .., 32sp + 16 + 4g ..]
+      u32x4 av[4][2];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const char* vrow = vt + (16 * ct + c16) * VT_STRIDE;
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+          const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vrow + (32 * sp + 4 * g) * 2);
+          const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vrow + (32 * sp + 16 + 4 * g) * 2);
+          av[ct][sp] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+        }
+      }
       const bool last = ragged && blk == nblk - 1;
       // one tile at a time keeps one tile's scores and weights live
 #pragma unroll
       for (int tl = 0; tl < TL; ++tl) {
         float s[4][4];
-        block_scores(kr, sm, tl, lane, s);
+        block_scores(kr, qlr, tl, s);
         if (tl == TL - 1 && blk + NW < nblk) load_k(kr, Kh, blk + NW, N, g, c16);
         if (last) {
 #pragma unroll
@@ -548,14 +574,9 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
         }
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-          const char* vrow = vt + (16 * ct + c16) * VT_STRIDE;
           f32x4 acc = accv[tl][ct];
 #pragma unroll
-          for (int sp = 0; sp < 2; ++sp) {
-            const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vrow + (32 * sp + 4 * g) * 2);
-            const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vrow + (32 * sp + 16 + 4 * g) * 2);
-            acc = mfma_f16(u32x4{lo2[0], lo2[1], hi2[0], hi2[1]}, bp[sp], acc);
-          }
+          for (int sp = 0; sp < 2; ++sp) acc = mfma_f16(av[ct][sp], bp[sp], acc);
           accv[tl][ct] = acc;
         }
         lsum[tl] = mfma_f16(ones, bp[0], lsum[tl]);
@@ -640,13 +661,15 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
 
   // ------------------------------------------------------------ H: histogram
   {
+    QLRegs qlr;
+    ql_load(qlr, sm, lane);
     KRegs kr = kpre;
     for (int blk = w; blk < nblk; blk += NW) {
       const bool last = ragged && blk == nblk - 1;
 #pragma unroll
       for (int tl = 0; tl < TL; ++tl) {
         float s[4][4];
-        block_scores(kr, sm, tl, lane, s);
+        block_scores(kr, qlr, tl, s);
         if (tl == TL - 1 && blk + NW < nblk) load_k(kr, Kh, blk + NW, N, g, c16);
         uint32_t* myhist =
             reinterpret_cast<uint32_t*>(sm + OFF_HIST + (16 * tl + c16) * HIST_STRIDE);
@@ -723,6 +746,8 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
 
   // ------------------------------------------------------------ C: collect
   {
+    QLRegs qlr;
+    ql_load(qlr, sm, lane);
     float bthr[TL];
 #pragma unroll
     for (int tl = 0; tl < TL; ++tl) bthr[tl] = rows[16 * tl + c16].bthr;
@@ -744,18 +769,13 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
           msk |= (q ? 1u : 0u) << (4 * kt + r);
         }
       if (__ballot(msk != 0u) == 0) return;
-      // the row's four lanes (g = 0..3) take consecutive slots
+      // each lane reserves its own run of slots (the order of entries in a
+      // row's buffer does not matter: they are ranked by score and key id)
       const int c = __popc(msk);
-      const int c0 = __shfl(c, c16, 64), c1 = __shfl(c, c16 + 16, 64);
-      const int c2 = __shfl(c, c16 + 32, 64), c3 = __shfl(c, c16 + 48, 64);
-      const int total = c0 + c1 + c2 + c3;
-      const int pre = (g > 0 ? c0 : 0) + (g > 1 ? c1 : 0) + (g > 2 ? c2 : 0);
-      int base = 0;
-      if (g == 0 && total > 0) base = atomicAdd(&rows[lr].cnt, total);
-      base = __shfl(base, c16, 64);
+      int pos = 0;
+      if (c > 0) pos = atomicAdd(&rows[lr].cnt, c);
       float* vals = reinterpret_cast<float*>(sm + OFF_UNION + (size_t)lr * a.cap * 8);
       int* keys = reinterpret_cast<int*>(vals + a.cap);
-      int pos = base + pre;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -774,7 +794,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
 #pragma unroll
         for (int tl = 0; tl < TL; ++tl) {
           float s[4][4];
-          block_scores(kr, sm, tl, lane, s);
+          block_scores(kr, qlr, tl, s);
           if (tl == TL - 1 && blk + NW < nblk) load_k(kr, Kh, blk + NW, N, g, c16);
           collect(s, tl, blk, last, false, 0.f, 0);
         }
@@ -790,7 +810,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
 #pragma unroll
           for (int tl = 0; tl < TL; ++tl) {
             float s[4][4];
-            block_scores(kr, sm, tl, lane, s);
+            block_scores(kr, qlr, tl, s);
             const int lr = 16 * tl + c16;
             collect(s, tl, blk, last, true, rows[lr].thr, rows[lr].thrkey);
           }
