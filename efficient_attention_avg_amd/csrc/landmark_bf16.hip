@@ -36,6 +36,8 @@
 #include "mfma.h"
 #include "select.h"
 
+#include <type_traits>
+
 namespace mita {
 namespace lmk {
 
@@ -46,6 +48,7 @@ constexpr int ROWS = 16 * TL;           // landmark rows per workgroup
 constexpr int VT_STRIDE = KB * 2 + 16;  // bytes per V^T row: 64 f16 keys + pad
 constexpr int VT_BYTES = 64 * VT_STRIDE;
 constexpr int HIST_STRIDE = 1040;       // one row's 256 32-bit bins + pad (rows 4 banks apart)
+constexpr int SPARE_BIN = 256;          // pad word: counts the keys past N of a ragged block
 constexpr int BITMAP_MAX_N = 8192;      // keys whose bitmap fits in a histogram row
 constexpr int LIST_MAX = 128;           // boundary entries listed in a histogram row
 constexpr int MERGE_STRIDE = 68;        // floats per (wave, row): 64 acc, max, sum, min, max
@@ -72,6 +75,7 @@ constexpr int OFF_UNION = OFF_QL + TL * 2 * 2 * 64 * 16;
 constexpr int VALUES_BYTES = NW * VT_BYTES;  // phase V staging (the merge area aliases it)
 static_assert(NW * ROWS * MERGE_STRIDE * 4 <= VALUES_BYTES, "merge area fits in the staging");
 static_assert(BITMAP_MAX_N / 8 <= HIST_STRIDE && LIST_MAX * 8 <= HIST_STRIDE, "row space");
+static_assert((SPARE_BIN + 1) * 4 <= HIST_STRIDE, "the spare counter sits in the row's pad");
 
 struct Args {
   const float* ql;
@@ -665,7 +669,15 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
     ql_load(qlr, sm, lane);
     KRegs kr = kpre;
     for (int blk = w; blk < nblk; blk += NW) {
-      const bool last = ragged && blk == nblk - 1;
+      // keys past N of a ragged last block count into the spare word past
+      // the 256 bins (no branch per score)
+      uint32_t spare = 0u;
+      if (ragged && blk == nblk - 1) {
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) spare |= (key_of(blk, kt, g, r) < N ? 0u : 1u) << (4 * kt + r);
+      }
 #pragma unroll
       for (int tl = 0; tl < TL; ++tl) {
         float s[4][4];
@@ -676,9 +688,10 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (!last || key_of(blk, kt, g, r) < N)
-              atomicAdd(myhist + bin_of(s[kt][r], A[tl], B[tl]), 1u);
+          for (int r = 0; r < 4; ++r) {
+            const int bin = bin_of(s[kt][r], A[tl], B[tl]);
+            atomicAdd(myhist + ((spare >> (4 * kt + r) & 1u) ? SPARE_BIN : bin), 1u);
+          }
       }
     }
   }
@@ -753,21 +766,36 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
     for (int tl = 0; tl < TL; ++tl) bthr[tl] = rows[16 * tl + c16].bthr;
     // appends the block's scores of tile tl that are in the boundary bin or
     // above (and, when bounded, beat the admission bound (thr, thrkey))
-    auto collect = [&](const float (&s)[4][4], int tl, int blk, bool last, bool bounded,
+    // the bits (4kt + r) of this lane's keys of block blk that lie below N
+    auto valid_bits = [&](int blk) {
+      uint32_t vb = 0u;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vb |= (key_of(blk, kt, g, r) < N ? 1u : 0u) << (4 * kt + r);
+      return vb;
+    };
+    // appends the block's scores of tile tl that are in the boundary bin or
+    // above (and, with BOUNDED, beat the admission bound (thr, thrkey));
+    // `valid` masks the keys past N of a ragged last block
+    auto collect = [&](auto bounded, const float (&s)[4][4], int tl, int blk, uint32_t valid,
                        float thr, int thrkey) {
+      constexpr bool BOUNDED = decltype(bounded)::value;
       const int lr = 16 * tl + c16;
       uint32_t msk = 0u;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int key = key_of(blk, kt, g, r);
           const float v = s[kt][r];
           bool q = __builtin_fmaf(v, A[tl], B[tl]) >= bthr[tl];
-          if (last) q = q && key < N;
-          if (bounded) q = q && (v > thr || (v == thr && key < thrkey));
+          if constexpr (BOUNDED) {
+            const int key = key_of(blk, kt, g, r);
+            q = q && (v > thr || (v == thr && key < thrkey));
+          }
           msk |= (q ? 1u : 0u) << (4 * kt + r);
         }
+      msk &= valid;
       if (__ballot(msk != 0u) == 0) return;
       // each lane reserves its own run of slots (the order of entries in a
       // row's buffer does not matter: they are ranked by score and key id)
@@ -790,13 +818,13 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
       // every row's candidates fit: one streaming pass
       KRegs kr = kpre;
       for (int blk = w; blk < nblk; blk += NW) {
-        const bool last = ragged && blk == nblk - 1;
+        const uint32_t valid = ragged && blk == nblk - 1 ? valid_bits(blk) : 0xFFFFu;
 #pragma unroll
         for (int tl = 0; tl < TL; ++tl) {
           float s[4][4];
           block_scores(kr, qlr, tl, s);
           if (tl == TL - 1 && blk + NW < nblk) load_k(kr, Kh, blk + NW, N, g, c16);
-          collect(s, tl, blk, last, false, 0.f, 0);
+          collect(std::false_type{}, s, tl, blk, valid, 0.f, 0);
         }
       }
     } else {
@@ -804,7 +832,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
       // row); rows that could overflow on the next block are cut back first
       for (int blk = 0; blk < nblk; ++blk) {
         if (blk % NW == w) {
-          const bool last = ragged && blk == nblk - 1;
+          const uint32_t valid = ragged && blk == nblk - 1 ? valid_bits(blk) : 0xFFFFu;
           KRegs kr;
           load_k(kr, Kh, blk, N, g, c16);
 #pragma unroll
@@ -812,7 +840,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
             float s[4][4];
             block_scores(kr, qlr, tl, s);
             const int lr = 16 * tl + c16;
-            collect(s, tl, blk, last, true, rows[lr].thr, rows[lr].thrkey);
+            collect(std::true_type{}, s, tl, blk, valid, rows[lr].thr, rows[lr].thrkey);
           }
         }
         __syncthreads();
