@@ -10,16 +10,18 @@ of synthetic, seeded inputs already resident in device memory.  Before every
 timed step a 512 MiB buffer is read (summed) so that neither L2 nor the 256 MB
 Infinity Cache holds the inputs (the DeiT-S inputs would otherwise fit in
 it); a read leaves clean lines, so the first kernel does not share HBM with
-the write-back of a flush buffer.  The library records HIP events before its
-first kernel and after each kernel (mita_forward_ex's timing events; the staged
-schedule runs routing and grouping on a side stream, which the binding owns and
-passes in, beside the landmark pass):
-a step's time is first event to last, a kernel's time the interval from its
-start event to its end; ms_per_step is the mean step time (median and p10/p90
-beside it).  Where a schedule forks onto the side stream, the same cold steps
-are also timed with every kernel on one stream (one_stream_*).  A warm (no
-flush) figure is reported beside it unless --no-warm.  Defaults: 100 timed
-steps after 20 warm-up steps.
+the write-back of a flush buffer.  A step is timed by HIP events on the
+caller's stream right before and after the call (the staged schedule runs
+routing and grouping on a side stream, which the binding owns and passes in,
+beside the landmark pass, and joins it back before attention); ms_per_step is
+the mean step time (median and p10/p90 beside it).  A second cold series runs
+with the library's per-kernel events (mita_forward_ex records one before its
+first kernel and one after each): a kernel's time is the interval from its
+start event to its end (stage_us), and that series' mean step time is
+instrumented_ms_per_step.  Where a schedule forks onto the side stream, the
+same cold steps are also timed with every kernel on one stream (one_stream_*).
+A warm (no flush) figure is reported beside it unless --no-warm.  Defaults:
+100 timed steps after 20 warm-up steps.
 
 Prints ONE JSON line.  ``value`` is query-heads per second (B*H*N per step)
 on the headline workload (DeiT-S shape); the 3136-token workload is reported
@@ -179,12 +181,37 @@ class Runner:
         # the first kernel's reads
         self.flush_sink += self.flush_f32.sum()
 
+    def timed_calls(self, n, flush=True, overlap=True):
+        """n steps, optionally flushing the caches before each, timed by HIP events on the
+        caller's stream right before and after each call (nothing recorded between the
+        kernels).  Returns the mean step time (ms) and every step's time."""
+        torch = self.torch
+        self.overlap = overlap
+        try:
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+            for e0, e1 in evs:
+                e0.record()  # creates the HIP events before the timed steps
+                e1.record()
+            torch.cuda.synchronize()
+            for e0, e1 in evs:
+                if flush:
+                    self.flush()
+                e0.record()
+                self.step()
+                e1.record()
+            torch.cuda.synchronize()
+        finally:
+            self.overlap = True
+        ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+        return sum(ms) / n, ms
+
     def timed(self, n, flush=True):
-        """n steps, optionally flushing the caches before each.  The library records an event
-        before its first kernel and after each kernel (the staged schedule's routing and
-        grouping on its side stream); a step's time is first event to last, each kernel's
-        time the interval from its start event (mita_kernel_schedule) to its own end.
-        Returns the mean step time (ms), every step's time, and each kernel's mean time (ms)."""
+        """n steps, optionally flushing the caches before each, with the library's per-kernel
+        events: it records one before its first kernel and one after each kernel (the staged
+        schedule's routing and grouping on its side stream); each kernel's time is the
+        interval from its start event (mita_kernel_schedule) to its own end.  Returns the
+        mean instrumented step time (ms), every step's time, and each kernel's mean time (ms)."""
         torch = self.torch
         kevs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(self.kernels) + 1)]
                 for _ in range(n)]
@@ -202,29 +229,6 @@ class Runner:
                for i, (name, st) in enumerate(self.sched)}
         return sum(ms) / len(ms), ms, per
 
-    def timed_one_stream(self, n):
-        """The same cold steps with every kernel on the caller's stream (no side stream);
-        returns the mean and median step time (ms)."""
-        torch = self.torch
-        self.overlap = False
-        try:
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(n)]
-            for _ in range(3):
-                self.flush()
-                self.step()
-            torch.cuda.synchronize()
-            for e0, e1 in evs:
-                self.flush()
-                e0.record()
-                self.step()
-                e1.record()
-            torch.cuda.synchronize()
-        finally:
-            self.overlap = True
-        ms = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
-        return sum(ms) / n, ms[n // 2]
-
 
 def measure(name, steps, warmup, path="auto", warm=True):
     import torch
@@ -236,18 +240,23 @@ def measure(name, steps, warmup, path="auto", warm=True):
         r.step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    cold_ms, cold_all, stages = r.timed(steps, flush=True)
+    cold_ms, cold_all = r.timed_calls(steps, flush=True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the per-kernel breakdown comes from a second cold series with the library's
+    # per-kernel events (which add a little time of their own)
+    inst_ms, _, stages = r.timed(steps, flush=True)
     warm_ms = None
     if warm:
-        warm_ms, _, _ = r.timed(steps, flush=False)
+        warm_ms, _ = r.timed_calls(steps, flush=False)
     one_stream = None
     if any(st != i for i, (_, st) in enumerate(r.sched)):
         # the staged schedule forks routing and grouping onto a side stream: time the
-        # single-stream form too (torch events around the call on the caller's stream)
-        one_stream = r.timed_one_stream(steps)
+        # single-stream form too
+        os_ms, os_all = r.timed_calls(steps, flush=True, overlap=False)
+        one_stream = (os_ms, sorted(os_all)[steps // 2])
         log(f"{name}: one stream {one_stream[0] * 1e3:.1f} us/step (median {one_stream[1] * 1e3:.1f})")
+    log(f"{name}: with per-kernel events {inst_ms * 1e3:.1f} us/step")
     log(f"{name}: cold {cold_ms * 1e3:.1f} us/step"
         + (f", warm {warm_ms * 1e3:.1f} us/step" if warm_ms else ""))
     qh = alg["qh"]
@@ -279,7 +288,7 @@ def measure(name, steps, warmup, path="auto", warm=True):
                              frac=alg["kernel_flops"][k] / (v * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS)
                      for k, v in stages.items() if alg["kernel_flops"].get(k)},
         schedule=sched, dtype=w["dtype"],
-        one_stream_ms=one_stream,
+        one_stream_ms=one_stream, instrumented_ms_per_step=inst_ms,
     )
     return r, res
 
@@ -408,6 +417,7 @@ def main():
             "ms_p10": res2["ms_p10"], "ms_p90": res2["ms_p90"],
             "warm_ms_per_step": res2["warm_ms_per_step"],
             "streams": "routing and grouping on a side stream beside the landmark pass",
+            "instrumented_ms_per_step": res2["instrumented_ms_per_step"],
             "one_stream_ms_per_step": res2["one_stream_ms"][0] if res2["one_stream_ms"] else None,
             "one_stream_ms_median": res2["one_stream_ms"][1] if res2["one_stream_ms"] else None,
             "roofline": res2["roofline"], "pass_roofline": res2["pass_roofline"],
@@ -424,11 +434,13 @@ def main():
         "config": {"workload": describe(w), "B": w["B"], "H": w["H"], "seq_len": w["grid_h"] * w["grid_w"],
                    "m": w["m_h"] * w["m_w"], "k": w["k"], "path": args.path,
                    "schedule": main_res["schedule"],
-                   "timing": "HIP events the library records around its kernels, mean over the "
+                   "timing": "HIP events on the caller's stream around each call, mean over the "
                              "timed steps (median and p10/p90 beside it), L2 + Infinity Cache "
-                             "flushed (512 MiB read) before each step"},
+                             "flushed (512 MiB read) before each step; per-kernel times from a "
+                             "second cold series with the library's per-kernel events"},
         "ms_median": main_res["ms_median"], "ms_p10": main_res["ms_p10"], "ms_p90": main_res["ms_p90"],
         "warm_ms_per_step": main_res["warm_ms_per_step"], "warm_value": main_res["warm_value"],
+        "instrumented_ms_per_step": main_res["instrumented_ms_per_step"],
         "roofline": main_res["roofline"], "pass_roofline": main_res["pass_roofline"],
         "stage_us": main_res["stage_us"], "kernel_gbs": main_res["kernel_gbs"],
         "kernel_mfma": main_res["kernel_mfma"],
