@@ -349,13 +349,31 @@ __device__ void row_final(char* sm, const Args& a, int lr, bool work, int t, int
   group_sync();
   uint32_t take = up;
   const int need = a.k - above;
-  for (int u = 0; 16 * u < cnt; ++u) {
-    const int e = t + 16 * u;
-    if (e < cnt && !(up >> u & 1u)) {
-      const float v = vals[e];
-      const int key = keys[e];
-      const int r = listed ? rank_in_list(list, nb, v, key) : rank_in(vals, keys, cnt, v, key) - above;
-      take |= (r < need ? 1u : 0u) << u;
+  const int nw = (a.N + 31) >> 5;
+  // a short list is ranked entry by entry (lane t: entries t and t + 16) and
+  // its winners' keys kept in registers for the bitmap and their slots;
+  // otherwise every buffer entry outside `up` is ranked where it sits
+  const bool short_list = listed && nb <= 32 && a.N <= BITMAP_MAX_N && nw * 6 <= HIST_STRIDE;
+  int win[2] = {-1, -1};
+  if (short_list) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = t + 16 * j;
+      if (i < nb) {
+        const float v = list[2 * i];
+        const int key = __float_as_int(list[2 * i + 1]);
+        if (rank_in_list(list, nb, v, key) < need) win[j] = key;
+      }
+    }
+  } else {
+    for (int u = 0; 16 * u < cnt; ++u) {
+      const int e = t + 16 * u;
+      if (e < cnt && !(up >> u & 1u)) {
+        const float v = vals[e];
+        const int key = keys[e];
+        const int r = listed ? rank_in_list(list, nb, v, key) : rank_in(vals, keys, cnt, v, key) - above;
+        take |= (r < need ? 1u : 0u) << u;
+      }
     }
   }
   group_sync();
@@ -363,13 +381,15 @@ __device__ void row_final(char* sm, const Args& a, int lr, bool work, int t, int
     // bitmap of the taken keys in the row's histogram space; slot = number of
     // taken keys below
     uint32_t* bm = reinterpret_cast<uint32_t*>(list);
-    const int nw = (a.N + 31) >> 5;
     for (int q = t; q < nw; q += 16) bm[q] = 0u;
     group_sync();
     for (int u = 0; 16 * u < cnt; ++u) {
       const int e = t + 16 * u;
       if (e < cnt && (take >> u & 1u)) atomicOr(&bm[keys[e] >> 5], 1u << (keys[e] & 31));
     }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (win[j] >= 0) atomicOr(&bm[win[j] >> 5], 1u << (win[j] & 31));
     group_sync();
     if (nw * 6 <= HIST_STRIDE) {
       // taken keys before each bitmap word (16-bit, after the bitmap), lane t
@@ -386,14 +406,18 @@ __device__ void row_final(char* sm, const Args& a, int lr, bool work, int t, int
       }
       group_sync();
       if (work) {
+        auto emit = [&](int key) {
+          const int wq = key >> 5;
+          const int pos = wpre[wq] + __popc(bm[wq] & ((1u << (key & 31)) - 1u));
+          if (pos < a.k) out[pos] = key;
+        };
         for (int u = 0; 16 * u < cnt; ++u) {
           const int e = t + 16 * u;
-          if (e < cnt && (take >> u & 1u)) {
-            const int key = keys[e], wq = key >> 5;
-            const int pos = wpre[wq] + __popc(bm[wq] & ((1u << (key & 31)) - 1u));
-            if (pos < a.k) out[pos] = key;
-          }
+          if (e < cnt && (take >> u & 1u)) emit(keys[e]);
         }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          if (win[j] >= 0) emit(win[j]);
       }
     } else {
       const int wpl = (nw + 15) >> 4;
