@@ -175,7 +175,7 @@ mita_status mita_pool(const void* Q, int B, int H, int grid_h, int grid_w, int d
  * Landmark pass: scores of ql [B,H,m,d] fp32 against K [B,H,N,d], each row's
  * top-k keys -> idx [B,H,m,k] (ascending), and the row softmax applied to V
  * -> vl [B,H,m,d] fp32.  Needs mita_landmark_workspace_bytes(...) of scratch
- * (0 when the bf16 MFMA kernel serves the shape -- bf16 inputs, k <= 432;
+ * (0 when the bf16 MFMA kernel serves the shape -- bf16 inputs, k <= 400;
  * workspace may then be NULL).
  */
 size_t mita_landmark_workspace_bytes(int B, int H, int N, int d, int m, int k,

@@ -124,6 +124,10 @@ def test_stage_entry_points_validate():
     assert L.mita_landmark(FAKE, FAKE, FAKE, 1, 1, 196, 64, 25, 25, mita.MITA_F32, FAKE, FAKE,
                            FAKE, 4, None) == mita.MITA_ERR_WORKSPACE
     assert L.mita_landmark_workspace_bytes(1, 1, 196, 64, 25, 25, mita.MITA_BF16) == 0
+    # the bf16 MFMA landmark kernel keeps a k + 64 candidate buffer per row in LDS: up to
+    # k = 400; beyond, the scalar kernel and its scratch take over
+    assert L.mita_landmark_workspace_bytes(1, 1, 16384, 64, 256, 400, mita.MITA_BF16) == 0
+    assert L.mita_landmark_workspace_bytes(1, 1, 16384, 64, 256, 401, mita.MITA_BF16) > 0
     assert L.mita_route(FAKE, FAKE, 1, 1, 196, 64, 25, 1, FAKE, FAKE, None, FAKE, FAKE, 1 << 40,
                         None) == mita.MITA_ERR_INVALID_ARG
     assert L.mita_route(FAKE, FAKE, 1, 1, 3136, 64, 49, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 8,
