@@ -58,6 +58,7 @@ SMALL = [
     (3, 1, 5, 5, 2, 2, 1, "bf16", True),      # k = 1
     (1, 1, 1, 1, 1, 1, 1, "f32", False),      # N = 1
     (1, 1, 33, 31, 4, 5, 200, "bf16", True),  # ragged everywhere
+    (1, 2, 24, 24, 4, 4, 450, "bf16", True),  # k past the MFMA landmark kernel's LDS buffers
     (2, 2, 14, 14, 5, 5, 25, "f32", False),
 ]
 
