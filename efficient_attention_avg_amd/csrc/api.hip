@@ -46,6 +46,10 @@ struct Marker {
     if (ev && i < n && ev[i]) hipEventRecord((hipEvent_t)ev[i], st);
     ++i;
   }
+  // records event j out of turn (a kernel enqueued before those listed ahead of it)
+  void mark_at(int j, hipStream_t st) {
+    if (ev && j < n && ev[j]) hipEventRecord((hipEvent_t)ev[j], st);
+  }
 };
 
 mita_status make_shape(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
@@ -255,13 +259,21 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V, int B, 
     if (fork) {
       if ((st = hip_status(hipEventRecord(ef, stream), "fork")) != MITA_OK) return st;
       if ((st = hip_status(hipStreamWaitEvent(rs, ef, 0), "fork")) != MITA_OK) return st;
+      // the landmark pass, the longer branch, is enqueued first so that its
+      // workgroups reach the CUs first and routing fills the rest; its end
+      // event keeps its place after routing's and grouping's in the list
+      if ((st = run_landmark(ql, K, V, idx_p, vl, scratch, s, stream)) != MITA_OK) return st;
+      mk.mark_at(mk.i + 2, stream);
+      if ((st = run_route(Q, ql, route_p, counts, offsets, perm, rscratch, s, rs, &mk)) != MITA_OK)
+        return st;
+      ++mk.i;  // (the landmark event, recorded above)
+      if ((st = hip_status(hipEventRecord(ej, rs), "join")) != MITA_OK) return st;
+      if ((st = hip_status(hipStreamWaitEvent(stream, ej, 0), "join")) != MITA_OK) return st;
+    } else {
+      if ((st = run_route(Q, ql, route_p, counts, offsets, perm, rscratch, s, rs, &mk)) != MITA_OK)
+        return st;
+      if ((st = run_landmark(ql, K, V, idx_p, vl, scratch, s, stream, &mk)) != MITA_OK) return st;
     }
-    if ((st = run_route(Q, ql, route_p, counts, offsets, perm, rscratch, s, rs, &mk)) != MITA_OK)
-      return st;
-    if (fork && (st = hip_status(hipEventRecord(ej, rs), "join")) != MITA_OK) return st;
-    if ((st = run_landmark(ql, K, V, idx_p, vl, scratch, s, stream, &mk)) != MITA_OK) return st;
-    if (fork && (st = hip_status(hipStreamWaitEvent(stream, ej, 0), "join")) != MITA_OK)
-      return st;
   }
   if ((st = run_attend(Q, K, V, ql, vl, idx_p, route_p, offsets, perm, out, s, stream, &mk)) !=
       MITA_OK)
