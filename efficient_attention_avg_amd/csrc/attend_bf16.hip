@@ -52,7 +52,7 @@ struct Args {
 // [q0, count, k key ids, first TQ query ids].
 struct Lay {
   int mp, vlt_stride, ew, ts;
-  int off_qlh, off_qll, off_vlt, off_ke, off_vet, off_tab, bytes;
+  int off_qlh, off_qll, off_vlt, off_ke, off_vet, off_tab, off_elist, bytes;
   __host__ __device__ Lay(int m, int k, int parts) {
     mp = (m + 31) & ~31;
     vlt_stride = mp * 2 + 16;
@@ -64,7 +64,8 @@ struct Lay {
     off_ke = off_vlt + 64 * vlt_stride;
     off_vet = off_ke + EC * 128;
     off_tab = off_vet + 64 * EVT_STRIDE;
-    bytes = off_tab + ew * ts * 4;
+    off_elist = off_tab + ew * ts * 4;
+    bytes = off_elist + (ew + 1) * 4;
   }
 };
 
@@ -134,7 +135,32 @@ void attend_bf16_kernel(Args a) {
   const int bh = xcd + 8 * (slot / a.parts), part = slot % a.parts;
   if (bh >= a.BH || part >= a.m) return;
   const int N = a.N, m = a.m, k = a.k, P = a.parts;
-  const int nexp = (m - part + P - 1) / P;  // this workgroup's experts
+  // The head's experts are dealt to its P workgroups in a snake (0, 1, ..,
+  // P-1, P-1, .., 0, ...) in order of their passes (then queries, then id),
+  // largest first, so that the workgroups' pass totals even out; every
+  // workgroup of the head computes the same deal.
+  int* elist = reinterpret_cast<int*>(sm + L.off_elist);
+  {
+    int* ecnt = reinterpret_cast<int*>(sm + L.off_tab);  // (the table is filled after)
+    for (int e = tid; e < m; e += blockDim.x) ecnt[e] = a.offsets[(size_t)bh * (m + 1) + e + 1] -
+                                                      a.offsets[(size_t)bh * (m + 1) + e];
+    __syncthreads();
+    for (int e = tid; e < m; e += blockDim.x) {
+      const int c = ecnt[e], pc = (c + TQ - 1) / TQ;
+      int rank = 0;
+      for (int e2 = 0; e2 < m; ++e2) {
+        const int c2 = ecnt[e2], p2 = (c2 + TQ - 1) / TQ;
+        rank += (p2 > pc || (p2 == pc && (c2 > c || (c2 == c && e2 < e)))) ? 1 : 0;
+      }
+      const int round = rank / P, pos = rank - round * P;
+      if (((round & 1) ? P - 1 - pos : pos) == part) elist[round] = e;
+    }
+    __syncthreads();
+  }
+  // this workgroup's experts: one per full round, plus one in the last
+  // (partial) round when the deal reaches it there
+  const int full = m / P, rest = m - full * P;
+  const int nexp = full + ((full & 1) ? (part >= P - rest ? 1 : 0) : (part < rest ? 1 : 0));
   const uint16_t* Qh = a.Q + (size_t)bh * N * 64;
   const uint16_t* Kh = a.K + (size_t)bh * N * 64;
   const uint16_t* Vh = a.V + (size_t)bh * N * 64;
@@ -148,7 +174,7 @@ void attend_bf16_kernel(Args a) {
   // ---- the experts' table: query ranges first, then key ids and first
   // query ids with every load of a thread issued before any is used
   if (tid < nexp) {
-    const int e = part + tid * P;
+    const int e = elist[tid];
     const int q0 = offs[e];
     tab[tid * L.ts] = q0;
     tab[tid * L.ts + 1] = offs[e + 1] - q0;
@@ -164,7 +190,7 @@ void attend_bf16_kernel(Args a) {
         const int it = base + 256 * u + tid;
         v[u] = -1;
         if (it < total) {
-          const int j = it / L.ts, o = it - j * L.ts, e = part + j * P;
+          const int j = it / L.ts, o = it - j * L.ts, e = elist[j];
           if (o >= 2 && o < 2 + k) {
             v[u] = idxh[(size_t)e * k + (o - 2)];
           } else if (o >= 2 + k) {
