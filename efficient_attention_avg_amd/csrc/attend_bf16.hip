@@ -120,9 +120,8 @@ __device__ __forceinline__ void store_out(float* outh, const PassOut& o, int g) 
   if (!o.live) return;
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct)
-    *reinterpret_cast<float4*>(outh + (size_t)o.nq * 64 + 16 * ct + 4 * g) =
-        make_float4(o.acc[ct][0] * o.inv, o.acc[ct][1] * o.inv, o.acc[ct][2] * o.inv,
-                    o.acc[ct][3] * o.inv);
+    __builtin_nontemporal_store(o.acc[ct] * o.inv,
+                                reinterpret_cast<f32x4*>(outh + (size_t)o.nq * 64 + 16 * ct + 4 * g));
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))

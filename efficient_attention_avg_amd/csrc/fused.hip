@@ -936,7 +936,7 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
         if (live) {
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct)
-            *reinterpret_cast<f32x4*>(outh + (size_t)qi * 64 + 16 * ct + 4 * g) = acc[ct] * inv;
+            __builtin_nontemporal_store(acc[ct] * inv, reinterpret_cast<f32x4*>(outh + (size_t)qi * 64 + 16 * ct + 4 * g));
         }
       }
     }
