@@ -23,7 +23,7 @@ PATHS = {"auto": 0, "fused": 1, "staged": 2}
 # Every symbol include/mita.h declares.
 EXPORTS = [
     "mita_status_string", "mita_last_error", "mita_version", "mita_workspace_bytes",
-    "mita_schedule", "mita_kernel_names",
+    "mita_schedule", "mita_kernel_names", "mita_sync_event_create",
     "mita_forward", "mita_forward_ex", "mita_pool", "mita_landmark_workspace_bytes",
     "mita_landmark", "mita_route_workspace_bytes", "mita_route", "mita_attend",
 ]
@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.mita_kernel_names.restype = I
         L.mita_kernel_names.argtypes = [I] * 8 + [I, I, I, ctypes.POINTER(ctypes.c_char_p),
                                                  ctypes.POINTER(ctypes.c_int), I]
+        L.mita_sync_event_create.restype = S
+        L.mita_sync_event_create.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         L.mita_forward.restype = S
         L.mita_forward.argtypes = [P, P, P] + [I] * 8 + [I, P, P, P, P, Z, P]
         L.mita_forward_ex.restype = S
@@ -186,6 +188,15 @@ def mita_kernel_names(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code, path="au
 _sides = {}
 
 
+class _SyncEvent:
+    """A fork / join event from mita_sync_event_create (kept for the process)."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        _check(lib().mita_sync_event_create(ctypes.byref(h)))
+        self.cuda_event = h.value
+
+
 def _side(device):
     """This process's side stream and fork/join events for `device` (created once)."""
     import torch
@@ -193,9 +204,7 @@ def _side(device):
     if key not in _sides:
         with torch.cuda.device(device):
             s = torch.cuda.Stream(device=device)
-            f, j = torch.cuda.Event(), torch.cuda.Event()
-            f.record(s)
-            j.record(s)  # creates the HIP events
+            f, j = _SyncEvent(), _SyncEvent()
         _sides[key] = (s, f, j)
     return _sides[key]
 

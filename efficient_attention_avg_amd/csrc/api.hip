@@ -183,6 +183,17 @@ const char* mita_last_error(void) { return g_error.c_str(); }
 
 const char* mita_version(void) { return "mita-gfx950 0.2"; }
 
+mita_status mita_sync_event_create(void** event) {
+  if (!event) return fail(MITA_ERR_INVALID_ARG, "event is required");
+  hipEvent_t e = nullptr;
+  const mita_status st =
+      hip_status(hipEventCreateWithFlags(&e, hipEventDisableTiming | hipEventDisableSystemFence),
+                 "sync event");
+  if (st != MITA_OK) return st;
+  *event = e;
+  return ok();
+}
+
 size_t mita_workspace_bytes(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
                             mita_dtype in_dtype) {
   Shape s;

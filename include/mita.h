@@ -124,6 +124,8 @@ mita_status mita_forward(const void* Q, const void* K, const void* V,
  *           once must not share them.  Without them every kernel goes on
  *           `stream`.  Either way the call is asynchronous with respect to
  *           the host, and work queued on `stream` after it sees every output.
+ *           Events from mita_sync_event_create make the fork and the join
+ *           cheapest.
  */
 typedef struct {
   float* ql;
@@ -145,6 +147,19 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V,
                             float* out, int32_t* idx, int32_t* route,
                             const mita_extras* extras,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Creates a hipEvent_t, on the current device, for mita_extras.fork_event or
+ * join_event: no timing, and a device-scope release when recorded instead of
+ * the default system-scope fence.  Two streams of one device need no more,
+ * and the default fence's cache write-back and invalidation put idle time
+ * between the kernels on either side of each fork and join.  The event
+ * cannot order work with the host or other devices.  Writes the handle to
+ * *event; the caller owns it (hipEventDestroy).  Returns
+ * MITA_ERR_INVALID_ARG for a NULL `event` and MITA_ERR_HIP when the runtime
+ * cannot create the event.
+ */
+mita_status mita_sync_event_create(void** event);
 
 /*
  * The kernels mita_forward_ex launches for this configuration and path, in

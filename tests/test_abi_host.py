@@ -30,6 +30,11 @@ def test_library_exports_every_declared_symbol():
     assert L.mita_route_workspace_bytes(1, 1, 196, 64, 25, mita.MITA_F32) == 0
 
 
+def test_sync_event_needs_a_pointer():
+    # rejected before any runtime call, so this runs without a GPU
+    assert mita.lib().mita_sync_event_create(None) == mita.MITA_ERR_INVALID_ARG
+
+
 def test_status_strings():
     L = mita.lib()
     names = [L.mita_status_string(s).decode() for s in range(5)]

@@ -296,6 +296,42 @@ def test_kernel_timing_events(name, path, overlap):
         assert ev[names.index("group") + 1].elapsed_time(ev[-1]) > 0
 
 
+def test_side_stream_matches_one_stream():
+    """Routing and grouping on the side stream, forked and joined through
+    events from mita_sync_event_create (a device-scope release, no system
+    fence), give the same bits as the one-stream schedule, over calls queued
+    back to back on changing inputs (a stale read across the streams would
+    show as a difference)."""
+    torch = _torch()
+    import efficient_attention_avg_amd as mita
+    w = synth.workload("hires-3136")
+    B, H = 2, w["H"]
+    args = (w["grid_h"], w["grid_w"], w["m_h"], w["m_w"], w["k"])
+    ins = [tuple(_to_dev(x, "bf16") for x in synth.make_qkv(B, H, w["grid_h"], w["grid_w"], 64,
+                                                             workload_id=60 + i))
+           for i in range(3)]
+    _say("side stream against one stream, 3 inputs x 2 rounds")
+    ref = [mita.mita_forward_ex(*qkv, *args, route=True)["out"] for qkv in ins]
+    torch.cuda.synchronize()
+    got = []
+    for _ in range(2):
+        for qkv in ins:
+            got.append(mita.mita_forward_ex(*qkv, *args, route=True, overlap=True))
+    torch.cuda.synchronize()
+    for i, res in enumerate(got):
+        assert torch.equal(res["out"], ref[i % 3]), i
+
+
+def test_sync_event_is_created():
+    torch = _torch()
+    import ctypes
+    import efficient_attention_avg_amd as mita
+    torch.cuda.init()
+    h = ctypes.c_void_p()
+    assert mita.lib().mita_sync_event_create(ctypes.byref(h)) == mita.MITA_OK
+    assert h.value
+
+
 def test_constant_values_give_constant_output():
     import efficient_attention_avg_amd as mita
     torch = _torch()
