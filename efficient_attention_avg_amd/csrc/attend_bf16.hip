@@ -116,12 +116,42 @@ struct PassOut {
   bool live;
 };
 
-__device__ __forceinline__ void store_out(float* outh, const PassOut& o, int g) {
-  if (!o.live) return;
+// Lane c16 <-> c16 ^ 8 of each 16-lane row (DPP row rotate by 8).
+__device__ __forceinline__ int swap8(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);
+}
+__device__ __forceinline__ f32x4 swap8(f32x4 v) {
+  // (element by value: a bit cast applied to the element expression v[i]
+  // itself was compiled as a read of element 0)
+  f32x4 r;
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct)
-    __builtin_nontemporal_store(o.acc[ct] * o.inv,
-                                reinterpret_cast<f32x4*>(outh + (size_t)o.nq * 64 + 16 * ct + 4 * g));
+  for (int i = 0; i < 4; ++i) r[i] = __int_as_float(swap8(__float_as_int(v[i])));
+  return r;
+}
+
+// The pass's output rows (non-temporal: the output is not read again here).
+// Lane (g, c16) holds channels 16 ct + 4g .. + 3 of its query; the lanes
+// c16 and c16 ^ 8 trade their odd channel tiles, so that each store writes
+// whole 128-byte lines: in one instruction the 8 lanes (g, c) and (g, c ^ 8)
+// cover channels 0..31 (or 32..63) of one query.  Called by the whole wave.
+__device__ __forceinline__ void store_out(float* outh, const PassOut& o, int g, int c16) {
+  const f32x4 v0 = o.acc[0] * o.inv, v1 = o.acc[1] * o.inv;
+  const f32x4 v2 = o.acc[2] * o.inv, v3 = o.acc[3] * o.inv;
+  const f32x4 r1 = swap8(v1), r3 = swap8(v3);
+  const int rnq = swap8(o.nq);
+  const bool rlive = swap8(o.live ? 1 : 0) != 0;
+  const bool lo = c16 < 8;
+  float* own = outh + (size_t)o.nq * 64 + 4 * g;
+  float* other = outh + (size_t)rnq * 64 + 4 * g;
+  // first store: the low half-row's own queries; second: the high half's
+  if (lo ? o.live : rlive)
+    __builtin_nontemporal_store(lo ? v0 : r1, reinterpret_cast<f32x4*>(lo ? own : other + 16));
+  if (lo ? rlive : o.live)
+    __builtin_nontemporal_store(lo ? r1 : v0, reinterpret_cast<f32x4*>(lo ? other + 16 : own));
+  if (lo ? o.live : rlive)
+    __builtin_nontemporal_store(lo ? v2 : r3, reinterpret_cast<f32x4*>(lo ? own + 32 : other + 48));
+  if (lo ? rlive : o.live)
+    __builtin_nontemporal_store(lo ? r3 : v2, reinterpret_cast<f32x4*>(lo ? other + 48 : own + 32));
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
@@ -411,7 +441,7 @@ void attend_bf16_kernel(Args a) {
     // take the Q rows now too: a wait after the stores below would also wait
     // for the stores
     asm volatile("" ::"v"(bq0), "v"(bq1));
-    store_out(outh, pending, g);  // the previous expert's last pass
+    store_out(outh, pending, g, c16);  // the previous expert's last pass
     pending.live = false;
     if (j + 1 < nexp) load_rows(j + 1, 0, rows);
     __syncthreads();
@@ -420,7 +450,7 @@ void attend_bf16_kernel(Args a) {
       PassOut o = run_pass(j, 0, max(n0, 0), bq0, bq1);
       for (int p0 = TQ; p0 < cnt; p0 += TQ) {
         // later passes: query ids and Q rows straight from global memory
-        store_out(outh, o, g);
+        store_out(outh, o, g, c16);
         const int qi = p0 + 16 * w + c16;
         const int nq = qi < cnt ? permh[q0 + qi] : 0;
         const u32x4 b0 = *reinterpret_cast<const u32x4*>(Qh + (size_t)nq * 64 + 8 * g);
@@ -431,7 +461,7 @@ void attend_bf16_kernel(Args a) {
     }
     __syncthreads();  // readers of this expert's rows are done
   }
-  store_out(outh, pending, g);
+  store_out(outh, pending, g, c16);
 }
 
 }  // namespace att
