@@ -127,6 +127,18 @@ constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIR
 constexpr int DPP_ROW_SHL1 = 0x101, DPP_ROW_SHL2 = 0x102, DPP_ROW_SHL4 = 0x104,
               DPP_ROW_SHL8 = 0x108;
 
+// Lane c16 <-> c16 ^ 8 of each 16-lane row (DPP row rotate by 8); the
+// vector form moves each element by value (a bit cast applied to the
+// element expression v[i] itself was compiled as a read of element 0).
+constexpr int DPP_ROW_ROR8 = 0x128;
+__device__ __forceinline__ int swap8(int v) { return dpp_i<DPP_ROW_ROR8>(v); }
+__device__ __forceinline__ f32x4 swap8(f32x4 v) {
+  f32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __int_as_float(swap8(__float_as_int(v[i])));
+  return r;
+}
+
 __device__ __forceinline__ float g16_max(float v) {
   v = fmaxf(v, dpp_f<DPP_XOR1>(v));
   v = fmaxf(v, dpp_f<DPP_XOR2>(v));
@@ -933,10 +945,26 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
             acc[ct] = mfma_f16(__builtin_bit_cast(u32x4, ave), bpe, acc[ct]);
           }
         }
-        if (live) {
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
-            __builtin_nontemporal_store(acc[ct] * inv, reinterpret_cast<f32x4*>(outh + (size_t)qi * 64 + 16 * ct + 4 * g));
+        // lanes c16 and c16 ^ 8 trade their odd channel tiles, so that each
+        // store writes whole 128-byte lines: in one instruction the 8 lanes
+        // (g, c) and (g, c ^ 8) cover channels 0..31 (or 32..63) of one query
+        // (non-temporal: the output is not read again here)
+        {
+          const f32x4 v0 = acc[0] * inv, v2 = acc[2] * inv;
+          const f32x4 r1 = swap8(acc[1] * inv), r3 = swap8(acc[3] * inv);
+          const int rqi = swap8(qi);
+          const bool rlive = swap8(live ? 1 : 0) != 0;
+          const bool lo = c16 < 8;
+          float* own = outh + (size_t)qi * 64 + 4 * g;
+          float* other = outh + (size_t)rqi * 64 + 4 * g;
+          if (lo ? live : rlive)
+            __builtin_nontemporal_store(lo ? v0 : r1, reinterpret_cast<f32x4*>(lo ? own : other + 16));
+          if (lo ? rlive : live)
+            __builtin_nontemporal_store(lo ? r1 : v0, reinterpret_cast<f32x4*>(lo ? other + 16 : own));
+          if (lo ? live : rlive)
+            __builtin_nontemporal_store(lo ? v2 : r3, reinterpret_cast<f32x4*>(lo ? own + 32 : other + 48));
+          if (lo ? rlive : live)
+            __builtin_nontemporal_store(lo ? r3 : v2, reinterpret_cast<f32x4*>(lo ? other + 48 : own + 32));
         }
       }
     }
