@@ -133,25 +133,24 @@ __device__ __forceinline__ f32x4 swap8(f32x4 v) {
 // Lane (g, c16) holds channels 16 ct + 4g .. + 3 of its query; the lanes
 // c16 and c16 ^ 8 trade their odd channel tiles, so that each store writes
 // whole 128-byte lines: in one instruction the 8 lanes (g, c) and (g, c ^ 8)
-// cover channels 0..31 (or 32..63) of one query.  Called by the whole wave.
-__device__ __forceinline__ void store_out(float* outh, const PassOut& o, int g, int c16) {
+// cover channels 0..31 (or 32..63) of one query.  Stores go through a buffer
+// descriptor over the head's output rows, and a lane without a query stores
+// at an offset past its range, which the hardware drops (no branch).  Called
+// by the whole wave.
+__device__ __forceinline__ void store_out(Rsrc outr, const PassOut& o, int g, int c16) {
   const f32x4 v0 = o.acc[0] * o.inv, v1 = o.acc[1] * o.inv;
   const f32x4 v2 = o.acc[2] * o.inv, v3 = o.acc[3] * o.inv;
   const f32x4 r1 = swap8(v1), r3 = swap8(v3);
   const int rnq = swap8(o.nq);
   const bool rlive = swap8(o.live ? 1 : 0) != 0;
   const bool lo = c16 < 8;
-  float* own = outh + (size_t)o.nq * 64 + 4 * g;
-  float* other = outh + (size_t)rnq * 64 + 4 * g;
+  const int own = o.live ? o.nq * 256 + 16 * g : PAST;
+  const int other = rlive ? rnq * 256 + 16 * g : PAST;
   // first store: the low half-row's own queries; second: the high half's
-  if (lo ? o.live : rlive)
-    __builtin_nontemporal_store(lo ? v0 : r1, reinterpret_cast<f32x4*>(lo ? own : other + 16));
-  if (lo ? rlive : o.live)
-    __builtin_nontemporal_store(lo ? r1 : v0, reinterpret_cast<f32x4*>(lo ? other + 16 : own));
-  if (lo ? o.live : rlive)
-    __builtin_nontemporal_store(lo ? v2 : r3, reinterpret_cast<f32x4*>(lo ? own + 32 : other + 48));
-  if (lo ? rlive : o.live)
-    __builtin_nontemporal_store(lo ? r3 : v2, reinterpret_cast<f32x4*>(lo ? other + 48 : own + 32));
+  st16_nt(outr, lo ? v0 : r1, lo ? own : other + 64);
+  st16_nt(outr, lo ? r1 : v0, lo ? other + 64 : own);
+  st16_nt(outr, lo ? v2 : r3, lo ? own + 128 : other + 192);
+  st16_nt(outr, lo ? r3 : v2, lo ? other + 192 : own + 128);
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
@@ -196,7 +195,7 @@ void attend_bf16_kernel(Args a) {
   const int32_t* offs = a.offsets + (size_t)bh * (m + 1);
   const int32_t* permh = a.perm + (size_t)bh * N;
   const int32_t* idxh = a.idx + (size_t)bh * m * k;
-  float* outh = a.out + (size_t)bh * N * 64;
+  const Rsrc outr = out_rows(a.out + (size_t)bh * N * 64, N);
   int* tab = reinterpret_cast<int*>(sm + L.off_tab);
   const u32x4 z = {0u, 0u, 0u, 0u};
 
@@ -441,7 +440,7 @@ void attend_bf16_kernel(Args a) {
     // take the Q rows now too: a wait after the stores below would also wait
     // for the stores
     asm volatile("" ::"v"(bq0), "v"(bq1));
-    store_out(outh, pending, g, c16);  // the previous expert's last pass
+    store_out(outr, pending, g, c16);  // the previous expert's last pass
     pending.live = false;
     if (j + 1 < nexp) load_rows(j + 1, 0, rows);
     __syncthreads();
@@ -450,7 +449,7 @@ void attend_bf16_kernel(Args a) {
       PassOut o = run_pass(j, 0, max(n0, 0), bq0, bq1);
       for (int p0 = TQ; p0 < cnt; p0 += TQ) {
         // later passes: query ids and Q rows straight from global memory
-        store_out(outh, o, g, c16);
+        store_out(outr, o, g, c16);
         const int qi = p0 + 16 * w + c16;
         const int nq = qi < cnt ? permh[q0 + qi] : 0;
         const u32x4 b0 = *reinterpret_cast<const u32x4*>(Qh + (size_t)nq * 64 + 8 * g);
@@ -461,7 +460,7 @@ void attend_bf16_kernel(Args a) {
     }
     __syncthreads();  // readers of this expert's rows are done
   }
-  store_out(outh, pending, g, c16);
+  store_out(outr, pending, g, c16);
 }
 
 }  // namespace att

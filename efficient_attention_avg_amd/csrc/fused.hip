@@ -815,7 +815,7 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
       const uint32_t nonempty =
           __builtin_amdgcn_readfirstlane(*lds<uint32_t>(sm, OFF_STAT));
       const int nqt = (N + 15) >> 4;
-      float* outh = o.out + (size_t)bh * N * 64;
+      const Rsrc outr = out_rows(o.out + (size_t)bh * N * 64, N);
       // expert e's key rows for this lane's two slot tiles, from the LDS copy
       // (slots past k hold key 0: their logits are masked)
       auto load_k = [&](int e, u32x4 (&ak)[2][2]) {
@@ -948,23 +948,20 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
         // lanes c16 and c16 ^ 8 trade their odd channel tiles, so that each
         // store writes whole 128-byte lines: in one instruction the 8 lanes
         // (g, c) and (g, c ^ 8) cover channels 0..31 (or 32..63) of one query
-        // (non-temporal: the output is not read again here)
+        // (non-temporal: the output is not read again here); a column past N
+        // stores past the buffer's range, which the hardware drops
         {
           const f32x4 v0 = acc[0] * inv, v2 = acc[2] * inv;
           const f32x4 r1 = swap8(acc[1] * inv), r3 = swap8(acc[3] * inv);
           const int rqi = swap8(qi);
           const bool rlive = swap8(live ? 1 : 0) != 0;
           const bool lo = c16 < 8;
-          float* own = outh + (size_t)qi * 64 + 4 * g;
-          float* other = outh + (size_t)rqi * 64 + 4 * g;
-          if (lo ? live : rlive)
-            __builtin_nontemporal_store(lo ? v0 : r1, reinterpret_cast<f32x4*>(lo ? own : other + 16));
-          if (lo ? rlive : live)
-            __builtin_nontemporal_store(lo ? r1 : v0, reinterpret_cast<f32x4*>(lo ? other + 16 : own));
-          if (lo ? live : rlive)
-            __builtin_nontemporal_store(lo ? v2 : r3, reinterpret_cast<f32x4*>(lo ? own + 32 : other + 48));
-          if (lo ? rlive : live)
-            __builtin_nontemporal_store(lo ? r3 : v2, reinterpret_cast<f32x4*>(lo ? other + 48 : own + 32));
+          const int own = live ? qi * 256 + 16 * g : PAST;
+          const int other = rlive ? rqi * 256 + 16 * g : PAST;
+          st16_nt(outr, lo ? v0 : r1, lo ? own : other + 64);
+          st16_nt(outr, lo ? r1 : v0, lo ? other + 64 : own);
+          st16_nt(outr, lo ? v2 : r3, lo ? own + 128 : other + 192);
+          st16_nt(outr, lo ? r3 : v2, lo ? other + 192 : own + 128);
         }
       }
     }

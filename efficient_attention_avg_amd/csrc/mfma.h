@@ -80,4 +80,14 @@ __device__ __forceinline__ u32x4 ld16(Rsrc r, int off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// A head's [N][64] fp32 output rows as a raw buffer for stores: a store at an
+// offset past the rows (PAST: N * 256 <= 2^30 for N <= 2^22) is dropped.
+__device__ __forceinline__ Rsrc out_rows(float* base, int N) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, N * 256, 0x00020000);
+}
+// 16-byte store with the non-temporal hint (data not read again soon).
+__device__ __forceinline__ void st16_nt(Rsrc r, f32x4 v, int off) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 2);
+}
+
 }  // namespace mita
