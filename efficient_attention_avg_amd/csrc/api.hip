@@ -1,6 +1,7 @@
 // C ABI of libmita.so: argument validation, workspace layout and the launch
 // sequence of the MiTA forward pass.  No allocation, no host copies, no
 // synchronisation: everything is enqueued on the caller's stream.
+#include <initializer_list>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -183,6 +184,13 @@ const char* mita_last_error(void) { return g_error.c_str(); }
 
 const char* mita_version(void) { return "mita-gfx950 0.2"; }
 
+// Tensors are read and written 16 bytes per lane.
+static bool aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (((uintptr_t)p) & 15) return false;
+  return true;
+}
+
 mita_status mita_sync_event_create(void** event) {
   if (!event) return fail(MITA_ERR_INVALID_ARG, "event is required");
   hipEvent_t e = nullptr;
@@ -216,6 +224,8 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V, int B, 
   mita_status st = make_shape(B, H, grid_h, grid_w, d, m_h, m_w, k, in_dtype, &s);
   if (st != MITA_OK) return st;
   if (!Q || !K || !V || !out) return fail(MITA_ERR_INVALID_ARG, "Q, K, V and out are required");
+  if (!aligned16({Q, K, V, out, extras ? extras->ql : nullptr, extras ? extras->vl : nullptr}))
+    return fail(MITA_ERR_INVALID_ARG, "Q, K, V, out, ql and vl must be 16-byte aligned");
   const Layout L = layout_of(s);
   if (!workspace) return fail(MITA_ERR_INVALID_ARG, "workspace is required");
   if (workspace_bytes < L.total)
@@ -334,6 +344,7 @@ mita_status mita_pool(const void* Q, int B, int H, int grid_h, int grid_w, int d
   mita_status st = make_shape(B, H, grid_h, grid_w, d, m_h, m_w, 1, in_dtype, &s);
   if (st != MITA_OK) return st;
   if (!Q || !ql) return fail(MITA_ERR_INVALID_ARG, "Q and ql are required");
+  if (!aligned16({Q, ql})) return fail(MITA_ERR_INVALID_ARG, "Q and ql must be 16-byte aligned");
   if ((st = run_pool(Q, ql, s, stream)) != MITA_OK) return st;
   return ok();
 }
@@ -353,6 +364,8 @@ mita_status mita_landmark(const float* ql, const void* K, const void* V, int B, 
   if (st != MITA_OK) return st;
   if (!ql || !K || !V || !idx || !vl)
     return fail(MITA_ERR_INVALID_ARG, "ql, K, V, idx and vl are required");
+  if (!aligned16({ql, K, V, vl}))
+    return fail(MITA_ERR_INVALID_ARG, "ql, K, V and vl must be 16-byte aligned");
   const size_t need = landmark_scratch(s);
   if (need && !workspace) return fail(MITA_ERR_INVALID_ARG, "workspace is required");
   if (workspace_bytes < need)
@@ -376,6 +389,7 @@ mita_status mita_route(const void* Q, const float* ql, int B, int H, int N, int 
   if (st != MITA_OK) return st;
   if (!Q || !ql || !route || !counts || !offsets || !perm)
     return fail(MITA_ERR_INVALID_ARG, "Q, ql, route, counts, offsets and perm are required");
+  if (!aligned16({Q, ql})) return fail(MITA_ERR_INVALID_ARG, "Q and ql must be 16-byte aligned");
   const size_t need = route_scratch(s);
   if (need && !workspace) return fail(MITA_ERR_INVALID_ARG, "workspace is required");
   if (workspace_bytes < need)
@@ -394,6 +408,8 @@ mita_status mita_attend(const void* Q, const void* K, const void* V, const float
   if (st != MITA_OK) return st;
   if (!Q || !K || !V || !ql || !vl || !idx || !route || !offsets || !perm || !out)
     return fail(MITA_ERR_INVALID_ARG, "every tensor argument of mita_attend is required");
+  if (!aligned16({Q, K, V, ql, vl, out}))
+    return fail(MITA_ERR_INVALID_ARG, "Q, K, V, ql, vl and out must be 16-byte aligned");
   if ((st = run_attend(Q, K, V, ql, vl, idx, route, offsets, perm, out, s, stream)) != MITA_OK)
     return st;
   return ok();

@@ -23,7 +23,9 @@
  *     library never allocates, frees, copies to the host or synchronises; it
  *     enqueues kernels on `stream` and returns (asynchronous).
  *   - Q, K, V, out are contiguous [B, H, N, d] row-major (token n = y*grid_w+x),
- *     16-byte aligned.  Q, K, V are fp32 or bf16 (`in_dtype`); out is fp32.
+ *     16-byte aligned, like ql and vl where an entry point takes them (a
+ *     misaligned one is MITA_ERR_INVALID_ARG).  Q, K, V are fp32 or bf16
+ *     (`in_dtype`); out is fp32.
  *   - Index outputs are int32.  idx rows list key ids in ascending order.
  *   - d must be 64 (MITA_ERR_UNSUPPORTED otherwise).
  *   - Arguments are validated on the host before anything is enqueued; on a

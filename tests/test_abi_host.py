@@ -108,6 +108,8 @@ def _fwd(B=1, H=1, gh=14, gw=14, d=64, mh=5, mw=5, k=25, dt=mita.MITA_BF16, q=FA
     (dict(ws=None), mita.MITA_ERR_INVALID_ARG),
     (dict(nbytes=16), mita.MITA_ERR_WORKSPACE),
     (dict(ws=ctypes.c_void_p(0x10010)), mita.MITA_ERR_INVALID_ARG),   # misaligned
+    (dict(q=ctypes.c_void_p(0x10004)), mita.MITA_ERR_INVALID_ARG),    # Q not 16-byte aligned
+    (dict(out=ctypes.c_void_p(0x10008)), mita.MITA_ERR_INVALID_ARG),  # out not 16-byte aligned
     (dict(B=65536), mita.MITA_ERR_UNSUPPORTED),
 ])
 def test_forward_rejects_before_launch(kw, status):

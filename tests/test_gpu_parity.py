@@ -262,6 +262,37 @@ def test_deterministic_and_fully_written():
     assert torch.equal(out1, out2)
 
 
+@pytest.mark.parametrize("shape,path", [((3, 2, 14, 14, 5, 5, 25), "fused"),
+                                        ((3, 2, 14, 14, 5, 5, 25), "staged"),
+                                        ((2, 2, 13, 11, 4, 3, 40), "staged"),
+                                        ((1, 3, 9, 7, 3, 2, 21), "fused")],
+                         ids=lambda c: "x".join(map(str, c)) if isinstance(c, tuple) else c)
+def test_output_stays_inside_its_buffer(shape, path):
+    """The output is a view in the middle of a larger buffer filled with a
+    sentinel: every element of the view is written (finite), and not one byte
+    on either side changes.  (The output stores address the head's rows through
+    a buffer descriptor and send lanes without a query past its range.)"""
+    import efficient_attention_avg_amd as mita
+    torch = _torch()
+    B, H, gh, gw, mh, mw, k = shape
+    N = gh * gw
+    _say(f"output guard {shape} {path}")
+    Q, K, V = synth.make_qkv(B, H, gh, gw, 64, workload_id=70)
+    q, kk, v = (_to_dev(x, "bf16") for x in (Q, K, V))
+    n = B * H * N * 64
+    guard = 4096 + 12  # floats on each side: the view is 16-byte aligned, not line-aligned
+    big = torch.full((guard + n + guard,), -12345.0, dtype=torch.float32, device="cuda")
+    out = big[guard:guard + n].view(B, H, N, 64)
+    mita.mita_forward_ex(q, kk, v, gh, gw, mh, mw, k, out=out, path=path)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    assert (out != -12345.0).all()
+    assert (big[:guard] == -12345.0).all() and (big[guard + n:] == -12345.0).all()
+    ref = mita.mita_forward_ex(q, kk, v, gh, gw, mh, mw, k, path=path)["out"]
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
 @pytest.mark.parametrize("name,path,overlap", [("deit-s", "auto", False), ("hires-3136", "auto", False),
                                                ("hires-3136", "auto", True)])
 def test_kernel_timing_events(name, path, overlap):
