@@ -4,8 +4,8 @@
 // shared ones under one softmax; partial results merge by online softmax).
 //
 // Persistent workgroups, P per head, placed on the head's XCD so the head's
-// K, V and Q rows are re-read from that XCD's L2.  Workgroup p of a head takes
-// experts p, p + P, ...  Per workgroup:
+// K, V and Q rows are re-read from that XCD's L2.  A head's experts are dealt
+// to its P workgroups in a snake, largest pass count first.  Per workgroup:
 //   * load its experts' table (query range, key ids, first 64 query ids)
 //     and the head's Q_L (bf16 hi + lo) and V_L^T (f16) into LDS once;
 //   * per expert: its k key rows (bf16) and value rows (f16, transposed) sit

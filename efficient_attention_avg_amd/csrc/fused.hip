@@ -4,11 +4,12 @@
 // "NeurIPS'26：注意力也是FFN？从快权重出发，重新理解高效注意力", section
 // "用少量地标查询，同时构造全局概括与细节专家" and Algorithm 1.
 //
-// A persistent grid of 4-wave workgroups, two per CU, each walking heads.  A
-// head needs 67 KB of LDS, so two heads are in flight per CU and one's
+// A persistent grid of 8-wave workgroups, two per CU, each walking heads.  A
+// head needs 78 KB of LDS, so two heads are in flight per CU and one's
 // barrier-bound phases overlap the other's work.  Q and K rows are read
-// straight from global memory (L2 after first touch) as MFMA operands; only
-// the transposed values, scores, histograms and small tables live in LDS:
+// straight from global memory (L2 after first touch) as MFMA operands; the
+// transposed values, scores, histograms, a copy of K for the expert tiles and
+// small tables live in LDS:
 //   B  landmark pooling from the Q rows -> Q_L (fp32), split bf16 hi + lo;
 //   C  S^T = K Q_L^T on bf16 MFMA (hi + lo: near-fp32 scores, so top-k sets
 //      and routes are decided at fp32 accuracy), into the shared region X;
@@ -20,12 +21,13 @@
 //   E  V_L^T = V^T P^T on f16 MFMA, normalised by the row sums;
 //   E' R^T = Q_L Q^T per token tile: routes by a 16-lane argmax (ties to the
 //      lower landmark);
-//   F  stable counting sort of the queries by route (ballots) and a list of
-//      <= 16-query tiles per expert;
+//   F  stable counting sort of the queries by route (popcounts of each
+//      expert's query bitmap) into 16-query tiles of the sorted order;
 //   G  per tile: logits^T = [Q_L; K_e] Q_g^T (bf16 MFMA; the shared half
-//      recomputed from Q_L, K_e rows gathered from global memory), one
+//      recomputed from Q_L, K_e rows gathered from the LDS copy of K), one
 //      softmax over the m + k entries per query, and out^T = [V_L; V_e]^T P^T
-//      (f16 MFMA, P fed straight from the logits' accumulators), in fp32.
+//      (f16 MFMA, P fed straight from the logits' accumulators), in fp32,
+//      stored in whole 128-byte lines.
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
