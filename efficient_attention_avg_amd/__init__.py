@@ -12,6 +12,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import threading
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmita.so")
@@ -23,7 +24,7 @@ PATHS = {"auto": 0, "fused": 1, "staged": 2}
 # Every symbol include/mita.h declares.
 EXPORTS = [
     "mita_status_string", "mita_last_error", "mita_version", "mita_workspace_bytes",
-    "mita_schedule", "mita_kernel_names", "mita_sync_event_create",
+    "mita_workspace_bytes_ex", "mita_schedule", "mita_kernel_names", "mita_sync_event_create",
     "mita_forward", "mita_forward_ex", "mita_pool", "mita_landmark_workspace_bytes",
     "mita_landmark", "mita_route_workspace_bytes", "mita_route", "mita_attend",
 ]
@@ -40,7 +41,7 @@ class _Extras(ctypes.Structure):
                 ("offsets", ctypes.c_void_p), ("perm", ctypes.c_void_p), ("path", ctypes.c_int),
                 ("events", ctypes.POINTER(ctypes.c_void_p)), ("n_events", ctypes.c_int),
                 ("side_stream", ctypes.c_void_p), ("fork_event", ctypes.c_void_p),
-                ("join_event", ctypes.c_void_p)]
+                ("join_event", ctypes.c_void_p), ("s", ctypes.c_int), ("route_only", ctypes.c_int)]
 
 
 _lib = None
@@ -63,10 +64,13 @@ def lib() -> ctypes.CDLL:
         L.mita_version.argtypes = []
         L.mita_workspace_bytes.restype = Z
         L.mita_workspace_bytes.argtypes = [I] * 8 + [I]
+        L.mita_workspace_bytes_ex.restype = Z
+        L.mita_workspace_bytes_ex.argtypes = [I] * 8 + [I, ctypes.POINTER(_Extras)]
         L.mita_schedule.restype = I
         L.mita_schedule.argtypes = [I] * 8 + [I]
         L.mita_kernel_names.restype = I
-        L.mita_kernel_names.argtypes = [I] * 8 + [I, I, I, ctypes.POINTER(ctypes.c_char_p),
+        L.mita_kernel_names.argtypes = [I] * 8 + [I, ctypes.POINTER(_Extras),
+                                                 ctypes.POINTER(ctypes.c_char_p),
                                                  ctypes.POINTER(ctypes.c_int), I]
         L.mita_sync_event_create.restype = S
         L.mita_sync_event_create.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
@@ -146,8 +150,21 @@ def _qkv(q, k, v):
     return _dtype_code(q), torch
 
 
-def mita_workspace_bytes(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code) -> int:
-    return int(lib().mita_workspace_bytes(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code))
+def _grid(q, grid_h, grid_w):
+    """The library takes N from the grid; tensors sized from q must agree with it."""
+    if q.dim() != 4:
+        raise ValueError("Q must be [B, H, N, d]")
+    if q.shape[2] != grid_h * grid_w:
+        raise ValueError(f"Q has N={q.shape[2]} tokens but the grid is {grid_h}x{grid_w} "
+                         f"= {grid_h * grid_w}")
+
+
+def mita_workspace_bytes(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code, path="auto", s=1,
+                         route_only=False) -> int:
+    """Device workspace bytes a call with this path and variant needs (0: none)."""
+    ex = _Extras(path=PATHS[path], s=s, route_only=1 if route_only else 0)
+    return int(lib().mita_workspace_bytes_ex(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code,
+                                             ctypes.byref(ex)))
 
 
 def mita_schedule(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code) -> str:
@@ -166,26 +183,31 @@ def mita_forward(q, k, v, grid_h, grid_w, m_h, m_w, topk, *, out=None, idx=None,
 
 
 def mita_kernel_schedule(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code, path="auto",
-                         overlap=False) -> list:
+                         overlap=False, s=1, route_only=False) -> list:
     """The kernels mita_forward_ex launches, in the order of its timing events, as
     (name, start) pairs: kernel i runs between events[start] and events[i + 1];
     ``overlap``: the call runs routing on a side stream (host only)."""
     names = (ctypes.c_char_p * 8)()
     starts = (ctypes.c_int * 8)()
-    n = int(lib().mita_kernel_names(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code, PATHS[path],
-                                    1 if overlap else 0, names, starts, 8))
+    # a non-null side stream marks the forked schedule (never dereferenced here)
+    ex = _Extras(path=PATHS[path], s=s, route_only=1 if route_only else 0,
+                 side_stream=1 if overlap else None)
+    n = int(lib().mita_kernel_names(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code,
+                                    ctypes.byref(ex), names, starts, 8))
     if n < 0:
         _check(-n)
     return [(names[i].decode(), int(starts[i])) for i in range(n)]
 
 
-def mita_kernel_names(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code, path="auto") -> list:
+def mita_kernel_names(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code, path="auto", s=1,
+                      route_only=False) -> list:
     """The kernels mita_forward_ex launches, in the order of its timing events (host only)."""
     return [nm for nm, _ in mita_kernel_schedule(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code,
-                                                 path)]
+                                                 path, s=s, route_only=route_only)]
 
 
 _sides = {}
+_sides_lock = threading.Lock()
 
 
 class _SyncEvent:
@@ -198,26 +220,35 @@ class _SyncEvent:
 
 
 def _side(device):
-    """This process's side stream and fork/join events for `device` (created once)."""
+    """The calling thread's side stream and fork/join events for `device` (created once).
+
+    Each host thread gets its own set: two calls in flight at once must not
+    share the fork and join events (one call's record could otherwise be
+    waited on by the other's side stream)."""
     import torch
-    key = torch.device(device).index
-    if key not in _sides:
-        with torch.cuda.device(device):
-            s = torch.cuda.Stream(device=device)
-            f, j = _SyncEvent(), _SyncEvent()
-        _sides[key] = (s, f, j)
-    return _sides[key]
+    key = (torch.device(device).index, threading.get_ident())
+    with _sides_lock:
+        if key not in _sides:
+            with torch.cuda.device(device):
+                s = torch.cuda.Stream(device=device)
+                f, j = _SyncEvent(), _SyncEvent()
+            _sides[key] = (s, f, j)
+        return _sides[key]
 
 
 def mita_forward_ex(q, k, v, grid_h, grid_w, m_h, m_w, topk, *, out=None, idx=None, route=None,
                     extras=False, path="auto", workspace=None, stream=None, events=None,
-                    overlap=False):
+                    overlap=False, s=1, route_only=False):
     """Whole pass with optional intermediates.
 
-    ``idx`` / ``route``: a preallocated int32 tensor, True (allocate) or None.
-    ``extras=True`` also returns ql, vl, counts, offsets and perm.
-    ``overlap=True``: the staged schedule runs routing and grouping on this
-    process's side stream for the device, beside the landmark pass.
+    ``idx`` / ``route``: a preallocated int32 tensor, True (allocate) or None;
+    route is [B, H, N] for s = 1 and [B, H, N, s] otherwise.
+    ``extras=True`` also returns ql, vl, counts, offsets and perm (perm and
+    counts over the N*s (query, rank) items when s > 1).
+    ``overlap=True``: the staged schedule runs routing and grouping on the
+    calling thread's side stream for the device, beside the landmark pass.
+    ``s``: experts per query; ``route_only``: the variant without the shared
+    expert.
     ``events``: torch.cuda.Event objects (enable_timing=True): events[0] before
     the first kernel, events[i + 1] after the i-th kernel of
     mita_kernel_schedule, whose start index gives the event the kernel's
@@ -225,6 +256,7 @@ def mita_forward_ex(q, k, v, grid_h, grid_w, m_h, m_w, topk, *, out=None, idx=No
     HIP event exists.
     """
     code, torch = _qkv(q, k, v)
+    _grid(q, grid_h, grid_w)
     B, H, N, d = q.shape
     m = m_h * m_w
     dev = q.device
@@ -237,9 +269,9 @@ def mita_forward_ex(q, k, v, grid_h, grid_w, m_h, m_w, topk, *, out=None, idx=No
 
     out = alloc(True if out is None else out, (B, H, N, d), torch.float32, "out")
     idx = alloc(idx, (B, H, m, topk), i32, "idx")
-    route = alloc(route, (B, H, N), i32, "route")
+    route = alloc(route, (B, H, N) if s == 1 else (B, H, N, s), i32, "route")
     res = dict(out=out, idx=idx, route=route)
-    ex = _Extras(path=PATHS[path])
+    ex = _Extras(path=PATHS[path], s=s, route_only=1 if route_only else 0)
     if overlap:
         side, fork, join = _side(dev)
         ex.side_stream, ex.fork_event, ex.join_event = side.cuda_stream, fork.cuda_event, \
@@ -253,21 +285,26 @@ def mita_forward_ex(q, k, v, grid_h, grid_w, m_h, m_w, topk, *, out=None, idx=No
                    vl=alloc(True, (B, H, m, d), torch.float32, "vl"),
                    counts=alloc(True, (B, H, m), i32, "counts"),
                    offsets=alloc(True, (B, H, m + 1), i32, "offsets"),
-                   perm=alloc(True, (B, H, N), i32, "perm"))
+                   perm=alloc(True, (B, H, N * s), i32, "perm"))
         for name in ("ql", "vl", "counts", "offsets", "perm"):
             setattr(ex, name, res[name].data_ptr())
-    nbytes = mita_workspace_bytes(B, H, grid_h, grid_w, d, m_h, m_w, topk, code)
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    nbytes = int(lib().mita_workspace_bytes_ex(B, H, grid_h, grid_w, d, m_h, m_w, topk, code,
+                                               ctypes.byref(ex)))
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        _dev(workspace, "workspace", torch.uint8)
     _check(lib().mita_forward_ex(_ptr(q), _ptr(k), _ptr(v), B, H, grid_h, grid_w, d, m_h, m_w,
                                  topk, code, _ptr(out), _ptr(idx), _ptr(route), ctypes.byref(ex),
-                                 _ptr(workspace), workspace.numel(), _stream(q, stream)))
+                                 _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                 _stream(q, stream)))
     return res
 
 
 def mita_pool(q, grid_h, grid_w, m_h, m_w, *, ql=None, stream=None):
     torch = _torch()
     _dev(q, "Q")
+    _grid(q, grid_h, grid_w)
     B, H, N, d = q.shape
     ql = torch.empty((B, H, m_h * m_w, d), dtype=torch.float32, device=q.device) if ql is None \
         else _dev(ql, "ql", torch.float32, (B, H, m_h * m_w, d))

@@ -38,7 +38,6 @@ mita_status hip_status(hipError_t e, const char* what) {
   return fail(MITA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-// Shape checks common to every entry point.  Returns MITA_OK and fills *s.
 // Records the caller's timing events around the kernels of one call.
 struct Marker {
   void* const* ev = nullptr;
@@ -53,6 +52,7 @@ struct Marker {
   }
 };
 
+// Shape checks common to every entry point.  Returns MITA_OK and fills *s.
 mita_status make_shape(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
                        mita_dtype dt, Shape* s) {
   if (B < 1 || H < 1) return fail(MITA_ERR_INVALID_ARG, "B=%d and H=%d must be >= 1", B, H);
@@ -78,6 +78,37 @@ mita_status make_shape(int B, int H, int grid_h, int grid_w, int d, int m_h, int
   s->N = (int)N; s->m = (int)m; s->BH = (int)BH;
   s->bf16 = (dt == MITA_BF16);
   return MITA_OK;
+}
+
+// The method variant carried by the extras (s experts per query, shared
+// branch or route-only); NULL extras or zeros mean the plain pass.
+mita_status set_variant(const mita_extras* ex, Shape* s) {
+  const int sv = ex && ex->s ? ex->s : 1;
+  const int ro = ex ? ex->route_only : 0;
+  if (sv < 1 || sv > MITA_MAX_S || sv > s->m)
+    return fail(MITA_ERR_INVALID_ARG, "s=%d must lie in [1, min(m=%d, %d)]", sv, s->m, MITA_MAX_S);
+  if (ro != 0 && ro != 1) return fail(MITA_ERR_INVALID_ARG, "route_only must be 0 or 1");
+  s->s = sv;
+  s->shared = ro == 0;
+  if (s->s != 1 || !s->shared)
+    return fail(MITA_ERR_UNSUPPORTED, "the s > 1 and route-only variants are not built yet");
+  return MITA_OK;
+}
+
+int path_of(const mita_extras* ex) { return ex ? ex->path : MITA_PATH_AUTO; }
+
+mita_status check_path(int path, const Shape& s) {
+  if (path != MITA_PATH_AUTO && path != MITA_PATH_STAGED && path != MITA_PATH_FUSED)
+    return fail(MITA_ERR_INVALID_ARG, "unknown path %d", path);
+  if (path == MITA_PATH_FUSED && !mita::fused_supported(s))
+    return fail(MITA_ERR_UNSUPPORTED,
+                "fused schedule needs bf16 inputs, N <= 208, m <= 32, k <= 32 and the plain "
+                "variant (s = 1, shared expert)");
+  return MITA_OK;
+}
+
+bool runs_fused(int path, const Shape& s) {
+  return mita::fused_supported(s) && path != MITA_PATH_STAGED;
 }
 
 // Which kernels each staged step uses: the MFMA kernels for bf16 inputs
@@ -202,11 +233,19 @@ mita_status mita_sync_event_create(void** event) {
   return ok();
 }
 
-size_t mita_workspace_bytes(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
-                            mita_dtype in_dtype) {
+size_t mita_workspace_bytes_ex(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w,
+                               int k, mita_dtype in_dtype, const mita_extras* extras) {
   Shape s;
   if (make_shape(B, H, grid_h, grid_w, d, m_h, m_w, k, in_dtype, &s) != MITA_OK) return 0;
-  return layout_of(s).total;
+  if (set_variant(extras, &s) != MITA_OK) return 0;
+  const int path = path_of(extras);
+  if (check_path(path, s) != MITA_OK) return 0;
+  return runs_fused(path, s) ? 0 : layout_of(s).total;
+}
+
+size_t mita_workspace_bytes(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
+                            mita_dtype in_dtype) {
+  return mita_workspace_bytes_ex(B, H, grid_h, grid_w, d, m_h, m_w, k, in_dtype, nullptr);
 }
 
 int mita_schedule(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
@@ -223,22 +262,19 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V, int B, 
   Shape s;
   mita_status st = make_shape(B, H, grid_h, grid_w, d, m_h, m_w, k, in_dtype, &s);
   if (st != MITA_OK) return st;
+  if ((st = set_variant(extras, &s)) != MITA_OK) return st;
   if (!Q || !K || !V || !out) return fail(MITA_ERR_INVALID_ARG, "Q, K, V and out are required");
   if (!aligned16({Q, K, V, out, extras ? extras->ql : nullptr, extras ? extras->vl : nullptr}))
     return fail(MITA_ERR_INVALID_ARG, "Q, K, V, out, ql and vl must be 16-byte aligned");
+  const int path = path_of(extras);
+  if ((st = check_path(path, s)) != MITA_OK) return st;
+  const bool fused = runs_fused(path, s);
   const Layout L = layout_of(s);
-  if (!workspace) return fail(MITA_ERR_INVALID_ARG, "workspace is required");
-  if (workspace_bytes < L.total)
-    return fail(MITA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes,
-                L.total);
+  const size_t need = fused ? 0 : L.total;
+  if (need && !workspace) return fail(MITA_ERR_INVALID_ARG, "workspace is required");
+  if (workspace_bytes < need)
+    return fail(MITA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
   if (((uintptr_t)workspace) & 255) return fail(MITA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
-  const int path = extras ? extras->path : MITA_PATH_AUTO;
-  if (path != MITA_PATH_AUTO && path != MITA_PATH_STAGED && path != MITA_PATH_FUSED)
-    return fail(MITA_ERR_INVALID_ARG, "unknown path %d", path);
-  const bool fusable = mita::fused_supported(s);
-  if (path == MITA_PATH_FUSED && !fusable)
-    return fail(MITA_ERR_UNSUPPORTED,
-                "fused schedule needs bf16 inputs, N <= 208, m <= 32 and k <= 32");
   const bool side = extras && (extras->side_stream || extras->fork_event || extras->join_event);
   if (side && !(extras->side_stream && extras->fork_event && extras->join_event))
     return fail(MITA_ERR_INVALID_ARG, "side_stream, fork_event and join_event go together");
@@ -248,7 +284,7 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V, int B, 
     mk.n = extras->n_events;
   }
   mk.mark(stream);
-  if (fusable && path != MITA_PATH_STAGED) {
+  if (fused) {
     st = hip_status(mita::launch_fused(Q, K, V, out, idx, route, extras ? extras->ql : nullptr,
                                        extras ? extras->vl : nullptr,
                                        extras ? extras->counts : nullptr,
@@ -303,22 +339,21 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V, int B, 
 }
 
 int mita_kernel_names(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
-                      mita_dtype in_dtype, int path, int forked, const char** names,
+                      mita_dtype in_dtype, const mita_extras* extras, const char** names,
                       int* starts, int capacity) {
   Shape s;
-  const mita_status st = make_shape(B, H, grid_h, grid_w, d, m_h, m_w, k, in_dtype, &s);
+  mita_status st = make_shape(B, H, grid_h, grid_w, d, m_h, m_w, k, in_dtype, &s);
   if (st != MITA_OK) return -(int)st;
-  if (path != MITA_PATH_AUTO && path != MITA_PATH_STAGED && path != MITA_PATH_FUSED)
-    return -(int)fail(MITA_ERR_INVALID_ARG, "unknown path %d", path);
-  const bool fusable = mita::fused_supported(s);
-  if (path == MITA_PATH_FUSED && !fusable)
-    return -(int)fail(MITA_ERR_UNSUPPORTED, "fused schedule not available for this shape");
+  if ((st = set_variant(extras, &s)) != MITA_OK) return -(int)st;
+  const int path = path_of(extras);
+  if ((st = check_path(path, s)) != MITA_OK) return -(int)st;
+  const bool forked = extras && extras->side_stream;
   static const char* const kFused[] = {"fused"};
   static const int kFusedStart[] = {0};
   static const char* const kStaged[] = {"pool", "route", "group", "landmark", "attend"};
   static const int kStagedStart[] = {0, 1, 2, 3, 4};
   static const int kForkedStart[] = {0, 1, 2, 1, 4};
-  const bool fused = fusable && path != MITA_PATH_STAGED;
+  const bool fused = runs_fused(path, s);
   const char* const* list = fused ? kFused : kStaged;
   const int* start = fused ? kFusedStart : forked ? kForkedStart : kStagedStart;
   const int n = fused ? 1 : 5;

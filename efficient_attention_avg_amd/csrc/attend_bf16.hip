@@ -49,7 +49,9 @@ struct Args {
 };
 
 // LDS layout; the expert table holds, per expert of the workgroup,
-// [q0, count, k key ids, first TQ query ids].
+// [q0, count, k key ids, first TQ query ids].  Before the table is filled
+// the same region holds the head's m expert counts, so it spans at least m
+// ints.
 struct Lay {
   int mp, vlt_stride, ew, ts;
   int off_qlh, off_qll, off_vlt, off_ke, off_vet, off_tab, off_elist, bytes;
@@ -64,7 +66,9 @@ struct Lay {
     off_ke = off_vlt + 64 * vlt_stride;
     off_vet = off_ke + EC * 128;
     off_tab = off_vet + 64 * EVT_STRIDE;
-    off_elist = off_tab + ew * ts * 4;
+    // the table region first holds the head's m per-expert counts (the deal),
+    // then the workgroup's ew table entries
+    off_elist = off_tab + (ew * ts > m ? ew * ts : m) * 4;
     bytes = off_elist + (ew + 1) * 4;
   }
 };
@@ -489,12 +493,8 @@ hipError_t launch_attend_bf16(const void* Q, const void* K, const void* V, const
   while (att::Lay(s.m, s.k, parts).bytes > 160 * 1024 && parts < s.m) ++parts;
   const att::Lay L(s.m, s.k, parts);
   if (L.bytes > 160 * 1024) return hipErrorInvalidValue;
-  static bool attr = false;
-  if (!attr) {
-    hipFuncSetAttribute((const void*)att::attend_bf16_kernel,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr = true;
-  }
+  if (const hipError_t e = allow_lds((const void*)att::attend_bf16_kernel, 160 * 1024); e != hipSuccess)
+    return e;
   att::Args a{(const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, ql, vl, idx, offsets,
               perm, out, s.BH, s.N, s.m, s.k, parts};
   const int grid = ((s.BH + 7) / 8) * 8 * parts;

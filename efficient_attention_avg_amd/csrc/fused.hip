@@ -973,7 +973,8 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
 }  // namespace fused
 
 bool fused_supported(const Shape& s) {
-  return s.bf16 && s.d == 64 && s.N <= fused::NP && s.m <= fused::MMAX && s.k <= fused::KMAX;
+  return s.bf16 && s.s == 1 && s.shared && s.d == 64 && s.N <= fused::NP && s.m <= fused::MMAX &&
+         s.k <= fused::KMAX;
 }
 
 static int device_cu_count() {

@@ -11,9 +11,19 @@ struct Shape {
   int B, H, grid_h, grid_w, d, m_h, m_w, k;
   int N, m, BH;
   bool bf16;
+  int s = 1;            // experts per query
+  bool shared = true;   // false: the route-only variant (no shared expert)
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Lets `kernel` take up to `bytes` of dynamic LDS.  Called before every launch
+// that needs more than the default: the attribute belongs to the current
+// device, and a per-launch call keeps the library free of process-wide flags
+// (two threads or two devices never depend on who launched first).
+inline hipError_t allow_lds(const void* kernel, int bytes) {
+  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
 
 // step a1: landmark pooling
 hipError_t launch_pool(const void* Q, float* ql, const Shape& s, hipStream_t st);

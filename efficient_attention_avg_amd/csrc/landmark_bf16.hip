@@ -910,12 +910,8 @@ hipError_t launch_landmark_bf16(const float* ql, const void* K, const void* V, i
   if (a.cap == 0) return hipErrorInvalidValue;
   const size_t lds = lmk::lds_bytes(a.cap);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  static bool attr = false;
-  if (!attr) {
-    hipFuncSetAttribute((const void*)lmk::landmark_kernel,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr = true;
-  }
+  if (const hipError_t e = allow_lds((const void*)lmk::landmark_kernel, 160 * 1024); e != hipSuccess)
+    return e;
   const int grid = ((s.BH + 7) / 8) * 8 * a.tiles;
   lmk::landmark_kernel<<<grid, 64 * lmk::NW, lds, st>>>(a);
   return hipGetLastError();

@@ -251,12 +251,8 @@ hipError_t launch_route_bf16(const void* Q, const float* ql, int32_t* route, int
   route_chunking(s, qc, nchunks, R, nruns);
   const size_t lds = route_lds(s, qc, R);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  static bool attr = false;
-  if (!attr) {
-    hipFuncSetAttribute((const void*)rt::route_bf16_kernel,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr = true;
-  }
+  if (const hipError_t e = allow_lds((const void*)rt::route_bf16_kernel, 160 * 1024); e != hipSuccess)
+    return e;
   dim3 grid(nchunks, s.BH);
   rt::route_bf16_kernel<<<grid, 64 * rt::RW, lds, st>>>((const uint16_t*)Q, ql, route, chist, s.N,
                                                         s.m, nruns, qc, R);
@@ -269,12 +265,8 @@ hipError_t launch_group_bf16(const int32_t* route, const int32_t* chist, int32_t
   route_chunking(s, qc, nchunks, R, nruns);
   const size_t lds = ((size_t)nruns * s.m + s.m) * 4;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  static bool attr = false;
-  if (!attr) {
-    hipFuncSetAttribute((const void*)rt::group_bf16_kernel,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    attr = true;
-  }
+  if (const hipError_t e = allow_lds((const void*)rt::group_bf16_kernel, 160 * 1024); e != hipSuccess)
+    return e;
   rt::group_bf16_kernel<<<s.BH, 1024, lds, st>>>(route, chist, counts, offsets, perm, s.N, s.m,
                                                  nruns, R);
   return hipGetLastError();

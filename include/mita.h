@@ -7,7 +7,8 @@
  * section "用少量地标查询，同时构造全局概括与细节专家" and its Algorithm 1
  * (English version: "NeurIPS'26: Is Attention Also FFN? ...", section
  * "Construct global generalization and detail experts at the same time with
- * a small number of landmark queries").  Per (batch b, head h), with
+ * a small number of landmark queries"); cited below as [ZH].  Per (batch b,
+ * head h), with
  * N = grid_h*grid_w tokens in row-major order, m = m_h*m_w landmarks and
  * tau = 1/sqrt(d):
  *   Q_L     = 2-D adaptive average pooling of Q over the token grid  (m x d)
@@ -25,7 +26,13 @@
  *   - Q, K, V, out are contiguous [B, H, N, d] row-major (token n = y*grid_w+x),
  *     16-byte aligned, like ql and vl where an entry point takes them (a
  *     misaligned one is MITA_ERR_INVALID_ARG).  Q, K, V are fp32 or bf16
- *     (`in_dtype`); out is fp32.
+ *     (`in_dtype`); out is always fp32 (no output-type argument: a bf16
+ *     output would round values near 5 by more than 1e-2).
+ *   - Precondition on bf16 inputs: every |V| < 65504.  The value products run
+ *     on f16 matrix cores (V, V_L and the softmax weights are staged as f16),
+ *     so larger values would become inf.  Nothing checks this (it would cost
+ *     a pass over V); the seeded workloads stay below 40.  fp32 inputs have
+ *     no such bound.
  *   - Index outputs are int32.  idx rows list key ids in ascending order.
  *   - d must be 64 (MITA_ERR_UNSUPPORTED otherwise).
  *   - Arguments are validated on the host before anything is enqueued; on a
@@ -75,7 +82,9 @@ const char* mita_version(void);
 /*
  * Bytes of device workspace mita_forward needs for this shape (the "device
  * memory query"): the caller allocates it (e.g. through PyTorch) and passes it
- * in.  Returns 0 for an invalid shape.  The layout inside is private.
+ * in.  0 when the schedule mita_forward runs for the shape needs none (the
+ * fused one): the workspace pointer may then be NULL.  Also 0 for an invalid
+ * shape (mita_forward then reports why).  The layout inside is private.
  */
 size_t mita_workspace_bytes(int B, int H, int grid_h, int grid_w, int d,
                             int m_h, int m_w, int k, mita_dtype in_dtype);
@@ -94,7 +103,8 @@ int mita_schedule(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w,
  *   idx   [B,H,m,k] int32 or NULL: each landmark's expert (ascending key ids).
  *   route [B,H,N]   int32 or NULL: each query's landmark id in [0, m).
  *   workspace: at least mita_workspace_bytes(...) bytes of device memory,
- *   256-byte aligned; contents on entry are ignored.
+ *   256-byte aligned (NULL allowed when that is 0); contents on entry are
+ *   ignored.
  */
 mita_status mita_forward(const void* Q, const void* K, const void* V,
                          int B, int H, int grid_h, int grid_w, int d,
@@ -104,8 +114,9 @@ mita_status mita_forward(const void* Q, const void* K, const void* V,
 
 /*
  * Optional extra outputs of mita_forward_ex (any member may be NULL), the
- * schedule to run, and optional per-kernel timing events.  Used to check
- * every intermediate of the pass and to time its kernels.
+ * schedule to run, the method variant, and optional per-kernel timing
+ * events.  Zero-initialised it asks for the plain pass.  Used to check every
+ * intermediate of the pass, to time its kernels, and to run the variants.
  *   ql      [B,H,m,d] fp32  landmark queries
  *   vl      [B,H,m,d] fp32  landmark values (shared expert values)
  *   counts  [B,H,m]   int32 queries routed to each landmark
@@ -128,6 +139,22 @@ mita_status mita_forward(const void* Q, const void* K, const void* V,
  *           the host, and work queued on `stream` after it sees every output.
  *           Events from mita_sync_event_create make the fork and the join
  *           cheapest.
+ *   s       experts per query (0 means 1).  With s > 1 each query is routed
+ *           to its s best landmarks (q . Q_L descending, ties to the lower
+ *           landmark) and takes ONE softmax over its m shared entries and the
+ *           s*k entries of those experts, concatenated without removing keys
+ *           that two experts share (page [ZH], landmark-query section: the
+ *           output is given there for one routed expert per query, s = 1;
+ *           this is the plain extension to s).  route is then [B,H,N,s]
+ *           (best first) and counts/offsets/perm group the N*s (query,
+ *           rank) items t = n*s + j by expert.  1 <= s <= min(m, MITA_MAX_S).
+ *   route_only
+ *           nonzero: the ablation without the shared (compressed) branch
+ *           (page [ZH], long-sequence section, the ablation with the same
+ *           number of entries per query): each query's softmax covers only
+ *           its routed experts' s*k entries; V_L is not computed (vl, if
+ *           given, is left untouched).  Pass k = m + k_mita to give every
+ *           query the same number of entries as the full method.
  */
 typedef struct {
   float* ql;
@@ -141,7 +168,20 @@ typedef struct {
   void* side_stream; /* hipStream_t */
   void* fork_event;  /* hipEvent_t */
   void* join_event;  /* hipEvent_t */
+  int s;
+  int route_only;
 } mita_extras;
+
+#define MITA_MAX_S 8
+
+/*
+ * Bytes of device workspace mita_forward_ex needs with these extras (its
+ * path, variant and supplied outputs; NULL means none): 0 when the schedule
+ * it runs needs none.  0 also for an invalid shape or variant.
+ */
+size_t mita_workspace_bytes_ex(int B, int H, int grid_h, int grid_w, int d,
+                               int m_h, int m_w, int k, mita_dtype in_dtype,
+                               const mita_extras* extras);
 
 mita_status mita_forward_ex(const void* Q, const void* K, const void* V,
                             int B, int H, int grid_h, int grid_w, int d,
@@ -164,34 +204,45 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V,
 mita_status mita_sync_event_create(void** event);
 
 /*
- * The kernels mita_forward_ex launches for this configuration and path, in
- * the order of its timing events: "fused" for the fused schedule; "pool",
- * "route", "group", "landmark", "attend" for the staged one.  Writes up to
- * `capacity` static strings to names and, to starts, the index of the event
- * each kernel's interval opens with: i when the kernel follows the previous
- * one on the same stream; with `forked` nonzero (a call given a side stream)
- * landmark opens with pooling's end event, like route.  names and starts may
- * be NULL.  Returns the kernel count, or a negative mita_status for invalid
- * sizes or an unsupported path.  Host only.
+ * The kernels mita_forward_ex launches for this configuration and these
+ * extras (path, variant; NULL means the plain pass), in the order of its
+ * timing events: "fused" for the fused schedule; "pool", "route", "group",
+ * "landmark", "attend" for the staged one, and "merge" after them when
+ * s > 1.  Writes up to `capacity` static strings to names and, to starts,
+ * the index of the event each kernel's interval opens with: i when the
+ * kernel follows the previous one on the same stream; when the extras carry
+ * a side stream, landmark opens with pooling's end event, like route.  names
+ * and starts may be NULL.  Returns the kernel count, or a negative
+ * mita_status for invalid sizes or an unsupported path.  Host only: the
+ * extras' pointers are not dereferenced.
  */
 int mita_kernel_names(int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
-                      mita_dtype in_dtype, int path, int forked, const char** names,
+                      mita_dtype in_dtype, const mita_extras* extras, const char** names,
                       int* starts, int capacity);
 
 /* ---------------------------------------------------------------------------
- * The steps one at a time (same kernels as the staged schedule).  Each takes
- * its inputs from device memory and writes its outputs there, so a caller can
- * run, time or check one step in isolation.
+ * The steps one at a time (same kernels as the staged schedule, plain pass,
+ * s = 1).  Each takes its inputs from device memory and writes its outputs
+ * there, so a caller can run, time or check one step in isolation.
  * ------------------------------------------------------------------------- */
 
-/* Landmark pooling: Q [B,H,N,d] -> ql [B,H,m,d] fp32 (window mean, fp32 sums). */
+/*
+ * Landmark pooling: Q [B,H,N,d] -> ql [B,H,m,d] fp32 (window mean, fp32 sums).
+ * Page [ZH], landmark-query section (m landmark queries by local average
+ * pooling of the queries); windows are those of 2-D adaptive average
+ * pooling, rows [floor(r*gh/mh), ceil((r+1)*gh/mh)), columns likewise.
+ */
 mita_status mita_pool(const void* Q, int B, int H, int grid_h, int grid_w, int d,
                       int m_h, int m_w, mita_dtype in_dtype, float* ql, hipStream_t stream);
 
 /*
  * Landmark pass: scores of ql [B,H,m,d] fp32 against K [B,H,N,d], each row's
  * top-k keys -> idx [B,H,m,k] (ascending), and the row softmax applied to V
- * -> vl [B,H,m,d] fp32.  Needs mita_landmark_workspace_bytes(...) of scratch
+ * -> vl [B,H,m,d] fp32.  Page [ZH], landmark-query section: each landmark
+ * query scores every key and its k best form a routed expert; the same
+ * scores, softmax-normalised over all keys, give the landmark values (the
+ * shared expert's values, "top-k selection and the global summary share the
+ * landmark scores").  Needs mita_landmark_workspace_bytes(...) of scratch
  * (0 when the bf16 MFMA kernel serves the shape -- bf16 inputs, k <= 400;
  * workspace may then be NULL).
  */
@@ -205,7 +256,10 @@ mita_status mita_landmark(const float* ql, const void* K, const void* V,
 /*
  * Routing and grouping: route [B,H,N] = argmax_i q_n . ql[i] (lowest i on
  * ties), then a stable counting sort of each head's queries by route:
- * counts [B,H,m], offsets [B,H,m+1], perm [B,H,N].  Needs
+ * counts [B,H,m], offsets [B,H,m+1], perm [B,H,N].  Page [ZH],
+ * landmark-query section (each query picks the expert of the landmark it
+ * matches best; the query-landmark scores are the ones the shared branch
+ * reuses) and Algorithm 1 (queries grouped by route).  Needs
  * mita_route_workspace_bytes(...) of scratch (may be 0; workspace may then be
  * NULL).
  */
@@ -218,8 +272,11 @@ mita_status mita_route(const void* Q, const float* ql, int B, int H, int N, int 
 /*
  * Grouped expert attention: for every query, one softmax over its m shared
  * logits and the k logits of its routed expert (idx row route_n), applied to
- * [vl; V[idx]] -> out [B,H,N,d] fp32.  offsets/perm must be the grouping of
- * `route` produced by mita_route.
+ * [vl; V[idx]] -> out [B,H,N,d] fp32.  Page [ZH], landmark-query section
+ * (the s = 1 output: the two sets of key-value pairs are concatenated under
+ * one softmax) and Algorithm 1 (queries grouped by route, partial results
+ * merged by online softmax).  offsets/perm must be the grouping of `route`
+ * produced by mita_route.
  */
 mita_status mita_attend(const void* Q, const void* K, const void* V,
                         const float* ql, const float* vl, const int32_t* idx,

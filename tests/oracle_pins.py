@@ -239,6 +239,36 @@ def pin_key_permutation(O):
         assert sorted(p[b["idx"][i]]) == list(a["idx"][i])
 
 
+# ---------------------------------------------------------------- the batched pass
+def pin_forward_layout(O):
+    """The [B, H] wrapper puts each head's results at its own (b, h), and a
+    ``heads`` list stacks them in the list's order.  Closed forms tell the
+    heads apart: V = c_bh everywhere gives V_L = out = c_bh; pooling to
+    m = N gives Q_L = Q of that head; Q of head (b, h) being zero except in
+    rows it does not share with the others makes its route pattern its own."""
+    rng = _rng(53)
+    B, H, gh, gw = 2, 3, 4, 5
+    N = gh * gw
+    c = 10.0 * np.arange(B)[:, None] + np.arange(H)[None, :] + 0.5      # c[b, h]
+    Q = rng.standard_normal((B, H, N, 8))
+    K = rng.standard_normal((B, H, N, 8))
+    V = np.broadcast_to(c[:, :, None, None], (B, H, N, 8)).copy()
+    r = O.mita_forward(Q, K, V, gh, gw, gh, gw, 3)
+    assert r["out"].shape == (B, H, N, 8) and r["idx"].shape == (B, H, N, 3)
+    assert r["route"].shape == (B, H, N)
+    for b in range(B):
+        for h in range(H):
+            assert np.allclose(r["VL"][b, h], c[b, h], rtol=0, atol=1e-12), (b, h)
+            assert np.allclose(r["out"][b, h], c[b, h], rtol=0, atol=1e-12), (b, h)
+            assert np.array_equal(r["QL"][b, h], Q[b, h]), (b, h)
+    pairs = [(1, 2), (0, 0), (1, 0)]
+    sub = O.mita_forward(Q, K, V, gh, gw, gh, gw, 3, heads=pairs)
+    assert sub["out"].shape == (3, N, 8)
+    for i, (b, h) in enumerate(pairs):
+        assert np.allclose(sub["out"][i], c[b, h], rtol=0, atol=1e-12), (i, b, h)
+        assert np.array_equal(sub["QL"][i], Q[b, h]), (i, b, h)
+
+
 # ---------------------------------------------------------------- the pages' own numbers
 def pin_page_numbers(O):
     """Entries per query (m+k) and the DeiT-S FLOPs drop printed on the pages.

@@ -44,8 +44,15 @@ def test_status_strings():
 
 def test_workspace_bytes():
     ws = mita.mita_workspace_bytes
-    assert ws(256, 6, 14, 14, 64, 5, 5, 25, mita.MITA_BF16) > 0
+    L = mita.lib()
+    # the fused schedule (DeiT shapes) needs no workspace; forcing the staged one does
+    assert L.mita_workspace_bytes(256, 6, 14, 14, 64, 5, 5, 25, mita.MITA_BF16) == 0
+    assert ws(256, 6, 14, 14, 64, 5, 5, 25, mita.MITA_BF16) == 0
+    assert ws(256, 6, 14, 14, 64, 5, 5, 25, mita.MITA_BF16, path="staged") > 0
+    assert ws(256, 6, 14, 14, 64, 5, 5, 25, mita.MITA_F32) > 0      # fp32: staged
+    assert L.mita_workspace_bytes_ex(256, 6, 14, 14, 64, 5, 5, 25, mita.MITA_BF16, None) == 0
     assert ws(32, 6, 56, 56, 64, 7, 7, 64, mita.MITA_BF16) > 0
+    assert ws(32, 6, 56, 56, 64, 7, 7, 64, mita.MITA_BF16, path="fused") == 0  # unsupported
     assert ws(1, 1, 14, 14, 64, 5, 5, 0, mita.MITA_F32) == 0       # k < 1
     assert ws(1, 1, 14, 14, 32, 5, 5, 25, mita.MITA_F32) == 0      # d != 64
     assert ws(1, 1, 14, 14, 64, 15, 5, 25, mita.MITA_F32) == 0     # m_h > grid_h
@@ -105,9 +112,10 @@ def _fwd(B=1, H=1, gh=14, gw=14, d=64, mh=5, mw=5, k=25, dt=mita.MITA_BF16, q=FA
     (dict(d=128), mita.MITA_ERR_UNSUPPORTED),
     (dict(q=None), mita.MITA_ERR_INVALID_ARG),
     (dict(out=None), mita.MITA_ERR_INVALID_ARG),
-    (dict(ws=None), mita.MITA_ERR_INVALID_ARG),
-    (dict(nbytes=16), mita.MITA_ERR_WORKSPACE),
-    (dict(ws=ctypes.c_void_p(0x10010)), mita.MITA_ERR_INVALID_ARG),   # misaligned
+    # fp32 inputs take the staged schedule, which needs a workspace
+    (dict(ws=None, dt=mita.MITA_F32), mita.MITA_ERR_INVALID_ARG),
+    (dict(nbytes=16, dt=mita.MITA_F32), mita.MITA_ERR_WORKSPACE),
+    (dict(ws=ctypes.c_void_p(0x10010), dt=mita.MITA_F32), mita.MITA_ERR_INVALID_ARG),  # misaligned
     (dict(q=ctypes.c_void_p(0x10004)), mita.MITA_ERR_INVALID_ARG),    # Q not 16-byte aligned
     (dict(out=ctypes.c_void_p(0x10008)), mita.MITA_ERR_INVALID_ARG),  # out not 16-byte aligned
     (dict(B=65536), mita.MITA_ERR_UNSUPPORTED),
@@ -120,6 +128,31 @@ def test_forward_rejects_before_launch(kw, status):
 def test_forward_rejects_unknown_path():
     ex = mita._Extras(path=9)
     assert _fwd(extras=ctypes.byref(ex)) == mita.MITA_ERR_INVALID_ARG
+
+
+def test_staged_schedule_needs_a_workspace():
+    ex = mita._Extras(path=mita.PATHS["staged"])
+    assert _fwd(ws=None, nbytes=0, extras=ctypes.byref(ex)) == mita.MITA_ERR_INVALID_ARG
+    assert "workspace" in mita.lib().mita_last_error().decode()
+
+
+@pytest.mark.parametrize("s,ro,status", [(0, 2, mita.MITA_ERR_INVALID_ARG),
+                                         (-1, 0, mita.MITA_ERR_INVALID_ARG),
+                                         (9, 0, mita.MITA_ERR_INVALID_ARG),
+                                         (26, 0, mita.MITA_ERR_INVALID_ARG)])  # s > m = 25
+def test_forward_rejects_bad_variant(s, ro, status):
+    ex = mita._Extras(s=s, route_only=ro)
+    assert _fwd(extras=ctypes.byref(ex)) == status
+    assert mita.lib().mita_last_error().decode() != ""
+
+
+def test_binding_checks_grid_against_tokens():
+    import torch
+    q = torch.zeros(1, 1, 196, 64, dtype=torch.bfloat16)
+    # the grid check runs before the device check would (host tensors here)
+    with pytest.raises(ValueError, match="grid"):
+        mita._grid(q, 14, 15)
+    mita._grid(q, 14, 14)
 
 
 def test_stage_entry_points_validate():

@@ -79,9 +79,19 @@ def _attend_variant(kind):
     return attend
 
 
+def _forward_heads_swapped(Q, K, V, grid_h, grid_w, m_h, m_w, k, heads=None):
+    """The batched wrapper with the (b, h) loop order swapped when stacking."""
+    res = _ORIG["mita_forward"](Q, K, V, grid_h, grid_w, m_h, m_w, k, heads=heads)
+    if heads is None:
+        B, H = np.asarray(Q).shape[:2]
+        return {key: val.reshape((B * H,) + val.shape[2:]).reshape((H, B) + val.shape[2:])
+                .swapaxes(0, 1) for key, val in res.items()}
+    return {key: val[::-1] for key, val in res.items()}
+
+
 _ORIG = {name: getattr(O, name) for name in
          ["pool_windows", "landmark_scores", "expert_topk", "shared_values", "route_queries",
-          "group_by_route", "attend_head"]}
+          "group_by_route", "attend_head", "mita_forward"]}
 
 MUTANTS = {
     "pool_floor_windows": ("pool_windows", _floor_windows),
@@ -96,6 +106,7 @@ MUTANTS = {
     "attend_two_softmaxes": ("attend_head", _attend_variant("two_softmaxes")),
     "attend_wrong_expert": ("attend_head", _attend_variant("wrong_expert")),
     "attend_no_shared": ("attend_head", _attend_variant("no_shared")),
+    "forward_heads_swapped": ("mita_forward", _forward_heads_swapped),
 }
 
 
