@@ -40,6 +40,21 @@ tau = 1/sqrt(d):
                        e = route_n: ONE softmax over the m + k concatenated
                        logits (the shared expert has keys Q_L, values V_L).
 
+Two variants the pages name beside the s = 1 pass ([ZH], landmark-query
+section, "在每个查询选择一个路由专家，即s=1的配置下", which gives the output for
+one routed expert per query; and [ZH], long-sequence section, the ablation
+against a route-only version with the same number of entries per query):
+
+  s > 1      each query goes to its s best landmarks (q_n . Q_L[i] descending,
+             ties to the lowest i) and takes ONE softmax over the m shared
+             entries and the s*k entries of its experts, concatenated in rank
+             order.  The pages do not say whether keys two experts share are
+             merged; the plain reading taken here concatenates them, so such a
+             key appears once per expert that holds it.
+  route-only no shared expert: each query's softmax covers only its routed
+             experts' entries (pass k = m + k_mita for the ablation's equal
+             entry count).  Pooling, scores, top-k and routing are unchanged.
+
 Every function is pinned by tests under ``tests/`` (brute force on tiny
 inputs, library special cases, closed forms and invariants); none is
 "parity unpinned".
@@ -123,17 +138,33 @@ def shared_values(S: np.ndarray, V: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 # step 5: each query goes to the expert of its best-matching landmark
 # --------------------------------------------------------------------------
-def route_queries(Q: np.ndarray, QL: np.ndarray):
-    """route [..., N] (lowest landmark id on ties) and rgap = tau*(R_(1) - R_(2))."""
+def route_queries(Q: np.ndarray, QL: np.ndarray, s: int = 1):
+    """Routes by q . Q_L, ties to the lowest landmark id.
+
+    s = 1: route [..., N] = argmax_i q_n . Q_L[i] and rgap = tau*(R_(1) - R_(2)).
+    s > 1: route [..., N, s], the s best landmarks best first (the stable order
+    of (score descending, id ascending)), and rgap = tau*(R_(s) - R_(s+1)), the
+    margin of the last landmark taken over the first one left out.
+    rgap is +inf when no landmark is left out (s = m).
+    """
     Q = np.asarray(Q, dtype=np.float64)
     R = Q @ np.swapaxes(QL, -1, -2)                  # [..., N, m]
-    route = np.argmax(R, axis=-1)                     # first maximum = lowest id
     m = R.shape[-1]
-    if m == 1:
-        rgap = np.full(R.shape[:-1], np.inf)
-    else:
-        srt = np.sort(R, axis=-1)
-        rgap = (srt[..., -1] - srt[..., -2]) * tau(Q.shape[-1])
+    if not 1 <= s <= m:
+        raise ValueError("need 1 <= s <= m")
+    if s == 1:
+        route = np.argmax(R, axis=-1)                 # first maximum = lowest id
+        if m == 1:
+            rgap = np.full(R.shape[:-1], np.inf)
+        else:
+            srt = np.sort(R, axis=-1)
+            rgap = (srt[..., -1] - srt[..., -2]) * tau(Q.shape[-1])
+        return route, rgap
+    order = np.argsort(-R, axis=-1, kind="stable")   # stable: equal scores keep id order
+    route = order[..., :s]
+    ranked = np.take_along_axis(R, order, axis=-1)
+    rgap = (ranked[..., s - 1] - ranked[..., s]) * tau(Q.shape[-1]) if s < m \
+        else np.full(R.shape[:-1], np.inf)
     return route, rgap
 
 
@@ -141,8 +172,13 @@ def route_queries(Q: np.ndarray, QL: np.ndarray):
 # step 6: group the queries by their route (Algorithm 1)
 # --------------------------------------------------------------------------
 def group_by_route(route: np.ndarray, m: int):
-    """Stable counting sort of one head's queries: counts [m], offsets [m+1], perm [N]."""
-    route = np.asarray(route)
+    """Stable counting sort of one head's queries: counts [m], offsets [m+1], perm [N].
+
+    With s > 1 routes per query (route [N, s]) the sorted items are the
+    (query, rank) pairs t = n*s + j, each under the expert route[n, j]: counts,
+    offsets and perm are then over the N*s items.
+    """
+    route = np.asarray(route).reshape(-1)
     counts = np.bincount(route, minlength=m)
     offsets = np.concatenate([[0], np.cumsum(counts)])
     perm = np.argsort(route, kind="stable")
@@ -152,28 +188,37 @@ def group_by_route(route: np.ndarray, m: int):
 # --------------------------------------------------------------------------
 # step 7: one softmax over shared + routed entries (s = 1)
 # --------------------------------------------------------------------------
-def attend_head(Q, K, V, QL, VL, idx, route, return_weights=False):
+def attend_head(Q, K, V, QL, VL, idx, route, return_weights=False, shared=True):
     """Output of one (b, h): query n attends [Q_L; K[idx_e]] -> [V_L; V[idx_e]], e = route_n.
 
-    The queries are visited expert group by expert group, as Algorithm 1
-    does; each query still gets its own single softmax over m + k logits.
+    route [N] (s = 1) or [N, s] (the query's experts in rank order): the
+    query's entries are then [Q_L; K[idx_e1]; ...; K[idx_es]] with values
+    [V_L; V[idx_e1]; ...], no key merged across experts.  shared=False drops
+    the Q_L / V_L entries (the route-only variant).  The queries are visited
+    group by group (all queries with the same experts), as Algorithm 1
+    groups them by route; each query still gets its own single softmax over
+    all of its (shared and routed) logits.
     """
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
     N, d = Q.shape
     m, k = idx.shape
+    routes = np.asarray(route).reshape(N, -1)               # [N, s]
+    s = routes.shape[1]
     t = tau(d)
     out = np.empty((N, d))
-    weights = np.empty((N, m + k)) if return_weights else None
-    counts, offsets, perm = group_by_route(route, m)
-    for e in range(m):
-        g = perm[offsets[e]:offsets[e + 1]]
-        if g.size == 0:
-            continue
-        keys = np.concatenate([QL, K[idx[e]]], axis=0)     # (m + k) x d
-        vals = np.concatenate([VL, V[idx[e]]], axis=0)
-        w = softmax_rows(t * (Q[g] @ keys.T))               # |g| x (m + k)
+    E = (m if shared else 0) + s * k
+    weights = np.empty((N, E)) if return_weights else None
+    experts, which = np.unique(routes, axis=0, return_inverse=True)
+    which = np.asarray(which).reshape(-1)
+    for gi, ex in enumerate(experts):
+        g = np.nonzero(which == gi)[0]
+        keys = ([QL] if shared else []) + [K[idx[e]] for e in ex]
+        vals = ([VL] if shared else []) + [V[idx[e]] for e in ex]
+        keys = np.concatenate(keys, axis=0)                 # E x d
+        vals = np.concatenate(vals, axis=0)
+        w = softmax_rows(t * (Q[g] @ keys.T))               # |g| x E
         out[g] = w @ vals
         if return_weights:
             weights[g] = w
@@ -183,15 +228,16 @@ def attend_head(Q, K, V, QL, VL, idx, route, return_weights=False):
 # --------------------------------------------------------------------------
 # the whole pass
 # --------------------------------------------------------------------------
-def mita_head(Q, K, V, grid_h, grid_w, m_h, m_w, k, keep_scores=False):
-    """All steps for one (b, h); Q, K, V are [N, d]."""
+def mita_head(Q, K, V, grid_h, grid_w, m_h, m_w, k, keep_scores=False, s=1, shared=True):
+    """All steps for one (b, h); Q, K, V are [N, d].  s: experts per query;
+    shared=False: the route-only variant (V_L is still returned, unused)."""
     QL = landmark_queries(Q, grid_h, grid_w, m_h, m_w)
     S = landmark_scores(QL, K)
     idx, gap = expert_topk(S, k)
     VL = shared_values(S, V)
-    route, rgap = route_queries(Q, QL)
+    route, rgap = route_queries(Q, QL, s)
     counts, offsets, perm = group_by_route(route, QL.shape[0])
-    out = attend_head(Q, K, V, QL, VL, idx, route)
+    out = attend_head(Q, K, V, QL, VL, idx, route, shared=shared)
     res = dict(QL=QL, idx=idx, gap=gap, VL=VL, route=route, rgap=rgap,
                counts=counts, offsets=offsets, perm=perm, out=out)
     if keep_scores:
@@ -199,7 +245,7 @@ def mita_head(Q, K, V, grid_h, grid_w, m_h, m_w, k, keep_scores=False):
     return res
 
 
-def mita_forward(Q, K, V, grid_h, grid_w, m_h, m_w, k, heads=None):
+def mita_forward(Q, K, V, grid_h, grid_w, m_h, m_w, k, heads=None, s=1, shared=True):
     """The pass over [B, H, N, d] inputs, head by head.
 
     ``heads`` optionally restricts the work to a list of (b, h) pairs; the
@@ -210,7 +256,8 @@ def mita_forward(Q, K, V, grid_h, grid_w, m_h, m_w, k, heads=None):
     if grid_h * grid_w != N:
         raise ValueError("grid does not match N")
     pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
-    per = [mita_head(Q[b, h], K[b, h], V[b, h], grid_h, grid_w, m_h, m_w, k) for b, h in pairs]
+    per = [mita_head(Q[b, h], K[b, h], V[b, h], grid_h, grid_w, m_h, m_w, k, s=s, shared=shared)
+           for b, h in pairs]
     res = {key: np.stack([p[key] for p in per]) for key in per[0]}
     if heads is None:
         res = {key: val.reshape((B, H) + val.shape[1:]) for key, val in res.items()}

@@ -239,6 +239,129 @@ def pin_key_permutation(O):
         assert sorted(p[b["idx"][i]]) == list(a["idx"][i])
 
 
+# ---------------------------------------------------------------- variants: s > 1, route-only
+def _brute_top_s(vals, s):
+    """The s ids of largest value, best first, ties to the lower id, by pairwise rank
+    counting; and the gap between the s-th and the (s+1)-th (inf when none is left)."""
+    n = len(vals)
+    by_rank = {}
+    for i in range(n):
+        r = sum(1 for j in range(n) if vals[j] > vals[i] or (vals[j] == vals[i] and j < i))
+        by_rank[r] = i
+    gap = vals[by_rank[s - 1]] - vals[by_rank[s]] if s < n else math.inf
+    return [by_rank[r] for r in range(s)], gap
+
+
+def pin_route_top_s_bruteforce(O):
+    """Top-s routing equals pairwise rank counting on exact (integer) dot products, with
+    duplicated landmarks forcing ties, for several s up to s = m."""
+    rng = _rng(59)
+    Q = rng.integers(-2, 3, size=(30, 5)).astype(np.float64)
+    QL = rng.integers(-2, 3, size=(9, 5)).astype(np.float64)
+    QL[5] = QL[2]
+    QL[8] = QL[0]
+    for s in (2, 3, 9):
+        route, rgap = O.route_queries(Q, QL, s)
+        assert route.shape == (30, s)
+        for n in range(30):
+            vals = [sum(float(Q[n, c]) * float(QL[i, c]) for c in range(5)) for i in range(9)]
+            sel, g = _brute_top_s(vals, s)
+            assert list(route[n]) == sel, (s, n)
+            want = g / math.sqrt(5)
+            assert rgap[n] == want or (math.isinf(want) and math.isinf(rgap[n])), (s, n)
+
+
+def pin_group_items(O):
+    """With s routes per query the grouped items are t = n*s + j: perm is Python's stable
+    sort of the item ids by expert, counts a tally of the items per expert."""
+    rng = _rng(67)
+    routes = rng.integers(0, 5, size=(17, 3))
+    counts, offsets, perm = O.group_by_route(routes, 6)
+    flat = [int(routes[t // 3, t % 3]) for t in range(51)]
+    assert list(perm) == sorted(range(51), key=lambda t: flat[t])
+    assert list(counts) == [flat.count(e) for e in range(6)]
+    assert list(offsets) == [sum(flat.count(e) for e in range(i)) for i in range(7)]
+
+
+def _log_count_mask(N, m, idx, routes, shared):
+    """Additive mask over the columns [Q_L; K] (or K alone): 0 on the shared columns, log c
+    on a key that c of the query's experts hold, -inf on keys none of them holds."""
+    routes = np.asarray(routes).reshape(len(routes), -1)
+    off = m if shared else 0
+    mask = np.full((len(routes), off + N), -np.inf)
+    mask[:, :off] = 0.0
+    for n in range(len(routes)):
+        held = [0] * N
+        for e in routes[n]:
+            for j in idx[e]:
+                held[j] += 1
+        for j in range(N):
+            if held[j]:
+                mask[n, off + j] = math.log(held[j])
+    return mask
+
+
+def pin_multi_expert_masked(O):
+    """s experts per query, shared or route-only: out equals dense attention (torch SDPA)
+    over [Q_L; K] (or K) under an additive log-count mask, i.e. one softmax in which a key
+    held by c of the query's experts counts c times (no key merged across experts)."""
+    rng = _rng(61)
+    repeats = 0
+    for gh, gw, mh, mw, k, s in [(6, 6, 2, 3, 14, 2), (5, 8, 2, 2, 20, 3), (7, 7, 3, 3, 5, 4),
+                                 (4, 6, 2, 2, 6, 1)]:
+        N, m = gh * gw, mh * mw
+        Q, K, V = (rng.standard_normal((N, 16)) for _ in range(3))
+        for shared in (True, False):
+            r = O.mita_head(Q, K, V, gh, gw, mh, mw, k, s=s, shared=shared)
+            mask = _log_count_mask(N, m, r["idx"], r["route"], shared)
+            repeats += int(np.sum(mask > 0))
+            keys = np.concatenate([r["QL"], K]) if shared else K
+            vals = np.concatenate([r["VL"], V]) if shared else V
+            ref = _sdpa(Q, keys, vals, mask)
+            assert np.allclose(r["out"], ref, rtol=0, atol=1e-12), (gh, gw, mh, mw, k, s, shared)
+    assert repeats > 0, "the cases must contain keys held by two experts of one query"
+
+
+def pin_route_only_dense(O):
+    """Route-only with k = N: every expert is all keys, so for any s the output is textbook
+    attention softmax(Q K^T / sqrt(d)) V (repeating every key s times changes no weight)."""
+    rng = _rng(71)
+    Q, K, V = (rng.standard_normal((5 * 6, 16)) for _ in range(3))
+    ref = _sdpa(Q, K, V)
+    for s in (1, 2, 4):
+        r = O.mita_head(Q, K, V, 5, 6, 2, 2, 30, s=s, shared=False)
+        assert np.allclose(r["out"], ref, rtol=0, atol=1e-12), s
+
+
+def pin_multi_expert_dense(O):
+    """Shared expert, k = N, s experts: every key is held s times, so out is attention over
+    [Q_L; K] with log(s) added to each key's logit (a closed form)."""
+    rng = _rng(73)
+    Q, K, V = (rng.standard_normal((6 * 5, 16)) for _ in range(3))
+    for s in (2, 3):
+        r = O.mita_head(Q, K, V, 6, 5, 2, 3, 30, s=s)
+        mask = np.concatenate([np.zeros((30, 6)), np.full((30, 30), math.log(s))], axis=1)
+        ref = _sdpa(Q, np.concatenate([r["QL"], K]), np.concatenate([r["VL"], V]), mask)
+        assert np.allclose(r["out"], ref, rtol=0, atol=1e-12), s
+
+
+def pin_variant_entry_counts(O):
+    """Each query spreads one softmax over exactly (m if shared) + s*k entries, summing to 1;
+    the route-only ablation at k' = m + k has the full method's entry count."""
+    rng = _rng(79)
+    Q, K, V = (rng.standard_normal((7 * 7, 8)) for _ in range(3))
+    m, k = 9, 6
+    for s, shared, kk in [(1, True, k), (3, True, k), (1, False, m + k), (2, False, m + k)]:
+        QL = O.landmark_queries(Q, 7, 7, 3, 3)
+        S = O.landmark_scores(QL, K)
+        idx, _ = O.expert_topk(S, kk)
+        route, _ = O.route_queries(Q, QL, s)
+        _, w = O.attend_head(Q, K, V, QL, O.shared_values(S, V), idx, route,
+                             return_weights=True, shared=shared)
+        assert w.shape == (49, (m if shared else 0) + s * kk)
+        assert np.all(w >= 0) and np.allclose(w.sum(1), 1.0, rtol=0, atol=1e-12)
+
+
 # ---------------------------------------------------------------- the batched pass
 def pin_forward_layout(O):
     """The [B, H] wrapper puts each head's results at its own (b, h), and a

@@ -35,19 +35,25 @@ def _shared_wrong_axis(S, V):
     return (z / z.sum(axis=-2, keepdims=True)) @ np.asarray(V, dtype=np.float64)
 
 
-def _route_high_ties(Q, QL):
+def _route_high_ties(Q, QL, s=1):
     R = np.asarray(Q, dtype=np.float64) @ np.swapaxes(QL, -1, -2)
     m = R.shape[-1]
+    if s > 1:
+        order = m - 1 - np.argsort(-R[..., ::-1], axis=-1, kind="stable")
+        return order[..., :s], _ORIG["route_queries"](Q, QL, s)[1]
     route = m - 1 - np.argmax(R[..., ::-1], axis=-1)
     return route, _ORIG["route_queries"](Q, QL)[1]
 
 
-def _route_argmin(Q, QL):
+def _route_argmin(Q, QL, s=1):
     R = np.asarray(Q, dtype=np.float64) @ np.swapaxes(QL, -1, -2)
+    if s > 1:
+        return np.argsort(R, axis=-1, kind="stable")[..., :s], _ORIG["route_queries"](Q, QL, s)[1]
     return np.argmin(R, axis=-1), _ORIG["route_queries"](Q, QL)[1]
 
 
 def _group_reversed(route, m):
+    route = np.asarray(route).reshape(-1)
     counts, offsets, _ = _ORIG["group_by_route"](route, m)
     n = np.arange(len(route))
     perm = np.lexsort((-n, route))
@@ -55,7 +61,12 @@ def _group_reversed(route, m):
 
 
 def _attend_variant(kind):
-    def attend(Q, K, V, QL, VL, idx, route, return_weights=False):
+    """The attend step written per query for s = 1 with one planted mistake
+    (or none, for "plain"); with s > 1 or without the shared expert it defers
+    to the oracle, so that only the s = 1 pins see the mistake."""
+    def attend(Q, K, V, QL, VL, idx, route, return_weights=False, shared=True):
+        if np.asarray(route).ndim > 1 or not shared:
+            return _ORIG["attend_head"](Q, K, V, QL, VL, idx, route, return_weights, shared)
         Q = np.asarray(Q, dtype=np.float64); K = np.asarray(K, dtype=np.float64)
         V = np.asarray(V, dtype=np.float64)
         N, d = Q.shape
@@ -79,14 +90,43 @@ def _attend_variant(kind):
     return attend
 
 
-def _forward_heads_swapped(Q, K, V, grid_h, grid_w, m_h, m_w, k, heads=None):
+def _forward_heads_swapped(Q, K, V, grid_h, grid_w, m_h, m_w, k, heads=None, **kw):
     """The batched wrapper with the (b, h) loop order swapped when stacking."""
-    res = _ORIG["mita_forward"](Q, K, V, grid_h, grid_w, m_h, m_w, k, heads=heads)
+    res = _ORIG["mita_forward"](Q, K, V, grid_h, grid_w, m_h, m_w, k, heads=heads, **kw)
     if heads is None:
         B, H = np.asarray(Q).shape[:2]
         return {key: val.reshape((B * H,) + val.shape[2:]).reshape((H, B) + val.shape[2:])
                 .swapaxes(0, 1) for key, val in res.items()}
     return {key: val[::-1] for key, val in res.items()}
+
+
+def _attend_multi(kind):
+    """The attend step for s > 1 / route-only with one planted mistake; the s = 1 shared
+    pass defers to the oracle."""
+    def attend(Q, K, V, QL, VL, idx, route, return_weights=False, shared=True):
+        route = np.asarray(route)
+        if route.ndim == 1 and shared:
+            return _ORIG["attend_head"](Q, K, V, QL, VL, idx, route, return_weights, shared)
+        Q = np.asarray(Q, dtype=np.float64); K = np.asarray(K, dtype=np.float64)
+        V = np.asarray(V, dtype=np.float64)
+        N, d = Q.shape
+        routes = route.reshape(N, -1)
+        t = 1.0 / np.sqrt(d)
+        out = np.empty((N, d))
+        W = []
+        for n in range(N):
+            ex = routes[n][:1] if kind == "first_only" else routes[n]
+            keys_id = np.concatenate([idx[e] for e in ex])
+            if kind == "dedup":
+                keys_id = np.unique(keys_id)
+            with_shared = shared or kind == "keeps_shared"
+            keys = np.concatenate(([QL] if with_shared else []) + [K[keys_id]])
+            vals = np.concatenate(([VL] if with_shared else []) + [V[keys_id]])
+            z = t * (keys @ Q[n]); w = np.exp(z - z.max()); w /= w.sum()
+            out[n] = w @ vals
+            W.append(w)
+        return (out, np.array(W, dtype=object)) if return_weights else out
+    return attend
 
 
 _ORIG = {name: getattr(O, name) for name in
@@ -107,6 +147,13 @@ MUTANTS = {
     "attend_wrong_expert": ("attend_head", _attend_variant("wrong_expert")),
     "attend_no_shared": ("attend_head", _attend_variant("no_shared")),
     "forward_heads_swapped": ("mita_forward", _forward_heads_swapped),
+    "multi_expert_dedup": ("attend_head", _attend_multi("dedup")),
+    "multi_expert_first_only": ("attend_head", _attend_multi("first_only")),
+    "route_only_keeps_shared": ("attend_head", _attend_multi("keeps_shared")),
+    "route_top_s_unsorted": ("route_queries",
+                             lambda Q, QL, s=1: (np.sort(_ORIG["route_queries"](Q, QL, s)[0], -1)
+                                                 if s > 1 else _ORIG["route_queries"](Q, QL, s)[0],
+                                                 _ORIG["route_queries"](Q, QL, s)[1])),
 }
 
 
