@@ -25,7 +25,7 @@ PATHS = {"auto": 0, "fused": 1, "staged": 2}
 EXPORTS = [
     "mita_status_string", "mita_last_error", "mita_version", "mita_workspace_bytes",
     "mita_workspace_bytes_ex", "mita_schedule", "mita_kernel_names", "mita_sync_event_create",
-    "mita_forward", "mita_forward_ex", "mita_pool", "mita_landmark_workspace_bytes",
+    "mita_forward", "mita_forward_ex", "mita_forward_noalloc", "mita_pool", "mita_landmark_workspace_bytes",
     "mita_landmark", "mita_route_workspace_bytes", "mita_route", "mita_attend",
 ]
 
@@ -76,6 +76,8 @@ def lib() -> ctypes.CDLL:
         L.mita_sync_event_create.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         L.mita_forward.restype = S
         L.mita_forward.argtypes = [P, P, P] + [I] * 8 + [I, P, P, P, P, Z, P]
+        L.mita_forward_noalloc.restype = S
+        L.mita_forward_noalloc.argtypes = [P, P, P] + [I] * 8 + [I, P, P, P, P]
         L.mita_forward_ex.restype = S
         L.mita_forward_ex.argtypes = [P, P, P] + [I] * 8 + [I, P, P, P, ctypes.POINTER(_Extras),
                                                             P, Z, P]
@@ -180,6 +182,30 @@ def mita_forward(q, k, v, grid_h, grid_w, m_h, m_w, topk, *, out=None, idx=None,
     """Whole pass; returns out [B,H,N,d] fp32.  idx/route are optional int32 outputs."""
     return mita_forward_ex(q, k, v, grid_h, grid_w, m_h, m_w, topk, out=out, idx=idx,
                            route=route, workspace=workspace, stream=stream)["out"]
+
+
+def mita_forward_noalloc(q, k, v, grid_h, grid_w, m_h, m_w, topk, *, out=None, idx=None,
+                         route=None, stream=None):
+    """The plain pass through mita_forward_noalloc (no workspace: the library's static
+    device scratch).  Returns dict(out, idx, route); idx/route as in mita_forward_ex."""
+    code, torch = _qkv(q, k, v)
+    _grid(q, grid_h, grid_w)
+    B, H, N, d = q.shape
+    m = m_h * m_w
+    i32 = torch.int32
+
+    def alloc(x, shape, dtype, name):
+        if x is True:
+            return torch.empty(shape, dtype=dtype, device=q.device)
+        return _dev(x, name, dtype, shape) if x is not None else None
+
+    out = alloc(True if out is None else out, (B, H, N, d), torch.float32, "out")
+    idx = alloc(idx, (B, H, m, topk), i32, "idx")
+    route = alloc(route, (B, H, N), i32, "route")
+    _check(lib().mita_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), B, H, grid_h, grid_w, d, m_h,
+                                      m_w, topk, code, _ptr(out), _ptr(idx), _ptr(route),
+                                      _stream(q, stream)))
+    return dict(out=out, idx=idx, route=route)
 
 
 def mita_kernel_schedule(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code, path="auto",

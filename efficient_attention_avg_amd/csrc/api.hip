@@ -2,6 +2,7 @@
 // sequence of the MiTA forward pass.  No allocation, no host copies, no
 // synchronisation: everything is enqueued on the caller's stream.
 #include <initializer_list>
+#include <mutex>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -9,6 +10,13 @@
 
 #include "../../include/mita.h"
 #include "internal.h"
+
+// Device scratch of mita_forward_noalloc: the staged schedule's workspace for
+// callers that cannot allocate.  Each GPU the library runs on holds its own
+// copy until the process ends.  In host code this name is only a stand-in:
+// kernels and copies get the address hipGetSymbolAddress returns for the
+// current device (scratch_address below), never the name itself.
+static __device__ __align__(256) char scratch[MITA_NOALLOC_SCRATCH_BYTES];
 
 
 using mita::Shape;
@@ -196,6 +204,30 @@ P* pick(P* user, void* ws, size_t off) {
   return user ? user : (P*)((char*)ws + off);
 }
 
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+mita_status scratch_address(void** ptr) {
+  int dev = -1;
+  if (const hipError_t e = hipGetDevice(&dev); e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MITA_ERR_UNSUPPORTED, "device %d: the static scratch serves devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); e != hipSuccess)
+      return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MITA_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MITA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -371,6 +403,25 @@ mita_status mita_forward(const void* Q, const void* K, const void* V, int B, int
                          size_t workspace_bytes, hipStream_t stream) {
   return mita_forward_ex(Q, K, V, B, H, grid_h, grid_w, d, m_h, m_w, k, in_dtype, out, idx, route,
                          nullptr, workspace, workspace_bytes, stream);
+}
+
+mita_status mita_forward_noalloc(const void* Q, const void* K, const void* V, int B, int H,
+                                int grid_h, int grid_w, int d, int m_h, int m_w, int k,
+                                mita_dtype in_dtype, float* out, int32_t* idx, int32_t* route,
+                                hipStream_t stream) {
+  Shape s;
+  mita_status st = make_shape(B, H, grid_h, grid_w, d, m_h, m_w, k, in_dtype, &s);
+  if (st != MITA_OK) return st;
+  const size_t need = runs_fused(MITA_PATH_AUTO, s) ? 0 : layout_of(s).total;
+  if (need > (size_t)MITA_NOALLOC_SCRATCH_BYTES)
+    return fail(MITA_ERR_WORKSPACE,
+                "this shape needs %zu bytes of scratch; the static scratch holds %zu "
+                "(use mita_forward with a workspace)",
+                need, (size_t)MITA_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need > 0 && (st = scratch_address(&ws)) != MITA_OK) return st;
+  return mita_forward_ex(Q, K, V, B, H, grid_h, grid_w, d, m_h, m_w, k, in_dtype, out, idx, route,
+                         nullptr, ws, need, stream);
 }
 
 mita_status mita_pool(const void* Q, int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w,

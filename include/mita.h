@@ -113,6 +113,27 @@ mita_status mita_forward(const void* Q, const void* K, const void* V,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * mita_forward without a workspace, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, results and plain pass (s = 1, shared
+ * expert, automatic schedule, every kernel on `stream`) as mita_forward; the
+ * staged schedule's intermediates go to a static device array of
+ * MITA_NOALLOC_SCRATCH_BYTES inside the library instead (one per GPU, held
+ * until the process ends; the fused schedule needs none).  The call
+ * allocates and frees nothing.  A shape whose workspace
+ * (mita_workspace_bytes) exceeds the array is MITA_ERR_WORKSPACE, nothing
+ * launched.  Every call on one GPU shares that GPU's array and leaves its
+ * contents behind; the kernels write every byte they read within a call, so
+ * nothing needs clearing, but calls that overlap on one GPU (two streams, two
+ * host threads) race on it and must be serialised by the caller.
+ */
+#define MITA_NOALLOC_SCRATCH_BYTES (32u << 20)
+mita_status mita_forward_noalloc(const void* Q, const void* K, const void* V,
+                                 int B, int H, int grid_h, int grid_w, int d,
+                                 int m_h, int m_w, int k, mita_dtype in_dtype,
+                                 float* out, int32_t* idx, int32_t* route, hipStream_t stream);
+
+/*
  * Optional extra outputs of mita_forward_ex (any member may be NULL), the
  * schedule to run, the method variant, and optional per-kernel timing
  * events.  Zero-initialised it asks for the plain pass.  Used to check every

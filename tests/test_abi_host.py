@@ -181,3 +181,14 @@ def test_binding_refuses_host_tensors():
     q = torch.zeros(1, 1, 196, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         mita.mita_forward(q, q, q, 14, 14, 5, 5, 25)
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    L = mita.lib()
+    # 1024 heads of 3136 tokens need far more than the 32 MiB static scratch;
+    # refused before any device call
+    assert L.mita_forward_noalloc(FAKE, FAKE, FAKE, 128, 8, 56, 56, 64, 7, 7, 64, mita.MITA_BF16,
+                                  FAKE, None, None, None) == mita.MITA_ERR_WORKSPACE
+    assert "scratch" in L.mita_last_error().decode()
+    assert L.mita_forward_noalloc(FAKE, FAKE, FAKE, 1, 1, 14, 14, 64, 5, 5, 0, mita.MITA_BF16,
+                                  FAKE, None, None, None) == mita.MITA_ERR_INVALID_ARG
