@@ -98,8 +98,6 @@ mita_status set_variant(const mita_extras* ex, Shape* s) {
   if (ro != 0 && ro != 1) return fail(MITA_ERR_INVALID_ARG, "route_only must be 0 or 1");
   s->s = sv;
   s->shared = ro == 0;
-  if (s->s != 1 || !s->shared)
-    return fail(MITA_ERR_UNSUPPORTED, "the s > 1 and route-only variants are not built yet");
   return MITA_OK;
 }
 
@@ -164,22 +162,28 @@ mita_status run_route(const void* Q, const float* ql, int32_t* route, int32_t* c
   if (mk) mk->mark(st);
   return r;
 }
+// s > 1 on the matrix-core attention kernel: per-item partials, then a merge
+bool merges(const Shape& s) { return s.s > 1 && attend_mfma(s); }
+
 mita_status run_attend(const void* Q, const void* K, const void* V, const float* ql,
                        const float* vl, const int32_t* idx, const int32_t* route,
-                       const int32_t* offsets, const int32_t* perm, float* out, const Shape& s,
-                       hipStream_t st, Marker* mk = nullptr) {
-  const mita_status r = hip_status(
+                       const int32_t* offsets, const int32_t* perm, float* out, void* partial,
+                       const Shape& s, hipStream_t st, Marker* mk = nullptr) {
+  mita_status r = hip_status(
       attend_mfma(s)
-          ? mita::launch_attend_bf16(Q, K, V, ql, vl, idx, offsets, perm, out, s, st)
+          ? mita::launch_attend_bf16(Q, K, V, ql, vl, idx, offsets, perm, out, partial, s, st)
           : mita::launch_attend(Q, K, V, ql, vl, idx, route, offsets, perm, out, s, st),
       "attend launch");
+  if (mk) mk->mark(st);
+  if (r != MITA_OK || !merges(s)) return r;
+  r = hip_status(mita::launch_merge(partial, out, s, st), "merge launch");
   if (mk) mk->mark(st);
   return r;
 }
 // Workspace of the staged schedule: every intermediate the caller did not
 // supply, then the landmark and route steps' scratch.
 struct Layout {
-  size_t ql, vl, idx, route, counts, offsets, perm, scratch, rscratch, total;
+  size_t ql, vl, idx, route, counts, offsets, perm, scratch, rscratch, partial, total;
 };
 
 Layout layout_of(const Shape& s) {
@@ -189,12 +193,13 @@ Layout layout_of(const Shape& s) {
   L.ql = take((size_t)s.BH * s.m * s.d * 4);
   L.vl = take((size_t)s.BH * s.m * s.d * 4);
   L.idx = take((size_t)s.BH * s.m * s.k * 4);
-  L.route = take((size_t)s.BH * s.N * 4);
+  L.route = take((size_t)s.BH * s.N * s.s * 4);
   L.counts = take((size_t)s.BH * s.m * 4);
   L.offsets = take((size_t)s.BH * (s.m + 1) * 4);
-  L.perm = take((size_t)s.BH * s.N * 4);
+  L.perm = take((size_t)s.BH * s.N * s.s * 4);
   L.scratch = take(landmark_scratch(s));
   L.rscratch = take(route_scratch(s));
+  L.partial = take(merges(s) ? mita::attend_partial_bytes(s) : 0);
   L.total = off;
   return L;
 }
@@ -328,7 +333,9 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V, int B, 
   }
 
   float* ql = pick(extras ? extras->ql : nullptr, workspace, L.ql);
-  float* vl = pick(extras ? extras->vl : nullptr, workspace, L.vl);
+  // route-only computes no landmark values for the caller: its V_L goes to
+  // the workspace, and a caller's vl is left untouched
+  float* vl = pick(extras && s.shared ? extras->vl : nullptr, workspace, L.vl);
   int32_t* counts = pick(extras ? extras->counts : nullptr, workspace, L.counts);
   int32_t* offsets = pick(extras ? extras->offsets : nullptr, workspace, L.offsets);
   int32_t* perm = pick(extras ? extras->perm : nullptr, workspace, L.perm);
@@ -336,6 +343,7 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V, int B, 
   int32_t* route_p = pick(route, workspace, L.route);
   void* scratch = (char*)workspace + L.scratch;
   void* rscratch = (char*)workspace + L.rscratch;
+  void* partial = (char*)workspace + L.partial;
 
   if ((st = run_pool(Q, ql, s, stream, &mk)) != MITA_OK) return st;
   {
@@ -364,8 +372,8 @@ mita_status mita_forward_ex(const void* Q, const void* K, const void* V, int B, 
       if ((st = run_landmark(ql, K, V, idx_p, vl, scratch, s, stream, &mk)) != MITA_OK) return st;
     }
   }
-  if ((st = run_attend(Q, K, V, ql, vl, idx_p, route_p, offsets, perm, out, s, stream, &mk)) !=
-      MITA_OK)
+  if ((st = run_attend(Q, K, V, ql, vl, idx_p, route_p, offsets, perm, out, partial, s, stream,
+                       &mk)) != MITA_OK)
     return st;
   return ok();
 }
@@ -382,13 +390,13 @@ int mita_kernel_names(int B, int H, int grid_h, int grid_w, int d, int m_h, int 
   const bool forked = extras && extras->side_stream;
   static const char* const kFused[] = {"fused"};
   static const int kFusedStart[] = {0};
-  static const char* const kStaged[] = {"pool", "route", "group", "landmark", "attend"};
-  static const int kStagedStart[] = {0, 1, 2, 3, 4};
-  static const int kForkedStart[] = {0, 1, 2, 1, 4};
+  static const char* const kStaged[] = {"pool", "route", "group", "landmark", "attend", "merge"};
+  static const int kStagedStart[] = {0, 1, 2, 3, 4, 5};
+  static const int kForkedStart[] = {0, 1, 2, 1, 4, 5};
   const bool fused = runs_fused(path, s);
   const char* const* list = fused ? kFused : kStaged;
   const int* start = fused ? kFusedStart : forked ? kForkedStart : kStagedStart;
-  const int n = fused ? 1 : 5;
+  const int n = fused ? 1 : merges(s) ? 6 : 5;
   for (int i = 0; i < n && i < capacity; ++i) {
     if (names) names[i] = list[i];
     if (starts) starts[i] = start[i];
@@ -496,7 +504,8 @@ mita_status mita_attend(const void* Q, const void* K, const void* V, const float
     return fail(MITA_ERR_INVALID_ARG, "every tensor argument of mita_attend is required");
   if (!aligned16({Q, K, V, ql, vl, out}))
     return fail(MITA_ERR_INVALID_ARG, "Q, K, V, ql, vl and out must be 16-byte aligned");
-  if ((st = run_attend(Q, K, V, ql, vl, idx, route, offsets, perm, out, s, stream)) != MITA_OK)
+  if ((st = run_attend(Q, K, V, ql, vl, idx, route, offsets, perm, out, nullptr, s, stream)) !=
+      MITA_OK)
     return st;
   return ok();
 }

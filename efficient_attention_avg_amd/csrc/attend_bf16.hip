@@ -21,6 +21,12 @@
 //     each chunk's weights go straight from the logit accumulators into
 //     out^T += [V_L; V_e]^T P^T on f16 MFMA, with the normaliser from an
 //     all-ones MFMA.
+// With s experts per query the grouped items are the (query, rank) pairs
+// t = n * s + j: an item attends its expert's keys, plus the shared entries
+// when j = 0 (masked to -inf for the others), and leaves its unnormalised
+// sums and softmax reference (max, sum) in a partial buffer; merge_kernel then
+// combines a query's s partials by log-sum-exp into its one softmax.  The
+// route-only variant skips the shared entries.
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
@@ -44,8 +50,10 @@ struct Args {
   const int32_t* idx;
   const int32_t* offsets;
   const int32_t* perm;
-  float* out;
+  float* out;    // s = 1: the output; s > 1: unnormalised partial sums per item
+  float2* pml;   // s > 1: each item's softmax reference maximum and sum
   int BH, N, m, k, parts;  // workgroups per head
+  int s, shared;
 };
 
 // LDS layout; the expert table holds, per expert of the workgroup,
@@ -112,10 +120,12 @@ __device__ __forceinline__ void softmax_update(const float (&x)[8 * NC], GetAv g
   }
 }
 
-// A pass's result for this lane's query, written to out row nq when live.
+// A pass's result for this lane's query (or item), written to row nq when
+// live.
 struct PassOut {
   f32x4 acc[4];
   float inv;
+  float mref, lsum;
   int nq;
   bool live;
 };
@@ -166,7 +176,8 @@ void attend_bf16_kernel(Args a) {
   const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
   const int bh = xcd + 8 * (slot / a.parts), part = slot % a.parts;
   if (bh >= a.BH || part >= a.m) return;
-  const int N = a.N, m = a.m, k = a.k, P = a.parts;
+  const int N = a.N, m = a.m, k = a.k, P = a.parts, S = a.s;
+  const bool shared = a.shared != 0;
   // The head's experts are dealt to its P workgroups in a snake (0, 1, ..,
   // P-1, P-1, .., 0, ...) in order of their passes (then queries, then id),
   // largest first, so that the workgroups' pass totals even out; every
@@ -197,9 +208,11 @@ void attend_bf16_kernel(Args a) {
   const uint16_t* Kh = a.K + (size_t)bh * N * 64;
   const uint16_t* Vh = a.V + (size_t)bh * N * 64;
   const int32_t* offs = a.offsets + (size_t)bh * (m + 1);
-  const int32_t* permh = a.perm + (size_t)bh * N;
+  const int32_t* permh = a.perm + (size_t)bh * N * S;
   const int32_t* idxh = a.idx + (size_t)bh * m * k;
-  const Rsrc outr = out_rows(a.out + (size_t)bh * N * 64, N);
+  // s = 1: output rows of the queries; s > 1: partial rows of the N * s items
+  const Rsrc outr = out_rows(a.out + (size_t)bh * N * S * 64, N * S);
+  float2* pmlh = S > 1 ? a.pml + (size_t)bh * N * S : nullptr;
   int* tab = reinterpret_cast<int*>(sm + L.off_tab);
   const u32x4 z = {0u, 0u, 0u, 0u};
 
@@ -239,8 +252,8 @@ void attend_bf16_kernel(Args a) {
     }
   }
   // ---- Q_L (hi / lo) and V_L^T for the head; rows past m are zero.  All of
-  // a thread's loads go out before any is used.
-  for (int base = 0; base < L.mp * 16; base += 256 * 4) {
+  // a thread's loads go out before any is used.  (None for route-only.)
+  for (int base = 0; shared && base < L.mp * 16; base += 256 * 4) {
     float4 fq[4], fv[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -292,7 +305,8 @@ void attend_bf16_kernel(Args a) {
     r.v0 = b0 < k ? *reinterpret_cast<const u32x4*>(Vh + (size_t)ke[b0] * 64 + 8 * vc) : z;
     r.v1 = b1 < k ? *reinterpret_cast<const u32x4*>(Vh + (size_t)ke[b1] * 64 + 8 * vc) : z;
     if (s0 == 0) {
-      const int n = max(te[2 + k + 16 * w + c16], 0);
+      const int t = max(te[2 + k + 16 * w + c16], 0);
+      const int n = S == 1 ? t : t / S;
       r.q0r = *reinterpret_cast<const u32x4*>(Qh + (size_t)n * 64 + 8 * g);
       r.q1r = *reinterpret_cast<const u32x4*>(Qh + (size_t)n * 64 + 32 + 8 * g);
     }
@@ -309,8 +323,9 @@ void attend_bf16_kernel(Args a) {
     }
   };
 
-  // logits of 32 shared entries (landmarks 32c ..) into x[0..8)
-  auto shared_logits = [&](int c, const u32x4 bq0, const u32x4 bq1, float* x) {
+  // logits of 32 shared entries (landmarks 32c ..) into x[0..8); -inf for
+  // a lane whose item does not take the shared entries (rank j > 0)
+  auto shared_logits = [&](int c, const u32x4 bq0, const u32x4 bq1, float* x, bool sh) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int row = 32 * c + 16 * h + c16;
@@ -332,6 +347,10 @@ void attend_bf16_kernel(Args a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (32 * c + 16 * h + 4 * g + r >= m) x[4 * h + r] = -INFINITY;
+    }
+    if (S > 1) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = sh ? x[i] : -INFINITY;
     }
   };
   auto shared_av = [&](int c, u32x4 (&av)[4]) {
@@ -374,31 +393,36 @@ void attend_bf16_kernel(Args a) {
     }
   };
 
-  // one pass over <= 64 queries of expert j starting at p0
-  auto run_pass = [&](int j, int p0, int nq, const u32x4 bq0, const u32x4 bq1) {
+  // one pass over <= 64 queries (items) of expert j starting at p0; `item`
+  // is this lane's query (s = 1) or (query, rank) item
+  auto run_pass = [&](int j, int p0, int item, const u32x4 bq0, const u32x4 bq1) {
     const int* te = tab + j * L.ts;
     const int cnt = te[1];
     const int qi = p0 + 16 * w + c16;
     const bool wave_has = p0 + 16 * w < cnt;
-    float mref = -INFINITY;
+    // (finite: a column whose shared logits are all masked must not make
+    // the first rescale exp2(-inf - -inf))
+    float mref = -1e30f;
     PassOut o;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) o.acc[ct] = zero4();
     f32x4 lsum = zero4();
-    // ---- shared entries: landmarks, 64 per softmax update
-    if (wave_has) {
+    // ---- shared entries: landmarks, 64 per softmax update (only rank 0
+    // items take them when s > 1)
+    const bool sh = shared && (S == 1 || item % S == 0);
+    if (wave_has && __ballot(sh) != 0) {
       const int nc = L.mp / 32;
       int c = 0;
       for (; c + 2 <= nc; c += 2) {
         float x[16];
-        shared_logits(c, bq0, bq1, x);
-        shared_logits(c + 1, bq0, bq1, x + 8);
+        shared_logits(c, bq0, bq1, x, sh);
+        shared_logits(c + 1, bq0, bq1, x + 8, sh);
         softmax_update<2>(x, [&](int i, u32x4 (&av)[4]) { shared_av(c + i, av); }, mref, o.acc,
                           lsum);
       }
       if (c < nc) {
         float x[8];
-        shared_logits(c, bq0, bq1, x);
+        shared_logits(c, bq0, bq1, x, sh);
         softmax_update<1>(x, [&](int, u32x4 (&av)[4]) { shared_av(c, av); }, mref, o.acc, lsum);
       }
     }
@@ -427,9 +451,15 @@ void attend_bf16_kernel(Args a) {
       }
     }
     o.live = qi < cnt;
-    o.nq = nq;
-    o.inv = 1.0f / lsum[0];
+    o.nq = item;
+    o.inv = S == 1 ? 1.0f / lsum[0] : 1.0f;  // partials stay unnormalised
+    o.mref = mref;
+    o.lsum = lsum[0];
     return o;
+  };
+  // an item's softmax reference and sum, beside its partial row
+  auto store_ml = [&](const PassOut& o) {
+    if (S > 1 && g == 0 && o.live) pmlh[o.nq] = make_float2(o.mref, o.lsum);
   };
 
   Rows rows;
@@ -445,6 +475,7 @@ void attend_bf16_kernel(Args a) {
     // for the stores
     asm volatile("" ::"v"(bq0), "v"(bq1));
     store_out(outr, pending, g, c16);  // the previous expert's last pass
+    store_ml(pending);
     pending.live = false;
     if (j + 1 < nexp) load_rows(j + 1, 0, rows);
     __syncthreads();
@@ -454,23 +485,61 @@ void attend_bf16_kernel(Args a) {
       for (int p0 = TQ; p0 < cnt; p0 += TQ) {
         // later passes: query ids and Q rows straight from global memory
         store_out(outr, o, g, c16);
+        store_ml(o);
         const int qi = p0 + 16 * w + c16;
-        const int nq = qi < cnt ? permh[q0 + qi] : 0;
+        const int it = qi < cnt ? permh[q0 + qi] : 0;
+        const int nq = S == 1 ? it : it / S;
         const u32x4 b0 = *reinterpret_cast<const u32x4*>(Qh + (size_t)nq * 64 + 8 * g);
         const u32x4 b1 = *reinterpret_cast<const u32x4*>(Qh + (size_t)nq * 64 + 32 + 8 * g);
-        o = run_pass(j, p0, nq, b0, b1);
+        o = run_pass(j, p0, it, b0, b1);
       }
       pending = o;
     }
     __syncthreads();  // readers of this expert's rows are done
   }
   store_out(outr, pending, g, c16);
+  store_ml(pending);
+}
+
+// s > 1: out_n = sum_j acc_j 2^((M_j - M) tau log2e) / sum_j l_j 2^(...), over
+// the query's s items (acc_j, M_j, l_j from the attention kernel), M the
+// largest M_j.  One thread per (query, 4 channels).
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part,
+                                                    const float2* __restrict__ pml,
+                                                    float* __restrict__ out, long long nq, int s) {
+  constexpr float cs = 0.125f * 1.4426950408889634f;  // tau * log2(e)
+  const long long it = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long n = it >> 4;
+  const int c4 = (int)(it & 15) * 4;
+  if (n >= nq) return;
+  float M = -INFINITY;
+  for (int j = 0; j < s; ++j) M = fmaxf(M, pml[n * s + j].x);
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float l = 0.f;
+  for (int j = 0; j < s; ++j) {
+    const float2 ml = pml[n * s + j];
+    const float f = __builtin_amdgcn_exp2f((ml.x - M) * cs);
+    const float4 v = *reinterpret_cast<const float4*>(part + (n * s + j) * 64 + c4);
+    o.x = fmaf(f, v.x, o.x);
+    o.y = fmaf(f, v.y, o.y);
+    o.z = fmaf(f, v.z, o.z);
+    o.w = fmaf(f, v.w, o.w);
+    l = fmaf(f, ml.y, l);
+  }
+  const float inv = 1.0f / l;
+  *reinterpret_cast<float4*>(out + n * 64 + c4) = make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
 }
 
 }  // namespace att
 
 bool attend_bf16_supported(const Shape& s) {
-  return s.bf16 && s.m <= att::MAXM;
+  // the partial rows of the N * s items are addressed by 32-bit byte offsets
+  return s.bf16 && s.m <= att::MAXM && (long long)s.N * s.s <= (1 << 22);
+}
+
+size_t attend_partial_bytes(const Shape& s) {
+  if (s.s == 1) return 0;
+  return (size_t)s.BH * s.N * s.s * (64 * 4 + 8);
 }
 
 static int attend_parts(const Shape& s) {
@@ -487,7 +556,8 @@ static int attend_parts(const Shape& s) {
 
 hipError_t launch_attend_bf16(const void* Q, const void* K, const void* V, const float* ql,
                               const float* vl, const int32_t* idx, const int32_t* offsets,
-                              const int32_t* perm, float* out, const Shape& s, hipStream_t st) {
+                              const int32_t* perm, float* out, void* partial, const Shape& s,
+                              hipStream_t st) {
   int parts = attend_parts(s);
   // the table must fit next to the rest: fewer experts per workgroup if not
   while (att::Lay(s.m, s.k, parts).bytes > 160 * 1024 && parts < s.m) ++parts;
@@ -495,10 +565,22 @@ hipError_t launch_attend_bf16(const void* Q, const void* K, const void* V, const
   if (L.bytes > 160 * 1024) return hipErrorInvalidValue;
   if (const hipError_t e = allow_lds((const void*)att::attend_bf16_kernel, 160 * 1024); e != hipSuccess)
     return e;
+  if (s.s > 1 && !partial) return hipErrorInvalidValue;
+  float* part = s.s > 1 ? (float*)partial : out;
+  float2* pml = s.s > 1 ? (float2*)((char*)partial + (size_t)s.BH * s.N * s.s * 64 * 4) : nullptr;
   att::Args a{(const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, ql, vl, idx, offsets,
-              perm, out, s.BH, s.N, s.m, s.k, parts};
+              perm, part, pml, s.BH, s.N, s.m, s.k, parts, s.s, s.shared ? 1 : 0};
   const int grid = ((s.BH + 7) / 8) * 8 * parts;
   att::attend_bf16_kernel<<<grid, 256, L.bytes, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const void* partial, float* out, const Shape& s, hipStream_t st) {
+  const long long nq = (long long)s.BH * s.N;
+  const float* part = (const float*)partial;
+  const float2* pml = (const float2*)((const char*)partial + (size_t)nq * s.s * 64 * 4);
+  const long long threads = nq * 16;
+  att::merge_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(part, pml, out, nq, s.s);
   return hipGetLastError();
 }
 

@@ -57,9 +57,14 @@ hipError_t launch_route_bf16(const void* Q, const float* ql, int32_t* route, int
 hipError_t launch_group_bf16(const int32_t* route, const int32_t* chist, int32_t* counts,
                              int32_t* offsets, int32_t* perm, const Shape& s, hipStream_t st);
 bool attend_bf16_supported(const Shape& s);
+// s > 1: the attention kernel leaves per-item partial sums in `partial`
+// (attend_partial_bytes) and launch_merge combines them into out
+size_t attend_partial_bytes(const Shape& s);
 hipError_t launch_attend_bf16(const void* Q, const void* K, const void* V, const float* ql,
                               const float* vl, const int32_t* idx, const int32_t* offsets,
-                              const int32_t* perm, float* out, const Shape& s, hipStream_t st);
+                              const int32_t* perm, float* out, void* partial, const Shape& s,
+                              hipStream_t st);
+hipError_t launch_merge(const void* partial, float* out, const Shape& s, hipStream_t st);
 
 // whole pass for short grids in one persistent kernel
 bool fused_supported(const Shape& s);

@@ -4,17 +4,24 @@
 // expert's keys are fetched once per group).
 //
 // route_n = argmax_i q_n . Q_L[i] with ties to the lowest i (a strict '>'
-// scan in landmark order).  Grouping is a per-head stable counting sort:
-// histogram, exclusive scan, then an order-preserving scatter.
+// scan in landmark order), or the s best landmarks in that order.  Grouping
+// is a per-head stable counting sort of the routes (the N * s (query, rank)
+// items when s > 1): histogram, exclusive scan, then an order-preserving
+// scatter.
 #include "common.h"
 #include "internal.h"
 
 namespace mita {
 
+constexpr int kMaxS = 8;
+
+// route[(bh * N + n) * s + j]: the j-th best landmark of query n (a strict '>'
+// in landmark order keeps the lower id ahead of an equal score).
 template <typename T>
 __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ Q,
                                                     const float* __restrict__ ql,
-                                                    int32_t* __restrict__ route, int N, int m) {
+                                                    int32_t* __restrict__ route, int N, int m,
+                                                    int s) {
   const int bh = blockIdx.y;
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= N) return;
@@ -23,18 +30,34 @@ __global__ __launch_bounds__(256) void route_kernel(const T* __restrict__ Q,
 #pragma unroll
   for (int c = 0; c < kHeadDim; ++c) q[c] = to_f32(qr[c]);
   const float* L = ql + (size_t)bh * m * kHeadDim;
-  float best = -INFINITY;
-  int arg = 0;
+  float bv[kMaxS];
+  int bi[kMaxS];
+#pragma unroll
+  for (int t = 0; t < kMaxS; ++t) {
+    bv[t] = -INFINITY;
+    bi[t] = 0;
+  }
   for (int i = 0; i < m; ++i) {
     float a = 0.f;
 #pragma unroll
     for (int c = 0; c < kHeadDim; ++c) a = fmaf(q[c], L[i * kHeadDim + c], a);
-    if (a > best) {
-      best = a;
-      arg = i;
+    // sorted insertion into the first s slots
+#pragma unroll
+    for (int t = kMaxS - 1; t > 0; --t) {
+      if (t >= s) continue;
+      const bool up = a > bv[t - 1];
+      const bool here = !up && a > bv[t];
+      bv[t] = up ? bv[t - 1] : (here ? a : bv[t]);
+      bi[t] = up ? bi[t - 1] : (here ? i : bi[t]);
+    }
+    if (a > bv[0]) {
+      bv[0] = a;
+      bi[0] = i;
     }
   }
-  route[(size_t)bh * N + n] = arg;
+#pragma unroll
+  for (int t = 0; t < kMaxS; ++t)
+    if (t < s) route[((size_t)bh * N + n) * s + t] = bi[t];
 }
 
 __global__ __launch_bounds__(256) void group_kernel(const int32_t* __restrict__ route,
@@ -80,18 +103,20 @@ __global__ __launch_bounds__(256) void group_kernel(const int32_t* __restrict__ 
 
 hipError_t launch_route(const void* Q, const float* ql, int32_t* route, const Shape& s,
                         hipStream_t st) {
+  if (s.s > kMaxS) return hipErrorInvalidValue;
   dim3 grid((s.N + 255) / 256, s.BH);
   if (s.bf16)
-    route_kernel<bf16_t><<<grid, 256, 0, st>>>((const bf16_t*)Q, ql, route, s.N, s.m);
+    route_kernel<bf16_t><<<grid, 256, 0, st>>>((const bf16_t*)Q, ql, route, s.N, s.m, s.s);
   else
-    route_kernel<float><<<grid, 256, 0, st>>>((const float*)Q, ql, route, s.N, s.m);
+    route_kernel<float><<<grid, 256, 0, st>>>((const float*)Q, ql, route, s.N, s.m, s.s);
   return hipGetLastError();
 }
 
 hipError_t launch_group(const int32_t* route, int32_t* counts, int32_t* offsets, int32_t* perm,
                         const Shape& s, hipStream_t st) {
+  // the N * s (query, rank) items in item order t = n * s + j
   const size_t lds = (size_t)(2 * s.m + 256) * sizeof(int);
-  group_kernel<<<s.BH, 256, lds, st>>>(route, counts, offsets, perm, s.N, s.m);
+  group_kernel<<<s.BH, 256, lds, st>>>(route, counts, offsets, perm, s.N * s.s, s.m);
   return hipGetLastError();
 }
 

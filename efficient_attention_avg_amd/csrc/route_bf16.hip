@@ -30,11 +30,66 @@ __device__ __forceinline__ int rc(int row, int c) { return row * 128 + ((c ^ (ro
 
 constexpr int RW = 8;  // waves per route workgroup
 
+// A lane's best landmarks for its query column, best first (MS slots; the
+// first s of them are the answer): landmarks arrive in increasing id order,
+// so a strict '>' keeps the lower id ahead of an equal score.
+template <int MS>
+struct TopS {
+  float v[MS];
+  int i[MS];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int t = 0; t < MS; ++t) {
+      v[t] = -INFINITY;
+      i[t] = 0x7FFFFFFF;
+    }
+  }
+  __device__ __forceinline__ void insert(float x, int L) {
+#pragma unroll
+    for (int t = MS - 1; t > 0; --t) {
+      const bool up = x > v[t - 1];           // x goes above slot t - 1
+      const bool here = !up && x > v[t];
+      v[t] = up ? v[t - 1] : (here ? x : v[t]);
+      i[t] = up ? i[t - 1] : (here ? L : i[t]);
+    }
+    const bool top = x > v[0];
+    v[0] = top ? x : v[0];
+    i[0] = top ? L : i[0];
+  }
+  // drops slot 0 (taken by the merge)
+  __device__ __forceinline__ void pop(bool p) {
+#pragma unroll
+    for (int t = 0; t < MS - 1; ++t) {
+      v[t] = p ? v[t + 1] : v[t];
+      i[t] = p ? i[t + 1] : i[t];
+    }
+    v[MS - 1] = p ? -INFINITY : v[MS - 1];
+    i[MS - 1] = p ? 0x7FFFFFFF : i[MS - 1];
+  }
+};
+
+// Best (score, id) of the four lane groups holding one query's landmarks,
+// ties to the lower landmark id.
+__device__ __forceinline__ void best_of_groups(float& v, int& i) {
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+    const float ov = __shfl_xor(v, off, 64);
+    const int oi = __shfl_xor(i, off, 64);
+    if (ov > v || (ov == v && oi < i)) {
+      v = ov;
+      i = oi;
+    }
+  }
+}
+
+// MS = 1: the argmax; MS > 1: the best s <= MS landmarks per query, written
+// best first as items t = n * s + j.
+template <int MS>
 __global__ __launch_bounds__(64 * RW) void route_bf16_kernel(const uint16_t* __restrict__ Q,
                                                          const float* __restrict__ ql,
                                                          int32_t* __restrict__ route,
                                                          int32_t* __restrict__ chist, int N, int m,
-                                                         int nruns, int qc, int R) {
+                                                         int nruns, int qc, int R, int s) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -43,8 +98,8 @@ __global__ __launch_bounds__(64 * RW) void route_bf16_kernel(const uint16_t* __r
   char* qlh = sm;
   char* qll = sm + mt * 16 * 128;
   const int cruns = qc / R;  // runs per chunk
-  int* hist = reinterpret_cast<int*>(sm + 2 * mt * 16 * 128);  // [cruns][m]
-  int* rbuf = hist + cruns * m;  // the chunk's routes
+  int* hist = reinterpret_cast<int*>(sm + 2 * mt * 16 * 128);  // [cruns][m] (items per run)
+  int* rbuf = hist + cruns * m;  // the chunk's routes, s per query
   const uint16_t* Qh = Q + (size_t)bh * N * 64;
   const int base = chunk * qc, ntile = qc >> 4;
   // Q_L (rows past m are zero): all of this thread's loads first, before the
@@ -109,6 +164,8 @@ __global__ __launch_bounds__(64 * RW) void route_bf16_kernel(const uint16_t* __r
     if (tt + RW < ntile) load_q(tt + RW, nb0, nb1);
     float best = -INFINITY;
     int bi = 0;
+    TopS<MS> top;
+    if constexpr (MS > 1) top.init();
     for (int lt = 0; lt < mt; ++lt) {
       const int row = 16 * lt + c16;
       const u32x4 ah0 = *reinterpret_cast<const u32x4*>(qlh + rc(row, g));
@@ -124,22 +181,40 @@ __global__ __launch_bounds__(64 * RW) void route_bf16_kernel(const uint16_t* __r
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int L = 16 * lt + 4 * g + r;
-        if (L < m && c[r] > best) { best = c[r]; bi = L; }
+        if constexpr (MS == 1) {
+          if (L < m && c[r] > best) { best = c[r]; bi = L; }
+        } else {
+          top.insert(L < m ? c[r] : -INFINITY, L < m ? L : 0x7FFFFFFF);
+        }
       }
     }
-#pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
-      const float ov = __shfl_xor(best, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (ov > best || (ov == best && oi < bi)) { best = ov; bi = oi; }
-    }
-    if (g == 0 && ok) {
-      rbuf[16 * tt + c16] = bi;
-      atomicAdd(&hist[(16 * tt / R) * m + bi], 1);
+    if constexpr (MS == 1) {
+      best_of_groups(best, bi);
+      if (g == 0 && ok) {
+        rbuf[16 * tt + c16] = bi;
+        atomicAdd(&hist[(16 * tt / R) * m + bi], 1);
+      }
+    } else {
+      // s rounds: the best head of the four groups' lists is the next route;
+      // the group holding it drops it
+      for (int j = 0; j < s; ++j) {
+        float v = top.v[0];
+        int i = top.i[0];
+        best_of_groups(v, i);
+        top.pop(top.i[0] == i);
+        // (an empty slot can win only when scores are NaN; keep the id in
+        // range so such input cannot index past the histogram)
+        i = i < m ? i : m - 1;
+        if (g == 0 && ok) {
+          rbuf[(16 * tt + c16) * s + j] = i;
+          atomicAdd(&hist[(16 * tt / R) * m + i], 1);
+        }
+      }
     }
   }
   __syncthreads();
-  for (int i = tid; i < qc && base + i < N; i += 64 * RW) route[(size_t)bh * N + base + i] = rbuf[i];
+  const int nq = min(qc, N - base) * s;
+  for (int i = tid; i < nq; i += 64 * RW) route[((size_t)bh * N + base) * s + i] = rbuf[i];
   const int run0 = chunk * cruns, nr = min(cruns, nruns - run0);
   int32_t* dst = chist + ((size_t)bh * nruns + run0) * m;
   for (int e = tid; e < nr * m; e += 64 * RW) dst[e] = hist[e];
@@ -229,13 +304,13 @@ static void route_chunking(const Shape& s, int& qc, int& nchunks, int& R, int& n
 
 static size_t route_lds(const Shape& s, int qc, int R) {
   const int mt = (s.m + 15) / 16;
-  return (size_t)2 * mt * 16 * 128 + (size_t)(qc / R) * s.m * 4 + (size_t)qc * 4;
+  return (size_t)2 * mt * 16 * 128 + (size_t)(qc / R) * s.m * 4 + (size_t)qc * s.s * 4;
 }
 
 bool route_bf16_supported(const Shape& s) {
   int qc, nchunks, R, nruns;
   route_chunking(s, qc, nchunks, R, nruns);
-  return s.bf16 && s.m <= 512 && ((size_t)nruns * s.m + s.m) * 4 <= 160 * 1024 &&
+  return s.bf16 && s.m <= 512 && s.s <= 8 && ((size_t)nruns * s.m + s.m) * 4 <= 160 * 1024 &&
          route_lds(s, qc, R) <= 160 * 1024;
 }
 
@@ -251,11 +326,14 @@ hipError_t launch_route_bf16(const void* Q, const float* ql, int32_t* route, int
   route_chunking(s, qc, nchunks, R, nruns);
   const size_t lds = route_lds(s, qc, R);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  if (const hipError_t e = allow_lds((const void*)rt::route_bf16_kernel, 160 * 1024); e != hipSuccess)
-    return e;
+  // the smallest list that holds s routes
+  auto kernel = s.s == 1 ? rt::route_bf16_kernel<1>
+                : s.s == 2 ? rt::route_bf16_kernel<2>
+                : s.s <= 4 ? rt::route_bf16_kernel<4> : rt::route_bf16_kernel<8>;
+  if (const hipError_t e = allow_lds((const void*)kernel, 160 * 1024); e != hipSuccess) return e;
   dim3 grid(nchunks, s.BH);
-  rt::route_bf16_kernel<<<grid, 64 * rt::RW, lds, st>>>((const uint16_t*)Q, ql, route, chist, s.N,
-                                                        s.m, nruns, qc, R);
+  kernel<<<grid, 64 * rt::RW, lds, st>>>((const uint16_t*)Q, ql, route, chist, s.N, s.m, nruns,
+                                         qc, R, s.s);
   return hipGetLastError();
 }
 
@@ -267,8 +345,9 @@ hipError_t launch_group_bf16(const int32_t* route, const int32_t* chist, int32_t
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   if (const hipError_t e = allow_lds((const void*)rt::group_bf16_kernel, 160 * 1024); e != hipSuccess)
     return e;
-  rt::group_bf16_kernel<<<s.BH, 1024, lds, st>>>(route, chist, counts, offsets, perm, s.N, s.m,
-                                                 nruns, R);
+  // the sort runs over the N * s (query, rank) items, R * s of them per run
+  rt::group_bf16_kernel<<<s.BH, 1024, lds, st>>>(route, chist, counts, offsets, perm, s.N * s.s,
+                                                 s.m, nruns, R * s.s);
   return hipGetLastError();
 }
 

@@ -37,12 +37,13 @@ def _to_dev(x, dtype):
     return t.cuda()
 
 
-def run_gpu(Q, K, V, dtype, grid_h, grid_w, m_h, m_w, k, path="auto", extras=True):
+def run_gpu(Q, K, V, dtype, grid_h, grid_w, m_h, m_w, k, path="auto", extras=True, s=1,
+            route_only=False):
     import efficient_attention_avg_amd as mita
     torch = _torch()
     q, kk, v = (_to_dev(x, dtype) for x in (Q, K, V))
     res = mita.mita_forward_ex(q, kk, v, grid_h, grid_w, m_h, m_w, k, idx=True, route=True,
-                               extras=extras, path=path)
+                               extras=extras, path=path, s=s, route_only=route_only)
     torch.cuda.synchronize()
     return {key: val.cpu().numpy() for key, val in res.items() if val is not None}
 
@@ -240,6 +241,56 @@ def test_scalar_fallback_steps(case):
     res = run_gpu(Q, K, V, "bf16", gh, gw, mh, mw, k)
     rep = parity.run_and_check(res, Q, K, V, gh, gw, mh, mw, k, TOL["bf16"])
     _say(f"ok {rep}")
+
+
+# The variants: s experts per query (one softmax over m + s*k entries) and
+# route-only (no shared expert), on the matrix-core kernels and the scalar ones.
+VARIANTS = [
+    # B, H, gh, gw, mh, mw, k, s, route_only, dtype
+    (2, 3, 14, 14, 5, 5, 25, 2, False, "bf16"),    # DeiT shape, two experts per query
+    (1, 2, 56, 56, 7, 7, 64, 2, False, "bf16"),
+    (1, 2, 56, 56, 7, 7, 64, 4, False, "bf16"),
+    (1, 1, 12, 12, 4, 4, 20, 8, False, "bf16"),    # the largest s
+    (1, 1, 10, 10, 3, 3, 100, 3, False, "bf16"),   # k = N: every key held s times
+    (2, 3, 14, 14, 5, 5, 50, 1, True, "bf16"),     # route-only at the DeiT budget m + k
+    (1, 2, 56, 56, 7, 7, 113, 1, True, "bf16"),    # route-only at the 3136 budget 49 + 64
+    (1, 2, 20, 24, 6, 5, 37, 3, True, "bf16"),     # route-only, three experts
+    (1, 2, 9, 7, 3, 2, 21, 2, False, "f32"),       # scalar kernels
+    (1, 1, 8, 8, 4, 4, 64, 3, True, "f32"),        # scalar, route-only, k = N
+    (1, 1, 32, 32, 20, 20, 30, 2, False, "bf16"),  # m = 400: scalar attention
+    (1, 1, 32, 32, 32, 20, 24, 3, False, "bf16"),  # m = 640: scalar routing and attention
+]
+
+
+@pytest.mark.parametrize("case", VARIANTS,
+                         ids=lambda c: "x".join(map(str, c[:7])) + f"-s{c[7]}" +
+                         ("-ro" if c[8] else "") + "-" + c[9])
+def test_variants(case):
+    B, H, gh, gw, mh, mw, k, s, ro, dtype = case
+    _say(f"variant {case}")
+    Q, K, V = synth.make_qkv(B, H, gh, gw, 64, workload_id=1300 + gh * 7 + gw + s,
+                             smooth=dtype == "bf16", dtype=dtype)
+    res = run_gpu(Q, K, V, dtype, gh, gw, mh, mw, k, s=s, route_only=ro)
+    assert res["route"].shape == ((B, H, gh * gw) if s == 1 else (B, H, gh * gw, s))
+    rep = parity.run_and_check(res, Q, K, V, gh, gw, mh, mw, k, TOL[dtype], s=s, shared=not ro)
+    _say(f"ok {rep}")
+
+
+@pytest.mark.parametrize("name,s,ro,k", [("deit-s", 2, False, None), ("hires-3136", 2, False, None),
+                                         ("deit-s", 1, True, 50), ("hires-3136", 1, True, 113)],
+                         ids=lambda v: str(v))
+def test_workload_variants(name, s, ro, k):
+    """The full DeiT-S and 3136-token workloads with two experts per query, and
+    route-only with the same number of entries per query as the plain pass."""
+    w = synth.workload(name)
+    k = w["k"] if k is None else k
+    _say(f"workload {name} s={s} route_only={ro} k={k} (all heads)")
+    Q, K, V = synth.workload_inputs(name)
+    res = run_gpu(Q, K, V, w["dtype"], w["grid_h"], w["grid_w"], w["m_h"], w["m_w"], k, s=s,
+                  route_only=ro)
+    rep = parity.run_and_check(res, Q, K, V, w["grid_h"], w["grid_w"], w["m_h"], w["m_w"], k,
+                               TOL[w["dtype"]], s=s, shared=not ro)
+    _say(f"ok {name}: {rep}")
 
 
 def test_expert_attention_with_one_workgroup_per_expert():
