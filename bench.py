@@ -25,7 +25,9 @@ A warm (no flush) figure is reported beside it unless --no-warm.  Defaults:
 
 Prints ONE JSON line.  ``value`` is query-heads per second (B*H*N per step)
 on the headline workload (DeiT-S shape); the 3136-token workload is reported
-in ``secondary``.  ``roofline`` covers the kernel that dominates the step;
+in ``secondary`` (with its own oracle baseline), and ``extras`` holds a
+shorter record (20 cold steps) for every other workload and for the variants
+(two experts per query; route-only with the plain pass's entry count).  ``roofline`` covers the kernel that dominates the step;
 ``kernel_gbs`` gives every kernel's algorithmic bytes per second and
 ``kernel_mfma`` the contraction kernels' algorithmic matrix flops per second
 against the dense bf16 MFMA peak (2.5 PFLOP/s);
@@ -96,10 +98,19 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def describe(w):
+def describe(w, s=1, route_only=False):
     return (f"{w['name']}: B={w['B']} H={w['H']} grid {w['grid_h']}x{w['grid_w']} "
             f"(N={w['grid_h'] * w['grid_w']}) d={w['d']} m={w['m_h'] * w['m_w']} "
-            f"({w['m_h']}x{w['m_w']} pool) k={w['k']} s=1, {w['dtype']} in, fp32 out")
+            f"({w['m_h']}x{w['m_w']} pool) k={w['k']} s={s}"
+            + (", route-only" if route_only else "") + f", {w['dtype']} in, fp32 out")
+
+
+def variant_flops_per_qh(w, s=1, route_only=False):
+    """Matrix flops per query-head of a variant: S and routing (2md each), with the
+    shared expert V_L and the shared logits and P V_L (2md each), and 4d per routed
+    entry (q.k and p v) for s*k entries."""
+    d, m, k = w["d"], w["m_h"] * w["m_w"], w["k"]
+    return 2 * m * d * 2 + (0 if route_only else 2 * m * d * 2) + 4 * d * s * k
 
 
 def algorithmic(w):
@@ -140,14 +151,17 @@ def algorithmic(w):
 
 
 class Runner:
-    def __init__(self, name, path="auto"):
+    def __init__(self, name, path="auto", s=1, route_only=False, k=None):
         import torch
 
         import efficient_attention_avg_amd as mita
         import synth
         self.torch, self.mita = torch, mita
         self.w = w = synth.workload(name)
+        if k is not None:
+            w["k"] = k
         self.path = path
+        self.s, self.route_only = s, route_only
         t0 = time.time()
         Q, K, V = synth.workload_inputs(name)
         self.host = (Q, K, V)
@@ -158,14 +172,15 @@ class Runner:
         self.out = torch.empty(self.q.shape, dtype=torch.float32, device="cuda")
         code = mita.MITA_BF16 if w["dtype"] == "bf16" else mita.MITA_F32
         nb = mita.mita_workspace_bytes(w["B"], w["H"], w["grid_h"], w["grid_w"], w["d"],
-                                       w["m_h"], w["m_w"], w["k"], code)
-        self.ws = torch.empty(max(nb, 1), dtype=torch.uint8, device="cuda")
+                                       w["m_h"], w["m_w"], w["k"], code, path=path, s=s,
+                                       route_only=route_only)
+        self.ws = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
         self.flush_buf = torch.ones(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
         self.flush_f32 = self.flush_buf.view(torch.float32)
         self.flush_sink = torch.zeros((), dtype=torch.float32, device="cuda")
         self.sched = mita.mita_kernel_schedule(w["B"], w["H"], w["grid_h"], w["grid_w"], w["d"],
                                               w["m_h"], w["m_w"], w["k"], code, path=path,
-                                              overlap=True)
+                                              overlap=True, s=s, route_only=route_only)
         self.kernels = [nm for nm, _ in self.sched]
 
         self.overlap = True
@@ -173,7 +188,7 @@ class Runner:
     def step(self, events=None):
         self.mita.mita_forward_ex(self.q, self.k, self.v, *self.args, out=self.out,
                                   workspace=self.ws, path=self.path, events=events,
-                                  overlap=self.overlap)
+                                  overlap=self.overlap, s=self.s, route_only=self.route_only)
 
     def flush(self):
         # a read of 512 MiB evicts L2 and the Infinity Cache with clean lines; a write
@@ -293,6 +308,49 @@ def measure(name, steps, warmup, path="auto", warm=True):
     return r, res
 
 
+def measure_light(name, steps, warmup, s=1, route_only=False, k=None):
+    """A shorter record for the other workloads and the variants: warm-up, then cold
+    steps timed by events around each call and a cold series with per-kernel events."""
+    import torch
+    r = Runner(name, "auto", s=s, route_only=route_only, k=k)
+    w = r.w
+    alg = algorithmic(w)
+    for _ in range(warmup):
+        r.flush()
+        r.step()
+    torch.cuda.synchronize()
+    cold_ms, cold_all = r.timed_calls(steps, flush=True)
+    inst_ms, _, stages = r.timed(steps, flush=True)
+    qh = alg["qh"]
+    pass_gbs = alg["bytes_per_qh"] * qh / (cold_ms * 1e-3) / 1e9
+    fl = variant_flops_per_qh(w, s, route_only)
+    res = dict(workload=describe(w, s, route_only), value=qh / (cold_ms * 1e-3),
+               unit="query-heads/s", ms_per_step=cold_ms,
+               ms_median=sorted(cold_all)[len(cold_all) // 2],
+               schedule="fused" if r.kernels == ["fused"] else "staged",
+               pass_roofline=dict(bound="hbm", achieved=pass_gbs, peak=HBM_PEAK_GBS, unit="GB/s",
+                                  frac=pass_gbs / HBM_PEAK_GBS, bytes_per_qh=alg["bytes_per_qh"],
+                                  flops_per_qh=fl,
+                                  mfma_frac=fl * qh / (cold_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS),
+               stage_us={kk: v * 1e3 for kk, v in stages.items()},
+               instrumented_ms_per_step=inst_ms)
+    log(f"{res['workload']}: {cold_ms * 1e3:.1f} us/step, kernels (us) "
+        + ", ".join(f"{kk}={v * 1e3:.1f}" for kk, v in stages.items()))
+    del r
+    torch.cuda.empty_cache()
+    return res
+
+
+# the other workloads and the variants, one light record each
+EXTRA_LINES = [
+    ("deit-t", 1, False, None), ("long-16k", 1, False, None), ("ade-1024", 1, False, None),
+    ("ade-1600", 1, False, None), ("seq-64k", 1, False, None), ("seq-256k", 1, False, None),
+    ("deit-s", 2, False, None), ("hires-3136", 2, False, None),
+    # route-only with the plain pass's m + k entries per query
+    ("deit-s", 1, True, 50), ("hires-3136", 1, True, 113),
+]
+
+
 def cpu_baseline(runner, seconds):
     """The fp64 oracle, as it stands, on the first heads of the same inputs (bounded time)."""
     from threadpoolctl import threadpool_limits
@@ -382,6 +440,9 @@ def main():
                     help="skip the warm (no flush) figure, e.g. under a profiler")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain copy kernel of known size (counter scaling)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the light records of the other workloads and the variants")
+    ap.add_argument("--extra-steps", type=int, default=20)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this MiTA build runs on exactly one GPU; every (batch, head) is "
@@ -410,7 +471,12 @@ def main():
     secondary = None
     if args.also:
         r2, res2 = measure(args.also, args.steps, args.warmup, args.path, warm=not args.no_warm)
+        cpu2 = None
+        if not args.no_cpu_baseline:
+            cpu2 = cpu_baseline(r2, args.cpu_seconds)
+            log(f"oracle ({args.also}): {cpu2['value']:.3g} qh/s ({cpu2['sample']})")
         del r2
+        torch.cuda.empty_cache()
         secondary = {
             "workload": describe(res2["workload"]), "value": res2["value"], "unit": "query-heads/s",
             "ms_per_step": res2["ms_per_step"], "ms_median": res2["ms_median"],
@@ -423,8 +489,12 @@ def main():
             "roofline": res2["roofline"], "pass_roofline": res2["pass_roofline"],
             "stage_us": res2["stage_us"], "kernel_gbs": res2["kernel_gbs"],
             "kernel_mfma": res2["kernel_mfma"],
-            "schedule": res2["schedule"], "dtype": res2["dtype"],
+            "schedule": res2["schedule"], "dtype": res2["dtype"], "cpu_baseline": cpu2,
         }
+    extras = []
+    if not args.no_extras:
+        for name, s_, ro, k in EXTRA_LINES:
+            extras.append(measure_light(name, args.extra_steps, 5, s=s_, route_only=ro, k=k))
     w = main_res["workload"]
     line = {
         "metric": METRIC, "value": main_res["value"], "unit": "query-heads/s", "n_gpus": 1,
@@ -444,7 +514,7 @@ def main():
         "roofline": main_res["roofline"], "pass_roofline": main_res["pass_roofline"],
         "stage_us": main_res["stage_us"], "kernel_gbs": main_res["kernel_gbs"],
         "kernel_mfma": main_res["kernel_mfma"],
-        "cpu_baseline": cpu, "secondary": secondary,
+        "cpu_baseline": cpu, "secondary": secondary, "extras": extras,
         "library": mita.lib().mita_version().decode(),
     }
     print(json.dumps(line))

@@ -119,13 +119,13 @@ bool runs_fused(int path, const Shape& s) {
 
 // Which kernels each staged step uses: the MFMA kernels for bf16 inputs
 // within their limits, the scalar kernels otherwise (fp32 inputs).
-bool pool_mfma(const Shape& s) { return s.bf16 && s.grid_w <= 256; }
+bool pool_mfma(const Shape& s) { return s.bf16; }
 bool landmark_mfma(const Shape& s) { return mita::landmark_bf16_supported(s); }
 bool route_mfma(const Shape& s) { return mita::route_bf16_supported(s); }
 bool attend_mfma(const Shape& s) { return mita::attend_bf16_supported(s); }
 
 size_t landmark_scratch(const Shape& s) {
-  return landmark_mfma(s) ? 0 : mita::landmark_scratch_bytes(s);
+  return landmark_mfma(s) ? mita::landmark_bf16_scratch_bytes(s) : mita::landmark_scratch_bytes(s);
 }
 size_t route_scratch(const Shape& s) { return route_mfma(s) ? mita::route_chist_bytes(s) : 0; }
 
@@ -140,7 +140,7 @@ mita_status run_pool(const void* Q, float* ql, const Shape& s, hipStream_t st,
 mita_status run_landmark(const float* ql, const void* K, const void* V, int32_t* idx, float* vl,
                          void* scratch, const Shape& s, hipStream_t st, Marker* mk = nullptr) {
   const mita_status r =
-      hip_status(landmark_mfma(s) ? mita::launch_landmark_bf16(ql, K, V, idx, vl, s, st)
+      hip_status(landmark_mfma(s) ? mita::launch_landmark_bf16(ql, K, V, idx, vl, scratch, s, st)
                                   : mita::launch_landmark(ql, K, V, idx, vl, scratch, s, st),
                  "landmark launch");
   if (mk) mk->mark(st);

@@ -35,6 +35,12 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+__device__ __forceinline__ float wave_min_f(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
 // Number of set bits of `mask` strictly below this lane.

@@ -84,6 +84,21 @@ struct Args {
   int32_t* idx;
   float* vl;
   int BH, N, m, k, cap, tiles;
+  // keys split into nch chunks of cblk blocks (nch > 1: each workgroup writes
+  // its chunk's top-k as (score, key) pairs and its unnormalised V_L partial,
+  // and merge_kernel finishes both)
+  int nch, cblk;
+  float* cand_s;   // [BH][m][nch][k] scores of each chunk's top-k
+  int32_t* cand_k; // [BH][m][nch][k] their key ids, ascending within a chunk
+  float* vlpart;   // [BH][m][nch][PART_STRIDE]: 64 sums, reference max, sum
+};
+
+constexpr int PART_STRIDE = 68;
+
+// This workgroup's keys: blocks [blk0, blk1), keys [kbase, kend); it selects
+// kk = min(k, kend - kbase) of them.
+struct Chunk {
+  int chunk, blk0, blk1, kbase, kend, kk;
 };
 
 __host__ __device__ constexpr size_t lds_bytes(int cap) {
@@ -263,7 +278,7 @@ __device__ __forceinline__ void group_sync() {
 // Cuts row lr's buffer back to its exact k best (kept in buffer order) and
 // sets the admission bound to the k-th of them.  Lane t of the group takes
 // entries t, t + 16, ...
-__device__ void row_cut(char* sm, const Args& a, int lr, bool work, int t, int g) {
+__device__ void row_cut(char* sm, const Args& a, int kk, int lr, bool work, int t, int g) {
   RowState* rs = reinterpret_cast<RowState*>(sm + OFF_ROW) + lr;
   float* vals = reinterpret_cast<float*>(sm + OFF_UNION + (size_t)lr * a.cap * 8);
   int* keys = reinterpret_cast<int*>(vals + a.cap);
@@ -277,8 +292,8 @@ __device__ void row_cut(char* sm, const Args& a, int lr, bool work, int t, int g
       const float v = vals[e];
       const int key = keys[e];
       const int r = rank_in(vals, keys, cnt, v, key);
-      keep |= (r < a.k ? 1u : 0u) << u;
-      if (r == a.k - 1) {
+      keep |= (r < kk ? 1u : 0u) << u;
+      if (r == kk - 1) {
         tv = v;
         tk = key + 1;
       }
@@ -312,9 +327,11 @@ __device__ void row_cut(char* sm, const Args& a, int lr, bool work, int t, int g
   }
 }
 
-// Row lr's k best of its buffer, written ascending to `out`.
-__device__ void row_final(char* sm, const Args& a, int lr, bool work, int t, int g,
-                          int32_t* out) {
+// Row lr's kk best of its buffer, written ascending by key id to `out`, and
+// (when outs is not null) their scores beside them.  The chunk's keys have
+// a bitmap of (kend - kbase) bits in the row's histogram space.
+__device__ void row_final(char* sm, const Args& a, const Chunk& ch, int lr, bool work, int t,
+                          int g, int32_t* out, float* outs) {
   RowState* rs = reinterpret_cast<RowState*>(sm + OFF_ROW) + lr;
   float* vals = reinterpret_cast<float*>(sm + OFF_UNION + (size_t)lr * a.cap * 8);
   int* keys = reinterpret_cast<int*>(vals + a.cap);
@@ -348,13 +365,14 @@ __device__ void row_final(char* sm, const Args& a, int lr, bool work, int t, int
   }
   group_sync();
   uint32_t take = up;
-  const int need = a.k - above;
-  const int nw = (a.N + 31) >> 5;
+  const int need = ch.kk - above;
+  const int nw = (ch.kend - ch.kbase + 31) >> 5;
   // a short list is ranked entry by entry (lane t: entries t and t + 16) and
   // its winners' keys kept in registers for the bitmap and their slots;
   // otherwise every buffer entry outside `up` is ranked where it sits
-  const bool short_list = listed && nb <= 32 && a.N <= BITMAP_MAX_N && nw * 6 <= HIST_STRIDE;
+  const bool short_list = listed && nb <= 32 && nw * 6 <= HIST_STRIDE;
   int win[2] = {-1, -1};
+  float winv[2] = {0.f, 0.f};
   if (short_list) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -362,7 +380,10 @@ __device__ void row_final(char* sm, const Args& a, int lr, bool work, int t, int
       if (i < nb) {
         const float v = list[2 * i];
         const int key = __float_as_int(list[2 * i + 1]);
-        if (rank_in_list(list, nb, v, key) < need) win[j] = key;
+        if (rank_in_list(list, nb, v, key) < need) {
+          win[j] = key;
+          winv[j] = v;
+        }
       }
     }
   } else {
@@ -377,97 +398,51 @@ __device__ void row_final(char* sm, const Args& a, int lr, bool work, int t, int
     }
   }
   group_sync();
-  if (a.N <= BITMAP_MAX_N) {
-    // bitmap of the taken keys in the row's histogram space; slot = number of
-    // taken keys below
+  {
+    // bitmap of the taken keys (relative to the chunk's first key) in the
+    // row's histogram space; slot = number of taken keys below
     uint32_t* bm = reinterpret_cast<uint32_t*>(list);
+    const int kb = ch.kbase;
     for (int q = t; q < nw; q += 16) bm[q] = 0u;
     group_sync();
     for (int u = 0; 16 * u < cnt; ++u) {
       const int e = t + 16 * u;
-      if (e < cnt && (take >> u & 1u)) atomicOr(&bm[keys[e] >> 5], 1u << (keys[e] & 31));
+      if (e < cnt && (take >> u & 1u))
+        atomicOr(&bm[(keys[e] - kb) >> 5], 1u << ((keys[e] - kb) & 31));
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j)
-      if (win[j] >= 0) atomicOr(&bm[win[j] >> 5], 1u << (win[j] & 31));
+      if (win[j] >= 0) atomicOr(&bm[(win[j] - kb) >> 5], 1u << ((win[j] - kb) & 31));
     group_sync();
-    if (nw * 6 <= HIST_STRIDE) {
-      // taken keys before each bitmap word (16-bit, after the bitmap), lane t
-      // taking words t, t + 16, ...; then every taken entry writes its own
-      // slot: the taken keys before its word plus those below it in the word
-      uint16_t* wpre = reinterpret_cast<uint16_t*>(bm + nw);
-      int run = 0;
-      for (int r0 = 0; r0 < nw; r0 += 16) {
-        const int q = r0 + t;
-        const int c = q < nw ? __popc(bm[q]) : 0;
-        const int tot = g16_addi(c);
-        if (q < nw) wpre[q] = (uint16_t)(run + tot - g16_suffix(c));
-        run += tot;
-      }
-      group_sync();
-      if (work) {
-        auto emit = [&](int key) {
-          const int wq = key >> 5;
-          const int pos = wpre[wq] + __popc(bm[wq] & ((1u << (key & 31)) - 1u));
-          if (pos < a.k) out[pos] = key;
-        };
-        for (int u = 0; 16 * u < cnt; ++u) {
-          const int e = t + 16 * u;
-          if (e < cnt && (take >> u & 1u)) emit(keys[e]);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          if (win[j] >= 0) emit(win[j]);
-      }
-    } else {
-      const int wpl = (nw + 15) >> 4;
-      const int q0 = t * wpl, q1 = min(nw, q0 + wpl);
-      int mine = 0;
-      for (int q = q0; q < q1; ++q) mine += __popc(bm[q]);
-      int pos = g16_addi(mine) - g16_suffix(mine);
-      if (work) {
-        for (int q = q0; q < q1; ++q) {
-          uint32_t wbits = bm[q];
-          while (wbits) {
-            const int b = __ffs(wbits) - 1;
-            wbits &= wbits - 1u;
-            if (pos < a.k) out[pos] = 32 * q + b;
-            ++pos;
-          }
-        }
-      }
-    }
-  } else {
-    // slot = number of taken keys below, counted over the buffer with the
-    // untaken keys replaced by INT_MAX (the scores are no longer needed)
-    int* tkeys = reinterpret_cast<int*>(vals);
-    for (int u = 0; 16 * u < cnt; ++u) {
-      const int e = t + 16 * u;
-      if (e < cnt) tkeys[e] = (take >> u & 1u) ? keys[e] : 0x7FFFFFFF;
+    // taken keys before each bitmap word (16-bit, after the bitmap), lane t
+    // taking words t, t + 16, ...; then every taken entry writes its own
+    // slot: the taken keys before its word plus those below it in the word
+    uint16_t* wpre = reinterpret_cast<uint16_t*>(bm + nw);
+    int run = 0;
+    for (int r0 = 0; r0 < nw; r0 += 16) {
+      const int q = r0 + t;
+      const int c = q < nw ? __popc(bm[q]) : 0;
+      const int tot = g16_addi(c);
+      if (q < nw) wpre[q] = (uint16_t)(run + tot - g16_suffix(c));
+      run += tot;
     }
     group_sync();
-    for (int u0 = 0; 16 * u0 < cnt; u0 += 4) {
-      int kq[4], pos[4] = {0, 0, 0, 0};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = t + 16 * (u0 + i);
-        kq[i] = (e < cnt && (take >> (u0 + i) & 1u)) ? tkeys[e] : -1;
-      }
-      int j = 0;
-      for (; j + 4 <= cnt; j += 4) {
-        const int4 kk = *reinterpret_cast<const int4*>(tkeys + j);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          pos[i] += (kk.x < kq[i]) + (kk.y < kq[i]) + (kk.z < kq[i]) + (kk.w < kq[i]);
-      }
-      for (; j < cnt; ++j) {
-        const int kj = tkeys[j];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pos[i] += kj < kq[i];
+    if (work) {
+      auto emit = [&](int key, float v) {
+        const int wq = (key - kb) >> 5;
+        const int pos = wpre[wq] + __popc(bm[wq] & ((1u << ((key - kb) & 31)) - 1u));
+        if (pos < ch.kk) {
+          out[pos] = key;
+          if (outs) outs[pos] = v;
+        }
+      };
+      for (int u = 0; 16 * u < cnt; ++u) {
+        const int e = t + 16 * u;
+        if (e < cnt && (take >> u & 1u)) emit(keys[e], vals[e]);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (work && kq[i] >= 0) out[pos[i]] = kq[i];
+      for (int j = 0; j < 2; ++j)
+        if (win[j] >= 0) emit(win[j], winv[j]);
     }
   }
 }
@@ -479,10 +454,20 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
   // round-robin dispatch puts workgroup b on XCD b % 8: keep a head's
   // workgroups on one XCD so its K and V stay in that XCD's L2
   const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
-  const int bh = xcd + 8 * (slot / a.tiles), row0 = (slot % a.tiles) * ROWS;
+  const int per_head = a.tiles * a.nch;
+  const int bh = xcd + 8 * (slot / per_head), rem = slot % per_head;
+  const int row0 = (rem % a.tiles) * ROWS;
   if (bh >= a.BH) return;
   const int N = a.N, nblk = (N + KB - 1) / KB;
   const bool ragged = (N % KB) != 0;  // the last block has keys past N
+  Chunk ch;
+  ch.chunk = rem / a.tiles;
+  ch.blk0 = ch.chunk * a.cblk;
+  ch.blk1 = min(nblk, ch.blk0 + a.cblk);
+  ch.kbase = ch.blk0 * KB;
+  ch.kend = min(N, ch.blk1 * KB);
+  ch.kk = min(a.k, ch.kend - ch.kbase);
+  const int blk0 = ch.blk0, blk1 = ch.blk1;
   const Rsrc Kh = head_rows(a.K + (size_t)bh * N * 64, N);
   const Rsrc Vh = head_rows(a.V + (size_t)bh * N * 64, N);
   RowState* rows = reinterpret_cast<RowState*>(sm + OFF_ROW);
@@ -524,15 +509,15 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
     ql_load(qlr, sm, lane);  // (this lane's own slots: no barrier needed)
     KRegs kr;
     VRegs vr;
-    if (w < nblk) {
-      load_k(kr, Kh, w, N, g, c16);
-      load_v(vr, Vh, w, N, lane);
+    if (blk0 + w < blk1) {
+      load_k(kr, Kh, blk0 + w, N, g, c16);
+      load_v(vr, Vh, blk0 + w, N, lane);
     }
-    for (int blk = w; blk < nblk; blk += NW) {
+    for (int blk = blk0 + w; blk < blk1; blk += NW) {
       // the V registers are free once stored and the K registers once the
       // scores are out: the next block's loads go out right after each
       store_vt(vr, vt, lane);
-      if (blk + NW < nblk) load_v(vr, Vh, blk + NW, N, lane);
+      if (blk + NW < blk1) load_v(vr, Vh, blk + NW, N, lane);
       group_sync();
       // the block's V^T A operands, shared by both row tiles:
       // V^T[channel 16ct + c16][keys 32sp + 4g .., 32sp + 16 + 4g ..]
@@ -553,7 +538,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
       for (int tl = 0; tl < TL; ++tl) {
         float s[4][4];
         block_scores(kr, qlr, tl, s);
-        if (tl == TL - 1 && blk + NW < nblk) load_k(kr, Kh, blk + NW, N, g, c16);
+        if (tl == TL - 1 && blk + NW < blk1) load_k(kr, Kh, blk + NW, N, g, c16);
         if (last) {
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt)
@@ -637,9 +622,11 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
         part[67] = mx[tl];
       }
     }
-    if (w < nblk) load_k(kpre, Kh, w, N, g, c16);
+    if (blk0 + w < blk1) load_k(kpre, Kh, blk0 + w, N, g, c16);
     __syncthreads();
-    // merge: thread -> (row, 4 channels), ROWS * 16 items
+    // merge: thread -> (row, 4 channels), ROWS * 16 items; with several
+    // chunks the merged sums stay unnormalised and go out as the chunk's
+    // partial (reference max M, sum L)
     const float* base = reinterpret_cast<const float*>(sm + OFF_UNION);
     for (int it = tid; it < ROWS * 16; it += 64 * NW) {
       const int r = it >> 4, c4 = (it & 15) * 4;
@@ -666,9 +653,16 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
         o.w += f * v.w;
       }
       if (row0 + r < a.m) {
-        const float inv = 1.0f / L;
-        *reinterpret_cast<float4*>(a.vl + ((size_t)bh * a.m + row0 + r) * 64 + c4) =
-            make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+        if (a.nch == 1) {
+          const float inv = 1.0f / L;
+          *reinterpret_cast<float4*>(a.vl + ((size_t)bh * a.m + row0 + r) * 64 + c4) =
+              make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
+        } else {
+          float* pp = a.vlpart +
+                      (((size_t)bh * a.m + row0 + r) * a.nch + ch.chunk) * PART_STRIDE;
+          *reinterpret_cast<float4*>(pp + c4) = o;
+          if (c4 == 0) *reinterpret_cast<float2*>(pp + 64) = make_float2(M, L);
+        }
       }
       if (c4 == 0) {
         // capped so that fma(c, A, B) stays finite
@@ -692,7 +686,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
     QLRegs qlr;
     ql_load(qlr, sm, lane);
     KRegs kr = kpre;
-    for (int blk = w; blk < nblk; blk += NW) {
+    for (int blk = blk0 + w; blk < blk1; blk += NW) {
       // keys past N of a ragged last block count into the spare word past
       // the 256 bins (no branch per score)
       uint32_t spare = 0u;
@@ -706,7 +700,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
       for (int tl = 0; tl < TL; ++tl) {
         float s[4][4];
         block_scores(kr, qlr, tl, s);
-        if (tl == TL - 1 && blk + NW < nblk) load_k(kr, Kh, blk + NW, N, g, c16);
+        if (tl == TL - 1 && blk + NW < blk1) load_k(kr, Kh, blk + NW, N, g, c16);
         uint32_t* myhist =
             reinterpret_cast<uint32_t*>(sm + OFF_HIST + (16 * tl + c16) * HIST_STRIDE);
 #pragma unroll
@@ -719,7 +713,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
       }
     }
   }
-  if (w < nblk) load_k(kpre, Kh, w, N, g, c16);
+  if (blk0 + w < blk1) load_k(kpre, Kh, blk0 + w, N, g, c16);
   __syncthreads();
   // the bin holding each row's k-th best: group g of wave w takes rows
   // 4w + g + 16i
@@ -741,7 +735,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
     for (int q = 0; q < 16; ++q) local += (int)cb[q];
     const int suf = g16_suffix(local);
     const int above_lane = suf - local;
-    const int need = a.k;
+    const int need = ch.kk;
     const bool mine = above_lane < need && need <= suf;
     int bstar = 0, above = 0, inbin = 0;
     if (mine) {
@@ -841,21 +835,21 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
     if (flag[0] == 0) {
       // every row's candidates fit: one streaming pass
       KRegs kr = kpre;
-      for (int blk = w; blk < nblk; blk += NW) {
+      for (int blk = blk0 + w; blk < blk1; blk += NW) {
         const uint32_t valid = ragged && blk == nblk - 1 ? valid_bits(blk) : 0xFFFFu;
 #pragma unroll
         for (int tl = 0; tl < TL; ++tl) {
           float s[4][4];
           block_scores(kr, qlr, tl, s);
-          if (tl == TL - 1 && blk + NW < nblk) load_k(kr, Kh, blk + NW, N, g, c16);
+          if (tl == TL - 1 && blk + NW < blk1) load_k(kr, Kh, blk + NW, N, g, c16);
           collect(std::false_type{}, s, tl, blk, valid, 0.f, 0);
         }
       }
     } else {
       // one block at a time (its owner wave appends, at most KB entries per
       // row); rows that could overflow on the next block are cut back first
-      for (int blk = 0; blk < nblk; ++blk) {
-        if (blk % NW == w) {
+      for (int blk = blk0; blk < blk1; ++blk) {
+        if ((blk - blk0) % NW == w) {
           const uint32_t valid = ragged && blk == nblk - 1 ? valid_bits(blk) : 0xFFFFu;
           KRegs kr;
           load_k(kr, Kh, blk, N, g, c16);
@@ -872,7 +866,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
         for (int i = 0; i < TL; ++i) {
           const int r = 4 * w + g + 16 * i;
           const bool work = row0 + r < a.m && rows[r].over && rows[r].cnt > a.cap - KB;
-          if (__ballot(work) != 0) row_cut(sm, a, r, work, c16, g);
+          if (__ballot(work) != 0) row_cut(sm, a, ch.kk, r, work, c16, g);
         }
         __syncthreads();
       }
@@ -885,8 +879,161 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
   for (int i = 0; i < TL; ++i) {
     const int r = 4 * w + g + 16 * i;
     const bool work = row0 + r < a.m;
-    int32_t* out = a.idx + ((size_t)bh * a.m + (work ? row0 + r : 0)) * a.k;
-    row_final(sm, a, r, work, c16, g, out);
+    const size_t row = (size_t)bh * a.m + (work ? row0 + r : 0);
+    if (a.nch == 1) {
+      row_final(sm, a, ch, r, work, c16, g, a.idx + row * a.k, nullptr);
+    } else {
+      const size_t at = (row * a.nch + ch.chunk) * a.k;
+      row_final(sm, a, ch, r, work, c16, g, a.cand_k + at, a.cand_s + at);
+    }
+  }
+}
+
+// One wave per (head, landmark row) joins the chunks of the landmark pass.
+// V_L: the chunks' unnormalised sums by log-sum-exp.  Top-k: the chunks'
+// candidate lists hold n = (nch - 1) * k + kk_last (score, key) entries,
+// ascending by key within a chunk and chunks in key order, so ascending over
+// the whole list; the row's k best (larger score, then lower key id) are
+// found by a 256-bin histogram over the entries' range: every entry above the
+// boundary bin is taken and the boundary bin's entries are ranked among
+// themselves (through an LDS list, or, when more than LISTCAP share the bin,
+// against every entry in it); winners are written in list order, which is
+// ascending key order.
+constexpr int MERGE_WAVES = 4;
+constexpr int LISTCAP = 256;
+
+__device__ __forceinline__ int wave_suffix(int v, int lane) {
+  // inclusive suffix sum over the 64 lanes
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int x = __shfl_down(v, o, 64);
+    v += lane + o < 64 ? x : 0;
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(64 * MERGE_WAVES) void merge_kernel(Args a) {
+  __shared__ uint32_t hist[MERGE_WAVES][256];
+  __shared__ float2 blist[MERGE_WAVES][LISTCAP];
+  __shared__ int bcount[MERGE_WAVES];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * MERGE_WAVES + w;
+  if (row >= (long long)a.BH * a.m) return;  // (wave-level work only below)
+  const int nch = a.nch, k = a.k;
+  // ---- V_L
+  {
+    const float* pp = a.vlpart + row * nch * PART_STRIDE;
+    float M = -INFINITY;
+    for (int c = 0; c < nch; ++c) M = fmaxf(M, pp[c * PART_STRIDE + 64]);
+    float o = 0.f, L = 0.f;
+    for (int c = 0; c < nch; ++c) {
+      const float f = __builtin_amdgcn_exp2f((pp[c * PART_STRIDE + 64] - M) * kTauLog2e);
+      o = fmaf(f, pp[c * PART_STRIDE + lane], o);
+      L = fmaf(f, pp[c * PART_STRIDE + 65], L);
+    }
+    a.vl[row * 64 + lane] = o / L;
+  }
+  // ---- top-k
+  const int last_keys = a.N - (nch - 1) * a.cblk * KB;
+  const int n = (nch - 1) * k + min(k, last_keys);
+  const float* cs = a.cand_s + row * nch * k;
+  const int32_t* ck = a.cand_k + row * nch * k;
+  float lo = INFINITY, hi = -INFINITY;
+  for (int e = lane; e < n; e += 64) {
+    const float v = cs[e];
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+  }
+  lo = wave_min_f(lo);
+  hi = wave_max(hi);
+  const float A = hi > lo ? fminf(256.0f / (hi - lo), 1e30f) : 0.f;
+  const float B = -lo * A;
+  uint32_t* h = hist[w];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) h[4 * lane + q] = 0u;
+  if (lane == 0) bcount[w] = 0;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  for (int e = lane; e < n; e += 64) atomicAdd(&h[bin_of(cs[e], A, B)], 1u);
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  // boundary bin: lane l holds bins 4l .. 4l + 3
+  int cb[4], local = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    cb[q] = (int)h[4 * lane + q];
+    local += cb[q];
+  }
+  const int suf = wave_suffix(local, lane);
+  const int above_lane = suf - local;
+  int bstar = 0, above = 0;
+  if (above_lane < k && k <= suf) {
+    int acc = above_lane;
+    bool found = false;
+#pragma unroll
+    for (int q = 3; q >= 0; --q) {
+      if (!found) {
+        if (acc + cb[q] >= k) {
+          found = true;
+          bstar = 4 * lane + q;
+          above = acc;
+        } else {
+          acc += cb[q];
+        }
+      }
+    }
+  }
+  // exactly one lane found it
+  const uint64_t who = __ballot(above_lane < k && k <= suf);
+  const int src = __ffsll((unsigned long long)who) - 1;
+  bstar = __shfl(bstar, src, 64);
+  above = __shfl(above, src, 64);
+  const int need = k - above;
+  const int nb = __shfl(cb[bstar & 3], bstar >> 2, 64);
+  // the boundary bin's entries into the list (when they fit)
+  const bool listed = nb <= LISTCAP;
+  if (listed) {
+    for (int e = lane; e < n; e += 64) {
+      const float v = cs[e];
+      if (bin_of(v, A, B) == bstar) {
+        const int at = atomicAdd(&bcount[w], 1);
+        blist[w][at] = make_float2(v, __int_as_float(ck[e]));
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+  // winners in list order
+  int32_t* out = a.idx + row * k;
+  int run = 0;
+  for (int e0 = 0; e0 < n; e0 += 64) {
+    const int e = e0 + lane;
+    bool win = false;
+    if (e < n) {
+      const float v = cs[e];
+      const int key = ck[e];
+      const int bn = bin_of(v, A, B);
+      if (bn > bstar) {
+        win = true;
+      } else if (bn == bstar) {
+        int r = 0;
+        if (listed) {
+          for (int j = 0; j < nb; ++j) {
+            const float2 x = blist[w][j];
+            r += better(x.x, __float_as_int(x.y), v, key);
+          }
+        } else {
+          for (int j = 0; j < n; ++j) {
+            const float x = cs[j];
+            r += (bin_of(x, A, B) == bstar && better(x, ck[j], v, key)) ? 1 : 0;
+          }
+        }
+        win = r < need;
+      }
+    }
+    const uint64_t bw = __ballot(win);
+    if (win) out[run + lanes_below(bw)] = ck[e];
+    run += __popcll(bw);
   }
 }
 
@@ -899,21 +1046,56 @@ static int landmark_cap(const Shape& s) {
   return cap <= 512 ? cap : 0;
 }
 
+// Keys per workgroup: the head's blocks split into the fewest chunks of at
+// most 4096 keys (a chunk's key bitmap must fit a histogram row), i.e. one
+// chunk up to 4096 keys.  Measured at 3136 tokens (192 heads, 384 workgroups
+// with one chunk), more chunks only cost: a workgroup's fixed work (clearing
+// its histograms, staging Q_L, each pass's set-up) does not shrink with its
+// share of the keys, and the landmark kernel took 107 us with one chunk, 125
+// us with three (plus 19 us of merge) and 250 us with fourteen.
+static void landmark_chunks(const Shape& s, int& nch, int& cblk) {
+  const int nblk = (s.N + lmk::KB - 1) / lmk::KB;
+  nch = (nblk + 63) / 64;
+  cblk = (nblk + nch - 1) / nch;
+  nch = (nblk + cblk - 1) / cblk;
+}
+
 bool landmark_bf16_supported(const Shape& s) {
   return s.bf16 && landmark_cap(s) > 0 && lmk::lds_bytes(landmark_cap(s)) <= 160 * 1024;
 }
 
+size_t landmark_bf16_scratch_bytes(const Shape& s) {
+  int nch, cblk;
+  landmark_chunks(s, nch, cblk);
+  if (nch == 1) return 0;
+  const size_t rows = (size_t)s.BH * s.m * nch;
+  return align_up(rows * s.k * 4, 256) * 2 + rows * lmk::PART_STRIDE * 4;
+}
+
 hipError_t launch_landmark_bf16(const float* ql, const void* K, const void* V, int32_t* idx,
-                                float* vl, const Shape& s, hipStream_t st) {
+                                float* vl, void* scratch, const Shape& s, hipStream_t st) {
+  int nch, cblk;
+  landmark_chunks(s, nch, cblk);
+  const size_t rows = (size_t)s.BH * s.m * nch;
+  char* sc = (char*)scratch;
+  float* cand_s = nch > 1 ? (float*)sc : nullptr;
+  int32_t* cand_k = nch > 1 ? (int32_t*)(sc + align_up(rows * s.k * 4, 256)) : nullptr;
+  float* vlpart = nch > 1 ? (float*)(sc + 2 * align_up(rows * s.k * 4, 256)) : nullptr;
+  if (nch > 1 && !scratch) return hipErrorInvalidValue;
   lmk::Args a{ql, (const uint16_t*)K, (const uint16_t*)V, idx, vl, s.BH, s.N, s.m, s.k,
-              landmark_cap(s), (s.m + lmk::ROWS - 1) / lmk::ROWS};
+              landmark_cap(s), (s.m + lmk::ROWS - 1) / lmk::ROWS, nch, cblk, cand_s, cand_k,
+              vlpart};
   if (a.cap == 0) return hipErrorInvalidValue;
   const size_t lds = lmk::lds_bytes(a.cap);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   if (const hipError_t e = allow_lds((const void*)lmk::landmark_kernel, 160 * 1024); e != hipSuccess)
     return e;
-  const int grid = ((s.BH + 7) / 8) * 8 * a.tiles;
+  const int grid = ((s.BH + 7) / 8) * 8 * a.tiles * nch;
   lmk::landmark_kernel<<<grid, 64 * lmk::NW, lds, st>>>(a);
+  if (nch == 1) return hipGetLastError();
+  const long long rws = (long long)s.BH * s.m;
+  lmk::merge_kernel<<<(unsigned)((rws + lmk::MERGE_WAVES - 1) / lmk::MERGE_WAVES),
+                      64 * lmk::MERGE_WAVES, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -7,10 +7,14 @@ they share.
 
 Workloads stand in for the token grids of the pages' experiments:
 DeiT-T / DeiT-S on 224x224 ImageNet images (14x14 patch grid), a
-high-resolution 56x56 vision grid, and a 128x128 long-sequence grid
-(page "NeurIPS'26: attention is also an FFN?", sections on image
-classification, semantic segmentation and long-sequence modelling).
-No dataset is read: every tensor is synthetic.
+high-resolution 56x56 vision grid, a 128x128 long-sequence grid, the
+segmentation grids of 1,024 and 1,600 tokens with m = k = 49, and
+one-dimensional sequences of 64K and 256K tokens with m * k = N / 4 (page
+"NeurIPS'26: attention is also an FFN?", sections on image classification,
+semantic segmentation and long-sequence modelling, Figure 4).  A 1-D
+sequence is a grid of one row, so pooling is 1-D adaptive average pooling
+and the smooth component varies along the sequence only.  No dataset is
+read: every tensor is synthetic.
 
 Recipe (per tensor Q, K, V of shape [B, H, N, d], N = grid_h * grid_w,
 token n = y * grid_w + x):
@@ -42,6 +46,17 @@ WORKLOADS = [
     dict(id=3, name="hires-3136", B=32, H=6, grid_h=56, grid_w=56, d=64, m_h=7, m_w=7, k=64,
          dtype="bf16", smooth=True),
     dict(id=4, name="long-16k", B=4, H=8, grid_h=128, grid_w=128, d=64, m_h=16, m_w=16, k=256,
+         dtype="bf16", smooth=True),
+    # segmentation-sized grids (1,024 and 1,600 patch tokens, m = k = 49) and
+    # one-dimensional long sequences (a single row of tokens; m * k = N / 4;
+    # two heads of width 64, i.e. model width 128)
+    dict(id=5, name="ade-1024", B=32, H=6, grid_h=32, grid_w=32, d=64, m_h=7, m_w=7, k=49,
+         dtype="bf16", smooth=True),
+    dict(id=6, name="ade-1600", B=32, H=6, grid_h=40, grid_w=40, d=64, m_h=7, m_w=7, k=49,
+         dtype="bf16", smooth=True),
+    dict(id=7, name="seq-64k", B=4, H=2, grid_h=1, grid_w=65536, d=64, m_h=1, m_w=128, k=128,
+         dtype="bf16", smooth=True),
+    dict(id=8, name="seq-256k", B=1, H=2, grid_h=1, grid_w=262144, d=64, m_h=1, m_w=256, k=256,
          dtype="bf16", smooth=True),
 ]
 

@@ -165,9 +165,13 @@ def test_stage_entry_points_validate():
                            FAKE, 4, None) == mita.MITA_ERR_WORKSPACE
     assert L.mita_landmark_workspace_bytes(1, 1, 196, 64, 25, 25, mita.MITA_BF16) == 0
     # the bf16 MFMA landmark kernel keeps a k + 64 candidate buffer per row in LDS: up to
-    # k = 400; beyond, the scalar kernel and its scratch take over
-    assert L.mita_landmark_workspace_bytes(1, 1, 16384, 64, 256, 400, mita.MITA_BF16) == 0
-    assert L.mita_landmark_workspace_bytes(1, 1, 16384, 64, 256, 401, mita.MITA_BF16) > 0
+    # k = 400; beyond, the scalar kernel and its score-row scratch (m * N floats) take over
+    assert L.mita_landmark_workspace_bytes(1, 1, 16384, 64, 256, 401, mita.MITA_BF16) >= \
+        256 * 16384 * 4
+    # keys split over several workgroups per row leave candidates for a merge: the
+    # long grid needs scratch, a short one (one chunk) none
+    assert 0 < L.mita_landmark_workspace_bytes(1, 1, 16384, 64, 256, 400, mita.MITA_BF16) < \
+        256 * 16384 * 4
     assert L.mita_route(FAKE, FAKE, 1, 1, 196, 64, 25, 1, FAKE, FAKE, None, FAKE, FAKE, 1 << 40,
                         None) == mita.MITA_ERR_INVALID_ARG
     assert L.mita_route(FAKE, FAKE, 1, 1, 3136, 64, 49, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 8,

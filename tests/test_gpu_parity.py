@@ -198,7 +198,8 @@ def test_equal_scores_overflow_the_candidate_buffer():
     _say(f"ok {rep}")
 
 
-@pytest.mark.parametrize("name", ["tiny-fp32", "deit-t", "deit-s", "hires-3136"])
+@pytest.mark.parametrize("name", ["tiny-fp32", "deit-t", "deit-s", "hires-3136", "ade-1024",
+                                  "ade-1600"])
 def test_workload_full(name):
     w = synth.workload(name)
     _say(f"workload {name} (all heads)")
@@ -221,15 +222,30 @@ def test_workload_long_16k_all_heads():
     _say(f"ok {name}: {rep}")
 
 
+@pytest.mark.parametrize("name,heads", [("seq-64k", [(0, 0), (3, 1)]), ("seq-256k", [(0, 1)])],
+                         ids=lambda v: v if isinstance(v, str) else "")
+def test_workload_sequence_sampled_heads(name, heads):
+    """The 1-D sequences at full size (the launch bench.py times); the oracle,
+    ~1.5 s (64K) and ~13 s (256K) a head, checks the listed heads."""
+    w = synth.workload(name)
+    _say(f"workload {name} (full launch, heads {heads})")
+    Q, K, V = synth.workload_inputs(name)
+    res = run_gpu(Q, K, V, w["dtype"], w["grid_h"], w["grid_w"], w["m_h"], w["m_w"], w["k"])
+    rep = parity.run_and_check(res, Q, K, V, w["grid_h"], w["grid_w"], w["m_h"], w["m_w"], w["k"],
+                               TOL[w["dtype"]], heads=heads)
+    _say(f"ok {name}: {rep}")
+
+
 # Shapes the ABI accepts whose bf16 inputs leave the MFMA kernels' ranges for a
-# step and take its scalar kernel: attention for m > 256, routing for m > 512,
-# pooling for grid_w > 256.
+# step and take another kernel: scalar attention for m > 256, scalar routing
+# for m > 512, per-landmark window pooling for grid_w > 256.
 FALLBACKS = [
     # B, H, gh, gw, mh, mw, k
     (1, 1, 32, 32, 20, 20, 30),   # m = 400: scalar attention
     (1, 1, 32, 32, 32, 20, 24),   # m = 640: scalar routing and attention
-    (1, 2, 2, 300, 2, 10, 20),    # grid_w = 300: scalar pooling
-    (1, 1, 3, 320, 1, 300, 9),    # grid_w = 320, m = 300: scalar pooling and attention
+    (1, 2, 2, 300, 2, 10, 20),    # grid_w = 300: window pooling
+    (1, 1, 3, 320, 1, 300, 9),    # grid_w = 320, m = 300: window pooling, scalar attention
+    (2, 1, 1, 5000, 1, 37, 50),   # a 1-D row: ragged windows, keys split over chunks
 ]
 
 

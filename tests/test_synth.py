@@ -35,10 +35,20 @@ def test_deterministic_and_prefix_stable():
 
 def test_workload_table():
     names = [w["name"] for w in synth.WORKLOADS]
-    assert names == ["tiny-fp32", "deit-t", "deit-s", "hires-3136", "long-16k"]
+    assert names == ["tiny-fp32", "deit-t", "deit-s", "hires-3136", "long-16k", "ade-1024",
+                     "ade-1600", "seq-64k", "seq-256k"]
     for w in synth.WORKLOADS:
         assert (w["grid_h"] * w["grid_w"]) >= w["k"] >= 1
         assert w["d"] == 64
+    # the segmentation grids take m = k = 49; the 1-D sequences m * k = N / 4
+    for name, n in [("ade-1024", 1024), ("ade-1600", 1600)]:
+        w = synth.workload(name)
+        assert w["grid_h"] * w["grid_w"] == n and w["m_h"] * w["m_w"] == w["k"] == 49
+    for name in ("seq-64k", "seq-256k"):
+        w = synth.workload(name)
+        N = w["grid_h"] * w["grid_w"]
+        assert w["grid_h"] == 1 and w["m_h"] == 1 and w["m_w"] * w["k"] * 4 == N
+        assert w["H"] * w["d"] == 128
 
 
 def test_tiny_is_plain_fp32_normal():
