@@ -245,6 +245,75 @@ def mita_head(Q, K, V, grid_h, grid_w, m_h, m_w, k, keep_scores=False, s=1, shar
     return res
 
 
+# --------------------------------------------------------------------------
+# backward: gradients of <dOut, out> with respect to Q, K and V
+# --------------------------------------------------------------------------
+# The pages time training with this attention ([ZH], long-sequence section,
+# Table 5 and the route-only ablation), so its gradients are part of the
+# method; they do not describe them.  The plain reading: the top-k sets and
+# the routes are discrete choices, constant under small changes of the
+# inputs, so no gradient flows through them (as through any argmax or sort);
+# everything else is differentiated exactly: the one softmax of step 7, the
+# shared expert's values V_L = softmax(S) V (step 4), the scores S (step 2),
+# and the pooling that makes Q_L (step 1), which feeds both the shared keys
+# and S.
+def softmax_backward(w, dw):
+    """Gradient with respect to the logits z of a row softmax w = softmax(z), given
+    dw = d(loss)/dw:  w * (dw - sum(w * dw))."""
+    return w * (dw - np.sum(w * dw, axis=-1, keepdims=True))
+
+
+def mita_head_backward(Q, K, V, dOut, grid_h, grid_w, m_h, m_w, k, s=1, shared=True):
+    """(dQ, dK, dV) of one (b, h): the gradients of sum(dOut * out), with the top-k sets and
+    routes of the forward pass held fixed.  Steps 7, 4, 2, 1 in reverse."""
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    dOut = np.asarray(dOut, dtype=np.float64)
+    N, d = Q.shape
+    t = tau(d)
+    f = mita_head(Q, K, V, grid_h, grid_w, m_h, m_w, k, keep_scores=True, s=s, shared=shared)
+    QL, S, idx, VL = f["QL"], f["S"], f["idx"], f["VL"]
+    m = QL.shape[0]
+    routes = np.asarray(f["route"]).reshape(N, -1)
+    dQ, dK, dV = np.zeros((N, d)), np.zeros((N, d)), np.zeros((N, d))
+    dQL, dVL = np.zeros((m, d)), np.zeros((m, d))
+    # step 7: out_n = softmax(tau * keys q_n) . vals over the query's entries
+    experts, which = np.unique(routes, axis=0, return_inverse=True)
+    which = np.asarray(which).reshape(-1)
+    for gi, ex in enumerate(experts):
+        g = np.nonzero(which == gi)[0]
+        keys = np.concatenate(([QL] if shared else []) + [K[idx[e]] for e in ex], axis=0)
+        vals = np.concatenate(([VL] if shared else []) + [V[idx[e]] for e in ex], axis=0)
+        w = softmax_rows(t * (Q[g] @ keys.T))                  # |g| x E
+        dz = t * softmax_backward(w, dOut[g] @ vals.T)        # d/d(q . key)
+        dQ[g] += dz @ keys
+        dkeys = dz.T @ Q[g]                                    # E x d
+        dvals = w.T @ dOut[g]
+        off = 0
+        if shared:
+            dQL += dkeys[:m]
+            dVL += dvals[:m]
+            off = m
+        for j, e in enumerate(ex):
+            rows = slice(off + j * k, off + (j + 1) * k)
+            np.add.at(dK, idx[e], dkeys[rows])
+            np.add.at(dV, idx[e], dvals[rows])
+    # step 4: V_L = A V with A = softmax_row(S), S = tau Q_L K^T (step 2)
+    if shared:
+        A = softmax_rows(S)
+        dS = softmax_backward(A, dVL @ V.T)                    # m x N
+        dV += A.T @ dVL
+        dQL += t * (dS @ K)
+        dK += t * (dS.T @ QL)
+    # step 1: Q_L[i] = mean of Q over window i
+    Qg = dQ.reshape(grid_h, grid_w, d)
+    for r, (y0, y1) in enumerate(pool_windows(grid_h, m_h)):
+        for c, (x0, x1) in enumerate(pool_windows(grid_w, m_w)):
+            Qg[y0:y1, x0:x1] += dQL[r * m_w + c] / ((y1 - y0) * (x1 - x0))
+    return dQ, dK, dV
+
+
 def mita_forward(Q, K, V, grid_h, grid_w, m_h, m_w, k, heads=None, s=1, shared=True):
     """The pass over [B, H, N, d] inputs, head by head.
 

@@ -362,6 +362,93 @@ def pin_variant_entry_counts(O):
         assert np.all(w >= 0) and np.allclose(w.sum(1), 1.0, rtol=0, atol=1e-12)
 
 
+# ---------------------------------------------------------------- backward
+def _loss(O, Q, K, V, G, shape, s, shared, want_choices=False):
+    gh, gw, mh, mw, k = shape
+    r = O.mita_head(Q, K, V, gh, gw, mh, mw, k, s=s, shared=shared)
+    loss = float(np.sum(G * r["out"]))
+    return (loss, r["idx"], r["route"]) if want_choices else loss
+
+
+def pin_backward_finite_differences(O):
+    """Every gradient element equals the central difference of sum(dOut * out) computed by
+    the forward oracle (step 1e-6, fp64), for the plain pass, two experts per query and
+    route-only; the inputs are checked to keep every top-k set and route unchanged under
+    each step, so the difference sees only the smooth part."""
+    rng = _rng(83)
+    shape = (4, 5, 2, 2, 6)
+    N, d, h = 20, 8, 1e-6
+    for s, shared in [(1, True), (2, True), (1, False)]:
+        Q, K, V, G = (rng.standard_normal((N, d)) for _ in range(4))
+        _, idx0, route0 = _loss(O, Q, K, V, G, shape, s, shared, True)
+        grads = O.mita_head_backward(Q, K, V, G, *shape, s=s, shared=shared)
+        for which, X in enumerate((Q, K, V)):
+            for n in range(N):
+                for c in range(d):
+                    xs = []
+                    for sign in (1, -1):
+                        Xp = X.copy()
+                        Xp[n, c] += sign * h
+                        args = [Q, K, V]
+                        args[which] = Xp
+                        loss, idx, route = _loss(O, *args, G, shape, s, shared, True)
+                        assert np.array_equal(idx, idx0) and np.array_equal(route, route0), \
+                            "a perturbation flipped a discrete choice: pick other inputs"
+                        xs.append(loss)
+                    fd = (xs[0] - xs[1]) / (2 * h)
+                    assert abs(fd - grads[which][n, c]) < 1e-6, (s, shared, which, n, c)
+
+
+def _torch_pass(Qt, Kt, Vt, shape, idx, route, shared, d):
+    """The forward from library routines: adaptive_avg_pool2d for Q_L, SDPA for V_L and for
+    the output over [Q_L; K] (or K) under an additive log-count mask from idx and route."""
+    gh, gw, mh, mw, k = shape
+    N = gh * gw
+    QL = F.adaptive_avg_pool2d(Qt.reshape(gh, gw, d).permute(2, 0, 1)[None], (mh, mw))
+    QL = QL[0].permute(1, 2, 0).reshape(mh * mw, d)
+    m = mh * mw
+    mask = torch.from_numpy(_log_count_mask(N, m, idx, route, shared))
+    if shared:
+        VL = F.scaled_dot_product_attention(QL[None], Kt[None], Vt[None])[0]
+        keys, vals = torch.cat([QL, Kt]), torch.cat([VL, Vt])
+    else:
+        keys, vals = Kt, Vt
+    return F.scaled_dot_product_attention(Qt[None], keys[None], vals[None], attn_mask=mask[None])[0]
+
+
+def pin_backward_vs_autograd(O):
+    """The gradients equal torch autograd (fp64, CPU) through adaptive average pooling and
+    scaled-dot-product attention, with the oracle's top-k sets and routes as a fixed mask,
+    on overlapping pooling windows, for the plain pass, s = 2 and route-only."""
+    rng = _rng(89)
+    for shape, d, s, shared in [((14, 14, 5, 5, 25), 16, 1, True), ((6, 9, 2, 4, 11), 8, 2, True),
+                                ((7, 6, 3, 3, 9), 8, 1, False), ((5, 8, 2, 3, 7), 8, 3, False)]:
+        gh, gw, mh, mw, k = shape
+        N = gh * gw
+        Q, K, V, G = (rng.standard_normal((N, d)) for _ in range(4))
+        r = O.mita_head(Q, K, V, *shape, s=s, shared=shared)
+        Qt, Kt, Vt = (torch.from_numpy(x.copy()).requires_grad_() for x in (Q, K, V))
+        out = _torch_pass(Qt, Kt, Vt, shape, r["idx"], r["route"], shared, d)
+        assert np.allclose(out.detach().numpy(), r["out"], rtol=0, atol=1e-12), "forward"
+        (out * torch.from_numpy(G)).sum().backward()
+        got = O.mita_head_backward(Q, K, V, G, *shape, s=s, shared=shared)
+        for g_o, t_ in zip(got, (Qt, Kt, Vt)):
+            assert np.allclose(g_o, t_.grad.numpy(), rtol=0, atol=1e-11), (shape, s, shared)
+
+
+def pin_backward_constant_values(O):
+    """V = c everywhere makes out = c whatever the weights: dQ = dK = 0, and since
+    shifting every value row by delta shifts every output by delta, the rows of dV
+    sum to the sum of dOut's rows."""
+    rng = _rng(97)
+    Q, K, G = (rng.standard_normal((6 * 6, 8)) for _ in range(3))
+    V = np.full((36, 8), -0.375)
+    for s, shared in [(1, True), (2, True), (1, False)]:
+        dQ, dK, dV = O.mita_head_backward(Q, K, V, G, 6, 6, 2, 2, 7, s=s, shared=shared)
+        assert np.allclose(dQ, 0, atol=1e-12) and np.allclose(dK, 0, atol=1e-12)
+        assert np.allclose(dV.sum(0), G.sum(0), rtol=0, atol=1e-11)
+
+
 # ---------------------------------------------------------------- the batched pass
 def pin_forward_layout(O):
     """The [B, H] wrapper puts each head's results at its own (b, h), and a

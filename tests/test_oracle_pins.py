@@ -129,6 +129,61 @@ def _attend_multi(kind):
     return attend
 
 
+def _backward_variant(kind):
+    """The oracle's backward with one planted mistake."""
+    def backward(Q, K, V, dOut, grid_h, grid_w, m_h, m_w, k, s=1, shared=True):
+        Q = np.asarray(Q, dtype=np.float64); K = np.asarray(K, dtype=np.float64)
+        V = np.asarray(V, dtype=np.float64); dOut = np.asarray(dOut, dtype=np.float64)
+        N, d = Q.shape
+        t = 1.0 / np.sqrt(d)
+        f = O.mita_head(Q, K, V, grid_h, grid_w, m_h, m_w, k, keep_scores=True, s=s,
+                        shared=shared)
+        QL, S, idx, VL = f["QL"], f["S"], f["idx"], f["VL"]
+        m = QL.shape[0]
+        routes = np.asarray(f["route"]).reshape(N, -1)
+        dQ, dK, dV = np.zeros((N, d)), np.zeros((N, d)), np.zeros((N, d))
+        dQL, dVL = np.zeros((m, d)), np.zeros((m, d))
+        for n in range(N):
+            keys = np.concatenate(([QL] if shared else []) + [K[idx[e]] for e in routes[n]])
+            vals = np.concatenate(([VL] if shared else []) + [V[idx[e]] for e in routes[n]])
+            z = t * (keys @ Q[n]); w = np.exp(z - z.max()); w /= w.sum()
+            dw = vals @ dOut[n]
+            dz = t * (w * dw if kind == "softmax_grad_not_centred" else w * (dw - w @ dw))
+            dQ[n] += dz @ keys
+            dkeys, dvals = np.outer(dz, Q[n]), np.outer(w, dOut[n])
+            off = m if shared else 0
+            if shared:
+                dQL += dkeys[:m]; dVL += dvals[:m]
+            for j, e in enumerate(routes[n]):
+                np.add.at(dK, idx[e], dkeys[off + j * k:off + (j + 1) * k])
+                np.add.at(dV, idx[e], dvals[off + j * k:off + (j + 1) * k])
+        if shared and kind != "no_landmark_value_path":
+            A = np.exp(S - S.max(1, keepdims=True)); A /= A.sum(1, keepdims=True)
+            dA = dVL @ V.T
+            dS = A * (dA - (A * dA).sum(1, keepdims=True))
+            dV += A.T @ dVL
+            dQL += (1.0 if kind == "scores_path_without_tau" else t) * (dS @ K)
+            dK += t * (dS.T @ QL)
+        if kind != "no_pooling_backward":
+            Qg = dQ.reshape(grid_h, grid_w, d)
+            for r, (y0, y1) in enumerate(O.pool_windows(grid_h, m_h)):
+                for c, (x0, x1) in enumerate(O.pool_windows(grid_w, m_w)):
+                    Qg[y0:y1, x0:x1] += dQL[r * m_w + c] / ((y1 - y0) * (x1 - x0))
+        return dQ, dK, dV
+    return backward
+
+
+def test_backward_harness_is_faithful():
+    """The mutant harness for the backward, unmutated, reproduces the oracle."""
+    rng = np.random.default_rng(1)
+    Q, K, V, G = (rng.standard_normal((30, 8)) for _ in range(4))
+    for s, shared in [(1, True), (2, True), (1, False)]:
+        a = O.mita_head_backward(Q, K, V, G, 5, 6, 2, 2, 6, s=s, shared=shared)
+        b = _backward_variant("plain")(Q, K, V, G, 5, 6, 2, 2, 6, s=s, shared=shared)
+        for x, y in zip(a, b):
+            assert np.allclose(x, y, rtol=0, atol=1e-12)
+
+
 _ORIG = {name: getattr(O, name) for name in
          ["pool_windows", "landmark_scores", "expert_topk", "shared_values", "route_queries",
           "group_by_route", "attend_head", "mita_forward"]}
@@ -150,6 +205,13 @@ MUTANTS = {
     "multi_expert_dedup": ("attend_head", _attend_multi("dedup")),
     "multi_expert_first_only": ("attend_head", _attend_multi("first_only")),
     "route_only_keeps_shared": ("attend_head", _attend_multi("keeps_shared")),
+    "backward_softmax_grad_not_centred": ("mita_head_backward",
+                                          _backward_variant("softmax_grad_not_centred")),
+    "backward_no_landmark_value_path": ("mita_head_backward",
+                                        _backward_variant("no_landmark_value_path")),
+    "backward_scores_path_without_tau": ("mita_head_backward",
+                                         _backward_variant("scores_path_without_tau")),
+    "backward_no_pooling_backward": ("mita_head_backward", _backward_variant("no_pooling_backward")),
     "route_top_s_unsorted": ("route_queries",
                              lambda Q, QL, s=1: (np.sort(_ORIG["route_queries"](Q, QL, s)[0], -1)
                                                  if s > 1 else _ORIG["route_queries"](Q, QL, s)[0],
