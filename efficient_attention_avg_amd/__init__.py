@@ -25,7 +25,8 @@ PATHS = {"auto": 0, "fused": 1, "staged": 2}
 EXPORTS = [
     "mita_status_string", "mita_last_error", "mita_version", "mita_workspace_bytes",
     "mita_workspace_bytes_ex", "mita_schedule", "mita_kernel_names", "mita_sync_event_create",
-    "mita_forward", "mita_forward_ex", "mita_forward_noalloc", "mita_pool", "mita_landmark_workspace_bytes",
+    "mita_forward", "mita_forward_ex", "mita_forward_noalloc", "mita_backward",
+    "mita_backward_workspace_bytes", "mita_pool", "mita_landmark_workspace_bytes",
     "mita_landmark", "mita_route_workspace_bytes", "mita_route", "mita_attend",
 ]
 
@@ -76,6 +77,11 @@ def lib() -> ctypes.CDLL:
         L.mita_sync_event_create.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         L.mita_forward.restype = S
         L.mita_forward.argtypes = [P, P, P] + [I] * 8 + [I, P, P, P, P, Z, P]
+        L.mita_backward_workspace_bytes.restype = Z
+        L.mita_backward_workspace_bytes.argtypes = [I] * 8 + [I, ctypes.POINTER(_Extras)]
+        L.mita_backward.restype = S
+        L.mita_backward.argtypes = [P, P, P, P] + [I] * 8 + [I, P, P, P,
+                                                            ctypes.POINTER(_Extras), P, Z, P]
         L.mita_forward_noalloc.restype = S
         L.mita_forward_noalloc.argtypes = [P, P, P] + [I] * 8 + [I, P, P, P, P]
         L.mita_forward_ex.restype = S
@@ -206,6 +212,26 @@ def mita_forward_noalloc(q, k, v, grid_h, grid_w, m_h, m_w, topk, *, out=None, i
                                       m_w, topk, code, _ptr(out), _ptr(idx), _ptr(route),
                                       _stream(q, stream)))
     return dict(out=out, idx=idx, route=route)
+
+
+def mita_backward(q, k, v, dout, grid_h, grid_w, m_h, m_w, topk, *, s=1, route_only=False,
+                  workspace=None, stream=None):
+    """Gradients (dQ, dK, dV), fp32 [B, H, N, d], of sum(dout * out) with the top-k sets
+    and routes of the forward held fixed."""
+    code, torch = _qkv(q, k, v)
+    _grid(q, grid_h, grid_w)
+    B, H, N, d = q.shape
+    _dev(dout, "dout", torch.float32, q.shape)
+    ex = _Extras(s=s, route_only=1 if route_only else 0)
+    nbytes = int(lib().mita_backward_workspace_bytes(B, H, grid_h, grid_w, d, m_h, m_w, topk,
+                                                     code, ctypes.byref(ex)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    grads = [torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(3)]
+    _check(lib().mita_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), B, H, grid_h, grid_w, d,
+                               m_h, m_w, topk, code, *[_ptr(x) for x in grads], ctypes.byref(ex),
+                               _ptr(workspace), workspace.numel(), _stream(q, stream)))
+    return tuple(grads)
 
 
 def mita_kernel_schedule(B, H, grid_h, grid_w, d, m_h, m_w, k, dtype_code, path="auto",

@@ -186,7 +186,7 @@ struct Layout {
   size_t ql, vl, idx, route, counts, offsets, perm, scratch, rscratch, partial, total;
 };
 
-Layout layout_of(const Shape& s) {
+Layout layout_of(const Shape& s, bool with_partial = true) {
   Layout L;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t at = off; off += align_up(bytes, 256); return at; };
@@ -199,7 +199,7 @@ Layout layout_of(const Shape& s) {
   L.perm = take((size_t)s.BH * s.N * s.s * 4);
   L.scratch = take(landmark_scratch(s));
   L.rscratch = take(route_scratch(s));
-  L.partial = take(merges(s) ? mita::attend_partial_bytes(s) : 0);
+  L.partial = take(with_partial && merges(s) ? mita::attend_partial_bytes(s) : 0);
   L.total = off;
   return L;
 }
@@ -430,6 +430,61 @@ mita_status mita_forward_noalloc(const void* Q, const void* K, const void* V, in
   if (need > 0 && (st = scratch_address(&ws)) != MITA_OK) return st;
   return mita_forward_ex(Q, K, V, B, H, grid_h, grid_w, d, m_h, m_w, k, in_dtype, out, idx, route,
                          nullptr, ws, need, stream);
+}
+
+// The backward's workspace: the forward's intermediates (recomputed, the
+// same kernels and so the same choices), then the backward's own buffers.
+size_t backward_layout(const Shape& s, Layout* L) {
+  *L = layout_of(s, false);
+  return L->total + mita::backward_scratch_bytes(s);
+}
+
+size_t mita_backward_workspace_bytes(int B, int H, int grid_h, int grid_w, int d, int m_h,
+                                     int m_w, int k, mita_dtype in_dtype,
+                                     const mita_extras* extras) {
+  Shape s;
+  if (make_shape(B, H, grid_h, grid_w, d, m_h, m_w, k, in_dtype, &s) != MITA_OK) return 0;
+  if (set_variant(extras, &s) != MITA_OK) return 0;
+  Layout L;
+  return backward_layout(s, &L);
+}
+
+mita_status mita_backward(const void* Q, const void* K, const void* V, const float* dout, int B,
+                          int H, int grid_h, int grid_w, int d, int m_h, int m_w, int k,
+                          mita_dtype in_dtype, float* dQ, float* dK, float* dV,
+                          const mita_extras* extras, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  Shape s;
+  mita_status st = make_shape(B, H, grid_h, grid_w, d, m_h, m_w, k, in_dtype, &s);
+  if (st != MITA_OK) return st;
+  if ((st = set_variant(extras, &s)) != MITA_OK) return st;
+  if (!Q || !K || !V || !dout || !dQ || !dK || !dV)
+    return fail(MITA_ERR_INVALID_ARG, "Q, K, V, dOut, dQ, dK and dV are required");
+  if (!aligned16({Q, K, V, dout, dQ, dK, dV}))
+    return fail(MITA_ERR_INVALID_ARG, "Q, K, V, dOut, dQ, dK and dV must be 16-byte aligned");
+  Layout L;
+  const size_t need = backward_layout(s, &L);
+  if (!workspace) return fail(MITA_ERR_INVALID_ARG, "workspace is required");
+  if (workspace_bytes < need)
+    return fail(MITA_ERR_WORKSPACE, "workspace of %zu bytes < %zu needed", workspace_bytes, need);
+  if (((uintptr_t)workspace) & 255) return fail(MITA_ERR_INVALID_ARG, "workspace not 256-byte aligned");
+  char* ws = (char*)workspace;
+  float* ql = (float*)(ws + L.ql);
+  float* vl = (float*)(ws + L.vl);
+  int32_t* idx = (int32_t*)(ws + L.idx);
+  int32_t* route = (int32_t*)(ws + L.route);
+  int32_t* counts = (int32_t*)(ws + L.counts);
+  int32_t* offsets = (int32_t*)(ws + L.offsets);
+  int32_t* perm = (int32_t*)(ws + L.perm);
+  if ((st = run_pool(Q, ql, s, stream)) != MITA_OK) return st;
+  if ((st = run_landmark(ql, K, V, idx, vl, ws + L.scratch, s, stream)) != MITA_OK) return st;
+  if ((st = run_route(Q, ql, route, counts, offsets, perm, ws + L.rscratch, s, stream)) != MITA_OK)
+    return st;
+  if ((st = hip_status(mita::launch_backward(Q, K, V, dout, ql, vl, idx, route, offsets, perm, dQ,
+                                             dK, dV, ws + L.total, s, stream),
+                       "backward launch")) != MITA_OK)
+    return st;
+  return ok();
 }
 
 mita_status mita_pool(const void* Q, int B, int H, int grid_h, int grid_w, int d, int m_h, int m_w,

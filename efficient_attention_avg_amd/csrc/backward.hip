@@ -1,0 +1,535 @@
+// Gradients of the MiTA pass: dQ, dK, dV of sum(dOut * out), with the top-k
+// sets and routes of the forward held fixed (they are discrete choices,
+// constant under small changes of the inputs).  The pages time training
+// with this attention (page "NeurIPS'26：注意力也是FFN？...", long-sequence
+// section, Table 5 and the route-only ablation) but do not describe its
+// backward; it is the chain rule through the forward's steps in reverse:
+//   7  out_n = sum_j w_nj val_j, w_n = softmax(tau q_n . key_j) over the
+//      query's entries (the m shared ones with keys Q_L and values V_L, and
+//      its experts' k routed ones with keys K[idx], values V[idx]):
+//        dz_nj = tau w_nj (dOut_n . val_j - dOut_n . out_n)
+//        dq_n += sum_j dz_nj key_j,  dkey_j += dz_nj q_n,  dval_j += w_nj dOut_n
+//   4  V_L = A V, A = softmax_row(S), S = tau Q_L K^T:
+//        dS_ij = A_ij (dV_L_i . V_j - dV_L_i . V_L_i)
+//        dV += A^T dV_L,  dQ_L += tau dS K,  dK += tau dS^T Q_L
+//   1  Q_L = window means of Q:  dQ_t += sum over windows i holding t of
+//      dQ_L_i / |window i|.
+//
+// Kernels (fp32 arithmetic, fp32 gradients; inputs bf16 or fp32):
+//   query     one wave per query: two sweeps over its entries in chunks of
+//             64 (lane = entry for dot products, lane = channel for sums):
+//             the softmax and out_n (online), then w and dz per entry, which
+//             go to a per-entry buffer, and dq_n;
+//   expert    one workgroup per (head, expert): its key slots' dK and dV
+//             rows summed over the expert's (query, rank) items from that
+//             buffer, then added to dK, dV with one atomic per element (an
+//             expert's keys may be another expert's too);
+//   shared    dQ_L, dV_L from the buffer's shared entries, per 16 landmarks;
+//   stats     each landmark row's softmax maximum and sum over all keys;
+//   landmark  per 64-key block: A and dS for every landmark, the block's dV
+//             and dK rows (owned by the workgroup, added in place) and its
+//             share of dQ_L (atomics);
+//   pool      dQ += each token's windows' dQ_L.
+#include "common.h"
+#include "internal.h"
+
+namespace mita {
+namespace bwd {
+
+template <typename T>
+__device__ __forceinline__ float dot64(const float* a, const T* row) {
+  float acc = 0.f;
+#pragma unroll 16
+  for (int c = 0; c < kHeadDim; ++c) acc = fmaf(a[c], to_f32(row[c]), acc);
+  return acc;
+}
+
+// Where entry j of query n lives: its key and value rows (fp32 for the shared
+// entries, T for the routed ones).
+template <typename T>
+struct Entry {
+  const void* key;
+  const void* val;
+  bool sh;
+};
+
+template <typename T>
+__device__ __forceinline__ Entry<T> entry_of(int j, int ms, int k, const float* qlh,
+                                             const float* vlh, const int32_t* rt,
+                                             const int32_t* idxh, const T* Kh, const T* Vh) {
+  Entry<T> e;
+  if (j < ms) {
+    e.key = qlh + (size_t)j * kHeadDim;
+    e.val = vlh + (size_t)j * kHeadDim;
+    e.sh = true;
+  } else {
+    const int jj = j - ms;
+    const int key = idxh[(size_t)rt[jj / k] * k + jj % k];
+    e.key = Kh + (size_t)key * kHeadDim;
+    e.val = Vh + (size_t)key * kHeadDim;
+    e.sh = false;
+  }
+  return e;
+}
+
+template <typename T>
+__device__ __forceinline__ float dot_entry(const float* a, const void* row, bool sh) {
+  return sh ? dot64<float>(a, reinterpret_cast<const float*>(row))
+            : dot64<T>(a, reinterpret_cast<const T*>(row));
+}
+
+template <typename T>
+__device__ __forceinline__ float elem(const void* row, bool sh, int c) {
+  return sh ? reinterpret_cast<const float*>(row)[c] : to_f32(reinterpret_cast<const T*>(row)[c]);
+}
+
+// ---------------------------------------------------------------- query
+template <typename T>
+__global__ __launch_bounds__(256) void query_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const float* __restrict__ ql, const float* __restrict__ vl, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ route, const float* __restrict__ dout, float* __restrict__ dq,
+    float2* __restrict__ G, int N, int m, int k, int s, int shared, float tau) {
+  __shared__ float qs[4][kHeadDim];
+  __shared__ float gs[4][kHeadDim];
+  __shared__ float pw[4][64];
+  __shared__ const void* prow[4][64];
+  __shared__ bool psh[4][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int bh = blockIdx.y;
+  const int n = blockIdx.x * 4 + wv;
+  if (n >= N) return;  // (wave-level synchronisation only below)
+  const size_t row = (size_t)bh * N + n;
+  qs[wv][lane] = to_f32(Q[row * kHeadDim + lane]);
+  const float g = dout[row * kHeadDim + lane];
+  gs[wv][lane] = g;
+  __builtin_amdgcn_wave_barrier();
+  const int ms = shared ? m : 0, E = ms + s * k;
+  const float* qlh = ql + (size_t)bh * m * kHeadDim;
+  const float* vlh = vl + (size_t)bh * m * kHeadDim;
+  const int32_t* rt = route + row * s;
+  const int32_t* idxh = idx + (size_t)bh * m * k;
+  const T* Kh = K + (size_t)bh * N * kHeadDim;
+  const T* Vh = V + (size_t)bh * N * kHeadDim;
+  // sweep 1: the softmax's maximum and sum, and out_n (lane = channel)
+  float M = -INFINITY, L = 0.f, acc = 0.f;
+  for (int c0 = 0; c0 < E; c0 += 64) {
+    const int j = c0 + lane;
+    float a = -INFINITY;
+    Entry<T> e{nullptr, nullptr, false};
+    if (j < E) {
+      e = entry_of<T>(j, ms, k, qlh, vlh, rt, idxh, Kh, Vh);
+      a = tau * dot_entry<T>(qs[wv], e.key, e.sh);
+    }
+    const float mnew = fmaxf(M, wave_max(a));
+    const float alpha = fast_exp(M - mnew);
+    const float p = j < E ? fast_exp(a - mnew) : 0.f;
+    L = L * alpha + wave_sum(p);
+    acc *= alpha;
+    M = mnew;
+    pw[wv][lane] = p;
+    prow[wv][lane] = e.val;
+    psh[wv][lane] = e.sh;
+    __builtin_amdgcn_wave_barrier();
+    const int nc = min(64, E - c0);
+    for (int t = 0; t < nc; ++t) acc = fmaf(pw[wv][t], elem<T>(prow[wv][t], psh[wv][t], lane), acc);
+    __builtin_amdgcn_wave_barrier();
+  }
+  const float inv = 1.0f / L;
+  const float D = wave_sum(acc * inv * g);  // dOut_n . out_n
+  // sweep 2: w and dz per entry (to the buffer), dq_n (lane = channel)
+  float dqa = 0.f;
+  float2* Gr = G + row * E;
+  for (int c0 = 0; c0 < E; c0 += 64) {
+    const int j = c0 + lane;
+    float dz = 0.f;
+    Entry<T> e{nullptr, nullptr, false};
+    if (j < E) {
+      e = entry_of<T>(j, ms, k, qlh, vlh, rt, idxh, Kh, Vh);
+      const float a = tau * dot_entry<T>(qs[wv], e.key, e.sh);
+      const float w = fast_exp(a - M) * inv;
+      const float dw = dot_entry<T>(gs[wv], e.val, e.sh);
+      dz = tau * w * (dw - D);
+      Gr[j] = make_float2(w, dz);
+    }
+    pw[wv][lane] = dz;
+    prow[wv][lane] = e.key;
+    psh[wv][lane] = e.sh;
+    __builtin_amdgcn_wave_barrier();
+    const int nc = min(64, E - c0);
+    for (int t = 0; t < nc; ++t) dqa = fmaf(pw[wv][t], elem<T>(prow[wv][t], psh[wv][t], lane), dqa);
+    __builtin_amdgcn_wave_barrier();
+  }
+  dq[row * kHeadDim + lane] = dqa;
+}
+
+// ---------------------------------------------------------------- expert
+// Workgroup (expert e, head bh); 64 key slots at a time: thread (slot tid/4,
+// channels 16 (tid%4) ..) sums dz q and w dOut over the expert's items,
+// staged 16 items at a time.
+template <typename T>
+__global__ __launch_bounds__(256) void expert_kernel(
+    const T* __restrict__ Q, const float* __restrict__ dout, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
+    const float2* __restrict__ G, float* __restrict__ dK, float* __restrict__ dV, int N, int m,
+    int k, int s, int ms) {
+  constexpr int IT = 16;
+  __shared__ float qs[IT][kHeadDim];
+  __shared__ float gs[IT][kHeadDim];
+  __shared__ float2 ws[IT][64];
+  const int e = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int E = ms + s * k;
+  const int q0 = offsets[(size_t)bh * (m + 1) + e], cnt = offsets[(size_t)bh * (m + 1) + e + 1] - q0;
+  if (cnt == 0) return;
+  const int32_t* ph = perm + (size_t)bh * N * s + q0;
+  const int sl = tid >> 2, c0 = 16 * (tid & 3);
+  for (int j0 = 0; j0 < k; j0 += 64) {
+    float ak[16], av[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) ak[c] = av[c] = 0.f;
+    for (int i0 = 0; i0 < cnt; i0 += IT) {
+      __syncthreads();
+      for (int it = tid; it < IT * kHeadDim; it += 256) {
+        const int i = it >> 6, c = it & 63;
+        float qv = 0.f, gv = 0.f;
+        if (i0 + i < cnt) {
+          const int t = ph[i0 + i], n = t / s;
+          qv = to_f32(Q[((size_t)bh * N + n) * kHeadDim + c]);
+          gv = dout[((size_t)bh * N + n) * kHeadDim + c];
+        }
+        qs[i][c] = qv;
+        gs[i][c] = gv;
+      }
+      for (int it = tid; it < IT * 64; it += 256) {
+        const int i = it >> 6, j = it & 63;
+        float2 v = make_float2(0.f, 0.f);
+        if (i0 + i < cnt && j0 + j < k) {
+          const int t = ph[i0 + i], n = t / s, r = t - n * s;
+          v = G[((size_t)bh * N + n) * E + ms + r * k + j0 + j];
+        }
+        ws[i][j] = v;
+      }
+      __syncthreads();
+      const int ni = min(IT, cnt - i0);
+      for (int i = 0; i < ni; ++i) {
+        const float2 wz = ws[i][sl];
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          ak[c] = fmaf(wz.y, qs[i][c0 + c], ak[c]);
+          av[c] = fmaf(wz.x, gs[i][c0 + c], av[c]);
+        }
+      }
+    }
+    if (j0 + sl < k) {
+      const int key = idx[((size_t)bh * m + e) * k + j0 + sl];
+      float* dk = dK + ((size_t)bh * N + key) * kHeadDim + c0;
+      float* dv = dV + ((size_t)bh * N + key) * kHeadDim + c0;
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        atomicAdd(dk + c, ak[c]);
+        atomicAdd(dv + c, av[c]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- shared
+// dQ_L[i] = sum_n dz_ni q_n, dV_L[i] = sum_n w_ni dOut_n for 16 landmarks per
+// workgroup (thread: landmark tid/16, channels 4 (tid%16) ..); then each
+// row's dV_L . V_L for the landmark step.
+template <typename T>
+__global__ __launch_bounds__(256) void shared_kernel(
+    const T* __restrict__ Q, const float* __restrict__ dout, const float2* __restrict__ G,
+    const float* __restrict__ vl, float* __restrict__ dql, float* __restrict__ dvl,
+    float4* __restrict__ stats, int N, int m, int E) {
+  constexpr int NB = 32;
+  __shared__ float qs[NB][kHeadDim];
+  __shared__ float gs[NB][kHeadDim];
+  __shared__ float2 ws[NB][16];
+  __shared__ float red[16][16];
+  const int i0 = blockIdx.x * 16, bh = blockIdx.y, tid = threadIdx.x;
+  const int li = tid >> 4, c0 = 4 * (tid & 15);
+  float aq[4] = {0.f, 0.f, 0.f, 0.f}, av[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int n0 = 0; n0 < N; n0 += NB) {
+    __syncthreads();
+    for (int it = tid; it < NB * kHeadDim; it += 256) {
+      const int i = it >> 6, c = it & 63;
+      const bool ok = n0 + i < N;
+      const size_t r = (size_t)bh * N + n0 + i;
+      qs[i][c] = ok ? to_f32(Q[r * kHeadDim + c]) : 0.f;
+      gs[i][c] = ok ? dout[r * kHeadDim + c] : 0.f;
+    }
+    for (int it = tid; it < NB * 16; it += 256) {
+      const int i = it >> 4, l = it & 15;
+      ws[i][l] = (n0 + i < N && i0 + l < m) ? G[((size_t)bh * N + n0 + i) * E + i0 + l]
+                                            : make_float2(0.f, 0.f);
+    }
+    __syncthreads();
+    const int nn = min(NB, N - n0);
+    for (int i = 0; i < nn; ++i) {
+      const float2 wz = ws[i][li];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        aq[c] = fmaf(wz.y, qs[i][c0 + c], aq[c]);
+        av[c] = fmaf(wz.x, gs[i][c0 + c], av[c]);
+      }
+    }
+  }
+  const int i = i0 + li;
+  float part = 0.f;
+  if (i < m) {
+    const size_t r = ((size_t)bh * m + i) * kHeadDim + c0;
+    *reinterpret_cast<float4*>(dql + r) = make_float4(aq[0], aq[1], aq[2], aq[3]);
+    *reinterpret_cast<float4*>(dvl + r) = make_float4(av[0], av[1], av[2], av[3]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) part = fmaf(av[c], vl[r + c], part);
+  }
+  red[li][tid & 15] = part;
+  __syncthreads();
+  if (tid < 16 && i0 + tid < m) {
+    float c = 0.f;
+    for (int q = 0; q < 16; ++q) c += red[tid][q];
+    stats[(size_t)bh * m + i0 + tid].z = c;
+  }
+}
+
+// ---------------------------------------------------------------- stats
+// Each landmark row's maximum and sum of exp(S - max) over all keys, with
+// S = tau Q_L . K: 16 rows per workgroup (thread: row tid/16, keys tid%16 +
+// 16 q of each staged 64-key block).
+template <typename T>
+__global__ __launch_bounds__(256) void stats_kernel(const float* __restrict__ ql,
+                                                    const T* __restrict__ K,
+                                                    float4* __restrict__ stats, int N, int m,
+                                                    float tau) {
+  __shared__ float kb[64][kHeadDim + 1];
+  __shared__ float qr[16][kHeadDim];
+  const int i0 = blockIdx.x * 16, bh = blockIdx.y, tid = threadIdx.x;
+  const int li = tid >> 4, lk = tid & 15;
+  for (int it = tid; it < 16 * kHeadDim; it += 256) {
+    const int i = it >> 6, c = it & 63;
+    qr[i][c] = i0 + i < m ? ql[((size_t)bh * m + i0 + i) * kHeadDim + c] : 0.f;
+  }
+  float M = -INFINITY, L = 0.f;
+  for (int b0 = 0; b0 < N; b0 += 64) {
+    __syncthreads();
+    for (int it = tid; it < 64 * kHeadDim; it += 256) {
+      const int j = it >> 6, c = it & 63;
+      kb[j][c] = b0 + j < N ? to_f32(K[((size_t)bh * N + b0 + j) * kHeadDim + c]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = lk + 16 * q;
+      if (b0 + j >= N) continue;
+      float a = 0.f;
+#pragma unroll 16
+      for (int c = 0; c < kHeadDim; ++c) a = fmaf(qr[li][c], kb[j][c], a);
+      a *= tau;
+      const float mn = fmaxf(M, a);
+      L = L * fast_exp(M - mn) + fast_exp(a - mn);
+      M = mn;
+    }
+  }
+  // combine the 16 threads of a row (lanes 16 li .. 16 li + 15 of one wave)
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) {
+    const float oM = __shfl_xor(M, o, 64), oL = __shfl_xor(L, o, 64);
+    const float mn = fmaxf(M, oM);
+    L = (M > -INFINITY ? L * fast_exp(M - mn) : 0.f) + (oM > -INFINITY ? oL * fast_exp(oM - mn) : 0.f);
+    M = mn;
+  }
+  if (lk == 0 && i0 + li < m) {
+    float4* st = stats + (size_t)bh * m + i0 + li;
+    st->x = M;
+    st->y = L;
+  }
+}
+
+// ---------------------------------------------------------------- landmark
+// Workgroup (64-key block, head): landmark rows 32 at a time; A_ij and dS_ij
+// for the rows and the block's keys into LDS; then the block's dV, dK rows
+// (thread: key tid/4, channels 16 (tid%4) ..) and the rows' dQ_L share
+// (thread: row tid/8, channels 8 (tid%8) .., atomics).
+template <typename T>
+__global__ __launch_bounds__(256) void landmark_kernel(
+    const float* __restrict__ ql, const T* __restrict__ K, const T* __restrict__ V,
+    const float* __restrict__ dvl, const float4* __restrict__ stats, float* __restrict__ dql,
+    float* __restrict__ dK, float* __restrict__ dV, int N, int m, float tau) {
+  constexpr int MR = 32;
+  __shared__ float kb[64][kHeadDim + 1];
+  __shared__ float vb[64][kHeadDim + 1];
+  __shared__ float qr[MR][kHeadDim + 1];
+  __shared__ float dr[MR][kHeadDim + 1];
+  __shared__ float A[MR][65];
+  __shared__ float dS[MR][65];
+  const int b0 = blockIdx.x * 64, bh = blockIdx.y, tid = threadIdx.x;
+  for (int it = tid; it < 64 * kHeadDim; it += 256) {
+    const int j = it >> 6, c = it & 63;
+    const bool ok = b0 + j < N;
+    const size_t r = ((size_t)bh * N + b0 + j) * kHeadDim + c;
+    kb[j][c] = ok ? to_f32(K[r]) : 0.f;
+    vb[j][c] = ok ? to_f32(V[r]) : 0.f;
+  }
+  const int kj = tid >> 2, kc = 16 * (tid & 3);
+  float adv[16], adk[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) adv[c] = adk[c] = 0.f;
+  for (int i0 = 0; i0 < m; i0 += MR) {
+    __syncthreads();
+    for (int it = tid; it < MR * kHeadDim; it += 256) {
+      const int i = it >> 6, c = it & 63;
+      const bool ok = i0 + i < m;
+      qr[i][c] = ok ? ql[((size_t)bh * m + i0 + i) * kHeadDim + c] : 0.f;
+      dr[i][c] = ok ? dvl[((size_t)bh * m + i0 + i) * kHeadDim + c] : 0.f;
+    }
+    __syncthreads();
+    for (int it = tid; it < MR * 64; it += 256) {
+      const int i = it >> 6, j = it & 63;
+      float a = 0.f, ds = 0.f;
+      if (i0 + i < m && b0 + j < N) {
+        const float4 st = stats[(size_t)bh * m + i0 + i];
+        float sc = 0.f, da = 0.f;
+#pragma unroll 16
+        for (int c = 0; c < kHeadDim; ++c) {
+          sc = fmaf(qr[i][c], kb[j][c], sc);
+          da = fmaf(dr[i][c], vb[j][c], da);
+        }
+        a = fast_exp(tau * sc - st.x) / st.y;
+        ds = a * (da - st.z);
+      }
+      A[i][j] = a;
+      dS[i][j] = ds;
+    }
+    __syncthreads();
+    const int nr = min(MR, m - i0);
+    for (int i = 0; i < nr; ++i) {
+      const float a = A[i][kj], ds = dS[i][kj];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        adv[c] = fmaf(a, dr[i][kc + c], adv[c]);
+        adk[c] = fmaf(ds, qr[i][kc + c], adk[c]);
+      }
+    }
+    {
+      const int ri = tid >> 3, rc = 8 * (tid & 7);
+      if (ri < nr) {
+        float aq[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) aq[c] = 0.f;
+        for (int j = 0; j < 64; ++j) {
+          const float ds = dS[ri][j];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) aq[c] = fmaf(ds, kb[j][rc + c], aq[c]);
+        }
+        float* dq = dql + ((size_t)bh * m + i0 + ri) * kHeadDim + rc;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) atomicAdd(dq + c, tau * aq[c]);
+      }
+    }
+  }
+  if (b0 + kj < N) {
+    // the block's rows belong to this workgroup alone: add in place
+    float* dv = dV + ((size_t)bh * N + b0 + kj) * kHeadDim + kc;
+    float* dk = dK + ((size_t)bh * N + b0 + kj) * kHeadDim + kc;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      dv[c] += adv[c];
+      dk[c] += tau * adk[c];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- pool
+// dQ[t] += sum over the windows i holding token t of dQ_L[i] / |window i|;
+// along an axis of g cells pooled to mg windows, cell y lies in windows
+// floor(y mg / g) .. ceil((y + 1) mg / g) - 1.
+__global__ __launch_bounds__(256) void pool_kernel(const float* __restrict__ dql,
+                                                   float* __restrict__ dq, int gh, int gw,
+                                                   int mh, int mw) {
+  const int N = gh * gw, m = mh * mw;
+  const long long it = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int bh = blockIdx.y;
+  if (it >= (long long)N * kHeadDim) return;
+  const int n = (int)(it >> 6), c = (int)(it & 63);
+  const int y = n / gw, x = n - y * gw;
+  const int r0 = (int)(((long long)y * mh) / gh);
+  const int r1 = (int)(((long long)(y + 1) * mh + gh - 1) / gh) - 1;
+  const int c0 = (int)(((long long)x * mw) / gw);
+  const int c1 = (int)(((long long)(x + 1) * mw + gw - 1) / gw) - 1;
+  float acc = 0.f;
+  for (int r = r0; r <= r1; ++r) {
+    int y0, y1;
+    pool_window(r, gh, mh, &y0, &y1);
+    for (int cc = c0; cc <= c1; ++cc) {
+      int x0, x1;
+      pool_window(cc, gw, mw, &x0, &x1);
+      acc += dql[((size_t)bh * m + r * mw + cc) * kHeadDim + c] / (float)((y1 - y0) * (x1 - x0));
+    }
+  }
+  dq[((size_t)bh * N + n) * kHeadDim + c] += acc;
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, long long n) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+}  // namespace bwd
+
+size_t backward_scratch_bytes(const Shape& s) {
+  const size_t E = (size_t)(s.shared ? s.m : 0) + (size_t)s.s * s.k;
+  return align_up((size_t)s.BH * s.N * E * 8, 256) + 2 * align_up((size_t)s.BH * s.m * 64 * 4, 256) +
+         align_up((size_t)s.BH * s.m * 16, 256);
+}
+
+template <typename T>
+static hipError_t run_backward(const T* Q, const T* K, const T* V, const float* dout,
+                               const float* ql, const float* vl, const int32_t* idx,
+                               const int32_t* route, const int32_t* offsets,
+                               const int32_t* perm, float* dq, float* dk, float* dv,
+                               void* scratch, const Shape& s, hipStream_t st) {
+  const int ms = s.shared ? s.m : 0;
+  const int E = ms + s.s * s.k;
+  const float tau = 1.0f / sqrtf((float)s.d);
+  char* p = (char*)scratch;
+  float2* G = (float2*)p;
+  p += align_up((size_t)s.BH * s.N * E * 8, 256);
+  float* dql = (float*)p;
+  p += align_up((size_t)s.BH * s.m * 64 * 4, 256);
+  float* dvl = (float*)p;
+  p += align_up((size_t)s.BH * s.m * 64 * 4, 256);
+  float4* stats = (float4*)p;
+  const long long nel = (long long)s.BH * s.N * 64;
+  const unsigned zb = (unsigned)((nel + 255) / 256);
+  bwd::zero_kernel<<<zb, 256, 0, st>>>(dk, nel);
+  bwd::zero_kernel<<<zb, 256, 0, st>>>(dv, nel);
+  bwd::query_kernel<T><<<dim3((s.N + 3) / 4, s.BH), 256, 0, st>>>(
+      Q, K, V, ql, vl, idx, route, dout, dq, G, s.N, s.m, s.k, s.s, s.shared ? 1 : 0, tau);
+  bwd::expert_kernel<T><<<dim3(s.m, s.BH), 256, 0, st>>>(Q, dout, idx, offsets, perm, G, dk, dv,
+                                                         s.N, s.m, s.k, s.s, ms);
+  if (s.shared) {
+    const dim3 rows((s.m + 15) / 16, s.BH);
+    bwd::shared_kernel<T><<<rows, 256, 0, st>>>(Q, dout, G, vl, dql, dvl, stats, s.N, s.m, E);
+    bwd::stats_kernel<T><<<rows, 256, 0, st>>>(ql, K, stats, s.N, s.m, tau);
+    bwd::landmark_kernel<T><<<dim3((s.N + 63) / 64, s.BH), 256, 0, st>>>(
+        ql, K, V, dvl, stats, dql, dk, dv, s.N, s.m, tau);
+    bwd::pool_kernel<<<dim3((unsigned)(((long long)s.N * 64 + 255) / 256), s.BH), 256, 0, st>>>(
+        dql, dq, s.grid_h, s.grid_w, s.m_h, s.m_w);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const void* Q, const void* K, const void* V, const float* dout,
+                           const float* ql, const float* vl, const int32_t* idx,
+                           const int32_t* route, const int32_t* offsets, const int32_t* perm,
+                           float* dq, float* dk, float* dv, void* scratch, const Shape& s,
+                           hipStream_t st) {
+  if (s.bf16)
+    return run_backward<bf16_t>((const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, dout, ql, vl,
+                                idx, route, offsets, perm, dq, dk, dv, scratch, s, st);
+  return run_backward<float>((const float*)Q, (const float*)K, (const float*)V, dout, ql, vl, idx,
+                             route, offsets, perm, dq, dk, dv, scratch, s, st);
+}
+
+}  // namespace mita

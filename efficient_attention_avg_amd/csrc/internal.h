@@ -69,6 +69,14 @@ hipError_t launch_attend_bf16(const void* Q, const void* K, const void* V, const
                               hipStream_t st);
 hipError_t launch_merge(const void* partial, float* out, const Shape& s, hipStream_t st);
 
+// gradients of the pass (dQ, dK, dV) given the forward's intermediates
+size_t backward_scratch_bytes(const Shape& s);
+hipError_t launch_backward(const void* Q, const void* K, const void* V, const float* dout,
+                           const float* ql, const float* vl, const int32_t* idx,
+                           const int32_t* route, const int32_t* offsets, const int32_t* perm,
+                           float* dq, float* dk, float* dv, void* scratch, const Shape& s,
+                           hipStream_t st);
+
 // whole pass for short grids in one persistent kernel
 bool fused_supported(const Shape& s);
 hipError_t launch_fused(const void* Q, const void* K, const void* V, float* out, int32_t* idx,

@@ -241,6 +241,27 @@ int mita_kernel_names(int B, int H, int grid_h, int grid_w, int d, int m_h, int 
                       mita_dtype in_dtype, const mita_extras* extras, const char** names,
                       int* starts, int capacity);
 
+/*
+ * Gradients of the pass (training; page [ZH], long-sequence section, Table 5:
+ * the training times with this attention): dQ, dK, dV [B,H,N,d] fp32 of
+ * sum(dOut * out) for dOut [B,H,N,d] fp32, with the top-k sets and routes of
+ * the forward held fixed (discrete choices: no gradient flows through them).
+ * The call recomputes the forward's intermediates with the staged kernels
+ * (the same kernels, so the same choices) and differentiates the one softmax
+ * of the output, the landmark values' softmax and the pooling exactly.
+ * extras: only s and route_only are read (NULL: the plain pass).  Needs
+ * mita_backward_workspace_bytes(...) of workspace, 256-byte aligned.
+ * dQ, dK, dV are overwritten.
+ */
+size_t mita_backward_workspace_bytes(int B, int H, int grid_h, int grid_w, int d,
+                                     int m_h, int m_w, int k, mita_dtype in_dtype,
+                                     const mita_extras* extras);
+mita_status mita_backward(const void* Q, const void* K, const void* V, const float* dout,
+                          int B, int H, int grid_h, int grid_w, int d,
+                          int m_h, int m_w, int k, mita_dtype in_dtype,
+                          float* dQ, float* dK, float* dV, const mita_extras* extras,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------------------
  * The steps one at a time (same kernels as the staged schedule, plain pass,
  * s = 1).  Each takes its inputs from device memory and writes its outputs

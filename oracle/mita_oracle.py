@@ -263,9 +263,12 @@ def softmax_backward(w, dw):
     return w * (dw - np.sum(w * dw, axis=-1, keepdims=True))
 
 
-def mita_head_backward(Q, K, V, dOut, grid_h, grid_w, m_h, m_w, k, s=1, shared=True):
+def mita_head_backward(Q, K, V, dOut, grid_h, grid_w, m_h, m_w, k, s=1, shared=True,
+                       idx=None, route=None):
     """(dQ, dK, dV) of one (b, h): the gradients of sum(dOut * out), with the top-k sets and
-    routes of the forward pass held fixed.  Steps 7, 4, 2, 1 in reverse."""
+    routes of the forward pass held fixed.  Steps 7, 4, 2, 1 in reverse.  idx / route, when
+    given, replace the forward's own choices (to compare with a pass that took the other
+    side of a near-tie)."""
     Q = np.asarray(Q, dtype=np.float64)
     K = np.asarray(K, dtype=np.float64)
     V = np.asarray(V, dtype=np.float64)
@@ -273,9 +276,10 @@ def mita_head_backward(Q, K, V, dOut, grid_h, grid_w, m_h, m_w, k, s=1, shared=T
     N, d = Q.shape
     t = tau(d)
     f = mita_head(Q, K, V, grid_h, grid_w, m_h, m_w, k, keep_scores=True, s=s, shared=shared)
-    QL, S, idx, VL = f["QL"], f["S"], f["idx"], f["VL"]
+    QL, S, VL = f["QL"], f["S"], f["VL"]
+    idx = f["idx"] if idx is None else np.asarray(idx)
     m = QL.shape[0]
-    routes = np.asarray(f["route"]).reshape(N, -1)
+    routes = np.asarray(f["route"] if route is None else route).reshape(N, -1)
     dQ, dK, dV = np.zeros((N, d)), np.zeros((N, d)), np.zeros((N, d))
     dQL, dVL = np.zeros((m, d)), np.zeros((m, d))
     # step 7: out_n = softmax(tau * keys q_n) . vals over the query's entries
