@@ -341,6 +341,55 @@ def measure_light(name, steps, warmup, s=1, route_only=False, k=None):
     return res
 
 
+def measure_backward(name, steps, warmup):
+    """The backward (mita_backward: the forward's choices recomputed, then dQ, dK, dV) on a
+    workload: cold steps timed by events around each call.  Algorithmic bytes per
+    query-head: Q, K, V and dOut read once, dQ, dK, dV written once."""
+    import torch
+
+    import efficient_attention_avg_amd as mita
+    import synth
+    w = synth.workload(name)
+    Q, K, V = synth.workload_inputs(name)
+    dt = torch.bfloat16 if w["dtype"] == "bf16" else torch.float32
+    q, k, v = (torch.from_numpy(x).to(dt).cuda() for x in (Q, K, V))
+    g = torch.randn(q.shape, dtype=torch.float32, device="cuda",
+                    generator=torch.Generator(device="cuda").manual_seed(0))
+    args = (w["grid_h"], w["grid_w"], w["m_h"], w["m_w"], w["k"])
+    code = mita.MITA_BF16 if w["dtype"] == "bf16" else mita.MITA_F32
+    ex = mita._Extras()
+    import ctypes
+    nb = int(mita.lib().mita_backward_workspace_bytes(w["B"], w["H"], *args[:2], w["d"],
+                                                     *args[2:], code, ctypes.byref(ex)))
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    flush = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros((), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        mita.mita_backward(q, k, v, g, *args, workspace=ws)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for e0, e1 in ev:
+        sink += flush.sum()
+        e0.record()
+        mita.mita_backward(q, k, v, g, *args, workspace=ws)
+        e1.record()
+    torch.cuda.synchronize()
+    ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    mean = sum(ms) / len(ms)
+    qh = w["B"] * w["H"] * w["grid_h"] * w["grid_w"]
+    s_in = 2 if w["dtype"] == "bf16" else 4
+    per_qh = 3 * w["d"] * s_in + w["d"] * 4 + 3 * w["d"] * 4
+    gbs = per_qh * qh / (mean * 1e-3) / 1e9
+    log(f"{name} backward: {mean * 1e3:.1f} us/step")
+    del q, k, v, g, ws, flush
+    torch.cuda.empty_cache()
+    return dict(workload=describe(w) + ", backward (dQ, dK, dV)", value=qh / (mean * 1e-3),
+                unit="query-heads/s", ms_per_step=mean, ms_median=ms[len(ms) // 2],
+                pass_roofline=dict(bound="hbm", achieved=gbs, peak=HBM_PEAK_GBS, unit="GB/s",
+                                   frac=gbs / HBM_PEAK_GBS, bytes_per_qh=per_qh))
+
+
 # the other workloads and the variants, one light record each
 EXTRA_LINES = [
     ("deit-t", 1, False, None), ("long-16k", 1, False, None), ("ade-1024", 1, False, None),
@@ -495,6 +544,8 @@ def main():
     if not args.no_extras:
         for name, s_, ro, k in EXTRA_LINES:
             extras.append(measure_light(name, args.extra_steps, 5, s=s_, route_only=ro, k=k))
+        for name in ("deit-s", "hires-3136"):
+            extras.append(measure_backward(name, args.extra_steps, 3))
     w = main_res["workload"]
     line = {
         "metric": METRIC, "value": main_res["value"], "unit": "query-heads/s", "n_gpus": 1,

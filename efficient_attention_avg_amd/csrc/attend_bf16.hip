@@ -30,6 +30,7 @@
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
+#include "select.h"
 
 namespace mita {
 namespace att {
@@ -38,8 +39,6 @@ constexpr int TQ = 64;    // queries per pass (16 per wave)
 constexpr int EC = 64;    // expert slots per LDS chunk
 constexpr int EVT_STRIDE = EC * 2 + 16;
 constexpr int MAXM = 256;
-
-__device__ __forceinline__ int rc(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
 
 struct Args {
   const uint16_t* Q;
@@ -129,19 +128,6 @@ struct PassOut {
   int nq;
   bool live;
 };
-
-// Lane c16 <-> c16 ^ 8 of each 16-lane row (DPP row rotate by 8).
-__device__ __forceinline__ int swap8(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, false);
-}
-__device__ __forceinline__ f32x4 swap8(f32x4 v) {
-  // (element by value: a bit cast applied to the element expression v[i]
-  // itself was compiled as a read of element 0)
-  f32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = __int_as_float(swap8(__float_as_int(v[i])));
-  return r;
-}
 
 // The pass's output rows (non-temporal: the output is not read again here).
 // Lane (g, c16) holds channels 16 ct + 4g .. + 3 of its query; the lanes

@@ -13,7 +13,7 @@
 //   B  landmark pooling from the Q rows -> Q_L (fp32), split bf16 hi + lo;
 //   C  S^T = K Q_L^T on bf16 MFMA (hi + lo: near-fp32 scores, so top-k sets
 //      and routes are decided at fp32 accuracy), into the shared region X;
-//   D  per landmark row, exact top-k: one 256-bin histogram over the row's
+//   D  per landmark row, exact top-k: one 128-bin histogram over the row's
 //      range, every key above the k-th best's bin taken, that bin's keys by
 //      rank (ties to the lower key id); then P = exp(S - max) in f16;
 //   V  V^T (f16, keys contiguous), loaded into registers at the head's start,
@@ -31,6 +31,7 @@
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
+#include "select.h"
 
 namespace mita {
 namespace fused {
@@ -104,123 +105,9 @@ __device__ __forceinline__ int opaque_zero() {
   (void)g;                                                                     \
   (void)c16
 
-// Byte offset of 16-byte chunk `c` (0..7) of a 128-byte row, XOR-swizzled so
-// that 16 consecutive rows read at one logical chunk spread over the banks.
-__device__ __forceinline__ int rc(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
-
 template <typename P>
 __device__ __forceinline__ P* lds(char* base, int off) {
   return reinterpret_cast<P*>(base + off);
-}
-
-// Reductions and scans inside a 16-lane group with DPP (full-rate VALU, no
-// LDS round trip).  quad_perm [1,0,3,2] and [2,3,0,1] pair lanes at xor 1 and
-// xor 2; row_half_mirror (i <-> 7-i) then row_mirror (i <-> 15-i) combine the
-// quads and then the halves, so after four steps every lane holds the result.
-template <int CTRL>
-__device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-}
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, v)));
-}
-constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
-constexpr int DPP_ROW_SHL1 = 0x101, DPP_ROW_SHL2 = 0x102, DPP_ROW_SHL4 = 0x104,
-              DPP_ROW_SHL8 = 0x108;
-
-// Lane c16 <-> c16 ^ 8 of each 16-lane row (DPP row rotate by 8); the
-// vector form moves each element by value (a bit cast applied to the
-// element expression v[i] itself was compiled as a read of element 0).
-constexpr int DPP_ROW_ROR8 = 0x128;
-__device__ __forceinline__ int swap8(int v) { return dpp_i<DPP_ROW_ROR8>(v); }
-__device__ __forceinline__ f32x4 swap8(f32x4 v) {
-  f32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = __int_as_float(swap8(__float_as_int(v[i])));
-  return r;
-}
-
-__device__ __forceinline__ float g16_max(float v) {
-  v = fmaxf(v, dpp_f<DPP_XOR1>(v));
-  v = fmaxf(v, dpp_f<DPP_XOR2>(v));
-  v = fmaxf(v, dpp_f<DPP_HALF_MIRROR>(v));
-  v = fmaxf(v, dpp_f<DPP_MIRROR>(v));
-  return v;
-}
-__device__ __forceinline__ float g16_min(float v) {
-  v = fminf(v, dpp_f<DPP_XOR1>(v));
-  v = fminf(v, dpp_f<DPP_XOR2>(v));
-  v = fminf(v, dpp_f<DPP_HALF_MIRROR>(v));
-  v = fminf(v, dpp_f<DPP_MIRROR>(v));
-  return v;
-}
-__device__ __forceinline__ float g16_sumf(float v) {
-  v += dpp_f<DPP_XOR1>(v);
-  v += dpp_f<DPP_XOR2>(v);
-  v += dpp_f<DPP_HALF_MIRROR>(v);
-  v += dpp_f<DPP_MIRROR>(v);
-  return v;
-}
-__device__ __forceinline__ int g16_sumi(int v) {
-  v += dpp_i<DPP_XOR1>(v);
-  v += dpp_i<DPP_XOR2>(v);
-  v += dpp_i<DPP_HALF_MIRROR>(v);
-  v += dpp_i<DPP_MIRROR>(v);
-  return v;
-}
-// Inclusive suffix sum over a 16-lane group: lane t gets sum over t' >= t
-// (row_shl:n hands lane t the value of lane t+n, zero past the row end).
-__device__ __forceinline__ int g16_suffix_sum(int v) {
-  v += dpp_i<DPP_ROW_SHL1>(v);
-  v += dpp_i<DPP_ROW_SHL2>(v);
-  v += dpp_i<DPP_ROW_SHL4>(v);
-  v += dpp_i<DPP_ROW_SHL8>(v);
-  return v;
-}
-// Inclusive prefix sum over a 16-lane group: lane t gets sum over t' <= t
-// (row_shr:n hands lane t the value of lane t-n, zero before the row start).
-constexpr int DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114,
-              DPP_ROW_SHR8 = 0x118;
-__device__ __forceinline__ int g16_prefix_sum(int v) {
-  v += dpp_i<DPP_ROW_SHR1>(v);
-  v += dpp_i<DPP_ROW_SHR2>(v);
-  v += dpp_i<DPP_ROW_SHR4>(v);
-  v += dpp_i<DPP_ROW_SHR8>(v);
-  return v;
-}
-// (value, index) argmax over a 16-lane group, ties to the lower index.
-__device__ __forceinline__ void g16_argmax(float& v, int& i) {
-#define MITA_ARGMAX_STEP(CTRL)                                         \
-  {                                                                    \
-    const float ov = dpp_f<CTRL>(v);                                   \
-    const int oi = dpp_i<CTRL>(i);                                     \
-    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }            \
-  }
-  MITA_ARGMAX_STEP(DPP_XOR1)
-  MITA_ARGMAX_STEP(DPP_XOR2)
-  MITA_ARGMAX_STEP(DPP_HALF_MIRROR)
-  MITA_ARGMAX_STEP(DPP_MIRROR)
-#undef MITA_ARGMAX_STEP
-}
-// (value, key) argmax over a 16-lane group: larger value, ties to the lower
-// key (keys distinct; empty lanes hold -inf and INT_MAX).
-__device__ __forceinline__ void g16_argmax_key(float& v, int& key) {
-#define MITA_ARGMAX_KEY_STEP(CTRL)                                    \
-  {                                                                    \
-    const float ov = dpp_f<CTRL>(v);                                   \
-    const int ok = dpp_i<CTRL>(key);                                   \
-    if (ov > v || (ov == v && ok < key)) { v = ov; key = ok; }         \
-  }
-  MITA_ARGMAX_KEY_STEP(DPP_XOR1)
-  MITA_ARGMAX_KEY_STEP(DPP_XOR2)
-  MITA_ARGMAX_KEY_STEP(DPP_HALF_MIRROR)
-  MITA_ARGMAX_KEY_STEP(DPP_MIRROR)
-#undef MITA_ARGMAX_KEY_STEP
-}
-// This lane's 16-lane group's bits of a wave ballot.
-__device__ __forceinline__ uint32_t g16_bits(uint64_t ballot, int g) {
-  return (uint32_t)(ballot >> (16 * g)) & 0xFFFFu;
 }
 
 // Q_L fragments (hi, lo) for both 16-landmark tiles and both 32-channel
@@ -467,8 +354,8 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
           lo = fminf(lo, key0 + u < N ? v[u] : INFINITY);
           hi = fmaxf(hi, v[u]);
         }
-        lo = g16_min(lo);
-        hi = g16_max(hi);
+        lo = g16_minf(lo);
+        hi = g16_maxf(hi);
         const float rmax = hi;
         // 128 equal bins over [lo, hi]: f = (x - lo) * 128 / (hi - lo), bin =
         // floor(f) clamped to [0, 127] (A > 0, so padding has f = -inf and
@@ -504,7 +391,7 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
 #pragma unroll
           for (int q = 0; q < 8; ++q) local += cb[q];
           // keys in bins above this lane's (higher lane = higher bins)
-          int acc = g16_suffix_sum(local) - local;
+          int acc = g16_suffix(local) - local;
           int hit_b = 0, hit_a = 0, hit_n = 0;
 #pragma unroll
           for (int q = 7; q >= 0; --q) {
@@ -516,9 +403,9 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
           }
           // exactly one lane of an active group hits: masked group sums broadcast
           const bool mine = active && hit_n > 0;
-          bstar = g16_sumi(mine ? hit_b : 0);
-          above = g16_sumi(mine ? hit_a : 0);
-          inb = g16_sumi(mine ? hit_n : 0);
+          bstar = g16_addi(mine ? hit_b : 0);
+          above = g16_addi(mine ? hit_a : 0);
+          inb = g16_addi(mine ? hit_n : 0);
         }
         // bin > b* <=> f >= b* + 1 and bin == b* <=> f in [b*, b* + 1), with the
         // clamped end bins open-ended
@@ -549,7 +436,7 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
           uint32_t* tbm = reinterpret_cast<uint32_t*>(hrow + 8 * BLIST);
           const bool sel = need > 0;
           const int nbl = sel ? __popc(bnd) : 0;
-          int p = g16_prefix_sum(nbl) - nbl;
+          int p = g16_prefix(nbl) - nbl;
           // (the histogram has been read: its row now takes the list)
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
           __builtin_amdgcn_wave_barrier();
@@ -605,7 +492,7 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
           for (; __ballot(need > 0) != 0; --need) {
             float wv = bv;
             int wk = bk;
-            g16_argmax_key(wv, wk);
+            g16_argmax(wv, wk);
             const bool win = need > 0 && wk == bk && bk != 0x7FFFFFFF;
             if (win) {
               const int u = bk - key0;
@@ -625,7 +512,7 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
         // own word of the spent histogram
         {
           const int cnt = __popc(take);
-          int pos = g16_prefix_sum(cnt) - cnt;
+          int pos = g16_prefix(cnt) - cnt;
 #pragma unroll
           for (int u = 0; u < MAXNT; ++u) {
             const bool bit = take >> u & 1u;

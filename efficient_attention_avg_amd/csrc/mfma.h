@@ -33,6 +33,11 @@ __device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Byte offset of 16-byte chunk `c` (0..7) of a 128-byte row in LDS,
+// XOR-swizzled so that 16 consecutive rows read at one logical chunk spread
+// over the banks.
+__device__ __forceinline__ int rc(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
+
 // fp32 -> bf16 bits, round to nearest even (inputs are finite).
 __device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
   uint32_t u = __float_as_uint(x);

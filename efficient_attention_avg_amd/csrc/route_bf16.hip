@@ -26,7 +26,6 @@ namespace mita {
 namespace rt {
 
 
-__device__ __forceinline__ int rc(int row, int c) { return row * 128 + ((c ^ (row & 7)) << 4); }
 
 constexpr int RW = 8;  // waves per route workgroup
 

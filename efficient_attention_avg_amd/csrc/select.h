@@ -56,5 +56,54 @@ __device__ __forceinline__ int g16_suffix(int v) {
 __device__ __forceinline__ uint32_t g16_ballot(bool p, int g) {
   return (uint32_t)(__ballot(p) >> (16 * g)) & 0xFFFFu;
 }
+// This lane's 16-lane group's bits of a wave ballot.
+__device__ __forceinline__ uint32_t g16_bits(uint64_t ballot, int g) {
+  return (uint32_t)(ballot >> (16 * g)) & 0xFFFFu;
+}
+__device__ __forceinline__ float g16_sumf(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  return v + dpp_f<kDppMirror>(v);
+}
+// inclusive prefix sum over the row: lane t gets sum over t' <= t (row_shr:n
+// hands lane t the value of lane t-n, zero before the row start)
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+__device__ __forceinline__ int g16_prefix(int v) {
+  v += dpp_i<kDppShr1>(v);
+  v += dpp_i<kDppShr2>(v);
+  v += dpp_i<kDppShr4>(v);
+  return v + dpp_i<kDppShr8>(v);
+}
+// (value, index) argmax over the row, ties to the lower index (empty lanes
+// hold -inf and INT_MAX)
+__device__ __forceinline__ void g16_argmax(float& v, int& i) {
+#define MITA_G16_ARGMAX_STEP(CTRL)                 \
+  {                                                \
+    const float ov = dpp_f<CTRL>(v);               \
+    const int oi = dpp_i<CTRL>(i);                 \
+    if (ov > v || (ov == v && oi < i)) {           \
+      v = ov;                                      \
+      i = oi;                                      \
+    }                                              \
+  }
+  MITA_G16_ARGMAX_STEP(kDppXor1)
+  MITA_G16_ARGMAX_STEP(kDppXor2)
+  MITA_G16_ARGMAX_STEP(kDppHalfMirror)
+  MITA_G16_ARGMAX_STEP(kDppMirror)
+#undef MITA_G16_ARGMAX_STEP
+}
+
+// Lane c16 <-> c16 ^ 8 of each 16-lane row (DPP row rotate by 8); the vector
+// form moves each element by value (a bit cast applied to the element
+// expression v[i] itself was compiled as a read of element 0).
+constexpr int kDppRor8 = 0x128;
+__device__ __forceinline__ int swap8(int v) { return dpp_i<kDppRor8>(v); }
+__device__ __forceinline__ f32x4 swap8(f32x4 v) {
+  f32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __int_as_float(swap8(__float_as_int(v[i])));
+  return r;
+}
 
 }  // namespace mita
