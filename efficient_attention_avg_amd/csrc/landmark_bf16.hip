@@ -15,10 +15,13 @@
 //      V_L^T = V^T P^T (f16 MFMA; V staged transposed in the wave's own LDS
 //      slot; the running maximum is only raised when a score exceeds it by
 //      more than 2^8 in weight, so most blocks skip the rescale); the four
-//      partial results merge by log-sum-exp into V_L, and each row's score
-//      min and max fix 256 equal histogram bins;
-//   H  histogram: the waves recompute their scores (K now in L2) and count
-//      them per row in LDS; the bin holding the k-th best is found per row;
+//      partial results merge by log-sum-exp into V_L.  For k <= 128 the
+//      same scores are counted into each row's 256-bin histogram as they
+//      stream by, on bins fixed from the waves' first blocks (each wave
+//      streams a contiguous quarter, so the samples spread over the keys);
+//   H  (k > 128) histogram: the rows' exact score ranges from pass V fix the
+//      bins, and the waves recompute their scores (K now in L2) to count
+//      them; either way the bin holding the k-th best is found per row;
 //   C  collect: scores in that bin or above go to the row's LDS buffer
 //      (k + 64 entries).  The histogram says beforehand whether a row's
 //      candidates fit; when one does not (many equal scores), the collection
@@ -71,7 +74,8 @@ constexpr int OFF_HIST = 0;
 constexpr int OFF_ROW = OFF_HIST + ROWS * HIST_STRIDE;
 constexpr int OFF_FLAG = OFF_ROW + ROWS * (int)sizeof(RowState);
 constexpr int OFF_QL = (OFF_FLAG + 16 + 15) & ~15;  // Q_L B operands: [tl][ks][hi, lo][lane] x 16 B
-constexpr int OFF_UNION = OFF_QL + TL * 2 * 2 * 64 * 16;
+constexpr int OFF_SAMP = OFF_QL + TL * 2 * 2 * 64 * 16;  // [wave][row] first-block (min, max)
+constexpr int OFF_UNION = OFF_SAMP + NW * ROWS * 8;
 constexpr int VALUES_BYTES = NW * VT_BYTES;  // phase V staging (the merge area aliases it)
 static_assert(NW * ROWS * MERGE_STRIDE * 4 <= VALUES_BYTES, "merge area fits in the staging");
 static_assert(BITMAP_MAX_N / 8 <= HIST_STRIDE && LIST_MAX * 8 <= HIST_STRIDE, "row space");
@@ -88,6 +92,9 @@ struct Args {
   // its chunk's top-k as (score, key) pairs and its unnormalised V_L partial,
   // and merge_kernel finishes both)
   int nch, cblk;
+  // 1: the histogram is built during the values pass on bins fixed from
+  // each wave's first block; 0: a third pass builds it on the exact range
+  int fuse_h;
   float* cand_s;   // [BH][m][nch][k] scores of each chunk's top-k
   int32_t* cand_k; // [BH][m][nch][k] their key ids, ascending within a chunk
   float* vlpart;   // [BH][m][nch][PART_STRIDE]: 64 sums, reference max, sum
@@ -490,9 +497,12 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
   // each pass's first K block is requested before the previous pass's tail
   // (merge, bin search), so that its latency hides behind that work
   KRegs kpre;
+  float A[TL], B[TL];  // this lane's rows' histogram bins: bin = fma(c, A, B)
   // ------------------------------------------------------------ V: values
+  // (and the histogram of the same scores)
   {
     char* vt = sm + OFF_UNION + w * VT_BYTES;
+    const bool fuse = a.fuse_h != 0;
     float mref[TL], mn[TL], mx[TL];
     f32x4 accv[TL][4], lsum[TL];
 #pragma unroll
@@ -509,15 +519,80 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
     ql_load(qlr, sm, lane);  // (this lane's own slots: no barrier needed)
     KRegs kr;
     VRegs vr;
-    if (blk0 + w < blk1) {
-      load_k(kr, Kh, blk0 + w, N, g, c16);
-      load_v(vr, Vh, blk0 + w, N, lane);
+    // in this pass wave w streams a contiguous quarter of the chunk's blocks,
+    // [vb0, vb1), so that the waves' first blocks are spread over it
+    const int nbc = blk1 - blk0;
+    const int vb0 = blk0 + (w * nbc) / NW, vb1 = blk0 + ((w + 1) * nbc) / NW;
+    if (vb0 < vb1) {
+      load_k(kr, Kh, vb0, N, g, c16);
+      load_v(vr, Vh, vb0, N, lane);
     }
-    for (int blk = blk0 + w; blk < blk1; blk += NW) {
+    // the histogram bins, fixed before the scores stream by: each wave's
+    // first block (spread over the chunk) samples every row's scores, and
+    // the 256 bins span [hi - 1.5 r, hi + 0.5 r] around the samples' range
+    // r = hi - lo; scores outside clamp into the end bins.  The bins decide
+    // only how many keys the exact steps below must rank, never which keys
+    // are taken.  (Without fuse the bins come from the exact range after
+    // this pass, and a third pass builds the histogram.)
+    if (fuse) {
+      float slo[TL], shi[TL];
+#pragma unroll
+      for (int tl = 0; tl < TL; ++tl) {
+        slo[tl] = INFINITY;
+        shi[tl] = -INFINITY;
+      }
+      if (vb0 < vb1) {
+        const int blk = vb0;
+#pragma unroll
+        for (int tl = 0; tl < TL; ++tl) {
+          float sc[4][4];
+          block_scores(kr, qlr, tl, sc);
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const bool ok = key_of(blk, kt, g, r) < N;
+              slo[tl] = ok ? fminf(slo[tl], sc[kt][r]) : slo[tl];
+              shi[tl] = ok ? fmaxf(shi[tl], sc[kt][r]) : shi[tl];
+            }
+        }
+      }
+      float2* samp = reinterpret_cast<float2*>(sm + OFF_SAMP);
+#pragma unroll
+      for (int tl = 0; tl < TL; ++tl) {
+        slo[tl] = fminf(slo[tl], __shfl_xor(slo[tl], 16, 64));
+        slo[tl] = fminf(slo[tl], __shfl_xor(slo[tl], 32, 64));
+        shi[tl] = fmaxf(shi[tl], __shfl_xor(shi[tl], 16, 64));
+        shi[tl] = fmaxf(shi[tl], __shfl_xor(shi[tl], 32, 64));
+        if (g == 0) samp[w * ROWS + 16 * tl + c16] = make_float2(slo[tl], shi[tl]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int tl = 0; tl < TL; ++tl) {
+        float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+          const float2 v = samp[ww * ROWS + 16 * tl + c16];
+          lo = fminf(lo, v.x);
+          hi = fmaxf(hi, v.y);
+        }
+        // (the last wave always has a block, so the row has samples)
+        const float r = hi > lo ? hi - lo : fmaxf(fabsf(hi), 1.0f);
+        const float bot = hi - 1.5f * r;
+        A[tl] = fminf(128.0f / r, 1e30f);
+        B[tl] = -bot * A[tl];
+        if (w == 0 && g == 0) {
+          rows[16 * tl + c16].lo = bot;
+          rows[16 * tl + c16].A = A[tl];
+          rows[16 * tl + c16].B = B[tl];
+        }
+      }
+    }
+    for (int blk = vb0; blk < vb1; ++blk) {
       // the V registers are free once stored and the K registers once the
       // scores are out: the next block's loads go out right after each
       store_vt(vr, vt, lane);
-      if (blk + NW < blk1) load_v(vr, Vh, blk + NW, N, lane);
+      if (blk + 1 < vb1) load_v(vr, Vh, blk + 1, N, lane);
       group_sync();
       // the block's V^T A operands, shared by both row tiles:
       // V^T[channel 16ct + c16][keys 32sp + 4g .., 32sp + 16 + 4g ..]
@@ -538,16 +613,26 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
       for (int tl = 0; tl < TL; ++tl) {
         float s[4][4];
         block_scores(kr, qlr, tl, s);
-        if (tl == TL - 1 && blk + NW < blk1) load_k(kr, Kh, blk + NW, N, g, c16);
+        if (tl == TL - 1 && blk + 1 < vb1) load_k(kr, Kh, blk + 1, N, g, c16);
+        // the scores' histogram (keys past N of a ragged last block count
+        // into the spare word past the 256 bins), then their weights
+        uint32_t* myhist =
+            reinterpret_cast<uint32_t*>(sm + OFF_HIST + (16 * tl + c16) * HIST_STRIDE);
         if (last) {
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const bool ok = key_of(blk, kt, g, r) < N;
+              if (fuse) atomicAdd(myhist + (ok ? bin_of(s[kt][r], A[tl], B[tl]) : SPARE_BIN), 1u);
               if (ok) mn[tl] = fminf(mn[tl], s[kt][r]);
               if (!ok) s[kt][r] = -INFINITY;
             }
+        } else if (fuse) {
+#pragma unroll
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) atomicAdd(myhist + bin_of(s[kt][r], A[tl], B[tl]), 1u);
         } else {
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt)
@@ -664,56 +749,59 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
           if (c4 == 0) *reinterpret_cast<float2*>(pp + 64) = make_float2(M, L);
         }
       }
-      if (c4 == 0) {
-        // capped so that fma(c, A, B) stays finite
-        const float A = hi > lo ? fminf(256.0f / (hi - lo), 1e30f) : 0.f;
+      if (!fuse && c4 == 0) {
+        // 256 bins over the chunk's exact score range (capped so that
+        // fma(c, A, B) stays finite)
+        const float Ax = hi > lo ? fminf(256.0f / (hi - lo), 1e30f) : 0.f;
         rows[r].lo = lo;
-        rows[r].A = A;
-        rows[r].B = -lo * A;
+        rows[r].A = Ax;
+        rows[r].B = -lo * Ax;
       }
     }
     __syncthreads();
   }
-  float A[TL], B[TL];
+  if (a.fuse_h == 0) {
 #pragma unroll
-  for (int tl = 0; tl < TL; ++tl) {
-    A[tl] = rows[16 * tl + c16].A;
-    B[tl] = rows[16 * tl + c16].B;
-  }
-
-  // ------------------------------------------------------------ H: histogram
-  {
-    QLRegs qlr;
-    ql_load(qlr, sm, lane);
-    KRegs kr = kpre;
-    for (int blk = blk0 + w; blk < blk1; blk += NW) {
-      // keys past N of a ragged last block count into the spare word past
-      // the 256 bins (no branch per score)
-      uint32_t spare = 0u;
-      if (ragged && blk == nblk - 1) {
+    for (int tl = 0; tl < TL; ++tl) {
+      A[tl] = rows[16 * tl + c16].A;
+      B[tl] = rows[16 * tl + c16].B;
+    }
+    // ---------------------------------------------------------- H: histogram
+    {
+      QLRegs qlr;
+      ql_load(qlr, sm, lane);
+      KRegs kr = kpre;
+      for (int blk = blk0 + w; blk < blk1; blk += NW) {
+        // keys past N of a ragged last block count into the spare word past
+        // the 256 bins (no branch per score)
+        uint32_t spare = 0u;
+        if (ragged && blk == nblk - 1) {
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+          for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) spare |= (key_of(blk, kt, g, r) < N ? 0u : 1u) << (4 * kt + r);
-      }
+            for (int r = 0; r < 4; ++r)
+              spare |= (key_of(blk, kt, g, r) < N ? 0u : 1u) << (4 * kt + r);
+        }
 #pragma unroll
-      for (int tl = 0; tl < TL; ++tl) {
-        float s[4][4];
-        block_scores(kr, qlr, tl, s);
-        if (tl == TL - 1 && blk + NW < blk1) load_k(kr, Kh, blk + NW, N, g, c16);
-        uint32_t* myhist =
-            reinterpret_cast<uint32_t*>(sm + OFF_HIST + (16 * tl + c16) * HIST_STRIDE);
+        for (int tl = 0; tl < TL; ++tl) {
+          float s[4][4];
+          block_scores(kr, qlr, tl, s);
+          if (tl == TL - 1 && blk + NW < blk1) load_k(kr, Kh, blk + NW, N, g, c16);
+          uint32_t* myhist =
+              reinterpret_cast<uint32_t*>(sm + OFF_HIST + (16 * tl + c16) * HIST_STRIDE);
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
+          for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int bin = bin_of(s[kt][r], A[tl], B[tl]);
-            atomicAdd(myhist + ((spare >> (4 * kt + r) & 1u) ? SPARE_BIN : bin), 1u);
-          }
+            for (int r = 0; r < 4; ++r) {
+              const int bin = bin_of(s[kt][r], A[tl], B[tl]);
+              atomicAdd(myhist + ((spare >> (4 * kt + r) & 1u) ? SPARE_BIN : bin), 1u);
+            }
+        }
       }
     }
+    if (blk0 + w < blk1) load_k(kpre, Kh, blk0 + w, N, g, c16);
   }
-  if (blk0 + w < blk1) load_k(kpre, Kh, blk0 + w, N, g, c16);
+
   __syncthreads();
   // the bin holding each row's k-th best: group g of wave w takes rows
   // 4w + g + 16i
@@ -1082,9 +1170,15 @@ hipError_t launch_landmark_bf16(const float* ql, const void* K, const void* V, i
   int32_t* cand_k = nch > 1 ? (int32_t*)(sc + align_up(rows * s.k * 4, 256)) : nullptr;
   float* vlpart = nch > 1 ? (float*)(sc + 2 * align_up(rows * s.k * 4, 256)) : nullptr;
   if (nch > 1 && !scratch) return hipErrorInvalidValue;
+  // the histogram rides the values pass when the candidate buffer's slack
+  // (64 entries past k) is at least half of k: the sampled bins are about
+  // twice as wide as exact ones, and a row whose boundary bin overflows the
+  // slack sends its workgroup down the block-by-block path (measured: 3136
+  // tokens, k = 64: 110 -> 100 us; long-16k, k = 256: 494 -> 733 us fused)
+  const int fuse_h = s.k <= 128 ? 1 : 0;
   lmk::Args a{ql, (const uint16_t*)K, (const uint16_t*)V, idx, vl, s.BH, s.N, s.m, s.k,
-              landmark_cap(s), (s.m + lmk::ROWS - 1) / lmk::ROWS, nch, cblk, cand_s, cand_k,
-              vlpart};
+              landmark_cap(s), (s.m + lmk::ROWS - 1) / lmk::ROWS, nch, cblk, fuse_h, cand_s,
+              cand_k, vlpart};
   if (a.cap == 0) return hipErrorInvalidValue;
   const size_t lds = lmk::lds_bytes(a.cap);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
