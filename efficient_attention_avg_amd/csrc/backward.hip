@@ -30,12 +30,17 @@
 //             and dK rows (owned by the workgroup, added in place) and its
 //             share of dQ_L (atomics);
 //   pool      dQ += each token's windows' dQ_L.
+// Float additions into global memory use the hardware's float atomics
+// (unsafeAtomicAdd: the buffers are ordinary device memory, where they are
+// exact adds), not a compare-and-swap loop.
 #include "common.h"
 #include "internal.h"
 
 namespace mita {
 namespace bwd {
 
+// a . row over 64 channels (`a` in LDS, read by every lane of the wave alike;
+// one row per lane).  (16-byte row loads measured slower: 2.0 -> 2.5 ms.)
 template <typename T>
 __device__ __forceinline__ float dot64(const float* a, const T* row) {
   float acc = 0.f;
@@ -88,8 +93,9 @@ template <typename T>
 __global__ __launch_bounds__(256) void query_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const float* __restrict__ ql, const float* __restrict__ vl, const int32_t* __restrict__ idx,
-    const int32_t* __restrict__ route, const float* __restrict__ dout, float* __restrict__ dq,
-    float2* __restrict__ G, int N, int m, int k, int s, int shared, float tau) {
+    const int32_t* __restrict__ route, const int32_t* __restrict__ perm,
+    const float* __restrict__ dout, float* __restrict__ dq, float2* __restrict__ G, int N, int m,
+    int k, int s, int shared, float tau) {
   __shared__ float qs[4][kHeadDim];
   __shared__ float gs[4][kHeadDim];
   __shared__ float pw[4][64];
@@ -97,8 +103,11 @@ __global__ __launch_bounds__(256) void query_kernel(
   __shared__ bool psh[4][64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int bh = blockIdx.y;
-  const int n = blockIdx.x * 4 + wv;
-  if (n >= N) return;  // (wave-level synchronisation only below)
+  const int p = blockIdx.x * 4 + wv;
+  if (p >= N) return;  // (wave-level synchronisation only below)
+  // s = 1: queries in grouped order, so that neighbouring waves read one
+  // expert's rows from cache
+  const int n = s == 1 ? perm[(size_t)bh * N + p] : p;
   const size_t row = (size_t)bh * N + n;
   qs[wv][lane] = to_f32(Q[row * kHeadDim + lane]);
   const float g = dout[row * kHeadDim + lane];
@@ -132,6 +141,7 @@ __global__ __launch_bounds__(256) void query_kernel(
     psh[wv][lane] = e.sh;
     __builtin_amdgcn_wave_barrier();
     const int nc = min(64, E - c0);
+#pragma unroll 8
     for (int t = 0; t < nc; ++t) acc = fmaf(pw[wv][t], elem<T>(prow[wv][t], psh[wv][t], lane), acc);
     __builtin_amdgcn_wave_barrier();
   }
@@ -157,6 +167,7 @@ __global__ __launch_bounds__(256) void query_kernel(
     psh[wv][lane] = e.sh;
     __builtin_amdgcn_wave_barrier();
     const int nc = min(64, E - c0);
+#pragma unroll 8
     for (int t = 0; t < nc; ++t) dqa = fmaf(pw[wv][t], elem<T>(prow[wv][t], psh[wv][t], lane), dqa);
     __builtin_amdgcn_wave_barrier();
   }
@@ -164,9 +175,10 @@ __global__ __launch_bounds__(256) void query_kernel(
 }
 
 // ---------------------------------------------------------------- expert
-// Workgroup (expert e, head bh); 64 key slots at a time: thread (slot tid/4,
-// channels 16 (tid%4) ..) sums dz q and w dOut over the expert's items,
-// staged 16 items at a time.
+// Workgroup (expert e, head bh); 64 key slots at a time: wave w takes slots
+// 16 w .. 16 w + 15 and lane c channel c, summing dz q and w dOut over the
+// expert's items (staged 16 at a time); each slot's row then goes out as one
+// atomic instruction over 64 contiguous floats (two cache lines).
 template <typename T>
 __global__ __launch_bounds__(256) void expert_kernel(
     const T* __restrict__ Q, const float* __restrict__ dout, const int32_t* __restrict__ idx,
@@ -182,7 +194,7 @@ __global__ __launch_bounds__(256) void expert_kernel(
   const int q0 = offsets[(size_t)bh * (m + 1) + e], cnt = offsets[(size_t)bh * (m + 1) + e + 1] - q0;
   if (cnt == 0) return;
   const int32_t* ph = perm + (size_t)bh * N * s + q0;
-  const int sl = tid >> 2, c0 = 16 * (tid & 3);
+  const int lane = tid & 63, w = tid >> 6;
   for (int j0 = 0; j0 < k; j0 += 64) {
     float ak[16], av[16];
 #pragma unroll
@@ -212,22 +224,22 @@ __global__ __launch_bounds__(256) void expert_kernel(
       __syncthreads();
       const int ni = min(IT, cnt - i0);
       for (int i = 0; i < ni; ++i) {
-        const float2 wz = ws[i][sl];
+        const float qv = qs[i][lane], gv = gs[i][lane];
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-          ak[c] = fmaf(wz.y, qs[i][c0 + c], ak[c]);
-          av[c] = fmaf(wz.x, gs[i][c0 + c], av[c]);
+        for (int j = 0; j < 16; ++j) {
+          const float2 wz = ws[i][16 * w + j];
+          ak[j] = fmaf(wz.y, qv, ak[j]);
+          av[j] = fmaf(wz.x, gv, av[j]);
         }
       }
     }
-    if (j0 + sl < k) {
-      const int key = idx[((size_t)bh * m + e) * k + j0 + sl];
-      float* dk = dK + ((size_t)bh * N + key) * kHeadDim + c0;
-      float* dv = dV + ((size_t)bh * N + key) * kHeadDim + c0;
 #pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        atomicAdd(dk + c, ak[c]);
-        atomicAdd(dv + c, av[c]);
+    for (int j = 0; j < 16; ++j) {
+      const int slot = j0 + 16 * w + j;
+      if (slot < k) {
+        const int key = idx[((size_t)bh * m + e) * k + slot];
+        unsafeAtomicAdd(dK + ((size_t)bh * N + key) * kHeadDim + lane, ak[j]);
+        unsafeAtomicAdd(dV + ((size_t)bh * N + key) * kHeadDim + lane, av[j]);
       }
     }
   }
@@ -412,19 +424,21 @@ __global__ __launch_bounds__(256) void landmark_kernel(
       }
     }
     {
-      const int ri = tid >> 3, rc = 8 * (tid & 7);
-      if (ri < nr) {
-        float aq[8];
+      // wave w: rows w, w + 4, ..; lane: channel (one atomic instruction per
+      // row over 64 contiguous floats)
+      const int lane = tid & 63, wv = tid >> 6;
+      float aq[MR / 4];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) aq[c] = 0.f;
-        for (int j = 0; j < 64; ++j) {
-          const float ds = dS[ri][j];
+      for (int q = 0; q < MR / 4; ++q) aq[q] = 0.f;
+      for (int j = 0; j < 64; ++j) {
+        const float kv = kb[j][lane];
 #pragma unroll
-          for (int c = 0; c < 8; ++c) aq[c] = fmaf(ds, kb[j][rc + c], aq[c]);
-        }
-        float* dq = dql + ((size_t)bh * m + i0 + ri) * kHeadDim + rc;
+        for (int q = 0; q < MR / 4; ++q) aq[q] = fmaf(dS[wv + 4 * q][j], kv, aq[q]);
+      }
 #pragma unroll
-        for (int c = 0; c < 8; ++c) atomicAdd(dq + c, tau * aq[c]);
+      for (int q = 0; q < MR / 4; ++q) {
+        const int ri = wv + 4 * q;
+        if (ri < nr) unsafeAtomicAdd(dql + ((size_t)bh * m + i0 + ri) * kHeadDim + lane, tau * aq[q]);
       }
     }
   }
@@ -443,31 +457,52 @@ __global__ __launch_bounds__(256) void landmark_kernel(
 // ---------------------------------------------------------------- pool
 // dQ[t] += sum over the windows i holding token t of dQ_L[i] / |window i|;
 // along an axis of g cells pooled to mg windows, cell y lies in windows
-// floor(y mg / g) .. ceil((y + 1) mg / g) - 1.
+// floor(y mg / g) .. ceil((y + 1) mg / g) - 1.  Thread: (token, 16 channels).
 __global__ __launch_bounds__(256) void pool_kernel(const float* __restrict__ dql,
                                                    float* __restrict__ dq, int gh, int gw,
                                                    int mh, int mw) {
   const int N = gh * gw, m = mh * mw;
   const long long it = (long long)blockIdx.x * 256 + threadIdx.x;
   const int bh = blockIdx.y;
-  if (it >= (long long)N * kHeadDim) return;
-  const int n = (int)(it >> 6), c = (int)(it & 63);
+  if (it >= (long long)N * 4) return;
+  const int n = (int)(it >> 2), c0 = 16 * (int)(it & 3);
   const int y = n / gw, x = n - y * gw;
   const int r0 = (int)(((long long)y * mh) / gh);
   const int r1 = (int)(((long long)(y + 1) * mh + gh - 1) / gh) - 1;
-  const int c0 = (int)(((long long)x * mw) / gw);
-  const int c1 = (int)(((long long)(x + 1) * mw + gw - 1) / gw) - 1;
-  float acc = 0.f;
+  const int cl = (int)(((long long)x * mw) / gw);
+  const int ch = (int)(((long long)(x + 1) * mw + gw - 1) / gw) - 1;
+  float4 acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int r = r0; r <= r1; ++r) {
     int y0, y1;
     pool_window(r, gh, mh, &y0, &y1);
-    for (int cc = c0; cc <= c1; ++cc) {
+    for (int cc = cl; cc <= ch; ++cc) {
       int x0, x1;
       pool_window(cc, gw, mw, &x0, &x1);
-      acc += dql[((size_t)bh * m + r * mw + cc) * kHeadDim + c] / (float)((y1 - y0) * (x1 - x0));
+      const float inv = 1.0f / (float)((y1 - y0) * (x1 - x0));
+      const float4* src =
+          reinterpret_cast<const float4*>(dql + ((size_t)bh * m + r * mw + cc) * kHeadDim + c0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = src[q];
+        acc[q].x = fmaf(v.x, inv, acc[q].x);
+        acc[q].y = fmaf(v.y, inv, acc[q].y);
+        acc[q].z = fmaf(v.z, inv, acc[q].z);
+        acc[q].w = fmaf(v.w, inv, acc[q].w);
+      }
     }
   }
-  dq[((size_t)bh * N + n) * kHeadDim + c] += acc;
+  float4* dst = reinterpret_cast<float4*>(dq + ((size_t)bh * N + n) * kHeadDim + c0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float4 d = dst[q];
+    d.x += acc[q].x;
+    d.y += acc[q].y;
+    d.z += acc[q].z;
+    d.w += acc[q].w;
+    dst[q] = d;
+  }
 }
 
 __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, long long n) {
@@ -505,7 +540,7 @@ static hipError_t run_backward(const T* Q, const T* K, const T* V, const float* 
   bwd::zero_kernel<<<zb, 256, 0, st>>>(dk, nel);
   bwd::zero_kernel<<<zb, 256, 0, st>>>(dv, nel);
   bwd::query_kernel<T><<<dim3((s.N + 3) / 4, s.BH), 256, 0, st>>>(
-      Q, K, V, ql, vl, idx, route, dout, dq, G, s.N, s.m, s.k, s.s, s.shared ? 1 : 0, tau);
+      Q, K, V, ql, vl, idx, route, perm, dout, dq, G, s.N, s.m, s.k, s.s, s.shared ? 1 : 0, tau);
   bwd::expert_kernel<T><<<dim3(s.m, s.BH), 256, 0, st>>>(Q, dout, idx, offsets, perm, G, dk, dv,
                                                          s.N, s.m, s.k, s.s, ms);
   if (s.shared) {
@@ -514,7 +549,7 @@ static hipError_t run_backward(const T* Q, const T* K, const T* V, const float* 
     bwd::stats_kernel<T><<<rows, 256, 0, st>>>(ql, K, stats, s.N, s.m, tau);
     bwd::landmark_kernel<T><<<dim3((s.N + 63) / 64, s.BH), 256, 0, st>>>(
         ql, K, V, dvl, stats, dql, dk, dv, s.N, s.m, tau);
-    bwd::pool_kernel<<<dim3((unsigned)(((long long)s.N * 64 + 255) / 256), s.BH), 256, 0, st>>>(
+    bwd::pool_kernel<<<dim3((unsigned)(((long long)s.N * 4 + 255) / 256), s.BH), 256, 0, st>>>(
         dql, dq, s.grid_h, s.grid_w, s.m_h, s.m_w);
   }
   return hipGetLastError();
