@@ -454,6 +454,9 @@ __device__ void row_final(char* sm, const Args& a, const Chunk& ch, int lr, bool
   }
 }
 
+// FUSE (a.fuse_h): the histogram is built during pass V; a template
+// parameter so that each form gets its own register allocation.
+template <bool FUSE>
 __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -502,7 +505,6 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
   // (and the histogram of the same scores)
   {
     char* vt = sm + OFF_UNION + w * VT_BYTES;
-    const bool fuse = a.fuse_h != 0;
     float mref[TL], mn[TL], mx[TL];
     f32x4 accv[TL][4], lsum[TL];
 #pragma unroll
@@ -534,7 +536,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
     // only how many keys the exact steps below must rank, never which keys
     // are taken.  (Without fuse the bins come from the exact range after
     // this pass, and a third pass builds the histogram.)
-    if (fuse) {
+    if constexpr (FUSE) {
       float slo[TL], shi[TL];
 #pragma unroll
       for (int tl = 0; tl < TL; ++tl) {
@@ -588,7 +590,12 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
         }
       }
     }
-    for (int blk = vb0; blk < vb1; ++blk) {
+    // one block of this pass; LAST: the chunk's ragged last block, whose keys
+    // past N get score -inf (weight 0) and count into the spare histogram
+    // word (compile-time, like FUSE, so that the steady-state blocks carry
+    // no per-key tests)
+    auto vblock = [&](auto last_c, int blk) {
+      constexpr bool LAST = decltype(last_c)::value;
       // the V registers are free once stored and the K registers once the
       // scores are out: the next block's loads go out right after each
       store_vt(vr, vt, lane);
@@ -607,38 +614,34 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
           av[ct][sp] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
         }
       }
-      const bool last = ragged && blk == nblk - 1;
-      // one tile at a time keeps one tile's scores and weights live
+      uint32_t valid = 0xFFFFu;  // bit 4kt + r: key 64blk + 16kt + 4g + r < N
+      if constexpr (LAST) {
+        valid = 0u;
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) valid |= (key_of(blk, kt, g, r) < N ? 1u : 0u) << (4 * kt + r);
+      }
+      // every tile's scores first, so that the next block's K loads go out
+      // before the weights and products
+      float sc[TL][4][4];
+#pragma unroll
+      for (int tl = 0; tl < TL; ++tl) block_scores(kr, qlr, tl, sc[tl]);
+      if (blk + 1 < vb1) load_k(kr, Kh, blk + 1, N, g, c16);
 #pragma unroll
       for (int tl = 0; tl < TL; ++tl) {
-        float s[4][4];
-        block_scores(kr, qlr, tl, s);
-        if (tl == TL - 1 && blk + 1 < vb1) load_k(kr, Kh, blk + 1, N, g, c16);
-        // the scores' histogram (keys past N of a ragged last block count
-        // into the spare word past the 256 bins), then their weights
+        float (&s)[4][4] = sc[tl];
         uint32_t* myhist =
             reinterpret_cast<uint32_t*>(sm + OFF_HIST + (16 * tl + c16) * HIST_STRIDE);
-        if (last) {
 #pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const bool ok = key_of(blk, kt, g, r) < N;
-              if (fuse) atomicAdd(myhist + (ok ? bin_of(s[kt][r], A[tl], B[tl]) : SPARE_BIN), 1u);
-              if (ok) mn[tl] = fminf(mn[tl], s[kt][r]);
-              if (!ok) s[kt][r] = -INFINITY;
-            }
-        } else if (fuse) {
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) atomicAdd(myhist + bin_of(s[kt][r], A[tl], B[tl]), 1u);
-        } else {
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) mn[tl] = fminf(mn[tl], s[kt][r]);
-        }
+          for (int r = 0; r < 4; ++r) {
+            const bool ok = !LAST || (valid >> (4 * kt + r) & 1u);
+            if constexpr (FUSE) atomicAdd(myhist + (ok ? bin_of(s[kt][r], A[tl], B[tl]) : SPARE_BIN), 1u);
+            else mn[tl] = ok ? fminf(mn[tl], s[kt][r]) : mn[tl];
+            if constexpr (LAST) s[kt][r] = ok ? s[kt][r] : -INFINITY;
+          }
         float bmax = s[0][0];
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
@@ -681,7 +684,13 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
         lsum[tl] = mfma_f16(ones, bp[1], lsum[tl]);
       }
       group_sync();
-    }
+    };
+    // the ragged last block (if this wave streams it) runs on its own
+    const int vsteady = ragged && vb0 < vb1 && vb1 == nblk ? vb1 - 1 : vb1;
+#pragma unroll 1
+    for (int blk = vb0; blk < vsteady; ++blk) vblock(std::false_type{}, blk);
+    if (vsteady < vb1) vblock(std::true_type{}, vsteady);
+
 #pragma unroll
     for (int tl = 0; tl < TL; ++tl) {
       mn[tl] = fminf(mn[tl], __shfl_xor(mn[tl], 16, 64));
@@ -749,7 +758,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
           if (c4 == 0) *reinterpret_cast<float2*>(pp + 64) = make_float2(M, L);
         }
       }
-      if (!fuse && c4 == 0) {
+      if (!FUSE && c4 == 0) {
         // 256 bins over the chunk's exact score range (capped so that
         // fma(c, A, B) stays finite)
         const float Ax = hi > lo ? fminf(256.0f / (hi - lo), 1e30f) : 0.f;
@@ -760,7 +769,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
     }
     __syncthreads();
   }
-  if (a.fuse_h == 0) {
+  if constexpr (!FUSE) {
 #pragma unroll
     for (int tl = 0; tl < TL; ++tl) {
       A[tl] = rows[16 * tl + c16].A;
@@ -921,17 +930,41 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
           }
     };
     if (flag[0] == 0) {
-      // every row's candidates fit: one streaming pass
-      KRegs kr = kpre;
-      for (int blk = blk0 + w; blk < blk1; blk += NW) {
-        const uint32_t valid = ragged && blk == nblk - 1 ? valid_bits(blk) : 0xFFFFu;
+      // every row's candidates fit: one streaming pass.  The wave's blocks
+      // alternate between two register sets, each refilled two blocks ahead
+      // (this pass does little work per block, so one block of lead would
+      // leave the loads' latency exposed).
+      KRegs ka = kpre, kb;
+      if (blk0 + w + NW < blk1) load_k(kb, Kh, blk0 + w + NW, N, g, c16);
+      // LAST: the ragged last block (masked keys), run on its own so that
+      // the steady-state blocks carry no per-key tests
+      auto cblock = [&](auto last_c, int blk, KRegs& kr) {
+        constexpr bool LAST = decltype(last_c)::value;
+        const uint32_t valid = LAST ? valid_bits(blk) : 0xFFFFu;
+        float s[TL][4][4];
 #pragma unroll
-        for (int tl = 0; tl < TL; ++tl) {
-          float s[4][4];
-          block_scores(kr, qlr, tl, s);
-          if (tl == TL - 1 && blk + NW < blk1) load_k(kr, Kh, blk + NW, N, g, c16);
-          collect(std::false_type{}, s, tl, blk, valid, 0.f, 0);
-        }
+        for (int tl = 0; tl < TL; ++tl) block_scores(kr, qlr, tl, s[tl]);
+        if (blk + 2 * NW < blk1) load_k(kr, Kh, blk + 2 * NW, N, g, c16);
+#pragma unroll
+        for (int tl = 0; tl < TL; ++tl) collect(std::false_type{}, s[tl], tl, blk, valid, 0.f, 0);
+      };
+      const int csteady = ragged && blk1 == nblk ? nblk - 1 : blk1;
+      int blk = blk0 + w;
+#pragma unroll 1
+      for (; blk + NW < csteady; blk += 2 * NW) {
+        cblock(std::false_type{}, blk, ka);
+        cblock(std::false_type{}, blk + NW, kb);
+      }
+      bool in_b = false;  // the next block's rows are in kb
+      if (blk < csteady) {
+        cblock(std::false_type{}, blk, ka);
+        in_b = true;
+      }
+      if (csteady < blk1 && (csteady - blk0) % NW == w) {
+        if (in_b)
+          cblock(std::true_type{}, csteady, kb);
+        else
+          cblock(std::true_type{}, csteady, ka);
       }
     } else {
       // one block at a time (its owner wave appends, at most KB entries per
@@ -1182,10 +1215,10 @@ hipError_t launch_landmark_bf16(const float* ql, const void* K, const void* V, i
   if (a.cap == 0) return hipErrorInvalidValue;
   const size_t lds = lmk::lds_bytes(a.cap);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  if (const hipError_t e = allow_lds((const void*)lmk::landmark_kernel, 160 * 1024); e != hipSuccess)
-    return e;
+  auto kernel = fuse_h ? lmk::landmark_kernel<true> : lmk::landmark_kernel<false>;
+  if (const hipError_t e = allow_lds((const void*)kernel, 160 * 1024); e != hipSuccess) return e;
   const int grid = ((s.BH + 7) / 8) * 8 * a.tiles * nch;
-  lmk::landmark_kernel<<<grid, 64 * lmk::NW, lds, st>>>(a);
+  kernel<<<grid, 64 * lmk::NW, lds, st>>>(a);
   if (nch == 1) return hipGetLastError();
   const long long rws = (long long)s.BH * s.m;
   lmk::merge_kernel<<<(unsigned)((rws + lmk::MERGE_WAVES - 1) / lmk::MERGE_WAVES),
