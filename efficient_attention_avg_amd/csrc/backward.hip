@@ -16,6 +16,9 @@
 //      dQ_L_i / |window i|.
 //
 // Kernels (fp32 arithmetic, fp32 gradients; inputs bf16 or fp32):
+//   tile      (s = 1, at most 128 entry columns) the query, expert and shared
+//             steps below in one workgroup per (head, expert) on fp32 MFMA;
+//             otherwise:
 //   query     one wave per query: two sweeps over its entries in chunks of
 //             64 (lane = entry for dot products, lane = channel for sums):
 //             the softmax and out_n (online), then w and dz per entry, which
@@ -35,6 +38,8 @@
 // exact adds), not a compare-and-swap loop.
 #include "common.h"
 #include "internal.h"
+#include "mfma.h"
+#include "select.h"
 
 namespace mita {
 namespace bwd {
@@ -245,6 +250,299 @@ __global__ __launch_bounds__(256) void expert_kernel(
   }
 }
 
+// ---------------------------------------------------------------- tile
+// The query, expert and shared steps in one kernel on fp32 MFMA (16x16x4),
+// for s = 1 with at most 128 entry columns (the m shared entries, then the k
+// routed ones, each padded to a multiple of 16).  Workgroup (expert e, head
+// bh), four waves; the expert's queries go 16 at a time (a tile) and wave w
+// owns the entry column tiles w and w + 4 (16 entries each):
+//   S = Q E_key^T and dW = dOut E_val^T, the wave's entry rows held in
+//     registers as B operands (lane (g, j): entry 16 t + j, channels 16 g ..
+//     16 g + 15, one per k-step) and the tile's rows read from LDS;
+//   the softmax maximum, the sum of weights and dOut . out = sum w dw per
+//     query, each a 16-lane reduction and a sum over the waves through LDS;
+//   dz = tau w (dw - dOut . out);
+//   dE_key += dz^T Q and dE_val += w^T dOut, with the S accumulators as the
+//     A operands as they stand (k-step r pairs lane group g with query
+//     4 g + r), kept in registers over the expert's tiles;
+//   dq = dz E_key over the wave's entries (dz transposed through LDS, the
+//     entry rows from an LDS copy), summed over the waves in LDS and stored
+//     once per query.
+// At the end each entry row goes out with float atomics: routed entries into
+// dK, dV (row = key id), shared ones into dQ_L, dV_L.
+constexpr int TILE_EP = 128;   // entry columns at most
+constexpr int KE_STRIDE = 80;  // floats per LDS entry row (rows 16 banks apart)
+constexpr int ZT_STRIDE = 17;  // floats per transposed dz row
+
+// 16 floats of a row (fp32 or bf16) from channel c0
+__device__ __forceinline__ void load16(const float* row, int c0, float (&v)[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 f = *reinterpret_cast<const float4*>(row + c0 + 4 * q);
+    v[4 * q] = f.x;
+    v[4 * q + 1] = f.y;
+    v[4 * q + 2] = f.z;
+    v[4 * q + 3] = f.w;
+  }
+}
+__device__ __forceinline__ void load16(const bf16_t* row, int c0, float (&v)[16]) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const u32x4 b = *reinterpret_cast<const u32x4*>(row + c0 + 8 * q);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      v[8 * q + 2 * t] = __uint_as_float(b[t] << 16);
+      v[8 * q + 2 * t + 1] = __uint_as_float(b[t] & 0xFFFF0000u);
+    }
+  }
+}
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256, 2) void tile_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const float* __restrict__ ql, const float* __restrict__ vl, const int32_t* __restrict__ idx,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
+    const float* __restrict__ dout, float* __restrict__ dq, float* __restrict__ dK,
+    float* __restrict__ dV, float* __restrict__ dql, float* __restrict__ dvl, int N, int m, int k,
+    int ms, int msp, int ep, float tau) {
+  __shared__ __attribute__((aligned(16))) float qt[16][68];
+  __shared__ __attribute__((aligned(16))) float gt[16][68];
+  __shared__ __attribute__((aligned(16))) float ke[4][32][KE_STRIDE];
+  __shared__ float zt[4][32][ZT_STRIDE];
+  __shared__ __attribute__((aligned(16))) float dqp[4][16][68];
+  __shared__ __attribute__((aligned(16))) float red[3][16][4];
+  __shared__ int qid[16];
+  const int e = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
+  const int q0 = offsets[(size_t)bh * (m + 1) + e], cnt = offsets[(size_t)bh * (m + 1) + e + 1] - q0;
+  if (cnt == 0) return;
+  const float kl2 = tau * 1.4426950408889634f;  // logits in the base-2 domain
+  const int ntile = ep >> 4;
+  // this wave's entry column tiles: w and w + 4 (nt of them)
+  const int nt = (w < ntile ? 1 : 0) + (w + 4 < ntile ? 1 : 0);
+  const int32_t* idxe = idx + ((size_t)bh * m + e) * k;
+  float kb[2][16], vb[2][16];
+  bool valid[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int col = 16 * (w + 4 * i) + j;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) kb[i][c] = vb[i][c] = 0.f;
+    valid[i] = false;
+    if (i < nt) {
+      if (16 * (w + 4 * i) < msp) {
+        valid[i] = col < ms;
+        if (valid[i]) {
+          load16(ql + ((size_t)bh * m + col) * kHeadDim, 16 * g, kb[i]);
+          load16(vl + ((size_t)bh * m + col) * kHeadDim, 16 * g, vb[i]);
+        }
+      } else {
+        const int slot = col - msp;
+        valid[i] = slot < k;
+        if (valid[i]) {
+          const size_t r = ((size_t)bh * N + idxe[slot]) * kHeadDim;
+          load16(K + r, 16 * g, kb[i]);
+          load16(V + r, 16 * g, vb[i]);
+        }
+      }
+      // the key rows again for dq's B operand
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(&ke[w][16 * i + j][16 * g + 4 * q]) =
+            make_float4(kb[i][4 * q], kb[i][4 * q + 1], kb[i][4 * q + 2], kb[i][4 * q + 3]);
+    }
+  }
+  f32x4 adk[2][4], adv[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) adk[i][c4] = adv[i][c4] = zero4();
+  const int32_t* ph = perm + (size_t)bh * N + q0;
+
+  for (int t0 = 0; t0 < cnt; t0 += 16) {
+    const int nq = min(16, cnt - t0);
+    __syncthreads();  // the previous tile's LDS is spent
+    if (tid < 16) qid[tid] = tid < nq ? ph[t0 + tid] : -1;
+    {
+      // rows: thread -> (query tid / 16, channels 4 (tid % 16) ..)
+      const int qi = tid >> 4, c0 = 4 * (tid & 15);
+      float4 qv = make_float4(0.f, 0.f, 0.f, 0.f), gv = qv;
+      if (qi < nq) {
+        const size_t r = ((size_t)bh * N + ph[t0 + qi]) * kHeadDim + c0;
+        qv = make_float4(to_f32(Q[r]), to_f32(Q[r + 1]), to_f32(Q[r + 2]), to_f32(Q[r + 3]));
+        gv = *reinterpret_cast<const float4*>(dout + r);
+      }
+      *reinterpret_cast<float4*>(&qt[qi][c0]) = qv;
+      *reinterpret_cast<float4*>(&gt[qi][c0]) = gv;
+    }
+    __syncthreads();
+    // S and dW: lane (g, j) holds [query 4g + r][entry 16 (w + 4i) + j]
+    f32x4 sa[2], sw[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) sa[i] = sw[i] = zero4();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 a4 = *reinterpret_cast<const float4*>(&qt[j][16 * g + 4 * q]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&gt[j][16 * g + 4 * q]);
+      const float av[4] = {a4.x, a4.y, a4.z, a4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          if (i < nt) {
+            sa[i] = mfma_f32(av[u], kb[i][4 * q + u], sa[i]);
+            sw[i] = mfma_f32(dv[u], vb[i][4 * q + u], sw[i]);
+          }
+    }
+    // logits (base 2; -inf for padding entries) and the row maxima
+    float x[2][4];
+    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[i][r] = i < nt && valid[i] ? sa[i][r] * kl2 : -INFINITY;
+        mx[r] = fmaxf(mx[r], x[i][r]);
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      mx[r] = g16_maxf(mx[r]);
+      if (j == r) red[0][4 * g + r][w] = mx[r];
+    }
+    __syncthreads();
+    float ps[4], pd[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float4 m4 = *reinterpret_cast<const float4*>(&red[0][4 * g + r][0]);
+      mx[r] = fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w));
+      ps[r] = pd[r] = 0.f;
+    }
+    float p[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[i][r] = __builtin_amdgcn_exp2f(x[i][r] - mx[r]);  // 0 at -inf
+        ps[r] += p[i][r];
+        pd[r] = fmaf(p[i][r], sw[i][r], pd[r]);
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      ps[r] = g16_sumf(ps[r]);
+      pd[r] = g16_sumf(pd[r]);
+      if (j == r) {
+        red[1][4 * g + r][w] = ps[r];
+        red[2][4 * g + r][w] = pd[r];
+      }
+    }
+    __syncthreads();
+    // w = p / L, dz = tau w (dw - D), D = sum p dw / L
+    float wt[2][4], dz[2][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float4 l4 = *reinterpret_cast<const float4*>(&red[1][4 * g + r][0]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&red[2][4 * g + r][0]);
+      const float inv = 1.0f / ((l4.x + l4.y) + (l4.z + l4.w));
+      const float D = ((d4.x + d4.y) + (d4.z + d4.w)) * inv;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        wt[i][r] = p[i][r] * inv;
+        dz[i][r] = tau * wt[i][r] * (sw[i][r] - D);
+      }
+    }
+    // dE_key += dz^T Q, dE_val += w^T dOut (k-step r: lane group g with query
+    // 4g + r); dz transposed into the wave's LDS rows for dq
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) {
+        const float bq = qt[4 * g + r][16 * c4 + j], bg = gt[4 * g + r][16 * c4 + j];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          if (i < nt) {
+            adk[i][c4] = mfma_f32(dz[i][r], bq, adk[i][c4]);
+            adv[i][c4] = mfma_f32(wt[i][r], bg, adv[i][c4]);
+          }
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (i < nt) zt[w][16 * i + j][4 * g + r] = dz[i][r];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // dq partial over this wave's entries: lane (g, j) -> [query 4g + r][channel 16 c4 + j]
+    f32x4 aq[4];
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) aq[c4] = zero4();
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (i < nt) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const float a = zt[w][16 * i + 4 * ks + g][j];
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4)
+            aq[c4] = mfma_f32(a, ke[w][16 * i + 4 * ks + g][16 * c4 + j], aq[c4]);
+        }
+      }
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dqp[w][4 * g + r][16 * c4 + j] = aq[c4][r];
+    __syncthreads();
+    {
+      const int qi = tid >> 4, c0 = 4 * (tid & 15);
+      if (qi < nq) {
+        float4 sum = *reinterpret_cast<const float4*>(&dqp[0][qi][c0]);
+#pragma unroll
+        for (int ww = 1; ww < 4; ++ww) {
+          const float4 v = *reinterpret_cast<const float4*>(&dqp[ww][qi][c0]);
+          sum.x += v.x;
+          sum.y += v.y;
+          sum.z += v.z;
+          sum.w += v.w;
+        }
+        *reinterpret_cast<float4*>(dq + ((size_t)bh * N + qid[qi]) * kHeadDim + c0) = sum;
+      }
+    }
+  }
+  // the entries' rows: lane (g, j) holds [entry 16 (w + 4i) + 4g + r][channel 16 c4 + j]
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (i >= nt) continue;
+    const int base = 16 * (w + 4 * i);
+    const bool sh = base < msp;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int col = base + 4 * g + r;
+      float* dk = nullptr;
+      float* dv = nullptr;
+      if (sh) {
+        if (col < ms) {
+          dk = dql + ((size_t)bh * m + col) * kHeadDim;
+          dv = dvl + ((size_t)bh * m + col) * kHeadDim;
+        }
+      } else if (col - msp < k) {
+        const size_t row = ((size_t)bh * N + idxe[col - msp]) * kHeadDim;
+        dk = dK + row;
+        dv = dV + row;
+      }
+      if (dk) {
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          unsafeAtomicAdd(dk + 16 * c4 + j, adk[i][c4][r]);
+          unsafeAtomicAdd(dv + 16 * c4 + j, adv[i][c4][r]);
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- shared
 // dQ_L[i] = sum_n dz_ni q_n, dV_L[i] = sum_n w_ni dOut_n for 16 landmarks per
 // workgroup (thread: landmark tid/16, channels 4 (tid%16) ..); then each
@@ -308,10 +606,13 @@ __global__ __launch_bounds__(256) void shared_kernel(
 // ---------------------------------------------------------------- stats
 // Each landmark row's maximum and sum of exp(S - max) over all keys, with
 // S = tau Q_L . K: 16 rows per workgroup (thread: row tid/16, keys tid%16 +
-// 16 q of each staged 64-key block).
+// 16 q of each staged 64-key block); with dvl given, also the row's
+// dV_L . V_L (otherwise left as the shared step wrote it).
 template <typename T>
 __global__ __launch_bounds__(256) void stats_kernel(const float* __restrict__ ql,
                                                     const T* __restrict__ K,
+                                                    const float* __restrict__ dvl,
+                                                    const float* __restrict__ vl,
                                                     float4* __restrict__ stats, int N, int m,
                                                     float tau) {
   __shared__ float kb[64][kHeadDim + 1];
@@ -351,10 +652,19 @@ __global__ __launch_bounds__(256) void stats_kernel(const float* __restrict__ ql
     L = (M > -INFINITY ? L * fast_exp(M - mn) : 0.f) + (oM > -INFINITY ? oL * fast_exp(oM - mn) : 0.f);
     M = mn;
   }
+  float z = 0.f;
+  if (dvl && i0 + li < m) {
+    const size_t r = ((size_t)bh * m + i0 + li) * kHeadDim + 4 * lk;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) z = fmaf(dvl[r + c], vl[r + c], z);
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);
   if (lk == 0 && i0 + li < m) {
     float4* st = stats + (size_t)bh * m + i0 + li;
     st->x = M;
     st->y = L;
+    if (dvl) st->z = z;
   }
 }
 
@@ -512,6 +822,13 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, long l
 
 }  // namespace bwd
 
+// The tile kernel's case: s = 1 and at most 128 entry columns (m and k each
+// padded to 16).
+static bool bwd_tiled(const Shape& s) {
+  const int ms = s.shared ? s.m : 0;
+  return s.s == 1 && ((ms + 15) & ~15) + ((s.k + 15) & ~15) <= bwd::TILE_EP;
+}
+
 size_t backward_scratch_bytes(const Shape& s) {
   const size_t E = (size_t)(s.shared ? s.m : 0) + (size_t)s.s * s.k;
   return align_up((size_t)s.BH * s.N * E * 8, 256) + 2 * align_up((size_t)s.BH * s.m * 64 * 4, 256) +
@@ -539,14 +856,30 @@ static hipError_t run_backward(const T* Q, const T* K, const T* V, const float* 
   const unsigned zb = (unsigned)((nel + 255) / 256);
   bwd::zero_kernel<<<zb, 256, 0, st>>>(dk, nel);
   bwd::zero_kernel<<<zb, 256, 0, st>>>(dv, nel);
-  bwd::query_kernel<T><<<dim3((s.N + 3) / 4, s.BH), 256, 0, st>>>(
-      Q, K, V, ql, vl, idx, route, perm, dout, dq, G, s.N, s.m, s.k, s.s, s.shared ? 1 : 0, tau);
-  bwd::expert_kernel<T><<<dim3(s.m, s.BH), 256, 0, st>>>(Q, dout, idx, offsets, perm, G, dk, dv,
-                                                         s.N, s.m, s.k, s.s, ms);
+  const dim3 rows((s.m + 15) / 16, s.BH);
+  if (bwd_tiled(s)) {
+    // one kernel for the query, expert and shared steps; dQ_L and dV_L then
+    // collect float atomics
+    const int msp = (ms + 15) & ~15, ep = msp + ((s.k + 15) & ~15);
+    if (s.shared) {
+      const long long nl = (long long)s.BH * s.m * 64;
+      bwd::zero_kernel<<<(unsigned)((nl + 255) / 256), 256, 0, st>>>(dql, nl);
+      bwd::zero_kernel<<<(unsigned)((nl + 255) / 256), 256, 0, st>>>(dvl, nl);
+    }
+    bwd::tile_kernel<T><<<dim3(s.m, s.BH), 256, 0, st>>>(Q, K, V, ql, vl, idx, offsets, perm, dout,
+                                                         dq, dk, dv, dql, dvl, s.N, s.m, s.k, ms,
+                                                         msp, ep, tau);
+  } else {
+    bwd::query_kernel<T><<<dim3((s.N + 3) / 4, s.BH), 256, 0, st>>>(
+        Q, K, V, ql, vl, idx, route, perm, dout, dq, G, s.N, s.m, s.k, s.s, s.shared ? 1 : 0, tau);
+    bwd::expert_kernel<T><<<dim3(s.m, s.BH), 256, 0, st>>>(Q, dout, idx, offsets, perm, G, dk, dv,
+                                                           s.N, s.m, s.k, s.s, ms);
+    if (s.shared)
+      bwd::shared_kernel<T><<<rows, 256, 0, st>>>(Q, dout, G, vl, dql, dvl, stats, s.N, s.m, E);
+  }
   if (s.shared) {
-    const dim3 rows((s.m + 15) / 16, s.BH);
-    bwd::shared_kernel<T><<<rows, 256, 0, st>>>(Q, dout, G, vl, dql, dvl, stats, s.N, s.m, E);
-    bwd::stats_kernel<T><<<rows, 256, 0, st>>>(ql, K, stats, s.N, s.m, tau);
+    bwd::stats_kernel<T><<<rows, 256, 0, st>>>(ql, K, bwd_tiled(s) ? dvl : nullptr, vl, stats,
+                                               s.N, s.m, tau);
     bwd::landmark_kernel<T><<<dim3((s.N + 63) / 64, s.BH), 256, 0, st>>>(
         ql, K, V, dvl, stats, dql, dk, dv, s.N, s.m, tau);
     bwd::pool_kernel<<<dim3((unsigned)(((long long)s.N * 4 + 255) / 256), s.BH), 256, 0, st>>>(
