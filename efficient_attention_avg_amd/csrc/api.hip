@@ -138,9 +138,10 @@ mita_status run_pool(const void* Q, float* ql, const Shape& s, hipStream_t st,
   return r;
 }
 mita_status run_landmark(const float* ql, const void* K, const void* V, int32_t* idx, float* vl,
-                         void* scratch, const Shape& s, hipStream_t st, Marker* mk = nullptr) {
+                         void* scratch, const Shape& s, hipStream_t st, Marker* mk = nullptr,
+                         float4* stats = nullptr) {
   const mita_status r =
-      hip_status(landmark_mfma(s) ? mita::launch_landmark_bf16(ql, K, V, idx, vl, scratch, s, st)
+      hip_status(landmark_mfma(s) ? mita::launch_landmark_bf16(ql, K, V, idx, vl, scratch, s, st, stats)
                                   : mita::launch_landmark(ql, K, V, idx, vl, scratch, s, st),
                  "landmark launch");
   if (mk) mk->mark(st);
@@ -477,11 +478,16 @@ mita_status mita_backward(const void* Q, const void* K, const void* V, const flo
   int32_t* offsets = (int32_t*)(ws + L.offsets);
   int32_t* perm = (int32_t*)(ws + L.perm);
   if ((st = run_pool(Q, ql, s, stream)) != MITA_OK) return st;
-  if ((st = run_landmark(ql, K, V, idx, vl, ws + L.scratch, s, stream)) != MITA_OK) return st;
+  // the MFMA landmark pass also leaves its rows' softmax statistics, which
+  // the backward's landmark step reuses
+  const bool stats_ready = s.shared && landmark_mfma(s);
+  if ((st = run_landmark(ql, K, V, idx, vl, ws + L.scratch, s, stream, nullptr,
+                         stats_ready ? mita::backward_stats(ws + L.total, s) : nullptr)) != MITA_OK)
+    return st;
   if ((st = run_route(Q, ql, route, counts, offsets, perm, ws + L.rscratch, s, stream)) != MITA_OK)
     return st;
   if ((st = hip_status(mita::launch_backward(Q, K, V, dout, ql, vl, idx, route, offsets, perm, dQ,
-                                             dK, dV, ws + L.total, s, stream),
+                                             dK, dV, ws + L.total, s, stream, stats_ready),
                        "backward launch")) != MITA_OK)
     return st;
   return ok();

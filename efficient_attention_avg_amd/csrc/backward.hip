@@ -301,8 +301,10 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <typename T>
-__global__ __launch_bounds__(256, 2) void tile_kernel(
+// NTW: entry column tiles per wave (1 when the entries fit 64 columns: fewer
+// registers and LDS, three workgroups per CU).
+template <typename T, int NTW>
+__global__ __launch_bounds__(256, NTW == 1 ? 3 : 2) void tile_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const float* __restrict__ ql, const float* __restrict__ vl, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
@@ -311,8 +313,8 @@ __global__ __launch_bounds__(256, 2) void tile_kernel(
     int ms, int msp, int ep, float tau) {
   __shared__ __attribute__((aligned(16))) float qt[16][68];
   __shared__ __attribute__((aligned(16))) float gt[16][68];
-  __shared__ __attribute__((aligned(16))) float ke[4][32][KE_STRIDE];
-  __shared__ float zt[4][32][ZT_STRIDE];
+  __shared__ __attribute__((aligned(16))) float ke[4][16 * NTW][KE_STRIDE];
+  __shared__ float zt[4][16 * NTW][ZT_STRIDE];
   __shared__ __attribute__((aligned(16))) float dqp[4][16][68];
   __shared__ __attribute__((aligned(16))) float red[3][16][4];
   __shared__ int qid[16];
@@ -323,12 +325,29 @@ __global__ __launch_bounds__(256, 2) void tile_kernel(
   const float kl2 = tau * 1.4426950408889634f;  // logits in the base-2 domain
   const int ntile = ep >> 4;
   // this wave's entry column tiles: w and w + 4 (nt of them)
-  const int nt = (w < ntile ? 1 : 0) + (w + 4 < ntile ? 1 : 0);
+  const int nt = (w < ntile ? 1 : 0) + (NTW > 1 && w + 4 < ntile ? 1 : 0);
   const int32_t* idxe = idx + ((size_t)bh * m + e) * k;
-  float kb[2][16], vb[2][16];
-  bool valid[2];
+  const int32_t* ph = perm + (size_t)bh * N + q0;
+  // a tile's rows: thread -> (query rq, channels rc0 ..); the next tile's are
+  // requested while the current one is computed
+  const int rq = tid >> 4, rc0 = 4 * (tid & 15);
+  auto fetch = [&](int t0, float4& qv, float4& gv, int& id) {
+    qv = gv = make_float4(0.f, 0.f, 0.f, 0.f);
+    id = -1;
+    if (t0 + rq < cnt) {
+      id = ph[t0 + rq];
+      const size_t r = ((size_t)bh * N + id) * kHeadDim + rc0;
+      qv = make_float4(to_f32(Q[r]), to_f32(Q[r + 1]), to_f32(Q[r + 2]), to_f32(Q[r + 3]));
+      gv = *reinterpret_cast<const float4*>(dout + r);
+    }
+  };
+  float4 qv, gv;
+  int qidv;
+  fetch(0, qv, gv, qidv);
+  float kb[NTW][16], vb[NTW][16];
+  bool valid[NTW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < NTW; ++i) {
     const int col = 16 * (w + 4 * i) + j;
 #pragma unroll
     for (int c = 0; c < 16; ++c) kb[i][c] = vb[i][c] = 0.f;
@@ -356,34 +375,24 @@ __global__ __launch_bounds__(256, 2) void tile_kernel(
             make_float4(kb[i][4 * q], kb[i][4 * q + 1], kb[i][4 * q + 2], kb[i][4 * q + 3]);
     }
   }
-  f32x4 adk[2][4], adv[2][4];
+  f32x4 adk[NTW][4], adv[NTW][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NTW; ++i)
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) adk[i][c4] = adv[i][c4] = zero4();
-  const int32_t* ph = perm + (size_t)bh * N + q0;
 
   for (int t0 = 0; t0 < cnt; t0 += 16) {
     const int nq = min(16, cnt - t0);
     __syncthreads();  // the previous tile's LDS is spent
-    if (tid < 16) qid[tid] = tid < nq ? ph[t0 + tid] : -1;
-    {
-      // rows: thread -> (query tid / 16, channels 4 (tid % 16) ..)
-      const int qi = tid >> 4, c0 = 4 * (tid & 15);
-      float4 qv = make_float4(0.f, 0.f, 0.f, 0.f), gv = qv;
-      if (qi < nq) {
-        const size_t r = ((size_t)bh * N + ph[t0 + qi]) * kHeadDim + c0;
-        qv = make_float4(to_f32(Q[r]), to_f32(Q[r + 1]), to_f32(Q[r + 2]), to_f32(Q[r + 3]));
-        gv = *reinterpret_cast<const float4*>(dout + r);
-      }
-      *reinterpret_cast<float4*>(&qt[qi][c0]) = qv;
-      *reinterpret_cast<float4*>(&gt[qi][c0]) = gv;
-    }
+    *reinterpret_cast<float4*>(&qt[rq][rc0]) = qv;
+    *reinterpret_cast<float4*>(&gt[rq][rc0]) = gv;
+    if ((tid & 15) == 0) qid[rq] = qidv;
+    if (t0 + 16 < cnt) fetch(t0 + 16, qv, gv, qidv);
     __syncthreads();
     // S and dW: lane (g, j) holds [query 4g + r][entry 16 (w + 4i) + j]
-    f32x4 sa[2], sw[2];
+    f32x4 sa[NTW], sw[NTW];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) sa[i] = sw[i] = zero4();
+    for (int i = 0; i < NTW; ++i) sa[i] = sw[i] = zero4();
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float4 a4 = *reinterpret_cast<const float4*>(&qt[j][16 * g + 4 * q]);
@@ -392,17 +401,17 @@ __global__ __launch_bounds__(256, 2) void tile_kernel(
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < NTW; ++i)
           if (i < nt) {
             sa[i] = mfma_f32(av[u], kb[i][4 * q + u], sa[i]);
             sw[i] = mfma_f32(dv[u], vb[i][4 * q + u], sw[i]);
           }
     }
     // logits (base 2; -inf for padding entries) and the row maxima
-    float x[2][4];
+    float x[NTW][4];
     float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NTW; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         x[i][r] = i < nt && valid[i] ? sa[i][r] * kl2 : -INFINITY;
@@ -421,9 +430,9 @@ __global__ __launch_bounds__(256, 2) void tile_kernel(
       mx[r] = fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w));
       ps[r] = pd[r] = 0.f;
     }
-    float p[2][4];
+    float p[NTW][4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NTW; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         p[i][r] = __builtin_amdgcn_exp2f(x[i][r] - mx[r]);  // 0 at -inf
@@ -441,7 +450,7 @@ __global__ __launch_bounds__(256, 2) void tile_kernel(
     }
     __syncthreads();
     // w = p / L, dz = tau w (dw - D), D = sum p dw / L
-    float wt[2][4], dz[2][4];
+    float wt[NTW][4], dz[NTW][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float4 l4 = *reinterpret_cast<const float4*>(&red[1][4 * g + r][0]);
@@ -449,7 +458,7 @@ __global__ __launch_bounds__(256, 2) void tile_kernel(
       const float inv = 1.0f / ((l4.x + l4.y) + (l4.z + l4.w));
       const float D = ((d4.x + d4.y) + (d4.z + d4.w)) * inv;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < NTW; ++i) {
         wt[i][r] = p[i][r] * inv;
         dz[i][r] = tau * wt[i][r] * (sw[i][r] - D);
       }
@@ -462,14 +471,14 @@ __global__ __launch_bounds__(256, 2) void tile_kernel(
       for (int c4 = 0; c4 < 4; ++c4) {
         const float bq = qt[4 * g + r][16 * c4 + j], bg = gt[4 * g + r][16 * c4 + j];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < NTW; ++i)
           if (i < nt) {
             adk[i][c4] = mfma_f32(dz[i][r], bq, adk[i][c4]);
             adv[i][c4] = mfma_f32(wt[i][r], bg, adv[i][c4]);
           }
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < NTW; ++i)
         if (i < nt) zt[w][16 * i + j][4 * g + r] = dz[i][r];
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -480,7 +489,7 @@ __global__ __launch_bounds__(256, 2) void tile_kernel(
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) aq[c4] = zero4();
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NTW; ++i)
       if (i < nt) {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -513,7 +522,7 @@ __global__ __launch_bounds__(256, 2) void tile_kernel(
   }
   // the entries' rows: lane (g, j) holds [entry 16 (w + 4i) + 4g + r][channel 16 c4 + j]
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < NTW; ++i) {
     if (i >= nt) continue;
     const int base = 16 * (w + 4 * i);
     const bool sh = base < msp;
@@ -614,7 +623,7 @@ __global__ __launch_bounds__(256) void stats_kernel(const float* __restrict__ ql
                                                     const float* __restrict__ dvl,
                                                     const float* __restrict__ vl,
                                                     float4* __restrict__ stats, int N, int m,
-                                                    float tau) {
+                                                    float tau, int with_ml) {
   __shared__ float kb[64][kHeadDim + 1];
   __shared__ float qr[16][kHeadDim];
   const int i0 = blockIdx.x * 16, bh = blockIdx.y, tid = threadIdx.x;
@@ -624,7 +633,7 @@ __global__ __launch_bounds__(256) void stats_kernel(const float* __restrict__ ql
     qr[i][c] = i0 + i < m ? ql[((size_t)bh * m + i0 + i) * kHeadDim + c] : 0.f;
   }
   float M = -INFINITY, L = 0.f;
-  for (int b0 = 0; b0 < N; b0 += 64) {
+  for (int b0 = 0; b0 < (with_ml ? N : 0); b0 += 64) {
     __syncthreads();
     for (int it = tid; it < 64 * kHeadDim; it += 256) {
       const int j = it >> 6, c = it & 63;
@@ -662,8 +671,10 @@ __global__ __launch_bounds__(256) void stats_kernel(const float* __restrict__ ql
   for (int o = 1; o < 16; o <<= 1) z += __shfl_xor(z, o, 64);
   if (lk == 0 && i0 + li < m) {
     float4* st = stats + (size_t)bh * m + i0 + li;
-    st->x = M;
-    st->y = L;
+    if (with_ml) {
+      st->x = M;
+      st->y = L;
+    }
     if (dvl) st->z = z;
   }
 }
@@ -764,6 +775,198 @@ __global__ __launch_bounds__(256) void landmark_kernel(
   }
 }
 
+// ---------------------------------------------------------------- landmark (MFMA)
+// m <= 64, on fp32 MFMA 16x16x4.  Workgroup (run of LMK_BLOCKS 64-key blocks,
+// head): the landmark rows' Q_L, dV_L, statistics and dV_L . V_L are staged
+// once; then per 64-key block wave w owns keys 16 w .. 16 w + 15 (their K and
+// V rows in registers as B operands: lane (g, j) holds key j, channels 16 g ..
+// 16 g + 15; the next block's rows are requested while this one is computed).
+// Per 16-row tile of landmarks:
+//   S = Q_L K_w^T and dA = dV_L V_w^T (Q_L and dV_L rows from LDS as A);
+//   A = exp(tau S - M) / L and dS = A (dA - dV_L . V_L), with the rows'
+//     statistics (zero past m and at keys past N);
+//   dV_w += A^T dV_L and dK_w += dS^T Q_L (the accumulators as A operands as
+//     they stand: k-step r pairs lane group g with row 4 g + r);
+//   dQ_L += dS K_w (dS transposed through LDS), held in registers over the
+//     blocks.
+// The blocks' dK, dV rows belong to this workgroup and are added in place;
+// dQ_L, the four waves' shares summed in LDS, goes out with one float atomic
+// per element per workgroup (tau applied to dK and dQ_L on the way out).
+constexpr int LMK_BLOCKS = 4;
+
+template <typename T>
+__global__ __launch_bounds__(256, 2) void landmark_mfma_kernel(
+    const float* __restrict__ ql, const T* __restrict__ K, const T* __restrict__ V,
+    const float* __restrict__ dvl, const float* __restrict__ vl, const float4* __restrict__ stats,
+    float* __restrict__ dql, float* __restrict__ dK, float* __restrict__ dV, int N, int m,
+    float tau) {
+  __shared__ __attribute__((aligned(16))) float qs[64][68];
+  __shared__ __attribute__((aligned(16))) float gs[64][68];
+  __shared__ __attribute__((aligned(16))) float acc_q[64][68];
+  __shared__ __attribute__((aligned(16))) float kt[4][16][KE_STRIDE];
+  __shared__ float zt[4][16][ZT_STRIDE];
+  __shared__ float rst[3][64];  // M, 1 / L, dV_L . V_L per row
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
+  const int mt = (m + 15) >> 4;
+  const int blk0 = blockIdx.x * LMK_BLOCKS, blk1 = min((N + 63) >> 6, blk0 + LMK_BLOCKS);
+  // this wave's keys of block blk: K and V rows (zero past N)
+  auto load_rows = [&](int blk, float (&kk)[16], float (&vv)[16]) {
+    const int key = 64 * blk + 16 * w + j;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) kk[c] = vv[c] = 0.f;
+    if (key < N) {
+      load16(K + ((size_t)bh * N + key) * kHeadDim, 16 * g, kk);
+      load16(V + ((size_t)bh * N + key) * kHeadDim, 16 * g, vv);
+    }
+  };
+  float kr[16], vr[16], kn[16], vn[16];
+  load_rows(blk0, kr, vr);
+  // this wave's dQ_L share: lane (g, j) -> [row 16 rt + 4g + r][channel 16 c4 + j]
+  f32x4 aq[4][4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) aq[rt][c4] = zero4();
+  // rows (zero past m), the dQ_L sums, the rows' statistics
+  for (int it = tid; it < 64 * 16; it += 256) {
+    const int r = it >> 4, c0 = 4 * (it & 15);
+    float4 q = make_float4(0.f, 0.f, 0.f, 0.f), d = q;
+    if (r < m) {
+      q = *reinterpret_cast<const float4*>(ql + ((size_t)bh * m + r) * kHeadDim + c0);
+      d = *reinterpret_cast<const float4*>(dvl + ((size_t)bh * m + r) * kHeadDim + c0);
+    }
+    *reinterpret_cast<float4*>(&qs[r][c0]) = q;
+    *reinterpret_cast<float4*>(&gs[r][c0]) = d;
+    *reinterpret_cast<float4*>(&acc_q[r][c0]) = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  {
+    // dV_L . V_L: thread (row tid / 4, channels 16 (tid % 4) ..)
+    const int r = tid >> 2, c0 = 16 * (tid & 3);
+    float z = 0.f;
+    if (r < m) {
+      const float4* a = reinterpret_cast<const float4*>(dvl + ((size_t)bh * m + r) * kHeadDim + c0);
+      const float4* b = reinterpret_cast<const float4*>(vl + ((size_t)bh * m + r) * kHeadDim + c0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 x = a[q], y = b[q];
+        z = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, fmaf(x.w, y.w, z))));
+      }
+    }
+    z += __shfl_xor(z, 1, 64);
+    z += __shfl_xor(z, 2, 64);
+    if ((tid & 3) == 0) {
+      const float4 st = r < m ? stats[(size_t)bh * m + r] : make_float4(0.f, 1.f, 0.f, 0.f);
+      rst[0][r] = st.x;
+      rst[1][r] = r < m ? 1.0f / st.y : 0.f;
+      rst[2][r] = z;
+    }
+  }
+  __syncthreads();
+  for (int blk = blk0; blk < blk1; ++blk) {
+    if (blk + 1 < blk1) load_rows(blk + 1, kn, vn);
+    const bool kok = 64 * blk + 16 * w + j < N;
+    // the wave's key rows for dQ_L's B operand (its own LDS slot: the previous
+    // block's reads are done)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<float4*>(&kt[w][j][16 * g + 4 * q]) =
+          make_float4(kr[4 * q], kr[4 * q + 1], kr[4 * q + 2], kr[4 * q + 3]);
+    f32x4 adk[4], adv[4];
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) adk[c4] = adv[c4] = zero4();
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      if (rt >= mt) break;
+      // S and dA: lane (g, j) holds [row 16 rt + 4g + r][key j of the wave]
+      f32x4 sa = zero4(), sd = zero4();
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 a4 = *reinterpret_cast<const float4*>(&qs[16 * rt + j][16 * g + 4 * q]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&gs[16 * rt + j][16 * g + 4 * q]);
+        sa = mfma_f32(a4.x, kr[4 * q], sa);
+        sd = mfma_f32(d4.x, vr[4 * q], sd);
+        sa = mfma_f32(a4.y, kr[4 * q + 1], sa);
+        sd = mfma_f32(d4.y, vr[4 * q + 1], sd);
+        sa = mfma_f32(a4.z, kr[4 * q + 2], sa);
+        sd = mfma_f32(d4.z, vr[4 * q + 2], sd);
+        sa = mfma_f32(a4.w, kr[4 * q + 3], sa);
+        sd = mfma_f32(d4.w, vr[4 * q + 3], sd);
+      }
+      float aw[4], ds[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * rt + 4 * g + r;
+        const float a = kok ? fast_exp(tau * sa[r] - rst[0][row]) * rst[1][row] : 0.f;
+        aw[r] = a;
+        ds[r] = a * (sd[r] - rst[2][row]);
+        zt[w][j][4 * g + r] = ds[r];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          adv[c4] = mfma_f32(aw[r], gs[16 * rt + 4 * g + r][16 * c4 + j], adv[c4]);
+          adk[c4] = mfma_f32(ds[r], qs[16 * rt + 4 * g + r][16 * c4 + j], adk[c4]);
+        }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const float a = zt[w][4 * ks + g][j];
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4)
+          aq[rt][c4] = mfma_f32(a, kt[w][4 * ks + g][16 * c4 + j], aq[rt][c4]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    // the wave's dK, dV rows: lane (g, j) holds [key 16 w + 4g + r][channel 16 c4 + j]
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int kk = 64 * blk + 16 * w + 4 * g + r;
+      if (kk < N) {
+        float* dk = dK + ((size_t)bh * N + kk) * kHeadDim;
+        float* dv = dV + ((size_t)bh * N + kk) * kHeadDim;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          dk[16 * c4 + j] += tau * adk[c4][r];
+          dv[16 * c4 + j] += adv[c4][r];
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      kr[c] = kn[c];
+      vr[c] = vn[c];
+    }
+  }
+  // the waves' dQ_L shares summed in LDS, then one atomic per element
+#pragma unroll
+  for (int ww = 0; ww < 4; ++ww) {
+    if (w == ww) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        if (rt >= mt) break;
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc_q[16 * rt + 4 * g + r][16 * c4 + j] += aq[rt][c4][r];
+      }
+    }
+    __syncthreads();
+  }
+  for (int it = tid; it < m * kHeadDim; it += 256) {
+    const int r = it >> 6, c = it & 63;
+    unsafeAtomicAdd(dql + ((size_t)bh * m + r) * kHeadDim + c, tau * acc_q[r][c]);
+  }
+}
+
 // ---------------------------------------------------------------- pool
 // dQ[t] += sum over the windows i holding token t of dQ_L[i] / |window i|;
 // along an axis of g cells pooled to mg windows, cell y lies in windows
@@ -829,10 +1032,17 @@ static bool bwd_tiled(const Shape& s) {
   return s.s == 1 && ((ms + 15) & ~15) + ((s.k + 15) & ~15) <= bwd::TILE_EP;
 }
 
+// Scratch: the landmark rows' statistics, dQ_L, dV_L, and (outside the tile
+// kernel's case) the per-entry (w, dz) buffer.
 size_t backward_scratch_bytes(const Shape& s) {
   const size_t E = (size_t)(s.shared ? s.m : 0) + (size_t)s.s * s.k;
-  return align_up((size_t)s.BH * s.N * E * 8, 256) + 2 * align_up((size_t)s.BH * s.m * 64 * 4, 256) +
-         align_up((size_t)s.BH * s.m * 16, 256);
+  return align_up((size_t)s.BH * s.m * 16, 256) + 2 * align_up((size_t)s.BH * s.m * 64 * 4, 256) +
+         (bwd_tiled(s) ? 0 : align_up((size_t)s.BH * s.N * E * 8, 256));
+}
+
+float4* backward_stats(void* scratch, const Shape& s) {
+  (void)s;
+  return (float4*)scratch;
 }
 
 template <typename T>
@@ -840,18 +1050,18 @@ static hipError_t run_backward(const T* Q, const T* K, const T* V, const float* 
                                const float* ql, const float* vl, const int32_t* idx,
                                const int32_t* route, const int32_t* offsets,
                                const int32_t* perm, float* dq, float* dk, float* dv,
-                               void* scratch, const Shape& s, hipStream_t st) {
+                               void* scratch, const Shape& s, hipStream_t st, bool stats_ready) {
   const int ms = s.shared ? s.m : 0;
   const int E = ms + s.s * s.k;
   const float tau = 1.0f / sqrtf((float)s.d);
   char* p = (char*)scratch;
-  float2* G = (float2*)p;
-  p += align_up((size_t)s.BH * s.N * E * 8, 256);
+  float4* stats = backward_stats(scratch, s);
+  p += align_up((size_t)s.BH * s.m * 16, 256);
   float* dql = (float*)p;
   p += align_up((size_t)s.BH * s.m * 64 * 4, 256);
   float* dvl = (float*)p;
   p += align_up((size_t)s.BH * s.m * 64 * 4, 256);
-  float4* stats = (float4*)p;
+  float2* G = (float2*)p;  // (outside the tile kernel's case)
   const long long nel = (long long)s.BH * s.N * 64;
   const unsigned zb = (unsigned)((nel + 255) / 256);
   bwd::zero_kernel<<<zb, 256, 0, st>>>(dk, nel);
@@ -866,9 +1076,9 @@ static hipError_t run_backward(const T* Q, const T* K, const T* V, const float* 
       bwd::zero_kernel<<<(unsigned)((nl + 255) / 256), 256, 0, st>>>(dql, nl);
       bwd::zero_kernel<<<(unsigned)((nl + 255) / 256), 256, 0, st>>>(dvl, nl);
     }
-    bwd::tile_kernel<T><<<dim3(s.m, s.BH), 256, 0, st>>>(Q, K, V, ql, vl, idx, offsets, perm, dout,
-                                                         dq, dk, dv, dql, dvl, s.N, s.m, s.k, ms,
-                                                         msp, ep, tau);
+    auto tile = ep <= 64 ? bwd::tile_kernel<T, 1> : bwd::tile_kernel<T, 2>;
+    tile<<<dim3(s.m, s.BH), 256, 0, st>>>(Q, K, V, ql, vl, idx, offsets, perm, dout, dq, dk, dv,
+                                          dql, dvl, s.N, s.m, s.k, ms, msp, ep, tau);
   } else {
     bwd::query_kernel<T><<<dim3((s.N + 3) / 4, s.BH), 256, 0, st>>>(
         Q, K, V, ql, vl, idx, route, perm, dout, dq, G, s.N, s.m, s.k, s.s, s.shared ? 1 : 0, tau);
@@ -878,10 +1088,20 @@ static hipError_t run_backward(const T* Q, const T* K, const T* V, const float* 
       bwd::shared_kernel<T><<<rows, 256, 0, st>>>(Q, dout, G, vl, dql, dvl, stats, s.N, s.m, E);
   }
   if (s.shared) {
-    bwd::stats_kernel<T><<<rows, 256, 0, st>>>(ql, K, bwd_tiled(s) ? dvl : nullptr, vl, stats,
-                                               s.N, s.m, tau);
-    bwd::landmark_kernel<T><<<dim3((s.N + 63) / 64, s.BH), 256, 0, st>>>(
-        ql, K, V, dvl, stats, dql, dk, dv, s.N, s.m, tau);
+    if (s.m <= 64) {
+      // statistics from the forward pass, or recomputed here; dV_L . V_L
+      // inside the landmark kernel
+      if (!stats_ready)
+        bwd::stats_kernel<T><<<rows, 256, 0, st>>>(ql, K, nullptr, vl, stats, s.N, s.m, tau, 1);
+      const int runs = ((s.N + 63) / 64 + bwd::LMK_BLOCKS - 1) / bwd::LMK_BLOCKS;
+      bwd::landmark_mfma_kernel<T><<<dim3(runs, s.BH), 256, 0, st>>>(
+          ql, K, V, dvl, vl, stats, dql, dk, dv, s.N, s.m, tau);
+    } else {
+      bwd::stats_kernel<T><<<rows, 256, 0, st>>>(ql, K, bwd_tiled(s) ? dvl : nullptr, vl, stats,
+                                                 s.N, s.m, tau, stats_ready ? 0 : 1);
+      bwd::landmark_kernel<T><<<dim3((s.N + 63) / 64, s.BH), 256, 0, st>>>(
+          ql, K, V, dvl, stats, dql, dk, dv, s.N, s.m, tau);
+    }
     bwd::pool_kernel<<<dim3((unsigned)(((long long)s.N * 4 + 255) / 256), s.BH), 256, 0, st>>>(
         dql, dq, s.grid_h, s.grid_w, s.m_h, s.m_w);
   }
@@ -892,12 +1112,12 @@ hipError_t launch_backward(const void* Q, const void* K, const void* V, const fl
                            const float* ql, const float* vl, const int32_t* idx,
                            const int32_t* route, const int32_t* offsets, const int32_t* perm,
                            float* dq, float* dk, float* dv, void* scratch, const Shape& s,
-                           hipStream_t st) {
+                           hipStream_t st, bool stats_ready) {
   if (s.bf16)
     return run_backward<bf16_t>((const bf16_t*)Q, (const bf16_t*)K, (const bf16_t*)V, dout, ql, vl,
-                                idx, route, offsets, perm, dq, dk, dv, scratch, s, st);
+                                idx, route, offsets, perm, dq, dk, dv, scratch, s, st, stats_ready);
   return run_backward<float>((const float*)Q, (const float*)K, (const float*)V, dout, ql, vl, idx,
-                             route, offsets, perm, dq, dk, dv, scratch, s, st);
+                             route, offsets, perm, dq, dk, dv, scratch, s, st, stats_ready);
 }
 
 }  // namespace mita

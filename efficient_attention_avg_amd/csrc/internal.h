@@ -51,8 +51,11 @@ bool landmark_bf16_supported(const Shape& s);
 // keys split over several workgroups need this much scratch (per-chunk
 // candidates and V_L partials) for the merge kernel; 0 for one chunk
 size_t landmark_bf16_scratch_bytes(const Shape& s);
+// stats (optional, [BH][m]): each landmark row's softmax maximum (x, tau
+// units) and sum (y) over all keys
 hipError_t launch_landmark_bf16(const float* ql, const void* K, const void* V, int32_t* idx,
-                                float* vl, void* scratch, const Shape& s, hipStream_t st);
+                                float* vl, void* scratch, const Shape& s, hipStream_t st,
+                                float4* stats = nullptr);
 bool route_bf16_supported(const Shape& s);
 size_t route_chist_bytes(const Shape& s);
 hipError_t launch_route_bf16(const void* Q, const float* ql, int32_t* route, int32_t* chist,
@@ -71,11 +74,14 @@ hipError_t launch_merge(const void* partial, float* out, const Shape& s, hipStre
 
 // gradients of the pass (dQ, dK, dV) given the forward's intermediates
 size_t backward_scratch_bytes(const Shape& s);
+// where the backward scratch keeps the landmark rows' softmax statistics: the
+// forward landmark pass may fill them (stats_ready), sparing a recomputation
+float4* backward_stats(void* scratch, const Shape& s);
 hipError_t launch_backward(const void* Q, const void* K, const void* V, const float* dout,
                            const float* ql, const float* vl, const int32_t* idx,
                            const int32_t* route, const int32_t* offsets, const int32_t* perm,
                            float* dq, float* dk, float* dv, void* scratch, const Shape& s,
-                           hipStream_t st);
+                           hipStream_t st, bool stats_ready = false);
 
 // whole pass for short grids in one persistent kernel
 bool fused_supported(const Shape& s);

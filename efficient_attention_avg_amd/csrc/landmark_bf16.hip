@@ -98,6 +98,10 @@ struct Args {
   float* cand_s;   // [BH][m][nch][k] scores of each chunk's top-k
   int32_t* cand_k; // [BH][m][nch][k] their key ids, ascending within a chunk
   float* vlpart;   // [BH][m][nch][PART_STRIDE]: 64 sums, reference max, sum
+  // optional [BH][m]: each row's softmax statistics over all N keys, x = the
+  // reference maximum tau * c_max and y = the sum of exp(tau c - x) (the
+  // backward pass reuses them)
+  float4* stats;
 };
 
 constexpr int PART_STRIDE = 68;
@@ -748,6 +752,11 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
       }
       if (row0 + r < a.m) {
         if (a.nch == 1) {
+          if (a.stats && c4 == 0) {
+            float4* st = a.stats + (size_t)bh * a.m + row0 + r;
+            st->x = M * 0.125f;
+            st->y = L;
+          }
           const float inv = 1.0f / L;
           *reinterpret_cast<float4*>(a.vl + ((size_t)bh * a.m + row0 + r) * 64 + c4) =
               make_float4(o.x * inv, o.y * inv, o.z * inv, o.w * inv);
@@ -1053,6 +1062,10 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void merge_kernel(Args a) {
       L = fmaf(f, pp[c * PART_STRIDE + 65], L);
     }
     a.vl[row * 64 + lane] = o / L;
+    if (a.stats && lane == 0) {
+      a.stats[row].x = M * 0.125f;
+      a.stats[row].y = L;
+    }
   }
   // ---- top-k
   const int last_keys = a.N - (nch - 1) * a.cblk * KB;
@@ -1194,7 +1207,8 @@ size_t landmark_bf16_scratch_bytes(const Shape& s) {
 }
 
 hipError_t launch_landmark_bf16(const float* ql, const void* K, const void* V, int32_t* idx,
-                                float* vl, void* scratch, const Shape& s, hipStream_t st) {
+                                float* vl, void* scratch, const Shape& s, hipStream_t st,
+                                float4* stats) {
   int nch, cblk;
   landmark_chunks(s, nch, cblk);
   const size_t rows = (size_t)s.BH * s.m * nch;
@@ -1211,7 +1225,7 @@ hipError_t launch_landmark_bf16(const float* ql, const void* K, const void* V, i
   const int fuse_h = s.k <= 128 ? 1 : 0;
   lmk::Args a{ql, (const uint16_t*)K, (const uint16_t*)V, idx, vl, s.BH, s.N, s.m, s.k,
               landmark_cap(s), (s.m + lmk::ROWS - 1) / lmk::ROWS, nch, cblk, fuse_h, cand_s,
-              cand_k, vlpart};
+              cand_k, vlpart, stats};
   if (a.cap == 0) return hipErrorInvalidValue;
   const size_t lds = lmk::lds_bytes(a.cap);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
