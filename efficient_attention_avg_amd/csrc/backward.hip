@@ -41,6 +41,8 @@
 #include "mfma.h"
 #include "select.h"
 
+#include <type_traits>
+
 namespace mita {
 namespace bwd {
 
@@ -311,7 +313,16 @@ __global__ __launch_bounds__(256, NTW == 1 ? 3 : 2) void tile_kernel(
     const float* __restrict__ dout, float* __restrict__ dq, float* __restrict__ dK,
     float* __restrict__ dV, float* __restrict__ dql, float* __restrict__ dvl, int N, int m, int k,
     int ms, int msp, int ep, float tau) {
+  // bf16 inputs with two column tiles per wave: S and dW on bf16 MFMA
+  // 16x16x32 (Q, K and V are exact in bf16; dOut and the shared entries' Q_L,
+  // V_L split into bf16 hi + lo).  Otherwise all on fp32 MFMA (measured: the
+  // one-tile form, bound by its loads' latency, ran 10% slower with the
+  // splits, the two-tile form 30% faster).
+  constexpr bool BF = std::is_same<T, bf16_t>::value && NTW == 2;
   __shared__ __attribute__((aligned(16))) float qt[16][68];
+  __shared__ __attribute__((aligned(16))) uint16_t qtb[16][72];
+  __shared__ __attribute__((aligned(16))) uint16_t gth[16][72];
+  __shared__ __attribute__((aligned(16))) uint16_t gtl[16][72];
   __shared__ __attribute__((aligned(16))) float gt[16][68];
   __shared__ __attribute__((aligned(16))) float ke[4][16 * NTW][KE_STRIDE];
   __shared__ float zt[4][16 * NTW][ZT_STRIDE];
@@ -331,48 +342,127 @@ __global__ __launch_bounds__(256, NTW == 1 ? 3 : 2) void tile_kernel(
   // a tile's rows: thread -> (query rq, channels rc0 ..); the next tile's are
   // requested while the current one is computed
   const int rq = tid >> 4, rc0 = 4 * (tid & 15);
+  // (bf16: qv.x, qv.y carry the four raw bf16 values)
   auto fetch = [&](int t0, float4& qv, float4& gv, int& id) {
     qv = gv = make_float4(0.f, 0.f, 0.f, 0.f);
     id = -1;
     if (t0 + rq < cnt) {
       id = ph[t0 + rq];
       const size_t r = ((size_t)bh * N + id) * kHeadDim + rc0;
-      qv = make_float4(to_f32(Q[r]), to_f32(Q[r + 1]), to_f32(Q[r + 2]), to_f32(Q[r + 3]));
+      if constexpr (BF) {
+        const u32x2 b = *reinterpret_cast<const u32x2*>(Q + r);
+        qv.x = __uint_as_float(b[0]);
+        qv.y = __uint_as_float(b[1]);
+      } else {
+        qv = make_float4(to_f32(Q[r]), to_f32(Q[r + 1]), to_f32(Q[r + 2]), to_f32(Q[r + 3]));
+      }
       gv = *reinterpret_cast<const float4*>(dout + r);
     }
   };
   float4 qv, gv;
   int qidv;
   fetch(0, qv, gv, qidv);
-  float kb[NTW][16], vb[NTW][16];
-  bool valid[NTW];
+  // the wave's entry rows as B operands.  fp32: kb/vb hold channels 16 g ..
+  // 16 g + 15 (one per 16x16x4 k-step); bf16: kh/vh (hi, or the exact bf16
+  // row) and kl/vlo (lo; zero for routed entries) hold channels 32 ks + 8 g
+  // .. + 7 for k-steps ks = 0, 1 of 16x16x32
+  float kb[BF ? 1 : NTW][16], vb[BF ? 1 : NTW][16];
+  u32x4 kh[NTW][2], kl[NTW][2], vh[NTW][2], vlo[NTW][2];
+  bool valid[NTW], sht[NTW];
 #pragma unroll
   for (int i = 0; i < NTW; ++i) {
     const int col = 16 * (w + 4 * i) + j;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) kb[i][c] = vb[i][c] = 0.f;
+    sht[i] = 16 * (w + 4 * i) < msp;
     valid[i] = false;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) kh[i][ks] = kl[i][ks] = vh[i][ks] = vlo[i][ks] = u32x4{0u, 0u, 0u, 0u};
+    if constexpr (!BF) {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) kb[i][c] = vb[i][c] = 0.f;
+    }
     if (i < nt) {
-      if (16 * (w + 4 * i) < msp) {
+      const float* srow_k = nullptr;
+      const float* srow_v = nullptr;
+      const T* rrow_k = nullptr;
+      const T* rrow_v = nullptr;
+      if (sht[i]) {
         valid[i] = col < ms;
-        if (valid[i]) {
-          load16(ql + ((size_t)bh * m + col) * kHeadDim, 16 * g, kb[i]);
-          load16(vl + ((size_t)bh * m + col) * kHeadDim, 16 * g, vb[i]);
-        }
+        srow_k = ql + ((size_t)bh * m + col) * kHeadDim;
+        srow_v = vl + ((size_t)bh * m + col) * kHeadDim;
       } else {
         const int slot = col - msp;
         valid[i] = slot < k;
         if (valid[i]) {
           const size_t r = ((size_t)bh * N + idxe[slot]) * kHeadDim;
-          load16(K + r, 16 * g, kb[i]);
-          load16(V + r, 16 * g, vb[i]);
+          rrow_k = K + r;
+          rrow_v = V + r;
         }
       }
-      // the key rows again for dq's B operand
+      float kf[16];  // the key row's channels for dq's B operand (ke)
+      if constexpr (BF) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<float4*>(&ke[w][16 * i + j][16 * g + 4 * q]) =
-            make_float4(kb[i][4 * q], kb[i][4 * q + 1], kb[i][4 * q + 2], kb[i][4 * q + 3]);
+        for (int ks = 0; ks < 2; ++ks) {
+          const int c0 = 32 * ks + 8 * g;
+          if (valid[i] && sht[i]) {
+            float a[8], b[8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const float4 fa = *reinterpret_cast<const float4*>(srow_k + c0 + 4 * h);
+              const float4 fb = *reinterpret_cast<const float4*>(srow_v + c0 + 4 * h);
+              a[4 * h] = fa.x; a[4 * h + 1] = fa.y; a[4 * h + 2] = fa.z; a[4 * h + 3] = fa.w;
+              b[4 * h] = fb.x; b[4 * h + 1] = fb.y; b[4 * h + 2] = fb.z; b[4 * h + 3] = fb.w;
+            }
+            uint32_t hk[8], lk[8], hv[8], lv[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              hk[t] = bf16_rne_bits(a[t]);
+              lk[t] = bf16_rne_bits(a[t] - bf16_bits_to_f32(hk[t]));
+              hv[t] = bf16_rne_bits(b[t]);
+              lv[t] = bf16_rne_bits(b[t] - bf16_bits_to_f32(hv[t]));
+              kf[8 * ks + t] = a[t];
+            }
+            kh[i][ks] = u32x4{pack2(hk[0], hk[1]), pack2(hk[2], hk[3]), pack2(hk[4], hk[5]), pack2(hk[6], hk[7])};
+            kl[i][ks] = u32x4{pack2(lk[0], lk[1]), pack2(lk[2], lk[3]), pack2(lk[4], lk[5]), pack2(lk[6], lk[7])};
+            vh[i][ks] = u32x4{pack2(hv[0], hv[1]), pack2(hv[2], hv[3]), pack2(hv[4], hv[5]), pack2(hv[6], hv[7])};
+            vlo[i][ks] = u32x4{pack2(lv[0], lv[1]), pack2(lv[2], lv[3]), pack2(lv[4], lv[5]), pack2(lv[6], lv[7])};
+          } else if (valid[i]) {
+            kh[i][ks] = *reinterpret_cast<const u32x4*>(rrow_k + c0);
+            vh[i][ks] = *reinterpret_cast<const u32x4*>(rrow_v + c0);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              kf[8 * ks + 2 * t] = __uint_as_float(kh[i][ks][t] << 16);
+              kf[8 * ks + 2 * t + 1] = __uint_as_float(kh[i][ks][t] & 0xFFFF0000u);
+            }
+          } else {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) kf[8 * ks + t] = 0.f;
+          }
+        }
+        // ke row: channels 8 g .. (from k-step 0) and 32 + 8 g .. (k-step 1)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            *reinterpret_cast<float4*>(&ke[w][16 * i + j][32 * ks + 8 * g + 4 * h]) =
+                make_float4(kf[8 * ks + 4 * h], kf[8 * ks + 4 * h + 1], kf[8 * ks + 4 * h + 2],
+                            kf[8 * ks + 4 * h + 3]);
+      } else {
+        if (valid[i]) {
+          if (sht[i]) {
+            load16(srow_k, 16 * g, kb[i]);
+            load16(srow_v, 16 * g, vb[i]);
+          } else {
+            load16(rrow_k, 16 * g, kb[i]);
+            load16(rrow_v, 16 * g, vb[i]);
+          }
+        }
+        (void)kf;
+        // the key rows again for dq's B operand
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<float4*>(&ke[w][16 * i + j][16 * g + 4 * q]) =
+              make_float4(kb[i][4 * q], kb[i][4 * q + 1], kb[i][4 * q + 2], kb[i][4 * q + 3]);
+      }
     }
   }
   f32x4 adk[NTW][4], adv[NTW][4];
@@ -384,7 +474,20 @@ __global__ __launch_bounds__(256, NTW == 1 ? 3 : 2) void tile_kernel(
   for (int t0 = 0; t0 < cnt; t0 += 16) {
     const int nq = min(16, cnt - t0);
     __syncthreads();  // the previous tile's LDS is spent
-    *reinterpret_cast<float4*>(&qt[rq][rc0]) = qv;
+    if constexpr (BF) {
+      *reinterpret_cast<u32x2*>(&qtb[rq][rc0]) = u32x2{__float_as_uint(qv.x), __float_as_uint(qv.y)};
+      const float gf[4] = {gv.x, gv.y, gv.z, gv.w};
+      uint32_t hh[4], ll[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        hh[t] = bf16_rne_bits(gf[t]);
+        ll[t] = bf16_rne_bits(gf[t] - bf16_bits_to_f32(hh[t]));
+      }
+      *reinterpret_cast<u32x2*>(&gth[rq][rc0]) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
+      *reinterpret_cast<u32x2*>(&gtl[rq][rc0]) = u32x2{pack2(ll[0], ll[1]), pack2(ll[2], ll[3])};
+    } else {
+      *reinterpret_cast<float4*>(&qt[rq][rc0]) = qv;
+    }
     *reinterpret_cast<float4*>(&gt[rq][rc0]) = gv;
     if ((tid & 15) == 0) qid[rq] = qidv;
     if (t0 + 16 < cnt) fetch(t0 + 16, qv, gv, qidv);
@@ -393,19 +496,39 @@ __global__ __launch_bounds__(256, NTW == 1 ? 3 : 2) void tile_kernel(
     f32x4 sa[NTW], sw[NTW];
 #pragma unroll
     for (int i = 0; i < NTW; ++i) sa[i] = sw[i] = zero4();
+    if constexpr (BF) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 a4 = *reinterpret_cast<const float4*>(&qt[j][16 * g + 4 * q]);
-      const float4 d4 = *reinterpret_cast<const float4*>(&gt[j][16 * g + 4 * q]);
-      const float av[4] = {a4.x, a4.y, a4.z, a4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int ks = 0; ks < 2; ++ks) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&qtb[j][32 * ks + 8 * g]);
+        const u32x4 ah = *reinterpret_cast<const u32x4*>(&gth[j][32 * ks + 8 * g]);
+        const u32x4 al = *reinterpret_cast<const u32x4*>(&gtl[j][32 * ks + 8 * g]);
 #pragma unroll
         for (int i = 0; i < NTW; ++i)
           if (i < nt) {
-            sa[i] = mfma_f32(av[u], kb[i][4 * q + u], sa[i]);
-            sw[i] = mfma_f32(dv[u], vb[i][4 * q + u], sw[i]);
+            sa[i] = mfma_bf16(a, kh[i][ks], sa[i]);
+            sw[i] = mfma_bf16(ah, vh[i][ks], sw[i]);
+            sw[i] = mfma_bf16(al, vh[i][ks], sw[i]);
+            if (sht[i]) {
+              sa[i] = mfma_bf16(a, kl[i][ks], sa[i]);
+              sw[i] = mfma_bf16(ah, vlo[i][ks], sw[i]);
+            }
           }
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 a4 = *reinterpret_cast<const float4*>(&qt[j][16 * g + 4 * q]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&gt[j][16 * g + 4 * q]);
+        const float av[4] = {a4.x, a4.y, a4.z, a4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < NTW; ++i)
+            if (i < nt) {
+              sa[i] = mfma_f32(av[u], kb[i][4 * q + u], sa[i]);
+              sw[i] = mfma_f32(dv[u], vb[i][4 * q + u], sw[i]);
+            }
+      }
     }
     // logits (base 2; -inf for padding entries) and the row maxima
     float x[NTW][4];
@@ -469,7 +592,12 @@ __global__ __launch_bounds__(256, NTW == 1 ? 3 : 2) void tile_kernel(
     for (int r = 0; r < 4; ++r) {
 #pragma unroll
       for (int c4 = 0; c4 < 4; ++c4) {
-        const float bq = qt[4 * g + r][16 * c4 + j], bg = gt[4 * g + r][16 * c4 + j];
+        float bq;
+        if constexpr (BF)
+          bq = bf16_bits_to_f32(qtb[4 * g + r][16 * c4 + j]);
+        else
+          bq = qt[4 * g + r][16 * c4 + j];
+        const float bg = gt[4 * g + r][16 * c4 + j];
 #pragma unroll
         for (int i = 0; i < NTW; ++i)
           if (i < nt) {
