@@ -41,6 +41,7 @@
 #include "mfma.h"
 #include "select.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace mita {
@@ -304,7 +305,13 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
 }
 
 // NTW: entry column tiles per wave (1 when the entries fit 64 columns: fewer
-// registers and LDS, three workgroups per CU).
+// registers and LDS, three workgroups per CU).  Workgroup (p, head bh) walks
+// the head's experts p, p + P, ..; its tiles run back to back, each tile's
+// successor's query rows (the next tile of the expert, or the next expert's
+// first) requested while it is computed, and with NTW = 1 the next expert's
+// routed rows too.  The shared entries' gradients accumulate over all of the
+// workgroup's experts and go out once at the end; the routed ones go out
+// after each expert.
 template <typename T, int NTW>
 __global__ __launch_bounds__(256, NTW == 1 ? 3 : 2) void tile_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
@@ -312,13 +319,14 @@ __global__ __launch_bounds__(256, NTW == 1 ? 3 : 2) void tile_kernel(
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ perm,
     const float* __restrict__ dout, float* __restrict__ dq, float* __restrict__ dK,
     float* __restrict__ dV, float* __restrict__ dql, float* __restrict__ dvl, int N, int m, int k,
-    int ms, int msp, int ep, float tau) {
+    int ms, int msp, int ep, int P, float tau) {
   // bf16 inputs with two column tiles per wave: S and dW on bf16 MFMA
   // 16x16x32 (Q, K and V are exact in bf16; dOut and the shared entries' Q_L,
   // V_L split into bf16 hi + lo).  Otherwise all on fp32 MFMA (measured: the
   // one-tile form, bound by its loads' latency, ran 10% slower with the
   // splits, the two-tile form 30% faster).
   constexpr bool BF = std::is_same<T, bf16_t>::value && NTW == 2;
+  constexpr bool PF = NTW == 1;  // the next expert's routed rows prefetched
   __shared__ __attribute__((aligned(16))) float qt[16][68];
   __shared__ __attribute__((aligned(16))) uint16_t qtb[16][72];
   __shared__ __attribute__((aligned(16))) uint16_t gth[16][72];
@@ -329,25 +337,33 @@ __global__ __launch_bounds__(256, NTW == 1 ? 3 : 2) void tile_kernel(
   __shared__ __attribute__((aligned(16))) float dqp[4][16][68];
   __shared__ __attribute__((aligned(16))) float red[3][16][4];
   __shared__ int qid[16];
-  const int e = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int p = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6, g = lane >> 4, j = lane & 15;
-  const int q0 = offsets[(size_t)bh * (m + 1) + e], cnt = offsets[(size_t)bh * (m + 1) + e + 1] - q0;
-  if (cnt == 0) return;
   const float kl2 = tau * 1.4426950408889634f;  // logits in the base-2 domain
   const int ntile = ep >> 4;
   // this wave's entry column tiles: w and w + 4 (nt of them)
   const int nt = (w < ntile ? 1 : 0) + (NTW > 1 && w + 4 < ntile ? 1 : 0);
-  const int32_t* idxe = idx + ((size_t)bh * m + e) * k;
-  const int32_t* ph = perm + (size_t)bh * N + q0;
-  // a tile's rows: thread -> (query rq, channels rc0 ..); the next tile's are
-  // requested while the current one is computed
+  const int32_t* offh = offsets + (size_t)bh * (m + 1);
+  const int32_t* permh = perm + (size_t)bh * N;
+  // the first non-empty expert at or after e0 in this workgroup's sequence
+  // (m when none): its query range [q0, q0 + cnt)
+  auto next_expert = [&](int e0, int& q0, int& cnt) {
+    for (int e = e0; e < m; e += P) {
+      q0 = offh[e];
+      cnt = offh[e + 1] - q0;
+      if (cnt > 0) return e;
+    }
+    q0 = cnt = 0;
+    return m;
+  };
+  // a tile's rows: thread -> (query rq, channels rc0 ..)  (bf16: qv.x, qv.y
+  // carry the four raw bf16 values)
   const int rq = tid >> 4, rc0 = 4 * (tid & 15);
-  // (bf16: qv.x, qv.y carry the four raw bf16 values)
-  auto fetch = [&](int t0, float4& qv, float4& gv, int& id) {
+  auto fetch = [&](int q0, int t0, int cnt, float4& qv, float4& gv, int& id) {
     qv = gv = make_float4(0.f, 0.f, 0.f, 0.f);
     id = -1;
     if (t0 + rq < cnt) {
-      id = ph[t0 + rq];
+      id = permh[q0 + t0 + rq];
       const size_t r = ((size_t)bh * N + id) * kHeadDim + rc0;
       if constexpr (BF) {
         const u32x2 b = *reinterpret_cast<const u32x2*>(Q + r);
@@ -359,325 +375,391 @@ __global__ __launch_bounds__(256, NTW == 1 ? 3 : 2) void tile_kernel(
       gv = *reinterpret_cast<const float4*>(dout + r);
     }
   };
-  float4 qv, gv;
-  int qidv;
-  fetch(0, qv, gv, qidv);
-  // the wave's entry rows as B operands.  fp32: kb/vb hold channels 16 g ..
+  // The wave's entry rows as B operands.  fp32: kb/vb hold channels 16 g ..
   // 16 g + 15 (one per 16x16x4 k-step); bf16: kh/vh (hi, or the exact bf16
   // row) and kl/vlo (lo; zero for routed entries) hold channels 32 ks + 8 g
-  // .. + 7 for k-steps ks = 0, 1 of 16x16x32
+  // .. + 7 for k-steps ks = 0, 1 of 16x16x32.  Shared tiles' rows (Q_L, V_L)
+  // are the same for every expert; routed tiles' rows are the expert's keys.
   float kb[BF ? 1 : NTW][16], vb[BF ? 1 : NTW][16];
+  float kn[PF ? NTW : 1][16], vn[PF ? NTW : 1][16];
   u32x4 kh[NTW][2], kl[NTW][2], vh[NTW][2], vlo[NTW][2];
   bool valid[NTW], sht[NTW];
 #pragma unroll
   for (int i = 0; i < NTW; ++i) {
-    const int col = 16 * (w + 4 * i) + j;
     sht[i] = 16 * (w + 4 * i) < msp;
-    valid[i] = false;
+    const int col = 16 * (w + 4 * i) + j;
+    valid[i] = i < nt && (sht[i] ? col < ms : col - msp < k);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) kh[i][ks] = kl[i][ks] = vh[i][ks] = vlo[i][ks] = u32x4{0u, 0u, 0u, 0u};
     if constexpr (!BF) {
 #pragma unroll
       for (int c = 0; c < 16; ++c) kb[i][c] = vb[i][c] = 0.f;
     }
-    if (i < nt) {
-      const float* srow_k = nullptr;
-      const float* srow_v = nullptr;
-      const T* rrow_k = nullptr;
-      const T* rrow_v = nullptr;
-      if (sht[i]) {
-        valid[i] = col < ms;
-        srow_k = ql + ((size_t)bh * m + col) * kHeadDim;
-        srow_v = vl + ((size_t)bh * m + col) * kHeadDim;
-      } else {
-        const int slot = col - msp;
-        valid[i] = slot < k;
-        if (valid[i]) {
-          const size_t r = ((size_t)bh * N + idxe[slot]) * kHeadDim;
-          rrow_k = K + r;
-          rrow_v = V + r;
-        }
-      }
-      float kf[16];  // the key row's channels for dq's B operand (ke)
-      if constexpr (BF) {
+  }
+  // rows of tile i for expert e (shared tiles: e is ignored) into the operand
+  // registers, and their key channels into the wave's LDS copy for dq
+  auto load_entries = [&](int i, int e) {
+    const int col = 16 * (w + 4 * i) + j;
+    const float* srow_k = nullptr;
+    const float* srow_v = nullptr;
+    const T* rrow_k = nullptr;
+    const T* rrow_v = nullptr;
+    if (sht[i]) {
+      srow_k = ql + ((size_t)bh * m + col) * kHeadDim;
+      srow_v = vl + ((size_t)bh * m + col) * kHeadDim;
+    } else if (valid[i]) {
+      const size_t r = ((size_t)bh * N + idx[((size_t)bh * m + e) * k + col - msp]) * kHeadDim;
+      rrow_k = K + r;
+      rrow_v = V + r;
+    }
+    if constexpr (BF) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int c0 = 32 * ks + 8 * g;
-          if (valid[i] && sht[i]) {
-            float a[8], b[8];
+      for (int ks = 0; ks < 2; ++ks) {
+        const int c0 = 32 * ks + 8 * g;
+        if (valid[i] && sht[i]) {
+          float a[8], b[8];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const float4 fa = *reinterpret_cast<const float4*>(srow_k + c0 + 4 * h);
-              const float4 fb = *reinterpret_cast<const float4*>(srow_v + c0 + 4 * h);
-              a[4 * h] = fa.x; a[4 * h + 1] = fa.y; a[4 * h + 2] = fa.z; a[4 * h + 3] = fa.w;
-              b[4 * h] = fb.x; b[4 * h + 1] = fb.y; b[4 * h + 2] = fb.z; b[4 * h + 3] = fb.w;
-            }
-            uint32_t hk[8], lk[8], hv[8], lv[8];
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-              hk[t] = bf16_rne_bits(a[t]);
-              lk[t] = bf16_rne_bits(a[t] - bf16_bits_to_f32(hk[t]));
-              hv[t] = bf16_rne_bits(b[t]);
-              lv[t] = bf16_rne_bits(b[t] - bf16_bits_to_f32(hv[t]));
-              kf[8 * ks + t] = a[t];
-            }
-            kh[i][ks] = u32x4{pack2(hk[0], hk[1]), pack2(hk[2], hk[3]), pack2(hk[4], hk[5]), pack2(hk[6], hk[7])};
-            kl[i][ks] = u32x4{pack2(lk[0], lk[1]), pack2(lk[2], lk[3]), pack2(lk[4], lk[5]), pack2(lk[6], lk[7])};
-            vh[i][ks] = u32x4{pack2(hv[0], hv[1]), pack2(hv[2], hv[3]), pack2(hv[4], hv[5]), pack2(hv[6], hv[7])};
-            vlo[i][ks] = u32x4{pack2(lv[0], lv[1]), pack2(lv[2], lv[3]), pack2(lv[4], lv[5]), pack2(lv[6], lv[7])};
-          } else if (valid[i]) {
-            kh[i][ks] = *reinterpret_cast<const u32x4*>(rrow_k + c0);
-            vh[i][ks] = *reinterpret_cast<const u32x4*>(rrow_v + c0);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              kf[8 * ks + 2 * t] = __uint_as_float(kh[i][ks][t] << 16);
-              kf[8 * ks + 2 * t + 1] = __uint_as_float(kh[i][ks][t] & 0xFFFF0000u);
-            }
-          } else {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) kf[8 * ks + t] = 0.f;
+          for (int h = 0; h < 2; ++h) {
+            const float4 fa = *reinterpret_cast<const float4*>(srow_k + c0 + 4 * h);
+            const float4 fb = *reinterpret_cast<const float4*>(srow_v + c0 + 4 * h);
+            a[4 * h] = fa.x; a[4 * h + 1] = fa.y; a[4 * h + 2] = fa.z; a[4 * h + 3] = fa.w;
+            b[4 * h] = fb.x; b[4 * h + 1] = fb.y; b[4 * h + 2] = fb.z; b[4 * h + 3] = fb.w;
           }
-        }
-        // ke row: channels 8 g .. (from k-step 0) and 32 + 8 g .. (k-step 1)
+          uint32_t hk[8], lk[8], hv[8], lv[8];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+          for (int t = 0; t < 8; ++t) {
+            hk[t] = bf16_rne_bits(a[t]);
+            lk[t] = bf16_rne_bits(a[t] - bf16_bits_to_f32(hk[t]));
+            hv[t] = bf16_rne_bits(b[t]);
+            lv[t] = bf16_rne_bits(b[t] - bf16_bits_to_f32(hv[t]));
+          }
+          kh[i][ks] = u32x4{pack2(hk[0], hk[1]), pack2(hk[2], hk[3]), pack2(hk[4], hk[5]), pack2(hk[6], hk[7])};
+          kl[i][ks] = u32x4{pack2(lk[0], lk[1]), pack2(lk[2], lk[3]), pack2(lk[4], lk[5]), pack2(lk[6], lk[7])};
+          vh[i][ks] = u32x4{pack2(hv[0], hv[1]), pack2(hv[2], hv[3]), pack2(hv[4], hv[5]), pack2(hv[6], hv[7])};
+          vlo[i][ks] = u32x4{pack2(lv[0], lv[1]), pack2(lv[2], lv[3]), pack2(lv[4], lv[5]), pack2(lv[6], lv[7])};
 #pragma unroll
           for (int h = 0; h < 2; ++h)
-            *reinterpret_cast<float4*>(&ke[w][16 * i + j][32 * ks + 8 * g + 4 * h]) =
-                make_float4(kf[8 * ks + 4 * h], kf[8 * ks + 4 * h + 1], kf[8 * ks + 4 * h + 2],
-                            kf[8 * ks + 4 * h + 3]);
-      } else {
-        if (valid[i]) {
-          if (sht[i]) {
-            load16(srow_k, 16 * g, kb[i]);
-            load16(srow_v, 16 * g, vb[i]);
-          } else {
-            load16(rrow_k, 16 * g, kb[i]);
-            load16(rrow_v, 16 * g, vb[i]);
+            *reinterpret_cast<float4*>(&ke[w][16 * i + j][c0 + 4 * h]) =
+                make_float4(a[4 * h], a[4 * h + 1], a[4 * h + 2], a[4 * h + 3]);
+        } else {
+          u32x4 kk = u32x4{0u, 0u, 0u, 0u}, vv = kk;
+          if (valid[i]) {
+            kk = *reinterpret_cast<const u32x4*>(rrow_k + c0);
+            vv = *reinterpret_cast<const u32x4*>(rrow_v + c0);
           }
-        }
-        (void)kf;
-        // the key rows again for dq's B operand
+          kh[i][ks] = kk;
+          vh[i][ks] = vv;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          *reinterpret_cast<float4*>(&ke[w][16 * i + j][16 * g + 4 * q]) =
-              make_float4(kb[i][4 * q], kb[i][4 * q + 1], kb[i][4 * q + 2], kb[i][4 * q + 3]);
+          for (int h = 0; h < 2; ++h)
+            *reinterpret_cast<float4*>(&ke[w][16 * i + j][c0 + 4 * h]) =
+                make_float4(__uint_as_float(kk[2 * h] << 16), __uint_as_float(kk[2 * h] & 0xFFFF0000u),
+                            __uint_as_float(kk[2 * h + 1] << 16),
+                            __uint_as_float(kk[2 * h + 1] & 0xFFFF0000u));
+        }
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) kb[i][c] = vb[i][c] = 0.f;
+      if (valid[i]) {
+        if (sht[i]) {
+          load16(srow_k, 16 * g, kb[i]);
+          load16(srow_v, 16 * g, vb[i]);
+        } else {
+          load16(rrow_k, 16 * g, kb[i]);
+          load16(rrow_v, 16 * g, vb[i]);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<float4*>(&ke[w][16 * i + j][16 * g + 4 * q]) =
+            make_float4(kb[i][4 * q], kb[i][4 * q + 1], kb[i][4 * q + 2], kb[i][4 * q + 3]);
+    }
+  };
+  // (PF) expert e's routed rows into kn/vn, ahead of their use
+  auto prefetch_entries = [&](int e) {
+    if constexpr (PF) {
+#pragma unroll
+      for (int i = 0; i < NTW; ++i) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) kn[i][c] = vn[i][c] = 0.f;
+        if (e < m && valid[i] && !sht[i]) {
+          const int col = 16 * (w + 4 * i) + j;
+          const size_t r = ((size_t)bh * N + idx[((size_t)bh * m + e) * k + col - msp]) * kHeadDim;
+          load16(K + r, 16 * g, kn[i]);
+          load16(V + r, 16 * g, vn[i]);
+        }
       }
     }
-  }
+  };
   f32x4 adk[NTW][4], adv[NTW][4];
 #pragma unroll
   for (int i = 0; i < NTW; ++i)
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) adk[i][c4] = adv[i][c4] = zero4();
-
-  for (int t0 = 0; t0 < cnt; t0 += 16) {
-    const int nq = min(16, cnt - t0);
-    __syncthreads();  // the previous tile's LDS is spent
-    if constexpr (BF) {
-      *reinterpret_cast<u32x2*>(&qtb[rq][rc0]) = u32x2{__float_as_uint(qv.x), __float_as_uint(qv.y)};
-      const float gf[4] = {gv.x, gv.y, gv.z, gv.w};
-      uint32_t hh[4], ll[4];
+  // the entries' rows go out: lane (g, j) holds [entry 16 (w + 4i) + 4g + r]
+  // [channel 16 c4 + j]; SH selects the shared tiles (else the routed ones)
+  auto flush = [&](bool sh_tiles, int e) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        hh[t] = bf16_rne_bits(gf[t]);
-        ll[t] = bf16_rne_bits(gf[t] - bf16_bits_to_f32(hh[t]));
-      }
-      *reinterpret_cast<u32x2*>(&gth[rq][rc0]) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
-      *reinterpret_cast<u32x2*>(&gtl[rq][rc0]) = u32x2{pack2(ll[0], ll[1]), pack2(ll[2], ll[3])};
-    } else {
-      *reinterpret_cast<float4*>(&qt[rq][rc0]) = qv;
-    }
-    *reinterpret_cast<float4*>(&gt[rq][rc0]) = gv;
-    if ((tid & 15) == 0) qid[rq] = qidv;
-    if (t0 + 16 < cnt) fetch(t0 + 16, qv, gv, qidv);
-    __syncthreads();
-    // S and dW: lane (g, j) holds [query 4g + r][entry 16 (w + 4i) + j]
-    f32x4 sa[NTW], sw[NTW];
+    for (int i = 0; i < NTW; ++i) {
+      if (i >= nt || sht[i] != sh_tiles) continue;
+      const int base = 16 * (w + 4 * i);
 #pragma unroll
-    for (int i = 0; i < NTW; ++i) sa[i] = sw[i] = zero4();
-    if constexpr (BF) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&qtb[j][32 * ks + 8 * g]);
-        const u32x4 ah = *reinterpret_cast<const u32x4*>(&gth[j][32 * ks + 8 * g]);
-        const u32x4 al = *reinterpret_cast<const u32x4*>(&gtl[j][32 * ks + 8 * g]);
-#pragma unroll
-        for (int i = 0; i < NTW; ++i)
-          if (i < nt) {
-            sa[i] = mfma_bf16(a, kh[i][ks], sa[i]);
-            sw[i] = mfma_bf16(ah, vh[i][ks], sw[i]);
-            sw[i] = mfma_bf16(al, vh[i][ks], sw[i]);
-            if (sht[i]) {
-              sa[i] = mfma_bf16(a, kl[i][ks], sa[i]);
-              sw[i] = mfma_bf16(ah, vlo[i][ks], sw[i]);
-            }
+      for (int r = 0; r < 4; ++r) {
+        const int col = base + 4 * g + r;
+        float* dk = nullptr;
+        float* dv = nullptr;
+        if (sh_tiles) {
+          if (col < ms) {
+            dk = dql + ((size_t)bh * m + col) * kHeadDim;
+            dv = dvl + ((size_t)bh * m + col) * kHeadDim;
           }
+        } else if (col - msp < k) {
+          const size_t row = ((size_t)bh * N + idx[((size_t)bh * m + e) * k + col - msp]) * kHeadDim;
+          dk = dK + row;
+          dv = dV + row;
+        }
+        if (dk) {
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) {
+            unsafeAtomicAdd(dk + 16 * c4 + j, adk[i][c4][r]);
+            unsafeAtomicAdd(dv + 16 * c4 + j, adv[i][c4][r]);
+          }
+        }
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) adk[i][c4][r] = adv[i][c4][r] = 0.f;
       }
-    } else {
+    }
+  };
+
+  int qa, ca, qb, cb;
+  int ea = next_expert(p, qa, ca);
+  if (ea >= m) return;
+  int eb = next_expert(ea + P, qb, cb);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 a4 = *reinterpret_cast<const float4*>(&qt[j][16 * g + 4 * q]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&gt[j][16 * g + 4 * q]);
-        const float av[4] = {a4.x, a4.y, a4.z, a4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+  for (int i = 0; i < NTW; ++i)
+    if (i < nt) load_entries(i, ea);
+  prefetch_entries(eb);
+  float4 qv, gv;
+  int qidv;
+  fetch(qa, 0, ca, qv, gv, qidv);
+
+  while (ea < m) {
+    for (int t0 = 0; t0 < ca; t0 += 16) {
+      const int nq = min(16, ca - t0);
+      __syncthreads();  // the previous tile's LDS is spent
+      if constexpr (BF) {
+        *reinterpret_cast<u32x2*>(&qtb[rq][rc0]) = u32x2{__float_as_uint(qv.x), __float_as_uint(qv.y)};
+        const float gf[4] = {gv.x, gv.y, gv.z, gv.w};
+        uint32_t hh[4], ll[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int t = 0; t < 4; ++t) {
+          hh[t] = bf16_rne_bits(gf[t]);
+          ll[t] = bf16_rne_bits(gf[t] - bf16_bits_to_f32(hh[t]));
+        }
+        *reinterpret_cast<u32x2*>(&gth[rq][rc0]) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
+        *reinterpret_cast<u32x2*>(&gtl[rq][rc0]) = u32x2{pack2(ll[0], ll[1]), pack2(ll[2], ll[3])};
+      } else {
+        *reinterpret_cast<float4*>(&qt[rq][rc0]) = qv;
+      }
+      *reinterpret_cast<float4*>(&gt[rq][rc0]) = gv;
+      if ((tid & 15) == 0) qid[rq] = qidv;
+      // the next tile's rows fly while this one is computed
+      if (t0 + 16 < ca)
+        fetch(qa, t0 + 16, ca, qv, gv, qidv);
+      else if (eb < m)
+        fetch(qb, 0, cb, qv, gv, qidv);
+      __syncthreads();
+      // S and dW: lane (g, j) holds [query 4g + r][entry 16 (w + 4i) + j]
+      f32x4 sa[NTW], sw[NTW];
+#pragma unroll
+      for (int i = 0; i < NTW; ++i) sa[i] = sw[i] = zero4();
+      if constexpr (BF) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(&qtb[j][32 * ks + 8 * g]);
+          const u32x4 ah = *reinterpret_cast<const u32x4*>(&gth[j][32 * ks + 8 * g]);
+          const u32x4 al = *reinterpret_cast<const u32x4*>(&gtl[j][32 * ks + 8 * g]);
 #pragma unroll
           for (int i = 0; i < NTW; ++i)
             if (i < nt) {
-              sa[i] = mfma_f32(av[u], kb[i][4 * q + u], sa[i]);
-              sw[i] = mfma_f32(dv[u], vb[i][4 * q + u], sw[i]);
+              sa[i] = mfma_bf16(a, kh[i][ks], sa[i]);
+              sw[i] = mfma_bf16(ah, vh[i][ks], sw[i]);
+              sw[i] = mfma_bf16(al, vh[i][ks], sw[i]);
+              if (sht[i]) {
+                sa[i] = mfma_bf16(a, kl[i][ks], sa[i]);
+                sw[i] = mfma_bf16(ah, vlo[i][ks], sw[i]);
+              }
             }
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 a4 = *reinterpret_cast<const float4*>(&qt[j][16 * g + 4 * q]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&gt[j][16 * g + 4 * q]);
+          const float av[4] = {a4.x, a4.y, a4.z, a4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int i = 0; i < NTW; ++i)
+              if (i < nt) {
+                sa[i] = mfma_f32(av[u], kb[i][4 * q + u], sa[i]);
+                sw[i] = mfma_f32(dv[u], vb[i][4 * q + u], sw[i]);
+              }
+        }
       }
-    }
-    // logits (base 2; -inf for padding entries) and the row maxima
-    float x[NTW][4];
-    float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-#pragma unroll
-    for (int i = 0; i < NTW; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        x[i][r] = i < nt && valid[i] ? sa[i][r] * kl2 : -INFINITY;
-        mx[r] = fmaxf(mx[r], x[i][r]);
-      }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      mx[r] = g16_maxf(mx[r]);
-      if (j == r) red[0][4 * g + r][w] = mx[r];
-    }
-    __syncthreads();
-    float ps[4], pd[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float4 m4 = *reinterpret_cast<const float4*>(&red[0][4 * g + r][0]);
-      mx[r] = fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w));
-      ps[r] = pd[r] = 0.f;
-    }
-    float p[NTW][4];
-#pragma unroll
-    for (int i = 0; i < NTW; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[i][r] = __builtin_amdgcn_exp2f(x[i][r] - mx[r]);  // 0 at -inf
-        ps[r] += p[i][r];
-        pd[r] = fmaf(p[i][r], sw[i][r], pd[r]);
-      }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      ps[r] = g16_sumf(ps[r]);
-      pd[r] = g16_sumf(pd[r]);
-      if (j == r) {
-        red[1][4 * g + r][w] = ps[r];
-        red[2][4 * g + r][w] = pd[r];
-      }
-    }
-    __syncthreads();
-    // w = p / L, dz = tau w (dw - D), D = sum p dw / L
-    float wt[NTW][4], dz[NTW][4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float4 l4 = *reinterpret_cast<const float4*>(&red[1][4 * g + r][0]);
-      const float4 d4 = *reinterpret_cast<const float4*>(&red[2][4 * g + r][0]);
-      const float inv = 1.0f / ((l4.x + l4.y) + (l4.z + l4.w));
-      const float D = ((d4.x + d4.y) + (d4.z + d4.w)) * inv;
-#pragma unroll
-      for (int i = 0; i < NTW; ++i) {
-        wt[i][r] = p[i][r] * inv;
-        dz[i][r] = tau * wt[i][r] * (sw[i][r] - D);
-      }
-    }
-    // dE_key += dz^T Q, dE_val += w^T dOut (k-step r: lane group g with query
-    // 4g + r); dz transposed into the wave's LDS rows for dq
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-#pragma unroll
-      for (int c4 = 0; c4 < 4; ++c4) {
-        float bq;
-        if constexpr (BF)
-          bq = bf16_bits_to_f32(qtb[4 * g + r][16 * c4 + j]);
-        else
-          bq = qt[4 * g + r][16 * c4 + j];
-        const float bg = gt[4 * g + r][16 * c4 + j];
-#pragma unroll
-        for (int i = 0; i < NTW; ++i)
-          if (i < nt) {
-            adk[i][c4] = mfma_f32(dz[i][r], bq, adk[i][c4]);
-            adv[i][c4] = mfma_f32(wt[i][r], bg, adv[i][c4]);
-          }
-      }
+      // logits (base 2; -inf for padding entries) and the row maxima
+      float x[NTW][4];
+      float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
       for (int i = 0; i < NTW; ++i)
-        if (i < nt) zt[w][16 * i + j][4 * g + r] = dz[i][r];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          x[i][r] = valid[i] ? sa[i][r] * kl2 : -INFINITY;
+          mx[r] = fmaxf(mx[r], x[i][r]);
+        }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        mx[r] = g16_maxf(mx[r]);
+        if (j == r) red[0][4 * g + r][w] = mx[r];
+      }
+      __syncthreads();
+      float ps[4], pd[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float4 m4 = *reinterpret_cast<const float4*>(&red[0][4 * g + r][0]);
+        mx[r] = fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w));
+        ps[r] = pd[r] = 0.f;
+      }
+      float pw[NTW][4];
+#pragma unroll
+      for (int i = 0; i < NTW; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pw[i][r] = __builtin_amdgcn_exp2f(x[i][r] - mx[r]);  // 0 at -inf
+          ps[r] += pw[i][r];
+          pd[r] = fmaf(pw[i][r], sw[i][r], pd[r]);
+        }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ps[r] = g16_sumf(ps[r]);
+        pd[r] = g16_sumf(pd[r]);
+        if (j == r) {
+          red[1][4 * g + r][w] = ps[r];
+          red[2][4 * g + r][w] = pd[r];
+        }
+      }
+      __syncthreads();
+      // w = p / L, dz = tau w (dw - D), D = sum p dw / L
+      float wt[NTW][4], dz[NTW][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float4 l4 = *reinterpret_cast<const float4*>(&red[1][4 * g + r][0]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&red[2][4 * g + r][0]);
+        const float inv = 1.0f / ((l4.x + l4.y) + (l4.z + l4.w));
+        const float D = ((d4.x + d4.y) + (d4.z + d4.w)) * inv;
+#pragma unroll
+        for (int i = 0; i < NTW; ++i) {
+          wt[i][r] = pw[i][r] * inv;
+          dz[i][r] = tau * wt[i][r] * (sw[i][r] - D);
+        }
+      }
+      // dE_key += dz^T Q, dE_val += w^T dOut (k-step r: lane group g with
+      // query 4g + r); dz transposed into the wave's LDS rows for dq
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          float bq;
+          if constexpr (BF)
+            bq = bf16_bits_to_f32(qtb[4 * g + r][16 * c4 + j]);
+          else
+            bq = qt[4 * g + r][16 * c4 + j];
+          const float bg = gt[4 * g + r][16 * c4 + j];
+#pragma unroll
+          for (int i = 0; i < NTW; ++i)
+            if (i < nt) {
+              adk[i][c4] = mfma_f32(dz[i][r], bq, adk[i][c4]);
+              adv[i][c4] = mfma_f32(wt[i][r], bg, adv[i][c4]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NTW; ++i)
+          if (i < nt) zt[w][16 * i + j][4 * g + r] = dz[i][r];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // dq share over this wave's entries: lane (g, j) -> [query 4g + r][channel 16 c4 + j]
+      f32x4 aq[4];
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4) aq[c4] = zero4();
+#pragma unroll
+      for (int i = 0; i < NTW; ++i)
+        if (i < nt) {
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const float a = zt[w][16 * i + 4 * ks + g][j];
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4)
+              aq[c4] = mfma_f32(a, ke[w][16 * i + 4 * ks + g][16 * c4 + j], aq[c4]);
+          }
+        }
+#pragma unroll
+      for (int c4 = 0; c4 < 4; ++c4)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dqp[w][4 * g + r][16 * c4 + j] = aq[c4][r];
+      __syncthreads();
+      {
+        const int qi = tid >> 4, c0 = 4 * (tid & 15);
+        if (qi < nq) {
+          float4 sum = *reinterpret_cast<const float4*>(&dqp[0][qi][c0]);
+#pragma unroll
+          for (int ww = 1; ww < 4; ++ww) {
+            const float4 v = *reinterpret_cast<const float4*>(&dqp[ww][qi][c0]);
+            sum.x += v.x;
+            sum.y += v.y;
+            sum.z += v.z;
+            sum.w += v.w;
+          }
+          *reinterpret_cast<float4*>(dq + ((size_t)bh * N + qid[qi]) * kHeadDim + c0) = sum;
+        }
+      }
     }
+    // the expert's routed rows go out; then on to the next expert
+    flush(false, ea);
+    ea = eb;
+    qa = qb;
+    ca = cb;
+    if (ea >= m) break;
+    eb = next_expert(ea + P, qb, cb);
+    // (the wave's own LDS copy of its key rows: its reads of the previous
+    // expert's are done)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // dq partial over this wave's entries: lane (g, j) -> [query 4g + r][channel 16 c4 + j]
-    f32x4 aq[4];
+    if constexpr (PF) {
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) aq[c4] = zero4();
+      for (int i = 0; i < NTW; ++i)
+        if (i < nt && !sht[i]) {
 #pragma unroll
-    for (int i = 0; i < NTW; ++i)
-      if (i < nt) {
+          for (int c = 0; c < 16; ++c) {
+            kb[i][c] = kn[i][c];
+            vb[i][c] = vn[i][c];
+          }
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const float a = zt[w][16 * i + 4 * ks + g][j];
-#pragma unroll
-          for (int c4 = 0; c4 < 4; ++c4)
-            aq[c4] = mfma_f32(a, ke[w][16 * i + 4 * ks + g][16 * c4 + j], aq[c4]);
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<float4*>(&ke[w][16 * i + j][16 * g + 4 * q]) =
+                make_float4(kb[i][4 * q], kb[i][4 * q + 1], kb[i][4 * q + 2], kb[i][4 * q + 3]);
         }
-      }
+      prefetch_entries(eb);
+    } else {
 #pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) dqp[w][4 * g + r][16 * c4 + j] = aq[c4][r];
-    __syncthreads();
-    {
-      const int qi = tid >> 4, c0 = 4 * (tid & 15);
-      if (qi < nq) {
-        float4 sum = *reinterpret_cast<const float4*>(&dqp[0][qi][c0]);
-#pragma unroll
-        for (int ww = 1; ww < 4; ++ww) {
-          const float4 v = *reinterpret_cast<const float4*>(&dqp[ww][qi][c0]);
-          sum.x += v.x;
-          sum.y += v.y;
-          sum.z += v.z;
-          sum.w += v.w;
-        }
-        *reinterpret_cast<float4*>(dq + ((size_t)bh * N + qid[qi]) * kHeadDim + c0) = sum;
-      }
+      for (int i = 0; i < NTW; ++i)
+        if (i < nt && !sht[i]) load_entries(i, ea);
     }
   }
-  // the entries' rows: lane (g, j) holds [entry 16 (w + 4i) + 4g + r][channel 16 c4 + j]
-#pragma unroll
-  for (int i = 0; i < NTW; ++i) {
-    if (i >= nt) continue;
-    const int base = 16 * (w + 4 * i);
-    const bool sh = base < msp;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int col = base + 4 * g + r;
-      float* dk = nullptr;
-      float* dv = nullptr;
-      if (sh) {
-        if (col < ms) {
-          dk = dql + ((size_t)bh * m + col) * kHeadDim;
-          dv = dvl + ((size_t)bh * m + col) * kHeadDim;
-        }
-      } else if (col - msp < k) {
-        const size_t row = ((size_t)bh * N + idxe[col - msp]) * kHeadDim;
-        dk = dK + row;
-        dv = dV + row;
-      }
-      if (dk) {
-#pragma unroll
-        for (int c4 = 0; c4 < 4; ++c4) {
-          unsafeAtomicAdd(dk + 16 * c4 + j, adk[i][c4][r]);
-          unsafeAtomicAdd(dv + 16 * c4 + j, adv[i][c4][r]);
-        }
-      }
-    }
-  }
+  // the shared entries' rows, summed over the workgroup's experts
+  flush(true, 0);
 }
 
 // ---------------------------------------------------------------- shared
@@ -1204,9 +1286,14 @@ static hipError_t run_backward(const T* Q, const T* K, const T* V, const float* 
       bwd::zero_kernel<<<(unsigned)((nl + 255) / 256), 256, 0, st>>>(dql, nl);
       bwd::zero_kernel<<<(unsigned)((nl + 255) / 256), 256, 0, st>>>(dvl, nl);
     }
+    // workgroups per head: one-tile form, enough for about six per CU in all
+    // (the shared entries' sums then go out once per workgroup); two-tile
+    // form, one per expert (measured at 3136 tokens: 715 us against 754 us
+    // with eight per head)
+    const int P = ep <= 64 ? std::max(1, std::min(s.m, (1536 + s.BH - 1) / s.BH)) : s.m;
     auto tile = ep <= 64 ? bwd::tile_kernel<T, 1> : bwd::tile_kernel<T, 2>;
-    tile<<<dim3(s.m, s.BH), 256, 0, st>>>(Q, K, V, ql, vl, idx, offsets, perm, dout, dq, dk, dv,
-                                          dql, dvl, s.N, s.m, s.k, ms, msp, ep, tau);
+    tile<<<dim3(P, s.BH), 256, 0, st>>>(Q, K, V, ql, vl, idx, offsets, perm, dout, dq, dk, dv,
+                                        dql, dvl, s.N, s.m, s.k, ms, msp, ep, P, tau);
   } else {
     bwd::query_kernel<T><<<dim3((s.N + 3) / 4, s.BH), 256, 0, st>>>(
         Q, K, V, ql, vl, idx, route, perm, dout, dq, G, s.N, s.m, s.k, s.s, s.shared ? 1 : 0, tau);
