@@ -492,6 +492,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the light records of the other workloads and the variants")
     ap.add_argument("--extra-steps", type=int, default=20)
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only the backward on --workload (and --also), one JSON line of "
+                         "backward records (for profiling the backward kernels)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this MiTA build runs on exactly one GPU; every (batch, head) is "
@@ -506,6 +509,10 @@ def main():
         _b.build()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
+    if args.backward_only:
+        recs = [measure_backward(n, args.steps, args.warmup) for n in (args.workload, args.also) if n]
+        print(json.dumps({"backward": recs}))
+        return
     if args.copy_calibration:
         copy_calibration()
     runner, main_res = measure(args.workload, args.steps, args.warmup, args.path,

@@ -1038,35 +1038,37 @@ __global__ __launch_bounds__(256, 2) void landmark_mfma_kernel(
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int c4 = 0; c4 < 4; ++c4) aq[rt][c4] = zero4();
-  // rows (zero past m), the dQ_L sums, the rows' statistics
-  for (int it = tid; it < 64 * 16; it += 256) {
-    const int r = it >> 4, c0 = 4 * (it & 15);
-    float4 q = make_float4(0.f, 0.f, 0.f, 0.f), d = q;
-    if (r < m) {
-      q = *reinterpret_cast<const float4*>(ql + ((size_t)bh * m + r) * kHeadDim + c0);
-      d = *reinterpret_cast<const float4*>(dvl + ((size_t)bh * m + r) * kHeadDim + c0);
-    }
-    *reinterpret_cast<float4*>(&qs[r][c0]) = q;
-    *reinterpret_cast<float4*>(&gs[r][c0]) = d;
-    *reinterpret_cast<float4*>(&acc_q[r][c0]) = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  // rows (zero past m), the dQ_L sums, the rows' statistics; every load of a
+  // thread goes out before any is used.  Thread (row tid / 4, channels
+  // 16 (tid % 4) ..): its Q_L, dV_L and V_L chunks, and dV_L . V_L
   {
-    // dV_L . V_L: thread (row tid / 4, channels 16 (tid % 4) ..)
     const int r = tid >> 2, c0 = 16 * (tid & 3);
-    float z = 0.f;
-    if (r < m) {
-      const float4* a = reinterpret_cast<const float4*>(dvl + ((size_t)bh * m + r) * kHeadDim + c0);
-      const float4* b = reinterpret_cast<const float4*>(vl + ((size_t)bh * m + r) * kHeadDim + c0);
+    float4 q[4], d[4], v[4];
+    float4 st = make_float4(0.f, 1.f, 0.f, 0.f);
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float4 x = a[q], y = b[q];
-        z = fmaf(x.x, y.x, fmaf(x.y, y.y, fmaf(x.z, y.z, fmaf(x.w, y.w, z))));
+    for (int u = 0; u < 4; ++u) q[u] = d[u] = v[u] = z4;
+    if (r < m) {
+      const size_t o = ((size_t)bh * m + r) * kHeadDim + c0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        q[u] = *reinterpret_cast<const float4*>(ql + o + 4 * u);
+        d[u] = *reinterpret_cast<const float4*>(dvl + o + 4 * u);
+        v[u] = *reinterpret_cast<const float4*>(vl + o + 4 * u);
       }
+      st = stats[(size_t)bh * m + r];
+    }
+    float z = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      *reinterpret_cast<float4*>(&qs[r][c0 + 4 * u]) = q[u];
+      *reinterpret_cast<float4*>(&gs[r][c0 + 4 * u]) = d[u];
+      *reinterpret_cast<float4*>(&acc_q[r][c0 + 4 * u]) = z4;
+      z = fmaf(d[u].x, v[u].x, fmaf(d[u].y, v[u].y, fmaf(d[u].z, v[u].z, fmaf(d[u].w, v[u].w, z))));
     }
     z += __shfl_xor(z, 1, 64);
     z += __shfl_xor(z, 2, 64);
     if ((tid & 3) == 0) {
-      const float4 st = r < m ? stats[(size_t)bh * m + r] : make_float4(0.f, 1.f, 0.f, 0.f);
       rst[0][r] = st.x;
       rst[1][r] = r < m ? 1.0f / st.y : 0.f;
       rst[2][r] = z;
