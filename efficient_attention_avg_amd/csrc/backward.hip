@@ -1191,11 +1191,21 @@ __global__ __launch_bounds__(256) void pool_kernel(const float* __restrict__ dql
   const int bh = blockIdx.y;
   if (it >= (long long)N * 4) return;
   const int n = (int)(it >> 2), c0 = 16 * (int)(it & 3);
+  // (32-bit arithmetic when every product below stays under 2^31, which holds
+  // for all but extreme grids; 64-bit otherwise, a uniform branch)
   const int y = n / gw, x = n - y * gw;
-  const int r0 = (int)(((long long)y * mh) / gh);
-  const int r1 = (int)(((long long)(y + 1) * mh + gh - 1) / gh) - 1;
-  const int cl = (int)(((long long)x * mw) / gw);
-  const int ch = (int)(((long long)(x + 1) * mw + gw - 1) / gw) - 1;
+  int r0, r1, cl, ch;
+  if ((long long)gh * (mh + 1) < (1LL << 31) && (long long)gw * (mw + 1) < (1LL << 31)) {
+    r0 = (y * mh) / gh;
+    r1 = ((y + 1) * mh + gh - 1) / gh - 1;
+    cl = (x * mw) / gw;
+    ch = ((x + 1) * mw + gw - 1) / gw - 1;
+  } else {
+    r0 = (int)(((long long)y * mh) / gh);
+    r1 = (int)(((long long)(y + 1) * mh + gh - 1) / gh) - 1;
+    cl = (int)(((long long)x * mw) / gw);
+    ch = (int)(((long long)(x + 1) * mw + gw - 1) / gw) - 1;
+  }
   float4 acc[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) acc[q] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -1230,9 +1240,20 @@ __global__ __launch_bounds__(256) void pool_kernel(const float* __restrict__ dql
   }
 }
 
-__global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, long long n) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0.f;
+// Clears two buffers of n4 float4s each (16-byte stores, grid-stride).
+__global__ __launch_bounds__(256) void zero_kernel(float4* __restrict__ a, float4* __restrict__ b,
+                                                   long long n4) {
+  const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4;
+       i += (long long)gridDim.x * 256) {
+    a[i] = z;
+    b[i] = z;
+  }
+}
+
+static unsigned zero_grid(long long n4) {
+  const long long g = (n4 + 255) / 256;
+  return (unsigned)(g < 4096 ? g : 4096);
 }
 
 }  // namespace bwd
@@ -1275,9 +1296,7 @@ static hipError_t run_backward(const T* Q, const T* K, const T* V, const float* 
   p += align_up((size_t)s.BH * s.m * 64 * 4, 256);
   float2* G = (float2*)p;  // (outside the tile kernel's case)
   const long long nel = (long long)s.BH * s.N * 64;
-  const unsigned zb = (unsigned)((nel + 255) / 256);
-  bwd::zero_kernel<<<zb, 256, 0, st>>>(dk, nel);
-  bwd::zero_kernel<<<zb, 256, 0, st>>>(dv, nel);
+  bwd::zero_kernel<<<bwd::zero_grid(nel / 4), 256, 0, st>>>((float4*)dk, (float4*)dv, nel / 4);
   const dim3 rows((s.m + 15) / 16, s.BH);
   if (bwd_tiled(s)) {
     // one kernel for the query, expert and shared steps; dQ_L and dV_L then
@@ -1285,8 +1304,7 @@ static hipError_t run_backward(const T* Q, const T* K, const T* V, const float* 
     const int msp = (ms + 15) & ~15, ep = msp + ((s.k + 15) & ~15);
     if (s.shared) {
       const long long nl = (long long)s.BH * s.m * 64;
-      bwd::zero_kernel<<<(unsigned)((nl + 255) / 256), 256, 0, st>>>(dql, nl);
-      bwd::zero_kernel<<<(unsigned)((nl + 255) / 256), 256, 0, st>>>(dvl, nl);
+      bwd::zero_kernel<<<bwd::zero_grid(nl / 4), 256, 0, st>>>((float4*)dql, (float4*)dvl, nl / 4);
     }
     // workgroups per head: one-tile form, enough for about six per CU in all
     // (the shared entries' sums then go out once per workgroup); two-tile

@@ -55,9 +55,16 @@ __device__ __forceinline__ float fast_exp(float x) {
 }
 
 // 2-D adaptive average pooling window along one axis: [lo, hi).
+// (32-bit arithmetic while (i + 1) g + mg - 1 < 2^31; 64-bit past that, for
+// the widest grids the API accepts)
 __host__ __device__ __forceinline__ void pool_window(int i, int g, int mg, int* lo, int* hi) {
-  *lo = (i * g) / mg;
-  *hi = ((i + 1) * g + mg - 1) / mg;
+  if ((long long)g * (mg + 1) < (1LL << 31)) {
+    *lo = (i * g) / mg;
+    *hi = ((i + 1) * g + mg - 1) / mg;
+  } else {
+    *lo = (int)(((long long)i * g) / mg);
+    *hi = (int)(((long long)(i + 1) * g + mg - 1) / mg);
+  }
 }
 
 }  // namespace mita
