@@ -70,6 +70,7 @@ CASES = [
     (1, 1, 12, 12, 4, 4, 20, "f32", 3, True),       # route-only, three experts
     (1, 1, 1, 3000, 1, 30, 50, "bf16", 1, False),   # a 1-D row
     (1, 1, 32, 32, 20, 20, 30, "bf16", 1, False),   # m = 400
+    (1, 2, 16, 16, 5, 5, 64, "f32", 1, False),      # fp32, two entry tiles per wave
 ]
 
 
@@ -87,9 +88,12 @@ def test_backward_matches_oracle(case):
 
 
 @pytest.mark.parametrize("name,B,heads", [("deit-s", 8, None), ("hires-3136", 2, None),
-                                          ("long-16k", 1, [(0, 0), (0, 5)])])
+                                          ("long-16k", 1, [(0, 0), (0, 5)]),
+                                          ("deit-s", 256, [(0, 0), (17, 3), (128, 1), (255, 5)])])
 def test_backward_workloads(name, B, heads):
-    """The workloads' shapes (leading batch entries), every head or a sample."""
+    """The workloads' shapes (leading batch entries), every head or a sample.  The full
+    DeiT-S batch is the case where one workgroup walks all of a head's experts (the
+    small batches give each expert a workgroup of its own)."""
     w = synth.workload(name)
     _say(f"backward workload {name} B={B}")
     Q, K, V = synth.workload_inputs(name, B=B)
