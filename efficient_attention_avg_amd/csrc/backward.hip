@@ -308,10 +308,11 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
 // registers and LDS, three workgroups per CU).  Workgroup (p, head bh) walks
 // the head's experts p, p + P, ..; its tiles run back to back, each tile's
 // successor's query rows (the next tile of the expert, or the next expert's
-// first) requested while it is computed, and with NTW = 1 the next expert's
-// routed rows too.  The shared entries' gradients accumulate over all of the
-// workgroup's experts and go out once at the end; the routed ones go out
-// after each expert.
+// first) requested while it is computed.  (Requesting the next expert's
+// routed rows early too needed 32 more registers, which at three workgroups
+// per CU spilled: 1005 us against 945 us per DeiT-S backward without.)  The
+// shared entries' gradients accumulate over all of the workgroup's experts
+// and go out once at the end; the routed ones go out after each expert.
 template <typename T, int NTW>
 __global__ __launch_bounds__(256, NTW == 1 ? 3 : 2) void tile_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
@@ -326,7 +327,6 @@ __global__ __launch_bounds__(256, NTW == 1 ? 3 : 2) void tile_kernel(
   // one-tile form, bound by its loads' latency, ran 10% slower with the
   // splits, the two-tile form 30% faster).
   constexpr bool BF = std::is_same<T, bf16_t>::value && NTW == 2;
-  constexpr bool PF = NTW == 1;  // the next expert's routed rows prefetched
   __shared__ __attribute__((aligned(16))) float qt[16][68];
   __shared__ __attribute__((aligned(16))) uint16_t qtb[16][72];
   __shared__ __attribute__((aligned(16))) uint16_t gth[16][72];
@@ -381,7 +381,6 @@ __global__ __launch_bounds__(256, NTW == 1 ? 3 : 2) void tile_kernel(
   // .. + 7 for k-steps ks = 0, 1 of 16x16x32.  Shared tiles' rows (Q_L, V_L)
   // are the same for every expert; routed tiles' rows are the expert's keys.
   float kb[BF ? 1 : NTW][16], vb[BF ? 1 : NTW][16];
-  float kn[PF ? NTW : 1][16], vn[PF ? NTW : 1][16];
   u32x4 kh[NTW][2], kl[NTW][2], vh[NTW][2], vlo[NTW][2];
   bool valid[NTW], sht[NTW];
 #pragma unroll
@@ -475,22 +474,6 @@ __global__ __launch_bounds__(256, NTW == 1 ? 3 : 2) void tile_kernel(
             make_float4(kb[i][4 * q], kb[i][4 * q + 1], kb[i][4 * q + 2], kb[i][4 * q + 3]);
     }
   };
-  // (PF) expert e's routed rows into kn/vn, ahead of their use
-  auto prefetch_entries = [&](int e) {
-    if constexpr (PF) {
-#pragma unroll
-      for (int i = 0; i < NTW; ++i) {
-#pragma unroll
-        for (int c = 0; c < 16; ++c) kn[i][c] = vn[i][c] = 0.f;
-        if (e < m && valid[i] && !sht[i]) {
-          const int col = 16 * (w + 4 * i) + j;
-          const size_t r = ((size_t)bh * N + idx[((size_t)bh * m + e) * k + col - msp]) * kHeadDim;
-          load16(K + r, 16 * g, kn[i]);
-          load16(V + r, 16 * g, vn[i]);
-        }
-      }
-    }
-  };
   f32x4 adk[NTW][4], adv[NTW][4];
 #pragma unroll
   for (int i = 0; i < NTW; ++i)
@@ -538,7 +521,6 @@ __global__ __launch_bounds__(256, NTW == 1 ? 3 : 2) void tile_kernel(
 #pragma unroll
   for (int i = 0; i < NTW; ++i)
     if (i < nt) load_entries(i, ea);
-  prefetch_entries(eb);
   float4 qv, gv;
   int qidv;
   fetch(qa, 0, ca, qv, gv, qidv);
@@ -737,26 +719,9 @@ __global__ __launch_bounds__(256, NTW == 1 ? 3 : 2) void tile_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if constexpr (PF) {
 #pragma unroll
-      for (int i = 0; i < NTW; ++i)
-        if (i < nt && !sht[i]) {
-#pragma unroll
-          for (int c = 0; c < 16; ++c) {
-            kb[i][c] = kn[i][c];
-            vb[i][c] = vn[i][c];
-          }
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<float4*>(&ke[w][16 * i + j][16 * g + 4 * q]) =
-                make_float4(kb[i][4 * q], kb[i][4 * q + 1], kb[i][4 * q + 2], kb[i][4 * q + 3]);
-        }
-      prefetch_entries(eb);
-    } else {
-#pragma unroll
-      for (int i = 0; i < NTW; ++i)
-        if (i < nt && !sht[i]) load_entries(i, ea);
-    }
+    for (int i = 0; i < NTW; ++i)
+      if (i < nt && !sht[i]) load_entries(i, ea);
   }
   // the shared entries' rows, summed over the workgroup's experts
   flush(true, 0);
