@@ -15,10 +15,10 @@
 //   1  Q_L = window means of Q:  dQ_t += sum over windows i holding t of
 //      dQ_L_i / |window i|.
 //
-// Kernels (fp32 arithmetic, fp32 gradients; inputs bf16 or fp32):
+// Kernels (fp32 accumulation, fp32 gradients; inputs bf16 or fp32):
 //   tile      (s = 1, at most 128 entry columns) the query, expert and shared
-//             steps below in one workgroup per (head, expert) on fp32 MFMA;
-//             otherwise:
+//             steps below in one kernel on MFMA: workgroups walk a head's
+//             experts, 16 queries at a time; otherwise:
 //   query     one wave per query: two sweeps over its entries in chunks of
 //             64 (lane = entry for dot products, lane = channel for sums):
 //             the softmax and out_n (online), then w and dz per entry, which
@@ -28,10 +28,12 @@
 //             buffer, then added to dK, dV with one atomic per element (an
 //             expert's keys may be another expert's too);
 //   shared    dQ_L, dV_L from the buffer's shared entries, per 16 landmarks;
-//   stats     each landmark row's softmax maximum and sum over all keys;
-//   landmark  per 64-key block: A and dS for every landmark, the block's dV
-//             and dK rows (owned by the workgroup, added in place) and its
-//             share of dQ_L (atomics);
+//   landmark  (m <= 64) on fp32 MFMA, per run of four 64-key blocks: A and
+//             dS for every landmark, the blocks' dV and dK rows (owned by the
+//             workgroup, added in place) and its share of dQ_L (one atomic
+//             per element); for m > 64 a scalar form per 64-key block, after
+//   stats     each landmark row's softmax maximum and sum over all keys (the
+//             forward's MFMA landmark pass leaves them when it runs);
 //   pool      dQ += each token's windows' dQ_L.
 // Float additions into global memory use the hardware's float atomics
 // (unsafeAtomicAdd: the buffers are ordinary device memory, where they are
