@@ -56,12 +56,11 @@ struct Args {
 };
 
 // LDS layout; the expert table holds, per expert of the workgroup,
-// [q0, count, k key ids, first TQ query ids].  Before the table is filled
-// the same region holds the head's m expert counts, so it spans at least m
-// ints.
+// [q0, count, k key ids, first TQ query ids]; the head's expert offsets sit
+// beside it.
 struct Lay {
   int mp, vlt_stride, ew, ts;
-  int off_qlh, off_qll, off_vlt, off_ke, off_vet, off_tab, off_elist, bytes;
+  int off_qlh, off_qll, off_vlt, off_ke, off_vet, off_tab, off_elist, off_offs, bytes;
   __host__ __device__ Lay(int m, int k, int parts) {
     mp = (m + 31) & ~31;
     vlt_stride = mp * 2 + 16;
@@ -73,10 +72,9 @@ struct Lay {
     off_ke = off_vlt + 64 * vlt_stride;
     off_vet = off_ke + EC * 128;
     off_tab = off_vet + 64 * EVT_STRIDE;
-    // the table region first holds the head's m per-expert counts (the deal),
-    // then the workgroup's ew table entries
-    off_elist = off_tab + (ew * ts > m ? ew * ts : m) * 4;
-    bytes = off_elist + (ew + 1) * 4;
+    off_elist = off_tab + ew * ts * 4;
+    off_offs = off_elist + (ew + 1) * 4;  // the head's m + 1 expert offsets
+    bytes = off_offs + (m + 1) * 4;
   }
 };
 
@@ -164,28 +162,45 @@ void attend_bf16_kernel(Args a) {
   if (bh >= a.BH || part >= a.m) return;
   const int N = a.N, m = a.m, k = a.k, P = a.parts, S = a.s;
   const bool shared = a.shared != 0;
+  // The prologue's global loads are few round trips deep: the head's expert
+  // offsets (one load per thread) and the first Q_L / V_L rows go out
+  // together at entry; the deal and the experts' query ranges then come from
+  // the LDS copy of the offsets, and only the key and query ids (then the
+  // first expert's rows) depend on them.
+  int* offl = reinterpret_cast<int*>(sm + L.off_offs);
+  const int32_t* offs = a.offsets + (size_t)bh * (m + 1);
+  const int o_mine = tid <= m ? offs[tid] : 0;
+  float4 fq[4], fv[4];
+  auto load_qv = [&](int base) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int it = base + 256 * u + tid, row = it >> 4, q4 = it & 15;
+      fq[u] = fv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (it < L.mp * 16 && row < m) {
+        fq[u] = *reinterpret_cast<const float4*>(a.ql + ((size_t)bh * m + row) * 64 + 4 * q4);
+        fv[u] = *reinterpret_cast<const float4*>(a.vl + ((size_t)bh * m + row) * 64 + 4 * q4);
+      }
+    }
+  };
+  if (shared) load_qv(0);
+  for (int e = tid; e <= m; e += blockDim.x) offl[e] = e == tid ? o_mine : offs[e];
+  __syncthreads();
   // The head's experts are dealt to its P workgroups in a snake (0, 1, ..,
   // P-1, P-1, .., 0, ...) in order of their passes (then queries, then id),
   // largest first, so that the workgroups' pass totals even out; every
   // workgroup of the head computes the same deal.
   int* elist = reinterpret_cast<int*>(sm + L.off_elist);
-  {
-    int* ecnt = reinterpret_cast<int*>(sm + L.off_tab);  // (the table is filled after)
-    for (int e = tid; e < m; e += blockDim.x) ecnt[e] = a.offsets[(size_t)bh * (m + 1) + e + 1] -
-                                                      a.offsets[(size_t)bh * (m + 1) + e];
-    __syncthreads();
-    for (int e = tid; e < m; e += blockDim.x) {
-      const int c = ecnt[e], pc = (c + TQ - 1) / TQ;
-      int rank = 0;
-      for (int e2 = 0; e2 < m; ++e2) {
-        const int c2 = ecnt[e2], p2 = (c2 + TQ - 1) / TQ;
-        rank += (p2 > pc || (p2 == pc && (c2 > c || (c2 == c && e2 < e)))) ? 1 : 0;
-      }
-      const int round = rank / P, pos = rank - round * P;
-      if (((round & 1) ? P - 1 - pos : pos) == part) elist[round] = e;
+  for (int e = tid; e < m; e += blockDim.x) {
+    const int c = offl[e + 1] - offl[e], pc = (c + TQ - 1) / TQ;
+    int rank = 0;
+    for (int e2 = 0; e2 < m; ++e2) {
+      const int c2 = offl[e2 + 1] - offl[e2], p2 = (c2 + TQ - 1) / TQ;
+      rank += (p2 > pc || (p2 == pc && (c2 > c || (c2 == c && e2 < e)))) ? 1 : 0;
     }
-    __syncthreads();
+    const int round = rank / P, pos = rank - round * P;
+    if (((round & 1) ? P - 1 - pos : pos) == part) elist[round] = e;
   }
+  __syncthreads();
   // this workgroup's experts: one per full round, plus one in the last
   // (partial) round when the deal reaches it there
   const int full = m / P, rest = m - full * P;
@@ -193,7 +208,6 @@ void attend_bf16_kernel(Args a) {
   const uint16_t* Qh = a.Q + (size_t)bh * N * 64;
   const uint16_t* Kh = a.K + (size_t)bh * N * 64;
   const uint16_t* Vh = a.V + (size_t)bh * N * 64;
-  const int32_t* offs = a.offsets + (size_t)bh * (m + 1);
   const int32_t* permh = a.perm + (size_t)bh * N * S;
   const int32_t* idxh = a.idx + (size_t)bh * m * k;
   // s = 1: output rows of the queries; s > 1: partial rows of the N * s items
@@ -202,15 +216,15 @@ void attend_bf16_kernel(Args a) {
   int* tab = reinterpret_cast<int*>(sm + L.off_tab);
   const u32x4 z = {0u, 0u, 0u, 0u};
 
-  // ---- the experts' table: query ranges first, then key ids and first
-  // query ids with every load of a thread issued before any is used
+  // ---- the experts' table: query ranges (from the LDS offsets), key ids
+  // and first query ids, with every load of a thread issued before any is
+  // used
   if (tid < nexp) {
     const int e = elist[tid];
-    const int q0 = offs[e];
+    const int q0 = offl[e];
     tab[tid * L.ts] = q0;
-    tab[tid * L.ts + 1] = offs[e + 1] - q0;
+    tab[tid * L.ts + 1] = offl[e + 1] - q0;
   }
-  __syncthreads();
   {
     constexpr int U = 8;
     const int total = nexp * L.ts;
@@ -225,7 +239,7 @@ void attend_bf16_kernel(Args a) {
           if (o >= 2 && o < 2 + k) {
             v[u] = idxh[(size_t)e * k + (o - 2)];
           } else if (o >= 2 + k) {
-            const int q0 = tab[j * L.ts], cnt = tab[j * L.ts + 1];
+            const int q0 = offl[e], cnt = offl[e + 1] - q0;
             if (o - 2 - k < cnt) v[u] = permh[q0 + (o - 2 - k)];
           }
         }
@@ -237,41 +251,36 @@ void attend_bf16_kernel(Args a) {
       }
     }
   }
-  // ---- Q_L (hi / lo) and V_L^T for the head; rows past m are zero.  All of
-  // a thread's loads go out before any is used.  (None for route-only.)
-  for (int base = 0; shared && base < L.mp * 16; base += 256 * 4) {
-    float4 fq[4], fv[4];
+  // ---- Q_L (hi / lo) and V_L^T for the head into LDS; rows past m are
+  // zero.  (None for route-only.)  Run after the first expert's rows are
+  // requested, so that the conversions overlap that latency; the barrier
+  // before the first pass publishes them.
+  auto store_qv = [&]() {
+    for (int base = 0; shared && base < L.mp * 16; base += 256 * 4) {
+      if (base > 0) load_qv(base);  // (the first chunk's loads went out at entry)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int it = base + 256 * u + tid, row = it >> 4, q4 = it & 15;
-      fq[u] = fv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (it < L.mp * 16 && row < m) {
-        fq[u] = *reinterpret_cast<const float4*>(a.ql + ((size_t)bh * m + row) * 64 + 4 * q4);
-        fv[u] = *reinterpret_cast<const float4*>(a.vl + ((size_t)bh * m + row) * 64 + 4 * q4);
+      for (int u = 0; u < 4; ++u) {
+        const int it = base + 256 * u + tid, row = it >> 4, q4 = it & 15;
+        if (it >= L.mp * 16) break;
+        const float f4[4] = {fq[u].x, fq[u].y, fq[u].z, fq[u].w};
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          h[i] = bf16_rne_bits(f4[i]);
+          l[i] = bf16_rne_bits(f4[i] - bf16_bits_to_f32(h[i]));
+        }
+        const int off = rc(row, q4 >> 1) + (q4 & 1) * 8;
+        *reinterpret_cast<u32x2*>(sm + L.off_qlh + off) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+        *reinterpret_cast<u32x2*>(sm + L.off_qll + off) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+        const float vv[4] = {fv[u].x, fv[u].y, fv[u].z, fv[u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<uint16_t*>(sm + L.off_vlt + (4 * q4 + i) * L.vlt_stride + 2 * row) =
+              (uint16_t)f16_bits(vv[i]);
       }
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int it = base + 256 * u + tid, row = it >> 4, q4 = it & 15;
-      if (it >= L.mp * 16) break;
-      const float f4[4] = {fq[u].x, fq[u].y, fq[u].z, fq[u].w};
-      uint32_t h[4], l[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        h[i] = bf16_rne_bits(f4[i]);
-        l[i] = bf16_rne_bits(f4[i] - bf16_bits_to_f32(h[i]));
-      }
-      const int off = rc(row, q4 >> 1) + (q4 & 1) * 8;
-      *reinterpret_cast<u32x2*>(sm + L.off_qlh + off) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-      *reinterpret_cast<u32x2*>(sm + L.off_qll + off) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
-      const float vv[4] = {fv[u].x, fv[u].y, fv[u].z, fv[u].w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint16_t*>(sm + L.off_vlt + (4 * q4 + i) * L.vlt_stride + 2 * row) =
-            (uint16_t)f16_bits(vv[i]);
-    }
-  }
-  __syncthreads();
+  };
+  __syncthreads();  // the table is complete
 
   // gather items of this thread: K rows (slots tid>>3 and +32, chunk tid&7)
   // and the V slot pair (2p, 2p+1) of chunk c
@@ -450,6 +459,7 @@ void attend_bf16_kernel(Args a) {
 
   Rows rows;
   if (nexp > 0) load_rows(0, 0, rows);
+  store_qv();
   PassOut pending;
   pending.live = false;
   for (int j = 0; j < nexp; ++j) {
