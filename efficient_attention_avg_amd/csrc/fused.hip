@@ -16,8 +16,10 @@
 //   D  per landmark row, exact top-k: one 128-bin histogram over the row's
 //      range, every key above the k-th best's bin taken, that bin's keys by
 //      rank (ties to the lower key id); then P = exp(S - max) in f16;
-//   V  V^T (f16, keys contiguous), loaded into registers at the head's start,
-//      replaces the scores in X;
+//   V  V rows (f16, one padded 144-byte row per key) replace the scores in
+//      X; E and G take V^T fragments from them with the transposing LDS read
+//      (four keys of one channel per lane and instruction), so an expert's
+//      scattered key rows are gathered eight bytes per lane at a time;
 //   E  V_L^T = V^T P^T on f16 MFMA, normalised by the row sums;
 //   E' R^T = Q_L Q^T per token tile: routes by a 16-lane argmax (ties to the
 //      lower landmark);
@@ -45,7 +47,8 @@ constexpr int TPW = (MAXNT + NWAVES - 1) / NWAVES;  // 16-token tiles per wave
 constexpr int VITEMS = (8 * (KPMAX / 2) + THREADS - 1) / THREADS;  // V pair items per thread
 constexpr int MMAX = 32, KMAX = 32;
 
-constexpr int VT_STRIDE = 464;      // bytes per V^T row (f16 keys)
+constexpr int QT_STRIDE = 464;      // bytes per Q^T row (bf16 tokens)
+constexpr int V_STRIDE = 144;       // bytes per V row (64 f16 channels + pad: rows 4 banks apart)
 constexpr int S_STRIDE = 212;       // floats per score row
 constexpr int H_STRIDE = 528;       // bytes per histogram / P row
 constexpr int BLIST = 16;           // boundary-bin entries ranked through a list
@@ -53,8 +56,9 @@ constexpr int TBM_WORDS = (16 * MAXNT + 63) / 32;  // key bitmap words (+1 for a
 static_assert(8 * BLIST + 4 * TBM_WORDS <= 512, "list and bitmap fit in a histogram row");
 constexpr int VLT_STRIDE = 80;      // bytes per V_L^T row (f16 landmarks)
 
-constexpr int X_BYTES = 64 * VT_STRIDE > MMAX * S_STRIDE * 4 ? 64 * VT_STRIDE : MMAX * S_STRIDE * 4;
-constexpr int OFF_X = 0;                          // S (phases C, D), then V^T (E, G)
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+constexpr int X_BYTES = cmax(cmax(64 * QT_STRIDE, MMAX * S_STRIDE * 4), KPMAX * V_STRIDE);
+constexpr int OFF_X = 0;                          // Q^T (B), S (C, D), then V rows (E, G)
 constexpr int OFF_H = OFF_X + X_BYTES;
 // H: histograms and P rows (D, E), then the head's K rows, bf16 and
 // chunk-swizzled like Q_L, for the expert tiles (G)
@@ -141,21 +145,36 @@ __device__ __forceinline__ void load_v(VRows& vr, Rsrc rows, int N, int tid) {
   }
 }
 
-__device__ __forceinline__ void store_vt(const VRows& vr, char* sm, int tid) {
+// V rows (f16) over X from the same items: each key's 8-channel chunk c as one
+// 16-byte store.
+__device__ __forceinline__ void store_v(const VRows& vr, char* sm, int tid) {
 #pragma unroll
   for (int i = 0; i < VITEMS; ++i) {
     const int id = tid + THREADS * i;
     const int c = id / (KPMAX / 2), p = id % (KPMAX / 2);
     if (c < 8) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const uint32_t a = (vr.v0[i][t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
-        const uint32_t b = (vr.v1[i][t >> 1] >> (16 * (t & 1))) & 0xFFFFu;
-        *lds<uint32_t>(sm, OFF_X + (8 * c + t) * VT_STRIDE + 4 * p) =
-            pk_f16(bf16_bits_to_f32(a), bf16_bits_to_f32(b));
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 x = h ? vr.v1[i] : vr.v0[i];
+        u32x4 f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          f[q] = pk_f16(__uint_as_float(x[q] << 16), __uint_as_float(x[q] & 0xFFFF0000u));
+        *lds<u32x4>(sm, OFF_X + (2 * p + h) * V_STRIDE + 16 * c) = f;
       }
     }
   }
+}
+
+// gfx950's transposing LDS read of 16-bit elements: in each 16-lane group,
+// lane s points at four consecutive elements (row s >> 2 of a 4 x 16 tile,
+// columns 4 (s & 3) ..), and lane t receives column t of the tile (rows
+// 0 .. 3), as an MFMA operand's four k values.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_tr16(const char* sm, int off) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(sm + off));
+  return __builtin_bit_cast(u32x2, v);
 }
 
 // Q^T (bf16, tokens contiguous) over X from the same register layout.
@@ -168,7 +187,7 @@ __device__ __forceinline__ void store_qt(const VRows& qr, char* sm, int tid) {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const uint32_t a = qr.v0[i][t >> 1], b = qr.v1[i][t >> 1];
-        *lds<uint32_t>(sm, OFF_X + (8 * c + t) * VT_STRIDE + 4 * p) =
+        *lds<uint32_t>(sm, OFF_X + (8 * c + t) * QT_STRIDE + 4 * p) =
             (t & 1) ? (a >> 16) | (b & 0xFFFF0000u) : (a & 0xFFFFu) | (b << 16);
       }
     }
@@ -266,7 +285,7 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
 #pragma unroll
       for (int ks = 0; ks < KPMAX / 32; ++ks) {
         if (ks < nks) {
-          const u32x4 a = *lds<u32x4>(sm, OFF_X + (16 * ct + c16) * VT_STRIDE + (32 * ks + 8 * g) * 2);
+          const u32x4 a = *lds<u32x4>(sm, OFF_X + (16 * ct + c16) * QT_STRIDE + (32 * ks + 8 * g) * 2);
           // B = W[tokens 32ks + 8g .. +7][landmark L]: one membership byte, two nibbles
           const uint32_t byte = (wb[ks >> 2] >> (8 * (ks & 3))) & 0xFFu;
           const u32x2 b01 = *lds<u32x2>(sm, OFF_LUT + (byte & 15u) * 8);
@@ -634,10 +653,10 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
       __syncthreads();
     }
 
-    // ---------------- V: V^T (f16) over the score region
+    // ---------------- V: V rows (f16) over the score region
     {
       FUSED_IDS;
-      store_vt(vr, sm, tid);
+      store_v(vr, sm, tid);
     }
     __syncthreads();
 
@@ -659,8 +678,13 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
         // the row sums of the same f16 weights: an all-ones A operand
         const u32x4 ones = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
         f32x4 acc = zero4(), tot = zero4();
+        // V^T[channels 16ct ..][keys 32ks + 8g ..]: lane (g, c16) points at key
+        // 32ks + 8g + (c16 >> 2) (+ 4), channels 16ct + 4 (c16 & 3) ..
+        const int va = OFF_X + (8 * g + (c16 >> 2)) * V_STRIDE + 32 * ct + 8 * (c16 & 3);
         for (int ks = 0; ks < KP / 32; ++ks) {
-          const u32x4 a = *lds<u32x4>(sm, OFF_X + (16 * ct + c16) * VT_STRIDE + (32 * ks + 8 * g) * 2);
+          const u32x2 lo = lds_tr16(sm, va + 32 * ks * V_STRIDE);
+          const u32x2 hi = lds_tr16(sm, va + (32 * ks + 4) * V_STRIDE);
+          const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
           const u32x4 b = *lds<u32x4>(sm, OFF_H + (16 * lt + c16) * H_STRIDE + (32 * ks + 8 * g) * 2);
           acc = mfma_f16(a, b, acc);
           tot = mfma_f16(ones, b, tot);
@@ -813,25 +837,19 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
           bl &= bl - 1u;
           const bool mine = ce == e;
           const u32x4 bpe = {mine ? bpr[0] : 0u, mine ? bpr[1] : 0u, mine ? bpr[2] : 0u, mine ? bpr[3] : 0u};
-          // key ids of this lane's routed slots {4g..4g+3, 16+4g..16+4g+3}
-          // (slots past k hold key 0, weighted 0)
-          const i32x4 kv0 = *lds<i32x4>(sm, OFF_IDX + (e * KMAX + 4 * g) * 4);
-          const i32x4 kv1 = *lds<i32x4>(sm, OFF_IDX + (e * KMAX + 16 + 4 * g) * 4);
-          // V_e^T gathered from V^T rows 16ct + c16: one address per key, the
-          // channel tile in the instruction offset, halves loaded in place
-          const _Float16* vk[8];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            vk[r] = reinterpret_cast<const _Float16*>(sm + OFF_X + c16 * VT_STRIDE + 2 * kv0[r]);
-            vk[4 + r] = reinterpret_cast<const _Float16*>(sm + OFF_X + c16 * VT_STRIDE + 2 * kv1[r]);
-          }
+          // V_e^T fragments by transposing reads of the expert's V rows: lane
+          // (g, c16) points at the row of slot 4g + (c16 >> 2) (and 16 + 4g +
+          // ..), channels 16ct + 4 (c16 & 3) .., and receives channel 16ct +
+          // c16 of slots 4g .. 4g + 3 (and 16 + 4g ..).  (Slots past k hold
+          // key 0, weighted 0.)
+          const int k0 = *lds<int>(sm, OFF_IDX + (e * KMAX + 4 * g + (c16 >> 2)) * 4);
+          const int k1 = *lds<int>(sm, OFF_IDX + (e * KMAX + 16 + 4 * g + (c16 >> 2)) * 4);
+          const int a0 = OFF_X + k0 * V_STRIDE + 8 * (c16 & 3);
+          const int a1 = OFF_X + k1 * V_STRIDE + 8 * (c16 & 3);
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct) {
-            constexpr int CT = 16 * VT_STRIDE / 2;  // halves per channel tile
-            f16x8_t ave;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) ave[q] = vk[q][CT * ct];
-            acc[ct] = mfma_f16(__builtin_bit_cast(u32x4, ave), bpe, acc[ct]);
+            const u32x2 lo = lds_tr16(sm, a0 + 32 * ct), hi = lds_tr16(sm, a1 + 32 * ct);
+            acc[ct] = mfma_f16(u32x4{lo[0], lo[1], hi[0], hi[1]}, bpe, acc[ct]);
           }
         }
         // lanes c16 and c16 ^ 8 trade their odd channel tiles, so that each
