@@ -8,8 +8,9 @@
 // to its P workgroups in a snake, largest pass count first.  Per workgroup:
 //   * load its experts' table (query range, key ids, first 64 query ids)
 //     and the head's Q_L (bf16 hi + lo) and V_L^T (f16) into LDS once;
-//   * per expert: its k key rows (bf16) and value rows (f16, transposed) sit
-//     in LDS, shared by the four waves.  While one expert is computed the
+//   * per expert: its k key rows (bf16) and value rows (f16) sit in LDS,
+//     shared by the four waves; V^T fragments come from the value rows by the
+//     transposing LDS read.  While one expert is computed the
 //     next one's rows (and the Q rows of its first 64 queries) are already
 //     loading into registers; the expert's output stores are issued only
 //     after those rows have been waited for, since stores and loads drain
@@ -37,7 +38,7 @@ namespace att {
 
 constexpr int TQ = 64;    // queries per pass (16 per wave)
 constexpr int EC = 64;    // expert slots per LDS chunk
-constexpr int EVT_STRIDE = EC * 2 + 16;
+constexpr int EV_STRIDE = 64 * 2 + 16;  // bytes per staged V row (f16 channels + pad)
 constexpr int MAXM = 256;
 
 struct Args {
@@ -71,7 +72,7 @@ struct Lay {
     off_vlt = off_qll + mp * 128;
     off_ke = off_vlt + 64 * vlt_stride;
     off_vet = off_ke + EC * 128;
-    off_tab = off_vet + 64 * EVT_STRIDE;
+    off_tab = off_vet + EC * EV_STRIDE;
     off_elist = off_tab + ew * ts * 4;
     off_offs = off_elist + (ew + 1) * 4;  // the head's m + 1 expert offsets
     bytes = off_offs + (m + 1) * 4;
@@ -283,9 +284,10 @@ void attend_bf16_kernel(Args a) {
   __syncthreads();  // the table is complete
 
   // gather items of this thread: K rows (slots tid>>3 and +32, chunk tid&7)
-  // and the V slot pair (2p, 2p+1) of chunk c
+  // and the V slot pair (2p, 2p+1) of chunk c (p = tid>>3, c = tid&7: eight
+  // threads read one 128-byte row)
   const int ksl = tid >> 3, kc = tid & 7;
-  const int vp = tid & 31, vc = tid >> 5;
+  const int vp = tid >> 3, vc = tid & 7;
   struct Rows {
     u32x4 k0, k1, v0, v1, q0r, q1r;
   };
@@ -310,11 +312,13 @@ void attend_bf16_kernel(Args a) {
     *reinterpret_cast<u32x4*>(sm + L.off_ke + rc(ksl, kc)) = r.k0;
     *reinterpret_cast<u32x4*>(sm + L.off_ke + rc(ksl + 32, kc)) = r.k1;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint32_t x0 = (r.v0[q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
-      const uint32_t x1 = (r.v1[q >> 1] >> (16 * (q & 1))) & 0xFFFFu;
-      *reinterpret_cast<uint32_t*>(sm + L.off_vet + (8 * vc + q) * EVT_STRIDE + 4 * vp) =
-          pk_f16(bf16_bits_to_f32(x0), bf16_bits_to_f32(x1));
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 x = h ? r.v1 : r.v0;
+      u32x4 f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        f[q] = pk_f16(__uint_as_float(x[q] << 16), __uint_as_float(x[q] & 0xFFFF0000u));
+      *reinterpret_cast<u32x4*>(sm + L.off_vet + (2 * vp + h) * EV_STRIDE + 16 * vc) = f;
     }
   };
 
@@ -378,12 +382,15 @@ void attend_bf16_kernel(Args a) {
           if (s0 + 32 * hs + 16 * h + 4 * g + r >= k) x[4 * h + r] = -INFINITY;
     }
   };
+  // V^T[ch 16ct + c16][slots 32hs + 4g .., 32hs + 16 + 4g ..] by transposing
+  // reads: lane points at slot 32hs + 4g + (c16 >> 2) (+ 16), channels
+  // 16ct + 4 (c16 & 3) ..
   auto routed_av = [&](int hs, u32x4 (&av)[4]) {
+    const char* vr = sm + L.off_vet + (32 * hs + 4 * g + (c16 >> 2)) * EV_STRIDE + 8 * (c16 & 3);
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
-      const char* vr = sm + L.off_vet + (16 * ct + c16) * EVT_STRIDE;
-      const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vr + (32 * hs + 4 * g) * 2);
-      const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vr + (32 * hs + 16 + 4 * g) * 2);
+      const u32x2 lo2 = lds_tr16(vr + 32 * ct);
+      const u32x2 hi2 = lds_tr16(vr + 16 * EV_STRIDE + 32 * ct);
       av[ct] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
     }
   };

@@ -166,17 +166,6 @@ __device__ __forceinline__ void store_v(const VRows& vr, char* sm, int tid) {
   }
 }
 
-// gfx950's transposing LDS read of 16-bit elements: in each 16-lane group,
-// lane s points at four consecutive elements (row s >> 2 of a 4 x 16 tile,
-// columns 4 (s & 3) ..), and lane t receives column t of the tile (rows
-// 0 .. 3), as an MFMA operand's four k values.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ u32x2 lds_tr16(const char* sm, int off) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(sm + off));
-  return __builtin_bit_cast(u32x2, v);
-}
-
 // Q^T (bf16, tokens contiguous) over X from the same register layout.
 __device__ __forceinline__ void store_qt(const VRows& qr, char* sm, int tid) {
 #pragma unroll
@@ -682,8 +671,8 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
         // 32ks + 8g + (c16 >> 2) (+ 4), channels 16ct + 4 (c16 & 3) ..
         const int va = OFF_X + (8 * g + (c16 >> 2)) * V_STRIDE + 32 * ct + 8 * (c16 & 3);
         for (int ks = 0; ks < KP / 32; ++ks) {
-          const u32x2 lo = lds_tr16(sm, va + 32 * ks * V_STRIDE);
-          const u32x2 hi = lds_tr16(sm, va + (32 * ks + 4) * V_STRIDE);
+          const u32x2 lo = lds_tr16(sm + va + 32 * ks * V_STRIDE);
+          const u32x2 hi = lds_tr16(sm + va + (32 * ks + 4) * V_STRIDE);
           const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
           const u32x4 b = *lds<u32x4>(sm, OFF_H + (16 * lt + c16) * H_STRIDE + (32 * ks + 8 * g) * 2);
           acc = mfma_f16(a, b, acc);
@@ -848,7 +837,7 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
           const int a1 = OFF_X + k1 * V_STRIDE + 8 * (c16 & 3);
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct) {
-            const u32x2 lo = lds_tr16(sm, a0 + 32 * ct), hi = lds_tr16(sm, a1 + 32 * ct);
+            const u32x2 lo = lds_tr16(sm + a0 + 32 * ct), hi = lds_tr16(sm + a1 + 32 * ct);
             acc[ct] = mfma_f16(u32x4{lo[0], lo[1], hi[0], hi[1]}, bpe, acc[ct]);
           }
         }

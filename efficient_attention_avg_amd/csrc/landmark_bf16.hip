@@ -12,8 +12,9 @@
 // with K rows loaded straight into the A operand and Q_L split hi + lo
 // (fp32-accurate).  Phases, separated by workgroup barriers:
 //   V  values: per wave, an online softmax of its keys' scores folded into
-//      V_L^T = V^T P^T (f16 MFMA; V staged transposed in the wave's own LDS
-//      slot; the running maximum is only raised when a score exceeds it by
+//      V_L^T = V^T P^T (f16 MFMA; the block's V rows staged as f16 in the
+//      wave's own LDS slot and read back as V^T fragments by the transposing
+//      LDS read; the running maximum is only raised when a score exceeds it by
 //      more than 2^8 in weight, so most blocks skip the rescale); the four
 //      partial results merge by log-sum-exp into V_L.  For k <= 128 the
 //      same scores are counted into each row's 256-bin histogram as they
@@ -48,8 +49,8 @@ constexpr int KB = 64;                  // keys per block
 constexpr int NW = 4;                   // waves per workgroup
 constexpr int TL = 2;                   // 16-row MFMA tiles per workgroup
 constexpr int ROWS = 16 * TL;           // landmark rows per workgroup
-constexpr int VT_STRIDE = KB * 2 + 16;  // bytes per V^T row: 64 f16 keys + pad
-constexpr int VT_BYTES = 64 * VT_STRIDE;
+constexpr int V_STRIDE = 64 * 2 + 16;  // bytes per staged V row: 64 f16 channels + pad
+constexpr int VT_BYTES = KB * V_STRIDE;  // a wave's staging slot: one block's V rows
 constexpr int HIST_STRIDE = 1040;       // one row's 256 32-bit bins + pad (rows 4 banks apart)
 constexpr int SPARE_BIN = 256;          // pad word: counts the keys past N of a ragged block
 constexpr int BITMAP_MAX_N = 8192;      // keys whose bitmap fits in a histogram row
@@ -154,19 +155,21 @@ __device__ __forceinline__ void load_v(VRegs& vr, Rsrc Vh, int blk, int N, int l
   }
 }
 
-// V^T (f16) into the wave's slot: row = channel, 64 keys per row.
-__device__ __forceinline__ void store_vt(const VRegs& vr, char* vt, int lane) {
+// The block's V rows (f16) into the wave's slot: row = key, chunk c of a
+// key as one 16-byte store.  (The products read V^T fragments from them with
+// the transposing LDS read.)
+__device__ __forceinline__ void store_v(const VRegs& vr, char* vt, int lane) {
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int it = lane + 64 * j, p = it >> 3, c = it & 7;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      float f[4];
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 x = vr.v[j][i];
+      u32x4 f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        f[i] = bf16_bits_to_f32((vr.v[j][i][t >> 1] >> (16 * (t & 1))) & 0xFFFFu);
-      *reinterpret_cast<u32x2*>(vt + (8 * c + t) * VT_STRIDE + 8 * p) =
-          u32x2{pk_f16(f[0], f[1]), pk_f16(f[2], f[3])};
+      for (int q = 0; q < 4; ++q)
+        f[q] = pk_f16(__uint_as_float(x[q] << 16), __uint_as_float(x[q] & 0xFFFF0000u));
+      *reinterpret_cast<u32x4*>(vt + (4 * p + i) * V_STRIDE + 16 * c) = f;
     }
   }
 }
@@ -602,19 +605,21 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
       constexpr bool LAST = decltype(last_c)::value;
       // the V registers are free once stored and the K registers once the
       // scores are out: the next block's loads go out right after each
-      store_vt(vr, vt, lane);
+      store_v(vr, vt, lane);
       if (blk + 1 < vb1) load_v(vr, Vh, blk + 1, N, lane);
       group_sync();
       // the block's V^T A operands, shared by both row tiles:
-      // V^T[channel 16ct + c16][keys 32sp + 4g .., 32sp + 16 + 4g ..]
+      // V^T[channel 16ct + c16][keys 32sp + 4g .., 32sp + 16 + 4g ..], by
+      // transposing reads (lane points at key 32sp + 4g + (c16 >> 2) (+ 16),
+      // channels 16ct + 4 (c16 & 3) ..)
       u32x4 av[4][2];
+      const char* vtl = vt + (4 * g + (c16 >> 2)) * V_STRIDE + 8 * (c16 & 3);
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
-        const char* vrow = vt + (16 * ct + c16) * VT_STRIDE;
 #pragma unroll
         for (int sp = 0; sp < 2; ++sp) {
-          const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vrow + (32 * sp + 4 * g) * 2);
-          const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vrow + (32 * sp + 16 + 4 * g) * 2);
+          const u32x2 lo2 = lds_tr16(vtl + 32 * sp * V_STRIDE + 32 * ct);
+          const u32x2 hi2 = lds_tr16(vtl + (32 * sp + 16) * V_STRIDE + 32 * ct);
           av[ct][sp] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
         }
       }

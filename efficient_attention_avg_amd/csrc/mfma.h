@@ -33,6 +33,18 @@ __device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// gfx950's transposing LDS read of 16-bit elements: in each 16-lane group,
+// lane s points at four consecutive elements (row s >> 2 of a 4 x 16 tile,
+// columns 4 (s & 3) ..), and lane t receives column t of the tile (rows
+// 0 .. 3), i.e. four k values of an MFMA operand.  Used to read V^T
+// fragments straight from V rows kept in LDS.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_tr16(const char* p) {
+  const s16x4 v =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // Byte offset of 16-byte chunk `c` (0..7) of a 128-byte row in LDS,
 // XOR-swizzled so that 16 consecutive rows read at one logical chunk spread
 // over the banks.
