@@ -47,8 +47,7 @@ constexpr int TPW = (MAXNT + NWAVES - 1) / NWAVES;  // 16-token tiles per wave
 constexpr int VITEMS = (8 * (KPMAX / 2) + THREADS - 1) / THREADS;  // V pair items per thread
 constexpr int MMAX = 32, KMAX = 32;
 
-constexpr int QT_STRIDE = 464;      // bytes per Q^T row (bf16 tokens)
-constexpr int V_STRIDE = 144;       // bytes per V row (64 f16 channels + pad: rows 4 banks apart)
+constexpr int V_STRIDE = 144;       // bytes per Q / V row (64 16-bit channels + pad: rows 4 banks apart)
 constexpr int S_STRIDE = 212;       // floats per score row
 constexpr int H_STRIDE = 528;       // bytes per histogram / P row
 constexpr int BLIST = 16;           // boundary-bin entries ranked through a list
@@ -57,8 +56,8 @@ static_assert(8 * BLIST + 4 * TBM_WORDS <= 512, "list and bitmap fit in a histog
 constexpr int VLT_STRIDE = 80;      // bytes per V_L^T row (f16 landmarks)
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
-constexpr int X_BYTES = cmax(cmax(64 * QT_STRIDE, MMAX * S_STRIDE * 4), KPMAX * V_STRIDE);
-constexpr int OFF_X = 0;                          // Q^T (B), S (C, D), then V rows (E, G)
+constexpr int X_BYTES = cmax(MMAX * S_STRIDE * 4, KPMAX * V_STRIDE);
+constexpr int OFF_X = 0;                          // Q rows (B), S (C, D), then V rows (E, G)
 constexpr int OFF_H = OFF_X + X_BYTES;
 // H: histograms and P rows (D, E), then the head's K rows, bf16 and
 // chunk-swizzled like Q_L, for the expert tiles (G)
@@ -128,8 +127,9 @@ __device__ __forceinline__ void load_ql(char* sm, u32x4 (&qlh)[2][2], u32x4 (&ql
     }
 }
 
-// The head's V rows for the transposed copy: key pairs (2p, 2p+1) of 8-channel
-// chunk c, items tid + THREADS i (c = item / 112, p = item % 112).
+// A head's Q or V rows as items: key pairs (2p, 2p+1) of 8-channel chunk c,
+// items tid + THREADS i (c = item % 8, p = item / 8: eight threads read one
+// 128-byte row, and their 16-byte LDS stores spread over the banks).
 struct VRows {
   u32x4 v0[VITEMS], v1[VITEMS];
 };
@@ -138,10 +138,10 @@ __device__ __forceinline__ void load_v(VRows& vr, Rsrc rows, int N, int tid) {
 #pragma unroll
   for (int i = 0; i < VITEMS; ++i) {
     const int id = tid + THREADS * i;
-    const int c = id / (KPMAX / 2), p = id % (KPMAX / 2);
+    const int c = id & 7, p = id >> 3;
     const int j0 = 2 * p, j1 = 2 * p + 1;
-    vr.v0[i] = ld16(rows, c < 8 && j0 < N ? j0 * 128 + c * 16 : PAST);
-    vr.v1[i] = ld16(rows, c < 8 && j1 < N ? j1 * 128 + c * 16 : PAST);
+    vr.v0[i] = ld16(rows, p < KPMAX / 2 && j0 < N ? j0 * 128 + c * 16 : PAST);
+    vr.v1[i] = ld16(rows, p < KPMAX / 2 && j1 < N ? j1 * 128 + c * 16 : PAST);
   }
 }
 
@@ -151,8 +151,8 @@ __device__ __forceinline__ void store_v(const VRows& vr, char* sm, int tid) {
 #pragma unroll
   for (int i = 0; i < VITEMS; ++i) {
     const int id = tid + THREADS * i;
-    const int c = id / (KPMAX / 2), p = id % (KPMAX / 2);
-    if (c < 8) {
+    const int c = id & 7, p = id >> 3;
+    if (p < KPMAX / 2) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const u32x4 x = h ? vr.v1[i] : vr.v0[i];
@@ -166,19 +166,17 @@ __device__ __forceinline__ void store_v(const VRows& vr, char* sm, int tid) {
   }
 }
 
-// Q^T (bf16, tokens contiguous) over X from the same register layout.
-__device__ __forceinline__ void store_qt(const VRows& qr, char* sm, int tid) {
+// Q rows (bf16, as loaded) over X from the same register layout: each token's
+// 8-channel chunk c as one 16-byte store.  (Pooling reads Q^T fragments from
+// them with the transposing LDS read.)
+__device__ __forceinline__ void store_q(const VRows& qr, char* sm, int tid) {
 #pragma unroll
   for (int i = 0; i < VITEMS; ++i) {
     const int id = tid + THREADS * i;
-    const int c = id / (KPMAX / 2), p = id % (KPMAX / 2);
-    if (c < 8) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const uint32_t a = qr.v0[i][t >> 1], b = qr.v1[i][t >> 1];
-        *lds<uint32_t>(sm, OFF_X + (8 * c + t) * QT_STRIDE + 4 * p) =
-            (t & 1) ? (a >> 16) | (b & 0xFFFF0000u) : (a & 0xFFFFu) | (b << 16);
-      }
+    const int c = id & 7, p = id >> 3;
+    if (p < KPMAX / 2) {
+      *lds<u32x4>(sm, OFF_X + (2 * p) * V_STRIDE + 16 * c) = qr.v0[i];
+      *lds<u32x4>(sm, OFF_X + (2 * p + 1) * V_STRIDE + 16 * c) = qr.v1[i];
     }
   }
 }
@@ -250,9 +248,9 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
     const uint16_t* Qh = Q + bh * head_elems;
     const Rsrc rQ = head_rows(Qh, N), rK = head_rows(K + bh * head_elems, N);
     __syncthreads();  // the previous head is done with LDS
-    store_qt(qr, sm, tid);
+    store_q(qr, sm, tid);
     if (tid < MMAX * 8) *lds<uint32_t>(sm, OFF_BM + tid * 4) = 0u;
-    // C's K rows, issued after the Q^T store so that its wait does not cover them
+    // C's K rows, issued after the Q row store so that its wait does not cover them
     u32x4 ka[TPW][2];
 #pragma unroll
     for (int j = 0; j < TPW; ++j) {
@@ -271,10 +269,15 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
       f32x4 acc = zero4();
       const u32x2 wb = *lds<u32x2>(sm, OFF_WB + (L * 4 + g) * 8);
       const int nks = KP / 32 + opaque_zero();  // per-step tests made here, not held
+      // Q^T[channels 16ct ..][tokens 32ks + 8g ..]: lane (g, c16) points at
+      // token 32ks + 8g + (c16 >> 2) (+ 4), channels 16ct + 4 (c16 & 3) ..
+      const int qa = OFF_X + (8 * g + (c16 >> 2)) * V_STRIDE + 32 * ct + 8 * (c16 & 3);
 #pragma unroll
       for (int ks = 0; ks < KPMAX / 32; ++ks) {
         if (ks < nks) {
-          const u32x4 a = *lds<u32x4>(sm, OFF_X + (16 * ct + c16) * QT_STRIDE + (32 * ks + 8 * g) * 2);
+          const u32x2 lo = lds_tr16(sm + qa + 32 * ks * V_STRIDE);
+          const u32x2 hi = lds_tr16(sm + qa + (32 * ks + 4) * V_STRIDE);
+          const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
           // B = W[tokens 32ks + 8g .. +7][landmark L]: one membership byte, two nibbles
           const uint32_t byte = (wb[ks >> 2] >> (8 * (ks & 3))) & 0xFFu;
           const u32x2 b01 = *lds<u32x2>(sm, OFF_LUT + (byte & 15u) * 8);
