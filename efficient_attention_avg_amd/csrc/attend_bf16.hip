@@ -566,7 +566,9 @@ hipError_t launch_attend_bf16(const void* Q, const void* K, const void* V, const
   while (att::Lay(s.m, s.k, parts).bytes > 160 * 1024 && parts < s.m) ++parts;
   const att::Lay L(s.m, s.k, parts);
   if (L.bytes > 160 * 1024) return hipErrorInvalidValue;
-  if (const hipError_t e = allow_lds((const void*)att::attend_bf16_kernel, 160 * 1024); e != hipSuccess)
+  static std::atomic<unsigned long long> lds_set;
+  if (const hipError_t e = allow_lds((const void*)att::attend_bf16_kernel, 160 * 1024, lds_set);
+      e != hipSuccess)
     return e;
   if (s.s > 1 && !partial) return hipErrorInvalidValue;
   float* part = s.s > 1 ? (float*)partial : out;

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace mita {
 
 struct Shape {
@@ -17,12 +19,21 @@ struct Shape {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Lets `kernel` take up to `bytes` of dynamic LDS.  Called before every launch
-// that needs more than the default: the attribute belongs to the current
-// device, and a per-launch call keeps the library free of process-wide flags
-// (two threads or two devices never depend on who launched first).
-inline hipError_t allow_lds(const void* kernel, int bytes) {
-  return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+// Lets `kernel` take up to `bytes` of dynamic LDS on the current device, once
+// per (kernel, device): `done` (one per kernel and byte count, at its launch
+// site) holds a bit per device id below 64, set after the attribute call
+// succeeded there.  The call costs about 5 us of host time, which on every
+// launch left the GPU idle between dependent kernels.  Threads racing on a
+// device's first launch both make the same idempotent call; devices with ids
+// of 64 and up make it on every launch.
+inline hipError_t allow_lds(const void* kernel, int bytes, std::atomic<unsigned long long>& done) {
+  int dev = 0;
+  if (const hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  const unsigned long long bit = dev >= 0 && dev < 64 ? 1ull << dev : 0ull;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  const hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
 }
 
 // step a1: landmark pooling

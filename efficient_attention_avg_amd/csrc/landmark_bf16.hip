@@ -1235,7 +1235,9 @@ hipError_t launch_landmark_bf16(const float* ql, const void* K, const void* V, i
   const size_t lds = lmk::lds_bytes(a.cap);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   auto kernel = fuse_h ? lmk::landmark_kernel<true> : lmk::landmark_kernel<false>;
-  if (const hipError_t e = allow_lds((const void*)kernel, 160 * 1024); e != hipSuccess) return e;
+  static std::atomic<unsigned long long> lds_set[2];
+  if (const hipError_t e = allow_lds((const void*)kernel, 160 * 1024, lds_set[fuse_h]); e != hipSuccess)
+    return e;
   const int grid = ((s.BH + 7) / 8) * 8 * a.tiles * nch;
   kernel<<<grid, 64 * lmk::NW, lds, st>>>(a);
   if (nch == 1) return hipGetLastError();

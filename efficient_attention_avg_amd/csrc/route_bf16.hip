@@ -326,10 +326,13 @@ hipError_t launch_route_bf16(const void* Q, const float* ql, int32_t* route, int
   const size_t lds = route_lds(s, qc, R);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   // the smallest list that holds s routes
-  auto kernel = s.s == 1 ? rt::route_bf16_kernel<1>
-                : s.s == 2 ? rt::route_bf16_kernel<2>
-                : s.s <= 4 ? rt::route_bf16_kernel<4> : rt::route_bf16_kernel<8>;
-  if (const hipError_t e = allow_lds((const void*)kernel, 160 * 1024); e != hipSuccess) return e;
+  const int form = s.s == 1 ? 0 : s.s == 2 ? 1 : s.s <= 4 ? 2 : 3;
+  auto kernel = form == 0 ? rt::route_bf16_kernel<1>
+                : form == 1 ? rt::route_bf16_kernel<2>
+                : form == 2 ? rt::route_bf16_kernel<4> : rt::route_bf16_kernel<8>;
+  static std::atomic<unsigned long long> lds_set[4];
+  if (const hipError_t e = allow_lds((const void*)kernel, 160 * 1024, lds_set[form]); e != hipSuccess)
+    return e;
   dim3 grid(nchunks, s.BH);
   kernel<<<grid, 64 * rt::RW, lds, st>>>((const uint16_t*)Q, ql, route, chist, s.N, s.m, nruns,
                                          qc, R, s.s);
@@ -342,7 +345,9 @@ hipError_t launch_group_bf16(const int32_t* route, const int32_t* chist, int32_t
   route_chunking(s, qc, nchunks, R, nruns);
   const size_t lds = ((size_t)nruns * s.m + s.m) * 4;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  if (const hipError_t e = allow_lds((const void*)rt::group_bf16_kernel, 160 * 1024); e != hipSuccess)
+  static std::atomic<unsigned long long> lds_set;
+  if (const hipError_t e = allow_lds((const void*)rt::group_bf16_kernel, 160 * 1024, lds_set);
+      e != hipSuccess)
     return e;
   // the sort runs over the N * s (query, rank) items, R * s of them per run
   rt::group_bf16_kernel<<<s.BH, 1024, lds, st>>>(route, chist, counts, offsets, perm, s.N * s.s,
