@@ -731,11 +731,14 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
           ak[st][1] = *lds<u32x4>(sm, OFF_H + rc(key, g + 4));
         }
       };
-      // lane masks of this lane's valid routed slots {4g+r, 16+4g+r}
-      uint32_t slot_ok = 0;
+      // whether this lane's routed slots 4g + r and 16 + 4g + r hold keys
+      // (lane masks, fixed for the head: computed once, not per expert)
+      bool ok0[4], ok1[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        slot_ok |= (4 * g + r < k ? 1u : 0u) << r | (16 + 4 * g + r < k ? 1u : 0u) << (4 + r);
+      for (int r = 0; r < 4; ++r) {
+        ok0[r] = 4 * g + r < k;
+        ok1[r] = 16 + 4 * g + r < k;
+      }
       for (int tile = w; tile < nqt; tile += NWAVES) {
         const int p0 = 16 * tile, p = p0 + c16;
         const bool live = p < N;  // columns past N compute on the tile's first query
@@ -781,16 +784,13 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
             c = mfma_bf16(ak[st][1], bq1, c);
             lr[st] = c;
           }
-          // the expert's columns take its valid slots' logits (bit selects;
-          // the other slots stay -inf)
-          const uint32_t take = ce == e ? slot_ok : 0u;
+          // the expert's columns take its valid slots' logits (the other
+          // slots stay -inf)
+          const bool mine = ce == e;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const uint32_t m0 = 0u - (take >> r & 1u), m1 = 0u - (take >> (4 + r) & 1u);
-            x[8 + r] = __uint_as_float((__float_as_uint(lr[0][r] * kLogitScale) & m0) |
-                                       (__float_as_uint(x[8 + r]) & ~m0));
-            x[12 + r] = __uint_as_float((__float_as_uint(lr[1][r] * kLogitScale) & m1) |
-                                        (__float_as_uint(x[12 + r]) & ~m1));
+            x[8 + r] = mine && ok0[r] ? lr[0][r] * kLogitScale : x[8 + r];
+            x[12 + r] = mine && ok1[r] ? lr[1][r] * kLogitScale : x[12 + r];
           }
         }
         float mx = x[0];

@@ -8,9 +8,11 @@
 
 namespace mita {
 
+// (bound_ctrl set: a lane whose source is past the row's end reads 0, so no
+// "old" value has to be materialised in the destination first)
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int v) {
-  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
