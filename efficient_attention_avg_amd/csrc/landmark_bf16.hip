@@ -255,8 +255,9 @@ __device__ __forceinline__ bool better(float va, int ka, float vb, int kb) {
   return va > vb || (va == vb && ka < kb);
 }
 
-// Number of the n entries at `list` (interleaved score, key) that rank
-// before (v, key).  The 16 lanes of a group read the same entries.
+// Number of the n entries at `list` (interleaved score, key: a row's
+// candidate buffer or boundary list) that rank before (v, key).  The 16 lanes
+// of a group read the same entries.
 __device__ __forceinline__ int rank_in_list(const float* list, int n, float v, int key) {
   int r = 0;
   int j = 0;
@@ -265,21 +266,6 @@ __device__ __forceinline__ int rank_in_list(const float* list, int n, float v, i
     r += better(e.x, __float_as_int(e.y), v, key) + better(e.z, __float_as_int(e.w), v, key);
   }
   if (j < n) r += better(list[2 * j], __float_as_int(list[2 * j + 1]), v, key);
-  return r;
-}
-
-// Same over the row's buffer (separate score and key arrays).
-__device__ __forceinline__ int rank_in(const float* vals, const int* keys, int n, float v,
-                                       int key) {
-  int r = 0;
-  int j = 0;
-  for (; j + 4 <= n; j += 4) {
-    const float4 vv = *reinterpret_cast<const float4*>(vals + j);
-    const int4 kk = *reinterpret_cast<const int4*>(keys + j);
-    r += better(vv.x, kk.x, v, key) + better(vv.y, kk.y, v, key) + better(vv.z, kk.z, v, key) +
-         better(vv.w, kk.w, v, key);
-  }
-  for (; j < n; ++j) r += better(vals[j], keys[j], v, key);
   return r;
 }
 
@@ -294,8 +280,7 @@ __device__ __forceinline__ void group_sync() {
 // entries t, t + 16, ...
 __device__ void row_cut(char* sm, const Args& a, int kk, int lr, bool work, int t, int g) {
   RowState* rs = reinterpret_cast<RowState*>(sm + OFF_ROW) + lr;
-  float* vals = reinterpret_cast<float*>(sm + OFF_UNION + (size_t)lr * a.cap * 8);
-  int* keys = reinterpret_cast<int*>(vals + a.cap);
+  float* buf = reinterpret_cast<float*>(sm + OFF_UNION + (size_t)lr * a.cap * 8);  // (score, key)
   const int cnt = work ? rs->cnt : 0;
   uint32_t keep = 0u;
   float tv = -INFINITY;
@@ -303,9 +288,10 @@ __device__ void row_cut(char* sm, const Args& a, int kk, int lr, bool work, int 
   for (int u = 0; 16 * u < cnt; ++u) {
     const int e = t + 16 * u;
     if (e < cnt) {
-      const float v = vals[e];
-      const int key = keys[e];
-      const int r = rank_in(vals, keys, cnt, v, key);
+      const float2 ev = *reinterpret_cast<const float2*>(buf + 2 * e);
+      const float v = ev.x;
+      const int key = __float_as_int(ev.y);
+      const int r = rank_in_list(buf, cnt, v, key);
       keep |= (r < kk ? 1u : 0u) << u;
       if (r == kk - 1) {
         tv = v;
@@ -324,14 +310,10 @@ __device__ void row_cut(char* sm, const Args& a, int kk, int lr, bool work, int 
   for (int u = 0; 16 * u < cnt; ++u) {
     const int e = t + 16 * u;
     const bool kp = e < cnt && (keep >> u & 1u);
-    const float v = kp ? vals[e] : 0.f;
-    const int key = kp ? keys[e] : 0;
+    const float2 ev = kp ? *reinterpret_cast<const float2*>(buf + 2 * e) : make_float2(0.f, 0.f);
     const uint32_t gm = g16_ballot(kp, g);
     group_sync();
-    if (kp) {
-      vals[run + __popc(gm & below)] = v;
-      keys[run + __popc(gm & below)] = key;
-    }
+    if (kp) *reinterpret_cast<float2*>(buf + 2 * (run + __popc(gm & below))) = ev;
     run += __popc(gm);
   }
   if (work && t == 0) {
@@ -347,8 +329,7 @@ __device__ void row_cut(char* sm, const Args& a, int kk, int lr, bool work, int 
 __device__ void row_final(char* sm, const Args& a, const Chunk& ch, int lr, bool work, int t,
                           int g, int32_t* out, float* outs) {
   RowState* rs = reinterpret_cast<RowState*>(sm + OFF_ROW) + lr;
-  float* vals = reinterpret_cast<float*>(sm + OFF_UNION + (size_t)lr * a.cap * 8);
-  int* keys = reinterpret_cast<int*>(vals + a.cap);
+  float* buf = reinterpret_cast<float*>(sm + OFF_UNION + (size_t)lr * a.cap * 8);  // (score, key)
   float* list = reinterpret_cast<float*>(sm + OFF_HIST + lr * HIST_STRIDE);
   const int cnt = work ? rs->cnt : 0;
   const float A = rs->A, B = rs->B;
@@ -364,17 +345,15 @@ __device__ void row_final(char* sm, const Args& a, const Chunk& ch, int lr, bool
   for (int u = 0; 16 * u < cnt; ++u) {
     const int e = t + 16 * u;
     bool inb = false;
+    float2 ev = make_float2(0.f, 0.f);
     if (e < cnt) {
-      const bool isup = __builtin_fmaf(vals[e], A, B) >= upthr;
+      ev = *reinterpret_cast<const float2*>(buf + 2 * e);
+      const bool isup = __builtin_fmaf(ev.x, A, B) >= upthr;
       up |= (isup ? 1u : 0u) << u;
       inb = !isup;
     }
     const uint32_t gm = g16_ballot(inb, g);
-    if (listed && inb) {
-      const int pos = run + __popc(gm & below);
-      list[2 * pos] = vals[e];
-      list[2 * pos + 1] = __int_as_float(keys[e]);
-    }
+    if (listed && inb) *reinterpret_cast<float2*>(list + 2 * (run + __popc(gm & below))) = ev;
     run += __popc(gm);
   }
   group_sync();
@@ -404,9 +383,10 @@ __device__ void row_final(char* sm, const Args& a, const Chunk& ch, int lr, bool
     for (int u = 0; 16 * u < cnt; ++u) {
       const int e = t + 16 * u;
       if (e < cnt && !(up >> u & 1u)) {
-        const float v = vals[e];
-        const int key = keys[e];
-        const int r = listed ? rank_in_list(list, nb, v, key) : rank_in(vals, keys, cnt, v, key) - above;
+        const float2 ev = *reinterpret_cast<const float2*>(buf + 2 * e);
+        const float v = ev.x;
+        const int key = __float_as_int(ev.y);
+        const int r = listed ? rank_in_list(list, nb, v, key) : rank_in_list(buf, cnt, v, key) - above;
         take |= (r < need ? 1u : 0u) << u;
       }
     }
@@ -421,8 +401,10 @@ __device__ void row_final(char* sm, const Args& a, const Chunk& ch, int lr, bool
     group_sync();
     for (int u = 0; 16 * u < cnt; ++u) {
       const int e = t + 16 * u;
-      if (e < cnt && (take >> u & 1u))
-        atomicOr(&bm[(keys[e] - kb) >> 5], 1u << ((keys[e] - kb) & 31));
+      if (e < cnt && (take >> u & 1u)) {
+        const int key = __float_as_int(buf[2 * e + 1]);
+        atomicOr(&bm[(key - kb) >> 5], 1u << ((key - kb) & 31));
+      }
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -452,7 +434,10 @@ __device__ void row_final(char* sm, const Args& a, const Chunk& ch, int lr, bool
       };
       for (int u = 0; 16 * u < cnt; ++u) {
         const int e = t + 16 * u;
-        if (e < cnt && (take >> u & 1u)) emit(keys[e], vals[e]);
+        if (e < cnt && (take >> u & 1u)) {
+          const float2 ev = *reinterpret_cast<const float2*>(buf + 2 * e);
+          emit(__float_as_int(ev.y), ev.x);
+        }
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -904,13 +889,12 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
         for (int r = 0; r < 4; ++r) vb |= (key_of(blk, kt, g, r) < N ? 1u : 0u) << (4 * kt + r);
       return vb;
     };
-    // appends the block's scores of tile tl that are in the boundary bin or
-    // above (and, with BOUNDED, beat the admission bound (thr, thrkey));
-    // `valid` masks the keys past N of a ragged last block
-    auto collect = [&](auto bounded, const float (&s)[4][4], int tl, int blk, uint32_t valid,
-                       float thr, int thrkey) {
+    // the block's scores of tile tl that are in the boundary bin or above
+    // (and, with BOUNDED, beat the admission bound (thr, thrkey)), as bits
+    // 4kt + r; `valid` masks the keys past N of a ragged last block
+    auto cand_mask = [&](auto bounded, const float (&s)[4][4], int tl, int blk, uint32_t valid,
+                         float thr, int thrkey) {
       constexpr bool BOUNDED = decltype(bounded)::value;
-      const int lr = 16 * tl + c16;
       uint32_t msk = 0u;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
@@ -924,22 +908,24 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
           }
           msk |= (q ? 1u : 0u) << (4 * kt + r);
         }
-      msk &= valid;
-      if (__ballot(msk != 0u) == 0) return;
-      // each lane reserves its own run of slots (the order of entries in a
-      // row's buffer does not matter: they are ranked by score and key id)
+      return msk & valid;
+    };
+    // each lane reserves its own run of slots in its row's buffer (the order
+    // of a buffer's entries does not matter: they are ranked by score and key
+    // id), then writes its candidates there as (score, key) pairs
+    auto reserve = [&](uint32_t msk, int tl) {
       const int c = __popc(msk);
-      int pos = 0;
-      if (c > 0) pos = atomicAdd(&rows[lr].cnt, c);
-      float* vals = reinterpret_cast<float*>(sm + OFF_UNION + (size_t)lr * a.cap * 8);
-      int* keys = reinterpret_cast<int*>(vals + a.cap);
+      return c > 0 ? atomicAdd(&rows[16 * tl + c16].cnt, c) : 0;
+    };
+    auto append = [&](const float (&s)[4][4], int tl, int blk, uint32_t msk, int pos) {
+      float* buf = reinterpret_cast<float*>(sm + OFF_UNION + (size_t)(16 * tl + c16) * a.cap * 8);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
           if (msk >> (4 * kt + r) & 1u) {
-            vals[pos] = s[kt][r];
-            keys[pos] = key_of(blk, kt, g, r);
+            *reinterpret_cast<float2*>(buf + 2 * pos) =
+                make_float2(s[kt][r], __int_as_float(key_of(blk, kt, g, r)));
             ++pos;
           }
     };
@@ -959,8 +945,21 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
 #pragma unroll
         for (int tl = 0; tl < TL; ++tl) block_scores(kr, qlr, tl, s[tl]);
         if (blk + 2 * NW < blk1) load_k(kr, Kh, blk + 2 * NW, N, g, c16);
+        // both tiles reserve before either writes, so that one wait covers
+        // both reservations
+        uint32_t msk[TL];
+        uint32_t any = 0u;
 #pragma unroll
-        for (int tl = 0; tl < TL; ++tl) collect(std::false_type{}, s[tl], tl, blk, valid, 0.f, 0);
+        for (int tl = 0; tl < TL; ++tl) {
+          msk[tl] = cand_mask(std::false_type{}, s[tl], tl, blk, valid, 0.f, 0);
+          any |= msk[tl];
+        }
+        if (__ballot(any != 0u) == 0) return;
+        int pos[TL];
+#pragma unroll
+        for (int tl = 0; tl < TL; ++tl) pos[tl] = reserve(msk[tl], tl);
+#pragma unroll
+        for (int tl = 0; tl < TL; ++tl) append(s[tl], tl, blk, msk[tl], pos[tl]);
       };
       const int csteady = ragged && blk1 == nblk ? nblk - 1 : blk1;
       int blk = blk0 + w;
@@ -993,7 +992,8 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
             float s[4][4];
             block_scores(kr, qlr, tl, s);
             const int lr = 16 * tl + c16;
-            collect(std::true_type{}, s, tl, blk, valid, rows[lr].thr, rows[lr].thrkey);
+            const uint32_t msk = cand_mask(std::true_type{}, s, tl, blk, valid, rows[lr].thr, rows[lr].thrkey);
+            if (__ballot(msk != 0u) != 0) append(s, tl, blk, msk, reserve(msk, tl));
           }
         }
         __syncthreads();
