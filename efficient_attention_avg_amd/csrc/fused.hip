@@ -198,6 +198,28 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
 
   // expert key slots past k stay 0 for every head (top-k fills slots < k)
   for (int q = threadIdx.x; q < MMAX * KMAX; q += THREADS) *lds<int>(sm, OFF_IDX + q * 4) = 0;
+  // each landmark's window (rows y0 .. y1, columns x0 .. x1) once, into the
+  // histogram region (spent long before the first head's top-k), and 1 /
+  // its size (0 past m)
+  if (threadIdx.x < MMAX) {
+    const int L = threadIdx.x;
+    float inv_cnt = 0.f;
+    int y0 = 0, y1 = 0, x0 = 0, x1 = 0;
+    if (L < m) {
+      pool_window(L / mw, gh, mh, &y0, &y1);
+      pool_window(L % mw, gw, mw, &x0, &x1);
+      inv_cnt = 1.0f / (float)((y1 - y0) * (x1 - x0));
+    }
+    *lds<i32x4>(sm, OFF_H + L * 16) = i32x4{y0, y1, x0, x1};
+    *lds<float>(sm, OFF_INVC + L * 4) = inv_cnt;
+  }
+  // bf16 1.0 / 0 for each bit of a nibble, pairs packed as the MFMA operand
+  if (threadIdx.x < 16) {
+    const uint32_t n = threadIdx.x, one = 0x3F80u;
+    *lds<u32x2>(sm, OFF_LUT + n * 8) = u32x2{(n & 1u ? one : 0u) | (n & 2u ? one << 16 : 0u),
+                                             (n & 4u ? one : 0u) | (n & 8u ? one << 16 : 0u)};
+  }
+  __syncthreads();
   // which tokens each landmark window holds (the same for every head): byte
   // [L][g][ks] has bit t set when token 32ks + 8g + t lies in L's window, so a
   // lane's bytes for every k-step of the pooling product are one 8-byte read
@@ -206,33 +228,18 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
     const int L = it >> 5, gg = (it >> 3) & 3, ks = it & 7, o = 4 * ks + gg;
     uint32_t bits = 0;
     if (L < m && 8 * o < KPMAX) {
-      int y0, y1, x0, x1;
-      pool_window(L / mw, gh, mh, &y0, &y1);
-      pool_window(L % mw, gw, mw, &x0, &x1);
+      const i32x4 wd = *lds<i32x4>(sm, OFF_H + L * 16);
+      // tokens 8o .. 8o + 7: one division, then step along the row
+      int y = (8 * o) / gw, x = 8 * o - y * gw;
       for (int t = 0; t < 8; ++t) {
-        const int tok = 8 * o + t, y = tok / gw, x = tok % gw;
-        bits |= (tok < N && y >= y0 && y < y1 && x >= x0 && x < x1 ? 1u : 0u) << t;
+        bits |= (8 * o + t < N && y >= wd[0] && y < wd[1] && x >= wd[2] && x < wd[3] ? 1u : 0u) << t;
+        if (++x == gw) {
+          x = 0;
+          ++y;
+        }
       }
     }
     *lds<uint8_t>(sm, OFF_WB + it) = (uint8_t)bits;
-  }
-  // bf16 1.0 / 0 for each bit of a nibble, pairs packed as the MFMA operand
-  if (threadIdx.x < 16) {
-    const uint32_t n = threadIdx.x, one = 0x3F80u;
-    *lds<u32x2>(sm, OFF_LUT + n * 8) = u32x2{(n & 1u ? one : 0u) | (n & 2u ? one << 16 : 0u),
-                                             (n & 4u ? one : 0u) | (n & 8u ? one << 16 : 0u)};
-  }
-  // 1 / window size per landmark (0 past m)
-  if (threadIdx.x < MMAX) {
-    const int L = threadIdx.x;
-    float inv_cnt = 0.f;
-    if (L < m) {
-      int y0, y1, x0, x1;
-      pool_window(L / mw, gh, mh, &y0, &y1);
-      pool_window(L % mw, gw, mw, &x0, &x1);
-      inv_cnt = 1.0f / (float)((y1 - y0) * (x1 - x0));
-    }
-    *lds<float>(sm, OFF_INVC + L * 4) = inv_cnt;
   }
 
   // a head's Q rows are requested while the previous head runs its expert tiles
