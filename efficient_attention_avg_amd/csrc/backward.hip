@@ -1149,7 +1149,9 @@ __global__ __launch_bounds__(256, 2) void landmark_mfma_kernel(
 // ---------------------------------------------------------------- pool
 // dQ[t] += sum over the windows i holding token t of dQ_L[i] / |window i|;
 // along an axis of g cells pooled to mg windows, cell y lies in windows
-// floor(y mg / g) .. ceil((y + 1) mg / g) - 1.  Thread: (token, 16 channels).
+// floor(y mg / g) .. ceil((y + 1) mg / g) - 1.  Thread: (token, 16 channels):
+// float4s sub, sub + 4, sub + 8, sub + 12 of the row (sub = thread % 4), so
+// that a token's four threads read 64 contiguous bytes per instruction.
 __global__ __launch_bounds__(256) void pool_kernel(const float* __restrict__ dql,
                                                    float* __restrict__ dq, int gh, int gw,
                                                    int mh, int mw) {
@@ -1157,7 +1159,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const float* __restrict__ dql
   const long long it = (long long)blockIdx.x * 256 + threadIdx.x;
   const int bh = blockIdx.y;
   if (it >= (long long)N * 4) return;
-  const int n = (int)(it >> 2), c0 = 16 * (int)(it & 3);
+  const int n = (int)(it >> 2), c0 = 4 * (int)(it & 3);
   // (32-bit arithmetic when every product below stays under 2^31, which holds
   // for all but extreme grids; 64-bit otherwise, a uniform branch)
   const int y = n / gw, x = n - y * gw;
@@ -1187,7 +1189,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const float* __restrict__ dql
           reinterpret_cast<const float4*>(dql + ((size_t)bh * m + r * mw + cc) * kHeadDim + c0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 v = src[q];
+        const float4 v = src[4 * q];
         acc[q].x = fmaf(v.x, inv, acc[q].x);
         acc[q].y = fmaf(v.y, inv, acc[q].y);
         acc[q].z = fmaf(v.z, inv, acc[q].z);
@@ -1198,12 +1200,12 @@ __global__ __launch_bounds__(256) void pool_kernel(const float* __restrict__ dql
   float4* dst = reinterpret_cast<float4*>(dq + ((size_t)bh * N + n) * kHeadDim + c0);
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    float4 d = dst[q];
+    float4 d = dst[4 * q];
     d.x += acc[q].x;
     d.y += acc[q].y;
     d.z += acc[q].z;
     d.w += acc[q].w;
-    dst[q] = d;
+    dst[4 * q] = d;
   }
 }
 
