@@ -55,6 +55,7 @@ constexpr int HIST_STRIDE = 1040;       // one row's 256 32-bit bins + pad (rows
 constexpr int SPARE_BIN = 256;          // pad word: counts the keys past N of a ragged block
 constexpr int BITMAP_MAX_N = 8192;      // keys whose bitmap fits in a histogram row
 constexpr int LIST_MAX = 128;           // boundary entries listed in a histogram row
+constexpr int CHUNK_BLOCKS = 64;        // key blocks per chunk at most (4096 keys)
 constexpr int MERGE_STRIDE = 68;        // floats per (wave, row): 64 acc, max, sum, min, max
 constexpr float kTauLog2e = 0.125f * 1.4426950408889634f;
 constexpr float kSlack = 8.0f;          // log2 headroom of the lazily raised maximum
@@ -80,6 +81,9 @@ constexpr int OFF_UNION = OFF_SAMP + NW * ROWS * 8;
 constexpr int VALUES_BYTES = NW * VT_BYTES;  // phase V staging (the merge area aliases it)
 static_assert(NW * ROWS * MERGE_STRIDE * 4 <= VALUES_BYTES, "merge area fits in the staging");
 static_assert(BITMAP_MAX_N / 8 <= HIST_STRIDE && LIST_MAX * 8 <= HIST_STRIDE, "row space");
+// a chunk's key bitmap, padded to whole 16-byte groups, and its 16-bit word
+// prefixes share one row's space
+static_assert(6 * ((CHUNK_BLOCKS * KB / 32 + 3) & ~3) <= HIST_STRIDE, "bitmap and prefixes fit a row");
 static_assert((SPARE_BIN + 1) * 4 <= HIST_STRIDE, "the spare counter sits in the row's pad");
 
 struct Args {
@@ -395,9 +399,12 @@ __device__ void row_final(char* sm, const Args& a, const Chunk& ch, int lr, bool
   {
     // bitmap of the taken keys (relative to the chunk's first key) in the
     // row's histogram space; slot = number of taken keys below
+    // (lane t clears and scans four words at a time: nw4 16-byte groups, the
+    // words past nw in the last group staying zero)
     uint32_t* bm = reinterpret_cast<uint32_t*>(list);
     const int kb = ch.kbase;
-    for (int q = t; q < nw; q += 16) bm[q] = 0u;
+    const int nw4 = (nw + 3) >> 2;
+    for (int q4 = t; q4 < nw4; q4 += 16) reinterpret_cast<u32x4*>(bm)[q4] = u32x4{0u, 0u, 0u, 0u};
     group_sync();
     for (int u = 0; 16 * u < cnt; ++u) {
       const int e = t + 16 * u;
@@ -410,16 +417,22 @@ __device__ void row_final(char* sm, const Args& a, const Chunk& ch, int lr, bool
     for (int j = 0; j < 2; ++j)
       if (win[j] >= 0) atomicOr(&bm[(win[j] - kb) >> 5], 1u << ((win[j] - kb) & 31));
     group_sync();
-    // taken keys before each bitmap word (16-bit, after the bitmap), lane t
-    // taking words t, t + 16, ...; then every taken entry writes its own
-    // slot: the taken keys before its word plus those below it in the word
-    uint16_t* wpre = reinterpret_cast<uint16_t*>(bm + nw);
+    // taken keys before each bitmap word (16-bit, after the bitmap's groups),
+    // lane t taking word groups t, t + 16, ...; then every taken entry writes
+    // its own slot: the taken keys before its word plus those below it in the
+    // word
+    uint16_t* wpre = reinterpret_cast<uint16_t*>(bm + 4 * nw4);
     int run = 0;
-    for (int r0 = 0; r0 < nw; r0 += 16) {
-      const int q = r0 + t;
-      const int c = q < nw ? __popc(bm[q]) : 0;
+    for (int r0 = 0; r0 < nw4; r0 += 16) {
+      const int q4 = r0 + t;
+      const u32x4 wv = q4 < nw4 ? reinterpret_cast<const u32x4*>(bm)[q4] : u32x4{0u, 0u, 0u, 0u};
+      const int c0 = __popc(wv[0]), c1 = __popc(wv[1]), c2 = __popc(wv[2]), c3 = __popc(wv[3]);
+      const int c = c0 + c1 + c2 + c3;
       const int tot = g16_addi(c);
-      if (q < nw) wpre[q] = (uint16_t)(run + tot - g16_suffix(c));
+      const uint32_t p0 = (uint32_t)(run + tot - g16_suffix(c));
+      if (q4 < nw4)
+        *reinterpret_cast<u32x2*>(wpre + 4 * q4) =
+            u32x2{p0 | (p0 + c0) << 16, (p0 + c0 + c1) | (p0 + c0 + c1 + c2) << 16};
       run += tot;
     }
     group_sync();
@@ -1194,7 +1207,7 @@ static int landmark_cap(const Shape& s) {
 // us with three (plus 19 us of merge) and 250 us with fourteen.
 static void landmark_chunks(const Shape& s, int& nch, int& cblk) {
   const int nblk = (s.N + lmk::KB - 1) / lmk::KB;
-  nch = (nblk + 63) / 64;
+  nch = (nblk + lmk::CHUNK_BLOCKS - 1) / lmk::CHUNK_BLOCKS;
   cblk = (nblk + nch - 1) / nch;
   nch = (nblk + cblk - 1) / cblk;
 }
