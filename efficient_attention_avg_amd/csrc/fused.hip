@@ -5,11 +5,12 @@
 // "用少量地标查询，同时构造全局概括与细节专家" and Algorithm 1.
 //
 // A persistent grid of 8-wave workgroups, two per CU, each walking heads.  A
-// head needs 78 KB of LDS, so two heads are in flight per CU and one's
-// barrier-bound phases overlap the other's work.  Q and K rows are read
-// straight from global memory (L2 after first touch) as MFMA operands; the
-// transposed values, scores, histograms, a copy of K for the expert tiles and
-// small tables live in LDS:
+// head needs 79 KB of LDS, so two heads are in flight per CU and one's
+// barrier-bound phases overlap the other's work.  K rows for the scores and
+// the routing and expert tiles' Q rows are read straight from global memory
+// (L2 after first touch) as MFMA operands; the head's Q rows (for pooling),
+// then its scores, then its V rows (f16), histograms, a copy of K for the
+// expert tiles and small tables live in LDS:
 //   B  landmark pooling from the Q rows -> Q_L (fp32), split bf16 hi + lo;
 //   C  S^T = K Q_L^T on bf16 MFMA (hi + lo: near-fp32 scores, so top-k sets
 //      and routes are decided at fp32 accuracy), into the shared region X;

@@ -140,7 +140,7 @@ __device__ __forceinline__ void load_k(KRegs& kr, Rsrc Kh, int blk, int N, int g
   }
 }
 
-// V block for the transposed LDS copy: lane holds keys 4p..4p+3 of chunk c
+// V block for the wave's LDS staging: lane holds keys 4p..4p+3 of chunk c
 // (8 channels) for items it = lane, lane + 64 (p = it >> 3, c = it & 7).
 // Keys past N read zeros (their weights are 0).
 struct VRegs {
