@@ -327,136 +327,179 @@ __device__ void row_cut(char* sm, const Args& a, int kk, int lr, bool work, int 
   }
 }
 
-// Row lr's kk best of its buffer, written ascending by key id to `out`, and
-// (when outs is not null) their scores beside them.  The chunk's keys have
-// a bitmap of (kend - kbase) bits in the row's histogram space.
-__device__ void row_final(char* sm, const Args& a, const Chunk& ch, int lr, bool work, int t,
-                          int g, int32_t* out, float* outs) {
-  RowState* rs = reinterpret_cast<RowState*>(sm + OFF_ROW) + lr;
-  float* buf = reinterpret_cast<float*>(sm + OFF_UNION + (size_t)lr * a.cap * 8);  // (score, key)
-  float* list = reinterpret_cast<float*>(sm + OFF_HIST + lr * HIST_STRIDE);
-  const int cnt = work ? rs->cnt : 0;
-  const float A = rs->A, B = rs->B;
-  const int bstar = rs->bstar, above = rs->above;
-  // entries above the boundary bin are in; the boundary bin's are ranked
-  // among themselves, in a compact list when it fits
-  const float upthr = bstar < 255 ? (float)(bstar + 1) : INFINITY;
-  const int nb = cnt - above;
-  const bool listed = nb <= LIST_MAX;
+// Rows lr[j]'s kk best of their buffers, each written ascending by key id to
+// out[j], and (when outs[j] is not null) their scores beside them.  The
+// chunk's keys have a bitmap of (kend - kbase) bits in each row's histogram
+// space.  The R rows of a lane group go through every step together, so that
+// one group barrier serves them all and their LDS round trips overlap.
+template <int R>
+__device__ void rows_final(char* sm, const Args& a, const Chunk& ch, const int (&lr)[R],
+                           const bool (&work)[R], int t, int g, int32_t* const (&out)[R],
+                           float* const (&outs)[R]) {
+  float* buf[R];   // (score, key) pairs
+  float* list[R];
+  int cnt[R], bstar[R], above[R], nb[R], need[R];
+  float A[R], B[R], upthr[R];
+  bool listed[R], short_list[R];
+  const int nw = (ch.kend - ch.kbase + 31) >> 5;
+  int cmax = 0;
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    const RowState* rs = reinterpret_cast<const RowState*>(sm + OFF_ROW) + lr[j];
+    buf[j] = reinterpret_cast<float*>(sm + OFF_UNION + (size_t)lr[j] * a.cap * 8);
+    list[j] = reinterpret_cast<float*>(sm + OFF_HIST + lr[j] * HIST_STRIDE);
+    cnt[j] = work[j] ? rs->cnt : 0;
+    A[j] = rs->A;
+    B[j] = rs->B;
+    bstar[j] = rs->bstar;
+    above[j] = rs->above;
+    // entries above the boundary bin are in; the boundary bin's are ranked
+    // among themselves, in a compact list when it fits
+    upthr[j] = bstar[j] < 255 ? (float)(bstar[j] + 1) : INFINITY;
+    nb[j] = cnt[j] - above[j];
+    listed[j] = nb[j] <= LIST_MAX;
+    need[j] = ch.kk - above[j];
+    // a short list is ranked entry by entry (lane t: entries t and t + 16)
+    // and its winners' keys kept in registers for the bitmap and their
+    // slots; otherwise every buffer entry outside `up` is ranked where it sits
+    short_list[j] = listed[j] && nb[j] <= 32 && nw * 6 <= HIST_STRIDE;
+    cmax = max(cmax, cnt[j]);
+  }
   const uint32_t below = (1u << t) - 1u;
-  uint32_t up = 0u;
-  int run = 0;
-  for (int u = 0; 16 * u < cnt; ++u) {
+  uint32_t up[R], take[R];
+  int run[R];
+#pragma unroll
+  for (int j = 0; j < R; ++j) {
+    up[j] = 0u;
+    run[j] = 0;
+  }
+  for (int u = 0; 16 * u < cmax; ++u) {
     const int e = t + 16 * u;
-    bool inb = false;
-    float2 ev = make_float2(0.f, 0.f);
-    if (e < cnt) {
-      ev = *reinterpret_cast<const float2*>(buf + 2 * e);
-      const bool isup = __builtin_fmaf(ev.x, A, B) >= upthr;
-      up |= (isup ? 1u : 0u) << u;
-      inb = !isup;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      bool inb = false;
+      float2 ev = make_float2(0.f, 0.f);
+      if (e < cnt[j]) {
+        ev = *reinterpret_cast<const float2*>(buf[j] + 2 * e);
+        const bool isup = __builtin_fmaf(ev.x, A[j], B[j]) >= upthr[j];
+        up[j] |= (isup ? 1u : 0u) << u;
+        inb = !isup;
+      }
+      const uint32_t gm = g16_ballot(inb, g);
+      if (listed[j] && inb) *reinterpret_cast<float2*>(list[j] + 2 * (run[j] + __popc(gm & below))) = ev;
+      run[j] += __popc(gm);
     }
-    const uint32_t gm = g16_ballot(inb, g);
-    if (listed && inb) *reinterpret_cast<float2*>(list + 2 * (run + __popc(gm & below))) = ev;
-    run += __popc(gm);
   }
   group_sync();
-  uint32_t take = up;
-  const int need = ch.kk - above;
-  const int nw = (ch.kend - ch.kbase + 31) >> 5;
-  // a short list is ranked entry by entry (lane t: entries t and t + 16) and
-  // its winners' keys kept in registers for the bitmap and their slots;
-  // otherwise every buffer entry outside `up` is ranked where it sits
-  const bool short_list = listed && nb <= 32 && nw * 6 <= HIST_STRIDE;
-  int win[2] = {-1, -1};
-  float winv[2] = {0.f, 0.f};
-  if (short_list) {
+  int win[R][2];
+  float winv[R][2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int i = t + 16 * j;
-      if (i < nb) {
-        const float v = list[2 * i];
-        const int key = __float_as_int(list[2 * i + 1]);
-        if (rank_in_list(list, nb, v, key) < need) {
-          win[j] = key;
-          winv[j] = v;
+  for (int j = 0; j < R; ++j) {
+    take[j] = up[j];
+    win[j][0] = win[j][1] = -1;
+    winv[j][0] = winv[j][1] = 0.f;
+    if (short_list[j]) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int i = t + 16 * h;
+        if (i < nb[j]) {
+          const float v = list[j][2 * i];
+          const int key = __float_as_int(list[j][2 * i + 1]);
+          if (rank_in_list(list[j], nb[j], v, key) < need[j]) {
+            win[j][h] = key;
+            winv[j][h] = v;
+          }
+        }
+      }
+    } else {
+      for (int u = 0; 16 * u < cnt[j]; ++u) {
+        const int e = t + 16 * u;
+        if (e < cnt[j] && !(up[j] >> u & 1u)) {
+          const float2 ev = *reinterpret_cast<const float2*>(buf[j] + 2 * e);
+          const float v = ev.x;
+          const int key = __float_as_int(ev.y);
+          const int r = listed[j] ? rank_in_list(list[j], nb[j], v, key)
+                                  : rank_in_list(buf[j], cnt[j], v, key) - above[j];
+          take[j] |= (r < need[j] ? 1u : 0u) << u;
         }
       }
     }
-  } else {
-    for (int u = 0; 16 * u < cnt; ++u) {
-      const int e = t + 16 * u;
-      if (e < cnt && !(up >> u & 1u)) {
-        const float2 ev = *reinterpret_cast<const float2*>(buf + 2 * e);
-        const float v = ev.x;
-        const int key = __float_as_int(ev.y);
-        const int r = listed ? rank_in_list(list, nb, v, key) : rank_in_list(buf, cnt, v, key) - above;
-        take |= (r < need ? 1u : 0u) << u;
-      }
-    }
   }
   group_sync();
-  {
-    // bitmap of the taken keys (relative to the chunk's first key) in the
-    // row's histogram space; slot = number of taken keys below
-    // (lane t clears and scans four words at a time: nw4 16-byte groups, the
-    // words past nw in the last group staying zero)
-    uint32_t* bm = reinterpret_cast<uint32_t*>(list);
-    const int kb = ch.kbase;
-    const int nw4 = (nw + 3) >> 2;
-    for (int q4 = t; q4 < nw4; q4 += 16) reinterpret_cast<u32x4*>(bm)[q4] = u32x4{0u, 0u, 0u, 0u};
-    group_sync();
-    for (int u = 0; 16 * u < cnt; ++u) {
-      const int e = t + 16 * u;
-      if (e < cnt && (take >> u & 1u)) {
-        const int key = __float_as_int(buf[2 * e + 1]);
-        atomicOr(&bm[(key - kb) >> 5], 1u << ((key - kb) & 31));
-      }
-    }
+  // bitmap of the taken keys (relative to the chunk's first key) in each
+  // row's histogram space; slot = number of taken keys below (lane t clears
+  // and scans four words at a time: nw4 16-byte groups, the words past nw in
+  // the last group staying zero)
+  const int kb = ch.kbase;
+  const int nw4 = (nw + 3) >> 2;
+  uint32_t* bm[R];
+  uint16_t* wpre[R];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      if (win[j] >= 0) atomicOr(&bm[(win[j] - kb) >> 5], 1u << ((win[j] - kb) & 31));
-    group_sync();
-    // taken keys before each bitmap word (16-bit, after the bitmap's groups),
-    // lane t taking word groups t, t + 16, ...; then every taken entry writes
-    // its own slot: the taken keys before its word plus those below it in the
-    // word
-    uint16_t* wpre = reinterpret_cast<uint16_t*>(bm + 4 * nw4);
-    int run = 0;
-    for (int r0 = 0; r0 < nw4; r0 += 16) {
-      const int q4 = r0 + t;
-      const u32x4 wv = q4 < nw4 ? reinterpret_cast<const u32x4*>(bm)[q4] : u32x4{0u, 0u, 0u, 0u};
+  for (int j = 0; j < R; ++j) {
+    bm[j] = reinterpret_cast<uint32_t*>(list[j]);
+    // taken keys before each bitmap word (16-bit, after the bitmap's groups)
+    wpre[j] = reinterpret_cast<uint16_t*>(bm[j] + 4 * nw4);
+    for (int q4 = t; q4 < nw4; q4 += 16) reinterpret_cast<u32x4*>(bm[j])[q4] = u32x4{0u, 0u, 0u, 0u};
+  }
+  group_sync();
+  for (int u = 0; 16 * u < cmax; ++u) {
+    const int e = t + 16 * u;
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if (e < cnt[j] && (take[j] >> u & 1u)) {
+        const int key = __float_as_int(buf[j][2 * e + 1]);
+        atomicOr(&bm[j][(key - kb) >> 5], 1u << ((key - kb) & 31));
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < R; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (win[j][h] >= 0) atomicOr(&bm[j][(win[j][h] - kb) >> 5], 1u << ((win[j][h] - kb) & 31));
+  group_sync();
+  // lane t takes word groups t, t + 16, ...; then every taken entry writes
+  // its own slot: the taken keys before its word plus those below it in the
+  // word
+#pragma unroll
+  for (int j = 0; j < R; ++j) run[j] = 0;
+  for (int r0 = 0; r0 < nw4; r0 += 16) {
+    const int q4 = r0 + t;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const u32x4 wv = q4 < nw4 ? reinterpret_cast<const u32x4*>(bm[j])[q4] : u32x4{0u, 0u, 0u, 0u};
       const int c0 = __popc(wv[0]), c1 = __popc(wv[1]), c2 = __popc(wv[2]), c3 = __popc(wv[3]);
       const int c = c0 + c1 + c2 + c3;
       const int tot = g16_addi(c);
-      const uint32_t p0 = (uint32_t)(run + tot - g16_suffix(c));
+      const uint32_t p0 = (uint32_t)(run[j] + tot - g16_suffix(c));
       if (q4 < nw4)
-        *reinterpret_cast<u32x2*>(wpre + 4 * q4) =
+        *reinterpret_cast<u32x2*>(wpre[j] + 4 * q4) =
             u32x2{p0 | (p0 + c0) << 16, (p0 + c0 + c1) | (p0 + c0 + c1 + c2) << 16};
-      run += tot;
-    }
-    group_sync();
-    if (work) {
-      auto emit = [&](int key, float v) {
-        const int wq = (key - kb) >> 5;
-        const int pos = wpre[wq] + __popc(bm[wq] & ((1u << ((key - kb) & 31)) - 1u));
-        if (pos < ch.kk) {
-          out[pos] = key;
-          if (outs) outs[pos] = v;
-        }
-      };
-      for (int u = 0; 16 * u < cnt; ++u) {
-        const int e = t + 16 * u;
-        if (e < cnt && (take >> u & 1u)) {
-          const float2 ev = *reinterpret_cast<const float2*>(buf + 2 * e);
-          emit(__float_as_int(ev.y), ev.x);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        if (win[j] >= 0) emit(win[j], winv[j]);
+      run[j] += tot;
     }
   }
+  group_sync();
+  auto emit = [&](int j, int key, float v) {
+    const int wq = (key - kb) >> 5;
+    const int pos = wpre[j][wq] + __popc(bm[j][wq] & ((1u << ((key - kb) & 31)) - 1u));
+    if (pos < ch.kk) {
+      out[j][pos] = key;
+      if (outs[j]) outs[j][pos] = v;
+    }
+  };
+  for (int u = 0; 16 * u < cmax; ++u) {
+    const int e = t + 16 * u;
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if (work[j] && e < cnt[j] && (take[j] >> u & 1u)) {
+        const float2 ev = *reinterpret_cast<const float2*>(buf[j] + 2 * e);
+        emit(j, __float_as_int(ev.y), ev.x);
+      }
+  }
+#pragma unroll
+  for (int j = 0; j < R; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (work[j] && win[j][h] >= 0) emit(j, win[j][h], winv[j][h]);
 }
 
 // FUSE (a.fuse_h): the histogram is built during pass V; a template
@@ -1023,17 +1066,27 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
   __syncthreads();
 
   // ------------------------------------------------------------ F: final
-#pragma unroll 1
-  for (int i = 0; i < TL; ++i) {
-    const int r = 4 * w + g + 16 * i;
-    const bool work = row0 + r < a.m;
-    const size_t row = (size_t)bh * a.m + (work ? row0 + r : 0);
-    if (a.nch == 1) {
-      row_final(sm, a, ch, r, work, c16, g, a.idx + row * a.k, nullptr);
-    } else {
-      const size_t at = (row * a.nch + ch.chunk) * a.k;
-      row_final(sm, a, ch, r, work, c16, g, a.cand_k + at, a.cand_s + at);
+  // group g of wave w takes rows 4w + g + 16i, all TL of them together
+  {
+    int lr[TL];
+    bool work[TL];
+    int32_t* outk[TL];
+    float* outs[TL];
+#pragma unroll
+    for (int i = 0; i < TL; ++i) {
+      lr[i] = 4 * w + g + 16 * i;
+      work[i] = row0 + lr[i] < a.m;
+      const size_t row = (size_t)bh * a.m + (work[i] ? row0 + lr[i] : 0);
+      if (a.nch == 1) {
+        outk[i] = a.idx + row * a.k;
+        outs[i] = nullptr;
+      } else {
+        const size_t at = (row * a.nch + ch.chunk) * a.k;
+        outk[i] = a.cand_k + at;
+        outs[i] = a.cand_s + at;
+      }
     }
+    rows_final<TL>(sm, a, ch, lr, work, c16, g, outk, outs);
   }
 }
 
