@@ -156,7 +156,7 @@ mita_status run_route(const void* Q, const float* ql, int32_t* route, int32_t* c
                              "route launch");
   if (mk) mk->mark(st);
   if (r != MITA_OK) return r;
-  r = hip_status(mfma ? mita::launch_group_bf16(route, (const int32_t*)scratch, counts, offsets,
+  r = hip_status(mfma ? mita::launch_group_bf16(route, (int32_t*)scratch, counts, offsets,
                                                 perm, s, st)
                       : mita::launch_group(route, counts, offsets, perm, s, st),
                  "group launch");

@@ -4,11 +4,15 @@
 // shared ones under one softmax; partial results merge by online softmax).
 //
 // Persistent workgroups, P per head, placed on the head's XCD so the head's
-// K, V and Q rows are re-read from that XCD's L2.  A head's experts are dealt
-// to its P workgroups in a snake, largest pass count first.  Per workgroup:
-//   * load its experts' table (query range, key ids, first 64 query ids)
-//     and the head's Q_L (bf16 hi + lo) and V_L^T (f16) into LDS once;
-//   * per expert: its k key rows (bf16) and value rows (f16) sit in LDS,
+// K, V and Q rows are re-read from that XCD's L2 (spread over the XCDs when
+// there are fewer than 8 heads).  A head's passes (runs of up to 64 of one
+// expert's queries, in expert order) are cut into P contiguous ranges of
+// near-equal length, one per workgroup, so that a large expert's queries are
+// spread over several workgroups.  Per workgroup:
+//   * load its segments' table (each a run of one expert's queries: range,
+//     key ids, first 64 query ids) and the head's Q_L (bf16 hi + lo) and
+//     V_L^T (f16) into LDS once;
+//   * per segment: its expert's k key rows (bf16) and value rows (f16) sit in LDS,
 //     shared by the four waves; V^T fragments come from the value rows by the
 //     transposing LDS read.  While one expert is computed the
 //     next one's rows (and the Q rows of its first 64 queries) are already
@@ -56,17 +60,25 @@ struct Args {
   int s, shared;
 };
 
-// LDS layout; the expert table holds, per expert of the workgroup,
-// [q0, count, k key ids, first TQ query ids]; the head's expert offsets sit
-// beside it.
+// Upper bound on a head's passes (TQ-item runs of one expert's items):
+// sum over experts of ceil(c_e / TQ) <= (N s) / TQ + m.
+__host__ __device__ inline int max_passes(int m, int N, int s) {
+  return m + (int)(((long long)N * s + TQ - 1) / TQ);
+}
+
+// LDS layout; the segment table holds, per segment of the workgroup (a run
+// of one expert's items), [first item's place in the expert order, count,
+// k key ids]; the head's expert offsets sit beside it.
+// A workgroup takes at most ceil(tmax / parts) passes, so at most that many
+// segments (each holds at least one of its passes).
 struct Lay {
   int mp, vlt_stride, ew, ts;
-  int off_qlh, off_qll, off_vlt, off_ke, off_vet, off_tab, off_elist, off_offs, bytes;
-  __host__ __device__ Lay(int m, int k, int parts) {
+  int off_qlh, off_qll, off_vlt, off_ke, off_vet, off_tab, off_elist, off_scan, off_offs, bytes;
+  __host__ __device__ Lay(int m, int k, int parts, int tmax) {
     mp = (m + 31) & ~31;
     vlt_stride = mp * 2 + 16;
-    ew = (m + parts - 1) / parts;
-    ts = 2 + k + TQ;
+    ew = (tmax + parts - 1) / parts;
+    ts = 2 + k;
     off_qlh = 0;
     off_qll = off_qlh + mp * 128;
     off_vlt = off_qll + mp * 128;
@@ -74,7 +86,8 @@ struct Lay {
     off_vet = off_ke + EC * 128;
     off_tab = off_vet + EC * EV_STRIDE;
     off_elist = off_tab + ew * ts * 4;
-    off_offs = off_elist + (ew + 1) * 4;  // the head's m + 1 expert offsets
+    off_scan = off_elist + (ew + 1) * 4;  // [10] ints: the deal's wave totals and bounds
+    off_offs = off_scan + 16 * 4;         // the head's m + 1 expert offsets
     bytes = off_offs + (m + 1) * 4;
   }
 };
@@ -155,20 +168,25 @@ __device__ __forceinline__ void store_out(Rsrc outr, const PassOut& o, int g, in
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void attend_bf16_kernel(Args a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
-  const Lay L(a.m, a.k, a.parts);
+  const Lay L(a.m, a.k, a.parts, max_passes(a.m, a.N, a.s));
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
-  const int bh = xcd + 8 * (slot / a.parts), part = slot % a.parts;
-  if (bh >= a.BH || part >= a.m) return;
+  // with 8 or more heads a head's workgroups share one XCD (and its L2:
+  // workgroups go to the XCDs round robin); with fewer, a head's workgroups
+  // alternate over the XCDs so that every XCD has work
+  const int b = blockIdx.x;
+  const int bh = a.BH >= 8 ? (b & 7) + 8 * ((b >> 3) / a.parts) : b % a.BH;
+  const int part = a.BH >= 8 ? (b >> 3) % a.parts : b / a.BH;
+  if (bh >= a.BH) return;
   const int N = a.N, m = a.m, k = a.k, P = a.parts, S = a.s;
   const bool shared = a.shared != 0;
   // The prologue's global loads are few round trips deep: the head's expert
   // offsets (one load per thread) and the first Q_L / V_L rows go out
-  // together at entry; the deal and the experts' query ranges then come from
-  // the LDS copy of the offsets, and only the key and query ids (then the
-  // first expert's rows) depend on them.
+  // together at entry; the deal and the segments' item ranges then come
+  // from the LDS copy of the offsets, and only the key and item ids (then
+  // the first segment's rows) depend on them.
   int* offl = reinterpret_cast<int*>(sm + L.off_offs);
+  int* scan = reinterpret_cast<int*>(sm + L.off_scan);
   const int32_t* offs = a.offsets + (size_t)bh * (m + 1);
   const int o_mine = tid <= m ? offs[tid] : 0;
   float4 fq[4], fv[4];
@@ -185,27 +203,62 @@ void attend_bf16_kernel(Args a) {
   };
   if (shared) load_qv(0);
   for (int e = tid; e <= m; e += blockDim.x) offl[e] = e == tid ? o_mine : offs[e];
+  if (tid == 0) scan[8] = scan[9] = 0;
   __syncthreads();
-  // The head's experts are dealt to its P workgroups in a snake (0, 1, ..,
-  // P-1, P-1, .., 0, ...) in order of their passes (then queries, then id),
-  // largest first, so that the workgroups' pass totals even out; every
-  // workgroup of the head computes the same deal.
+  // The deal: the head's passes, in expert order (expert e's passes run
+  // over its items TQ at a time), are cut into P contiguous ranges of
+  // floor / ceil(T / P) passes; this workgroup takes range [lo, hi), i.e. a
+  // segment (one expert's run of items) of every expert that has passes in
+  // it.  A large expert is so spread over several workgroups, and each
+  // workgroup's pass count is within one of the mean.  Every workgroup of
+  // the head computes the same cut.  One thread per expert (m <= 256).
+  static_assert(MAXM <= 256, "one thread per expert");
   int* elist = reinterpret_cast<int*>(sm + L.off_elist);
-  for (int e = tid; e < m; e += blockDim.x) {
-    const int c = offl[e + 1] - offl[e], pc = (c + TQ - 1) / TQ;
-    int rank = 0;
-    for (int e2 = 0; e2 < m; ++e2) {
-      const int c2 = offl[e2 + 1] - offl[e2], p2 = (c2 + TQ - 1) / TQ;
-      rank += (p2 > pc || (p2 == pc && (c2 > c || (c2 == c && e2 < e)))) ? 1 : 0;
+  int* tab = reinterpret_cast<int*>(sm + L.off_tab);
+  int nexp = 0;
+  {
+    const int e = tid;
+    const int c = e < m ? offl[e + 1] - offl[e] : 0;
+    const int pc = (c + TQ - 1) / TQ, ne1 = pc > 0 ? 1 : 0;
+    // inclusive wave scans of the pass counts and of the non-empty flags
+    int ip = pc, in = ne1;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int xp = __shfl_up(ip, off, 64), xn = __shfl_up(in, off, 64);
+      ip += lane >= off ? xp : 0;
+      in += lane >= off ? xn : 0;
     }
-    const int round = rank / P, pos = rank - round * P;
-    if (((round & 1) ? P - 1 - pos : pos) == part) elist[round] = e;
+    if (lane == 63) {
+      scan[w] = ip;
+      scan[4 + w] = in;
+    }
+    __syncthreads();
+    // exclusive block prefixes: pe = passes before expert e, ne = non-empty
+    // experts before it; T = the head's passes
+    int pe = ip - pc, ne = in - ne1, T = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pe += i < w ? scan[i] : 0;
+      ne += i < w ? scan[4 + i] : 0;
+      T += scan[i];
+    }
+    const int lo = (int)((long long)part * T / P), hi = (int)((long long)(part + 1) * T / P);
+    const int a0 = max(pe, lo), b0 = min(pe + pc, hi);
+    const bool ov = pc > 0 && a0 < b0;
+    // the experts holding passes lo and hi - 1 bound this workgroup's run
+    // of non-empty experts (their ne and ne + 1)
+    if (pc > 0 && pe <= lo && lo < pe + pc) scan[8] = ne;
+    if (pc > 0 && pe < hi && hi <= pe + pc) scan[9] = ne + 1;
+    __syncthreads();
+    nexp = lo < hi ? scan[9] - scan[8] : 0;
+    if (ov) {
+      const int j = ne - scan[8];
+      elist[j] = e;
+      tab[j * L.ts] = offl[e] + TQ * (a0 - pe);
+      tab[j * L.ts + 1] = min(TQ * (b0 - pe), c) - TQ * (a0 - pe);
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  // this workgroup's experts: one per full round, plus one in the last
-  // (partial) round when the deal reaches it there
-  const int full = m / P, rest = m - full * P;
-  const int nexp = full + ((full & 1) ? (part >= P - rest ? 1 : 0) : (part < rest ? 1 : 0));
   const uint16_t* Qh = a.Q + (size_t)bh * N * 64;
   const uint16_t* Kh = a.K + (size_t)bh * N * 64;
   const uint16_t* Vh = a.V + (size_t)bh * N * 64;
@@ -214,18 +267,11 @@ void attend_bf16_kernel(Args a) {
   // s = 1: output rows of the queries; s > 1: partial rows of the N * s items
   const Rsrc outr = out_rows(a.out + (size_t)bh * N * S * 64, N * S);
   float2* pmlh = S > 1 ? a.pml + (size_t)bh * N * S : nullptr;
-  int* tab = reinterpret_cast<int*>(sm + L.off_tab);
   const u32x4 z = {0u, 0u, 0u, 0u};
 
-  // ---- the experts' table: query ranges (from the LDS offsets), key ids
-  // and first query ids, with every load of a thread issued before any is
+  // ---- the segments' table: key ids of each segment's expert (its item
+  // range is in place), with every load of a thread issued before any is
   // used
-  if (tid < nexp) {
-    const int e = elist[tid];
-    const int q0 = offl[e];
-    tab[tid * L.ts] = q0;
-    tab[tid * L.ts + 1] = offl[e + 1] - q0;
-  }
   {
     constexpr int U = 8;
     const int total = nexp * L.ts;
@@ -237,12 +283,7 @@ void attend_bf16_kernel(Args a) {
         v[u] = -1;
         if (it < total) {
           const int j = it / L.ts, o = it - j * L.ts, e = elist[j];
-          if (o >= 2 && o < 2 + k) {
-            v[u] = idxh[(size_t)e * k + (o - 2)];
-          } else if (o >= 2 + k) {
-            const int q0 = offl[e], cnt = offl[e + 1] - q0;
-            if (o - 2 - k < cnt) v[u] = permh[q0 + (o - 2 - k)];
-          }
+          if (o >= 2) v[u] = idxh[(size_t)e * k + (o - 2)];
         }
       }
 #pragma unroll
@@ -290,19 +331,27 @@ void attend_bf16_kernel(Args a) {
   const int vp = tid >> 3, vc = tid & 7;
   struct Rows {
     u32x4 k0, k1, v0, v1, q0r, q1r;
+    int it0;
   };
-  // rows of slots [s0, s0 + 64) of expert j, and (s0 == 0) the Q row of this
-  // lane's first-pass query
+  // rows of slots [s0, s0 + 64) of segment j's expert, and (s0 == 0) this
+  // lane's first-pass item and the Q row of its query (the item id is
+  // requested first, so that the Q row's wait does not cover the key and
+  // value rows)
   auto load_rows = [&](int j, int s0, Rows& r) {
     const int* te = tab + j * L.ts;
     const int* ke = te + 2;
+    int t = 0;
+    if (s0 == 0) {
+      const int qi = 16 * w + c16;
+      t = qi < te[1] ? permh[te[0] + qi] : 0;
+    }
     const int a0 = s0 + ksl, a1 = a0 + 32, b0 = s0 + 2 * vp, b1 = b0 + 1;
     r.k0 = a0 < k ? *reinterpret_cast<const u32x4*>(Kh + (size_t)ke[a0] * 64 + 8 * kc) : z;
     r.k1 = a1 < k ? *reinterpret_cast<const u32x4*>(Kh + (size_t)ke[a1] * 64 + 8 * kc) : z;
     r.v0 = b0 < k ? *reinterpret_cast<const u32x4*>(Vh + (size_t)ke[b0] * 64 + 8 * vc) : z;
     r.v1 = b1 < k ? *reinterpret_cast<const u32x4*>(Vh + (size_t)ke[b1] * 64 + 8 * vc) : z;
     if (s0 == 0) {
-      const int t = max(te[2 + k + 16 * w + c16], 0);
+      r.it0 = t;
       const int n = S == 1 ? t : t / S;
       r.q0r = *reinterpret_cast<const u32x4*>(Qh + (size_t)n * 64 + 8 * g);
       r.q1r = *reinterpret_cast<const u32x4*>(Qh + (size_t)n * 64 + 32 + 8 * g);
@@ -474,6 +523,7 @@ void attend_bf16_kernel(Args a) {
     const int q0 = te[0], cnt = te[1];
     store_rows(rows);  // waits for this expert's rows (and the stores before them)
     const u32x4 bq0 = rows.q0r, bq1 = rows.q1r;
+    const int it0 = rows.it0;
     // take the Q rows now too: a wait after the stores below would also wait
     // for the stores
     asm volatile("" ::"v"(bq0), "v"(bq1));
@@ -483,8 +533,7 @@ void attend_bf16_kernel(Args a) {
     if (j + 1 < nexp) load_rows(j + 1, 0, rows);
     __syncthreads();
     if (cnt > 0) {
-      const int n0 = te[2 + k + 16 * w + c16];
-      PassOut o = run_pass(j, 0, max(n0, 0), bq0, bq1);
+      PassOut o = run_pass(j, 0, it0, bq0, bq1);
       for (int p0 = TQ; p0 < cnt; p0 += TQ) {
         // later passes: query ids and Q rows straight from global memory
         store_out(outr, o, g, c16);
@@ -550,9 +599,10 @@ static int attend_parts(const Shape& s) {
   if (hipGetDevice(&dev) == hipSuccess)
     hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
   // about three resident workgroups per CU in total, at least one per head,
-  // at most one per expert
+  // no more than the head can have passes
   int parts = (3 * ncu + s.BH - 1) / s.BH;
-  if (parts > s.m) parts = s.m;
+  const int tmax = att::max_passes(s.m, s.N, s.s);
+  if (parts > tmax) parts = tmax;
   if (parts < 1) parts = 1;
   return parts;
 }
@@ -562,9 +612,10 @@ hipError_t launch_attend_bf16(const void* Q, const void* K, const void* V, const
                               const int32_t* perm, float* out, void* partial, const Shape& s,
                               hipStream_t st) {
   int parts = attend_parts(s);
-  // the table must fit next to the rest: fewer experts per workgroup if not
-  while (att::Lay(s.m, s.k, parts).bytes > 160 * 1024 && parts < s.m) ++parts;
-  const att::Lay L(s.m, s.k, parts);
+  const int tmax = att::max_passes(s.m, s.N, s.s);
+  // the table must fit next to the rest: fewer passes per workgroup if not
+  while (att::Lay(s.m, s.k, parts, tmax).bytes > 160 * 1024 && parts < tmax) ++parts;
+  const att::Lay L(s.m, s.k, parts, tmax);
   if (L.bytes > 160 * 1024) return hipErrorInvalidValue;
   static std::atomic<unsigned long long> lds_set;
   if (const hipError_t e = allow_lds((const void*)att::attend_bf16_kernel, 160 * 1024, lds_set);
@@ -575,7 +626,7 @@ hipError_t launch_attend_bf16(const void* Q, const void* K, const void* V, const
   float2* pml = s.s > 1 ? (float2*)((char*)partial + (size_t)s.BH * s.N * s.s * 64 * 4) : nullptr;
   att::Args a{(const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, ql, vl, idx, offsets,
               perm, part, pml, s.BH, s.N, s.m, s.k, parts, s.s, s.shared ? 1 : 0};
-  const int grid = ((s.BH + 7) / 8) * 8 * parts;
+  const int grid = s.BH >= 8 ? ((s.BH + 7) / 8) * 8 * parts : s.BH * parts;
   att::attend_bf16_kernel<<<grid, 256, L.bytes, st>>>(a);
   return hipGetLastError();
 }

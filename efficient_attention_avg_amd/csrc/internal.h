@@ -71,7 +71,7 @@ bool route_bf16_supported(const Shape& s);
 size_t route_chist_bytes(const Shape& s);
 hipError_t launch_route_bf16(const void* Q, const float* ql, int32_t* route, int32_t* chist,
                              const Shape& s, hipStream_t st);
-hipError_t launch_group_bf16(const int32_t* route, const int32_t* chist, int32_t* counts,
+hipError_t launch_group_bf16(const int32_t* route, int32_t* chist, int32_t* counts,
                              int32_t* offsets, int32_t* perm, const Shape& s, hipStream_t st);
 bool attend_bf16_supported(const Shape& s);
 // s > 1: the attention kernel leaves per-item partial sums in `partial`

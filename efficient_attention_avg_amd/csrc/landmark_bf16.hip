@@ -510,10 +510,13 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   // round-robin dispatch puts workgroup b on XCD b % 8: keep a head's
-  // workgroups on one XCD so its K and V stay in that XCD's L2
-  const int b = blockIdx.x, xcd = b & 7, slot = b >> 3;
+  // workgroups on one XCD so its K and V stay in that XCD's L2; with fewer
+  // than 8 heads a head's workgroups alternate over the XCDs instead, so
+  // that every XCD has work
+  const int b = blockIdx.x;
   const int per_head = a.tiles * a.nch;
-  const int bh = xcd + 8 * (slot / per_head), rem = slot % per_head;
+  const int bh = a.BH >= 8 ? (b & 7) + 8 * ((b >> 3) / per_head) : b % a.BH;
+  const int rem = a.BH >= 8 ? (b >> 3) % per_head : b / a.BH;
   const int row0 = (rem % a.tiles) * ROWS;
   if (bh >= a.BH) return;
   const int N = a.N, nblk = (N + KB - 1) / KB;
@@ -1113,6 +1116,11 @@ __device__ __forceinline__ int wave_suffix(int v, int lane) {
   return v;
 }
 
+// Entries per lane in flight: every loop over the candidate list reads
+// MU entries per lane (MU * 64 per wave) before using any, so a row's list
+// takes n / (64 MU) round trips per pass instead of n / 64.
+constexpr int MU = 8;
+
 __global__ __launch_bounds__(64 * MERGE_WAVES) void merge_kernel(Args a) {
   __shared__ uint32_t hist[MERGE_WAVES][256];
   __shared__ float2 blist[MERGE_WAVES][LISTCAP];
@@ -1125,12 +1133,30 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void merge_kernel(Args a) {
   {
     const float* pp = a.vlpart + row * nch * PART_STRIDE;
     float M = -INFINITY;
-    for (int c = 0; c < nch; ++c) M = fmaxf(M, pp[c * PART_STRIDE + 64]);
+    for (int c0 = 0; c0 < nch; c0 += MU) {
+      float mv[MU];
+#pragma unroll
+      for (int u = 0; u < MU; ++u) mv[u] = c0 + u < nch ? pp[(c0 + u) * PART_STRIDE + 64] : -INFINITY;
+#pragma unroll
+      for (int u = 0; u < MU; ++u) M = fmaxf(M, mv[u]);
+    }
     float o = 0.f, L = 0.f;
-    for (int c = 0; c < nch; ++c) {
-      const float f = __builtin_amdgcn_exp2f((pp[c * PART_STRIDE + 64] - M) * kTauLog2e);
-      o = fmaf(f, pp[c * PART_STRIDE + lane], o);
-      L = fmaf(f, pp[c * PART_STRIDE + 65], L);
+    for (int c0 = 0; c0 < nch; c0 += MU) {
+      float mv[MU], ov[MU], lv[MU];
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        const bool ok = c0 + u < nch;
+        const float* q = pp + (ok ? c0 + u : 0) * PART_STRIDE;
+        mv[u] = ok ? q[64] : -INFINITY;
+        ov[u] = ok ? q[lane] : 0.f;
+        lv[u] = ok ? q[65] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        const float f = __builtin_amdgcn_exp2f((mv[u] - M) * kTauLog2e);
+        o = fmaf(f, ov[u], o);
+        L = fmaf(f, lv[u], L);
+      }
     }
     a.vl[row * 64 + lane] = o / L;
     if (a.stats && lane == 0) {
@@ -1143,11 +1169,24 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void merge_kernel(Args a) {
   const int n = (nch - 1) * k + min(k, last_keys);
   const float* cs = a.cand_s + row * nch * k;
   const int32_t* ck = a.cand_k + row * nch * k;
+  // this lane's entries e0 + 64 u (u < MU) of a step starting at e0; past n
+  // they read -inf (the min / max below skip them)
+  auto load_s = [&](int e0, float (&v)[MU]) {
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      const int e = e0 + 64 * u + lane;
+      v[u] = e < n ? cs[e] : -INFINITY;
+    }
+  };
   float lo = INFINITY, hi = -INFINITY;
-  for (int e = lane; e < n; e += 64) {
-    const float v = cs[e];
-    lo = fminf(lo, v);
-    hi = fmaxf(hi, v);
+  for (int e0 = 0; e0 < n; e0 += 64 * MU) {
+    float v[MU];
+    load_s(e0, v);
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      lo = fminf(lo, e0 + 64 * u + lane < n ? v[u] : INFINITY);
+      hi = fmaxf(hi, v[u]);
+    }
   }
   lo = wave_min_f(lo);
   hi = wave_max(hi);
@@ -1159,7 +1198,13 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void merge_kernel(Args a) {
   if (lane == 0) bcount[w] = 0;
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  for (int e = lane; e < n; e += 64) atomicAdd(&h[bin_of(cs[e], A, B)], 1u);
+  for (int e0 = 0; e0 < n; e0 += 64 * MU) {
+    float v[MU];
+    load_s(e0, v);
+#pragma unroll
+    for (int u = 0; u < MU; ++u)
+      if (e0 + 64 * u + lane < n) atomicAdd(&h[bin_of(v[u], A, B)], 1u);
+  }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
   // boundary bin: lane l holds bins 4l .. 4l + 3
@@ -1198,47 +1243,66 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void merge_kernel(Args a) {
   // the boundary bin's entries into the list (when they fit)
   const bool listed = nb <= LISTCAP;
   if (listed) {
-    for (int e = lane; e < n; e += 64) {
-      const float v = cs[e];
-      if (bin_of(v, A, B) == bstar) {
-        const int at = atomicAdd(&bcount[w], 1);
-        blist[w][at] = make_float2(v, __int_as_float(ck[e]));
+    for (int e0 = 0; e0 < n; e0 += 64 * MU) {
+      float v[MU];
+      load_s(e0, v);
+      int kk[MU];
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        const int e = e0 + 64 * u + lane;
+        kk[u] = e < n && bin_of(v[u], A, B) == bstar ? ck[e] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        if (kk[u] >= 0) {
+          const int at = atomicAdd(&bcount[w], 1);
+          blist[w][at] = make_float2(v[u], __int_as_float(kk[u]));
+        }
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
   }
-  // winners in list order
+  // winners in list order (entry e0 + 64 u + lane: u-major steps of 64)
   int32_t* out = a.idx + row * k;
   int run = 0;
-  for (int e0 = 0; e0 < n; e0 += 64) {
-    const int e = e0 + lane;
-    bool win = false;
-    if (e < n) {
-      const float v = cs[e];
-      const int key = ck[e];
-      const int bn = bin_of(v, A, B);
-      if (bn > bstar) {
-        win = true;
-      } else if (bn == bstar) {
-        int r = 0;
-        if (listed) {
-          for (int j = 0; j < nb; ++j) {
-            const float2 x = blist[w][j];
-            r += better(x.x, __float_as_int(x.y), v, key);
-          }
-        } else {
-          for (int j = 0; j < n; ++j) {
-            const float x = cs[j];
-            r += (bin_of(x, A, B) == bstar && better(x, ck[j], v, key)) ? 1 : 0;
-          }
-        }
-        win = r < need;
-      }
+  for (int e0 = 0; e0 < n; e0 += 64 * MU) {
+    float v[MU];
+    int key[MU];
+    load_s(e0, v);
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      const int e = e0 + 64 * u + lane;
+      key[u] = e < n ? ck[e] : 0;
     }
-    const uint64_t bw = __ballot(win);
-    if (win) out[run + lanes_below(bw)] = ck[e];
-    run += __popcll(bw);
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      const int e = e0 + 64 * u + lane;
+      bool win = false;
+      if (e < n) {
+        const int bn = bin_of(v[u], A, B);
+        if (bn > bstar) {
+          win = true;
+        } else if (bn == bstar) {
+          int r = 0;
+          if (listed) {
+            for (int j = 0; j < nb; ++j) {
+              const float2 x = blist[w][j];
+              r += better(x.x, __float_as_int(x.y), v[u], key[u]);
+            }
+          } else {
+            for (int j = 0; j < n; ++j) {
+              const float x = cs[j];
+              r += (bin_of(x, A, B) == bstar && better(x, ck[j], v[u], key[u])) ? 1 : 0;
+            }
+          }
+          win = r < need;
+        }
+      }
+      const uint64_t bw = __ballot(win);
+      if (win) out[run + lanes_below(bw)] = key[u];
+      run += __popcll(bw);
+    }
   }
 }
 
@@ -1304,7 +1368,7 @@ hipError_t launch_landmark_bf16(const float* ql, const void* K, const void* V, i
   static std::atomic<unsigned long long> lds_set[2];
   if (const hipError_t e = allow_lds((const void*)kernel, 160 * 1024, lds_set[fuse_h]); e != hipSuccess)
     return e;
-  const int grid = ((s.BH + 7) / 8) * 8 * a.tiles * nch;
+  const int grid = s.BH >= 8 ? ((s.BH + 7) / 8) * 8 * a.tiles * nch : s.BH * a.tiles * nch;
   kernel<<<grid, 64 * lmk::NW, lds, st>>>(a);
   if (nch == 1) return hipGetLastError();
   const long long rws = (long long)s.BH * s.m;

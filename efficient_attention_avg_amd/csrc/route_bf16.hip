@@ -17,7 +17,10 @@
 // group_bf16_kernel: one workgroup per head.  Run histograms -> per-expert
 // counts and offsets -> per-run starting positions; the sixteen waves then
 // place the runs' queries stably, 64 at a time: queries sharing a route are
-// found by ballot and ranked by lane order.
+// found by ballot and ranked by lane order.  With few heads (fewer than 128)
+// the workgroup only writes the starting positions back over the run
+// histograms, and group_place_kernel places each run's queries with a wave
+// of its own, so that the placement spreads over the GPU.
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
@@ -219,8 +222,11 @@ __global__ __launch_bounds__(64 * RW) void route_bf16_kernel(const uint16_t* __r
   for (int e = tid; e < nr * m; e += 64 * RW) dst[e] = hist[e];
 }
 
+// PLACE: place the queries here (else write each run's starting positions
+// over its histogram for group_place_kernel).
+template <bool PLACE>
 __global__ __launch_bounds__(1024) void group_bf16_kernel(const int32_t* __restrict__ route,
-                                                         const int32_t* __restrict__ chist,
+                                                         int32_t* __restrict__ chist,
                                                          int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ perm, int N, int m,
@@ -231,7 +237,7 @@ __global__ __launch_bounds__(1024) void group_bf16_kernel(const int32_t* __restr
   int* tot = gsm + nchunks * m;     // [m]
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int nt = blockDim.x, nw = nt >> 6;
-  const int32_t* ch = chist + (size_t)bh * nchunks * m;
+  int32_t* ch = chist + (size_t)bh * nchunks * m;
   // the chunk histograms into LDS in one coalesced sweep (independent loads),
   // then per expert: totals and each chunk's count before it
   for (int it = tid; it < nchunks * m; it += nt) cur[it] = ch[it];
@@ -259,6 +265,10 @@ __global__ __launch_bounds__(1024) void group_bf16_kernel(const int32_t* __restr
   }
   __syncthreads();
   for (int it = tid; it < nchunks * m; it += nt) cur[it] += tot[it % m];
+  if (!PLACE) {
+    for (int it = tid; it < nchunks * m; it += nt) ch[it] = cur[it];
+    return;
+  }
   __syncthreads();
   // stable scatter: wave w takes chunks w, w + nw, ...; runs of 64 queries in order
   const int32_t* r = route + (size_t)bh * N;
@@ -285,14 +295,68 @@ __global__ __launch_bounds__(1024) void group_bf16_kernel(const int32_t* __restr
   }
 }
 
+// One wave per (run, head): the run's qc items placed stably from its
+// starting positions (written by group_bf16_kernel<false>), 64 at a time,
+// with the routes of the next GU steps requested together.
+constexpr int GU = 4;
+
+__global__ __launch_bounds__(64) void group_place_kernel(const int32_t* __restrict__ route,
+                                                         const int32_t* __restrict__ pos,
+                                                         int32_t* __restrict__ perm, int N, int m,
+                                                         int nruns, int qc) {
+  extern __shared__ int cc[];  // [m]: next free position per expert
+  const int run = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
+  const int32_t* ps = pos + ((size_t)bh * nruns + run) * m;
+  for (int e = lane; e < m; e += 64) cc[e] = ps[e];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int32_t* r = route + (size_t)bh * N;
+  int32_t* pm = perm + (size_t)bh * N;
+  const int lo = run * qc, hi = min(N, lo + qc);
+  for (int b0 = lo; b0 < hi; b0 += 64 * GU) {
+    int ev[GU];
+#pragma unroll
+    for (int u = 0; u < GU; ++u) {
+      const int n = b0 + 64 * u + lane;
+      ev[u] = n < hi ? r[n] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < GU; ++u) {
+      const int n = b0 + 64 * u + lane, e = ev[u];
+      uint64_t left = __ballot(e >= 0);
+      while (left) {
+        const int src = __ffsll((unsigned long long)left) - 1;
+        const int v = __shfl(e, src, 64);
+        const uint64_t same = __ballot(e == v);
+        const int at = cc[v];  // read by every lane before the update below
+        if (e == v) pm[at + __popcll(same & ((1ull << lane) - 1ull))] = n;
+        __builtin_amdgcn_wave_barrier();
+        if (lane == src) cc[v] = at + __popcll(same);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        left &= ~same;
+      }
+    }
+  }
+}
+
 }  // namespace rt
 
+// Grouping in two kernels (starting positions per head, then one wave per
+// run placing its queries) when there are too few heads for one workgroup
+// per head to fill the GPU.
+static bool group_split(const Shape& s) { return s.BH < 128; }
+
 // Run length R: a multiple of 64, doubled until a head's run histograms fit
-// in 64 KB of LDS.  Queries per route workgroup qc: a multiple of R such that
-// about 768 workgroups cover all heads.
+// in 64 KB of LDS (128 KB when the grouping is split: that workgroup then
+// holds nothing else, and shorter runs give the routing and placement
+// kernels more workgroups).  Queries per route workgroup qc: a multiple of R
+// such that about 768 workgroups cover all heads.
 static void route_chunking(const Shape& s, int& qc, int& nchunks, int& R, int& nruns) {
+  const size_t budget = (group_split(s) ? 128 : 64) * 1024;
   R = 64;
-  while ((size_t)((s.N + R - 1) / R) * s.m * 4 > 64 * 1024 && R < s.N) R *= 2;
+  while ((size_t)((s.N + R - 1) / R) * s.m * 4 > budget && R < s.N) R *= 2;
   nruns = (s.N + R - 1) / R;
   int parts = (768 + s.BH - 1) / s.BH;
   if (parts > nruns) parts = nruns;
@@ -339,19 +403,25 @@ hipError_t launch_route_bf16(const void* Q, const float* ql, int32_t* route, int
   return hipGetLastError();
 }
 
-hipError_t launch_group_bf16(const int32_t* route, const int32_t* chist, int32_t* counts,
+hipError_t launch_group_bf16(const int32_t* route, int32_t* chist, int32_t* counts,
                              int32_t* offsets, int32_t* perm, const Shape& s, hipStream_t st) {
   int qc, nchunks, R, nruns;
   route_chunking(s, qc, nchunks, R, nruns);
   const size_t lds = ((size_t)nruns * s.m + s.m) * 4;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  static std::atomic<unsigned long long> lds_set;
-  if (const hipError_t e = allow_lds((const void*)rt::group_bf16_kernel, 160 * 1024, lds_set);
+  const bool split = group_split(s);
+  auto kernel = split ? rt::group_bf16_kernel<false> : rt::group_bf16_kernel<true>;
+  static std::atomic<unsigned long long> lds_set[2];
+  if (const hipError_t e = allow_lds((const void*)kernel, 160 * 1024, lds_set[split ? 1 : 0]);
       e != hipSuccess)
     return e;
   // the sort runs over the N * s (query, rank) items, R * s of them per run
-  rt::group_bf16_kernel<<<s.BH, 1024, lds, st>>>(route, chist, counts, offsets, perm, s.N * s.s,
-                                                 s.m, nruns, R * s.s);
+  kernel<<<s.BH, 1024, lds, st>>>(route, chist, counts, offsets, perm, s.N * s.s, s.m, nruns,
+                                  R * s.s);
+  if (!split) return hipGetLastError();
+  if (const hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  rt::group_place_kernel<<<dim3(nruns, s.BH), 64, (size_t)s.m * 4, st>>>(
+      route, chist, perm, s.N * s.s, s.m, nruns, R * s.s);
   return hipGetLastError();
 }
 
