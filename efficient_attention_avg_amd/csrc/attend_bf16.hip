@@ -58,6 +58,7 @@ struct Args {
   float2* pml;   // s > 1: each item's softmax reference maximum and sum
   int BH, N, m, k, parts;  // workgroups per head
   int s, shared;
+  int kres;  // expert slots staged at once: k rounded up to EC (all resident), or EC
 };
 
 // Upper bound on a head's passes (TQ-item runs of one expert's items):
@@ -70,21 +71,23 @@ __host__ __device__ inline int max_passes(int m, int N, int s) {
 // of one expert's items), [first item's place in the expert order, count,
 // k key ids]; the head's expert offsets sit beside it.
 // A workgroup takes at most ceil(tmax / parts) passes, so at most that many
-// segments (each holds at least one of its passes).
+// segments (each holds at least one of its passes).  Q_L is held as bf16 hi +
+// lo, or (ql16) as one f16 copy; kres expert slots of K and V rows are staged
+// at a time.
 struct Lay {
   int mp, vlt_stride, ew, ts;
   int off_qlh, off_qll, off_vlt, off_ke, off_vet, off_tab, off_elist, off_scan, off_offs, bytes;
-  __host__ __device__ Lay(int m, int k, int parts, int tmax) {
+  __host__ __device__ Lay(int m, int k, int parts, int tmax, bool ql16, int kres) {
     mp = (m + 31) & ~31;
     vlt_stride = mp * 2 + 16;
     ew = (tmax + parts - 1) / parts;
     ts = 2 + k;
     off_qlh = 0;
     off_qll = off_qlh + mp * 128;
-    off_vlt = off_qll + mp * 128;
+    off_vlt = off_qll + (ql16 ? 0 : mp * 128);
     off_ke = off_vlt + 64 * vlt_stride;
-    off_vet = off_ke + EC * 128;
-    off_tab = off_vet + EC * EV_STRIDE;
+    off_vet = off_ke + kres * 128;
+    off_tab = off_vet + kres * EV_STRIDE;
     off_elist = off_tab + ew * ts * 4;
     off_scan = off_elist + (ew + 1) * 4;  // [10] ints: the deal's wave totals and bounds
     off_offs = off_scan + 16 * 4;         // the head's m + 1 expert offsets
@@ -165,10 +168,18 @@ __device__ __forceinline__ void store_out(Rsrc outr, const PassOut& o, int g, in
   st16_nt(outr, lo ? r3 : v2, lo ? other + 192 : own + 128);
 }
 
+// QL16: Q_L as one f16 copy (the shared logits on f16 MFMA, one product per
+// 32 channels instead of the hi and lo products), which leaves room to keep
+// all of an expert's k slots in LDS for large m and k.  The shared logits only
+// weigh values: top-k sets and routes are decided elsewhere.
+// RES: every slot of the expert resident in LDS (staged once per segment;
+// a.kres = k rounded up to 64), else 64-slot chunks re-staged per pass.
+template <bool QL16, bool RES>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void attend_bf16_kernel(Args a) {
   extern __shared__ __attribute__((aligned(16))) char sm[];
-  const Lay L(a.m, a.k, a.parts, max_passes(a.m, a.N, a.s));
+  const Lay L(a.m, a.k, a.parts, max_passes(a.m, a.N, a.s), QL16, RES ? a.kres : EC);
+  constexpr bool res = RES;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   // with 8 or more heads a head's workgroups share one XCD (and its L2:
@@ -305,15 +316,20 @@ void attend_bf16_kernel(Args a) {
         const int it = base + 256 * u + tid, row = it >> 4, q4 = it & 15;
         if (it >= L.mp * 16) break;
         const float f4[4] = {fq[u].x, fq[u].y, fq[u].z, fq[u].w};
-        uint32_t h[4], l[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          h[i] = bf16_rne_bits(f4[i]);
-          l[i] = bf16_rne_bits(f4[i] - bf16_bits_to_f32(h[i]));
-        }
         const int off = rc(row, q4 >> 1) + (q4 & 1) * 8;
-        *reinterpret_cast<u32x2*>(sm + L.off_qlh + off) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-        *reinterpret_cast<u32x2*>(sm + L.off_qll + off) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+        if (QL16) {
+          *reinterpret_cast<u32x2*>(sm + L.off_qlh + off) =
+              u32x2{pk_f16(f4[0], f4[1]), pk_f16(f4[2], f4[3])};
+        } else {
+          uint32_t h[4], l[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            h[i] = bf16_rne_bits(f4[i]);
+            l[i] = bf16_rne_bits(f4[i] - bf16_bits_to_f32(h[i]));
+          }
+          *reinterpret_cast<u32x2*>(sm + L.off_qlh + off) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+          *reinterpret_cast<u32x2*>(sm + L.off_qll + off) = u32x2{l[0] | (l[1] << 16), l[2] | (l[3] << 16)};
+        }
         const float vv[4] = {fv[u].x, fv[u].y, fv[u].z, fv[u].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -357,9 +373,10 @@ void attend_bf16_kernel(Args a) {
       r.q1r = *reinterpret_cast<const u32x4*>(Qh + (size_t)n * 64 + 32 + 8 * g);
     }
   };
-  auto store_rows = [&](const Rows& r) {
-    *reinterpret_cast<u32x4*>(sm + L.off_ke + rc(ksl, kc)) = r.k0;
-    *reinterpret_cast<u32x4*>(sm + L.off_ke + rc(ksl + 32, kc)) = r.k1;
+  // into LDS slots [base, base + 64)
+  auto store_rows = [&](const Rows& r, int base) {
+    *reinterpret_cast<u32x4*>(sm + L.off_ke + rc(base + ksl, kc)) = r.k0;
+    *reinterpret_cast<u32x4*>(sm + L.off_ke + rc(base + ksl + 32, kc)) = r.k1;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const u32x4 x = h ? r.v1 : r.v0;
@@ -367,25 +384,46 @@ void attend_bf16_kernel(Args a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         f[q] = pk_f16(__uint_as_float(x[q] << 16), __uint_as_float(x[q] & 0xFFFF0000u));
-      *reinterpret_cast<u32x4*>(sm + L.off_vet + (2 * vp + h) * EV_STRIDE + 16 * vc) = f;
+      *reinterpret_cast<u32x4*>(sm + L.off_vet + (base + 2 * vp + h) * EV_STRIDE + 16 * vc) = f;
+    }
+  };
+  // resident slots: segment j's slots past the first 64 (the first chunk is
+  // prefetched), up to three chunks' loads issued before any store
+  auto stage_rest = [&](int j) {
+    for (int s0 = EC; s0 < k; s0 += 3 * EC) {
+      Rows r[3];
+#pragma unroll
+      for (int u = 0; u < 3; ++u)
+        if (s0 + u * EC < k) load_rows(j, s0 + u * EC, r[u]);
+#pragma unroll
+      for (int u = 0; u < 3; ++u)
+        if (s0 + u * EC < k) store_rows(r[u], s0 + u * EC);
     }
   };
 
   // logits of 32 shared entries (landmarks 32c ..) into x[0..8); -inf for
-  // a lane whose item does not take the shared entries (rank j > 0)
+  // a lane whose item does not take the shared entries (rank j > 0).  (QL16:
+  // bq0 / bq1 are the query's channels as f16.)
   auto shared_logits = [&](int c, const u32x4 bq0, const u32x4 bq1, float* x, bool sh) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int row = 32 * c + 16 * h + c16;
-      const u32x4 ah0 = *reinterpret_cast<const u32x4*>(sm + L.off_qlh + rc(row, g));
-      const u32x4 al0 = *reinterpret_cast<const u32x4*>(sm + L.off_qll + rc(row, g));
-      const u32x4 ah1 = *reinterpret_cast<const u32x4*>(sm + L.off_qlh + rc(row, 4 + g));
-      const u32x4 al1 = *reinterpret_cast<const u32x4*>(sm + L.off_qll + rc(row, 4 + g));
       f32x4 s = zero4();
-      s = mfma_bf16(ah0, bq0, s);
-      s = mfma_bf16(al0, bq0, s);
-      s = mfma_bf16(ah1, bq1, s);
-      s = mfma_bf16(al1, bq1, s);
+      if (QL16) {
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(sm + L.off_qlh + rc(row, g));
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(sm + L.off_qlh + rc(row, 4 + g));
+        s = mfma_f16(a0, bq0, s);
+        s = mfma_f16(a1, bq1, s);
+      } else {
+        const u32x4 ah0 = *reinterpret_cast<const u32x4*>(sm + L.off_qlh + rc(row, g));
+        const u32x4 al0 = *reinterpret_cast<const u32x4*>(sm + L.off_qll + rc(row, g));
+        const u32x4 ah1 = *reinterpret_cast<const u32x4*>(sm + L.off_qlh + rc(row, 4 + g));
+        const u32x4 al1 = *reinterpret_cast<const u32x4*>(sm + L.off_qll + rc(row, 4 + g));
+        s = mfma_bf16(ah0, bq0, s);
+        s = mfma_bf16(al0, bq0, s);
+        s = mfma_bf16(ah1, bq1, s);
+        s = mfma_bf16(al1, bq1, s);
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) x[4 * h + r] = s[r];
     }
@@ -410,11 +448,12 @@ void attend_bf16_kernel(Args a) {
       av[ct] = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
     }
   };
-  // logits of 32 routed entries (LDS slots 32hs .., expert slots s0 + 32hs ..)
-  auto routed_logits = [&](int s0, int hs, const u32x4 bq0, const u32x4 bq1, float* x) {
+  // logits of 32 routed entries (expert slots s0 + 32hs .., at LDS slots
+  // lb + 32hs ..: lb = s0 when every slot is resident, else 0)
+  auto routed_logits = [&](int s0, int lb, int hs, const u32x4 bq0, const u32x4 bq1, float* x) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int row = 32 * hs + 16 * h + c16;
+      const int row = lb + 32 * hs + 16 * h + c16;
       const u32x4 a0 = *reinterpret_cast<const u32x4*>(sm + L.off_ke + rc(row, g));
       const u32x4 a1 = *reinterpret_cast<const u32x4*>(sm + L.off_ke + rc(row, 4 + g));
       f32x4 s = zero4();
@@ -434,8 +473,8 @@ void attend_bf16_kernel(Args a) {
   // V^T[ch 16ct + c16][slots 32hs + 4g .., 32hs + 16 + 4g ..] by transposing
   // reads: lane points at slot 32hs + 4g + (c16 >> 2) (+ 16), channels
   // 16ct + 4 (c16 & 3) ..
-  auto routed_av = [&](int hs, u32x4 (&av)[4]) {
-    const char* vr = sm + L.off_vet + (32 * hs + 4 * g + (c16 >> 2)) * EV_STRIDE + 8 * (c16 & 3);
+  auto routed_av = [&](int lb, int hs, u32x4 (&av)[4]) {
+    const char* vr = sm + L.off_vet + (lb + 32 * hs + 4 * g + (c16 >> 2)) * EV_STRIDE + 8 * (c16 & 3);
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
       const u32x2 lo2 = lds_tr16(vr + 32 * ct);
@@ -462,42 +501,54 @@ void attend_bf16_kernel(Args a) {
     // items take them when s > 1)
     const bool sh = shared && (S == 1 || item % S == 0);
     if (wave_has && __ballot(sh) != 0) {
+      // (QL16: the query's channels as f16, exact for |q| < 65504)
+      u32x4 sq0 = bq0, sq1 = bq1;
+      if (QL16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          sq0[q] = pk_f16(__uint_as_float(bq0[q] << 16), __uint_as_float(bq0[q] & 0xFFFF0000u));
+          sq1[q] = pk_f16(__uint_as_float(bq1[q] << 16), __uint_as_float(bq1[q] & 0xFFFF0000u));
+        }
+      }
       const int nc = L.mp / 32;
       int c = 0;
       for (; c + 2 <= nc; c += 2) {
         float x[16];
-        shared_logits(c, bq0, bq1, x, sh);
-        shared_logits(c + 1, bq0, bq1, x + 8, sh);
+        shared_logits(c, sq0, sq1, x, sh);
+        shared_logits(c + 1, sq0, sq1, x + 8, sh);
         softmax_update<2>(x, [&](int i, u32x4 (&av)[4]) { shared_av(c + i, av); }, mref, o.acc,
                           lsum);
       }
       if (c < nc) {
         float x[8];
-        shared_logits(c, bq0, bq1, x, sh);
+        shared_logits(c, sq0, sq1, x, sh);
         softmax_update<1>(x, [&](int, u32x4 (&av)[4]) { shared_av(c, av); }, mref, o.acc, lsum);
       }
     }
-    // ---- routed entries: the expert's keys, 64 slots per LDS chunk
+    // ---- routed entries: the expert's keys, 64 slots per step (from the
+    // resident slots, or from an LDS chunk staged for the step)
     for (int s0 = 0; s0 < k; s0 += EC) {
-      if (k > EC && (s0 > 0 || p0 > 0)) {
+      if (!res && k > EC && (s0 > 0 || p0 > 0)) {
         // slots past the first 64, or a later pass over a multi-chunk expert
         __syncthreads();  // the previous chunk's readers are done
         Rows r;
         load_rows(j, s0, r);
-        store_rows(r);
+        store_rows(r, 0);
         __syncthreads();
       }
+      const int lb = res ? s0 : 0;
       if (wave_has) {
         if (s0 + 32 < k) {
           float x[16];
-          routed_logits(s0, 0, bq0, bq1, x);
-          routed_logits(s0, 1, bq0, bq1, x + 8);
-          softmax_update<2>(x, [&](int i, u32x4 (&av)[4]) { routed_av(i, av); }, mref, o.acc,
+          routed_logits(s0, lb, 0, bq0, bq1, x);
+          routed_logits(s0, lb, 1, bq0, bq1, x + 8);
+          softmax_update<2>(x, [&](int i, u32x4 (&av)[4]) { routed_av(lb, i, av); }, mref, o.acc,
                             lsum);
         } else {
           float x[8];
-          routed_logits(s0, 0, bq0, bq1, x);
-          softmax_update<1>(x, [&](int, u32x4 (&av)[4]) { routed_av(0, av); }, mref, o.acc, lsum);
+          routed_logits(s0, lb, 0, bq0, bq1, x);
+          softmax_update<1>(x, [&](int, u32x4 (&av)[4]) { routed_av(lb, 0, av); }, mref, o.acc,
+                            lsum);
         }
       }
     }
@@ -521,7 +572,8 @@ void attend_bf16_kernel(Args a) {
   for (int j = 0; j < nexp; ++j) {
     const int* te = tab + j * L.ts;
     const int q0 = te[0], cnt = te[1];
-    store_rows(rows);  // waits for this expert's rows (and the stores before them)
+    if (res) stage_rest(j);
+    store_rows(rows, 0);  // waits for this segment's first rows (and the stores before them)
     const u32x4 bq0 = rows.q0r, bq1 = rows.q1r;
     const int it0 = rows.it0;
     // take the Q rows now too: a wait after the stores below would also wait
@@ -607,27 +659,68 @@ static int attend_parts(const Shape& s) {
   return parts;
 }
 
+namespace {
+struct AttCfg {
+  int parts, kres, bytes;
+  bool ql16;
+};
+}  // namespace
+
+// The LDS layout: the one that leaves the most resident workgroups per CU (up
+// to the three the register budget allows); on a tie, all of an expert's
+// slots resident before 64-slot chunks re-staged per pass, and Q_L as bf16
+// hi + lo before one f16 copy.  A layout that does not fit may take more
+// workgroups per head (a smaller segment table): up to twice as many for the
+// resident layouts, as many as the head has passes for the chunked one.
+static AttCfg attend_config(const Shape& s) {
+  constexpr int cap = 160 * 1024;
+  const int base = attend_parts(s), tmax = att::max_passes(s.m, s.N, s.s);
+  const int kfull = (s.k + att::EC - 1) / att::EC * att::EC;
+  struct Opt {
+    bool ql16;
+    int kres, pmax;
+  };
+  const int p2 = 2 * base < tmax ? 2 * base : tmax;
+  const Opt opts[3] = {{false, kfull, p2}, {true, kfull, p2}, {false, att::EC, tmax}};
+  AttCfg best{0, 0, 0, false};
+  int best_occ = 0;
+  for (const Opt& o : opts) {
+    int p = base;
+    while (att::Lay(s.m, s.k, p, tmax, o.ql16, o.kres).bytes > cap && p < o.pmax) ++p;
+    const int bytes = att::Lay(s.m, s.k, p, tmax, o.ql16, o.kres).bytes;
+    if (bytes > cap) continue;
+    const int occ = cap / bytes < 3 ? cap / bytes : 3;
+    if (occ > best_occ) {
+      best_occ = occ;
+      best = AttCfg{p, o.kres, bytes, o.ql16};
+    }
+  }
+  return best;  // parts == 0: no layout fits
+}
+
 hipError_t launch_attend_bf16(const void* Q, const void* K, const void* V, const float* ql,
                               const float* vl, const int32_t* idx, const int32_t* offsets,
                               const int32_t* perm, float* out, void* partial, const Shape& s,
                               hipStream_t st) {
-  int parts = attend_parts(s);
-  const int tmax = att::max_passes(s.m, s.N, s.s);
-  // the table must fit next to the rest: fewer passes per workgroup if not
-  while (att::Lay(s.m, s.k, parts, tmax).bytes > 160 * 1024 && parts < tmax) ++parts;
-  const att::Lay L(s.m, s.k, parts, tmax);
-  if (L.bytes > 160 * 1024) return hipErrorInvalidValue;
-  static std::atomic<unsigned long long> lds_set;
-  if (const hipError_t e = allow_lds((const void*)att::attend_bf16_kernel, 160 * 1024, lds_set);
+  const AttCfg c = attend_config(s);
+  if (c.parts == 0) return hipErrorInvalidValue;
+  // (f16 Q_L is only chosen with resident slots: three instances)
+  const bool res = c.kres > att::EC;
+  auto kernel = c.ql16 ? att::attend_bf16_kernel<true, true>
+                : res  ? att::attend_bf16_kernel<false, true>
+                       : att::attend_bf16_kernel<false, false>;
+  const int form = c.ql16 ? 2 : res ? 1 : 0;
+  static std::atomic<unsigned long long> lds_set[3];
+  if (const hipError_t e = allow_lds((const void*)kernel, 160 * 1024, lds_set[form]);
       e != hipSuccess)
     return e;
   if (s.s > 1 && !partial) return hipErrorInvalidValue;
   float* part = s.s > 1 ? (float*)partial : out;
   float2* pml = s.s > 1 ? (float2*)((char*)partial + (size_t)s.BH * s.N * s.s * 64 * 4) : nullptr;
   att::Args a{(const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, ql, vl, idx, offsets,
-              perm, part, pml, s.BH, s.N, s.m, s.k, parts, s.s, s.shared ? 1 : 0};
-  const int grid = s.BH >= 8 ? ((s.BH + 7) / 8) * 8 * parts : s.BH * parts;
-  att::attend_bf16_kernel<<<grid, 256, L.bytes, st>>>(a);
+              perm, part, pml, s.BH, s.N, s.m, s.k, c.parts, s.s, s.shared ? 1 : 0, c.kres};
+  const int grid = s.BH >= 8 ? ((s.BH + 7) / 8) * 8 * c.parts : s.BH * c.parts;
+  kernel<<<grid, 256, c.bytes, st>>>(a);
   return hipGetLastError();
 }
 

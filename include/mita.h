@@ -28,11 +28,13 @@
  *     misaligned one is MITA_ERR_INVALID_ARG).  Q, K, V are fp32 or bf16
  *     (`in_dtype`); out is always fp32 (no output-type argument: a bf16
  *     output would round values near 5 by more than 1e-2).
- *   - Precondition on bf16 inputs: every |V| < 65504.  The value products run
- *     on f16 matrix cores (V, V_L and the softmax weights are staged as f16),
- *     so larger values would become inf.  Nothing checks this (it would cost
- *     a pass over V); the seeded workloads stay below 40.  fp32 inputs have
- *     no such bound.
+ *   - Precondition on bf16 inputs: every |V| < 65504, and every |Q| < 65504.
+ *     The value products run on f16 matrix cores (V, V_L and the softmax
+ *     weights are staged as f16), and for large m and k (when keeping all of
+ *     an expert's k rows in LDS needs the room) the shared logits q . Q_L run
+ *     on f16 matrix cores too (q and Q_L as f16), so larger values would
+ *     become inf.  Nothing checks this (it would cost a pass over Q and V);
+ *     the seeded workloads stay below 40.  fp32 inputs have no such bound.
  *   - Index outputs are int32.  idx rows list key ids in ascending order.
  *   - d must be 64 (MITA_ERR_UNSUPPORTED otherwise).
  *   - Arguments are validated on the host before anything is enqueued; on a
