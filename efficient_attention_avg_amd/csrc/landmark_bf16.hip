@@ -46,7 +46,7 @@ namespace mita {
 namespace lmk {
 
 constexpr int KB = 64;                  // keys per block
-constexpr int NW = 4;                   // waves per workgroup
+constexpr int NW4 = 4;                  // waves per workgroup (8 where one workgroup fills a CU's LDS)
 constexpr int TL = 2;                   // 16-row MFMA tiles per workgroup
 constexpr int ROWS = 16 * TL;           // landmark rows per workgroup
 constexpr int V_STRIDE = 64 * 2 + 16;  // bytes per staged V row: 64 f16 channels + pad
@@ -76,10 +76,14 @@ constexpr int OFF_HIST = 0;
 constexpr int OFF_ROW = OFF_HIST + ROWS * HIST_STRIDE;
 constexpr int OFF_FLAG = OFF_ROW + ROWS * (int)sizeof(RowState);
 constexpr int OFF_QL = (OFF_FLAG + 16 + 15) & ~15;  // Q_L B operands: [tl][ks][hi, lo][lane] x 16 B
-constexpr int OFF_SAMP = OFF_QL + TL * 2 * 2 * 64 * 16;  // [wave][row] first-block (min, max)
-constexpr int OFF_UNION = OFF_SAMP + NW * ROWS * 8;
-constexpr int VALUES_BYTES = NW * VT_BYTES;  // phase V staging (the merge area aliases it)
-static_assert(NW * ROWS * MERGE_STRIDE * 4 <= VALUES_BYTES, "merge area fits in the staging");
+constexpr int OFF_UNION = OFF_QL + TL * 2 * 2 * 64 * 16;
+// The union holds phase V's staging (one VT_BYTES slot per wave; the merge
+// area aliases it), then the rows' candidate buffers; the [wave][row]
+// first-block (min, max) samples follow it.
+__host__ __device__ constexpr int union_bytes(int cap, int nw) {
+  return ROWS * cap * 8 > nw * VT_BYTES ? ROWS * cap * 8 : nw * VT_BYTES;
+}
+static_assert(ROWS * MERGE_STRIDE * 4 <= VT_BYTES, "a wave's merge area fits in its staging slot");
 static_assert(BITMAP_MAX_N / 8 <= HIST_STRIDE && LIST_MAX * 8 <= HIST_STRIDE, "row space");
 // a chunk's key bitmap, padded to whole 16-byte groups, and its 16-bit word
 // prefixes share one row's space
@@ -117,10 +121,8 @@ struct Chunk {
   int chunk, blk0, blk1, kbase, kend, kk;
 };
 
-__host__ __device__ constexpr size_t lds_bytes(int cap) {
-  return (size_t)OFF_UNION + ((size_t)ROWS * cap * 8 > (size_t)VALUES_BYTES
-                                  ? (size_t)ROWS * cap * 8
-                                  : (size_t)VALUES_BYTES);
+__host__ __device__ constexpr size_t lds_bytes(int cap, int nw) {
+  return (size_t)OFF_UNION + (size_t)union_bytes(cap, nw) + (size_t)nw * ROWS * 8;
 }
 
 // A operands of one 64-key block: lane (g, c16) holds key 16kt + c16,
@@ -504,8 +506,13 @@ __device__ void rows_final(char* sm, const Args& a, const Chunk& ch, const int (
 
 // FUSE (a.fuse_h): the histogram is built during pass V; a template
 // parameter so that each form gets its own register allocation.
-template <bool FUSE>
+// NW: waves per workgroup (4, or 8 where one workgroup's LDS fills a CU
+// anyway); the waves split the keys, and lane group g of wave w finishes
+// rows 4w + g + 4 NW i (RPG of them).
+template <bool FUSE, int NW>
 __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
+  constexpr int RPG = ROWS / (4 * NW);
+  static_assert(RPG * 4 * NW == ROWS, "rows split evenly over the lane groups");
   extern __shared__ __attribute__((aligned(16))) char sm[];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -610,7 +617,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
             }
         }
       }
-      float2* samp = reinterpret_cast<float2*>(sm + OFF_SAMP);
+      float2* samp = reinterpret_cast<float2*>(sm + OFF_UNION + union_bytes(a.cap, NW));
 #pragma unroll
       for (int tl = 0; tl < TL; ++tl) {
         slo[tl] = fminf(slo[tl], __shfl_xor(slo[tl], 16, 64));
@@ -871,10 +878,10 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
 
   __syncthreads();
   // the bin holding each row's k-th best: group g of wave w takes rows
-  // 4w + g + 16i
+  // 4w + g + 4 NW i
 #pragma unroll
-  for (int i = 0; i < TL; ++i) {
-    const int r = 4 * w + g + 16 * i;
+  for (int i = 0; i < RPG; ++i) {
+    const int r = 4 * w + g + 4 * NW * i;
     const uint32_t* hrow = reinterpret_cast<const uint32_t*>(sm + OFF_HIST + r * HIST_STRIDE);
     uint32_t cb[16];
 #pragma unroll
@@ -1057,8 +1064,8 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
         }
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < TL; ++i) {
-          const int r = 4 * w + g + 16 * i;
+        for (int i = 0; i < RPG; ++i) {
+          const int r = 4 * w + g + 4 * NW * i;
           const bool work = row0 + r < a.m && rows[r].over && rows[r].cnt > a.cap - KB;
           if (__ballot(work) != 0) row_cut(sm, a, ch.kk, r, work, c16, g);
         }
@@ -1069,15 +1076,15 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
   __syncthreads();
 
   // ------------------------------------------------------------ F: final
-  // group g of wave w takes rows 4w + g + 16i, all TL of them together
+  // group g of wave w takes rows 4w + g + 4 NW i, all RPG of them together
   {
-    int lr[TL];
-    bool work[TL];
-    int32_t* outk[TL];
-    float* outs[TL];
+    int lr[RPG];
+    bool work[RPG];
+    int32_t* outk[RPG];
+    float* outs[RPG];
 #pragma unroll
-    for (int i = 0; i < TL; ++i) {
-      lr[i] = 4 * w + g + 16 * i;
+    for (int i = 0; i < RPG; ++i) {
+      lr[i] = 4 * w + g + 4 * NW * i;
       work[i] = row0 + lr[i] < a.m;
       const size_t row = (size_t)bh * a.m + (work[i] ? row0 + lr[i] : 0);
       if (a.nch == 1) {
@@ -1089,7 +1096,7 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
         outs[i] = a.cand_s + at;
       }
     }
-    rows_final<TL>(sm, a, ch, lr, work, c16, g, outk, outs);
+    rows_final<RPG>(sm, a, ch, lr, work, c16, g, outk, outs);
   }
 }
 
@@ -1330,7 +1337,7 @@ static void landmark_chunks(const Shape& s, int& nch, int& cblk) {
 }
 
 bool landmark_bf16_supported(const Shape& s) {
-  return s.bf16 && landmark_cap(s) > 0 && lmk::lds_bytes(landmark_cap(s)) <= 160 * 1024;
+  return s.bf16 && landmark_cap(s) > 0 && lmk::lds_bytes(landmark_cap(s), lmk::NW4) <= 160 * 1024;
 }
 
 size_t landmark_bf16_scratch_bytes(const Shape& s) {
@@ -1362,14 +1369,22 @@ hipError_t launch_landmark_bf16(const float* ql, const void* K, const void* V, i
               landmark_cap(s), (s.m + lmk::ROWS - 1) / lmk::ROWS, nch, cblk, fuse_h, cand_s,
               cand_k, vlpart, stats};
   if (a.cap == 0) return hipErrorInvalidValue;
-  const size_t lds = lmk::lds_bytes(a.cap);
-  if (lds > 160 * 1024) return hipErrorInvalidValue;
-  auto kernel = fuse_h ? lmk::landmark_kernel<true> : lmk::landmark_kernel<false>;
-  static std::atomic<unsigned long long> lds_set[2];
-  if (const hipError_t e = allow_lds((const void*)kernel, 160 * 1024, lds_set[fuse_h]); e != hipSuccess)
+  // eight waves where a four-wave workgroup's LDS (the candidate buffers for
+  // k >= 128) already leaves room for only one workgroup per CU: the same
+  // LDS then carries twice the waves streaming the keys
+  constexpr size_t cu_lds = 160 * 1024;
+  const bool wide = 2 * lmk::lds_bytes(a.cap, 4) > cu_lds && lmk::lds_bytes(a.cap, 8) <= cu_lds;
+  const int nw = wide ? 8 : lmk::NW4;
+  const size_t lds = lmk::lds_bytes(a.cap, nw);
+  if (lds > cu_lds) return hipErrorInvalidValue;
+  auto kernel = fuse_h ? (wide ? lmk::landmark_kernel<true, 8> : lmk::landmark_kernel<true, 4>)
+                       : (wide ? lmk::landmark_kernel<false, 8> : lmk::landmark_kernel<false, 4>);
+  static std::atomic<unsigned long long> lds_set[4];
+  if (const hipError_t e = allow_lds((const void*)kernel, 160 * 1024, lds_set[fuse_h + 2 * wide]);
+      e != hipSuccess)
     return e;
   const int grid = s.BH >= 8 ? ((s.BH + 7) / 8) * 8 * a.tiles * nch : s.BH * a.tiles * nch;
-  kernel<<<grid, 64 * lmk::NW, lds, st>>>(a);
+  kernel<<<grid, 64 * nw, lds, st>>>(a);
   if (nch == 1) return hipGetLastError();
   const long long rws = (long long)s.BH * s.m;
   lmk::merge_kernel<<<(unsigned)((rws + lmk::MERGE_WAVES - 1) / lmk::MERGE_WAVES),
