@@ -1107,10 +1107,16 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
 // the whole list; the row's k best (larger score, then lower key id) are
 // found by a 256-bin histogram over the entries' range: every entry above the
 // boundary bin is taken and the boundary bin's entries are ranked among
-// themselves (through an LDS list, or, when more than LISTCAP share the bin,
-// against every entry in it); winners are written in list order, which is
-// ascending key order.
-constexpr int MERGE_WAVES = 4;
+// themselves (listed in LDS and ranked once: the listed entry of rank need - 1
+// is the cut, and a boundary entry wins when it is at least as good; or, when
+// more than LISTCAP share the bin, each against every entry in it); winners
+// are written in list order, which is ascending key order.
+// MW rows per workgroup (a wave each) and MU entries per lane in flight:
+// every loop over the candidate list reads MU entries per lane before using
+// any.  Many short rows (long-16k: 8,192 rows of 1,024) take MW = 4, MU = 8;
+// few long ones (a 1-D sequence, seq-256k: 512 rows of 16,384) a workgroup
+// per row, so that they spread over every CU, and MU = 32 (8 round trips per
+// pass instead of 32).
 constexpr int LISTCAP = 256;
 
 __device__ __forceinline__ int wave_suffix(int v, int lane) {
@@ -1123,17 +1129,14 @@ __device__ __forceinline__ int wave_suffix(int v, int lane) {
   return v;
 }
 
-// Entries per lane in flight: every loop over the candidate list reads
-// MU entries per lane (MU * 64 per wave) before using any, so a row's list
-// takes n / (64 MU) round trips per pass instead of n / 64.
-constexpr int MU = 8;
-
-__global__ __launch_bounds__(64 * MERGE_WAVES) void merge_kernel(Args a) {
-  __shared__ uint32_t hist[MERGE_WAVES][256];
-  __shared__ float2 blist[MERGE_WAVES][LISTCAP];
-  __shared__ int bcount[MERGE_WAVES];
+template <int MU, int MW>
+__global__ __launch_bounds__(64 * MW) void merge_kernel(Args a) {
+  __shared__ uint32_t hist[MW][256];
+  __shared__ float2 blist[MW][LISTCAP];
+  __shared__ int bcount[MW];
+  __shared__ float2 cut[MW];
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const long long row = (long long)blockIdx.x * MERGE_WAVES + w;
+  const long long row = (long long)blockIdx.x * MW + w;
   if (row >= (long long)a.BH * a.m) return;  // (wave-level work only below)
   const int nch = a.nch, k = a.k;
   // ---- V_L
@@ -1269,7 +1272,23 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void merge_kernel(Args a) {
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
+    // the cut: the listed entry with need - 1 entries of the list before it
+    // (keys are distinct, so the ranks are 0 .. nb - 1 and one entry has it)
+    for (int j = lane; j < nb; j += 64) {
+      const float2 x = blist[w][j];
+      int r = 0;
+      for (int i = 0; i < nb; ++i) {
+        const float2 y = blist[w][i];
+        r += better(y.x, __float_as_int(y.y), x.x, __float_as_int(x.y)) ? 1 : 0;
+      }
+      if (r == need - 1) cut[w] = x;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
   }
+  const float2 cu = cut[w];  // (read only when listed)
+  const float cv = cu.x;
+  const int ckey = __float_as_int(cu.y);
   // winners in list order (entry e0 + 64 u + lane: u-major steps of 64)
   int32_t* out = a.idx + row * k;
   int run = 0;
@@ -1291,19 +1310,17 @@ __global__ __launch_bounds__(64 * MERGE_WAVES) void merge_kernel(Args a) {
         if (bn > bstar) {
           win = true;
         } else if (bn == bstar) {
-          int r = 0;
           if (listed) {
-            for (int j = 0; j < nb; ++j) {
-              const float2 x = blist[w][j];
-              r += better(x.x, __float_as_int(x.y), v[u], key[u]);
-            }
+            // the cut itself or better
+            win = v[u] > cv || (v[u] == cv && key[u] <= ckey);
           } else {
+            int r = 0;
             for (int j = 0; j < n; ++j) {
               const float x = cs[j];
               r += (bin_of(x, A, B) == bstar && better(x, ck[j], v[u], key[u])) ? 1 : 0;
             }
+            win = r < need;
           }
-          win = r < need;
         }
       }
       const uint64_t bw = __ballot(win);
@@ -1386,9 +1403,13 @@ hipError_t launch_landmark_bf16(const float* ql, const void* K, const void* V, i
   const int grid = s.BH >= 8 ? ((s.BH + 7) / 8) * 8 * a.tiles * nch : s.BH * a.tiles * nch;
   kernel<<<grid, 64 * nw, lds, st>>>(a);
   if (nch == 1) return hipGetLastError();
+  // many short rows: four rows per workgroup, eight entries per lane in
+  // flight; few long ones: a workgroup per row, 32 in flight
   const long long rws = (long long)s.BH * s.m;
-  lmk::merge_kernel<<<(unsigned)((rws + lmk::MERGE_WAVES - 1) / lmk::MERGE_WAVES),
-                      64 * lmk::MERGE_WAVES, 0, st>>>(a);
+  if (rws >= 4096)
+    lmk::merge_kernel<8, 4><<<(unsigned)((rws + 3) / 4), 64 * 4, 0, st>>>(a);
+  else
+    lmk::merge_kernel<32, 1><<<(unsigned)rws, 64, 0, st>>>(a);
   return hipGetLastError();
 }
 
