@@ -198,6 +198,40 @@ def test_equal_scores_overflow_the_candidate_buffer():
     _say(f"ok {rep}")
 
 
+def test_equal_scores_across_key_chunks():
+    """A grid past 4096 keys (5120: two key chunks of 2560, joined by the
+    merge kernel) with k = 200, so the landmark pass runs its three-pass,
+    eight-wave form.  Windows of 16 x 16 tokens keep Q_L = (integer sum) / 256
+    exact, so every score and route logit is exact in fp32 and ties are
+    decided by key id alone.  Head 0 has Q = 0: every score is equal, each
+    chunk hands the merge its 200 lowest keys, and the 400 equal candidates
+    overflow the merge's 256-entry boundary list (the rank-against-everything
+    path); the answer is keys 0..199.  Head 1 has integer Q and sparse
+    ternary K: scores repeat exactly, most rows tie at the boundary, and the
+    winners span both chunks (the ranked list and its cut).  idx and route
+    must equal the oracle's lowest-index picks bit for bit."""
+    import oracle.mita_oracle as O
+    B, H, gh, gw, mh, mw, k = 1, 2, 64, 80, 4, 5, 200
+    N = gh * gw
+    rng = np.random.default_rng(13)
+    Q = rng.integers(-2, 3, size=(B, H, N, 64)).astype(np.float32)
+    Q[0, 0] = 0.0
+    K = (rng.integers(-1, 2, size=(B, H, N, 64)) * (rng.random((B, H, N, 64)) < 0.1)).astype(np.float32)
+    V = synth.bf16_round(rng.standard_normal((B, H, N, 64)).astype(np.float32))
+    _say("equal scores across key chunks")
+    res = run_gpu(Q, K, V, "bf16", gh, gw, mh, mw, k)
+    ties = 0
+    for h in range(H):
+        ref = O.mita_head(Q[0, h], K[0, h], V[0, h], gh, gw, mh, mw, k)
+        ties += int(np.sum(ref["gap"] == 0))
+        assert np.array_equal(res["idx"][0, h], ref["idx"]), h
+        assert np.array_equal(res["route"][0, h], ref["route"]), h
+    assert np.array_equal(res["idx"][0, 0], np.tile(np.arange(k), (mh * mw, 1)))
+    assert ties > mh * mw + 8, "the case must tie at the boundary beyond head 0"
+    rep = parity.run_and_check(res, Q, K, V, gh, gw, mh, mw, k, TOL["bf16"])
+    _say(f"ok ties={ties} {rep}")
+
+
 @pytest.mark.parametrize("name", ["tiny-fp32", "deit-t", "deit-s", "hires-3136", "ade-1024",
                                   "ade-1600"])
 def test_workload_full(name):
