@@ -1330,6 +1330,248 @@ __global__ __launch_bounds__(64 * MW) void merge_kernel(Args a) {
   }
 }
 
+// The same join with a four-wave workgroup per row, for few long rows (a
+// 1-D sequence: seq-256k has 512 rows of 16,384 candidates): wave w takes
+// the contiguous quarter [w n / 4, (w + 1) n / 4) of the row's list and
+// chunks w, w + 4, .. of its V_L partials; the histogram, the boundary list
+// and its cut are shared in LDS, and winners are first counted per quarter,
+// then written in list order from each quarter's offset.
+constexpr int CW = 4;  // waves per row
+
+template <int MU>
+__global__ __launch_bounds__(64 * CW) void merge_row_kernel(Args a) {
+  __shared__ uint32_t hist[256];
+  __shared__ float2 blist[LISTCAP];
+  __shared__ float vlo[CW][64];
+  __shared__ float wred[4][CW];  // per wave: V_L max, V_L sum, score min, score max
+  __shared__ int bcount, bsel[3], wcnt[CW];
+  __shared__ float2 cut;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const long long row = blockIdx.x;
+  if (row >= (long long)a.BH * a.m) return;  // (uniform over the workgroup)
+  const int nch = a.nch, k = a.k;
+  for (int i = tid; i < 256; i += 64 * CW) hist[i] = 0u;
+  if (tid == 0) bcount = 0;
+  // ---- V_L: this wave's chunks, then the four partials joined by wave 0
+  {
+    const float* pp = a.vlpart + row * nch * PART_STRIDE;
+    float M = -INFINITY;
+    for (int c0 = w; c0 < nch; c0 += CW * MU) {
+      float mv[MU];
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        const int c = c0 + CW * u;
+        mv[u] = c < nch ? pp[c * PART_STRIDE + 64] : -INFINITY;
+      }
+#pragma unroll
+      for (int u = 0; u < MU; ++u) M = fmaxf(M, mv[u]);
+    }
+    float o = 0.f, L = 0.f;
+    for (int c0 = w; c0 < nch; c0 += CW * MU) {
+      float mv[MU], ov[MU], lv[MU];
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        const int c = c0 + CW * u;
+        const bool ok = c < nch;
+        const float* q = pp + (ok ? c : 0) * PART_STRIDE;
+        mv[u] = ok ? q[64] : -INFINITY;
+        ov[u] = ok ? q[lane] : 0.f;
+        lv[u] = ok ? q[65] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        // (a wave without chunks keeps M = -inf and sums of 0)
+        const float f = mv[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mv[u] - M) * kTauLog2e);
+        o = fmaf(f, ov[u], o);
+        L = fmaf(f, lv[u], L);
+      }
+    }
+    vlo[w][lane] = o;
+    if (lane == 0) {
+      wred[0][w] = M;
+      wred[1][w] = L;
+    }
+  }
+  // ---- top-k: this wave's quarter of the list
+  const int last_keys = a.N - (nch - 1) * a.cblk * KB;
+  const int n = (nch - 1) * k + min(k, last_keys);
+  const int q0 = (int)((long long)w * n / CW), q1 = (int)((long long)(w + 1) * n / CW);
+  const float* cs = a.cand_s + row * nch * k;
+  const int32_t* ck = a.cand_k + row * nch * k;
+  auto load_s = [&](int e0, float (&v)[MU]) {
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      const int e = e0 + 64 * u + lane;
+      v[u] = e < q1 ? cs[e] : -INFINITY;
+    }
+  };
+  {
+    float lo = INFINITY, hi = -INFINITY;
+    for (int e0 = q0; e0 < q1; e0 += 64 * MU) {
+      float v[MU];
+      load_s(e0, v);
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        lo = fminf(lo, e0 + 64 * u + lane < q1 ? v[u] : INFINITY);
+        hi = fmaxf(hi, v[u]);
+      }
+    }
+    lo = wave_min_f(lo);
+    hi = wave_max(hi);
+    if (lane == 0) {
+      wred[2][w] = lo;
+      wred[3][w] = hi;
+    }
+  }
+  __syncthreads();
+  if (w == 0) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < CW; ++i) M = fmaxf(M, wred[0][i]);
+    float o = 0.f, L = 0.f;
+#pragma unroll
+    for (int i = 0; i < CW; ++i) {
+      const float f = wred[0][i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((wred[0][i] - M) * kTauLog2e);
+      o = fmaf(f, vlo[i][lane], o);
+      L = fmaf(f, wred[1][i], L);
+    }
+    a.vl[row * 64 + lane] = o / L;
+    if (a.stats && lane == 0) {
+      a.stats[row].x = M * 0.125f;
+      a.stats[row].y = L;
+    }
+  }
+  float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < CW; ++i) {
+    lo = fminf(lo, wred[2][i]);
+    hi = fmaxf(hi, wred[3][i]);
+  }
+  const float A = hi > lo ? fminf(256.0f / (hi - lo), 1e30f) : 0.f;
+  const float B = -lo * A;
+  for (int e0 = q0; e0 < q1; e0 += 64 * MU) {
+    float v[MU];
+    load_s(e0, v);
+#pragma unroll
+    for (int u = 0; u < MU; ++u)
+      if (e0 + 64 * u + lane < q1) atomicAdd(&hist[bin_of(v[u], A, B)], 1u);
+  }
+  __syncthreads();
+  // the boundary bin (wave 0; lane l holds bins 4l .. 4l + 3)
+  if (w == 0) {
+    int cb[4], local = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      cb[q] = (int)hist[4 * lane + q];
+      local += cb[q];
+    }
+    const int suf = wave_suffix(local, lane);
+    const int above_lane = suf - local;
+    if (above_lane < k && k <= suf) {
+      int acc = above_lane;
+#pragma unroll
+      for (int q = 3; q >= 0; --q) {
+        if (acc + cb[q] >= k) {
+          bsel[0] = 4 * lane + q;
+          bsel[1] = acc;
+          bsel[2] = cb[q];
+          break;
+        }
+        acc += cb[q];
+      }
+    }
+  }
+  __syncthreads();
+  const int bstar = bsel[0], above = bsel[1], nb = bsel[2];
+  const int need = k - above;
+  const bool listed = nb <= LISTCAP;
+  if (listed) {
+    for (int e0 = q0; e0 < q1; e0 += 64 * MU) {
+      float v[MU];
+      load_s(e0, v);
+      int kk[MU];
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        const int e = e0 + 64 * u + lane;
+        kk[u] = e < q1 && bin_of(v[u], A, B) == bstar ? ck[e] : -1;
+      }
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        if (kk[u] >= 0) {
+          const int at = atomicAdd(&bcount, 1);
+          blist[at] = make_float2(v[u], __int_as_float(kk[u]));
+        }
+      }
+    }
+    __syncthreads();
+    // the cut: the listed entry with need - 1 entries of the list before it
+    for (int j = tid; j < nb; j += 64 * CW) {
+      const float2 x = blist[j];
+      int r = 0;
+      for (int i = 0; i < nb; ++i) {
+        const float2 y = blist[i];
+        r += better(y.x, __float_as_int(y.y), x.x, __float_as_int(x.y)) ? 1 : 0;
+      }
+      if (r == need - 1) cut = x;
+    }
+    __syncthreads();
+  }
+  const float cv = cut.x;  // (read only when listed)
+  const int ckey = __float_as_int(cut.y);
+  auto wins = [&](float v, int key) {
+    const int bn = bin_of(v, A, B);
+    if (bn > bstar) return true;
+    if (bn < bstar) return false;
+    if (listed) return v > cv || (v == cv && key <= ckey);
+    int r = 0;
+    for (int j = 0; j < n; ++j) {
+      const float x = cs[j];
+      r += (bin_of(x, A, B) == bstar && better(x, ck[j], v, key)) ? 1 : 0;
+    }
+    return r < need;
+  };
+  // winners: counted per quarter, then written in list order
+  int mine = 0;
+  for (int e0 = q0; e0 < q1; e0 += 64 * MU) {
+    float v[MU];
+    int key[MU];
+    load_s(e0, v);
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      const int e = e0 + 64 * u + lane;
+      key[u] = e < q1 ? ck[e] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      const int e = e0 + 64 * u + lane;
+      mine += __popcll(__ballot(e < q1 && wins(v[u], key[u])));
+    }
+  }
+  if (lane == 0) wcnt[w] = mine;
+  __syncthreads();
+  int run = 0;
+  for (int i = 0; i < w; ++i) run += wcnt[i];
+  int32_t* out = a.idx + row * k;
+  for (int e0 = q0; e0 < q1; e0 += 64 * MU) {
+    float v[MU];
+    int key[MU];
+    load_s(e0, v);
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      const int e = e0 + 64 * u + lane;
+      key[u] = e < q1 ? ck[e] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      const int e = e0 + 64 * u + lane;
+      const bool win = e < q1 && wins(v[u], key[u]);
+      const uint64_t bw = __ballot(win);
+      if (win) out[run + lanes_below(bw)] = key[u];
+      run += __popcll(bw);
+    }
+  }
+}
+
 }  // namespace lmk
 
 // The row buffer holds k plus one block of candidates (k + 64 entries, at
@@ -1404,12 +1646,12 @@ hipError_t launch_landmark_bf16(const float* ql, const void* K, const void* V, i
   kernel<<<grid, 64 * nw, lds, st>>>(a);
   if (nch == 1) return hipGetLastError();
   // many short rows: four rows per workgroup, eight entries per lane in
-  // flight; few long ones: a workgroup per row, 32 in flight
+  // flight; few long ones: a four-wave workgroup per row
   const long long rws = (long long)s.BH * s.m;
   if (rws >= 4096)
     lmk::merge_kernel<8, 4><<<(unsigned)((rws + 3) / 4), 64 * 4, 0, st>>>(a);
   else
-    lmk::merge_kernel<32, 1><<<(unsigned)rws, 64, 0, st>>>(a);
+    lmk::merge_row_kernel<8><<<(unsigned)rws, 64 * lmk::CW, 0, st>>>(a);
   return hipGetLastError();
 }
 
