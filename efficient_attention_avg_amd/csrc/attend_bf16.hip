@@ -9,17 +9,19 @@
 // expert's queries, in expert order) are cut into P contiguous ranges of
 // near-equal length, one per workgroup, so that a large expert's queries are
 // spread over several workgroups.  Per workgroup:
-//   * load its segments' table (each a run of one expert's queries: range,
-//     key ids, first 64 query ids) and the head's Q_L (bf16 hi + lo) and
-//     V_L^T (f16) into LDS once;
+//   * load its segments' table (each a run of one expert's queries: range
+//     and the expert's key ids) and the head's Q_L (bf16 hi + lo, or one f16
+//     copy where that leaves the room for resident slots) and V_L^T (f16)
+//     into LDS once;
 //   * per segment: its expert's k key rows (bf16) and value rows (f16) sit in LDS,
 //     shared by the four waves; V^T fragments come from the value rows by the
-//     transposing LDS read.  While one expert is computed the
-//     next one's rows (and the Q rows of its first 64 queries) are already
-//     loading into registers; the expert's output stores are issued only
-//     after those rows have been waited for, since stores and loads drain
-//     through one counter.  For k > 64 the slots past the first 64 are
-//     gathered in place, 64 at a time;
+//     transposing LDS read.  While one segment is computed the
+//     next one's first 64 rows (and the Q rows of its first 64 queries) are
+//     already loading into registers; the segment's output stores are issued
+//     only after those rows have been waited for, since stores and loads
+//     drain through one counter.  For k > 64 the slots past the first 64 are
+//     staged once per segment when all k fit (resident), else gathered in
+//     place 64 at a time for every pass;
 //   * per pass of <= 64 of the expert's queries, each wave owns 16: Q rows
 //     are the B operand of logits^T = [Q_L; K_e] Q^T; an online softmax runs
 //     over 32-entry chunks (shared entries first, then the expert's keys), and

@@ -5,8 +5,9 @@
 // into the landmark values V_L).
 //
 // One kernel.  A workgroup owns 32 landmark rows of one head (two 16-row MFMA
-// tiles, so every K block loaded feeds both); its four waves split the head's
-// keys (wave w takes the 64-key blocks w, w+4, ...).  Raw scores
+// tiles, so every K block loaded feeds both); its four waves (eight where the
+// candidate buffers of a large k already leave one workgroup per CU) split
+// the head's keys (wave w takes the 64-key blocks w, w+NW, ...).  Raw scores
 // c = Q_L . K (the scale tau = 1/8 is a power of two, so it is folded into the
 // softmax and bin constants without changing any order) run on bf16 MFMA
 // with K rows loaded straight into the A operand and Q_L split hi + lo
@@ -34,7 +35,8 @@
 //      are written ascending through a bitmap in the row's histogram space
 //      (or, for N > 8192, by counting).
 // Workgroups of one head are launched on one XCD so its K and V come from HBM
-// once and are re-read from that XCD's L2.
+// once and are re-read from that XCD's L2 (with fewer than 8 heads they
+// alternate over the XCDs, so that every XCD has work).
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
@@ -99,7 +101,7 @@ struct Args {
   int BH, N, m, k, cap, tiles;
   // keys split into nch chunks of cblk blocks (nch > 1: each workgroup writes
   // its chunk's top-k as (score, key) pairs and its unnormalised V_L partial,
-  // and merge_kernel finishes both)
+  // and merge_kernel or merge_row_kernel finishes both)
   int nch, cblk;
   // 1: the histogram is built during the values pass on bins fixed from
   // each wave's first block; 0: a third pass builds it on the exact range
@@ -1113,10 +1115,9 @@ __global__ __launch_bounds__(64 * NW) void landmark_kernel(Args a) {
 // are written in list order, which is ascending key order.
 // MW rows per workgroup (a wave each) and MU entries per lane in flight:
 // every loop over the candidate list reads MU entries per lane before using
-// any.  Many short rows (long-16k: 8,192 rows of 1,024) take MW = 4, MU = 8;
-// few long ones (a 1-D sequence, seq-256k: 512 rows of 16,384) a workgroup
-// per row, so that they spread over every CU, and MU = 32 (8 round trips per
-// pass instead of 32).
+// any.  Used for many short rows (long-16k: 8,192 rows of 1,024, MW = 4,
+// MU = 8); few long ones (a 1-D sequence, seq-256k: 512 rows of 16,384) go
+// to merge_row_kernel below, four waves per row.
 constexpr int LISTCAP = 256;
 
 __device__ __forceinline__ int wave_suffix(int v, int lane) {
