@@ -269,6 +269,13 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
     }
     __syncthreads();
 
+    // The head's short, barrier-separated phases (B to F and the V_L step)
+    // issue at a raised wave priority, the expert tiles (G) at the normal
+    // one: the other workgroup on the CU is then most often in its tiles, and
+    // its instructions fill the gaps of this workgroup's barrier-bound path
+    // instead of delaying it (DeiT-S: 67.0 -> 64.9 us per step; priority 1
+    // gave 65.1, a higher level for top-k and routing alone none).
+    __builtin_amdgcn_s_setprio(3);
     // ---------------- B: landmark pooling as a contraction over tokens,
     // Q_L^T = Q^T W (W: 0/1 window membership) on bf16 MFMA, then / window size
     {
@@ -717,6 +724,7 @@ __global__ __launch_bounds__(THREADS, 4) void mita_fused_kernel(
     }
     __syncthreads();
 
+    __builtin_amdgcn_s_setprio(0);
     // ---------------- G: grouped expert attention over 16-query tiles of the
     // sorted order; a tile spans the experts of its queries, each column
     // taking the routed half of its own expert
